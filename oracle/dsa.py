@@ -1,0 +1,220 @@
+"""The indexer -> Top-K -> sparse-attention step, written out in binary64.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Each function follows one step of the method as Baidu AI Cloud's "Day0
+Inference Support and Performance Optimization for New Architecture LLMs"
+describes it in section 2.2 (score every historical position, aggregate the
+per-head scores with head weights, keep the Top-K positions, attend over only
+those rows), with the paged caches of sections 4.1-4.2.  Library primitives
+(a matrix product, a sort, exp/log) serve as steps; there is no blocking,
+fusion or reordering beyond the definitions.
+
+Array conventions (raw storage bits, exactly what the GPU reads):
+
+* ``qI``  uint8 E4M3 codes   [rows, H_I, D_I]   indexer queries
+* ``w``   float32            [rows, H_I]        head weights
+* ``kI_cache`` uint8 E4M3    [num_blocks, 64, D_I]  paged index keys
+* ``q``   uint16 bf16 bits   [rows, H_q, D_qk]  attention queries
+* ``k_cache`` uint16 bf16    [num_blocks, 64, D_qk] paged keys (latent rows)
+* ``v_cache`` uint16 bf16    [num_blocks, 64, D_v] or None (latent layout:
+  V is the first D_v columns of the K row)
+* ``block_table`` int32 [num_seqs, max_blocks]; ``seq_lens`` int32 [num_seqs]
+"""
+
+import numpy as np
+
+from .formats import bf16_to_f64, e4m3_to_f64
+
+#: tokens per page of every paged cache
+BLOCK = 64
+
+
+def resolve_rows(seq_lens, num_rows=None, row_seq=None, row_pos=None):
+    """Sequence and position of every query row.
+
+    Decode (no row arrays): row r belongs to sequence r and sits at that
+    sequence's last position seq_lens[r] - 1.  Chunked prefill passes
+    ``row_seq`` / ``row_pos`` explicitly.  Reading of "all historical
+    positions" (Day0 article, section 2.2): row r's history is positions
+    0 .. p_r inclusive -- the current token's key is already in the cache.
+    """
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    if num_rows is None:
+        num_rows = len(row_seq) if row_seq is not None else len(seq_lens)
+    rs = np.arange(num_rows) if row_seq is None else np.asarray(row_seq, np.int64)
+    rp = seq_lens[rs] - 1 if row_pos is None else np.asarray(row_pos, np.int64)
+    return rs.astype(np.int64), rp.astype(np.int64)
+
+
+def gather_positions(cache, table_row, positions, block=BLOCK):
+    """Rows of a paged cache for logical positions of one sequence.
+
+    Position s lives in physical block table_row[s // block], row s % block
+    (paged K cache read directly by the indexer, Day0 article section 4.1;
+    selected KV rows gathered from the main cache, section 4.2).
+    """
+    positions = np.asarray(positions, dtype=np.int64)
+    phys = np.asarray(table_row, dtype=np.int64)[positions // block]
+    return cache[phys, positions % block]
+
+
+def indexer_scores_row(qI_codes, w, kI_rows):
+    """Index score of one query row against the given key rows.
+
+    I[s] = sum_h w[h] * max(0, sum_d qI[h, d] * kI[s, d])
+
+    Scoring against every historical position, then aggregating the per-head
+    scores with head weights (Day0 article, section 2.2; the fused call
+    ``fused_topk(q8, k, g)`` of section 4.3 takes exactly these three
+    inputs).  Readings: the per-head score passes a ReLU gate before the
+    weighting; one shared index key per position serves every indexer head.
+
+    The per-head dot products are exact in binary64: E4M3 products carry at
+    most 8 significant bits, lie between 2**-18 and 448**2, so a sum of a few
+    hundred of them needs far fewer than 53 bits.  The weighted head sum is
+    formed in binary64 and rounded once to float32; a zero score is stored as
+    +0.
+    """
+    q = e4m3_to_f64(qI_codes)                       # [H_I, D_I]
+    k = e4m3_to_f64(kI_rows)                        # [L, D_I]
+    dot = q @ k.T                                   # [H_I, L]
+    gated = np.maximum(dot, 0.0)                    # ReLU gate, per head
+    weights = np.asarray(w, dtype=np.float32).astype(np.float64)
+    total = weights @ gated                         # head-weighted sum, [L]
+    return (total.astype(np.float32) + np.float32(0.0)).astype(np.float32)
+
+
+def score_keys(scores):
+    """Order-preserving unsigned 32-bit key of each float32 score.
+
+    Larger score -> larger key.  -0 and +0 share one key.  NaN gets key 0 and
+    so ranks below every number (reading: the pages say nothing about NaN;
+    generated inputs never produce one).
+    """
+    s = np.array(scores, dtype=np.float32, copy=True)
+    s[s == 0] = np.float32(0.0)
+    u = s.view(np.uint32)
+    negative = (u >> np.uint32(31)) == 1
+    key = np.where(negative, ~u, u | np.uint32(0x80000000)).astype(np.uint32)
+    key[np.isnan(s)] = 0
+    return key
+
+
+def topk_row(scores, K):
+    """Top-K positions of one row's scores.
+
+    Keeps the min(K, L) positions with the largest score (Day0 article,
+    section 2.2).  Readings: equal scores go to the lower position; the kept
+    positions are returned in ascending order, padded with -1 up to K.
+    Returns (indices int32 [K], count).
+    """
+    L = len(scores)
+    keys = score_keys(scores).astype(np.int64)
+    positions = np.arange(L, dtype=np.int64)
+    order = np.lexsort((positions, -keys))          # key descending, then position ascending
+    count = min(int(K), L)
+    out = np.full(int(K), -1, dtype=np.int32)
+    out[:count] = np.sort(order[:count])
+    return out, count
+
+
+def sparse_attn_row(q_bits, k_rows_bits, v_rows_bits, scale):
+    """Softmax attention of one query row over the gathered rows only.
+
+    For every query head h and selected row j:
+      logit[h, j] = scale * sum_d q[h, d] * k[j, d]
+      o[h] = sum_j exp(logit[h, j] - m_h) v[j] / sum_j exp(logit[h, j] - m_h)
+    with m_h the largest logit; lse[h] = m_h + log(sum_j exp(logit[h, j] - m_h)).
+    The sparse core reads only the selected KV rows (Day0 article, section
+    2.2); one KV head serves every query head (SPLASH summary, section 2).
+    With no rows selected the output is 0 and lse is -inf.
+    Returns (o float64 [H_q, D_v], lse float64 [H_q]).
+    """
+    q = bf16_to_f64(q_bits)
+    k = bf16_to_f64(k_rows_bits)
+    v = bf16_to_f64(v_rows_bits)
+    H_q, D_v = q.shape[0], v.shape[1]
+    if k.shape[0] == 0:
+        return np.zeros((H_q, D_v)), np.full(H_q, -np.inf)
+    logits = scale * (q @ k.T)                      # [H_q, n]
+    m = logits.max(axis=1)
+    p = np.exp(logits - m[:, None])
+    l = p.sum(axis=1)
+    o = (p @ v) / l[:, None]
+    return o, m + np.log(l)
+
+
+def masked_dense_attn_row(q_bits, k_all_bits, v_all_bits, selected, scale):
+    """Dense attention over every history row, with unselected rows masked out.
+
+    Computes logits against all rows 0..L-1, sets the unselected ones to -inf
+    and normalises over the whole row: the brute-force counterpart of
+    ``sparse_attn_row`` (no gather).  Returns (o [H_q, D_v], lse [H_q]).
+    """
+    q = bf16_to_f64(q_bits)
+    k = bf16_to_f64(k_all_bits)
+    v = bf16_to_f64(v_all_bits)
+    mask = np.asarray(selected, dtype=bool)
+    logits = scale * (q @ k.T)
+    logits[:, ~mask] = -np.inf
+    m = logits.max(axis=1)
+    e = np.exp(logits - m[:, None])
+    l = e.sum(axis=1)
+    return (e @ v) / l[:, None], m + np.log(l)
+
+
+def dense_causal_attn_row(q_bits, k_all_bits, v_all_bits, scale):
+    """softmax(scale * q K^T) V over the whole history of one row.
+
+    The dense attention of THInfer ("Bandwidth-Aware LLM Inference on
+    Heterogeneous Many-Core Supercomputers"), eq. 9, with the scale as an
+    argument; causal because the history stops at the row's own position.
+    """
+    q = bf16_to_f64(q_bits)
+    k = bf16_to_f64(k_all_bits)
+    v = bf16_to_f64(v_all_bits)
+    s = scale * (q @ k.T)
+    s -= s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=1, keepdims=True)
+    return p @ v
+
+
+def decode_step(*, qI, w, kI_cache, q, k_cache, v_cache, block_table, seq_lens,
+                K, scale, D_v, row_seq=None, row_pos=None, rows=None,
+                keep_scores=True):
+    """The whole step for the chosen query rows (default: all rows).
+
+    Row by row: index scores over positions 0..p_r, Top-K, gather of the
+    selected KV rows, sparse softmax attention.  Returns a dict with
+    ``scores`` (list of float32 arrays, or None), ``indices`` int32 [R, K],
+    ``counts`` int64 [R], ``out`` float64 [R, H_q, D_v], ``lse`` float64
+    [R, H_q] and ``rows`` (the row ids, in order).
+    """
+    num_rows = qI.shape[0]
+    rs, rp = resolve_rows(seq_lens, num_rows, row_seq, row_pos)
+    rows = np.arange(num_rows) if rows is None else np.asarray(rows, np.int64)
+    H_q = q.shape[1]
+    out = np.zeros((len(rows), H_q, D_v))
+    lse = np.zeros((len(rows), H_q))
+    indices = np.full((len(rows), int(K)), -1, dtype=np.int32)
+    counts = np.zeros(len(rows), dtype=np.int64)
+    scores = [] if keep_scores else None
+    for i, r in enumerate(rows):
+        b, p = rs[r], rp[r]
+        history = np.arange(p + 1)
+        sc = indexer_scores_row(qI[r], w[r], gather_positions(kI_cache, block_table[b], history))
+        idx, n = topk_row(sc, K)
+        chosen = idx[:n]
+        k_rows = gather_positions(k_cache, block_table[b], chosen)
+        if v_cache is None:
+            v_rows = k_rows[:, :D_v]
+        else:
+            v_rows = gather_positions(v_cache, block_table[b], chosen)
+        out[i], lse[i] = sparse_attn_row(q[r], k_rows, v_rows, scale)
+        indices[i], counts[i] = idx, n
+        if keep_scores:
+            scores.append(sc)
+    return {"scores": scores, "indices": indices, "counts": counts,
+            "out": out, "lse": lse, "rows": rows}

@@ -1,0 +1,40 @@
+"""Storage formats of the hot path's inputs, decoded from their definitions.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+* FP8 E4M3, OCP "FN" flavour -- the FP8 the indexer and KV cache are stored in
+  (Baidu Day0 article, sections 5.1-5.2; "FP8 E4M3" KV in the SPLASH summary,
+  section 5): 1 sign bit, a 4-bit exponent with bias 7 and a 3-bit mantissa.
+  Exponent field 0 holds subnormals m * 2**-9.  The two codes whose exponent
+  and mantissa bits are all ones (0x7F and 0xFF) are NaN; there is no
+  infinity, so the largest finite magnitude is 1.75 * 2**8 = 448.
+* bfloat16: the upper 16 bits of an IEEE-754 binary32 value.
+"""
+
+import numpy as np
+
+
+def _e4m3_value(code: int) -> float:
+    sign = -1.0 if code & 0x80 else 1.0
+    exponent = (code >> 3) & 0xF
+    mantissa = code & 0x7
+    if exponent == 0xF and mantissa == 0x7:
+        return float("nan")
+    if exponent == 0:
+        return sign * mantissa * 2.0 ** -9
+    return sign * (1.0 + mantissa / 8.0) * 2.0 ** (exponent - 7)
+
+
+#: value of every one of the 256 E4M3 codes, as binary64
+E4M3_TABLE = np.array([_e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Decode an array of E4M3 byte codes to binary64 (exact)."""
+    return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Decode an array of bfloat16 bit patterns (uint16) to binary64 (exact)."""
+    wide = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return wide.view(np.float32).astype(np.float64)

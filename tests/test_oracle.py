@@ -1,0 +1,321 @@
+"""Pins of the CPU oracle against things other than itself.
+
+The pages print no worked numeric example for any step of the path, so every
+pin here is a closed form, a brute-force route that does not share the
+oracle's code path, a library routine, or an invariant that a plausible slip
+(a dropped term, a wrong sign or index, a transposed operand, a misplaced
+gate, a wrong tie rule) breaks.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from oracle.formats import E4M3_TABLE
+from tests.helpers import run_oracle
+from workloads import make_batch, oracle_arrays, small_workload
+
+
+# ----------------------------------------------------------------- formats
+
+def test_e4m3_closed_form_codes():
+    # values worked out by hand from the E4M3 field layout (s eeee mmm, bias 7)
+    cases = {
+        0x00: 0.0, 0x38: 1.0, 0x40: 2.0, 0x44: 3.0, 0x48: 4.0, 0x4A: 5.0,
+        0x4C: 6.0, 0x4E: 7.0, 0x50: 8.0, 0x30: 0.5, 0x7E: 448.0, 0xFE: -448.0,
+        0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0xB8: -1.0,
+        0x3C: 1.5, 0x77: 240.0,
+    }
+    for code, val in cases.items():
+        assert oracle.e4m3_to_f64([code])[0] == val, hex(code)
+    neg_zero = oracle.e4m3_to_f64([0x80])[0]
+    assert neg_zero == 0.0 and math.copysign(1.0, neg_zero) < 0
+    assert np.isnan(E4M3_TABLE[0x7F]) and np.isnan(E4M3_TABLE[0xFF])
+    assert np.isfinite(np.delete(E4M3_TABLE, [0x7F, 0xFF])).all()
+
+
+def test_e4m3_matches_torch_decoder():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = oracle.e4m3_to_f64(np.arange(256))
+    both_nan = np.isnan(ref) & np.isnan(mine)
+    assert (both_nan | (ref == mine)).all()
+    assert (np.signbit(ref) == np.signbit(mine))[~both_nan].all()
+
+
+def test_e4m3_ordering_and_integers():
+    pos = E4M3_TABLE[0x00:0x7F]
+    assert (np.diff(pos) > 0).all()                         # codes 0..0x7E strictly increasing
+    assert (E4M3_TABLE[0x80:0xFF] == -pos).all()            # sign-magnitude mirror
+    ints = torch.arange(-8, 9, dtype=torch.float32)
+    codes = ints.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (oracle.e4m3_to_f64(codes) == ints.numpy()).all()
+
+
+def test_bf16_decoder():
+    cases = {0x3F80: 1.0, 0xC000: -2.0, 0x4049: 3.140625, 0x0000: 0.0, 0x7F80: np.inf,
+             0x3E80: 0.25, 0x0001: 2.0 ** -133}
+    for bits, val in cases.items():
+        assert oracle.bf16_to_f64([bits])[0] == val, hex(bits)
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0, 1 << 16, 50000).astype(np.uint16)
+    bits = bits[((bits >> 7) & 0xFF) != 0xFF]               # no inf/NaN
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert (oracle.bf16_to_f64(bits) == ref).all()
+
+
+# ----------------------------------------------------------- index scores
+
+def _e4m3(x):
+    return torch.tensor(x, dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_scores_one_hot_keys_closed_form():
+    # key s = c_s * e_{d_s}: the dot product collapses to c_s * q[h, d_s], so
+    # I[s] = sum_h w_h * max(0, c_s * q[h, d_s]).  H_I != D_I so a transposed
+    # operand cannot pass.
+    rng = np.random.default_rng(1)
+    H, D, L = 5, 16, 40
+    q = rng.integers(-8, 9, (H, D))
+    w = rng.integers(0, 4, H).astype(np.float32)
+    d_s = rng.integers(0, D, L)
+    c_s = rng.choice([-3, -1, 1, 2, 4], L)
+    k = np.zeros((L, D))
+    k[np.arange(L), d_s] = c_s
+    got = oracle.indexer_scores_row(_e4m3(q), w, _e4m3(k))
+    for s in range(L):
+        want = 0.0
+        for h in range(H):
+            want += float(w[h]) * max(0.0, float(c_s[s]) * float(q[h, d_s[s]]))
+        assert got[s] == np.float32(want), s
+
+
+def test_scores_gate_is_per_head():
+    # two heads of opposite sign on one key: a gate applied after the head sum
+    # would give max(0, 3*4 - 2*4) = 4; the per-head gate gives 3*4 = 12.
+    q = np.zeros((2, 4)); q[0, 0] = 4; q[1, 0] = -4
+    k = np.zeros((1, 4)); k[0, 0] = 1
+    w = np.array([3.0, 2.0], np.float32)
+    assert oracle.indexer_scores_row(_e4m3(q), w, _e4m3(k))[0] == 12.0
+    # every head gated off, with a negative weight: the score is +0
+    w2 = np.array([-1.0, -2.0], np.float32)
+    z = oracle.indexer_scores_row(_e4m3(-np.abs(q)), w2, _e4m3(k))[0]
+    assert z == 0 and not np.signbit(z)
+
+
+def test_scores_linear_identity():
+    # max(0, x) - max(0, -x) = x, so I(q) - I(-q) = sum_h w_h q_h . k_s
+    # = k_s . (sum_h w_h q_h): weights folded into the query first, a
+    # different association than the oracle's (per-head dots, then weights).
+    rng = np.random.default_rng(2)
+    H, D, L = 7, 64, 300
+    q = rng.integers(-8, 9, (H, D)).astype(np.float64)
+    k = rng.integers(-8, 9, (L, D)).astype(np.float64)
+    w = rng.integers(0, 4, H).astype(np.float32)
+    plus = oracle.indexer_scores_row(_e4m3(q), w, _e4m3(k)).astype(np.float64)
+    minus = oracle.indexer_scores_row(_e4m3(-q), w, _e4m3(k)).astype(np.float64)
+    folded = (w.astype(np.float64)[:, None] * q).sum(axis=0)      # [D]
+    want = (k * folded[None, :]).sum(axis=1)
+    assert (plus - minus == want).all()
+
+
+def test_scores_integer_mode_exact_and_invariant():
+    rng = np.random.default_rng(3)
+    H, D, L = 64, 128, 200
+    q = rng.integers(-8, 9, (H, D))
+    k = rng.integers(-8, 9, (L, D))
+    w = rng.integers(0, 4, H).astype(np.float32)
+    s = oracle.indexer_scores_row(_e4m3(q), w, _e4m3(k))
+    assert (s == np.round(s)).all()
+    # exact integer arithmetic as an independent route
+    dots = [[sum(int(a) * int(b) for a, b in zip(q[h], k[j])) for j in range(L)] for h in range(H)]
+    want = [sum(int(w[h]) * max(0, dots[h][j]) for h in range(H)) for j in range(L)]
+    assert (s.astype(np.int64) == np.array(want)).all()
+    # doubling every weight doubles every score exactly
+    assert (oracle.indexer_scores_row(_e4m3(q), 2 * w, _e4m3(k)) == 2 * s).all()
+    # permuting heads together with their weights changes nothing
+    perm = rng.permutation(H)
+    assert (oracle.indexer_scores_row(_e4m3(q[perm]), w[perm], _e4m3(k)) == s).all()
+
+
+def test_scores_gaussian_close_to_float64_reference():
+    # Gaussian E4M3 inputs: the float32 score is the binary64 value rounded
+    # once; compare with torch's float64 route at half an ulp.
+    g = torch.Generator().manual_seed(4)
+    qc = torch.randn(64, 128, generator=g).to(torch.float8_e4m3fn)
+    kc = torch.randn(500, 128, generator=g).to(torch.float8_e4m3fn)
+    w = torch.rand(64, generator=g) * 3
+    ref = (w.double()[:, None] * torch.relu(qc.double() @ kc.double().T)).sum(0)
+    got = oracle.indexer_scores_row(qc.view(torch.uint8).numpy(), w.numpy(), kc.view(torch.uint8).numpy())
+    ulp = np.spacing(np.abs(got).astype(np.float32)).astype(np.float64)
+    assert (np.abs(got.astype(np.float64) - ref.numpy()) <= 0.5 * ulp + 1e-300).all()
+
+
+# ------------------------------------------------------------------ Top-K
+
+def test_score_keys_order():
+    vals = np.array([-np.inf, -3.4e38, -1.0, -1e-40, -0.0, 0.0, 1e-45, 1e-40, 1.0, 2.0,
+                     3.4e38, np.inf], dtype=np.float32)
+    keys = oracle.score_keys(vals).astype(np.int64)
+    assert (np.diff(keys)[[0, 1, 2, 3]] > 0).all()
+    assert keys[4] == keys[5]                                # -0 and +0 tie
+    assert (np.diff(keys)[5:] > 0).all()
+    assert oracle.score_keys(np.array([np.nan], np.float32))[0] == 0
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000)).astype(np.float32)
+    kx = oracle.score_keys(x).astype(np.int64)
+    i, j = rng.integers(0, len(x), (2, 20000))
+    assert ((x[i] < x[j]) == (kx[i] < kx[j])).all()
+
+
+def _topk_brute(values, K):
+    # Python's own sort on the float values: largest first, ties to the lower index
+    order = sorted(range(len(values)), key=lambda i: (-float(values[i]), i))
+    chosen = sorted(order[:min(K, len(values))])
+    return chosen + [-1] * (K - len(chosen))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_topk_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    L = int(rng.integers(1, 400))
+    K = int(rng.integers(1, 80))
+    if seed % 3 == 0:
+        vals = rng.integers(-5, 6, L).astype(np.float32)            # heavy ties
+    elif seed % 3 == 1:
+        vals = rng.standard_normal(L).astype(np.float32)
+    else:
+        vals = rng.choice(np.array([-np.inf, -2.0, -0.0, 0.0, 1.0, 7.0, np.inf], np.float32), L)
+    idx, n = oracle.topk_row(vals, K)
+    assert n == min(K, L)
+    assert idx.tolist() == _topk_brute(vals, K)
+
+
+def test_topk_closed_forms():
+    idx, n = oracle.topk_row(np.full(100, 3.0, np.float32), 10)
+    assert n == 10 and idx.tolist() == list(range(10))             # all equal: lowest positions
+    idx, n = oracle.topk_row(np.arange(5, dtype=np.float32), 8)
+    assert n == 5 and idx.tolist() == [0, 1, 2, 3, 4, -1, -1, -1]  # K >= L: everything
+    vals = np.zeros(1000, np.float32)
+    planted = [3, 77, 500, 999]
+    vals[planted] = [5, 9, 7, 6]
+    idx, n = oracle.topk_row(vals, 4)
+    assert idx.tolist() == planted                                  # ascending positions
+    vals[[10, 20]] = -0.0                                           # -0 ties +0: lower positions win
+    idx, _ = oracle.topk_row(vals, 6)
+    assert idx.tolist() == [0, 1, 3, 77, 500, 999]
+
+
+# -------------------------------------------------------------- attention
+
+def _bf16(x):
+    return torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_attention_sparse_equals_masked_dense():
+    rng = np.random.default_rng(6)
+    H, D, Dv, L = 8, 64, 48, 90
+    q, k, v = _bf16(rng.standard_normal((H, D))), _bf16(rng.standard_normal((L, D))), \
+        _bf16(rng.standard_normal((L, Dv)))
+    sel = np.sort(rng.choice(L, 30, replace=False))
+    o, lse = oracle.sparse_attn_row(q, k[sel], v[sel], 0.125)
+    mask = np.zeros(L, bool); mask[sel] = True
+    o2, lse2 = oracle.masked_dense_attn_row(q, k, v, mask, 0.125)
+    assert np.allclose(o, o2, rtol=1e-13, atol=1e-13) and np.allclose(lse, lse2, rtol=1e-13)
+    logits = 0.125 * oracle.bf16_to_f64(q) @ oracle.bf16_to_f64(k[sel]).T
+    assert np.allclose(lse, scipy.special.logsumexp(logits, axis=1), rtol=1e-13)
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(7)
+    H, D, Dv, n = 4, 32, 16, 12
+    q, k, v = _bf16(rng.standard_normal((H, D))), _bf16(rng.standard_normal((n, D))), \
+        _bf16(rng.standard_normal((n, Dv)))
+    vf = oracle.bf16_to_f64(v)
+    o, lse = oracle.sparse_attn_row(q, k[5:6], v[5:6], 0.3)         # one row: o = v_s
+    assert np.allclose(o, np.broadcast_to(vf[5], o.shape), rtol=0, atol=1e-15)
+    assert np.allclose(lse, 0.3 * oracle.bf16_to_f64(q) @ oracle.bf16_to_f64(k[5]), rtol=1e-14)
+    const = _bf16(np.full((n, Dv), 1.5))
+    o, _ = oracle.sparse_attn_row(q, k, const, 0.3)                 # constant V
+    assert np.allclose(o, 1.5, rtol=0, atol=1e-14)
+    o, lse = oracle.sparse_attn_row(_bf16(np.zeros((H, D))), k, v, 0.3)   # q = 0: mean of V
+    assert np.allclose(o, np.broadcast_to(vf.mean(axis=0), o.shape), atol=1e-14)
+    assert np.allclose(lse, math.log(n))
+    o, lse = oracle.sparse_attn_row(q, k[:0], v[:0], 0.3)
+    assert (o == 0).all() and np.isneginf(lse).all()
+
+
+def test_dense_causal_matches_torch_sdpa():
+    rng = np.random.default_rng(8)
+    H, D, Dv, L = 6, 64, 32, 77
+    q, k, v = _bf16(rng.standard_normal((H, D))), _bf16(rng.standard_normal((L, D))), \
+        _bf16(rng.standard_normal((L, Dv)))
+    scale = 1 / 8
+    got = oracle.dense_causal_attn_row(q, k, v, scale)
+    tq = torch.from_numpy(oracle.bf16_to_f64(q))[None, :, None, :]
+    tk = torch.from_numpy(oracle.bf16_to_f64(k))[None, None].expand(1, H, L, D)
+    tv = torch.from_numpy(oracle.bf16_to_f64(v))[None, None].expand(1, H, L, Dv)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale)[0, :, 0].numpy()
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------- end to end
+
+def _tiny(**kw):
+    base = dict(H_I=4, D_I=64, H_q=8, D_qk=64, D_v=64, K=64, scale=0.125, mode="int")
+    base.update(kw)
+    return base
+
+
+def test_decode_step_K_at_least_L_is_dense_causal():
+    # with K >= every history length the sparse step is dense causal attention
+    wl = small_workload("t", lengths=[1, 37, 64, 65, 130], latent=True, **_tiny(K=256, D_qk=96))
+    arr = oracle_arrays(make_batch(wl, seed=9))
+    res = run_oracle(arr)
+    for i in range(5):
+        b, p = arr["row_seq"][i], arr["row_pos"][i]
+        hist = np.arange(p + 1)
+        assert res["counts"][i] == p + 1
+        assert res["indices"][i][:p + 1].tolist() == hist.tolist()
+        k_all = oracle.gather_positions(arr["k_cache"], arr["block_table"][b], hist)
+        dense = oracle.dense_causal_attn_row(arr["q"][i], k_all, k_all[:, :64], wl.scale)
+        assert np.allclose(res["out"][i], dense, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_step_block_table_shuffle_invariance():
+    wl = small_workload("t", lengths=[300, 129, 700], latent=False, **_tiny(K=40))
+    a = oracle_arrays(make_batch(wl, seed=10, table="identity"))
+    b = oracle_arrays(make_batch(wl, seed=10, table="shuffled"))
+    # same values, different physical placement: re-place b's blocks where a has them
+    assert not (a["block_table"] == b["block_table"]).all()
+    for key in ("kI_cache", "k_cache", "v_cache"):
+        moved = np.empty_like(b[key])
+        for s in range(3):
+            nb = (a["seq_lens"][s] + 63) // 64
+            moved[b["block_table"][s, :nb]] = a[key][a["block_table"][s, :nb]]
+        b[key] = moved
+    ra, rb = run_oracle(a), run_oracle(b)
+    assert (ra["indices"] == rb["indices"]).all()
+    assert all((x == y).all() for x, y in zip(ra["scores"], rb["scores"]))
+    assert (ra["out"] == rb["out"]).all()
+
+
+def test_decode_step_row_alone_equals_row_in_batch_and_prefill_rows():
+    wl = small_workload("t", lengths=[500, 260, 900], **_tiny(K=32, D_qk=96, latent=True))
+    batch = make_batch(wl, seed=11)
+    full = run_oracle(oracle_arrays(batch))
+    one = run_oracle(oracle_arrays(batch, rows=[2]))
+    assert (one["indices"][0] == full["indices"][2]).all()
+    assert (one["out"][0] == full["out"][2]).all()
+    # a chunked-prefill row at position p sees exactly positions 0..p
+    pre = small_workload("p", lengths=[400], prefill_rows=16, **_tiny(K=32))
+    arr = oracle_arrays(make_batch(pre, seed=12))
+    res = run_oracle(arr)
+    assert arr["row_pos"].tolist() == list(range(384, 400))
+    for i in range(16):
+        assert len(res["scores"][i]) == arr["row_pos"][i] + 1
+        assert res["indices"][i].max() <= arr["row_pos"][i]

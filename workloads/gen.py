@@ -1,0 +1,207 @@
+"""Seeded generation of one batch of inputs, on any torch device.
+
+Two generators per batch: a CPU one for the structure (sequence lengths,
+block-table permutation), so every device sees the same structure for a seed,
+and one on the target device for the bulk values.  Large tensors are filled
+chunk by chunk to bound temporary memory.
+"""
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+from .configs import Workload
+
+BLOCK = 64
+_CHUNK = 1 << 26          # elements per generation chunk
+
+
+@dataclass
+class Batch:
+    wl: Workload
+    lengths: list            # host copy of seq_lens
+    row_seq_host: list       # host copy of each row's sequence
+    row_pos_host: list       # host copy of each row's position
+    max_blocks: int
+    num_blocks: int
+    seq_lens: torch.Tensor   # int32 [B]
+    block_table: torch.Tensor  # int32 [B, max_blocks], -1 past each sequence's blocks
+    row_seq: Optional[torch.Tensor]  # int32 [rows] or None (decode)
+    row_pos: Optional[torch.Tensor]
+    qI: torch.Tensor         # uint8 E4M3 [rows, H_I, D_I]
+    w: torch.Tensor          # float32 [rows, H_I]
+    kI: torch.Tensor         # uint8 E4M3 [num_blocks, 64, D_I]
+    q: torch.Tensor          # bfloat16 [rows, H_q, D_qk]
+    kv: torch.Tensor         # bfloat16 [num_blocks, 64, D_qk]
+    v: Optional[torch.Tensor] = None   # bfloat16 [num_blocks, 64, D_v] (separate V)
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def rows(self) -> int:
+        return self.qI.shape[0]
+
+
+def _fill(out: torch.Tensor, draw):
+    flat = out.view(-1)
+    n = flat.numel()
+    for i in range(0, n, _CHUNK):
+        j = min(n, i + _CHUNK)
+        flat[i:j] = draw(j - i)
+    return out
+
+
+def _fp8_codes(shape, mode, gen, device):
+    out = torch.empty(shape, dtype=torch.uint8, device=device)
+    if mode == "int":
+        def draw(n):
+            x = torch.randint(-8, 9, (n,), generator=gen, device=device, dtype=torch.int32)
+            return x.to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)
+    else:
+        def draw(n):
+            x = torch.randn(n, generator=gen, device=device, dtype=torch.float32)
+            return x.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    return _fill(out, draw)
+
+
+def _bf16_normal(shape, gen, device):
+    out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    return _fill(out, lambda n: torch.randn(n, generator=gen, device=device,
+                                            dtype=torch.float32).to(torch.bfloat16))
+
+
+def _weights(shape, mode, gen, device):
+    if mode == "int":
+        return torch.randint(0, 4, shape, generator=gen, device=device,
+                             dtype=torch.int32).to(torch.float32)
+    return torch.rand(shape, generator=gen, device=device, dtype=torch.float32) * 3.0
+
+
+def make_batch(wl: Workload, device="cpu", seed=None, mode=None, table=None,
+               lengths=None) -> Batch:
+    """Draw one batch for workload ``wl``.
+
+    ``seed``, ``mode`` ("int"/"gauss") and ``table`` ("identity"/"shuffled")
+    override the workload's own.  Integer mode: indexer q and k are integers
+    in [-8, 8] (exact in E4M3) and head weights integers in [0, 3].  Gaussian
+    mode: q and k are N(0, 1) rounded to E4M3, weights uniform on [0, 3).
+    Attention q and the KV rows are N(0, 1) rounded to bf16 in both modes.
+    """
+    seed = wl.seed if seed is None else seed
+    mode = wl.mode if mode is None else mode
+    table = wl.table if table is None else table
+    device = torch.device(device)
+    gs = torch.Generator(device="cpu")
+    gs.manual_seed(seed)
+    gd = torch.Generator(device=device)
+    gd.manual_seed(seed * 7919 + 17)
+
+    if lengths is not None:
+        lens = [int(x) for x in lengths]
+    elif wl.lengths:
+        lens = list(wl.lengths)
+    elif wl.context:
+        lens = [wl.context] * wl.batch
+    else:
+        lo, hi = wl.ragged
+        lens = torch.randint(lo, hi + 1, (wl.batch,), generator=gs).tolist()
+    B = len(lens)
+    nblk = [(L + BLOCK - 1) // BLOCK for L in lens]
+    max_blocks = max(nblk)
+    num_blocks = sum(nblk)
+    if table == "shuffled":
+        phys = torch.randperm(num_blocks, generator=gs)
+    else:
+        phys = torch.arange(num_blocks)
+    bt = torch.full((B, max_blocks), -1, dtype=torch.int32)
+    off = 0
+    for b in range(B):
+        bt[b, :nblk[b]] = phys[off:off + nblk[b]].to(torch.int32)
+        off += nblk[b]
+
+    if wl.prefill_rows:
+        # one chunk of new tokens at the end of sequence 0
+        R = wl.prefill_rows
+        first = lens[0] - R
+        row_seq_h = [0] * R
+        row_pos_h = list(range(first, lens[0]))
+        row_seq = torch.tensor(row_seq_h, dtype=torch.int32, device=device)
+        row_pos = torch.tensor(row_pos_h, dtype=torch.int32, device=device)
+    else:
+        R = B
+        row_seq_h = list(range(B))
+        row_pos_h = [L - 1 for L in lens]
+        row_seq = row_pos = None
+
+    qI = _fp8_codes((R, wl.H_I, wl.D_I), mode, gd, device)
+    w = _weights((R, wl.H_I), mode, gd, device)
+    kI = _fp8_codes((num_blocks, BLOCK, wl.D_I), mode, gd, device)
+    q = _bf16_normal((R, wl.H_q, wl.D_qk), gd, device)
+    kv = _bf16_normal((num_blocks, BLOCK, wl.D_qk), gd, device)
+    v = None if wl.latent else _bf16_normal((num_blocks, BLOCK, wl.D_v), gd, device)
+
+    return Batch(wl=wl, lengths=lens, row_seq_host=row_seq_h, row_pos_host=row_pos_h,
+                 max_blocks=max_blocks, num_blocks=num_blocks,
+                 seq_lens=torch.tensor(lens, dtype=torch.int32, device=device),
+                 block_table=bt.to(device), row_seq=row_seq, row_pos=row_pos,
+                 qI=qI, w=w, kI=kI, q=q, kv=kv, v=v)
+
+
+def row_positions(batch: Batch):
+    """(sequence, position) of every row, as recorded when the batch was drawn."""
+    return list(zip(batch.row_seq_host, batch.row_pos_host))
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def oracle_arrays(batch: Batch, rows=None) -> dict:
+    """The batch as plain numpy arrays of raw storage bits.
+
+    The per-row arrays hold the chosen ``rows`` (default: all) in order, with
+    their sequences and positions in ``row_seq`` / ``row_pos`` and their ids
+    in the batch in ``row_ids``.  With ``rows`` given, only the cache blocks
+    those rows' sequences own are copied to the host and the block table is
+    renumbered to the copied blocks (whole blocks move; no value is touched).
+    """
+    wl = batch.wl
+    if rows is None:
+        rows = np.arange(batch.rows)
+        bt = _np(batch.block_table)
+        kI, kv = _np(batch.kI), _np(batch.kv.view(torch.int16)).view(np.uint16)
+        v = None if batch.v is None else _np(batch.v.view(torch.int16)).view(np.uint16)
+        seqs = None
+    else:
+        rows = np.asarray(rows, dtype=np.int64)
+        seqs = sorted({batch.row_seq_host[r] for r in rows})
+        bt_full = batch.block_table.cpu()
+        ids = []
+        for b in seqs:
+            nb = (batch.lengths[b] + BLOCK - 1) // BLOCK
+            ids.append(bt_full[b, :nb].to(torch.int64))
+        ids_t = torch.cat(ids)
+        idx_dev = ids_t.to(batch.kI.device)
+        kI = _np(batch.kI.index_select(0, idx_dev))
+        kv = _np(batch.kv.index_select(0, idx_dev).view(torch.int16)).view(np.uint16)
+        v = None if batch.v is None else \
+            _np(batch.v.index_select(0, idx_dev).view(torch.int16)).view(np.uint16)
+        bt = np.full(_np(bt_full).shape, -1, dtype=np.int32)
+        off = 0
+        for b in seqs:
+            nb = (batch.lengths[b] + BLOCK - 1) // BLOCK
+            bt[b, :nb] = np.arange(off, off + nb, dtype=np.int32)
+            off += nb
+    sel = torch.as_tensor(rows, dtype=torch.int64).to(batch.qI.device)
+    return {
+        "qI": _np(batch.qI.index_select(0, sel)),
+        "w": _np(batch.w.index_select(0, sel)),
+        "q": _np(batch.q.index_select(0, sel).view(torch.int16)).view(np.uint16),
+        "kI_cache": kI, "k_cache": kv, "v_cache": v,
+        "block_table": bt, "seq_lens": np.asarray(batch.lengths, np.int32),
+        "row_seq": np.asarray(batch.row_seq_host, np.int64)[rows],
+        "row_pos": np.asarray(batch.row_pos_host, np.int64)[rows],
+        "row_ids": np.asarray(rows, np.int64),
+        "K": wl.K, "scale": wl.scale, "D_v": wl.D_v,
+    }
