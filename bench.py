@@ -1,0 +1,236 @@
+"""Benchmark of the fused indexer -> Top-K -> sparse-attention decode step.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line.  A step is one dsa_decode_step over one batch of the
+workload (default: long-context decode, batch 4 x 131072, FP8 indexer
+64 x 128, Top-2048, 128-head MQA over a 576/512 bf16 latent).  Inputs are
+resident in HBM before timing starts; R independent input sets rotate so the
+bytes touched per rotation exceed the 256 MB Infinity Cache several times.
+
+value      decode tokens/s = rows * steps / timed seconds (whole GPU)
+roofline   the dominant kernel (the indexer scan): algorithmic bytes per
+           launch / its average launch time, measured here with HIP events
+           on the launch stream, against the 8 TB/s HBM peak
+cpu_baseline  the oracle timed on the host on a bounded sample of rows
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--mode", default=None, help="int or gauss (default: the workload's)")
+    ap.add_argument("--rotate", type=int, default=0, help="input sets (0: auto)")
+    ap.add_argument("--graph", type=int, default=1, help="replay captured HIP graphs")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--table", default=None)
+    return ap.parse_args()
+
+
+def step_bytes(wl, lengths):
+    """Algorithmic HBM bytes of one step: every index key of every history,
+    the gathered KV rows, the queries, weights, block-table entries and the
+    output (no score matrix: the fused step need not materialise one)."""
+    total = 0
+    row_kv = 2 * (wl.D_qk if wl.latent else wl.D_qk + wl.D_v)
+    for L in lengths:
+        n = min(wl.K, L)
+        total += (wl.D_I * L + row_kv * n + wl.H_I * wl.D_I + 4 * wl.H_I
+                  + 2 * wl.H_q * wl.D_qk + 2 * wl.H_q * wl.D_v + 4 * ((L + 63) // 64))
+    return total
+
+
+def indexer_bytes(wl, lengths):
+    """Algorithmic bytes of one indexer-scan launch: index keys, queries,
+    weights, block-table entries, and the float32 scores it writes."""
+    return sum(wl.D_I * L + wl.H_I * wl.D_I + 4 * wl.H_I + 4 * ((L + 63) // 64) + 4 * L
+               for L in lengths)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(decode shards by request; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from indexer_top_sparse_score_amd import binding as B
+    from workloads import BENCH_WORKLOAD, CONFIGS, make_batch, row_positions
+
+    B.load()
+    name = args.workload or BENCH_WORKLOAD
+    wl = CONFIGS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    first = make_batch(wl, device=dev, seed=wl.seed, mode=args.mode, table=args.table)
+    lengths = [first.lengths[b] if not wl.prefill_rows else p + 1
+               for b, p in row_positions(first)]
+    rows = first.rows
+    sb = step_bytes(wl, lengths)
+    rotate = args.rotate or max(1, min(16, -(-4 * MALL_BYTES // sb)))
+    sets = [first] + [make_batch(wl, device=dev, seed=wl.seed + 1000 * i, mode=args.mode,
+                                 table=args.table) for i in range(1, rotate)]
+
+    stream = torch.cuda.Stream()
+    probs, outs, wss = [], [], []
+    for s in sets:
+        p = B.problem_for_batch(s)
+        probs.append(p)
+        outs.append((torch.empty((rows, wl.H_q, wl.D_v), dtype=torch.bfloat16, device=dev),
+                     torch.empty((rows, wl.H_q), dtype=torch.float32, device=dev)))
+    ws = B.workspace(probs[0], B.DSA_OP_DECODE_STEP, device=dev)
+
+    def step(i):
+        s, p = sets[i % rotate], probs[i % rotate]
+        v = s.v if s.v is not None else s.kv
+        out, lse = outs[i % rotate]
+        B.dsa_decode_step(p, s.qI, s.w, s.kI, s.q, s.kv, v, out, ws, lse=lse, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+    torch.cuda.synchronize()
+
+    launch = "stream"
+    graphs = []
+    if args.graph:
+        try:
+            for i in range(rotate):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    step(i)
+                graphs.append(g)
+            with torch.cuda.stream(stream):
+                for i in range(rotate):
+                    graphs[i].replay()
+            torch.cuda.synchronize()
+            launch = "graph"
+        except Exception as e:  # capture unsupported: fall back to stream launches
+            print(f"bench.py: graph capture failed ({e}); timing stream launches",
+                  file=sys.stderr)
+            graphs = []
+    assert B.device_errors(ws) == 0
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for i in range(args.steps):
+            if graphs:
+                graphs[i % rotate].replay()
+            else:
+                step(i)
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = ev0.elapsed_time(ev1) / 1e3
+    assert B.device_errors(ws) == 0
+    ms_per_step = 1e3 * gpu_s / args.steps
+    value = rows * args.steps / gpu_s
+
+    # ---- dominant kernel: the indexer scan, timed alone on the same stream
+    ld = 64 * first.max_blocks
+    scores = torch.empty((rows, ld), dtype=torch.float32, device=dev)
+    ws_i = B.workspace(probs[0], B.DSA_OP_INDEXER_SCORES, device=dev)
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            s = sets[i % rotate]
+            B.dsa_indexer_scores(probs[i % rotate], s.qI, s.w, s.kI, scores, ws_i, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            s = sets[i % rotate]
+            B.dsa_indexer_scores(probs[i % rotate], s.qI, s.w, s.kI, scores, ws_i, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    idx_us = 1e3 * e0.elapsed_time(e1) / args.steps
+    ib = indexer_bytes(wl, lengths)
+    achieved = ib / (idx_us * 1e-6) / 1e9
+
+    result = {
+        "metric": "sparse-attn decode tokens/s at 128k ctx, K=2048; % of HBM peak (GB/s)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3+bf16 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {
+            "workload": name, "rows": rows, "context": max(lengths), "K": wl.K,
+            "indexer": f"{wl.H_I}x{wl.D_I} e4m3", "attention": f"{wl.H_q} heads {wl.D_qk}/{wl.D_v} bf16"
+            + (" latent" if wl.latent else ""), "mode": args.mode or wl.mode,
+            "table": args.table or wl.table, "rotation_sets": rotate, "launch": launch,
+        },
+        "step_gbs": round(sb / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(sb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_bytes": sb,
+        "roofline": {
+            "bound": "hbm", "kernel": "indexer_scan_kernel", "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None, "bytes_per_launch": ib, "avg_launch_us": round(idx_us, 3),
+        },
+        "wall_s": round(wall, 4),
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(first, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(batch, budget_s):
+    """The oracle, as it stands, on whole rows of the first input set until
+    about budget_s seconds of host time are spent (at least one row)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from workloads import oracle_arrays
+
+    t_copy = time.perf_counter()
+    arr = oracle_arrays(batch, rows=list(range(batch.rows)))
+    t_copy = time.perf_counter() - t_copy
+    done = 0
+    t0 = time.perf_counter()
+    while done < batch.rows and (done == 0 or time.perf_counter() - t0 < budget_s):
+        one = {k: (v[done:done + 1] if k in ("qI", "w", "q", "row_seq", "row_pos") else v)
+               for k, v in arr.items()}
+        oracle.decode_step(qI=one["qI"], w=one["w"], kI_cache=one["kI_cache"], q=one["q"],
+                           k_cache=one["k_cache"], v_cache=one["v_cache"],
+                           block_table=one["block_table"], seq_lens=one["seq_lens"],
+                           K=one["K"], scale=one["scale"], D_v=one["D_v"],
+                           row_seq=one["row_seq"], row_pos=one["row_pos"], keep_scores=False)
+        done += 1
+    el = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(done / el, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {batch.rows} rows of {batch.wl.name} (full history each), "
+                      f"{el:.1f} s; host copy {t_copy:.1f} s not timed",
+            "numpy_threads": threads, "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) indexer -> Top-K -> sparse-attention
+ * library (libdsa.so).
+ *
+ * The method (Baidu AI Cloud, "Day0 Inference Support and Performance
+ * Optimization for New Architecture LLMs", section 2.2): a lightweight
+ * indexer scores each query row against every historical position, the
+ * per-head scores are aggregated with per-head weights, the Top-K positions
+ * are kept, and the sparse attention core reads only those KV rows.  The
+ * indexer reads the paged K cache directly (section 4.1); the attention core
+ * gathers the selected rows of the main KV cache from the indexer's position
+ * list (section 4.2); the fused call takes the FP8 indexer query, the index
+ * keys and the head weights (section 4.3, "idx = fused_topk(q8, k, g)").
+ * One KV latent row is shared by every query head ("SPLASH: Switching
+ * Parallel Layouts of Attention with Seamless Handoff for LLM Serving",
+ * section 2).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every tensor argument is a DEVICE pointer owned by the caller.  The
+ *   library never allocates, frees or retains memory, never synchronises
+ *   and never reads device memory from the host.  Calls enqueue kernels on
+ *   `stream` (a hipStream_t; NULL = the null stream) and return at once;
+ *   they are capturable into a hipGraph.
+ * - Validation is synchronous and happens before anything is enqueued: a
+ *   negative dsa_status comes back and nothing runs.  A failed kernel launch
+ *   returns DSA_ERR_HIP.  Faults during execution surface on the caller's
+ *   next synchronisation.  Nothing is printed and no exception crosses the
+ *   ABI.
+ * - The library keeps no state; calls are reentrant.  Calls that overlap in
+ *   time need separate workspaces.
+ * - Row r of the problem is a query at absolute position p_r of sequence
+ *   b_r.  Its history is positions 0 .. p_r inclusive (L_r = p_r + 1): the
+ *   current token's own index key and KV row are already in the caches.
+ *   Decode passes row_seq = row_pos = NULL (row r is sequence r at position
+ *   seq_lens[r] - 1); chunked prefill passes both arrays.
+ * - Paging: position s of sequence b lives in physical block
+ *   block_table[b * max_blocks + s / 64], row s % 64.  The index-key cache and
+ *   the KV cache share the block table.
+ * - Device-side checks: a row whose sequence or position is out of range, a
+ *   block id outside [0, num_blocks) or an attention index outside [-1, p_r]
+ *   is never dereferenced.  The row, page or index is treated as absent and a
+ *   DSA_DEVERR_* bit is OR-ed into the 32-bit error word at byte 0 of the
+ *   workspace.  The word is sticky: the caller zeroes the workspace once after
+ *   allocating it and may read the word back after synchronising.
+ * - Alignment: qI, q, out and cache bases 16 bytes; cache strides multiples
+ *   of 16 bytes; scores, w, lse, indices, counts 4 bytes; workspace 256.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define DSA_API __attribute__((visibility("default")))
+#else
+#define DSA_API
+#endif
+
+#define DSA_ABI_VERSION 1
+#define DSA_BLOCK_SIZE 64
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID = -1,     /* a NULL, misaligned, negative or inconsistent argument */
+  DSA_ERR_UNSUPPORTED = -2, /* valid, but a shape this build does not implement      */
+  DSA_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than dsa_workspace_size()    */
+  DSA_ERR_HIP = -4          /* a kernel launch failed                                 */
+} dsa_status;
+
+/* bits of the sticky device error word at byte 0 of the workspace */
+#define DSA_DEVERR_ROW 1u   /* row's sequence / position out of range: row treated as empty */
+#define DSA_DEVERR_BLOCK 2u /* block id outside [0, num_blocks): page treated as absent      */
+#define DSA_DEVERR_INDEX 4u /* attention index outside [-1, p_r]: index skipped              */
+
+/* A paged cache: [num_blocks][64 rows][row bytes], rows at any stride. */
+typedef struct {
+  const void* base;     /* device address of physical block 0, row 0            */
+  int64_t block_stride; /* bytes from one physical block to the next             */
+  int64_t row_stride;   /* bytes from one row (token) to the next inside a block */
+  int64_t num_blocks;   /* number of physical blocks addressable from base       */
+} dsa_paged;
+
+/* Shapes and the row -> (sequence, position) map, shared by every call. */
+typedef struct {
+  int32_t num_seqs;           /* sequences in the batch (>= 1)                         */
+  int32_t num_rows;           /* query rows (0 = nothing to do)                         */
+  const int32_t* seq_lens;    /* [num_seqs] tokens in each sequence's caches            */
+  const int32_t* block_table; /* [num_seqs][max_blocks] physical block ids              */
+  int32_t max_blocks;         /* columns of block_table (>= 1)                          */
+  int32_t block_size;         /* tokens per block; must be 64                           */
+  const int32_t* row_seq;     /* [num_rows] sequence of each row, or NULL (row r -> r)  */
+  const int32_t* row_pos;     /* [num_rows] position p_r, or NULL (seq_lens[b] - 1)     */
+  int32_t H_I;                /* indexer heads, 1..64                                   */
+  int32_t D_I;                /* indexer head dim, 64 or 128                            */
+  int32_t H_q;                /* attention query heads, 1..128                          */
+  int32_t D_qk;               /* attention q/k dim: 64 or 576                           */
+  int32_t D_v;                /* attention v / output dim: 64 (with D_qk 64) or 512     */
+  int32_t K;                  /* positions kept per row, >= 1                           */
+  float scale;                /* attention logit scale, finite (e.g. 1/sqrt(D_qk))      */
+} dsa_problem;
+
+/* which call dsa_workspace_size() sizes */
+enum {
+  DSA_OP_INDEXER_SCORES = 0,
+  DSA_OP_TOPK = 1,
+  DSA_OP_SPARSE_ATTN = 2,
+  DSA_OP_DECODE_STEP = 3
+};
+
+/* Bytes of workspace `op` needs for problem `p` (a multiple of 256, at least
+ * 256), or 0 when the problem is invalid or unsupported.  Host-only. */
+DSA_API size_t dsa_workspace_size(const dsa_problem* p, int op);
+
+/*
+ * Index scores (Day0 article, section 2.2, first two steps):
+ *   scores[r * ld_scores + s] = sum_h w[r, h] * max(0, sum_d qI[r, h, d] * kI[s, d])
+ * for s = 0 .. p_r, in float32; a zero score is stored as +0.
+ *   qI      E4M3 (OCP FN) codes, [num_rows][H_I][D_I], row-major
+ *   w       float32 head weights, [num_rows][H_I]
+ *   kI      paged index-key cache, one D_I-byte E4M3 row per position,
+ *           shared by all indexer heads
+ *   scores  float32 [num_rows][ld_scores]; ld_scores >= 64 * max_blocks.
+ *           Entries s > p_r are neither read nor written.
+ * FP8 products are exact and accumulate in float32, so integer-valued inputs
+ * whose partial sums stay below 2**24 give exact scores in any order.
+ */
+DSA_API int dsa_indexer_scores(const dsa_problem* p, const uint8_t* qI, const float* w, dsa_paged kI,
+                       float* scores, int64_t ld_scores, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/*
+ * Top-K (Day0 article, section 2.2, third step): for each row keep the
+ * min(K, L_r) positions with the largest score among scores[r, 0 .. p_r];
+ * equal scores go to the lower position; -0 equals +0; NaN ranks last.
+ *   indices  int32 [num_rows][K]: the kept positions in ascending order,
+ *            then -1 up to K
+ *   counts   int32 [num_rows] = min(K, L_r), or NULL
+ */
+DSA_API int dsa_topk(const dsa_problem* p, const float* scores, int64_t ld_scores, int32_t* indices,
+             int32_t* counts, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Sparse MQA (Day0 article, sections 2.2 and 4.2): for each row and query
+ * head h, softmax attention over the KV rows named in indices[r, 0 .. K-1]
+ * (entries of -1 are skipped):
+ *   logit_j = scale * sum_d q[r, h, d] * k_j[d]
+ *   out[r, h, :] = sum_j exp(logit_j - m) v_j / sum_j exp(logit_j - m)
+ *   lse[r, h]    = m + ln(sum_j exp(logit_j - m))       (natural log)
+ * with m the largest logit.  A row with no valid index gives out = 0 and
+ * lse = -inf.
+ *   q        bf16 [num_rows][H_q][D_qk]
+ *   k        paged cache of bf16 rows of D_qk elements
+ *   v        paged cache of bf16 rows whose first D_v elements are V; pass
+ *            the k descriptor again for the latent layout (V = the leading
+ *            D_v columns of each K row)
+ *   indices  int32 [num_rows][K]
+ *   out      bf16 [num_rows][H_q][D_v]; lse float32 [num_rows][H_q] or NULL
+ * Products are bf16 x bf16 with float32 accumulation; softmax in float32.
+ */
+DSA_API int dsa_sparse_attn(const dsa_problem* p, const uint16_t* q, dsa_paged k, dsa_paged v,
+                    const int32_t* indices, uint16_t* out, float* lse, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/*
+ * The whole step, fused (Day0 article, sections 4.1-4.3): index scores,
+ * Top-K and sparse MQA for every row, with the same results as calling the
+ * three entry points above in turn.  Scores stay in the workspace.
+ *   indices_out  int32 [num_rows][K] copy of the selection, or NULL
+ *   counts_out   int32 [num_rows], or NULL
+ * Other arguments as above.
+ */
+DSA_API int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa_paged kI,
+                    const uint16_t* q, dsa_paged k, dsa_paged v, uint16_t* out, float* lse,
+                    int32_t* indices_out, int32_t* counts_out, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* Static text for a dsa_status value ("unknown status" otherwise). */
+DSA_API const char* dsa_status_string(int status);
+
+/* DSA_ABI_VERSION of the loaded library. */
+DSA_API int dsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

@@ -1,0 +1,323 @@
+// C-ABI front end of libdsa.so: argument validation, workspace sizing and
+// the launch sequence of each entry point.  Validation touches no HIP API,
+// so every error code can be produced on a machine without a GPU.
+
+#include <cmath>
+#include <cstdint>
+
+#include "dsa_common.h"
+
+namespace dsa {
+namespace {
+
+constexpr size_t kHeader = 256;                    // error word + reserved
+constexpr size_t kScoresBudget = size_t(512) << 20;  // fused step: scores kept per pass
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+int check_rows(const dsa_problem* p) {
+  if (!p) return DSA_ERR_INVALID;
+  if (p->num_rows < 0 || p->num_seqs < 1 || p->max_blocks < 1) return DSA_ERR_INVALID;
+  if (!p->seq_lens || !p->block_table) return DSA_ERR_INVALID;
+  if (!aligned(p->seq_lens, 4) || !aligned(p->block_table, 4)) return DSA_ERR_INVALID;
+  if ((p->row_seq && !aligned(p->row_seq, 4)) || (p->row_pos && !aligned(p->row_pos, 4)))
+    return DSA_ERR_INVALID;
+  if (p->block_size != DSA_BLOCK_SIZE) return DSA_ERR_UNSUPPORTED;
+  if (p->max_blocks > (1 << 24)) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
+}
+
+int check_indexer_shape(const dsa_problem* p) {
+  if (p->H_I < 1 || p->D_I < 1) return DSA_ERR_INVALID;
+  if (p->H_I > 64) return DSA_ERR_UNSUPPORTED;
+  if (p->D_I != 64 && p->D_I != 128) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
+}
+
+int check_attn_shape(const dsa_problem* p) {
+  if (p->H_q < 1 || p->D_qk < 1 || p->D_v < 1 || p->K < 1) return DSA_ERR_INVALID;
+  if (!std::isfinite(p->scale)) return DSA_ERR_INVALID;
+  if (p->H_q > 128) return DSA_ERR_UNSUPPORTED;
+  const bool small = p->D_qk == 64 && p->D_v == 64;
+  const bool mla = p->D_qk == 576 && p->D_v == 512;
+  if (!small && !mla) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
+}
+
+int check_paged(const dsa_paged& c, int64_t row_bytes) {
+  if (!c.base || !aligned(c.base, 16)) return DSA_ERR_INVALID;
+  if (c.num_blocks < 1 || c.block_stride <= 0 || c.row_stride <= 0) return DSA_ERR_INVALID;
+  if (c.block_stride % 16 || c.row_stride % 16) return DSA_ERR_INVALID;
+  if (c.row_stride < row_bytes) return DSA_ERR_INVALID;
+  return DSA_OK;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return DSA_ERR_INVALID;
+  return DSA_OK;
+}
+
+RowMap row_map(const dsa_problem* p) {
+  RowMap m;
+  m.seq_lens = p->seq_lens;
+  m.block_table = p->block_table;
+  m.row_seq = p->row_seq;
+  m.row_pos = p->row_pos;
+  m.num_seqs = p->num_seqs;
+  m.max_blocks = p->max_blocks;
+  return m;
+}
+
+int64_t max_len(const dsa_problem* p) { return (int64_t)p->max_blocks * DSA_BLOCK_SIZE; }
+
+int rows_per_pass(const dsa_problem* p) {
+  const size_t per_row = (size_t)max_len(p) * sizeof(float);
+  size_t rp = kScoresBudget / per_row;
+  if (rp < 1) rp = 1;
+  if (rp > (size_t)p->num_rows) rp = (size_t)p->num_rows;
+  return (int)rp;
+}
+
+bool is_latent(const dsa_paged& k, const dsa_paged& v) {
+  return k.base == v.base && k.block_stride == v.block_stride && k.row_stride == v.row_stride;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+struct DecodeLayout {
+  int rp;
+  size_t idx_off, scores_off, part_off, total;
+};
+
+DecodeLayout decode_layout(const dsa_problem* p) {
+  DecodeLayout d;
+  d.rp = rows_per_pass(p);
+  const int nc = attn_chunks(d.rp, p->H_q, p->K);
+  d.idx_off = kHeader;
+  d.scores_off = d.idx_off + round256((size_t)d.rp * p->K * sizeof(int32_t));
+  d.part_off = d.scores_off + round256((size_t)d.rp * max_len(p) * sizeof(float));
+  d.total = d.part_off + round256(attn_partial_bytes(d.rp, p->H_q, p->D_v, nc));
+  return d;
+}
+
+}  // namespace
+}  // namespace dsa
+
+using namespace dsa;
+
+extern "C" {
+
+int dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_INVALID: return "invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "unsupported shape";
+    case DSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case DSA_ERR_HIP: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t dsa_workspace_size(const dsa_problem* p, int op) {
+  if (check_rows(p) != DSA_OK) return 0;
+  switch (op) {
+    case DSA_OP_INDEXER_SCORES:
+      return check_indexer_shape(p) == DSA_OK ? kHeader : 0;
+    case DSA_OP_TOPK:
+      return p->K >= 1 ? kHeader : 0;
+    case DSA_OP_SPARSE_ATTN: {
+      if (check_attn_shape(p) != DSA_OK) return 0;
+      const int nc = attn_chunks(p->num_rows, p->H_q, p->K);
+      return kHeader + round256(attn_partial_bytes(p->num_rows, p->H_q, p->D_v, nc));
+    }
+    case DSA_OP_DECODE_STEP:
+      if (check_indexer_shape(p) != DSA_OK || check_attn_shape(p) != DSA_OK) return 0;
+      if (p->num_rows == 0) return kHeader;
+      return decode_layout(p).total;
+    default:
+      return 0;
+  }
+}
+
+int dsa_indexer_scores(const dsa_problem* p, const uint8_t* qI, const float* w, dsa_paged kI,
+                       float* scores, int64_t ld_scores, void* ws, size_t ws_bytes,
+                       void* stream) {
+  int st = check_rows(p);
+  if (st != DSA_OK) return st;
+  if ((st = check_indexer_shape(p)) != DSA_OK) return st;
+  if (!qI || !w || !scores) return DSA_ERR_INVALID;
+  if (!aligned(qI, 16) || !aligned(w, 4) || !aligned(scores, 4)) return DSA_ERR_INVALID;
+  if ((st = check_paged(kI, p->D_I)) != DSA_OK) return st;
+  if (ld_scores < max_len(p)) return DSA_ERR_INVALID;
+  if ((st = check_ws(ws, ws_bytes, kHeader)) != DSA_OK) return st;
+  if (p->num_rows == 0) return DSA_OK;
+  IndexerLaunch a;
+  a.rows = row_map(p);
+  a.qI = qI;
+  a.w = w;
+  a.kI = kI;
+  a.scores = scores;
+  a.ld = ld_scores;
+  a.err = static_cast<uint32_t*>(ws);
+  a.H_I = p->H_I;
+  a.D_I = p->D_I;
+  a.row_begin = 0;
+  a.num_rows = p->num_rows;
+  a.max_len = (int32_t)max_len(p);
+  return status_of(launch_indexer_scores(a, static_cast<hipStream_t>(stream)));
+}
+
+int dsa_topk(const dsa_problem* p, const float* scores, int64_t ld_scores, int32_t* indices,
+             int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_rows(p);
+  if (st != DSA_OK) return st;
+  if (p->K < 1) return DSA_ERR_INVALID;
+  if (!scores || !indices) return DSA_ERR_INVALID;
+  if (!aligned(scores, 4) || !aligned(indices, 4) || (counts && !aligned(counts, 4)))
+    return DSA_ERR_INVALID;
+  if (ld_scores < max_len(p)) return DSA_ERR_INVALID;
+  if ((st = check_ws(ws, ws_bytes, kHeader)) != DSA_OK) return st;
+  if (p->num_rows == 0) return DSA_OK;
+  TopkLaunch a;
+  a.rows = row_map(p);
+  a.scores = scores;
+  a.ld = ld_scores;
+  a.indices = indices;
+  a.counts = counts;
+  a.err = static_cast<uint32_t*>(ws);
+  a.K = p->K;
+  a.row_begin = 0;
+  a.num_rows = p->num_rows;
+  a.scores_row_offset = 0;
+  return status_of(launch_topk(a, static_cast<hipStream_t>(stream)));
+}
+
+static int check_attn_args(const dsa_problem* p, const uint16_t* q, const dsa_paged& k,
+                           const dsa_paged& v, uint16_t* out, float* lse) {
+  int st = check_attn_shape(p);
+  if (st != DSA_OK) return st;
+  if (!q || !out) return DSA_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(out, 16) || (lse && !aligned(lse, 4))) return DSA_ERR_INVALID;
+  if ((st = check_paged(k, 2 * (int64_t)p->D_qk)) != DSA_OK) return st;
+  if ((st = check_paged(v, 2 * (int64_t)p->D_v)) != DSA_OK) return st;
+  return DSA_OK;
+}
+
+static AttnLaunch attn_launch(const dsa_problem* p, const uint16_t* q, dsa_paged k, dsa_paged v,
+                              uint16_t* out, float* lse, uint32_t* err) {
+  AttnLaunch a;
+  a.rows = row_map(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.latent = is_latent(k, v);
+  a.indices = nullptr;
+  a.indices_row_offset = 0;
+  a.out = out;
+  a.lse = lse;
+  a.partial = nullptr;
+  a.err = err;
+  a.H_q = p->H_q;
+  a.D_qk = p->D_qk;
+  a.D_v = p->D_v;
+  a.K = p->K;
+  a.scale = p->scale;
+  a.row_begin = 0;
+  a.num_rows = p->num_rows;
+  a.n_chunks = 1;
+  return a;
+}
+
+int dsa_sparse_attn(const dsa_problem* p, const uint16_t* q, dsa_paged k, dsa_paged v,
+                    const int32_t* indices, uint16_t* out, float* lse, void* ws,
+                    size_t ws_bytes, void* stream) {
+  int st = check_rows(p);
+  if (st != DSA_OK) return st;
+  if ((st = check_attn_args(p, q, k, v, out, lse)) != DSA_OK) return st;
+  if (!indices || !aligned(indices, 4)) return DSA_ERR_INVALID;
+  if ((st = check_ws(ws, ws_bytes, dsa_workspace_size(p, DSA_OP_SPARSE_ATTN))) != DSA_OK)
+    return st;
+  if (p->num_rows == 0) return DSA_OK;
+  AttnLaunch a = attn_launch(p, q, k, v, out, lse, static_cast<uint32_t*>(ws));
+  a.indices = indices;
+  a.n_chunks = attn_chunks(p->num_rows, p->H_q, p->K);
+  a.partial = a.n_chunks > 1
+                  ? reinterpret_cast<float*>(static_cast<char*>(ws) + kHeader)
+                  : nullptr;
+  return status_of(launch_sparse_attn(a, static_cast<hipStream_t>(stream)));
+}
+
+int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa_paged kI,
+                    const uint16_t* q, dsa_paged k, dsa_paged v, uint16_t* out, float* lse,
+                    int32_t* indices_out, int32_t* counts_out, void* ws, size_t ws_bytes,
+                    void* stream) {
+  int st = check_rows(p);
+  if (st != DSA_OK) return st;
+  if ((st = check_indexer_shape(p)) != DSA_OK) return st;
+  if ((st = check_attn_args(p, q, k, v, out, lse)) != DSA_OK) return st;
+  if (!qI || !w || !aligned(qI, 16) || !aligned(w, 4)) return DSA_ERR_INVALID;
+  if ((st = check_paged(kI, p->D_I)) != DSA_OK) return st;
+  if ((indices_out && !aligned(indices_out, 4)) || (counts_out && !aligned(counts_out, 4)))
+    return DSA_ERR_INVALID;
+  if ((st = check_ws(ws, ws_bytes, dsa_workspace_size(p, DSA_OP_DECODE_STEP))) != DSA_OK)
+    return st;
+  if (p->num_rows == 0) return DSA_OK;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const DecodeLayout d = decode_layout(p);
+  char* base = static_cast<char*>(ws);
+  uint32_t* err = reinterpret_cast<uint32_t*>(base);
+  float* scores = reinterpret_cast<float*>(base + d.scores_off);
+  const int64_t ld = max_len(p);
+
+  for (int row0 = 0; row0 < p->num_rows; row0 += d.rp) {
+    const int nr = p->num_rows - row0 < d.rp ? p->num_rows - row0 : d.rp;
+    int32_t* idx = indices_out ? indices_out + (int64_t)row0 * p->K
+                               : reinterpret_cast<int32_t*>(base + d.idx_off);
+
+    IndexerLaunch ia;
+    ia.rows = row_map(p);
+    ia.qI = qI;
+    ia.w = w;
+    ia.kI = kI;
+    ia.scores = scores;
+    ia.ld = ld;
+    ia.err = err;
+    ia.H_I = p->H_I;
+    ia.D_I = p->D_I;
+    ia.row_begin = row0;
+    ia.num_rows = nr;
+    ia.max_len = (int32_t)ld;
+    if ((st = status_of(launch_indexer_scores(ia, s))) != DSA_OK) return st;
+
+    TopkLaunch ta;
+    ta.rows = row_map(p);
+    ta.scores = scores;
+    ta.ld = ld;
+    ta.indices = idx;
+    ta.counts = counts_out ? counts_out + row0 : nullptr;
+    ta.err = err;
+    ta.K = p->K;
+    ta.row_begin = row0;
+    ta.num_rows = nr;
+    ta.scores_row_offset = 0;
+    if ((st = status_of(launch_topk(ta, s))) != DSA_OK) return st;
+
+    AttnLaunch aa = attn_launch(p, q, k, v, out, lse, err);
+    aa.indices = idx;
+    aa.indices_row_offset = 0;
+    aa.row_begin = row0;
+    aa.num_rows = nr;
+    aa.n_chunks = attn_chunks(d.rp, p->H_q, p->K);  // the count the workspace was sized for
+    aa.partial = aa.n_chunks > 1 ? reinterpret_cast<float*>(base + d.part_off) : nullptr;
+    if ((st = status_of(launch_sparse_attn(aa, s))) != DSA_OK) return st;
+  }
+  return DSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI front end.
+// Nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dsa.h"
+
+namespace dsa {
+
+constexpr int kBlock = 64;  // tokens per cache page
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+
+// Row -> (sequence, position) map and the block table, as kernels see it.
+struct RowMap {
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  const int32_t* row_seq;  // NULL: row r -> sequence r
+  const int32_t* row_pos;  // NULL: position seq_lens[b] - 1
+  int32_t num_seqs;
+  int32_t max_blocks;
+};
+
+// Resolves row r.  Returns false (and leaves b, p unspecified) when the
+// sequence id or the position is out of range; the caller then treats the
+// row as having no history and reports DSA_DEVERR_ROW.
+__device__ __forceinline__ bool resolve_row(const RowMap& m, int r, int& b, int& p) {
+  b = m.row_seq ? m.row_seq[r] : r;
+  if (b < 0 || b >= m.num_seqs) return false;
+  const int len = m.seq_lens[b];
+  p = m.row_pos ? m.row_pos[r] : len - 1;
+  if (p < 0 || p >= len || p >= m.max_blocks * kBlock) return false;
+  return true;
+}
+
+__device__ __forceinline__ void report(uint32_t* err, uint32_t bit) {
+  if (err) atomicOr(err, bit);
+}
+
+// Order-preserving 32-bit key of a float32 score: larger score, larger key;
+// -0 and +0 share a key; NaN gets 0 and ranks below every number.
+__device__ __forceinline__ uint32_t score_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  const uint32_t mag = u & 0x7FFFFFFFu;
+  if (mag == 0) u = 0;
+  uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return mag > 0x7F800000u ? 0u : k;
+}
+
+// Number of set bits of `mask` below this lane (wave64).
+__device__ __forceinline__ int lane_prefix(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  Arguments are validated by
+// the front end before these run.
+
+struct IndexerLaunch {
+  RowMap rows;
+  const uint8_t* qI;
+  const float* w;
+  dsa_paged kI;
+  float* scores;
+  int64_t ld;
+  uint32_t* err;
+  int32_t H_I, D_I;
+  int32_t row_begin, num_rows;  // rows [row_begin, row_begin + num_rows)
+  int32_t max_len;              // upper bound of any row's history length
+};
+hipError_t launch_indexer_scores(const IndexerLaunch& a, hipStream_t s);
+
+struct TopkLaunch {
+  RowMap rows;
+  const float* scores;
+  int64_t ld;
+  int32_t* indices;  // [rows][K]
+  int32_t* counts;   // [rows] or NULL
+  uint32_t* err;
+  int32_t K;
+  int32_t row_begin, num_rows;
+  int64_t scores_row_offset;  // scores row of row_begin (row r reads scores[(r - row_begin + offset) * ld])
+};
+hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
+
+struct AttnLaunch {
+  RowMap rows;
+  const uint16_t* q;
+  dsa_paged k, v;
+  bool latent;  // v aliases k (same base and strides)
+  const int32_t* indices;
+  int64_t indices_row_offset;  // indices row of row_begin
+  uint16_t* out;
+  float* lse;
+  float* partial;  // workspace for split-key partials, or NULL when n_chunks == 1
+  uint32_t* err;
+  int32_t H_q, D_qk, D_v, K;
+  float scale;
+  int32_t row_begin, num_rows;
+  int32_t n_chunks;
+};
+int attn_chunks(int num_rows, int H_q, int K);
+size_t attn_partial_bytes(int num_rows, int H_q, int D_v, int n_chunks);
+hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s);
+
+}  // namespace dsa

@@ -1,0 +1,140 @@
+"""Plumbing shared by the GPU tests: run the HIP entry points on a seeded
+batch and compare with the oracle at the stated tolerances."""
+
+import math
+
+import numpy as np
+import torch
+
+from indexer_top_sparse_score_amd import binding as B
+
+# attention output tolerance (bf16 output, fp32 softmax): max and mean |error|
+ATT_MAX_ABS = 2e-2
+ATT_MEAN_ABS = 2e-3
+RECALL_MIN = 0.999
+U32 = 2.0 ** -24
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def kv_and_v(batch):
+    return batch.kv, (batch.v if batch.v is not None else batch.kv)
+
+
+def gpu_scores(batch):
+    """dsa_indexer_scores into a NaN-filled [rows, 64 * max_blocks] buffer."""
+    prob = B.problem_for_batch(batch)
+    ld = 64 * batch.max_blocks
+    scores = torch.full((batch.rows, ld), float("nan"), dtype=torch.float32, device="cuda")
+    ws = B.workspace(prob, B.DSA_OP_INDEXER_SCORES)
+    B.dsa_indexer_scores(prob, batch.qI, batch.w, batch.kI, scores, ws)
+    torch.cuda.synchronize()
+    assert B.device_errors(ws) == 0
+    return scores
+
+
+def gpu_topk(batch, scores):
+    prob = B.problem_for_batch(batch)
+    idx = torch.full((batch.rows, batch.wl.K), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((batch.rows,), -7, dtype=torch.int32, device="cuda")
+    ws = B.workspace(prob, B.DSA_OP_TOPK)
+    B.dsa_topk(prob, scores, idx, ws, counts=cnt)
+    torch.cuda.synchronize()
+    assert B.device_errors(ws) == 0
+    return idx, cnt
+
+
+def gpu_attn(batch, indices):
+    prob = B.problem_for_batch(batch)
+    wl = batch.wl
+    out = torch.full((batch.rows, wl.H_q, wl.D_v), float("nan"), dtype=torch.bfloat16,
+                     device="cuda")
+    lse = torch.full((batch.rows, wl.H_q), float("nan"), dtype=torch.float32, device="cuda")
+    ws = B.workspace(prob, B.DSA_OP_SPARSE_ATTN)
+    k, v = kv_and_v(batch)
+    B.dsa_sparse_attn(prob, batch.q, k, v, indices, out, ws, lse=lse)
+    torch.cuda.synchronize()
+    assert B.device_errors(ws) == 0
+    return out, lse
+
+
+def gpu_decode(batch, ws=None, stream=None):
+    prob = B.problem_for_batch(batch)
+    wl = batch.wl
+    out = torch.full((batch.rows, wl.H_q, wl.D_v), float("nan"), dtype=torch.bfloat16,
+                     device="cuda")
+    lse = torch.full((batch.rows, wl.H_q), float("nan"), dtype=torch.float32, device="cuda")
+    idx = torch.full((batch.rows, wl.K), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((batch.rows,), -7, dtype=torch.int32, device="cuda")
+    if ws is None:
+        ws = B.workspace(prob, B.DSA_OP_DECODE_STEP)
+    k, v = kv_and_v(batch)
+    B.dsa_decode_step(prob, batch.qI, batch.w, batch.kI, batch.q, k, v, out, ws, lse=lse,
+                      indices=idx, counts=cnt, stream=stream)
+    torch.cuda.synchronize()
+    assert B.device_errors(ws) == 0
+    return {"out": out, "lse": lse, "indices": idx, "counts": cnt}
+
+
+def np_(t):
+    return t.detach().cpu().numpy()
+
+
+def check_scores_exact(gpu_scores_t, orc, rows_pos):
+    g = np_(gpu_scores_t)
+    for i, (_, p) in enumerate(rows_pos):
+        want = orc["scores"][i]
+        got = g[i, :p + 1]
+        assert (got.view(np.uint32) == want.view(np.uint32)).all(), \
+            f"row {i}: {int((got != want).sum())} score mismatches"
+        assert np.isnan(g[i, p + 1:]).all(), f"row {i}: wrote past its history"
+
+
+def score_bound(arr, i, p):
+    """Forward-error bound of a float32 head-weighted, ReLU-gated FP8 dot
+    product against the correctly rounded value: 2 * gamma_n * sum_h |w_h| *
+    sum_d |q_hd k_sd| + 1 ulp, n = D_I + H_I + 1 (per-position array)."""
+    import oracle
+    b = arr["row_seq"][i]
+    q = np.abs(oracle.e4m3_to_f64(arr["qI"][i]))
+    k = np.abs(oracle.e4m3_to_f64(
+        oracle.gather_positions(arr["kI_cache"], arr["block_table"][b], np.arange(p + 1))))
+    mag = np.abs(arr["w"][i].astype(np.float64)) @ (q @ k.T)
+    n = q.shape[1] + q.shape[0] + 1
+    gamma = n * U32 / (1 - n * U32)
+    return 2 * gamma * mag
+
+
+def recall(gpu_idx, orc_idx, counts):
+    hit = tot = 0
+    per_row = []
+    for g, o, n in zip(gpu_idx, orc_idx, counts):
+        sg = set(int(x) for x in g[:n])
+        so = set(int(x) for x in o[:n])
+        hit += len(sg & so)
+        tot += len(so)
+        per_row.append(len(sg & so) / max(1, len(so)))
+    return hit / max(1, tot), min(per_row) if per_row else 1.0
+
+
+def check_attention(out_t, lse_t, orc_out, orc_lse, rows=None):
+    o = np_(out_t.float()).astype(np.float64)
+    l = np_(lse_t).astype(np.float64)
+    if rows is not None:
+        o, l = o[rows], l[rows]
+        orc_out, orc_lse = orc_out[rows], orc_lse[rows]
+    err = np.abs(o - orc_out)
+    assert np.isfinite(o).all()
+    assert err.max() <= ATT_MAX_ABS, f"max abs error {err.max():.3g}"
+    assert err.mean() <= ATT_MEAN_ABS, f"mean abs error {err.mean():.3g}"
+    fin = np.isfinite(orc_lse)
+    assert (np.isfinite(l) == fin).all()
+    assert np.allclose(l[fin], orc_lse[fin], rtol=1e-4, atol=1e-3), \
+        f"lse error {np.abs(l[fin] - orc_lse[fin]).max():.3g}"
+    return float(err.max()), float(err.mean())
+
+
+def log2ceil(x):
+    return int(math.ceil(math.log2(max(1, x))))

@@ -1,0 +1,151 @@
+"""The C ABI on the host: the library loads, exports every symbol its header
+declares, sizes workspaces, and rejects bad arguments synchronously with the
+documented status codes.  Nothing here launches a kernel."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from indexer_top_sparse_score_amd import binding as B
+from workloads import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000  # an aligned address that host code never dereferences
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    return sorted(set(re.findall(r"DSA_API\s+[\w\s\*]+?\b(dsa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def test_exports_every_header_symbol(lib):
+    syms = header_symbols()
+    assert len(syms) == 7 and sorted(B.EXPORTS) == syms
+    for s in syms:
+        assert getattr(lib, s) is not None
+    assert lib.dsa_abi_version() == B.ABI_VERSION
+
+
+def test_status_strings():
+    assert B.status_string(0) == "ok"
+    assert B.status_string(-3).startswith("workspace")
+    assert B.status_string(99) == "unknown status"
+
+
+def prob(**kw):
+    base = dict(num_seqs=4, num_rows=4, seq_lens=FAKE, block_table=FAKE + 4096, max_blocks=2048,
+                block_size=64, row_seq=None, row_pos=None, H_I=64, D_I=128, H_q=128, D_qk=576,
+                D_v=512, K=2048, scale=576 ** -0.5)
+    base.update(kw)
+    return B.DsaProblem(**base)
+
+
+def paged(base=FAKE + (1 << 30), row=128, nb=8192):
+    return B.DsaPaged(base, 64 * row, row, nb)
+
+
+def ws_size(p, op):
+    return B.load().dsa_workspace_size(ctypes.byref(p), op)
+
+
+def test_workspace_sizes_for_every_workload():
+    for name, wl in CONFIGS.items():
+        max_blocks = -(-(wl.context or wl.ragged[1]) // 64)
+        p = prob(num_seqs=wl.batch, num_rows=wl.rows, max_blocks=max_blocks, H_I=wl.H_I,
+                 D_I=wl.D_I, H_q=wl.H_q, D_qk=wl.D_qk, D_v=wl.D_v, K=wl.K, scale=wl.scale,
+                 row_seq=FAKE if wl.prefill_rows else None, row_pos=FAKE if wl.prefill_rows else None)
+        for op in range(4):
+            n = ws_size(p, op)
+            assert n >= 256 and n % 256 == 0, (name, op, n)
+        # the fused step keeps its scores in the workspace: at least one row's worth
+        assert ws_size(p, B.DSA_OP_DECODE_STEP) >= 64 * max_blocks * 4
+
+
+@pytest.mark.parametrize("field,value", [
+    ("num_seqs", 0), ("num_rows", -1), ("max_blocks", 0), ("seq_lens", None),
+    ("block_table", None), ("H_I", 0), ("K", 0), ("seq_lens", FAKE + 2)])
+def test_invalid_problem_has_no_workspace(field, value):
+    assert ws_size(prob(**{field: value}), B.DSA_OP_DECODE_STEP) == 0
+
+
+@pytest.mark.parametrize("field,value", [("block_size", 32), ("H_I", 65), ("D_I", 96),
+                                         ("H_q", 129), ("D_qk", 128), ("D_v", 256)])
+def test_unsupported_shapes(field, value):
+    assert ws_size(prob(**{field: value}), B.DSA_OP_DECODE_STEP) == 0
+
+
+def call_scores(p, *, qI=FAKE, w=FAKE, kI=None, scores=FAKE, ld=131072, ws=FAKE, ws_bytes=256):
+    return B.raw_call("dsa_indexer_scores", ctypes.byref(p), ctypes.c_void_p(qI),
+                      ctypes.c_void_p(w), kI or paged(), ctypes.c_void_p(scores),
+                      ctypes.c_int64(ld), ctypes.c_void_p(ws), ctypes.c_size_t(ws_bytes), None)
+
+
+def test_indexer_scores_rejections():
+    p = prob()
+    assert call_scores(prob(block_size=16)) == B.DSA_ERR_UNSUPPORTED
+    assert call_scores(prob(D_I=256)) == B.DSA_ERR_UNSUPPORTED
+    assert call_scores(prob(H_I=0)) == B.DSA_ERR_INVALID
+    assert call_scores(p, qI=0) == B.DSA_ERR_INVALID
+    assert call_scores(p, qI=FAKE + 8) == B.DSA_ERR_INVALID          # misaligned
+    assert call_scores(p, ld=1000) == B.DSA_ERR_INVALID              # ld < 64 * max_blocks
+    assert call_scores(p, kI=paged(row=64)) == B.DSA_ERR_INVALID     # row shorter than D_I
+    assert call_scores(p, kI=B.DsaPaged(FAKE, 8200, 128, 4)) == B.DSA_ERR_INVALID  # stride % 16
+    assert call_scores(p, kI=B.DsaPaged(FAKE, 8192, 128, 0)) == B.DSA_ERR_INVALID  # no blocks
+    assert call_scores(p, ws=0) == B.DSA_ERR_WORKSPACE
+    assert call_scores(p, ws_bytes=255) == B.DSA_ERR_WORKSPACE
+    assert call_scores(p, ws=FAKE + 16) == B.DSA_ERR_INVALID         # workspace alignment
+    assert call_scores(None if False else prob(num_rows=0)) == B.DSA_OK  # empty: nothing runs
+    assert B.raw_call("dsa_indexer_scores", None, None, None, paged(), None, 0, None, 0,
+                      None) == B.DSA_ERR_INVALID
+
+
+def test_topk_rejections():
+    def call(p, scores=FAKE, ld=131072, idx=FAKE, counts=None, ws=FAKE, nbytes=256):
+        return B.raw_call("dsa_topk", ctypes.byref(p), ctypes.c_void_p(scores),
+                          ctypes.c_int64(ld), ctypes.c_void_p(idx), ctypes.c_void_p(counts),
+                          ctypes.c_void_p(ws), ctypes.c_size_t(nbytes), None)
+    assert call(prob(K=0)) == B.DSA_ERR_INVALID
+    assert call(prob(), idx=0) == B.DSA_ERR_INVALID
+    assert call(prob(), counts=FAKE + 2) == B.DSA_ERR_INVALID
+    assert call(prob(), ld=10) == B.DSA_ERR_INVALID
+    assert call(prob(), nbytes=0) == B.DSA_ERR_WORKSPACE
+    assert call(prob(num_rows=0)) == B.DSA_OK
+
+
+def test_sparse_attn_rejections():
+    def call(p, q=FAKE, k=None, v=None, idx=FAKE, out=FAKE, lse=None, ws=FAKE, nbytes=1 << 30):
+        return B.raw_call("dsa_sparse_attn", ctypes.byref(p), ctypes.c_void_p(q),
+                          k or paged(row=1152), v or paged(row=1152), ctypes.c_void_p(idx),
+                          ctypes.c_void_p(out), ctypes.c_void_p(lse), ctypes.c_void_p(ws),
+                          ctypes.c_size_t(nbytes), None)
+    assert call(prob(D_qk=128, D_v=128)) == B.DSA_ERR_UNSUPPORTED
+    assert call(prob(scale=float("nan"))) == B.DSA_ERR_INVALID
+    assert call(prob(), k=paged(row=1024)) == B.DSA_ERR_INVALID      # K row < 576 bf16
+    assert call(prob(), q=FAKE + 4) == B.DSA_ERR_INVALID
+    assert call(prob(), idx=0) == B.DSA_ERR_INVALID
+    assert call(prob(), lse=FAKE + 1) == B.DSA_ERR_INVALID
+    need = ws_size(prob(), B.DSA_OP_SPARSE_ATTN)
+    assert call(prob(), nbytes=need - 256) == B.DSA_ERR_WORKSPACE
+    assert call(prob(num_rows=0)) == B.DSA_OK
+
+
+def test_decode_step_rejections():
+    def call(p, kI=None, k=None, nbytes=None, ws=FAKE, indices=None):
+        nbytes = ws_size(prob(), 3) if nbytes is None else nbytes
+        return B.raw_call("dsa_decode_step", ctypes.byref(p), ctypes.c_void_p(FAKE),
+                          ctypes.c_void_p(FAKE), kI or paged(), ctypes.c_void_p(FAKE),
+                          k or paged(row=1152), k or paged(row=1152), ctypes.c_void_p(FAKE),
+                          None, ctypes.c_void_p(indices), None, ctypes.c_void_p(ws),
+                          ctypes.c_size_t(nbytes), None)
+    assert call(prob(H_I=100)) == B.DSA_ERR_UNSUPPORTED
+    assert call(prob(), kI=paged(row=16)) == B.DSA_ERR_INVALID
+    assert call(prob(), nbytes=1024) == B.DSA_ERR_WORKSPACE
+    assert call(prob(), indices=FAKE + 2) == B.DSA_ERR_INVALID
+    assert call(prob(num_rows=0), nbytes=256) == B.DSA_OK

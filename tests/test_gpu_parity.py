@@ -1,0 +1,210 @@
+"""GPU parity at oracle-speed sizes: every entry point against the oracle,
+element by element, on shapes that span several tiles and ragged tails.
+
+Bars: integer mode -- scores and indices bit-exact; Gaussian mode -- scores
+within the float32 forward-error bound, Top-K recall >= 0.999, and Top-K
+bit-exact when both sides select from the same scores; attention -- max
+|error| <= 2e-2 and mean |error| <= 2e-3 against the oracle on the same
+indices."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_helpers import (RECALL_MIN, check_attention, check_scores_exact, gpu_attn,
+                               gpu_decode, gpu_scores, gpu_topk, np_, recall, say, score_bound)
+from tests.helpers import run_oracle
+from workloads import CONFIGS, make_batch, oracle_arrays, row_positions, small_workload
+
+pytestmark = pytest.mark.gpu
+
+# lengths chosen to hit: a single position, a partial first page, exact page
+# and tile edges, L < K, L == K, L == K + 1, several 1024-position tiles and
+# ragged last pages
+LENGTHS = [1, 63, 64, 65, 1000, 2048, 2049, 4097, 5000]
+MLA = dict(H_I=64, D_I=128, H_q=128, D_qk=576, D_v=512, K=2048, scale=576 ** -0.5)
+TINY = dict(H_I=4, D_I=64, H_q=8, D_qk=64, D_v=64, K=64, scale=0.125, latent=False)
+
+CASES = {
+    "mla_int": dict(lengths=LENGTHS, mode="int", **MLA),
+    "mla_int_shuffled": dict(lengths=LENGTHS, mode="int", table="shuffled", **MLA),
+    "tiny_int": dict(lengths=[1, 50, 64, 1024, 3000], mode="int", **TINY),
+    "mla_int_k100": dict(lengths=[99, 100, 101, 3000], mode="int", **{**MLA, "K": 100}),
+    "mla_int_k1": dict(lengths=[1, 2, 700], mode="int", **{**MLA, "K": 1}),
+    "h48_d64": dict(lengths=[777, 2500], mode="int", **{**MLA, "H_I": 48, "D_I": 64, "H_q": 80}),
+}
+
+
+def _batch(name, seed=21, **over):
+    kw = dict(CASES[name])
+    kw.update(over)
+    lengths = kw.pop("lengths")
+    wl = small_workload(name, lengths=lengths, **kw)
+    say(f"case {name} seed {seed} lengths {lengths}")
+    return make_batch(wl, device="cuda", seed=seed)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_scores_exact_integer_mode(name):
+    batch = _batch(name)
+    arr = oracle_arrays(batch)
+    orc = run_oracle(arr)
+    check_scores_exact(gpu_scores(batch), orc, row_positions(batch))
+
+
+def test_scores_gaussian_within_fp32_bound():
+    batch = _batch("mla_int", mode="gauss", seed=22)
+    arr = oracle_arrays(batch)
+    orc = run_oracle(arr)
+    g = np_(gpu_scores(batch))
+    for i, (_, p) in enumerate(row_positions(batch)):
+        want = orc["scores"][i].astype(np.float64)
+        got = g[i, :p + 1].astype(np.float64)
+        ulp = np.spacing(np.abs(orc["scores"][i])).astype(np.float64)
+        bound = score_bound(arr, i, p) + ulp
+        assert (np.abs(got - want) <= bound).all(), f"row {i}"
+        assert np.isnan(g[i, p + 1:]).all()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_topk_exact_on_oracle_scores(name):
+    # both sides select from the same float32 scores: indices must be identical
+    batch = _batch(name, mode="gauss", seed=23)
+    arr = oracle_arrays(batch)
+    orc = run_oracle(arr)
+    ld = 64 * batch.max_blocks
+    sc = np.full((batch.rows, ld), np.nan, np.float32)
+    for i, s in enumerate(orc["scores"]):
+        sc[i, :len(s)] = s
+    idx, cnt = gpu_topk(batch, torch.from_numpy(sc).cuda())
+    assert (np_(cnt) == orc["counts"]).all()
+    assert (np_(idx) == orc["indices"]).all()
+
+
+def test_topk_ties_and_special_values():
+    # heavy ties, signed zeros, infinities, all-equal rows: exact vs the oracle
+    wl = small_workload("ties", lengths=[5000, 5000, 5000, 5000, 3000, 2049], **MLA)
+    batch = make_batch(wl, device="cuda", seed=24)
+    rng = np.random.default_rng(24)
+    ld = 64 * batch.max_blocks
+    sc = np.full((batch.rows, ld), np.nan, np.float32)
+    L = batch.lengths
+    sc[0, :L[0]] = rng.integers(0, 7, L[0])                        # 7 distinct values
+    sc[1, :L[1]] = 3.0                                              # all equal
+    sc[2, :L[2]] = rng.choice(np.array([-0.0, 0.0, 1.0, -1.0], np.float32), L[2])
+    sc[3, :L[3]] = rng.choice(np.array([-np.inf, np.inf, 5.0, -2.0], np.float32), L[3])
+    sc[4, :L[4]] = rng.standard_normal(L[4]).astype(np.float32) * 1e-30  # subnormal-ish range
+    sc[5, :L[5]] = -np.arange(L[5], dtype=np.float32)              # K+1 distinct, descending
+    idx, cnt = gpu_topk(batch, torch.from_numpy(sc).cuda())
+    for i in range(batch.rows):
+        want, n = oracle.topk_row(sc[i, :L[i]], wl.K)
+        assert int(np_(cnt)[i]) == n
+        assert (np_(idx)[i] == want).all(), f"row {i}"
+
+
+@pytest.mark.parametrize("name", ["mla_int", "tiny_int", "mla_int_k100", "h48_d64"])
+def test_sparse_attn_on_oracle_indices(name):
+    batch = _batch(name, mode="gauss", seed=25)
+    arr = oracle_arrays(batch)
+    orc = run_oracle(arr)
+    out, lse = gpu_attn(batch, torch.from_numpy(orc["indices"]).cuda())
+    mx, mean = check_attention(out, lse, orc["out"], orc["lse"])
+    say(f"attention {name}: max {mx:.3g} mean {mean:.3g}")
+
+
+def test_sparse_attn_skips_padding_and_handles_empty_rows():
+    batch = _batch("mla_int", mode="gauss", seed=26)
+    arr = oracle_arrays(batch)
+    K = batch.wl.K
+    rng = np.random.default_rng(26)
+    idx = np.full((batch.rows, K), -1, np.int32)
+    for i, (_, p) in enumerate(row_positions(batch)):
+        if i == 2:
+            continue                                                # no valid index: out 0, lse -inf
+        n = int(rng.integers(1, min(K, p + 1) + 1))
+        sel = np.sort(rng.choice(p + 1, n, replace=False))
+        slots = np.sort(rng.choice(K, n, replace=False))            # scattered among -1 pads
+        idx[i, slots] = sel
+    out, lse = gpu_attn(batch, torch.from_numpy(idx).cuda())
+    want_o = np.zeros((batch.rows, batch.wl.H_q, batch.wl.D_v))
+    want_l = np.full((batch.rows, batch.wl.H_q), -np.inf)
+    for i, (b, p) in enumerate(row_positions(batch)):
+        sel = np.sort(idx[i][idx[i] >= 0])
+        if len(sel) == 0:
+            continue
+        k_rows = oracle.gather_positions(arr["k_cache"], arr["block_table"][b], sel)
+        want_o[i], want_l[i] = oracle.sparse_attn_row(arr["q"][i], k_rows, k_rows[:, :512],
+                                                      batch.wl.scale)
+    check_attention(out, lse, want_o, want_l)
+    assert (np_(out.float())[2] == 0).all() and np.isneginf(np_(lse)[2]).all()
+
+
+@pytest.mark.parametrize("name", ["mla_int", "mla_int_shuffled", "tiny_int", "mla_int_k100"])
+def test_decode_step_integer_mode(name):
+    batch = _batch(name, seed=27)
+    arr = oracle_arrays(batch)
+    orc = run_oracle(arr, keep_scores=False)
+    res = gpu_decode(batch)
+    assert (np_(res["counts"]) == orc["counts"]).all()
+    assert (np_(res["indices"]) == orc["indices"]).all()
+    check_attention(res["out"], res["lse"], orc["out"], orc["lse"])
+
+
+def test_decode_step_gaussian_mode():
+    batch = _batch("mla_int", mode="gauss", seed=28)
+    arr = oracle_arrays(batch)
+    orc = run_oracle(arr, keep_scores=False)
+    res = gpu_decode(batch)
+    gi = np_(res["indices"])
+    rec, worst = recall(gi, orc["indices"], orc["counts"])
+    say(f"recall {rec:.6f} (worst row {worst:.6f})")
+    assert rec >= RECALL_MIN
+    same = [i for i in range(batch.rows) if (gi[i] == orc["indices"][i]).all()]
+    assert len(same) >= batch.rows - 1
+    check_attention(res["out"], res["lse"], orc["out"], orc["lse"], rows=same)
+    # every selection is valid: ascending, distinct, inside the history, -1 padded
+    for i, (_, p) in enumerate(row_positions(batch)):
+        n = int(orc["counts"][i])
+        sel = gi[i, :n]
+        assert (np.diff(sel) > 0).all() and sel.min() >= 0 and sel.max() <= p
+        assert (gi[i, n:] == -1).all()
+
+
+def test_decode_step_prefill_rows():
+    wl = small_workload("prefill", lengths=[6000], prefill_rows=48, mode="int", **MLA)
+    batch = make_batch(wl, device="cuda", seed=29)
+    arr = oracle_arrays(batch)
+    orc = run_oracle(arr, keep_scores=False)
+    res = gpu_decode(batch)
+    assert (np_(res["indices"]) == orc["indices"]).all()
+    check_attention(res["out"], res["lse"], orc["out"], orc["lse"])
+
+
+def test_decode_step_deterministic_and_matches_unfused_calls():
+    batch = _batch("mla_int", mode="gauss", seed=30)
+    a = gpu_decode(batch)
+    b = gpu_decode(batch)
+    for key in ("out", "lse", "indices", "counts"):
+        assert torch.equal(a[key].view(torch.uint8) if a[key].dtype == torch.bfloat16 else a[key],
+                           b[key].view(torch.uint8) if b[key].dtype == torch.bfloat16 else b[key])
+    sc = gpu_scores(batch)
+    idx, cnt = gpu_topk(batch, sc)
+    assert torch.equal(idx, a["indices"]) and torch.equal(cnt, a["counts"])
+    out, lse = gpu_attn(batch, idx)
+    assert torch.equal(out.view(torch.int16), a["out"].view(torch.int16))
+    assert torch.equal(lse, a["lse"])
+
+
+def test_tiny_workload_matches_golden_fixture():
+    import json
+    import os
+    wl = CONFIGS["tiny_decode_1x1k"]
+    path = os.path.join(os.path.dirname(__file__), "golden", "tiny_decode_1x1k_seed1.json")
+    want = json.load(open(path))
+    batch = make_batch(wl, device="cpu", seed=wl.seed)
+    for name in ("seq_lens", "block_table", "qI", "w", "kI", "q", "kv", "v"):
+        setattr(batch, name, getattr(batch, name).cuda())
+    res = gpu_decode(batch)
+    assert np_(res["indices"])[0].tolist() == want["indices"]
+    assert int(np_(res["counts"])[0]) == want["count"]
