@@ -110,23 +110,27 @@ def main():
     torch.cuda.synchronize()
 
     launch = "stream"
-    graphs = []
+    graphs = {}
     if args.graph:
+        # one graph holds `rotate` consecutive steps (one per input set), the
+        # way a decode graph holds every layer of a step; a second graph holds
+        # the remainder so that exactly `steps` steps are timed
         try:
-            for i in range(rotate):
+            for n in sorted({rotate, args.steps % rotate} - {0}):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=stream):
-                    step(i)
-                graphs.append(g)
+                    for i in range(n):
+                        step(i)
+                graphs[n] = g
             with torch.cuda.stream(stream):
-                for i in range(rotate):
-                    graphs[i].replay()
+                for g in graphs.values():
+                    g.replay()
             torch.cuda.synchronize()
-            launch = "graph"
+            launch = f"graph ({rotate} steps per replay)"
         except Exception as e:  # capture unsupported: fall back to stream launches
             print(f"bench.py: graph capture failed ({e}); timing stream launches",
                   file=sys.stderr)
-            graphs = []
+            graphs = {}
     assert B.device_errors(ws) == 0
 
     torch.cuda.synchronize()
@@ -134,10 +138,13 @@ def main():
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         ev0.record(stream)
-        for i in range(args.steps):
-            if graphs:
-                graphs[i % rotate].replay()
-            else:
+        if graphs:
+            for _ in range(args.steps // rotate):
+                graphs[rotate].replay()
+            if args.steps % rotate:
+                graphs[args.steps % rotate].replay()
+        else:
+            for i in range(args.steps):
                 step(i)
         ev1.record(stream)
     torch.cuda.synchronize()

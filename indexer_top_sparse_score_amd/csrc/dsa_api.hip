@@ -89,7 +89,7 @@ int status_of(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
 
 struct DecodeLayout {
   int rp;
-  size_t idx_off, scores_off, part_off, total;
+  size_t idx_off, scores_off, topk_off, part_off, total;
 };
 
 DecodeLayout decode_layout(const dsa_problem* p) {
@@ -98,7 +98,8 @@ DecodeLayout decode_layout(const dsa_problem* p) {
   const int nc = attn_chunks(d.rp, p->H_q, p->K);
   d.idx_off = kHeader;
   d.scores_off = d.idx_off + round256((size_t)d.rp * p->K * sizeof(int32_t));
-  d.part_off = d.scores_off + round256((size_t)d.rp * max_len(p) * sizeof(float));
+  d.topk_off = d.scores_off + round256((size_t)d.rp * max_len(p) * sizeof(float));
+  d.part_off = d.topk_off + round256(topk_work_bytes(d.rp, max_len(p)));
   d.total = d.part_off + round256(attn_partial_bytes(d.rp, p->H_q, p->D_v, nc));
   return d;
 }
@@ -129,7 +130,8 @@ size_t dsa_workspace_size(const dsa_problem* p, int op) {
     case DSA_OP_INDEXER_SCORES:
       return check_indexer_shape(p) == DSA_OK ? kHeader : 0;
     case DSA_OP_TOPK:
-      return p->K >= 1 ? kHeader : 0;
+      if (p->K < 1) return 0;
+      return kHeader + round256(topk_work_bytes(p->num_rows, max_len(p)));
     case DSA_OP_SPARSE_ATTN: {
       if (check_attn_shape(p) != DSA_OK) return 0;
       const int nc = attn_chunks(p->num_rows, p->H_q, p->K);
@@ -169,6 +171,8 @@ int dsa_indexer_scores(const dsa_problem* p, const uint8_t* qI, const float* w, 
   a.row_begin = 0;
   a.num_rows = p->num_rows;
   a.max_len = (int32_t)max_len(p);
+  a.tw = TopkWork{};
+  a.feed_topk = false;
   return status_of(launch_indexer_scores(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -181,7 +185,7 @@ int dsa_topk(const dsa_problem* p, const float* scores, int64_t ld_scores, int32
   if (!aligned(scores, 4) || !aligned(indices, 4) || (counts && !aligned(counts, 4)))
     return DSA_ERR_INVALID;
   if (ld_scores < max_len(p)) return DSA_ERR_INVALID;
-  if ((st = check_ws(ws, ws_bytes, kHeader)) != DSA_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, dsa_workspace_size(p, DSA_OP_TOPK))) != DSA_OK) return st;
   if (p->num_rows == 0) return DSA_OK;
   TopkLaunch a;
   a.rows = row_map(p);
@@ -193,7 +197,9 @@ int dsa_topk(const dsa_problem* p, const float* scores, int64_t ld_scores, int32
   a.K = p->K;
   a.row_begin = 0;
   a.num_rows = p->num_rows;
-  a.scores_row_offset = 0;
+  a.max_len = (int32_t)max_len(p);
+  a.tw = topk_work_carve(static_cast<char*>(ws) + kHeader, p->num_rows, max_len(p));
+  a.prep = true;
   return status_of(launch_topk(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -274,6 +280,7 @@ int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa
   uint32_t* err = reinterpret_cast<uint32_t*>(base);
   float* scores = reinterpret_cast<float*>(base + d.scores_off);
   const int64_t ld = max_len(p);
+  const TopkWork tw = topk_work_carve(base + d.topk_off, d.rp, ld);
 
   for (int row0 = 0; row0 < p->num_rows; row0 += d.rp) {
     const int nr = p->num_rows - row0 < d.rp ? p->num_rows - row0 : d.rp;
@@ -293,6 +300,8 @@ int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa
     ia.row_begin = row0;
     ia.num_rows = nr;
     ia.max_len = (int32_t)ld;
+    ia.tw = tw;
+    ia.feed_topk = true;
     if ((st = status_of(launch_indexer_scores(ia, s))) != DSA_OK) return st;
 
     TopkLaunch ta;
@@ -305,7 +314,9 @@ int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa
     ta.K = p->K;
     ta.row_begin = row0;
     ta.num_rows = nr;
-    ta.scores_row_offset = 0;
+    ta.max_len = (int32_t)ld;
+    ta.tw = tw;
+    ta.prep = false;
     if ((st = status_of(launch_topk(ta, s))) != DSA_OK) return st;
 
     AttnLaunch aa = attn_launch(p, q, k, v, out, lse, err);

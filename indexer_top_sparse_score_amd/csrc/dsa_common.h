@@ -64,6 +64,37 @@ __device__ __forceinline__ int lane_prefix(uint64_t mask) {
 // Each returns hipSuccess or the launch error.  Arguments are validated by
 // the front end before these run.
 
+// ------------------------------------------------------ Top-K work area
+// Per-row scratch of the Top-K kernels, carved from the caller's workspace.
+// The indexer scan (fused step) or the Top-K prep kernel (standalone call)
+// writes the per-tile key ranges and clears `hist` and `state` for the rows
+// of the call, so nothing is carried over from one call to the next.
+#ifndef DSA_IDX_TILE
+#define DSA_IDX_TILE 256
+#endif
+constexpr int kMMTile = DSA_IDX_TILE;  // positions per key-range tile (= indexer workgroup tile)
+constexpr int kTopkBins = 2048; // histogram bins
+constexpr int kCandCap = 4096;  // candidates kept per row
+constexpr int kStateWords = 8;  // per-row state (see topk.hip)
+
+struct TopkWork {
+  uint32_t* tile_mm;  // [rows][mm_tiles][2]: min and max key of each tile
+  uint32_t* hist;     // [rows][kTopkBins]
+  uint32_t* state;    // [rows][kStateWords]
+  uint32_t* s_def;    // [rows][n_slices]: keys above the threshold (bin) in the slice
+  uint32_t* s_eq;     // [rows][n_slices]: keys equal to the threshold in the slice
+  uint32_t* s_off;    // [rows][n_slices]: first output slot of the slice
+  uint32_t* s_eqb;    // [rows][n_slices]: keys equal to the threshold before the slice
+  uint64_t* cand;     // [rows][kCandCap]: (key, position) composites
+  int32_t mm_tiles;   // ceil(max_len / kMMTile)
+  int32_t slice;      // positions per slice
+  int32_t n_slices;   // ceil(max_len / slice)
+};
+// bytes of the work area for `rows` rows of history up to max_len
+size_t topk_work_bytes(int rows, int64_t max_len);
+// carves the work area out of `base` (256-byte aligned)
+TopkWork topk_work_carve(void* base, int rows, int64_t max_len);
+
 struct IndexerLaunch {
   RowMap rows;
   const uint8_t* qI;
@@ -75,19 +106,23 @@ struct IndexerLaunch {
   int32_t H_I, D_I;
   int32_t row_begin, num_rows;  // rows [row_begin, row_begin + num_rows)
   int32_t max_len;              // upper bound of any row's history length
+  TopkWork tw;                  // key ranges + clearing for a Top-K that follows,
+  bool feed_topk;               // or nothing when feed_topk is false
 };
 hipError_t launch_indexer_scores(const IndexerLaunch& a, hipStream_t s);
 
 struct TopkLaunch {
   RowMap rows;
-  const float* scores;
+  const float* scores;  // row r reads scores[(r - row_begin) * ld]
   int64_t ld;
-  int32_t* indices;  // [rows][K]
-  int32_t* counts;   // [rows] or NULL
+  int32_t* indices;     // [num_rows][K]
+  int32_t* counts;      // [num_rows] or NULL
   uint32_t* err;
   int32_t K;
   int32_t row_begin, num_rows;
-  int64_t scores_row_offset;  // scores row of row_begin (row r reads scores[(r - row_begin + offset) * ld])
+  int32_t max_len;
+  TopkWork tw;
+  bool prep;            // compute key ranges here (no fused indexer before)
 };
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
 

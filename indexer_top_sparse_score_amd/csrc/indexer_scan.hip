@@ -7,57 +7,50 @@
 // positions, aggregate with head weights) and section 4.1 (read the paged K
 // cache directly, no intermediate per-head score matrix in memory).
 //
-// Mapping.  One v_mfma_f32_32x32x64_f8f6f4 multiplies 32 indexer heads (M)
-// by 32 positions (N) over 64 dims (K).  Heads sit on M so each lane's 16
-// accumulator registers hold 16 heads of ONE position: the gate and the
-// weighting are per-lane FMAs, and only one cross-lane add (the two 32-lane
-// halves) finishes the head sum.  The K dimension is split over the two lane
-// halves identically for the query (A) and the key (B) operands, so each lane
-// loads one contiguous run of 32 * D_I / 64 bytes of its position's key row.
+// Mapping.  One v_mfma_f32_16x16x128_f8f6f4 multiplies 16 indexer heads (M)
+// by 16 positions (N) over all 128 dims (K).  Heads sit on M, so each lane's
+// 4 accumulator registers hold 4 heads of ONE position: the gate and the
+// weighting are per-lane FMAs, and two cross-lane adds (over the four lane
+// groups) finish the head sum.  Lane group g holds bytes 16g..16g+15 and
+// 64+16g..64+16g+15 of its position's key row, the same slice rule as for the
+// query, so one 16-byte load instruction covers 16 rows x 64 contiguous bytes.
 //
 // Work split.  A workgroup (4 waves) owns a tile of kTile consecutive
-// positions of one row; each wave walks 32-position sub-tiles of it with a
-// one-deep register prefetch of the next sub-tile's keys.  A 32-position
-// sub-tile never straddles a 64-row page, so one block-table lookup serves
-// the whole wave.
+// positions of one row; each wave owns every fourth 16-position sub-tile of
+// it and issues all of their key loads before its first MFMA, so several KiB
+// per wave are in flight.  A sub-tile never straddles a 64-row page; the
+// tile's block ids are fetched once, one per lane.  The query and weights
+// are staged once per workgroup in LDS.
 
 #include "dsa_common.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kTile = 1024;    // positions per workgroup
+constexpr int kTile = kMMTile;  // positions per workgroup (= one key-range tile)
 constexpr int kWaves = 4;
-constexpr int kSub = 32;       // positions per MFMA column block
+constexpr int kSub = 16;  // positions per MFMA column block
 
-template <int NKS>
-struct KeyFrag {
-  v8i k[NKS];
-};
-
-// Loads this lane's part of a key row: 32*NKS bytes at byte offset
-// half*32*NKS of the row (zeros when the position is past the history or the
-// page is absent).
-template <int NKS>
-__device__ __forceinline__ KeyFrag<NKS> load_keys(const uint8_t* row, bool ok) {
-  KeyFrag<NKS> f;
-  if (ok) {
-    const v4i* src = reinterpret_cast<const v4i*>(row);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const v4i lo = __builtin_nontemporal_load(src + 2 * ks);
-      const v4i hi = __builtin_nontemporal_load(src + 2 * ks + 1);
-      f.k[ks] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) f.k[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-  }
-  return f;
+// This lane's 32-byte K slice of a 128-byte row (D_I = 128): the 16-byte
+// pieces g and g + 4, g = lane / 16.  For D_I = 64 the slice is piece g and
+// 16 zero bytes.  The same rule builds both MFMA operands, so the
+// contraction pairs query and key bytes of the same dimension.
+//
+// `row` must be readable even when `ok` is false (callers point it at valid
+// memory): the load is unconditional and the data is zeroed by a select,
+// which keeps the code free of branches so every wait is exact.
+template <int NKP>
+__device__ __forceinline__ v8i load_slice(const uint8_t* row, int g, bool ok) {
+  const v4i* src = reinterpret_cast<const v4i*>(row);
+  const v4i lo = src[g];
+  const v4i hi = NKP == 2 ? src[g + 4] : v4i{0, 0, 0, 0};
+  const int m = ok ? -1 : 0;
+  return v8i{lo[0] & m, lo[1] & m, lo[2] & m, lo[3] & m,
+             hi[0] & m, hi[1] & m, hi[2] & m, hi[3] & m};
 }
 
-// NKS = D_I / 64 K-steps; HT = 32-head tiles (ceil(H_I / 32)).
-template <int NKS, int HT>
+// NKP = D_I / 64 pieces per lane; HT = 16-head tiles (ceil(H_I / 16)).
+template <int NKP, int HT>
 __global__ __launch_bounds__(256) void indexer_scan_kernel(IndexerLaunch a) {
   const int r = a.row_begin + (int)blockIdx.y;
   int b, p;
@@ -68,94 +61,139 @@ __global__ __launch_bounds__(256) void indexer_scan_kernel(IndexerLaunch a) {
   const int L = p + 1;
   const int tile0 = (int)blockIdx.x * kTile;
   if (tile0 >= L) return;
-  const int tile_end = min(L, tile0 + kTile);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int col = lane & 31;   // head row of A, position column of B
-  const int half = lane >> 5;  // which half of each 64-dim K step this lane holds
-  constexpr int kRowBytes = 64 * NKS;
-  constexpr int kLaneBytes = 32 * NKS;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15;  // head row of A, position column of B
+  const int g = lane >> 4;    // K slice group
+  constexpr int kRowBytes = 64 * NKP;
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[64 * 128];
+  __shared__ float w_lds[64];
 
-  // A operands: the indexer query of heads ht*32 + col.
-  v8i aq[HT][NKS];
-  const uint8_t* qrow = a.qI + (int64_t)r * a.H_I * kRowBytes;
+  // Load order matters (vector loads complete in issue order): one round
+  // trip fetches the tile's block ids and the row's query and weights (once
+  // per workgroup, staged in LDS), then every key load is issued, and each
+  // sub-tile is computed as soon as its own keys have landed.
+
+  // 1. block ids of the tile's pages, one per lane (read back into scalar
+  //    registers per sub-tile); query and weights into LDS, heads past H_I
+  //    as zero
+  constexpr int kPages = kTile / kBlock;
+  static_assert(kPages <= 64, "tile spans more pages than a wave has lanes");
+  const int32_t* bt = a.rows.block_table + (int64_t)b * a.rows.max_blocks;
+  int my_page = -1;
+  if (lane < kPages && tile0 + lane * kBlock < L) my_page = bt[tile0 / kBlock + lane];
+  {
+    // the padded query is HT*16 rows of kRowBytes <= 8 KiB: two 16-byte
+    // pieces per thread; all loads are issued before any LDS write
+    const uint8_t* qrow = a.qI + (int64_t)r * a.H_I * kRowBytes;
+    const int qbytes = a.H_I * kRowBytes;
+    constexpr int kQBytes = HT * 16 * kRowBytes;
+    const int off0 = threadIdx.x * 16, off1 = off0 + 256 * 16;
+    const v4i z = v4i{0, 0, 0, 0};
+    const v4i q0 = off0 < qbytes ? *reinterpret_cast<const v4i*>(qrow + off0) : z;
+    const v4i q1 = off1 < qbytes ? *reinterpret_cast<const v4i*>(qrow + off1) : z;
+    const float wv = threadIdx.x < a.H_I ? a.w[(int64_t)r * a.H_I + threadIdx.x] : 0.0f;
+    if (off0 < kQBytes) *reinterpret_cast<v4i*>(&q_lds[off0]) = q0;
+    if (off1 < kQBytes) *reinterpret_cast<v4i*>(&q_lds[off1]) = q1;
+    if (threadIdx.x < HT * 16) w_lds[threadIdx.x] = wv;
+  }
+
+  // 2. keys: this wave's sub-tiles j start at tile0 + (wave + kWaves*j)*16.
+  //    Straight-line code lets the compiler wait for each sub-tile alone
+  //    (vmcnt(N)) while the later loads stay in flight.
+  constexpr int kSubPerWave = kTile / (kWaves * kSub);
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.kI.base);
+  v8i keys[kSubPerWave];
+  bool page_ok[kSubPerWave];
+#pragma unroll
+  for (int j = 0; j < kSubPerWave; ++j) {
+    const int s0 = tile0 + (wave + kWaves * j) * kSub;
+    const int phys = __builtin_amdgcn_readlane(my_page, (s0 - tile0) >> 6);
+    page_ok[j] = phys >= 0 && (int64_t)phys < a.kI.num_blocks;
+    const uint8_t* row = kbase + (int64_t)(page_ok[j] ? phys : 0) * a.kI.block_stride +
+                         (int64_t)((s0 + col) & 63) * a.kI.row_stride;
+    keys[j] = load_slice<NKP>(row, g, page_ok[j] && s0 + col < L);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  // A operands (heads 16*ht + col) and the head weights of this lane's
+  // accumulator rows (register v of a 16x16 tile is row 4*g + v)
+  v8i aq[HT];
+  float wr[HT][4];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
-    const int head = ht * 32 + col;
-    KeyFrag<NKS> f = load_keys<NKS>(qrow + (int64_t)head * kRowBytes + half * kLaneBytes,
-                                    head < a.H_I);
+    const v4i* src = reinterpret_cast<const v4i*>(&q_lds[(16 * ht + col) * kRowBytes]);
+    const v4i lo = src[g];
+    const v4i hi = NKP == 2 ? src[g + 4] : v4i{0, 0, 0, 0};
+    aq[ht] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) aq[ht][ks] = f.k[ks];
+    for (int v = 0; v < 4; ++v) wr[ht][v] = w_lds[16 * ht + 4 * g + v];
   }
-  // Head weights of the 16 accumulator rows this lane holds:
-  // register v of a 32x32 tile is row 8*(v/4) + 4*half + v%4.
-  float wr[HT][16];
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int head = ht * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-      wr[ht][v] = head < a.H_I ? a.w[(int64_t)r * a.H_I + head] : 0.0f;
-    }
-
-  const int32_t* bt = a.rows.block_table + (int64_t)b * a.rows.max_blocks;
-  const uint8_t* kbase = static_cast<const uint8_t*>(a.kI.base);
   float* out = a.scores + (int64_t)(r - a.row_begin) * a.ld;
 
-  auto key_row = [&](int s0, bool& page_ok) -> const uint8_t* {
-    const int phys = bt[s0 >> 6];
-    page_ok = phys >= 0 && (int64_t)phys < a.kI.num_blocks;
-    return kbase + (int64_t)(page_ok ? phys : 0) * a.kI.block_stride +
-           (int64_t)((s0 + col) & 63) * a.kI.row_stride + half * kLaneBytes;
-  };
-
-  int s0 = tile0 + wave * kSub;
-  if (s0 >= tile_end) return;
-  bool ok_cur;
-  const uint8_t* row_cur = key_row(s0, ok_cur);
-  KeyFrag<NKS> cur = load_keys<NKS>(row_cur, ok_cur && s0 + col < L);
-  bool page_cur = ok_cur;
-
-  while (true) {
-    const int s1 = s0 + kWaves * kSub;
-    KeyFrag<NKS> nxt;
-    bool page_nxt = false;
-    if (s1 < tile_end) {
-      const uint8_t* row_nxt = key_row(s1, page_nxt);
-      nxt = load_keys<NKS>(row_nxt, page_nxt && s1 + col < L);
-    }
-
+  // key range of the scores this wave writes (for the Top-K that follows)
+  uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+#pragma unroll
+  for (int j = 0; j < kSubPerWave; ++j) {
+    const int s0 = tile0 + (wave + kWaves * j) * kSub;
     float part = 0.0f;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      v16f acc = {};
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[ht], keys[j], acc, 0, 0, 0, 0,
+                                                             0, 0);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aq[ht][ks], cur.k[ks], acc,
-                                                              0, 0, 0, 0, 0, 0);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) part += wr[ht][v] * fmaxf(acc[v], 0.0f);
+      for (int v = 0; v < 4; ++v) part += wr[ht][v] * fmaxf(acc[v], 0.0f);
     }
+    part += __shfl_xor(part, 16);
     part += __shfl_xor(part, 32);
     const int s = s0 + col;
-    if (half == 0 && s < L) {
+    if (g == 0 && s < L) {
       // canonical +0 for a zero score; an absent page scores -inf
-      out[s] = page_cur ? part + 0.0f : -__builtin_inff();
+      const float v = page_ok[j] ? part + 0.0f : -__builtin_inff();
+      out[s] = v;
+      const uint32_t k = score_key(v);
+      kmn = min(kmn, k);
+      kmx = max(kmx, k);
     }
-    if (!page_cur && lane == 0) report(a.err, DSA_DEVERR_BLOCK);
+    if (s0 < L && !page_ok[j] && lane == 0) report(a.err, DSA_DEVERR_BLOCK);
+  }
 
-    if (s1 >= tile_end) break;
-    s0 = s1;
-    cur = nxt;
-    page_cur = page_nxt;
+  if (a.feed_topk) {
+    __shared__ uint32_t red[2 * kWaves];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, o));
+      kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o));
+    }
+    if (lane == 0) {
+      red[wave] = kmn;
+      red[kWaves + wave] = kmx;
+    }
+    __syncthreads();
+    const int r_local = r - a.row_begin;
+    if (threadIdx.x == 0) {
+      for (int w = 0; w < kWaves; ++w) {
+        kmn = min(kmn, red[w]);
+        kmx = max(kmx, red[kWaves + w]);
+      }
+      uint32_t* mm = a.tw.tile_mm + ((int64_t)r_local * a.tw.mm_tiles + blockIdx.x) * 2;
+      mm[0] = kmn;
+      mm[1] = kmx;
+    }
+    if (blockIdx.x == 0) {
+      uint32_t* h = a.tw.hist + (int64_t)r_local * kTopkBins;
+      for (int i = threadIdx.x; i < kTopkBins; i += 256) h[i] = 0;
+      if (threadIdx.x < kStateWords) a.tw.state[(int64_t)r_local * kStateWords + threadIdx.x] = 0;
+    }
   }
 }
 
-template <int NKS, int HT>
+template <int NKP, int HT>
 hipError_t launch_t(const IndexerLaunch& a, hipStream_t s) {
   dim3 grid((a.max_len + kTile - 1) / kTile, a.num_rows);
-  indexer_scan_kernel<NKS, HT><<<grid, 256, 0, s>>>(a);
+  indexer_scan_kernel<NKP, HT><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -163,9 +201,21 @@ hipError_t launch_t(const IndexerLaunch& a, hipStream_t s) {
 
 hipError_t launch_indexer_scores(const IndexerLaunch& a, hipStream_t s) {
   if (a.num_rows <= 0 || a.max_len <= 0) return hipSuccess;
-  const bool two = a.H_I > 32;
-  if (a.D_I == 128) return two ? launch_t<2, 2>(a, s) : launch_t<2, 1>(a, s);
-  return two ? launch_t<1, 2>(a, s) : launch_t<1, 1>(a, s);
+  const int ht = (a.H_I + 15) / 16;
+  if (a.D_I == 128) {
+    switch (ht) {
+      case 1: return launch_t<2, 1>(a, s);
+      case 2: return launch_t<2, 2>(a, s);
+      case 3: return launch_t<2, 3>(a, s);
+      default: return launch_t<2, 4>(a, s);
+    }
+  }
+  switch (ht) {
+    case 1: return launch_t<1, 1>(a, s);
+    case 2: return launch_t<1, 2>(a, s);
+    case 3: return launch_t<1, 3>(a, s);
+    default: return launch_t<1, 4>(a, s);
+  }
 }
 
 }  // namespace dsa
