@@ -142,7 +142,7 @@ struct AttnLaunch {
   int32_t row_begin, num_rows;
   int32_t n_chunks;
 };
-int attn_chunks(int num_rows, int H_q, int K);
+int attn_chunks(int num_rows, int H_q, int D_qk, int K);
 size_t attn_partial_bytes(int num_rows, int H_q, int D_v, int n_chunks);
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s);
 
