@@ -11,7 +11,9 @@ bytes touched per rotation exceed the 256 MB Infinity Cache several times.
 value      decode tokens/s = rows * steps / timed seconds (whole GPU)
 roofline   the dominant kernel (the indexer scan): algorithmic bytes per
            launch / its average launch time, measured here with HIP events
-           on the launch stream, against the 8 TB/s HBM peak
+           on the launch stream, against the 8 TB/s HBM peak; `traffic` is
+           the counter-measured HBM bytes per launch from profiles/ (null
+           when the kernel source changed since they were taken)
 cpu_baseline  the oracle timed on the host on a bounded sample of rows
 """
 
@@ -40,6 +42,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--table", default=None)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain elementwise copy of MIB MiB (float32 in, float32 out) "
+                         "so that hardware byte counters can be scaled against known traffic")
     return ap.parse_args()
 
 
@@ -61,6 +66,26 @@ def indexer_bytes(wl, lengths):
     weights, block-table entries, and the float32 scores it writes."""
     return sum(wl.D_I * L + wl.H_I * wl.D_I + 4 * wl.H_I + 4 * ((L + 63) // 64) + 4 * L
                for L in lengths)
+
+
+def recorded_traffic(workload):
+    """HBM bytes per indexer-scan dispatch from the committed counter summary
+    for this workload, or None when there is none or when the kernel's source
+    has changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"indexer_scan_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    h = re.search(r"source_sha256: ([0-9a-f]{64})", text)
+    if not m or not h:
+        return None
+    csrc = os.path.join(ROOT, "indexer_top_sparse_score_amd", "csrc")
+    src = b"".join(open(os.path.join(csrc, f), "rb").read()
+                   for f in ("indexer_scan.hip", "dsa_common.h"))
+    return int(m.group(1)) if hashlib.sha256(src).hexdigest() == h.group(1) else None
 
 
 def main():
@@ -172,6 +197,7 @@ def main():
     idx_us = 1e3 * e0.elapsed_time(e1) / args.steps
     ib = indexer_bytes(wl, lengths)
     achieved = ib / (idx_us * 1e-6) / 1e9
+    traffic = recorded_traffic(name)
 
     result = {
         "metric": "sparse-attn decode tokens/s at 128k ctx, K=2048; % of HBM peak (GB/s)",
@@ -198,10 +224,21 @@ def main():
         "roofline": {
             "bound": "hbm", "kernel": "indexer_scan_kernel", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None, "bytes_per_launch": ib, "avg_launch_us": round(idx_us, 3),
+            "traffic": traffic, "bytes_per_launch": ib, "avg_launch_us": round(idx_us, 3),
         },
         "wall_s": round(wall, 4),
     }
+
+    if args.copy_calibration:
+        n = (args.copy_calibration << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        result["copy_calibration"] = {"kernel": "elementwise neg (float32)",
+                                      "read_bytes": 4 * n, "write_bytes": 4 * n, "launches": 3}
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(first, args.cpu_seconds)
