@@ -10,7 +10,7 @@
 // kernel runs one workgroup per (slice, row):
 //
 //  0. key ranges (prep kernel, or the indexer scan's epilogue in the fused
-//     step): the min and max key of every 1024-position tile; the row's
+//     step): the min and max key of every kMMTile-position tile; the row's
 //     histogram and state are cleared.
 //  1. hist: histogram of the row's keys over 2048 bins of width 2^shift laid
 //     from the row's min key, so the bins follow the scores' actual range.
@@ -36,12 +36,14 @@
 namespace dsa {
 
 // per-row state words
-enum : int { kCandCount = 0, kArrived = 1, kT = 2, kPT = 3, kNeedEq = 4 };
+enum : int { kCandCount = 0, kArrived = 1, kT = 2, kNeedEq = 3, kMode = 4, kLoB = 5, kAbove = 6 };
 
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+constexpr int kPer = 8;                   // positions per thread per pass
+constexpr int kPass = kPer * kThreads;    // positions per pass; slices are multiples of it
 constexpr int kBinBits = 11;
 static_assert((1 << kBinBits) == kTopkBins, "bins");
 
@@ -137,18 +139,28 @@ __device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_
   }
 }
 
-// The row's key range from its tiles' ranges.
-__device__ __forceinline__ void row_range(const TopkLaunch& a, int r_local, int L, uint32_t& kmin,
-                                          uint32_t& kmax, uint32_t* scratch) {
+// This thread's share of the row's key range (the tiles' ranges), loaded
+// two tiles per step; block_minmax finishes it.
+__device__ __forceinline__ void row_range_load(const TopkLaunch& a, int r_local, int L,
+                                               uint32_t& kmin, uint32_t& kmax) {
   const int tiles = (L + kMMTile - 1) / kMMTile;
   const uint32_t* mm = a.tw.tile_mm + (int64_t)r_local * a.tw.mm_tiles * 2;
   kmin = 0xFFFFFFFFu;
   kmax = 0u;
-  for (int t = threadIdx.x; t < tiles; t += kThreads) {
-    kmin = min(kmin, mm[2 * t]);
-    kmax = max(kmax, mm[2 * t + 1]);
+  for (int t = threadIdx.x; t < tiles; t += 2 * kThreads) {
+    const int u = min(t + kThreads, tiles - 1);
+    const uint2 x = *reinterpret_cast<const uint2*>(mm + 2 * t);
+    const uint2 y = *reinterpret_cast<const uint2*>(mm + 2 * u);
+    kmin = min(kmin, min(x.x, y.x));
+    kmax = max(kmax, max(x.y, y.y));
   }
-  block_minmax(kmin, kmax, scratch);
+}
+
+// The keys of one pass (kPer per thread, coalesced; positions past `end`
+// repeat the last one and are masked by the caller).
+__device__ __forceinline__ void load_pass(const float* sc, int base, int end, uint32_t* k) {
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) k[j] = score_key(sc[min(base + j * kThreads + (int)threadIdx.x, end - 1)]);
 }
 
 __device__ __forceinline__ int range_shift(uint32_t kmin, uint32_t kmax) {
@@ -218,23 +230,21 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(TopkLaunch a) {
   const int start = blockIdx.x * a.tw.slice;
   if (start >= ri.L) return;
   const int end = min(ri.L, start + a.tw.slice);
-  uint32_t kmin, kmax;
-  row_range(a, ri.r_local, ri.L, kmin, kmax, scratch);
-  const int shift = range_shift(kmin, kmax);
-  for (int i = threadIdx.x; i < kTopkBins; i += kThreads) h[i] = 0;
-  __syncthreads();
   const float* sc = a.scores + (int64_t)ri.r_local * a.ld;
-  for (int base = start; base < end; base += 8 * kThreads) {
-    float v[8];
+  // the first pass's keys and the row's range are loaded together
+  uint32_t k[kPer];
+  load_pass(sc, start, end, k);
+  uint32_t kmin, kmax;
+  row_range_load(a, ri.r_local, ri.L, kmin, kmax);
+  for (int i = threadIdx.x; i < kTopkBins; i += kThreads) h[i] = 0;
+  block_minmax(kmin, kmax, scratch);  // its barriers also order the clearing
+  const int shift = range_shift(kmin, kmax);
+  for (int base = start; base < end; base += kPass) {
+    if (base != start) load_pass(sc, base, end, k);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kPer; ++j) {
       const int i = base + j * kThreads + threadIdx.x;
-      v[j] = i < end ? sc[i] : 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = base + j * kThreads + threadIdx.x;
-      if (i < end) atomicAdd(&h[min((score_key(v[j]) - kmin) >> shift, (uint32_t)kTopkBins - 1)], 1u);
+      if (i < end) atomicAdd(&h[min((k[j] - kmin) >> shift, (uint32_t)kTopkBins - 1)], 1u);
     }
   }
   __syncthreads();
@@ -297,6 +307,20 @@ __device__ uint64_t select_composite(const uint64_t* c, int n, uint32_t need, ui
   return lo;
 }
 
+// The need-th largest (1-based) of n <= kRankMax distinct composites in LDS:
+// a composite's rank is the number of larger ones.
+constexpr int kRankMax = 2 * kThreads;
+__device__ uint64_t select_by_rank(const uint64_t* c, int n, uint32_t need, uint64_t* out) {
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const uint64_t x = c[i];
+    uint32_t rank = 0;
+    for (int j = 0; j < n; ++j) rank += c[j] > x ? 1u : 0u;
+    if (rank + 1 == need) *out = x;
+  }
+  __syncthreads();
+  return *out;
+}
+
 // Fallback inside the last workgroup: narrow [lo, hi] over the row's keys
 // (read from global memory) until one key value T remains; returns T and the
 // number of keys equal to T still to keep in `need`.
@@ -327,7 +351,6 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkLaunch a) {
   __shared__ uint32_t h[kTopkBins];
   __shared__ uint32_t scratch[2 * kWaves];
   __shared__ uint32_t res[4];
-  __shared__ uint64_t cl[kCandCap];
   __shared__ uint32_t sel_cnt[256];
   __shared__ uint32_t sl_a[256];
   __shared__ int last;
@@ -342,12 +365,22 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkLaunch a) {
   uint32_t* st = a.tw.state + (int64_t)ri.r_local * kStateWords;
   const float* sc = a.scores + (int64_t)ri.r_local * a.ld;
 
+  // every independent load first: the first pass's keys, the row's range
+  // and the finished histogram
+  uint32_t k0[kPer];
+  load_pass(sc, start, end, k0);
   uint32_t kmin, kmax;
-  row_range(a, ri.r_local, ri.L, kmin, kmax, scratch);
+  row_range_load(a, ri.r_local, ri.L, kmin, kmax);
+  {
+    const uint32_t* gh = a.tw.hist + (int64_t)ri.r_local * kTopkBins;
+    uint32_t hv[kTopkBins / kThreads];
+#pragma unroll
+    for (int j = 0; j < kTopkBins / kThreads; ++j) hv[j] = gh[j * kThreads + threadIdx.x];
+#pragma unroll
+    for (int j = 0; j < kTopkBins / kThreads; ++j) h[j * kThreads + threadIdx.x] = hv[j];
+  }
+  block_minmax(kmin, kmax, scratch);  // its barriers also publish h
   const int shift = range_shift(kmin, kmax);
-  const uint32_t* gh = a.tw.hist + (int64_t)ri.r_local * kTopkBins;
-  for (int i = threadIdx.x; i < kTopkBins; i += kThreads) h[i] = gh[i];
-  __syncthreads();
   find_bin(h, (uint32_t)a.K, res, scratch);
   const uint32_t bstar = res[0];
   const uint32_t above = res[1];
@@ -356,33 +389,58 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkLaunch a) {
   const uint32_t span = (uint32_t)((1ull << shift) - 1);
   const uint32_t hi_b = (kmax - lo_b < span) ? kmax : lo_b + span;
   const int mode = lo_b == hi_b ? kTie : (cnt_b <= (uint32_t)kCandCap ? kCand : kFallback);
+  if (s == 0 && threadIdx.x == 0) {  // read by the compact kernel
+    st[kMode] = (uint32_t)mode;
+    st[kLoB] = lo_b;
+    st[kAbove] = above;
+  }
 
   if (mode != kFallback) {
+    // One pass of kPass positions per iteration (one, for slices of 2048):
+    // all loads are issued before any is used, and a wave reserves its
+    // candidate slots with a single atomic for the whole pass.  Everything
+    // written here is read by the next kernel, so plain stores suffice.
     uint32_t n_above = 0, n_eq = 0;
     const int lane = threadIdx.x & 63;
     uint64_t* cand = a.tw.cand + (int64_t)ri.r_local * kCandCap;
-    for (int base = start; base < end; base += kThreads) {
-      const int i = base + threadIdx.x;
-      const bool ok = i < end;
-      const uint32_t k = ok ? score_key(sc[i]) : 0u;
-      n_above += (ok && k > hi_b) ? 1u : 0u;
-      const bool in_bin = ok && k >= lo_b && k <= hi_b;
-      if (mode == kTie) {
-        n_eq += in_bin ? 1u : 0u;
-      } else {
-        const uint64_t m = __ballot(in_bin);
-        uint32_t slot = 0;
-        if (lane == 0 && m) slot = atomicAdd(&st[kCandCount], (uint32_t)__popcll(m));
-        slot = (uint32_t)__shfl((int)slot, 0);
-        const uint32_t at = slot + (uint32_t)lane_prefix(m);
-        if (in_bin && at < (uint32_t)kCandCap)
-          publish64(&cand[at], ((uint64_t)k << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)i));
+    for (int base = start; base < end; base += kPass) {
+      uint32_t k[kPer];
+      bool inb[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) k[j] = k0[j];
+      if (base != start) load_pass(sc, base, end, k);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const bool ok = base + j * kThreads + (int)threadIdx.x < end;
+        n_above += (ok && k[j] > hi_b) ? 1u : 0u;
+        inb[j] = ok && k[j] >= lo_b && k[j] <= hi_b;
+        n_eq += inb[j] ? 1u : 0u;
+      }
+      if (mode == kCand) {
+        uint64_t m[kPer];
+        uint32_t total = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          m[j] = __ballot(inb[j]);
+          total += (uint32_t)__popcll(m[j]);
+        }
+        if (total != 0) {  // wave-uniform
+          uint32_t slot = 0;
+          if (lane == 0) slot = atomicAdd(&st[kCandCount], total);
+          uint32_t at = (uint32_t)__shfl((int)slot, 0);
+#pragma unroll
+          for (int j = 0; j < kPer; ++j) {
+            const uint32_t mine = at + (uint32_t)lane_prefix(m[j]);
+            const uint32_t i = (uint32_t)(base + j * kThreads + (int)threadIdx.x);
+            if (inb[j] && mine < (uint32_t)kCandCap)
+              cand[mine] = ((uint64_t)k[j] << 32) | (0xFFFFFFFFu - i);
+            at += (uint32_t)__popcll(m[j]);
+          }
+        }
       }
     }
-    uint32_t t1;
     n_above = wave_sum(n_above);
     n_eq = wave_sum(n_eq);
-    __syncthreads();
     if (lane == 0) {
       scratch[threadIdx.x >> 6] = n_above;
       scratch[kWaves + (threadIdx.x >> 6)] = n_eq;
@@ -394,14 +452,15 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkLaunch a) {
         sa += scratch[w];
         se += scratch[kWaves + w];
       }
-      publish32(&a.tw.s_def[rs + s], sa);
-      publish32(&a.tw.s_eq[rs + s], se);
+      a.tw.s_def[rs + s] = sa;
+      a.tw.s_eq[rs + s] = se;
     }
-    (void)t1;
+    return;  // the compact kernel finishes the selection
   }
 
-  // ---- arrival: the last workgroup of the row finishes the selection
-  drain_memory();
+  // ---- fallback (bin b* too full for the candidate buffer): the last
+  // workgroup of the row to arrive refines the threshold over the whole row
+  // and sets every slice's output offset
   __syncthreads();
   if (threadIdx.x == 0)
     last = __hip_atomic_fetch_add(&st[kArrived], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
@@ -409,60 +468,27 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkLaunch a) {
   __syncthreads();
   if (!last) return;
 
-  uint32_t need = (uint32_t)a.K - above;  // keys still to keep from inside bin b*
-  uint32_t T, PT, need_eq;
-  // per-slice counts in LDS: keys above the threshold, and keys equal to it
-  // (tie modes) or chosen candidates (composite mode)
-  for (int j = threadIdx.x; j < 256; j += kThreads) {
-    sl_a[j] = j < n_sl && mode != kFallback ? fetch32(&a.tw.s_def[rs + j]) : 0u;
-    sel_cnt[j] = j < n_sl && mode == kTie ? fetch32(&a.tw.s_eq[rs + j]) : 0u;
+  uint32_t need = (uint32_t)a.K - above;
+  const uint32_t T = select_in_row(sc, ri.L, lo_b, hi_b, need, h, scratch, res);
+  for (int j = 0; j < n_sl; ++j) {
+    const int a0 = j * a.tw.slice, a1 = min(ri.L, a0 + a.tw.slice);
+    uint32_t g = 0, e = 0;
+    for (int i = a0 + threadIdx.x; i < a1; i += kThreads) {
+      const uint32_t k = score_key(sc[i]);
+      g += k > T ? 1u : 0u;
+      e += k == T ? 1u : 0u;
+    }
+    uint32_t tg, te;
+    block_exclusive_scan(g, scratch, tg);
+    block_exclusive_scan(e, scratch, te);
+    if (threadIdx.x == 0) {
+      sl_a[j] = tg;
+      sel_cnt[j] = te;
+    }
   }
   __syncthreads();
-  if (mode == kCand) {
-    const int n = (int)min(fetch32(&st[kCandCount]), (uint32_t)kCandCap);
-    const uint64_t* cand = a.tw.cand + (int64_t)ri.r_local * kCandCap;
-    for (int i = threadIdx.x; i < n; i += kThreads) cl[i] = fetch64(&cand[i]);
-    __syncthreads();
-    const uint64_t cstar = select_composite(cl, n, need, h, scratch, res);
-    for (int i = threadIdx.x; i < n; i += kThreads)
-      if (cl[i] >= cstar) {
-        const uint32_t pos = 0xFFFFFFFFu - (uint32_t)cl[i];
-        atomicAdd(&sel_cnt[min(pos / (uint32_t)a.tw.slice, 255u)], 1u);
-      }
-    __syncthreads();
-    T = (uint32_t)(cstar >> 32);
-    PT = 0xFFFFFFFFu - (uint32_t)cstar;
-    need_eq = 0xFFFFFFFFu;
-  } else {
-    if (mode == kTie) {
-      T = lo_b;
-    } else {
-      // refine inside bin b* over the whole row, then count per slice
-      T = select_in_row(sc, ri.L, lo_b, hi_b, need, h, scratch, res);
-      for (int j = 0; j < n_sl; ++j) {
-        const int a0 = j * a.tw.slice, a1 = min(ri.L, a0 + a.tw.slice);
-        uint32_t g = 0, e = 0;
-        for (int i = a0 + threadIdx.x; i < a1; i += kThreads) {
-          const uint32_t k = score_key(sc[i]);
-          g += k > T ? 1u : 0u;
-          e += k == T ? 1u : 0u;
-        }
-        uint32_t tg, te;
-        block_exclusive_scan(g, scratch, tg);
-        block_exclusive_scan(e, scratch, te);
-        if (threadIdx.x == 0) {
-          sl_a[j] = tg;
-          sel_cnt[j] = te;
-        }
-      }
-      __syncthreads();
-    }
-    need_eq = need;
-    PT = 0x7FFFFFFFu;
-  }
-  // output offsets: slices in order; in the tie modes the budget of keys
-  // equal to T is spent in position order
-  const bool ties = mode != kCand;
+  // output offsets: slices in order, the budget of keys equal to T spent in
+  // position order
   if (threadIdx.x == 0) {
     res[2] = 0;
     res[3] = 0;
@@ -470,17 +496,16 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkLaunch a) {
   __syncthreads();
   for (int c0 = 0; c0 < n_sl; c0 += kThreads) {
     const int j = c0 + threadIdx.x;
-    const uint32_t e = (j < n_sl && ties) ? sel_cnt[j] : 0u;
+    const uint32_t e = j < n_sl ? sel_cnt[j] : 0u;
     uint32_t te;
     const uint32_t eqb = res[3] + block_exclusive_scan(e, scratch, te);
-    const uint32_t take = ties ? (eqb >= need_eq ? 0u : min(e, need_eq - eqb))
-                               : (j < n_sl ? sel_cnt[j] : 0u);
+    const uint32_t take = eqb >= need ? 0u : min(e, need - eqb);
     const uint32_t cnt = j < n_sl ? sl_a[j] + take : 0u;
     uint32_t tot;
     const uint32_t ex = block_exclusive_scan(cnt, scratch, tot);
     if (j < n_sl) {
       a.tw.s_off[rs + j] = res[2] + ex;
-      a.tw.s_eqb[rs + j] = ties ? eqb : 0u;
+      a.tw.s_eqb[rs + j] = eqb;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -491,14 +516,36 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkLaunch a) {
   }
   if (threadIdx.x == 0) {
     st[kT] = T;
-    st[kPT] = PT;
-    st[kNeedEq] = need_eq;
+    st[kNeedEq] = need;
   }
 }
 
 // -------------------------------------------------------------- 3. compact
+// Every workgroup first settles the selection rule for itself -- the
+// threshold key T with its position cut P_T or tie budget, and its own first
+// output slot -- from the per-slice counts and the candidate list (a few
+// dozen composites in the usual case), so no workgroup of the previous
+// kernel has to wait for the others:
+//   composite mode: C* = the need-th largest candidate; keep key > T, or
+//     key == T and position <= P_T; offset = keys above b* in earlier slices
+//     + chosen candidates at earlier positions;
+//   tie mode: T = the single key of b*; keep key > T, or key == T while
+//     fewer than `need` such keys precede it; offset = keys above T in
+//     earlier slices + min(need, keys equal to T in earlier slices);
+//   fallback: all of it was set by the last workgroup of the cand kernel.
+// Positions are then visited kPass at a time, thread t taking positions
+// base + j*kThreads + t (j < kPer): every load is coalesced and issued
+// before any is used.  Output order is position order, i.e. (j, wave, lane);
+// ballots give the order inside a wave and per-wave counts in LDS the order
+// across waves.
 __global__ __launch_bounds__(kThreads) void topk_compact_kernel(TopkLaunch a) {
+  __shared__ uint32_t wcnt[2][kPer][kWaves];  // per pass row and wave: [0] ties, [1] kept
+  __shared__ uint64_t cl[kCandCap];
+  __shared__ uint32_t h[kTopkBins];
   __shared__ uint32_t scratch[2 * kWaves];
+  __shared__ uint32_t res[4];
+  __shared__ uint64_t pick;
+  __shared__ uint32_t pre[2];
   const RowInfo ri = row_info(a);
   const int K = a.K;
   const int s = blockIdx.x;
@@ -514,41 +561,144 @@ __global__ __launch_bounds__(kThreads) void topk_compact_kernel(TopkLaunch a) {
   const int start = s * a.tw.slice;
   if (start >= ri.L) return;
   const int end = min(ri.L, start + a.tw.slice);
-  const uint32_t* st = a.tw.state + (int64_t)ri.r_local * kStateWords;
-  const uint32_t T = st[kT], PT = st[kPT], need_eq = st[kNeedEq];
-  const int64_t rs = (int64_t)ri.r_local * a.tw.n_slices;
-  const uint32_t off0 = a.tw.s_off[rs + s];
-  const uint32_t eqb0 = a.tw.s_eqb[rs + s];
+  const int n_sl = (ri.L + a.tw.slice - 1) / a.tw.slice;
   const float* sc = a.scores + (int64_t)ri.r_local * a.ld;
+  const int64_t rs = (int64_t)ri.r_local * a.tw.n_slices;
+  const uint32_t* st = a.tw.state + (int64_t)ri.r_local * kStateWords;
+  const uint64_t* cand = a.tw.cand + (int64_t)ri.r_local * kCandCap;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
 
-  // each thread owns a contiguous run of `per` positions
-  const int per = (a.tw.slice + kThreads - 1) / kThreads;
-  const int i0 = start + threadIdx.x * per;
-  const int i1 = min(end, i0 + per);
-  uint32_t n_eq = 0;
-  if (need_eq != 0xFFFFFFFFu)
-    for (int i = i0; i < i1; ++i) n_eq += score_key(sc[i]) == T ? 1u : 0u;
-  uint32_t tot;
-  uint32_t eq_rank = eqb0 + block_exclusive_scan(n_eq, scratch, tot);
-  uint32_t n_sel = 0;
-  {
-    uint32_t er = eq_rank;
-    for (int i = i0; i < i1; ++i) {
-      const uint32_t k = score_key(sc[i]);
-      const bool eq = k == T;
-      n_sel += (k > T || (eq && (uint32_t)i <= PT && er < need_eq)) ? 1u : 0u;
-      er += eq ? 1u : 0u;
+  // one trip for everything: this slice's first keys, the row state, every
+  // slice's counts and the first kThreads candidate slots (read whether
+  // filled or not: the slots always exist)
+  uint32_t k0[kPer];
+  load_pass(sc, start, end, k0);
+  const uint32_t mode = st[kMode];
+  const uint32_t n_cand = st[kCandCount];
+  static_assert(kThreads == 256, "one slice per thread");
+  const uint32_t sd = tid < n_sl ? a.tw.s_def[rs + tid] : 0u;
+  const uint32_t se = tid < n_sl ? a.tw.s_eq[rs + tid] : 0u;
+  const uint64_t c0 = cand[tid];
+
+  uint32_t T, PT, need_eq, off, eqb;
+  if (mode == kFallback) {
+    T = st[kT];
+    PT = 0x7FFFFFFFu;
+    need_eq = st[kNeedEq];
+    off = a.tw.s_off[rs + s];
+    eqb = a.tw.s_eqb[rs + s];
+  } else {
+    const uint32_t need = (uint32_t)K - st[kAbove];
+    // keys above b* (and, tie mode, keys equal to T) in the slices before s
+    uint32_t t1, t2;
+    const uint32_t ex_d = block_exclusive_scan(sd, scratch, t1);
+    const uint32_t ex_e = block_exclusive_scan(se, scratch, t2);
+    if (tid == s) {
+      pre[0] = ex_d;
+      pre[1] = ex_e;
+    }
+    __syncthreads();
+    if (mode == kTie) {
+      T = st[kLoB];
+      PT = 0x7FFFFFFFu;
+      need_eq = need;
+      eqb = pre[1];
+      off = pre[0] + min(need, eqb);
+    } else {
+      const int n = (int)min(n_cand, (uint32_t)kCandCap);
+      cl[tid] = c0;
+      for (int i = kThreads + tid; i < n; i += kThreads) cl[i] = cand[i];
+      __syncthreads();
+      const uint64_t cstar = n <= kRankMax ? select_by_rank(cl, n, need, &pick)
+                                           : select_composite(cl, n, need, h, scratch, res);
+      T = (uint32_t)(cstar >> 32);
+      PT = 0xFFFFFFFFu - (uint32_t)cstar;
+      need_eq = 0xFFFFFFFFu;
+      eqb = 0;
+      // chosen candidates at positions before this slice
+      uint32_t c = 0;
+      for (int i = tid; i < n; i += kThreads)
+        c += (cl[i] >= cstar && 0xFFFFFFFFu - (uint32_t)cl[i] < (uint32_t)start) ? 1u : 0u;
+      c = wave_sum(c);
+      if (lane == 0) scratch[wave] = c;
+      __syncthreads();
+      uint32_t before = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) before += scratch[w];
+      off = pre[0] + before;
     }
   }
-  uint32_t at = off0 + block_exclusive_scan(n_sel, scratch, tot);
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t k = score_key(sc[i]);
-    const bool eq = k == T;
-    if (k > T || (eq && (uint32_t)i <= PT && eq_rank < need_eq)) {
-      if (at < (uint32_t)K) out[at] = i;
-      ++at;
+  const bool ties = need_eq != 0xFFFFFFFFu;
+
+  for (int base = start; base < end; base += kPass) {
+    uint32_t k[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) k[j] = k0[j];
+    if (base != start) load_pass(sc, base, end, k);
+    uint64_t me[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const bool ok = base + j * kThreads + tid < end;
+      me[j] = __ballot(ok && k[j] == T);
     }
-    eq_rank += eq ? 1u : 0u;
+    // rank among keys equal to T, in position order (tie modes only)
+    uint32_t eq_rank[kPer];
+    uint32_t eq_pass = 0;
+    if (ties) {
+      if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) wcnt[0][j][wave] = (uint32_t)__popcll(me[j]);
+      }
+      __syncthreads();
+      uint32_t run = eqb;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        uint32_t before = 0, all = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const uint32_t c = wcnt[0][j][w];
+          before += w < wave ? c : 0u;
+          all += c;
+        }
+        eq_rank[j] = run + before + (uint32_t)lane_prefix(me[j]);
+        run += all;
+      }
+      eq_pass = run - eqb;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) eq_rank[j] = 0;
+    }
+    uint64_t ms[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t i = (uint32_t)(base + j * kThreads + tid);
+      const bool ok = (int)i < end;
+      const bool eq = (me[j] >> lane) & 1u;
+      ms[j] = __ballot(ok && (k[j] > T || (eq && i <= PT && eq_rank[j] < need_eq)));
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) wcnt[1][j][wave] = (uint32_t)__popcll(ms[j]);
+    }
+    __syncthreads();
+    uint32_t run = off;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      uint32_t before = 0, all = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const uint32_t c = wcnt[1][j][w];
+        before += w < wave ? c : 0u;
+        all += c;
+      }
+      const uint32_t at = run + before + (uint32_t)lane_prefix(ms[j]);
+      if (((ms[j] >> lane) & 1u) && at < (uint32_t)K) out[at] = base + j * kThreads + tid;
+      run += all;
+    }
+    off = run;
+    eqb += eq_pass;
+    __syncthreads();  // wcnt is rewritten by the next pass
   }
 }
 
@@ -562,8 +712,8 @@ size_t topk_work_bytes(int rows, int64_t max_len) {
 TopkWork topk_work_carve(void* base, int rows, int64_t max_len) {
   TopkWork w;
   w.mm_tiles = (int)((max_len + kMMTile - 1) / kMMTile);
-  int64_t slice = 2048;
-  while ((max_len + slice - 1) / slice > 256) slice += 2048;
+  int64_t slice = kPass;
+  while ((max_len + slice - 1) / slice > 256) slice += kPass;
   w.slice = (int)slice;
   w.n_slices = (int)((max_len + slice - 1) / slice);
   auto r256 = [](size_t x) { return (x + 255) & ~size_t(255); };
