@@ -23,6 +23,13 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fvisibility=hidden", "-Wno-unused-command-line-argument",
 ]
+# Per-source additions.  The attention kernel's loop is bound by LDS-read
+# latency; the ILP-oriented machine scheduler keeps several reads in flight
+# ahead of their MFMAs where the default one issues each read just before
+# its use (measured: 27.6 vs 31.5 us for attention + combine on 4 x 131072).
+SOURCE_FLAGS = {
+    "sparse_attn.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
 
 
 def _run(cmd):
@@ -38,7 +45,8 @@ def build(verbose: bool = False) -> str:
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
-    cmds = [[HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    cmds = [[HIPCC, *FLAGS, *SOURCE_FLAGS.get(s, []), "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
     with ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():

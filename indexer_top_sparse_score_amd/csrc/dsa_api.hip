@@ -89,15 +89,20 @@ int status_of(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
 
 struct DecodeLayout {
   int rp;
-  size_t idx_off, scores_off, topk_off, part_off, total;
+  size_t idx_off, roff_off, scores_off, topk_off, part_off, total;
 };
 
+// The fused step hands the attention kernel the selected rows' byte offsets
+// (written by the Top-K compaction) for the latent 576-wide rows; the
+// workspace reserves them for every shape so its size does not depend on
+// the caches' strides.
 DecodeLayout decode_layout(const dsa_problem* p) {
   DecodeLayout d;
   d.rp = rows_per_pass(p);
   const int nc = attn_chunks(d.rp, p->H_q, p->D_qk, p->K);
   d.idx_off = kHeader;
-  d.scores_off = d.idx_off + round256((size_t)d.rp * p->K * sizeof(int32_t));
+  d.roff_off = d.idx_off + round256((size_t)d.rp * p->K * sizeof(int32_t));
+  d.scores_off = d.roff_off + round256((size_t)d.rp * p->K * sizeof(int64_t));
   d.topk_off = d.scores_off + round256((size_t)d.rp * max_len(p) * sizeof(float));
   d.part_off = d.topk_off + round256(topk_work_bytes(d.rp, max_len(p)));
   d.total = d.part_off + round256(attn_partial_bytes(d.rp, p->H_q, p->D_v, nc));
@@ -200,6 +205,8 @@ int dsa_topk(const dsa_problem* p, const float* scores, int64_t ld_scores, int32
   a.max_len = (int32_t)max_len(p);
   a.tw = topk_work_carve(static_cast<char*>(ws) + kHeader, p->num_rows, max_len(p));
   a.prep = true;
+  a.rowoff = nullptr;
+  a.kv = dsa_paged{};
   return status_of(launch_topk(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -224,6 +231,7 @@ static AttnLaunch attn_launch(const dsa_problem* p, const uint16_t* q, dsa_paged
   a.latent = is_latent(k, v);
   a.indices = nullptr;
   a.indices_row_offset = 0;
+  a.rowoff = nullptr;
   a.out = out;
   a.lse = lse;
   a.partial = nullptr;
@@ -253,7 +261,7 @@ int dsa_sparse_attn(const dsa_problem* p, const uint16_t* q, dsa_paged k, dsa_pa
   a.indices = indices;
   a.n_chunks = attn_chunks(p->num_rows, p->H_q, p->D_qk, p->K);
   a.partial = a.n_chunks > 1
-                  ? reinterpret_cast<float*>(static_cast<char*>(ws) + kHeader)
+                  ? static_cast<void*>(static_cast<char*>(ws) + kHeader)
                   : nullptr;
   return status_of(launch_sparse_attn(a, static_cast<hipStream_t>(stream)));
 }
@@ -281,6 +289,8 @@ int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa
   float* scores = reinterpret_cast<float*>(base + d.scores_off);
   const int64_t ld = max_len(p);
   const TopkWork tw = topk_work_carve(base + d.topk_off, d.rp, ld);
+  const bool use_rowoff = is_latent(k, v) && p->D_qk == 576;
+  int64_t* roff = reinterpret_cast<int64_t*>(base + d.roff_off);
 
   for (int row0 = 0; row0 < p->num_rows; row0 += d.rp) {
     const int nr = p->num_rows - row0 < d.rp ? p->num_rows - row0 : d.rp;
@@ -317,15 +327,18 @@ int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa
     ta.max_len = (int32_t)ld;
     ta.tw = tw;
     ta.prep = false;
+    ta.rowoff = use_rowoff ? roff : nullptr;
+    ta.kv = k;
     if ((st = status_of(launch_topk(ta, s))) != DSA_OK) return st;
 
     AttnLaunch aa = attn_launch(p, q, k, v, out, lse, err);
     aa.indices = idx;
     aa.indices_row_offset = 0;
+    aa.rowoff = use_rowoff ? roff : nullptr;
     aa.row_begin = row0;
     aa.num_rows = nr;
     aa.n_chunks = attn_chunks(d.rp, p->H_q, p->D_qk, p->K);  // the count the workspace was sized for
-    aa.partial = aa.n_chunks > 1 ? reinterpret_cast<float*>(base + d.part_off) : nullptr;
+    aa.partial = aa.n_chunks > 1 ? static_cast<void*>(base + d.part_off) : nullptr;
     if ((st = status_of(launch_sparse_attn(aa, s))) != DSA_OK) return st;
   }
   return DSA_OK;

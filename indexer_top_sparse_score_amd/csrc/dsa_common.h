@@ -123,6 +123,11 @@ struct TopkLaunch {
   int32_t max_len;
   TopkWork tw;
   bool prep;            // compute key ranges here (no fused indexer before)
+  // Optional: also write each kept position's byte offset in the paged KV
+  // cache `kv` (block table -> physical block), -1 for padding and for
+  // positions whose block id is out of range, to rowoff[num_rows][K].
+  int64_t* rowoff;
+  dsa_paged kv;
 };
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
 
@@ -133,9 +138,12 @@ struct AttnLaunch {
   bool latent;  // v aliases k (same base and strides)
   const int32_t* indices;
   int64_t indices_row_offset;  // indices row of row_begin
+  const int64_t* rowoff;       // optional [num_rows][K] byte offsets of the selected
+                               // rows (latent layout), -1 = absent; replaces the
+                               // index -> block table lookup
   uint16_t* out;
   float* lse;
-  float* partial;  // workspace for split-key partials, or NULL when n_chunks == 1
+  void* partial;   // workspace for split-key partials, or NULL when n_chunks == 1
   uint32_t* err;
   int32_t H_q, D_qk, D_v, K;
   float scale;

@@ -35,6 +35,12 @@
 #ifndef DSA_ATTN_MAX_CHUNKS
 #define DSA_ATTN_MAX_CHUNKS 16
 #endif
+#ifndef DSA_ATTN_LATENT_DMA
+#define DSA_ATTN_LATENT_DMA 1
+#endif
+#ifndef DSA_ATTN_NBUF
+#define DSA_ATTN_NBUF 4
+#endif
 #ifndef DSA_ATTN_TARGET_WGS
 #define DSA_ATTN_TARGET_WGS 256
 #endif
@@ -48,8 +54,20 @@ constexpr int kMaxChunk = 256; // index slots per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// floats per (row, chunk, head) partial record: O[DV], max, sum, 2 pad
-__host__ __device__ constexpr int part_stride(int dv) { return dv + 4; }
+// Split-key partials of a call: (max, sum) as float2 [rows][chunks][H_q],
+// then the chunk's normalised output O / sum as bf16 [rows][chunks][H_q][D_v]
+// (256-byte aligned).
+__host__ __device__ inline size_t part_stats_bytes(int rows, int chunks, int H_q) {
+  return ((size_t)rows * chunks * H_q * sizeof(float2) + 255) & ~size_t(255);
+}
+__device__ __forceinline__ float2* part_stats(const AttnLaunch& a, int row_local, int chunk) {
+  return reinterpret_cast<float2*>(a.partial) + ((int64_t)row_local * a.n_chunks + chunk) * a.H_q;
+}
+__device__ __forceinline__ uint16_t* part_out(const AttnLaunch& a, int row_local, int chunk, int DV) {
+  return reinterpret_cast<uint16_t*>(static_cast<char*>(a.partial) +
+                                     part_stats_bytes(a.num_rows, a.n_chunks, a.H_q)) +
+         ((int64_t)row_local * a.n_chunks + chunk) * a.H_q * DV;
+}
 
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
   __bf16 h = (__bf16)x;
@@ -76,6 +94,70 @@ __device__ __forceinline__ uint4 keep_or_zero(const uint4& x, bool keep) {
 // 32-bit word c of a 16-byte register group
 __device__ __forceinline__ uint32_t word(const uint4& x, int c) {
   return c == 0 ? x.x : c == 1 ? x.y : c == 2 ? x.z : x.w;
+}
+
+// Epilogue of one wave: lane (grp, cidx) holds O^T[16mt + 4grp + v][head]
+// in o[mt][v], the head's reference max m2 (log2 units) and its sum of
+// exponentials.  One chunk: out = O / sum (bf16) and lse; several: the
+// chunk's (max, sum) and O / sum as bf16 partials.
+template <int MT>
+__device__ __forceinline__ void write_result(const AttnLaunch& a, int r, int row_local, int chunk,
+                                             int head, int grp, const v4f* o, float m2, float lsum) {
+  constexpr int DV = 16 * MT;
+  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  uint16_t* dst = a.n_chunks == 1 ? a.out + ((int64_t)r * a.H_q + head) * DV
+                                  : part_out(a, row_local, chunk, DV) + (int64_t)head * DV;
+  dst += 4 * grp;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    uint2 w;
+    w.x = pack2(o[mt][0] * inv, o[mt][1] * inv);
+    w.y = pack2(o[mt][2] * inv, o[mt][3] * inv);
+    *reinterpret_cast<uint2*>(dst + 16 * mt) = w;
+  }
+  if (grp != 0) return;
+  if (a.n_chunks == 1) {
+    if (a.lse)
+      a.lse[(int64_t)r * a.H_q + head] = lsum > 0.0f ? (m2 + log2f(lsum)) * kLn2 : -__builtin_inff();
+  } else {
+    part_stats(a, row_local, chunk)[head] = float2{lsum > 0.0f ? m2 : -__builtin_inff(), lsum};
+  }
+}
+
+// The same results written through LDS, so that every global store is a
+// whole 1 KB head row (64 lanes x 16 B) rather than 16 scattered 32-byte
+// pieces: the wave's 16 x 512 bf16 go to `stage` (16 rows, pitch 1040 B to
+// spread the banks) and come back one head row per instruction.  `stage` is
+// this wave's own 16.25 KB of LDS; nothing else may use it meanwhile.
+__device__ __forceinline__ void write_result_staged(const AttnLaunch& a, int r, int row_local,
+                                                    int chunk, int head0, int lane, const v4f* o,
+                                                    float m2, float lsum, uint8_t* stage) {
+  constexpr int DV = 512, MT = DV / 16, kPitch = 2 * DV + 16;
+  const int cidx = lane & 15, grp = lane >> 4;
+  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    uint2 w;
+    w.x = pack2(o[mt][0] * inv, o[mt][1] * inv);
+    w.y = pack2(o[mt][2] * inv, o[mt][3] * inv);
+    *reinterpret_cast<uint2*>(stage + cidx * kPitch + 2 * (16 * mt + 4 * grp)) = w;
+  }
+  uint16_t* dst = a.n_chunks == 1 ? a.out + ((int64_t)r * a.H_q + head0) * DV
+                                  : part_out(a, row_local, chunk, DV) + (int64_t)head0 * DV;
+  const int nh = min(kHPW, a.H_q - head0);
+#pragma unroll
+  for (int h = 0; h < kHPW; ++h)
+    if (h < nh)
+      *reinterpret_cast<uint4*>(dst + (int64_t)h * DV + 8 * lane) =
+          *reinterpret_cast<const uint4*>(stage + h * kPitch + 16 * lane);
+  const int head = head0 + cidx;
+  if (grp != 0 || cidx >= nh) return;
+  if (a.n_chunks == 1) {
+    if (a.lse)
+      a.lse[(int64_t)r * a.H_q + head] = lsum > 0.0f ? (m2 + log2f(lsum)) * kLn2 : -__builtin_inff();
+  } else {
+    part_stats(a, row_local, chunk)[head] = float2{lsum > 0.0f ? m2 : -__builtin_inff(), lsum};
+  }
 }
 
 struct AttnGrid {
@@ -354,33 +436,342 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
   lsum += __shfl_xor(lsum, 32);
   if (!head_ok) return;
 
-  if (a.n_chunks == 1) {
-    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-    uint16_t* orow = a.out + ((int64_t)r * a.H_q + head) * DV + 4 * grp;
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) {
-      uint2 w;
-      w.x = pack2(o[mt][0] * inv, o[mt][1] * inv);
-      w.y = pack2(o[mt][2] * inv, o[mt][3] * inv);
-      *reinterpret_cast<uint2*>(orow + 16 * mt) = w;
-    }
-    if (a.lse && grp == 0)
-      a.lse[(int64_t)r * a.H_q + head] = lsum > 0.0f ? (m2 + log2f(lsum)) * kLn2 : -__builtin_inff();
-  } else {
-    float* part = a.partial +
-                  (((int64_t)row_local * a.n_chunks + chunk) * a.H_q + head) * part_stride(DV);
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
-      *reinterpret_cast<v4f*>(part + 16 * mt + 4 * grp) = o[mt];
-    if (grp == 0) {
-      part[DV] = m2;
-      part[DV + 1] = lsum;
-    }
+  write_result<C::MT>(a, r, row_local, chunk, head, grp, o, m2, lsum);
+}
+
+// ---------------------------------------------------------------------------
+// Latent rows (576 bf16 = 1152 B; V = the first 512 elements): the gathered
+// rows move HBM -> LDS by DMA (global_load_lds, 16 B per lane, no staging
+// registers), NBUF sub-blocks deep, and both MFMA operands are read from the
+// one key-major tile: the K rows as they are for the logits, and V^T through
+// the transposing LDS read (ds_read_b64_tr_b16).
+//
+// Tile of a sub-block: 32 rows x 72 pieces of 16 B, piece p of row r at
+// slot r*72 + (p ^ (r & 7)) -- the XOR keeps both the logit reads (16 rows,
+// same piece) and the transposing reads (4 rows x 4 dim groups) within two
+// lanes per bank.  DMA instruction i of a sub-block fills slots 64i..64i+63
+// (lane l -> slot 64i + l), so each wave issues exactly kDmaPerWave of them
+// per sub-block and waits on them with a fixed vmcnt.
+//
+// Transposing read: within each 16-lane group, lane j names 4 consecutive
+// bf16 e_j[0..3]; lane i receives e_{i/4 + 4k}[i % 4] for k = 0..3.  With
+// lane j naming row 4g + j/4 (key) and dims 16mt + 4(j%4) .. +3, lane i of
+// group g gets V[4g + k][16mt + i], k = 0..3: the A operand of
+// O^T += V^T . P^T in the contraction order the S^T accumulators hold.
+namespace lat {
+constexpr int kDqk = 576, kDv = 512, kNW = 4;
+constexpr int kPieces = kDqk * 2 / 16;             // 72
+constexpr int kTileBytes = kSB * kPieces * 16;     // 36864
+constexpr int kDmaPerWave = kSB * kPieces / 64 / kNW;  // 9
+constexpr int kKS = kDqk / 32;                     // 18
+constexpr int kMT = kDv / 16;                      // 32
+static_assert(kSB * kPieces % (64 * kNW) == 0, "DMA instructions per wave");
+__device__ __forceinline__ int slot(int row, int piece) { return row * kPieces + (piece ^ (row & 7)); }
+}  // namespace lat
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// One 16-byte-per-lane DMA, global -> LDS (lane l lands at lds + 16 l).
+// Issued through inline asm on purpose: with the builtin, the compiler makes
+// every later LDS read wait for all DMAs in flight (vmcnt(0)), since it
+// cannot tell the buffers apart, which would serialise the prefetch.  The
+// caller orders the tile accesses itself (wait_vm + barrier).  M0 carries
+// the LDS address and is restored; the s_nop is the wait state an M0 write
+// needs before an LDS DMA reads it.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+
+__device__ __forceinline__ void wait_vm(int n) {
+  // n is one of the few counts the caller can have in flight
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1 * lat::kDmaPerWave: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+    case 2 * lat::kDmaPerWave: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(27)" ::: "memory"); break;
   }
 }
 
-// Merges the per-chunk (max, sum, unnormalised O) of each (row, head): one
-// wave per head; lane c holds chunk c's statistics.
+template <int NBUF>
+__global__ __launch_bounds__(64 * lat::kNW, 1) void sparse_attn_latent_kernel(AttnLaunch a, AttnGrid g) {
+  static_assert(NBUF >= 2 && NBUF <= 4, "vmcnt cases");
+  static_assert(lat::kNW * 16 * (2 * lat::kDv + 16) <= NBUF * lat::kTileBytes,
+                "epilogue staging fits the tiles");
+  using namespace lat;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[NBUF][kTileBytes];
+  __shared__ int64_t koff[kMaxChunk];
+
+  int unit, hg;
+  if (!decode_wg(g, unit, hg)) return;
+  const int r = a.row_begin + unit / a.n_chunks;
+  const int chunk = unit % a.n_chunks;
+  const int row_local = r - a.row_begin;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cidx = lane & 15, grp = lane >> 4;
+
+  int b = 0, p = -1;
+  if (!resolve_row(a.rows, r, b, p)) {
+    p = -1;
+    if (chunk == 0 && hg == 0 && tid == 0) report(a.err, DSA_DEVERR_ROW);
+  }
+  const int slot0 = chunk * g.chunk;
+  const int n_slots = max(0, min(a.K, slot0 + g.chunk) - slot0);
+  const int nsb = (n_slots + kSB - 1) / kSB;
+
+  // Q^T operand: this lane's head, 8 dims per MFMA step (issued first: the
+  // loads overlap the prologue's dependent index -> block-table loads)
+  const int head = hg * (kHPW * kNW) + wave * kHPW + cidx;
+  const bool head_ok = head < a.H_q;
+  v8s qb[kKS];
+  {
+    const uint16_t* qrow = a.q + ((int64_t)r * a.H_q + (head_ok ? head : 0)) * kDqk + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      const v8s x = *reinterpret_cast<const v8s*>(qrow + 32 * ks);
+      qb[ks] = head_ok ? x : v8s{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+
+  // ---- prologue: every index of the chunk -> row byte offset (-1: absent);
+  //      ready-made when the Top-K compaction wrote them
+  if (a.rowoff) {
+    const int64_t* ro = a.rowoff + (int64_t)row_local * a.K + slot0;
+    for (int i = tid; i < nsb * kSB; i += 64 * kNW) koff[i] = i < n_slots && p >= 0 ? ro[i] : -1;
+  } else {
+    const int32_t* idx_row = a.indices + (a.indices_row_offset + row_local) * (int64_t)a.K;
+    const int32_t* bt = a.rows.block_table + (int64_t)b * a.rows.max_blocks;
+    for (int i = tid; i < nsb * kSB; i += 64 * kNW) {
+      int64_t ko = -1;
+      if (i < n_slots && p >= 0) {
+        const int idx = idx_row[slot0 + i];
+        if (idx >= 0 && idx <= p) {
+          const int phys = bt[idx >> 6];
+          if (phys >= 0 && (int64_t)phys < a.k.num_blocks)
+            ko = (int64_t)phys * a.k.block_stride + (int64_t)(idx & 63) * a.k.row_stride;
+          else
+            report(a.err, DSA_DEVERR_BLOCK);
+        } else if (idx != -1) {
+          report(a.err, DSA_DEVERR_INDEX);
+        }
+      }
+      koff[i] = ko;
+    }
+  }
+
+  __syncthreads();
+
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k.base);
+  // DMA of sub-block sb: this wave's instructions t = 0..kDmaPerWave-1 fill
+  // slots 64*(wave*kDmaPerWave + t) + lane.  Absent rows read row 0 of block
+  // 0 (which always exists) and are zeroed after they land.
+  auto issue = [&](int sb) {
+    uint8_t* buf = tile[sb % NBUF];
+#pragma unroll
+    for (int t = 0; t < kDmaPerWave; ++t) {
+      const int i = wave * kDmaPerWave + t;
+      const int sl = 64 * i + lane;
+      const int row = sl / kPieces;
+      const int piece = (sl - row * kPieces) ^ (row & 7);
+      const int64_t off = koff[sb * kSB + row];
+      dma16(kbase + (off >= 0 ? off : 0) + 16 * piece, (uint32_t)(uintptr_t)(buf + 1024 * i));
+    }
+  };
+  auto zero_absent = [&](int sb) {
+    uint8_t* buf = tile[sb % NBUF];
+#pragma unroll
+    for (int t = 0; t < kDmaPerWave; ++t) {
+      const int i = wave * kDmaPerWave + t;
+      const int sl = 64 * i + lane;
+      if (koff[sb * kSB + sl / kPieces] < 0)
+        *reinterpret_cast<uint4*>(buf + 16 * sl) = uint4{0u, 0u, 0u, 0u};
+    }
+  };
+
+  const float c2 = a.scale * kLog2e;
+
+  // Per-lane tile offsets.  Logits: lane (grp, cidx) reads row 16kt + cidx,
+  // piece 4kk + grp; the XOR touches only the low 3 bits of the piece, so
+  // the piece's slot is 8(kk/2) + ((4(kk&1) + grp) ^ (row & 7)).  P.V: lane
+  // reads rows rlo, rlo + 16 and piece 2mt + h, i.e. slot
+  // 8(mt/4) + ((2(mt&3) + h) ^ (rlo & 7)), plus `within` bytes.
+  constexpr int kRow16 = 16 * kPieces * 16;  // bytes of 16 tile rows
+  const int r7 = cidx & 7;
+  const int s_even = 16 * (cidx * kPieces + (grp ^ r7));
+  const int s_odd = 16 * (cidx * kPieces + ((4 + grp) ^ r7));
+  int v_base[4];
+  {
+    const int rlo = 4 * grp + (cidx >> 2);
+    const int h = (cidx & 3) >> 1, within = (cidx & 1) * 8;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v_base[q] = 16 * (rlo * kPieces + ((2 * q + h) ^ (rlo & 7))) + within;
+  }
+
+  // Softmax reference.  The exponentials are taken against a fixed
+  // per-head reference m2, so the accumulators are only ever touched by
+  // MFMAs (a rescale would need every accumulator in VGPRs).  First pass:
+  // m2 = the head's max over the first sub-block with a valid key.  Should a
+  // later logit exceed it by more than kSlack (log2 units; exponentials stay
+  // <= 2^kSlack otherwise), the workgroup runs the chunk again with m2 = the
+  // true chunk max, which the first pass has collected by then.  Any
+  // reference gives the same softmax; lse uses the same one.
+  constexpr float kSlack = 16.0f;
+  v4f o[kMT];
+  float m2 = -__builtin_inff();
+  float lsum = 0.0f;   // this lane's share of the sum of exponentials
+  float m_fix = -__builtin_inff();
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) o[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    m2 = m_fix;
+    lsum = 0.0f;
+    float m_all = -__builtin_inff();  // the head's max over every logit seen
+    bool over = false;                // (wave) a logit exceeded m2 + kSlack
+
+    for (int sb = 0; sb < min(NBUF - 1, nsb); ++sb) issue(sb);
+    for (int sb = 0; sb < nsb; ++sb) {
+      wait_vm(kDmaPerWave * min(nsb - 1 - sb, NBUF - 2));
+      const uint32_t valid =
+          (uint32_t)__ballot(lane < kSB && koff[sb * kSB + (lane & (kSB - 1))] >= 0);
+      if (valid != 0xFFFFFFFFu) zero_absent(sb);
+      // every wave's DMAs of sb have landed, and every wave is done with the
+      // buffer the next DMA overwrites (last read in sub-block sb-1)
+      __syncthreads();
+      if (sb + NBUF - 1 < nsb) issue(sb + NBUF - 1);
+
+      // No early exit below: every sub-block runs its MFMAs (a sub-block
+      // without a valid key, or after an overrun, adds P = 0), so the
+      // accumulators have one producer and stay in AGPRs across the loop.
+      const uint8_t* buf = tile[sb % NBUF];
+      // ---- logits S^T (keys x heads): two 16-key tiles; every read is one
+      //      of two per-lane bases plus an immediate offset
+      // The two tiles' MFMA chains alternate, so consecutive MFMAs are
+      // independent; the group barriers keep the LDS reads kPre ahead.
+      __builtin_amdgcn_sched_barrier(0);
+      v4f s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int kk = 0; kk < kKS; ++kk)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const v8s ka = *reinterpret_cast<const v8s*>(buf + ((kk & 1) ? s_odd : s_even) +
+                                                       128 * (kk >> 1) + kt * kRow16);
+          s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(v8bf, ka), __builtin_bit_cast(v8bf, qb[kk]), s[kt], 0, 0, 0);
+        }
+      {
+        constexpr int kPre = 6, kN = 2 * kKS;
+        __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);  // DS reads
+#pragma unroll
+        for (int i = 0; i < kN - kPre; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- softmax for this lane's head over keys 16kt + 4grp + v
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int key = 16 * kt + 4 * grp + v;
+          const float x = ((valid >> key) & 1u) ? s[kt][v] * c2 : -__builtin_inff();
+          s[kt][v] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));  // -inf only without a valid key
+      m_all = fmaxf(m_all, mx);
+      if (m2 == -__builtin_inff()) m2 = mx;
+      over = over || __ballot(mx > m2 + kSlack) != 0;
+      // past an overrun the pass only collects m_all
+      float pv[8];
+      float psum = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float x = s[kt][v];
+          const float e = (over || x == -__builtin_inff()) ? 0.0f : exp2f(x - m2);
+          pv[kt * 4 + v] = e;
+          psum += e;
+        }
+      lsum += psum;
+      const v8bf pb = __builtin_bit_cast(
+          v8bf, (uint4){pack2(pv[0], pv[1]), pack2(pv[2], pv[3]), pack2(pv[4], pv[5]),
+                        pack2(pv[6], pv[7])});
+      // ---- O^T += V^T . P^T, V^T read transposed from the key-major tile;
+      //      rows rlo and rlo + 16 share their swizzle, so every read is one
+      //      of four per-lane bases plus an immediate offset
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) {
+        const uint8_t* at = buf + v_base[mt & 3] + 128 * (mt >> 2);
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)at);
+        const v4s hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(at + kRow16));
+        const v8s va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, va), pb, o[mt], 0, 0, 0);
+      }
+      {
+        constexpr int kPre = 4;  // MFMAs' worth of reads in flight
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPre, 0);
+#pragma unroll
+        for (int i = 0; i < kMT - kPre; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the last iteration waited for every DMA; the barrier also makes the
+    // buffers free for a second pass
+    if (!__syncthreads_or(over)) break;
+    m_fix = m_all;
+  }
+
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  // every wave is past the last barrier and every DMA has landed: the tile
+  // buffers are free for staging (16.25 KB per wave)
+  const int head0 = hg * (kHPW * kNW) + wave * kHPW;
+  if (head0 >= a.H_q) return;
+  write_result_staged(a, r, row_local, chunk, head0, lane, o, m2, lsum,
+                      &tile[0][0] + wave * (16 * (2 * kDv + 16)));
+}
+
+// PER consecutive bf16 values as floats (16-byte load when PER == 8)
+template <int PER>
+__device__ __forceinline__ void load_bf16(const uint16_t* p, float* x) {
+  if constexpr (PER == 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) x[i] = __uint_as_float((uint32_t)p[i] << 16);
+  }
+}
+
+// Merges the chunks of each (row, head): one wave per head; lane c holds
+// chunk c's (max, sum).  With M the largest max, chunk c weighs
+// w_c = sum_c * 2^(max_c - M); out = sum_c w_c O_c / sum_c w_c, where O_c
+// is the chunk's normalised output.
 template <int DV>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   constexpr int PER = DV / 64;  // dims per lane
@@ -390,46 +781,48 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   const int lane = threadIdx.x & 63;
   if (head >= a.H_q) return;
   const int n = a.n_chunks;  // <= 64
-  const float* part0 = a.partial + ((int64_t)row_local * n * a.H_q + head) * part_stride(DV);
-  const int64_t cstride = (int64_t)a.H_q * part_stride(DV);
-  const float mc = lane < n ? part0[lane * cstride + DV] : -__builtin_inff();
-  const float lc = lane < n ? part0[lane * cstride + DV + 1] : 0.0f;
-  float M = mc;
+  const float2 st = lane < n ? part_stats(a, row_local, lane)[head] : float2{-__builtin_inff(), 0.0f};
+  const uint16_t* o0 = part_out(a, row_local, 0, DV) + (int64_t)head * DV + lane * PER;
+  const int64_t cstride = (int64_t)a.H_q * DV;
+  float M = st.x;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.0f;
-  float Ls = 0.0f;
-  if (M != -__builtin_inff()) {
-    const float f = mc == -__builtin_inff() ? 0.0f : exp2f(mc - M);
-    Ls = lc * f;
+  // no branch on M: with every chunk empty all weights are 0, and the
+  // output loads below need not wait for the statistics
+  const float f = st.x == -__builtin_inff() ? 0.0f : st.y * exp2f(st.x - M);
+  float Ls = f;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) Ls += __shfl_xor(Ls, o);
-    int c = 0;
-    for (; c + 4 <= n; c += 4) {
-      float x[4][PER];
+  for (int o = 32; o > 0; o >>= 1) Ls += __shfl_xor(Ls, o);
+  // kBatch chunks per round trip: every load of a batch is issued before
+  // any is used (chunks past n reload the last one with weight 0)
+  constexpr int kBatch = 16;
+  for (int c0 = 0; c0 < n; c0 += kBatch) {
+    float x[kBatch][PER];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < kBatch; ++u) load_bf16<PER>(o0 + min(c0 + u, n - 1) * cstride, x[u]);
 #pragma unroll
-        for (int i = 0; i < PER; ++i) x[u][i] = part0[(c + u) * cstride + lane * PER + i];
+    for (int u = 0; u < kBatch; ++u) {
+      const float fu = c0 + u < n ? __shfl(f, c0 + u) : 0.0f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float fu = __shfl(f, c + u);
-#pragma unroll
-        for (int i = 0; i < PER; ++i) acc[i] += x[u][i] * fu;
-      }
-    }
-    for (; c < n; ++c) {
-      const float fu = __shfl(f, c);
-#pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] += part0[c * cstride + lane * PER + i] * fu;
+      for (int i = 0; i < PER; ++i) acc[i] += x[u][i] * fu;
     }
   }
   const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
   uint16_t* orow = a.out + ((int64_t)r * a.H_q + head) * DV + lane * PER;
+  if constexpr (PER == 8) {
+    uint4 w;
+    w.x = pack2(acc[0] * inv, acc[1] * inv);
+    w.y = pack2(acc[2] * inv, acc[3] * inv);
+    w.z = pack2(acc[4] * inv, acc[5] * inv);
+    w.w = pack2(acc[6] * inv, acc[7] * inv);
+    *reinterpret_cast<uint4*>(orow) = w;
+  } else {
 #pragma unroll
-  for (int i = 0; i < PER; ++i) orow[i] = bf16_bits(acc[i] * inv);
+    for (int i = 0; i < PER; ++i) orow[i] = bf16_bits(acc[i] * inv);
+  }
   if (a.lse && lane == 0)
     a.lse[(int64_t)r * a.H_q + head] = Ls > 0.0f ? (M + log2f(Ls)) * kLn2 : -__builtin_inff();
 }
@@ -446,7 +839,9 @@ hipError_t launch_t(const AttnLaunch& a, hipStream_t s) {
   const int per = (a.K + a.n_chunks - 1) / a.n_chunks;
   g.chunk = (per + kSB - 1) / kSB * kSB;
   const int grid = (g.n_units + 7) / 8 * 8 * g.n_hg;
-  if (a.latent)
+  if (DSA_ATTN_LATENT_DMA && a.latent && DQK == lat::kDqk && NW == lat::kNW)
+    sparse_attn_latent_kernel<DSA_ATTN_NBUF><<<grid, 64 * NW, 0, s>>>(a, g);
+  else if (a.latent)
     sparse_attn_kernel<DQK, DV, true, NW><<<grid, 64 * NW, 0, s>>>(a, g);
   else
     sparse_attn_kernel<DQK, DV, false, NW><<<grid, 64 * NW, 0, s>>>(a, g);
@@ -470,7 +865,7 @@ int attn_chunks(int num_rows, int H_q, int D_qk, int K) {
 
 size_t attn_partial_bytes(int num_rows, int H_q, int D_v, int n_chunks) {
   if (n_chunks <= 1) return 0;
-  return (size_t)num_rows * n_chunks * H_q * part_stride(D_v) * sizeof(float);
+  return part_stats_bytes(num_rows, n_chunks, H_q) + (size_t)num_rows * n_chunks * H_q * D_v * 2;
 }
 
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s) {

@@ -50,15 +50,27 @@ static_assert((1 << kBinBits) == kTopkBins, "bins");
 struct RowInfo {
   int L;       // history length (0: invalid row)
   int r_local; // row index within the call
+  int b;       // sequence (valid when L > 0)
 };
 
 __device__ __forceinline__ RowInfo row_info(const TopkLaunch& a) {
   RowInfo ri;
   ri.r_local = (int)blockIdx.y;
-  int b, p;
+  int b = 0, p;
   const int r = a.row_begin + ri.r_local;
   ri.L = resolve_row(a.rows, r, b, p) ? p + 1 : 0;
+  ri.b = b;
   return ri;
+}
+
+// Byte offset of position i's row in the paged KV cache, given its block id
+// (-1, and an error report, when the id is out of range).
+__device__ __forceinline__ int64_t kv_offset(const TopkLaunch& a, int i, int phys) {
+  if (phys < 0 || (int64_t)phys >= a.kv.num_blocks) {
+    report(a.err, DSA_DEVERR_BLOCK);
+    return -1;
+  }
+  return (int64_t)phys * a.kv.block_stride + (int64_t)(i & 63) * a.kv.row_stride;
 }
 
 // Cross-workgroup hand-off inside one kernel, without full-L2 fences: the
@@ -546,16 +558,25 @@ __global__ __launch_bounds__(kThreads) void topk_compact_kernel(TopkLaunch a) {
   __shared__ uint32_t res[4];
   __shared__ uint64_t pick;
   __shared__ uint32_t pre[2];
+  __shared__ int32_t blk[kPass / 64];  // block ids of the current pass (rowoff only)
   const RowInfo ri = row_info(a);
   const int K = a.K;
   const int s = blockIdx.x;
   int32_t* out = a.indices + (int64_t)ri.r_local * K;
+  int64_t* roff = a.rowoff ? a.rowoff + (int64_t)ri.r_local * K : nullptr;
+  const int32_t* bt = a.rows.block_table + (int64_t)ri.b * a.rows.max_blocks;
   if (s == 0 && threadIdx.x == 0 && a.counts) a.counts[ri.r_local] = min(K, ri.L);
   if (ri.L <= K) {
     const int a0 = s * a.tw.slice, a1 = min(ri.L, a0 + a.tw.slice);
-    for (int j = a0 + threadIdx.x; j < a1; j += kThreads) out[j] = j;
+    for (int j = a0 + threadIdx.x; j < a1; j += kThreads) {
+      out[j] = j;
+      if (roff) roff[j] = kv_offset(a, j, bt[j >> 6]);
+    }
     if (s == 0)
-      for (int j = ri.L + threadIdx.x; j < K; j += kThreads) out[j] = -1;
+      for (int j = ri.L + threadIdx.x; j < K; j += kThreads) {
+        out[j] = -1;
+        if (roff) roff[j] = -1;
+      }
     return;
   }
   const int start = s * a.tw.slice;
@@ -574,6 +595,14 @@ __global__ __launch_bounds__(kThreads) void topk_compact_kernel(TopkLaunch a) {
   // filled or not: the slots always exist)
   uint32_t k0[kPer];
   load_pass(sc, start, end, k0);
+  // the pass's block ids travel with its keys
+  auto load_blocks = [&](int base) {
+    if (roff && tid < kPass / 64) {
+      const int bi = (base >> 6) + tid;
+      blk[tid] = bi <= (end - 1) >> 6 ? bt[bi] : -1;
+    }
+  };
+  load_blocks(start);
   const uint32_t mode = st[kMode];
   const uint32_t n_cand = st[kCandCount];
   static_assert(kThreads == 256, "one slice per thread");
@@ -635,7 +664,10 @@ __global__ __launch_bounds__(kThreads) void topk_compact_kernel(TopkLaunch a) {
     uint32_t k[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) k[j] = k0[j];
-    if (base != start) load_pass(sc, base, end, k);
+    if (base != start) {
+      load_pass(sc, base, end, k);
+      load_blocks(base);  // the previous pass's readers are past its final barrier
+    }
     uint64_t me[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
@@ -693,7 +725,11 @@ __global__ __launch_bounds__(kThreads) void topk_compact_kernel(TopkLaunch a) {
         all += c;
       }
       const uint32_t at = run + before + (uint32_t)lane_prefix(ms[j]);
-      if (((ms[j] >> lane) & 1u) && at < (uint32_t)K) out[at] = base + j * kThreads + tid;
+      if (((ms[j] >> lane) & 1u) && at < (uint32_t)K) {
+        const int i = base + j * kThreads + tid;
+        out[at] = i;
+        if (roff) roff[at] = kv_offset(a, i, blk[(i - base) >> 6]);
+      }
       run += all;
     }
     off = run;
