@@ -99,7 +99,7 @@ struct DecodeLayout {
 DecodeLayout decode_layout(const dsa_problem* p) {
   DecodeLayout d;
   d.rp = rows_per_pass(p);
-  const int nc = attn_chunks(d.rp, p->H_q, p->D_qk, p->K);
+  const int nc = attn_chunks_max(d.rp, p->H_q, p->D_qk, p->K);
   d.idx_off = kHeader;
   d.roff_off = d.idx_off + round256((size_t)d.rp * p->K * sizeof(int32_t));
   d.scores_off = d.roff_off + round256((size_t)d.rp * p->K * sizeof(int64_t));
@@ -139,7 +139,7 @@ size_t dsa_workspace_size(const dsa_problem* p, int op) {
       return kHeader + round256(topk_work_bytes(p->num_rows, max_len(p)));
     case DSA_OP_SPARSE_ATTN: {
       if (check_attn_shape(p) != DSA_OK) return 0;
-      const int nc = attn_chunks(p->num_rows, p->H_q, p->D_qk, p->K);
+      const int nc = attn_chunks_max(p->num_rows, p->H_q, p->D_qk, p->K);
       return kHeader + round256(attn_partial_bytes(p->num_rows, p->H_q, p->D_v, nc));
     }
     case DSA_OP_DECODE_STEP:
@@ -259,7 +259,7 @@ int dsa_sparse_attn(const dsa_problem* p, const uint16_t* q, dsa_paged k, dsa_pa
   if (p->num_rows == 0) return DSA_OK;
   AttnLaunch a = attn_launch(p, q, k, v, out, lse, static_cast<uint32_t*>(ws));
   a.indices = indices;
-  a.n_chunks = attn_chunks(p->num_rows, p->H_q, p->D_qk, p->K);
+  a.n_chunks = attn_chunks(p->num_rows, p->H_q, p->D_qk, p->K, a.latent);
   a.partial = a.n_chunks > 1
                   ? static_cast<void*>(static_cast<char*>(ws) + kHeader)
                   : nullptr;
@@ -337,7 +337,8 @@ int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa
     aa.rowoff = use_rowoff ? roff : nullptr;
     aa.row_begin = row0;
     aa.num_rows = nr;
-    aa.n_chunks = attn_chunks(d.rp, p->H_q, p->D_qk, p->K);  // the count the workspace was sized for
+    // the workspace holds partials for the larger of the two layouts' counts
+    aa.n_chunks = attn_chunks(d.rp, p->H_q, p->D_qk, p->K, aa.latent);
     aa.partial = aa.n_chunks > 1 ? static_cast<void*>(base + d.part_off) : nullptr;
     if ((st = status_of(launch_sparse_attn(aa, s))) != DSA_OK) return st;
   }

@@ -150,7 +150,11 @@ struct AttnLaunch {
   int32_t row_begin, num_rows;
   int32_t n_chunks;
 };
-int attn_chunks(int num_rows, int H_q, int D_qk, int K);
+// Chunks the index list of each row is split into for the kernel that the
+// layout (latent or not) selects, and the most either layout may use (for
+// workspace sizes, which do not know the layout).
+int attn_chunks(int num_rows, int H_q, int D_qk, int K, bool latent);
+int attn_chunks_max(int num_rows, int H_q, int D_qk, int K);
 size_t attn_partial_bytes(int num_rows, int H_q, int D_v, int n_chunks);
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s);
 

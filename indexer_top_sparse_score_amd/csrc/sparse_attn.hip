@@ -166,14 +166,17 @@ struct AttnGrid {
   int chunk;    // index slots per chunk (multiple of kSB, <= kMaxChunk)
 };
 
-// Maps a workgroup to (unit, head group) so that the head groups of one
-// (row, chunk) unit land on the same XCD (workgroups are dealt round-robin
-// to the 8 XCDs) and share the gathered rows through that XCD's L2.
+// Maps a workgroup to (unit, head group).  Workgroups are dealt round-robin
+// to the 8 XCDs (id & 7); XCD x takes the contiguous unit range
+// [x*U, x*U + U), U = ceil(units / 8), head groups innermost.  So the head
+// groups of a (row, chunk) unit share its gathered rows, and the chunks of
+// a row share its queries, through one XCD's L2.
 __device__ __forceinline__ bool decode_wg(const AttnGrid& g, int& unit, int& hg) {
   const int id = (int)blockIdx.x;
   const int xcd = id & 7, slot = id >> 3;
+  const int per_xcd = (g.n_units + 7) / 8;
   hg = slot % g.n_hg;
-  unit = (slot / g.n_hg) * 8 + xcd;
+  unit = xcd * per_xcd + slot / g.n_hg;
   return unit < g.n_units;
 }
 
@@ -459,13 +462,12 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
 // group g gets V[4g + k][16mt + i], k = 0..3: the A operand of
 // O^T += V^T . P^T in the contraction order the S^T accumulators hold.
 namespace lat {
-constexpr int kDqk = 576, kDv = 512, kNW = 4;
+constexpr int kDqk = 576, kDv = 512;
 constexpr int kPieces = kDqk * 2 / 16;             // 72
 constexpr int kTileBytes = kSB * kPieces * 16;     // 36864
-constexpr int kDmaPerWave = kSB * kPieces / 64 / kNW;  // 9
+constexpr int kDmaPerSB = kSB * kPieces / 64;      // 36 DMA instructions per sub-block
 constexpr int kKS = kDqk / 32;                     // 18
 constexpr int kMT = kDv / 16;                      // 32
-static_assert(kSB * kPieces % (64 * kNW) == 0, "DMA instructions per wave");
 __device__ __forceinline__ int slot(int row, int piece) { return row * kPieces + (piece ^ (row & 7)); }
 }  // namespace lat
 
@@ -491,22 +493,25 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
       : "memory");
 }
 
-__device__ __forceinline__ void wait_vm(int n) {
-  // n is one of the few counts the caller can have in flight
-  switch (n) {
+// Waits until at most `groups` groups of PER DMA instructions are in flight.
+template <int PER>
+__device__ __forceinline__ void wait_vm(int groups) {
+  static_assert(3 * PER <= 63, "vmcnt field");
+  switch (groups) {
     case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1 * lat::kDmaPerWave: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
-    case 2 * lat::kDmaPerWave: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(27)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PER) : "memory"); break;
   }
 }
 
-template <int NBUF>
-__global__ __launch_bounds__(64 * lat::kNW, 1) void sparse_attn_latent_kernel(AttnLaunch a, AttnGrid g) {
-  static_assert(NBUF >= 2 && NBUF <= 4, "vmcnt cases");
-  static_assert(lat::kNW * 16 * (2 * lat::kDv + 16) <= NBUF * lat::kTileBytes,
-                "epilogue staging fits the tiles");
+template <int NBUF, int kNW>
+__global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLaunch a, AttnGrid g) {
   using namespace lat;
+  constexpr int kDmaPerWave = kDmaPerSB / kNW;
+  static_assert(kDmaPerSB % kNW == 0, "DMA instructions per wave");
+  static_assert(NBUF >= 2 && NBUF <= 4, "vmcnt cases");
+  static_assert(kNW * 16 * (2 * kDv + 16) <= NBUF * kTileBytes, "epilogue staging fits the tiles");
   __shared__ __attribute__((aligned(16))) uint8_t tile[NBUF][kTileBytes];
   __shared__ int64_t koff[kMaxChunk];
 
@@ -574,17 +579,22 @@ __global__ __launch_bounds__(64 * lat::kNW, 1) void sparse_attn_latent_kernel(At
   // DMA of sub-block sb: this wave's instructions t = 0..kDmaPerWave-1 fill
   // slots 64*(wave*kDmaPerWave + t) + lane.  Absent rows read row 0 of block
   // 0 (which always exists) and are zeroed after they land.
+  // (All row offsets are read before the first DMA: the DMA's asm is a
+  // compiler memory barrier, so reads interleaved with it would each wait.)
   auto issue = [&](int sb) {
     uint8_t* buf = tile[sb % NBUF];
+    const uint8_t* src[kDmaPerWave];
 #pragma unroll
     for (int t = 0; t < kDmaPerWave; ++t) {
-      const int i = wave * kDmaPerWave + t;
-      const int sl = 64 * i + lane;
+      const int sl = 64 * (wave * kDmaPerWave + t) + lane;
       const int row = sl / kPieces;
       const int piece = (sl - row * kPieces) ^ (row & 7);
       const int64_t off = koff[sb * kSB + row];
-      dma16(kbase + (off >= 0 ? off : 0) + 16 * piece, (uint32_t)(uintptr_t)(buf + 1024 * i));
+      src[t] = kbase + (off >= 0 ? off : 0) + 16 * piece;
     }
+#pragma unroll
+    for (int t = 0; t < kDmaPerWave; ++t)
+      dma16(src[t], (uint32_t)(uintptr_t)(buf + 1024 * (wave * kDmaPerWave + t)));
   };
   auto zero_absent = [&](int sb) {
     uint8_t* buf = tile[sb % NBUF];
@@ -637,9 +647,11 @@ __global__ __launch_bounds__(64 * lat::kNW, 1) void sparse_attn_latent_kernel(At
     float m_all = -__builtin_inff();  // the head's max over every logit seen
     bool over = false;                // (wave) a logit exceeded m2 + kSlack
 
-    for (int sb = 0; sb < min(NBUF - 1, nsb); ++sb) issue(sb);
+    // NBUF-1 sub-blocks are requested up front; iteration sb requests
+    // sub-block sb+NBUF-1 into the buffer freed by iteration sb-1.
+    for (int x = 0; x < min(NBUF - 1, nsb); ++x) issue(x);
     for (int sb = 0; sb < nsb; ++sb) {
-      wait_vm(kDmaPerWave * min(nsb - 1 - sb, NBUF - 2));
+      wait_vm<kDmaPerWave>(min(nsb - 1 - sb, NBUF - 2));
       const uint32_t valid =
           (uint32_t)__ballot(lane < kSB && koff[sb * kSB + (lane & (kSB - 1))] >= 0);
       if (valid != 0xFFFFFFFFu) zero_absent(sb);
@@ -654,30 +666,33 @@ __global__ __launch_bounds__(64 * lat::kNW, 1) void sparse_attn_latent_kernel(At
       const uint8_t* buf = tile[sb % NBUF];
       // ---- logits S^T (keys x heads): two 16-key tiles; every read is one
       //      of two per-lane bases plus an immediate offset
-      // The two tiles' MFMA chains alternate, so consecutive MFMAs are
-      // independent; the group barriers keep the LDS reads kPre ahead.
-      __builtin_amdgcn_sched_barrier(0);
+      // The two tiles' MFMA chains alternate (step i: tile i % 2, dims
+      // 32(i / 2)), so consecutive MFMAs are independent, and the fragment
+      // reads run kDepth steps ahead.  The fences pin this order: left
+      // alone, the scheduler issues each read just before its MFMA and the
+      // LDS latency is exposed on every step.
       v4f s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int kk = 0; kk < kKS; ++kk)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const v8s ka = *reinterpret_cast<const v8s*>(buf + ((kk & 1) ? s_odd : s_even) +
-                                                       128 * (kk >> 1) + kt * kRow16);
-          s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(v8bf, ka), __builtin_bit_cast(v8bf, qb[kk]), s[kt], 0, 0, 0);
-        }
       {
-        constexpr int kPre = 6, kN = 2 * kKS;
-        __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);  // DS reads
+        constexpr int kSteps = 2 * kKS, kDepth = 8;
+        auto frag = [&](int i) {
+          const int kk = i >> 1, kt = i & 1;
+          return *reinterpret_cast<const v8s*>(buf + ((kk & 1) ? s_odd : s_even) + 128 * (kk >> 1) +
+                                               kt * kRow16);
+        };
+        v8s f[kDepth];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < kN - kPre; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        for (int i = 0; i < kDepth; ++i) f[i] = frag(i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kSteps; ++i) {
+          s[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(v8bf, f[i % kDepth]), __builtin_bit_cast(v8bf, qb[i >> 1]), s[i & 1],
+              0, 0, 0);
+          if (i + kDepth < kSteps) f[i % kDepth] = frag(i + kDepth);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
       }
-      __builtin_amdgcn_sched_barrier(0);
       // ---- softmax for this lane's head over keys 16kt + 4grp + v
       float mx = -__builtin_inff();
 #pragma unroll
@@ -713,27 +728,29 @@ __global__ __launch_bounds__(64 * lat::kNW, 1) void sparse_attn_latent_kernel(At
       // ---- O^T += V^T . P^T, V^T read transposed from the key-major tile;
       //      rows rlo and rlo + 16 share their swizzle, so every read is one
       //      of four per-lane bases plus an immediate offset
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) {
-        const uint8_t* at = buf + v_base[mt & 3] + 128 * (mt >> 2);
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)at);
-        const v4s hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(at + kRow16));
-        const v8s va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, va), pb, o[mt], 0, 0, 0);
-      }
       {
-        constexpr int kPre = 4;  // MFMAs' worth of reads in flight
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPre, 0);
+        // V^T fragments read kDepth MFMAs ahead, order pinned as above
+        constexpr int kDepth = 8;
+        auto vfrag = [&](int mt) {
+          const uint8_t* at = buf + v_base[mt & 3] + 128 * (mt >> 2);
+          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)at);
+          const v4s hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(at + kRow16));
+          return v8s{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        };
+        v8s f[kDepth];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < kMT - kPre; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        for (int mt = 0; mt < kDepth; ++mt) f[mt] = vfrag(mt);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt) {
+          o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, f[mt % kDepth]), pb,
+                                                          o[mt], 0, 0, 0);
+          if (mt + kDepth < kMT) f[mt % kDepth] = vfrag(mt + kDepth);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
     // the last iteration waited for every DMA; the barrier also makes the
     // buffers free for a second pass
@@ -827,9 +844,17 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
     a.lse[(int64_t)r * a.H_q + head] = Ls > 0.0f ? (M + log2f(Ls)) * kLn2 : -__builtin_inff();
 }
 
-// four waves (64 heads, one wave per SIMD and so the whole register file
-// each) per workgroup, except for small heads and few of them
-int waves_for(int H_q, int D_qk) { return (H_q > kHPW || D_qk > 64) ? 4 : 1; }
+// Waves (16 heads each) per workgroup.  The latent 576/512 kernel uses
+// DSA_ATTN_LAT_WAVES (one workgroup per CU, as its tiles take most of the
+// LDS: two waves make twice the workgroups of four, filling every CU for
+// few rows); the staged kernel four, except for small heads and few of them.
+#ifndef DSA_ATTN_LAT_WAVES
+#define DSA_ATTN_LAT_WAVES 2
+#endif
+int waves_for(int H_q, int D_qk, bool latent) {
+  if (D_qk == 576 && latent && DSA_ATTN_LATENT_DMA) return DSA_ATTN_LAT_WAVES;
+  return (H_q > kHPW || D_qk > 64) ? 4 : 1;
+}
 
 template <int DQK, int DV, int NW>
 hipError_t launch_t(const AttnLaunch& a, hipStream_t s) {
@@ -839,12 +864,19 @@ hipError_t launch_t(const AttnLaunch& a, hipStream_t s) {
   const int per = (a.K + a.n_chunks - 1) / a.n_chunks;
   g.chunk = (per + kSB - 1) / kSB * kSB;
   const int grid = (g.n_units + 7) / 8 * 8 * g.n_hg;
-  if (DSA_ATTN_LATENT_DMA && a.latent && DQK == lat::kDqk && NW == lat::kNW)
-    sparse_attn_latent_kernel<DSA_ATTN_NBUF><<<grid, 64 * NW, 0, s>>>(a, g);
-  else if (a.latent)
-    sparse_attn_kernel<DQK, DV, true, NW><<<grid, 64 * NW, 0, s>>>(a, g);
-  else
-    sparse_attn_kernel<DQK, DV, false, NW><<<grid, 64 * NW, 0, s>>>(a, g);
+  bool done = false;
+  if constexpr (DQK == lat::kDqk && NW > 1) {
+    if (DSA_ATTN_LATENT_DMA && a.latent) {
+      sparse_attn_latent_kernel<DSA_ATTN_NBUF, NW><<<grid, 64 * NW, 0, s>>>(a, g);
+      done = true;
+    }
+  }
+  if (!done) {
+    if (a.latent)
+      sparse_attn_kernel<DQK, DV, true, NW><<<grid, 64 * NW, 0, s>>>(a, g);
+    else
+      sparse_attn_kernel<DQK, DV, false, NW><<<grid, 64 * NW, 0, s>>>(a, g);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks == 1) return e;
   attn_combine_kernel<DV><<<dim3(a.num_rows, (a.H_q + 3) / 4), 256, 0, s>>>(a);
@@ -853,9 +885,9 @@ hipError_t launch_t(const AttnLaunch& a, hipStream_t s) {
 
 }  // namespace
 
-int attn_chunks(int num_rows, int H_q, int D_qk, int K) {
+int attn_chunks(int num_rows, int H_q, int D_qk, int K, bool latent) {
   if (num_rows <= 0) return 1;
-  const int hpw = kHPW * waves_for(H_q, D_qk);
+  const int hpw = kHPW * waves_for(H_q, D_qk, latent);
   const int n_hg = (H_q + hpw - 1) / hpw;
   const int want = (DSA_ATTN_TARGET_WGS + num_rows * n_hg - 1) / (num_rows * n_hg);
   const int least = (K + kMaxChunk - 1) / kMaxChunk;  // chunks must fit kMaxChunk slots
@@ -868,10 +900,18 @@ size_t attn_partial_bytes(int num_rows, int H_q, int D_v, int n_chunks) {
   return part_stats_bytes(num_rows, n_chunks, H_q) + (size_t)num_rows * n_chunks * H_q * D_v * 2;
 }
 
+int attn_chunks_max(int num_rows, int H_q, int D_qk, int K) {
+  return max(attn_chunks(num_rows, H_q, D_qk, K, true), attn_chunks(num_rows, H_q, D_qk, K, false));
+}
+
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s) {
   if (a.num_rows <= 0) return hipSuccess;
-  if (a.D_qk == 576) return launch_t<576, 512, 4>(a, s);
-  return waves_for(a.H_q, a.D_qk) == 4 ? launch_t<64, 64, 4>(a, s) : launch_t<64, 64, 1>(a, s);
+  switch (waves_for(a.H_q, a.D_qk, a.latent) * 1000 + a.D_qk) {
+    case 2576: return launch_t<576, 512, 2>(a, s);
+    case 4576: return launch_t<576, 512, 4>(a, s);
+    case 4064: return launch_t<64, 64, 4>(a, s);
+    default: return launch_t<64, 64, 1>(a, s);
+  }
 }
 
 }  // namespace dsa

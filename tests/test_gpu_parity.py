@@ -33,6 +33,8 @@ CASES = {
     "mla_int_k100": dict(lengths=[99, 100, 101, 3000], mode="int", **{**MLA, "K": 100}),
     "mla_int_k1": dict(lengths=[1, 2, 700], mode="int", **{**MLA, "K": 1}),
     "h48_d64": dict(lengths=[777, 2500], mode="int", **{**MLA, "H_I": 48, "D_I": 64, "H_q": 80}),
+    # 576/512 with a separate V cache (not the latent layout)
+    "mla_sepv": dict(lengths=[1, 777, 3000], mode="int", latent=False, **MLA),
 }
 
 
@@ -103,7 +105,7 @@ def test_topk_ties_and_special_values():
         assert (np_(idx)[i] == want).all(), f"row {i}"
 
 
-@pytest.mark.parametrize("name", ["mla_int", "tiny_int", "mla_int_k100", "h48_d64"])
+@pytest.mark.parametrize("name", ["mla_int", "tiny_int", "mla_int_k100", "h48_d64", "mla_sepv"])
 def test_sparse_attn_on_oracle_indices(name):
     batch = _batch(name, mode="gauss", seed=25)
     arr = oracle_arrays(batch)
@@ -140,7 +142,8 @@ def test_sparse_attn_skips_padding_and_handles_empty_rows():
     assert (np_(out.float())[2] == 0).all() and np.isneginf(np_(lse)[2]).all()
 
 
-@pytest.mark.parametrize("name", ["mla_int", "mla_int_shuffled", "tiny_int", "mla_int_k100"])
+@pytest.mark.parametrize("name", ["mla_int", "mla_int_shuffled", "tiny_int", "mla_int_k100",
+                                  "mla_sepv"])
 def test_decode_step_integer_mode(name):
     batch = _batch(name, seed=27)
     arr = oracle_arrays(batch)
