@@ -74,7 +74,7 @@ RowMap row_map(const dsa_problem* p) {
 int64_t max_len(const dsa_problem* p) { return (int64_t)p->max_blocks * DSA_BLOCK_SIZE; }
 
 int rows_per_pass(const dsa_problem* p) {
-  const size_t per_row = (size_t)max_len(p) * sizeof(float);
+  const size_t per_row = (size_t)max_len(p) * sizeof(float) + topk_work_bytes(1, max_len(p));
   size_t rp = kScoresBudget / per_row;
   if (rp < 1) rp = 1;
   if (rp > (size_t)p->num_rows) rp = (size_t)p->num_rows;
@@ -177,7 +177,7 @@ int dsa_indexer_scores(const dsa_problem* p, const uint8_t* qI, const float* w, 
   a.num_rows = p->num_rows;
   a.max_len = (int32_t)max_len(p);
   a.tw = TopkWork{};
-  a.feed_topk = false;
+  a.topk_K = 0;
   return status_of(launch_indexer_scores(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -205,6 +205,7 @@ int dsa_topk(const dsa_problem* p, const float* scores, int64_t ld_scores, int32
   a.max_len = (int32_t)max_len(p);
   a.tw = topk_work_carve(static_cast<char*>(ws) + kHeader, p->num_rows, max_len(p));
   a.prep = true;
+  a.vec = aligned(scores, 16) && ld_scores % 4 == 0;
   a.rowoff = nullptr;
   a.kv = dsa_paged{};
   return status_of(launch_topk(a, static_cast<hipStream_t>(stream)));
@@ -311,7 +312,7 @@ int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa
     ia.num_rows = nr;
     ia.max_len = (int32_t)ld;
     ia.tw = tw;
-    ia.feed_topk = true;
+    ia.topk_K = p->K;
     if ((st = status_of(launch_indexer_scores(ia, s))) != DSA_OK) return st;
 
     TopkLaunch ta;
@@ -327,6 +328,7 @@ int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa
     ta.max_len = (int32_t)ld;
     ta.tw = tw;
     ta.prep = false;
+    ta.vec = true;  // 256-byte aligned slab, ld a multiple of 64
     ta.rowoff = use_rowoff ? roff : nullptr;
     ta.kv = k;
     if ((st = status_of(launch_topk(ta, s))) != DSA_OK) return st;

@@ -65,30 +65,29 @@ __device__ __forceinline__ int lane_prefix(uint64_t mask) {
 // the front end before these run.
 
 // ------------------------------------------------------ Top-K work area
-// Per-row scratch of the Top-K kernels, carved from the caller's workspace.
-// The indexer scan (fused step) or the Top-K prep kernel (standalone call)
-// writes the per-tile key ranges and clears `hist` and `state` for the rows
-// of the call, so nothing is carried over from one call to the next.
-#ifndef DSA_IDX_TILE
-#define DSA_IDX_TILE 256
-#endif
-constexpr int kMMTile = DSA_IDX_TILE;  // positions per key-range tile (= indexer workgroup tile)
-constexpr int kTopkBins = 2048; // histogram bins
-constexpr int kCandCap = 4096;  // candidates kept per row
-constexpr int kStateWords = 8;  // per-row state (see topk.hip)
+// Positions per group whose maximum key the Top-K pre-selects on, for a row
+// of L positions keeping K: the largest power of two up to kMaxGroup that
+// leaves at least 2K groups, or 1 (no grouping).  The fused indexer and the
+// Top-K kernels call the same function, so they agree on every row's
+// grouping.
+constexpr int kMaxGroup = 8;
+__host__ __device__ inline int topk_group(int L, int K) {
+  int g = 1;
+  while (g < kMaxGroup && (int64_t)L >= (int64_t)4 * K * g) g <<= 1;
+  return g;
+}
+// Row stride (elements) of the group maxima: rows that group at all hold
+// at most ceil(max_len / 2) groups; a multiple of 4 for 16-byte loads.
+__host__ __device__ inline int64_t topk_gstride(int64_t max_len) {
+  return ((max_len + 1) / 2 + 3) & ~int64_t(3);
+}
 
+// The Top-K's work area, carved from the caller's workspace: the maximum
+// key of every group of every row, [rows][gstride] (rows with G = 1 leave
+// theirs unused).
 struct TopkWork {
-  uint32_t* tile_mm;  // [rows][mm_tiles][2]: min and max key of each tile
-  uint32_t* hist;     // [rows][kTopkBins]
-  uint32_t* state;    // [rows][kStateWords]
-  uint32_t* s_def;    // [rows][n_slices]: keys above the threshold (bin) in the slice
-  uint32_t* s_eq;     // [rows][n_slices]: keys equal to the threshold in the slice
-  uint32_t* s_off;    // [rows][n_slices]: first output slot of the slice
-  uint32_t* s_eqb;    // [rows][n_slices]: keys equal to the threshold before the slice
-  uint64_t* cand;     // [rows][kCandCap]: (key, position) composites
-  int32_t mm_tiles;   // ceil(max_len / kMMTile)
-  int32_t slice;      // positions per slice
-  int32_t n_slices;   // ceil(max_len / slice)
+  uint32_t* gmax;
+  int64_t gstride;
 };
 // bytes of the work area for `rows` rows of history up to max_len
 size_t topk_work_bytes(int rows, int64_t max_len);
@@ -106,8 +105,8 @@ struct IndexerLaunch {
   int32_t H_I, D_I;
   int32_t row_begin, num_rows;  // rows [row_begin, row_begin + num_rows)
   int32_t max_len;              // upper bound of any row's history length
-  TopkWork tw;                  // key ranges + clearing for a Top-K that follows,
-  bool feed_topk;               // or nothing when feed_topk is false
+  TopkWork tw;                  // group maxima for a Top-K of topk_K that follows,
+  int32_t topk_K;               // or nothing when tw.gmax is NULL
 };
 hipError_t launch_indexer_scores(const IndexerLaunch& a, hipStream_t s);
 
@@ -122,7 +121,8 @@ struct TopkLaunch {
   int32_t row_begin, num_rows;
   int32_t max_len;
   TopkWork tw;
-  bool prep;            // compute key ranges here (no fused indexer before)
+  bool prep;            // compute the group maxima here (no fused indexer before)
+  bool vec;             // every score row is 16-byte aligned (ld % 4 == 0)
   // Optional: also write each kept position's byte offset in the paged KV
   // cache `kv` (block table -> physical block), -1 for padding and for
   // positions whose block id is out of range, to rowoff[num_rows][K].

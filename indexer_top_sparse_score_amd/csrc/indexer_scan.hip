@@ -27,7 +27,10 @@
 namespace dsa {
 namespace {
 
-constexpr int kTile = kMMTile;  // positions per workgroup (= one key-range tile)
+#ifndef DSA_IDX_TILE
+#define DSA_IDX_TILE 256
+#endif
+constexpr int kTile = DSA_IDX_TILE;  // positions per workgroup
 constexpr int kWaves = 4;
 constexpr int kSub = 16;  // positions per MFMA column block
 
@@ -131,9 +134,11 @@ __global__ __launch_bounds__(256) void indexer_scan_kernel(IndexerLaunch a) {
     for (int v = 0; v < 4; ++v) wr[ht][v] = w_lds[16 * ht + 4 * g + v];
   }
   float* out = a.scores + (int64_t)(r - a.row_begin) * a.ld;
+  // Group maxima for the Top-K that follows (groups of G positions, G <= 16
+  // a power of two, so a group never straddles a 16-position sub-tile)
+  const int G = a.tw.gmax && L > a.topk_K ? topk_group(L, a.topk_K) : 1;
+  uint32_t* gmax = a.tw.gmax + (int64_t)(r - a.row_begin) * a.tw.gstride;
 
-  // key range of the scores this wave writes (for the Top-K that follows)
-  uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
   for (int j = 0; j < kSubPerWave; ++j) {
     const int s0 = tile0 + (wave + kWaves * j) * kSub;
@@ -149,44 +154,15 @@ __global__ __launch_bounds__(256) void indexer_scan_kernel(IndexerLaunch a) {
     part += __shfl_xor(part, 16);
     part += __shfl_xor(part, 32);
     const int s = s0 + col;
-    if (g == 0 && s < L) {
-      // canonical +0 for a zero score; an absent page scores -inf
-      const float v = page_ok[j] ? part + 0.0f : -__builtin_inff();
-      out[s] = v;
-      const uint32_t k = score_key(v);
-      kmn = min(kmn, k);
-      kmx = max(kmx, k);
+    // canonical +0 for a zero score; an absent page scores -inf
+    const float v = page_ok[j] ? part + 0.0f : -__builtin_inff();
+    if (g == 0 && s < L) out[s] = v;
+    if (G > 1) {  // wave-uniform
+      uint32_t k = s < L ? score_key(v) : 0u;
+      for (int o = 1; o < G; o <<= 1) k = max(k, (uint32_t)__shfl_xor((int)k, o));
+      if (g == 0 && s < L && (col & (G - 1)) == 0) gmax[s / G] = k;
     }
     if (s0 < L && !page_ok[j] && lane == 0) report(a.err, DSA_DEVERR_BLOCK);
-  }
-
-  if (a.feed_topk) {
-    __shared__ uint32_t red[2 * kWaves];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, o));
-      kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o));
-    }
-    if (lane == 0) {
-      red[wave] = kmn;
-      red[kWaves + wave] = kmx;
-    }
-    __syncthreads();
-    const int r_local = r - a.row_begin;
-    if (threadIdx.x == 0) {
-      for (int w = 0; w < kWaves; ++w) {
-        kmn = min(kmn, red[w]);
-        kmx = max(kmx, red[kWaves + w]);
-      }
-      uint32_t* mm = a.tw.tile_mm + ((int64_t)r_local * a.tw.mm_tiles + blockIdx.x) * 2;
-      mm[0] = kmn;
-      mm[1] = kmx;
-    }
-    if (blockIdx.x == 0) {
-      uint32_t* h = a.tw.hist + (int64_t)r_local * kTopkBins;
-      for (int i = threadIdx.x; i < kTopkBins; i += 256) h[i] = 0;
-      if (threadIdx.x < kStateWords) a.tw.state[(int64_t)r_local * kStateWords + threadIdx.x] = 0;
-    }
   }
 }
 

@@ -1,790 +1,654 @@
-// Per-row Top-K on gfx950, spread over the whole GPU.
+// Per-row Top-K on gfx950: one workgroup of 1024 threads per row.
 //
 // Method: Baidu AI Cloud, "Day0 Inference Support and Performance
 // Optimization for New Architecture LLMs", section 2.2 (keep the Top-K most
 // relevant historical positions).  Readings: ties go to the lower position,
 // the kept positions are written in ascending order, -1 pads to K.
 //
-// Scores are compared through an order-preserving 32-bit key; the selection
-// is exact.  Each row is cut into slices of `slice` positions and every
-// kernel runs one workgroup per (slice, row):
+// Scores are compared through an order-preserving 32-bit key (score_key);
+// the selection is exact.  A row's history is cut into groups of G
+// consecutive positions (topk_group: a power of two up to 8 that leaves at
+// least 2K groups), and the maximum key of every group is known before this
+// kernel runs -- the fused indexer writes it in its epilogue; the standalone
+// entry point runs topk_group_max_kernel first.
 //
-//  0. key ranges (prep kernel, or the indexer scan's epilogue in the fused
-//     step): the min and max key of every kMMTile-position tile; the row's
-//     histogram and state are cleared.
-//  1. hist: histogram of the row's keys over 2048 bins of width 2^shift laid
-//     from the row's min key, so the bins follow the scores' actual range.
-//  2. cand: every workgroup reads the finished histogram and finds the bin
-//     b* that holds the K-th largest key; keys above b* are kept for sure.
-//       - b* holds a single key value T (exact ties): each slice counts its
-//         keys > T and == T (tie mode);
-//       - b* holds at most kCandCap keys (the usual case: a handful): each
-//         slice appends them as 64-bit composites (key << 32 | ~position),
-//         which are all distinct and order exactly as the selection rule
-//         ranks (larger key first, then lower position);
-//       - otherwise nothing (fallback).
-//     The last workgroup of the row to finish (atomic arrival count) ends
-//     the selection: the need-th largest composite C* (or, in the fallback,
-//     a one-workgroup refinement over the row), and the output offset of
-//     every slice.
-//  3. compact: each slice writes its kept positions, in order, at its
-//     offset: key > T, or key == T with position <= P_T (composite mode) /
-//     with tie rank below the tie budget (tie mode).
+//  1. A lower bound t on the row's K-th largest key T: one 2048-bin histogram
+//     of the group maxima over their range, and t = the lower edge of the bin
+//     that holds the K-th largest maximum.  At least K groups have a maximum
+//     >= t, so at least K keys are >= t and T >= t; every kept position lies
+//     in a group whose maximum is >= t (a candidate group).  Without heavy
+//     ties there are about K candidate groups holding some 1.1-1.4 K keys
+//     >= t.
+//  2. The candidate groups' keys are loaded and those >= t are compacted, in
+//     position order, into LDS with their positions.
+//  3. T is selected exactly among them, together with the number of keys
+//     equal to T that are kept (the first ones in position order).
+//  4. The kept positions are written in ascending order: block-wide prefix
+//     sums over the compacted list, staged in LDS, then stored in one
+//     coalesced pass (with the KV row offsets, from a copy of the row's block
+//     table in LDS).
+//
+// With G = 1 the keys themselves are loaded and step 3 runs on them
+// directly.  Rows with L <= K keep every position.  A row that does not fit
+// these buffers (K > 2048, more than 16384 groups, more than 4096 candidate
+// groups or 8192 keys >= t because of ties, or t = 0 because of NaN scores)
+// runs the same selection over its keys streamed from memory.
+//
+// Selection (select_kth): histograms of 2048 bins laid over the current key
+// range [lo, hi] narrow the range to the bin that holds the wanted rank,
+// until one key value remains or the bin holds at most kSmall keys, which
+// one wave then ranks directly.  Wave-level scans and reductions use DPP
+// row shifts and broadcasts.
 
 #include "dsa_common.h"
 
 namespace dsa {
-
-// per-row state words
-enum : int { kCandCount = 0, kArrived = 1, kT = 2, kNeedEq = 3, kMode = 4, kLoB = 5, kAbove = 6 };
-
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr int kPer = 8;                   // positions per thread per pass
-constexpr int kPass = kPer * kThreads;    // positions per pass; slices are multiples of it
+constexpr int kT = 1024;                  // threads per workgroup
+constexpr int kWaves = kT / 64;           // 16
 constexpr int kBinBits = 11;
-static_assert((1 << kBinBits) == kTopkBins, "bins");
+constexpr int kBins = 1 << kBinBits;      // 2048
+constexpr int kSmall = 64;                // bin size ranked directly by one wave
+constexpr int kPerThread = 16;            // group maxima (or keys) per thread
+constexpr int kMaxN = kPerThread * kT;    // 16384
+constexpr int kCandPer = 4;               // candidate groups per thread
+constexpr int kMaxCand = kCandPer * kT;   // 4096
+constexpr int kKeysPer = 8;               // compacted keys per thread
+constexpr int kMaxKeys = kKeysPer * kT;   // 8192
+constexpr int kBtCache = 2048;            // block-table entries cached in LDS
+constexpr int kScanWords = 4 * kWaves + 1;
+static_assert(kBins == 2 * kT, "find_bin gives each thread two bins");
 
-struct RowInfo {
-  int L;       // history length (0: invalid row)
-  int r_local; // row index within the call
-  int b;       // sequence (valid when L > 0)
+struct Smem {
+  uint32_t hist[kBins];    // histograms; afterwards slot -> kept position
+  uint32_t list[kMaxCand]; // candidate group ids, in position order
+  uint32_t ck[kMaxKeys];   // compacted keys >= t, in position order
+  int32_t cp[kMaxKeys];    // and their positions
+  int32_t bt[kBtCache];    // the row's block table (rows of <= 2048 blocks)
+  uint32_t buf[kSmall];
+  uint32_t res[4];
+  uint32_t wsum[kScanWords];
+  uint32_t red[2 * kWaves];
 };
 
-__device__ __forceinline__ RowInfo row_info(const TopkLaunch& a) {
-  RowInfo ri;
-  ri.r_local = (int)blockIdx.y;
-  int b = 0, p;
-  const int r = a.row_begin + ri.r_local;
-  ri.L = resolve_row(a.rows, r, b, p) ? p + 1 : 0;
-  ri.b = b;
-  return ri;
-}
-
-// Byte offset of position i's row in the paged KV cache, given its block id
-// (-1, and an error report, when the id is out of range).
-__device__ __forceinline__ int64_t kv_offset(const TopkLaunch& a, int i, int phys) {
-  if (phys < 0 || (int64_t)phys >= a.kv.num_blocks) {
-    report(a.err, DSA_DEVERR_BLOCK);
-    return -1;
-  }
-  return (int64_t)phys * a.kv.block_stride + (int64_t)(i & 63) * a.kv.row_stride;
-}
-
-// Cross-workgroup hand-off inside one kernel, without full-L2 fences: the
-// producers publish with agent-scope atomic RMWs (performed coherently for
-// every XCD), wait for their completion before the arrival count, and the
-// last workgroup reads them back with agent-scope loads, which skip stale
-// copies in its own XCD's L2.
-__device__ __forceinline__ void publish32(uint32_t* p, uint32_t v) {
-  __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void publish64(uint64_t* p, uint64_t v) {
-  __hip_atomic_exchange(reinterpret_cast<unsigned long long*>(p), (unsigned long long)v,
-                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t fetch32(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t fetch64(const uint64_t* p) {
-  return (uint64_t)__hip_atomic_load(reinterpret_cast<const unsigned long long*>(p),
-                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// waits until this wave's outstanding memory operations have completed
-__device__ __forceinline__ void drain_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 __device__ __forceinline__ int bitlen32(uint32_t x) { return x ? 32 - __clz(x) : 0; }
-__device__ __forceinline__ int bitlen64(uint64_t x) { return x ? 64 - __clzll(x) : 0; }
 
-template <typename T>
-__device__ __forceinline__ T wave_sum(T x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+// ------------------------------------------------------------ wave / block
+// DPP controls: row_shr:n = 0x110 + n; row_bcast:15 = 0x142; row_bcast:31 =
+// 0x143.  A lane whose DPP source is absent (or whose row is masked off)
+// receives `id`, the identity of the operation.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp(uint32_t id, uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, kCtrl, kRowMask, 0xF, false);
+}
+
+// Inclusive prefix over the 64 lanes of a wave, for an associative op with
+// identity id.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x, uint32_t id, Op op) {
+  x = op(x, dpp<0x111, 0xF>(id, x));
+  x = op(x, dpp<0x112, 0xF>(id, x));
+  x = op(x, dpp<0x114, 0xF>(id, x));
+  x = op(x, dpp<0x118, 0xF>(id, x));
+  x = op(x, dpp<0x142, 0xA>(id, x));
+  x = op(x, dpp<0x143, 0xC>(id, x));
   return x;
 }
+struct Add { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
+struct Min { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); } };
+struct Max { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); } };
 
-// Exclusive prefix sum over the 256 threads; `tot` receives the total.
-// `scratch` holds kWaves words of LDS.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* scratch,
-                                                         uint32_t& tot) {
+// Exclusive prefix sum over the block in thread order; `tot` receives the
+// total.  Starts and ends with a barrier, so `wsum` may be reused at once.
+__device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t* wsum, uint32_t& tot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t inc = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_up((int)inc, o);
-    if (lane >= o) inc += y;
+  const uint32_t inc = wave_scan(x, 0u, Add());
+  __syncthreads();
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t v = lane < kWaves ? wsum[lane] : 0u;
+    const uint32_t c = wave_scan(v, 0u, Add());
+    if (lane < kWaves) wsum[lane] = c - v;
+    if (lane == 63) wsum[kWaves] = c;
   }
   __syncthreads();
-  if (lane == 63) scratch[wave] = inc;
+  const uint32_t ex = wsum[wave] + inc - x;
+  tot = wsum[kWaves];
   __syncthreads();
-  uint32_t before = 0;
-  tot = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const uint32_t v = scratch[w];
-    before += w < wave ? v : 0u;
-    tot += v;
-  }
-  return before + inc - x;
+  return ex;
 }
 
-// Min/max reduction over the 256 threads (results valid in every thread).
-__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_t* scratch) {
+// Exclusive prefix sums of N sequences of one value per thread, taken one
+// after another (sequence 0 over threads 0..1023, then sequence 1, ...):
+// ex[i] sums every earlier value of that order.  Returns the grand total.
+// Wave 0 scans the N x 16 wave totals.  Starts and ends with a barrier.
+template <int N>
+__device__ __forceinline__ uint32_t block_scan_n(const uint32_t (&x)[N], uint32_t (&ex)[N],
+                                                 uint32_t* wsum) {
+  static_assert(N * kWaves <= 64, "one wave scans the wave totals");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t inc[N];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+  for (int i = 0; i < N; ++i) inc[i] = wave_scan(x[i], 0u, Add());
+  __syncthreads();
+  if (lane == 63) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) wsum[i * kWaves + wave] = inc[i];
   }
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t v = lane < N * kWaves ? wsum[lane] : 0u;
+    const uint32_t c = wave_scan(v, 0u, Add());
+    if (lane < N * kWaves) wsum[lane] = c - v;
+    if (lane == 63) wsum[4 * kWaves] = c;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) ex[i] = wsum[i * kWaves + wave] + inc[i] - x[i];
+  const uint32_t total = wsum[4 * kWaves];
+  __syncthreads();
+  return total;
+}
+
+// Min and max over the block (results in every thread).
+__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_t* red) {
+  mn = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan(mn, 0xFFFFFFFFu, Min()), 63);
+  mx = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan(mx, 0u, Max()), 63);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
   if (lane == 0) {
-    scratch[wave] = mn;
-    scratch[kWaves + wave] = mx;
+    red[wave] = mn;
+    red[kWaves + wave] = mx;
   }
   __syncthreads();
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
-    mn = min(mn, scratch[w]);
-    mx = max(mx, scratch[kWaves + w]);
+    mn = min(mn, red[w]);
+    mx = max(mx, red[kWaves + w]);
   }
 }
 
-// This thread's share of the row's key range (the tiles' ranges), loaded
-// two tiles per step; block_minmax finishes it.
-__device__ __forceinline__ void row_range_load(const TopkLaunch& a, int r_local, int L,
-                                               uint32_t& kmin, uint32_t& kmax) {
-  const int tiles = (L + kMMTile - 1) / kMMTile;
-  const uint32_t* mm = a.tw.tile_mm + (int64_t)r_local * a.tw.mm_tiles * 2;
-  kmin = 0xFFFFFFFFu;
-  kmax = 0u;
-  for (int t = threadIdx.x; t < tiles; t += 2 * kThreads) {
-    const int u = min(t + kThreads, tiles - 1);
-    const uint2 x = *reinterpret_cast<const uint2*>(mm + 2 * t);
-    const uint2 y = *reinterpret_cast<const uint2*>(mm + 2 * u);
-    kmin = min(kmin, min(x.x, y.x));
-    kmax = max(kmax, max(x.y, y.y));
-  }
-}
-
-// The keys of one pass (kPer per thread, coalesced; positions past `end`
-// repeat the last one and are masked by the caller).
-__device__ __forceinline__ void load_pass(const float* sc, int base, int end, uint32_t* k) {
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) k[j] = score_key(sc[min(base + j * kThreads + (int)threadIdx.x, end - 1)]);
-}
-
-__device__ __forceinline__ int range_shift(uint32_t kmin, uint32_t kmax) {
-  return max(0, bitlen32(kmax - kmin) - kBinBits);
-}
-
-// Finds, over a 2048-bin histogram in LDS, the bin b with
-// above(b) < need <= above(b) + h[b], where above(b) counts bins > b.
-// Thread t owns bins 2047-8t .. 2040-8t.  Results land in out[0] (bin) and
-// out[1] (above).
-__device__ __forceinline__ void find_bin(const uint32_t* h, uint32_t need, uint32_t* out,
-                                         uint32_t* scratch) {
-  const int t = threadIdx.x;
-  const int top = kTopkBins - 1 - 8 * t;
-  uint32_t mine = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) mine += h[top - j];
+// Over the 2048-bin histogram h, the bin b with above(b) < need <=
+// above(b) + h[b], where above(b) counts the keys in bins above b; thread t
+// owns bins 2047 - 2t and 2046 - 2t.  Results: res[0] = b, res[1] = above(b).
+// Requires 1 <= need <= sum of h.  Ends with a barrier.
+__device__ __forceinline__ void find_bin(const uint32_t* h, uint32_t need, uint32_t* res,
+                                         uint32_t* wsum) {
+  const int top = kBins - 1 - 2 * (int)threadIdx.x;
+  const uint32_t c0 = h[top], c1 = h[top - 1];
   uint32_t tot;
-  uint32_t above = block_exclusive_scan(mine, scratch, tot);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t c = h[top - j];
-    if (above < need && need <= above + c) {
-      out[0] = (uint32_t)(top - j);
-      out[1] = above;
-    }
-    above += c;
+  const uint32_t above = block_scan(c0 + c1, wsum, tot);
+  if (above < need && need <= above + c0) {
+    res[0] = (uint32_t)top;
+    res[1] = above;
+  } else if (above + c0 < need && need <= above + c0 + c1) {
+    res[0] = (uint32_t)(top - 1);
+    res[1] = above + c0;
   }
   __syncthreads();
 }
 
-// ----------------------------------------------------------------- 0. prep
-__global__ __launch_bounds__(kThreads) void topk_prep_kernel(TopkLaunch a) {
-  __shared__ uint32_t scratch[2 * kWaves];
-  const RowInfo ri = row_info(a);
-  if (ri.L <= a.K) return;
-  const int t = blockIdx.x;
-  const int start = t * kMMTile;
-  if (start >= ri.L) return;
-  const int end = min(ri.L, start + kMMTile);
-  const float* sc = a.scores + (int64_t)ri.r_local * a.ld;
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (int i = start + threadIdx.x; i < end; i += kThreads) {
-    const uint32_t k = score_key(sc[i]);
-    mn = min(mn, k);
-    mx = max(mx, k);
-  }
-  block_minmax(mn, mx, scratch);
-  if (threadIdx.x == 0) {
-    uint32_t* mm = a.tw.tile_mm + ((int64_t)ri.r_local * a.tw.mm_tiles + t) * 2;
-    mm[0] = mn;
-    mm[1] = mx;
-  }
-  if (t == 0) {
-    uint32_t* h = a.tw.hist + (int64_t)ri.r_local * kTopkBins;
-    for (int i = threadIdx.x; i < kTopkBins; i += kThreads) h[i] = 0;
-    if (threadIdx.x < kStateWords) a.tw.state[(int64_t)ri.r_local * kStateWords + threadIdx.x] = 0;
-  }
+__device__ __forceinline__ int range_shift(uint32_t lo, uint32_t hi) {
+  return max(0, bitlen32(hi - lo) - kBinBits);
 }
 
-// ----------------------------------------------------------------- 1. hist
-__global__ __launch_bounds__(kThreads) void topk_hist_kernel(TopkLaunch a) {
-  __shared__ uint32_t h[kTopkBins];
-  __shared__ uint32_t scratch[2 * kWaves];
-  const RowInfo ri = row_info(a);
-  if (ri.L <= a.K) return;
-  const int start = blockIdx.x * a.tw.slice;
-  if (start >= ri.L) return;
-  const int end = min(ri.L, start + a.tw.slice);
-  const float* sc = a.scores + (int64_t)ri.r_local * a.ld;
-  // the first pass's keys and the row's range are loaded together
-  uint32_t k[kPer];
-  load_pass(sc, start, end, k);
-  uint32_t kmin, kmax;
-  row_range_load(a, ri.r_local, ri.L, kmin, kmax);
-  for (int i = threadIdx.x; i < kTopkBins; i += kThreads) h[i] = 0;
-  block_minmax(kmin, kmax, scratch);  // its barriers also order the clearing
-  const int shift = range_shift(kmin, kmax);
-  for (int base = start; base < end; base += kPass) {
-    if (base != start) load_pass(sc, base, end, k);
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int i = base + j * kThreads + threadIdx.x;
-      if (i < end) atomicAdd(&h[min((k[j] - kmin) >> shift, (uint32_t)kTopkBins - 1)], 1u);
-    }
-  }
+// Histogram of the keys in [lo, hi] that visit(f) hands to f, on 2048 bins
+// of width 2^shift from lo, and the bin b holding the need-th largest
+// (res[0] = b, res[1] = keys above b).
+template <class Visit>
+__device__ __forceinline__ void histogram_bin(Visit&& visit, uint32_t lo, uint32_t hi, int shift,
+                                              uint32_t need, Smem& s) {
+  for (int i = threadIdx.x; i < kBins; i += kT) s.hist[i] = 0;
   __syncthreads();
-  uint32_t* gh = a.tw.hist + (int64_t)ri.r_local * kTopkBins;
-  for (int i = threadIdx.x; i < kTopkBins; i += kThreads)
-    if (h[i]) atomicAdd(&gh[i], h[i]);
+  visit([&](uint32_t k) {
+    if (k >= lo && k <= hi) atomicAdd(&s.hist[(k - lo) >> shift], 1u);
+  });
+  __syncthreads();
+  find_bin(s.hist, need, s.res, s.wsum);
 }
 
-// ----------------------------------------------------------------- 2. cand
-
-enum Mode : int { kTie = 0, kCand = 1, kFallback = 2 };
-
-// Exact selection inside the last workgroup, composite mode: the need-th
-// largest of n composites held in LDS.
-__device__ uint64_t select_composite(const uint64_t* c, int n, uint32_t need, uint32_t* h,
-                                     uint32_t* scratch, uint32_t* res) {
-  // range of the composites
-  uint64_t lo = ~0ull, hi = 0ull;
-  for (int i = threadIdx.x; i < n; i += kThreads) {
-    lo = min(lo, c[i]);
-    hi = max(hi, c[i]);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    lo = min(lo, (uint64_t)__shfl_xor((long long)lo, o));
-    hi = max(hi, (uint64_t)__shfl_xor((long long)hi, o));
-  }
-  __shared__ uint64_t red[2 * kWaves];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) {
-    red[wave] = lo;
-    red[kWaves + wave] = hi;
-  }
-  __syncthreads();
-  for (int w = 0; w < kWaves; ++w) {
-    lo = min(lo, red[w]);
-    hi = max(hi, red[kWaves + w]);
-  }
-  __syncthreads();
-  while (lo < hi) {
-    const int shift = max(0, bitlen64(hi - lo) - kBinBits);
-    for (int i = threadIdx.x; i < kTopkBins; i += kThreads) h[i] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += kThreads) {
-      const uint64_t x = c[i];
-      if (x >= lo && x <= hi)
-        atomicAdd(&h[min((uint32_t)((x - lo) >> shift), (uint32_t)kTopkBins - 1)], 1u);
-    }
-    __syncthreads();
-    find_bin(h, need, res, scratch);
-    const uint32_t b = res[0];
-    need -= res[1];
-    const uint64_t nlo = lo + ((uint64_t)b << shift);
-    const uint64_t span = (uint64_t(1) << shift) - 1;
-    const uint64_t nhi = (hi - nlo < span) ? hi : nlo + span;
-    lo = nlo;
-    hi = nhi;
-    __syncthreads();
-  }
-  return lo;
-}
-
-// The need-th largest (1-based) of n <= kRankMax distinct composites in LDS:
-// a composite's rank is the number of larger ones.
-constexpr int kRankMax = 2 * kThreads;
-__device__ uint64_t select_by_rank(const uint64_t* c, int n, uint32_t need, uint64_t* out) {
-  for (int i = threadIdx.x; i < n; i += kThreads) {
-    const uint64_t x = c[i];
-    uint32_t rank = 0;
-    for (int j = 0; j < n; ++j) rank += c[j] > x ? 1u : 0u;
-    if (rank + 1 == need) *out = x;
-  }
-  __syncthreads();
-  return *out;
-}
-
-// Fallback inside the last workgroup: narrow [lo, hi] over the row's keys
-// (read from global memory) until one key value T remains; returns T and the
-// number of keys equal to T still to keep in `need`.
-__device__ uint32_t select_in_row(const float* sc, int L, uint32_t lo, uint32_t hi,
-                                  uint32_t& need, uint32_t* h, uint32_t* scratch,
-                                  uint32_t* res) {
-  while (lo < hi) {
-    const int shift = max(0, bitlen32(hi - lo) - kBinBits);
-    for (int i = threadIdx.x; i < kTopkBins; i += kThreads) h[i] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < L; i += kThreads) {
-      const uint32_t k = score_key(sc[i]);
-      if (k >= lo && k <= hi) atomicAdd(&h[min((k - lo) >> shift, (uint32_t)kTopkBins - 1)], 1u);
-    }
-    __syncthreads();
-    find_bin(h, need, res, scratch);
-    need -= res[1];
-    const uint32_t nlo = lo + (res[0] << shift);
-    const uint32_t span = (uint32_t)((1ull << shift) - 1);
-    hi = (hi - nlo < span) ? hi : nlo + span;
-    lo = nlo;
-    __syncthreads();
-  }
-  return lo;
-}
-
-__global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkLaunch a) {
-  __shared__ uint32_t h[kTopkBins];
-  __shared__ uint32_t scratch[2 * kWaves];
-  __shared__ uint32_t res[4];
-  __shared__ uint32_t sel_cnt[256];
-  __shared__ uint32_t sl_a[256];
-  __shared__ int last;
-  const RowInfo ri = row_info(a);
-  if (ri.L <= a.K) return;
-  const int s = blockIdx.x;
-  const int start = s * a.tw.slice;
-  if (start >= ri.L) return;
-  const int end = min(ri.L, start + a.tw.slice);
-  const int n_sl = (ri.L + a.tw.slice - 1) / a.tw.slice;
-  const int64_t rs = (int64_t)ri.r_local * a.tw.n_slices;
-  uint32_t* st = a.tw.state + (int64_t)ri.r_local * kStateWords;
-  const float* sc = a.scores + (int64_t)ri.r_local * a.ld;
-
-  // every independent load first: the first pass's keys, the row's range
-  // and the finished histogram
-  uint32_t k0[kPer];
-  load_pass(sc, start, end, k0);
-  uint32_t kmin, kmax;
-  row_range_load(a, ri.r_local, ri.L, kmin, kmax);
-  {
-    const uint32_t* gh = a.tw.hist + (int64_t)ri.r_local * kTopkBins;
-    uint32_t hv[kTopkBins / kThreads];
-#pragma unroll
-    for (int j = 0; j < kTopkBins / kThreads; ++j) hv[j] = gh[j * kThreads + threadIdx.x];
-#pragma unroll
-    for (int j = 0; j < kTopkBins / kThreads; ++j) h[j * kThreads + threadIdx.x] = hv[j];
-  }
-  block_minmax(kmin, kmax, scratch);  // its barriers also publish h
-  const int shift = range_shift(kmin, kmax);
-  find_bin(h, (uint32_t)a.K, res, scratch);
-  const uint32_t bstar = res[0];
-  const uint32_t above = res[1];
-  const uint32_t cnt_b = h[bstar];
-  const uint32_t lo_b = kmin + (bstar << shift);
-  const uint32_t span = (uint32_t)((1ull << shift) - 1);
-  const uint32_t hi_b = (kmax - lo_b < span) ? kmax : lo_b + span;
-  const int mode = lo_b == hi_b ? kTie : (cnt_b <= (uint32_t)kCandCap ? kCand : kFallback);
-  if (s == 0 && threadIdx.x == 0) {  // read by the compact kernel
-    st[kMode] = (uint32_t)mode;
-    st[kLoB] = lo_b;
-    st[kAbove] = above;
-  }
-
-  if (mode != kFallback) {
-    // One pass of kPass positions per iteration (one, for slices of 2048):
-    // all loads are issued before any is used, and a wave reserves its
-    // candidate slots with a single atomic for the whole pass.  Everything
-    // written here is read by the next kernel, so plain stores suffice.
-    uint32_t n_above = 0, n_eq = 0;
-    const int lane = threadIdx.x & 63;
-    uint64_t* cand = a.tw.cand + (int64_t)ri.r_local * kCandCap;
-    for (int base = start; base < end; base += kPass) {
-      uint32_t k[kPer];
-      bool inb[kPer];
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) k[j] = k0[j];
-      if (base != start) load_pass(sc, base, end, k);
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const bool ok = base + j * kThreads + (int)threadIdx.x < end;
-        n_above += (ok && k[j] > hi_b) ? 1u : 0u;
-        inb[j] = ok && k[j] >= lo_b && k[j] <= hi_b;
-        n_eq += inb[j] ? 1u : 0u;
-      }
-      if (mode == kCand) {
-        uint64_t m[kPer];
-        uint32_t total = 0;
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-          m[j] = __ballot(inb[j]);
-          total += (uint32_t)__popcll(m[j]);
-        }
-        if (total != 0) {  // wave-uniform
-          uint32_t slot = 0;
-          if (lane == 0) slot = atomicAdd(&st[kCandCount], total);
-          uint32_t at = (uint32_t)__shfl((int)slot, 0);
-#pragma unroll
-          for (int j = 0; j < kPer; ++j) {
-            const uint32_t mine = at + (uint32_t)lane_prefix(m[j]);
-            const uint32_t i = (uint32_t)(base + j * kThreads + (int)threadIdx.x);
-            if (inb[j] && mine < (uint32_t)kCandCap)
-              cand[mine] = ((uint64_t)k[j] << 32) | (0xFFFFFFFFu - i);
-            at += (uint32_t)__popcll(m[j]);
-          }
-        }
-      }
-    }
-    n_above = wave_sum(n_above);
-    n_eq = wave_sum(n_eq);
-    if (lane == 0) {
-      scratch[threadIdx.x >> 6] = n_above;
-      scratch[kWaves + (threadIdx.x >> 6)] = n_eq;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t sa = 0, se = 0;
-      for (int w = 0; w < kWaves; ++w) {
-        sa += scratch[w];
-        se += scratch[kWaves + w];
-      }
-      a.tw.s_def[rs + s] = sa;
-      a.tw.s_eq[rs + s] = se;
-    }
-    return;  // the compact kernel finishes the selection
-  }
-
-  // ---- fallback (bin b* too full for the candidate buffer): the last
-  // workgroup of the row to arrive refines the threshold over the whole row
-  // and sets every slice's output offset
-  __syncthreads();
-  if (threadIdx.x == 0)
-    last = __hip_atomic_fetch_add(&st[kArrived], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-           (uint32_t)(n_sl - 1);
-  __syncthreads();
-  if (!last) return;
-
-  uint32_t need = (uint32_t)a.K - above;
-  const uint32_t T = select_in_row(sc, ri.L, lo_b, hi_b, need, h, scratch, res);
-  for (int j = 0; j < n_sl; ++j) {
-    const int a0 = j * a.tw.slice, a1 = min(ri.L, a0 + a.tw.slice);
-    uint32_t g = 0, e = 0;
-    for (int i = a0 + threadIdx.x; i < a1; i += kThreads) {
-      const uint32_t k = score_key(sc[i]);
-      g += k > T ? 1u : 0u;
-      e += k == T ? 1u : 0u;
-    }
-    uint32_t tg, te;
-    block_exclusive_scan(g, scratch, tg);
-    block_exclusive_scan(e, scratch, te);
-    if (threadIdx.x == 0) {
-      sl_a[j] = tg;
-      sel_cnt[j] = te;
-    }
-  }
-  __syncthreads();
-  // output offsets: slices in order, the budget of keys equal to T spent in
-  // position order
-  if (threadIdx.x == 0) {
-    res[2] = 0;
-    res[3] = 0;
-  }
-  __syncthreads();
-  for (int c0 = 0; c0 < n_sl; c0 += kThreads) {
-    const int j = c0 + threadIdx.x;
-    const uint32_t e = j < n_sl ? sel_cnt[j] : 0u;
-    uint32_t te;
-    const uint32_t eqb = res[3] + block_exclusive_scan(e, scratch, te);
-    const uint32_t take = eqb >= need ? 0u : min(e, need - eqb);
-    const uint32_t cnt = j < n_sl ? sl_a[j] + take : 0u;
-    uint32_t tot;
-    const uint32_t ex = block_exclusive_scan(cnt, scratch, tot);
-    if (j < n_sl) {
-      a.tw.s_off[rs + j] = res[2] + ex;
-      a.tw.s_eqb[rs + j] = eqb;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      res[2] += tot;
-      res[3] += te;
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    st[kT] = T;
-    st[kNeedEq] = need;
-  }
-}
-
-// -------------------------------------------------------------- 3. compact
-// Every workgroup first settles the selection rule for itself -- the
-// threshold key T with its position cut P_T or tie budget, and its own first
-// output slot -- from the per-slice counts and the candidate list (a few
-// dozen composites in the usual case), so no workgroup of the previous
-// kernel has to wait for the others:
-//   composite mode: C* = the need-th largest candidate; keep key > T, or
-//     key == T and position <= P_T; offset = keys above b* in earlier slices
-//     + chosen candidates at earlier positions;
-//   tie mode: T = the single key of b*; keep key > T, or key == T while
-//     fewer than `need` such keys precede it; offset = keys above T in
-//     earlier slices + min(need, keys equal to T in earlier slices);
-//   fallback: all of it was set by the last workgroup of the cand kernel.
-// Positions are then visited kPass at a time, thread t taking positions
-// base + j*kThreads + t (j < kPer): every load is coalesced and issued
-// before any is used.  Output order is position order, i.e. (j, wave, lane);
-// ballots give the order inside a wave and per-wave counts in LDS the order
-// across waves.
-__global__ __launch_bounds__(kThreads) void topk_compact_kernel(TopkLaunch a) {
-  __shared__ uint32_t wcnt[2][kPer][kWaves];  // per pass row and wave: [0] ties, [1] kept
-  __shared__ uint64_t cl[kCandCap];
-  __shared__ uint32_t h[kTopkBins];
-  __shared__ uint32_t scratch[2 * kWaves];
-  __shared__ uint32_t res[4];
-  __shared__ uint64_t pick;
-  __shared__ uint32_t pre[2];
-  __shared__ int32_t blk[kPass / 64];  // block ids of the current pass (rowoff only)
-  const RowInfo ri = row_info(a);
-  const int K = a.K;
-  const int s = blockIdx.x;
-  int32_t* out = a.indices + (int64_t)ri.r_local * K;
-  int64_t* roff = a.rowoff ? a.rowoff + (int64_t)ri.r_local * K : nullptr;
-  const int32_t* bt = a.rows.block_table + (int64_t)ri.b * a.rows.max_blocks;
-  if (s == 0 && threadIdx.x == 0 && a.counts) a.counts[ri.r_local] = min(K, ri.L);
-  if (ri.L <= K) {
-    const int a0 = s * a.tw.slice, a1 = min(ri.L, a0 + a.tw.slice);
-    for (int j = a0 + threadIdx.x; j < a1; j += kThreads) {
-      out[j] = j;
-      if (roff) roff[j] = kv_offset(a, j, bt[j >> 6]);
-    }
-    if (s == 0)
-      for (int j = ri.L + threadIdx.x; j < K; j += kThreads) {
-        out[j] = -1;
-        if (roff) roff[j] = -1;
-      }
-    return;
-  }
-  const int start = s * a.tw.slice;
-  if (start >= ri.L) return;
-  const int end = min(ri.L, start + a.tw.slice);
-  const int n_sl = (ri.L + a.tw.slice - 1) / a.tw.slice;
-  const float* sc = a.scores + (int64_t)ri.r_local * a.ld;
-  const int64_t rs = (int64_t)ri.r_local * a.tw.n_slices;
-  const uint32_t* st = a.tw.state + (int64_t)ri.r_local * kStateWords;
-  const uint64_t* cand = a.tw.cand + (int64_t)ri.r_local * kCandCap;
+// The need-th largest key (1-based, counted with multiplicity) among the keys
+// in [lo, hi] that visit(f) hands to f in the threads of the block; there
+// must be at least `need` of them.  On return `need` holds how many keys
+// equal to the result belong to the need largest (the others are larger).
+// Every thread calls it with the same lo, hi and need.
+template <class Visit>
+__device__ __forceinline__ uint32_t select_kth(Visit&& visit, uint32_t lo, uint32_t hi,
+                                               uint32_t& need, Smem& s) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  while (lo < hi) {
+    const int shift = range_shift(lo, hi);
+    histogram_bin(visit, lo, hi, shift, need, s);
+    const uint32_t b = s.res[0];
+    need -= s.res[1];
+    const uint32_t cnt = s.hist[b];
+    const uint32_t nlo = lo + (b << shift);
+    const uint32_t span = (1u << shift) - 1u;
+    hi = (hi - nlo <= span) ? hi : nlo + span;
+    lo = nlo;
+    __syncthreads();  // hist and res are rewritten below
+    if (lo < hi && cnt <= (uint32_t)kSmall) {
+      // rank the bin's keys directly: wave 0, one key per lane
+      if (tid == 0) s.res[2] = 0;
+      __syncthreads();
+      visit([&](uint32_t k) {
+        if (k >= lo && k <= hi) s.buf[atomicAdd(&s.res[2], 1u)] = k;
+      });
+      __syncthreads();
+      if (tid < 64) {
+        const uint32_t m = s.res[2];
+        const uint32_t x = (uint32_t)tid < m ? s.buf[tid] : 0u;
+        uint32_t gt = 0, ge = 0;
+        for (uint32_t i = 0; i < m; ++i) {
+          const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, (int)i);
+          gt += y > x ? 1u : 0u;
+          ge += y >= x ? 1u : 0u;
+        }
+        if ((uint32_t)tid < m && gt < need && need <= ge) {  // equal keys write equal values
+          s.res[0] = x;
+          s.res[1] = need - gt;
+        }
+      }
+      __syncthreads();
+      const uint32_t T = s.res[0];
+      need = s.res[1];
+      __syncthreads();
+      return T;
+    }
+  }
+  return lo;
+}
 
-  // one trip for everything: this slice's first keys, the row state, every
-  // slice's counts and the first kThreads candidate slots (read whether
-  // filled or not: the slots always exist)
-  uint32_t k0[kPer];
-  load_pass(sc, start, end, k0);
-  // the pass's block ids travel with its keys
-  auto load_blocks = [&](int base) {
-    if (roff && tid < kPass / 64) {
-      const int bi = (base >> 6) + tid;
-      blk[tid] = bi <= (end - 1) >> 6 ? bt[bi] : -1;
+// ------------------------------------------------------------------ output
+// Where the kept positions go.  The emission records slot -> position in
+// LDS (`pos`, the histogram's storage, free by then; K <= 2048) and flush()
+// writes them out once all are known: coalesced index stores and the KV row
+// offsets (block ids from the LDS copy of the block table when the row's
+// table fits it).  Larger K (only on the streamed path) writes through put()
+// directly.
+struct Out {
+  int32_t* idx;        // [K]
+  int64_t* roff;       // [K] or NULL: byte offsets of the kept rows in the KV cache
+  const int32_t* bt;   // the row's block table
+  const int32_t* bt_lds;  // its LDS copy, or NULL
+  int64_t kv_blocks, kv_block_stride, kv_row_stride;
+  uint32_t* err;
+  uint32_t* pos;       // LDS staging of the selection, or NULL
+  __device__ __forceinline__ int64_t row_offset(int p, int phys) const {
+    if (phys >= 0 && (int64_t)phys < kv_blocks)
+      return (int64_t)phys * kv_block_stride + (int64_t)(p & 63) * kv_row_stride;
+    report(err, DSA_DEVERR_BLOCK);
+    return -1;
+  }
+  __device__ __forceinline__ int block_of(int p) const {
+    return bt_lds ? bt_lds[p >> 6] : bt[p >> 6];
+  }
+  // kStaged: into `pos` (then flush()), else straight to memory
+  template <bool kStaged>
+  __device__ __forceinline__ void put(uint32_t slot, int p) const {
+    if (kStaged) {
+      pos[slot] = (uint32_t)p;
+      return;
+    }
+    idx[slot] = p;
+    if (roff) roff[slot] = row_offset(p, bt[p >> 6]);
+  }
+  // after the emission (and a barrier): the staged selection to memory
+  __device__ __forceinline__ void flush(int K) const {
+    constexpr int kPer = kBins / kT;  // slots per thread
+    int p[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int slot = (int)threadIdx.x + i * kT;
+      p[i] = slot < K ? (int)pos[slot] : 0;
+      if (slot < K) idx[slot] = p[i];
+    }
+    if (!roff) return;
+    int phys[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) phys[i] = (int)threadIdx.x + i * kT < K ? block_of(p[i]) : 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int slot = (int)threadIdx.x + i * kT;
+      if (slot < K) roff[slot] = row_offset(p[i], phys[i]);
+    }
+  }
+};
+
+// N consecutive keys of a row starting at position i0 (entries at or past L
+// are 0).  Vector loads when the row and i0 allow them.
+template <int N>
+__device__ __forceinline__ void load_keys(const float* sc, int i0, int L, bool vec, uint32_t (&k)[N]) {
+  if (vec && (N % 4) == 0 && i0 + N <= L) {
+#pragma unroll
+    for (int j = 0; j < N; j += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(sc + i0 + j);
+      k[j] = score_key(v.x);
+      k[j + 1] = score_key(v.y);
+      k[j + 2] = score_key(v.z);
+      k[j + 3] = score_key(v.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < N; ++j) k[j] = i0 + j < L ? score_key(sc[i0 + j]) : 0u;
+  }
+}
+
+// Emits one run of N entries per thread (threads in order, entry j of a
+// thread at position pos(j)), masked to the first `n`, given T and the
+// budget of keys equal to T.  `eq_before` / `out_before` carry the counts of
+// earlier runs and are advanced past this one.
+template <int N, bool kStaged, class Pos>
+__device__ __forceinline__ void emit_runs(const uint32_t (&k)[N], int n, Pos&& pos, uint32_t T,
+                                          uint32_t need_eq, uint32_t& eq_before,
+                                          uint32_t& out_before, const Out& o, Smem& s) {
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    gt += (j < n && k[j] > T) ? 1u : 0u;
+    eq += (j < n && k[j] == T) ? 1u : 0u;
+  }
+  uint32_t tot;
+  const uint32_t eqx = eq_before + block_scan(eq, s.wsum, tot);
+  eq_before += tot;
+  const uint32_t take_eq = eqx >= need_eq ? 0u : min(eq, need_eq - eqx);
+  const uint32_t slot0 = out_before + block_scan(gt + take_eq, s.wsum, tot);
+  out_before += tot;
+  uint32_t slot = slot0, e = eqx;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    if (j < n) {
+      const bool is_eq = k[j] == T;
+      const bool keep = k[j] > T || (is_eq && e < need_eq);
+      e += is_eq ? 1u : 0u;
+      if (keep) o.template put<kStaged>(slot++, pos(j));
+    }
+  }
+}
+
+// ------------------------------------------------------------------- paths
+
+// The general path: the same selection over the row's keys streamed from
+// memory (several passes), then the emission run by run.
+template <bool kStaged>
+__device__ __forceinline__ void select_streamed(const float* sc, int L, int K, bool vec,
+                                                const Out& o, Smem& s) {
+  constexpr int kRun = 8;
+  auto visit = [&](auto f) {
+    for (int i0 = 0; i0 < L; i0 += kRun * kT) {
+      const int p = i0 + kRun * (int)threadIdx.x;
+      uint32_t k[kRun];
+      load_keys<kRun>(sc, p, L, vec, k);
+#pragma unroll
+      for (int j = 0; j < kRun; ++j)
+        if (p + j < L) f(k[j]);
     }
   };
-  load_blocks(start);
-  const uint32_t mode = st[kMode];
-  const uint32_t n_cand = st[kCandCount];
-  static_assert(kThreads == 256, "one slice per thread");
-  const uint32_t sd = tid < n_sl ? a.tw.s_def[rs + tid] : 0u;
-  const uint32_t se = tid < n_sl ? a.tw.s_eq[rs + tid] : 0u;
-  const uint64_t c0 = cand[tid];
-
-  uint32_t T, PT, need_eq, off, eqb;
-  if (mode == kFallback) {
-    T = st[kT];
-    PT = 0x7FFFFFFFu;
-    need_eq = st[kNeedEq];
-    off = a.tw.s_off[rs + s];
-    eqb = a.tw.s_eqb[rs + s];
-  } else {
-    const uint32_t need = (uint32_t)K - st[kAbove];
-    // keys above b* (and, tie mode, keys equal to T) in the slices before s
-    uint32_t t1, t2;
-    const uint32_t ex_d = block_exclusive_scan(sd, scratch, t1);
-    const uint32_t ex_e = block_exclusive_scan(se, scratch, t2);
-    if (tid == s) {
-      pre[0] = ex_d;
-      pre[1] = ex_e;
-    }
-    __syncthreads();
-    if (mode == kTie) {
-      T = st[kLoB];
-      PT = 0x7FFFFFFFu;
-      need_eq = need;
-      eqb = pre[1];
-      off = pre[0] + min(need, eqb);
-    } else {
-      const int n = (int)min(n_cand, (uint32_t)kCandCap);
-      cl[tid] = c0;
-      for (int i = kThreads + tid; i < n; i += kThreads) cl[i] = cand[i];
-      __syncthreads();
-      const uint64_t cstar = n <= kRankMax ? select_by_rank(cl, n, need, &pick)
-                                           : select_composite(cl, n, need, h, scratch, res);
-      T = (uint32_t)(cstar >> 32);
-      PT = 0xFFFFFFFFu - (uint32_t)cstar;
-      need_eq = 0xFFFFFFFFu;
-      eqb = 0;
-      // chosen candidates at positions before this slice
-      uint32_t c = 0;
-      for (int i = tid; i < n; i += kThreads)
-        c += (cl[i] >= cstar && 0xFFFFFFFFu - (uint32_t)cl[i] < (uint32_t)start) ? 1u : 0u;
-      c = wave_sum(c);
-      if (lane == 0) scratch[wave] = c;
-      __syncthreads();
-      uint32_t before = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) before += scratch[w];
-      off = pre[0] + before;
-    }
+  uint32_t need = (uint32_t)K;
+  const uint32_t T = select_kth(visit, 0u, 0xFFFFFFFFu, need, s);
+  uint32_t eq_before = 0, out_before = 0;
+  for (int i0 = 0; i0 < L && out_before < (uint32_t)K; i0 += kRun * kT) {
+    const int p = i0 + kRun * (int)threadIdx.x;
+    uint32_t k[kRun];
+    load_keys<kRun>(sc, p, L, vec, k);
+    emit_runs<kRun, kStaged>(k, max(0, min(kRun, L - p)), [&](int j) { return p + j; }, T,
+                             need, eq_before, out_before, o, s);
   }
-  const bool ties = need_eq != 0xFFFFFFFFu;
+}
 
-  for (int base = start; base < end; base += kPass) {
-    uint32_t k[kPer];
+// Steps 2-4 for groups of G positions.  The candidate groups' keys are
+// loaded in pieces of P = G/4 (at least 1) float4 or float2 loads, lane-
+// adjacent within a group so that one cache line serves its pieces: piece q
+// of list entry e is taken by thread (e P + q) mod 1024 in round
+// (e P + q) / 1024.  The keys >= t are compacted in (round, thread) order,
+// which is position order.  Returns false, having written nothing, when
+// more than kMaxKeys keys are >= t.
+template <int G>
+__device__ __forceinline__ bool select_groups(const float* sc, int L, int K, uint32_t t,
+                                              uint32_t kmax, uint32_t n_cg, bool vec,
+                                              const Out& o, Smem& s) {
+  constexpr int W = G < 4 ? G : 4;      // keys per piece
+  constexpr int P = G / W;              // pieces per group
+  constexpr int R = kCandPer * P;       // rounds (pieces per thread)
+  const int tid = threadIdx.x;
+  uint32_t n_c;
+  {
+    int base[R];  // first position of the piece, L: none
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) k[j] = k0[j];
-    if (base != start) {
-      load_pass(sc, base, end, k);
-      load_blocks(base);  // the previous pass's readers are past its final barrier
+    for (int m = 0; m < R; ++m) {
+      const uint32_t q = (uint32_t)(m * kT + tid);
+      const uint32_t e = q / P;
+      base[m] = e < n_cg ? (int)s.list[e] * G + (int)(q % P) * W : L;
     }
-    uint64_t me[kPer];
+    uint32_t k[R][W];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const bool ok = base + j * kThreads + tid < end;
-      me[j] = __ballot(ok && k[j] == T);
+    for (int m = 0; m < R; ++m) load_keys<W>(sc, base[m], L, vec, k[m]);
+    uint32_t c[R], at[R];
+#pragma unroll
+    for (int m = 0; m < R; ++m) {
+      c[m] = 0;
+#pragma unroll
+      for (int j = 0; j < W; ++j) c[m] += k[m][j] >= t ? 1u : 0u;  // t >= 1: absent keys never count
     }
-    // rank among keys equal to T, in position order (tie modes only)
-    uint32_t eq_rank[kPer];
-    uint32_t eq_pass = 0;
-    if (ties) {
-      if (lane == 0) {
+    static_assert(R <= 8, "rounds");
+    if constexpr (R <= 4) {
+      n_c = block_scan_n<R>(c, at, s.wsum);
+    } else {  // two scans of four rounds
+      uint32_t c0[4], c1[4], a0[4], a1[4];
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) wcnt[0][j][wave] = (uint32_t)__popcll(me[j]);
+      for (int m = 0; m < 4; ++m) {
+        c0[m] = c[m];
+        c1[m] = c[m + 4];
       }
-      __syncthreads();
-      uint32_t run = eqb;
+      const uint32_t n0 = block_scan_n<4>(c0, a0, s.wsum);
+      n_c = n0 + block_scan_n<4>(c1, a1, s.wsum);
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        uint32_t before = 0, all = 0;
+      for (int m = 0; m < 4; ++m) {
+        at[m] = a0[m];
+        at[m + 4] = n0 + a1[m];
+      }
+    }
+    if (n_c > (uint32_t)kMaxKeys) return false;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const uint32_t c = wcnt[0][j][w];
-          before += w < wave ? c : 0u;
-          all += c;
+    for (int m = 0; m < R; ++m)
+#pragma unroll
+      for (int j = 0; j < W; ++j)
+        if (k[m][j] >= t) {
+          s.ck[at[m]] = k[m][j];
+          s.cp[at[m]] = base[m] + j;
+          ++at[m];
         }
-        eq_rank[j] = run + before + (uint32_t)lane_prefix(me[j]);
-        run += all;
+  }
+  __syncthreads();
+  const int c0 = kKeysPer * tid;
+  const int n = max(0, min(kKeysPer, (int)n_c - c0));
+  uint32_t k[kKeysPer];
+#pragma unroll
+  for (int j = 0; j < kKeysPer; ++j) k[j] = j < n ? s.ck[c0 + j] : 0u;
+  auto visit = [&](auto f) {
+#pragma unroll
+    for (int j = 0; j < kKeysPer; ++j)
+      if (j < n) f(k[j]);
+  };
+  uint32_t need = (uint32_t)K;
+  const uint32_t T = select_kth(visit, t, kmax, need, s);
+  uint32_t eq_before = 0, out_before = 0;
+  emit_runs<kKeysPer, true>(k, n, [&](int j) { return s.cp[c0 + j]; }, T, need, eq_before,
+                            out_before, o, s);
+  return true;
+}
+
+// Steps 1-4.  `gm` holds the thread's group maxima 16t .. 16t+15 (loaded
+// before the row was resolved).  Returns false, having written nothing, when
+// the row needs the streamed path.
+__device__ __forceinline__ bool select_fast(const float* sc, int L, int K, bool vec,
+                                            uint32_t (&gm)[kPerThread], const Out& o, Smem& s) {
+  const int tid = threadIdx.x;
+  const int G = topk_group(L, K);
+  const int N = (L + G - 1) / G;
+  if (N > kMaxN) return false;
+  const int g0 = kPerThread * tid;
+  if (G == 1) load_keys<kPerThread>(sc, g0, L, vec, gm);
+  const int n_mine = max(0, min(kPerThread, N - g0));
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j)
+    if (j < n_mine) {
+      kmin = min(kmin, gm[j]);
+      kmax = max(kmax, gm[j]);
+    }
+  block_minmax(kmin, kmax, s.red);
+  auto visit = [&](auto f) {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j)
+      if (j < n_mine) f(gm[j]);
+  };
+
+  if (G == 1) {  // the keys themselves: select T and emit
+    uint32_t need = (uint32_t)K;
+    const uint32_t T = select_kth(visit, kmin, kmax, need, s);
+    uint32_t eq_before = 0, out_before = 0;
+    emit_runs<kPerThread, true>(gm, n_mine, [&](int j) { return g0 + j; }, T, need, eq_before,
+                                out_before, o, s);
+    return true;
+  }
+
+  // 1. t = lower edge of the bin holding the K-th largest group maximum
+  uint32_t t = kmin;
+  if (kmin < kmax) {
+    const int shift = range_shift(kmin, kmax);
+    histogram_bin(visit, kmin, kmax, shift, (uint32_t)K, s);
+    t = kmin + (s.res[0] << shift);
+  }
+  // candidate groups: maxima >= t, listed in position order
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) c += (j < n_mine && gm[j] >= t) ? 1u : 0u;
+  uint32_t n_cg;
+  uint32_t at = block_scan(c, s.wsum, n_cg);
+  // heavy ties at t, or t = 0 (NaN scores at the threshold)
+  if (n_cg > (uint32_t)kMaxCand || t == 0) return false;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j)
+    if (j < n_mine && gm[j] >= t) s.list[at++] = (uint32_t)(g0 + j);
+  __syncthreads();
+  switch (G) {
+    case 2: return select_groups<2>(sc, L, K, t, kmax, n_cg, vec, o, s);
+    case 4: return select_groups<4>(sc, L, K, t, kmax, n_cg, vec, o, s);
+    default: return select_groups<kMaxGroup>(sc, L, K, t, kmax, n_cg, vec, o, s);
+  }
+}
+
+__global__ __launch_bounds__(kT) void topk_row_kernel(TopkLaunch a) {
+  __shared__ Smem s;
+  const int tid = threadIdx.x;
+  const int r_local = (int)blockIdx.x;
+  const int K = a.K;
+  // independent loads first: this thread's share of the group maxima (the
+  // row's slice is gstride long, whatever the row's length turns out to be)
+  uint32_t gm[kPerThread];
+  {
+    const uint32_t* src = a.tw.gmax + (int64_t)r_local * a.tw.gstride;
+    const int g0 = kPerThread * tid;
+    if (g0 + kPerThread <= a.tw.gstride) {
+#pragma unroll
+      for (int j = 0; j < kPerThread; j += 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src + g0 + j);
+        gm[j] = v.x;
+        gm[j + 1] = v.y;
+        gm[j + 2] = v.z;
+        gm[j + 3] = v.w;
       }
-      eq_pass = run - eqb;
     } else {
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) eq_rank[j] = 0;
+      for (int j = 0; j < kPerThread; ++j) gm[j] = g0 + j < a.tw.gstride ? src[g0 + j] : 0u;
     }
-    uint64_t ms[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const uint32_t i = (uint32_t)(base + j * kThreads + tid);
-      const bool ok = (int)i < end;
-      const bool eq = (me[j] >> lane) & 1u;
-      ms[j] = __ballot(ok && (k[j] > T || (eq && i <= PT && eq_rank[j] < need_eq)));
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) wcnt[1][j][wave] = (uint32_t)__popcll(ms[j]);
-    }
-    __syncthreads();
-    uint32_t run = off;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      uint32_t before = 0, all = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const uint32_t c = wcnt[1][j][w];
-        before += w < wave ? c : 0u;
-        all += c;
-      }
-      const uint32_t at = run + before + (uint32_t)lane_prefix(ms[j]);
-      if (((ms[j] >> lane) & 1u) && at < (uint32_t)K) {
-        const int i = base + j * kThreads + tid;
-        out[at] = i;
-        if (roff) roff[at] = kv_offset(a, i, blk[(i - base) >> 6]);
-      }
-      run += all;
-    }
-    off = run;
-    eqb += eq_pass;
-    __syncthreads();  // wcnt is rewritten by the next pass
   }
+  int b = 0, p;
+  const int L = resolve_row(a.rows, a.row_begin + r_local, b, p) ? p + 1 : 0;
+  Out o;
+  o.idx = a.indices + (int64_t)r_local * K;
+  o.roff = a.rowoff ? a.rowoff + (int64_t)r_local * K : nullptr;
+  o.bt = a.rows.block_table + (int64_t)b * a.rows.max_blocks;
+  o.bt_lds = nullptr;
+  o.kv_blocks = a.kv.num_blocks;
+  o.kv_block_stride = a.kv.block_stride;
+  o.kv_row_stride = a.kv.row_stride;
+  o.err = a.err;
+  o.pos = nullptr;
+  if (tid == 0 && a.counts) a.counts[r_local] = min(K, L);
+  if (L <= K) {  // keep the whole history (nothing for an invalid row)
+    for (int j = tid; j < K; j += kT) {
+      if (j < L) {
+        o.template put<false>((uint32_t)j, j);
+      } else {
+        o.idx[j] = -1;
+        if (o.roff) o.roff[j] = -1;
+      }
+    }
+    return;
+  }
+  const float* sc = a.scores + (int64_t)r_local * a.ld;
+  if (K > kBins) {  // too many to stage: straight to memory
+    select_streamed<false>(sc, L, K, a.vec, o, s);
+    return;
+  }
+  const int nblk = (L + kBlock - 1) / kBlock;
+  if (o.roff && nblk <= kBtCache) {  // the row's block table, read while selecting
+    for (int i = tid; i < nblk; i += kT) s.bt[i] = o.bt[i];
+    o.bt_lds = s.bt;
+  }
+  o.pos = s.hist;
+  if (!(K <= kMaxCand - kT && select_fast(sc, L, K, a.vec, gm, o, s)))
+    select_streamed<true>(sc, L, K, a.vec, o, s);
+  __syncthreads();
+  o.flush(K);
+}
+
+// Group maxima for a standalone Top-K call: thread -> one group of its row.
+__global__ __launch_bounds__(256) void topk_group_max_kernel(TopkLaunch a) {
+  int b, p;
+  const int r_local = (int)blockIdx.y;
+  if (!resolve_row(a.rows, a.row_begin + r_local, b, p)) return;
+  const int L = p + 1;
+  if (L <= a.K) return;
+  const int G = topk_group(L, a.K);
+  if (G == 1) return;
+  const int g = (int)(blockIdx.x * 256 + threadIdx.x);
+  const int N = (L + G - 1) / G;
+  if (g >= N) return;
+  const float* sc = a.scores + (int64_t)r_local * a.ld + (int64_t)g * G;
+  const int n = min(G, L - g * G);
+  uint32_t m = 0;
+  for (int j = 0; j < n; ++j) m = max(m, score_key(sc[j]));
+  a.tw.gmax[(int64_t)r_local * a.tw.gstride + g] = m;
 }
 
 }  // namespace
 
 size_t topk_work_bytes(int rows, int64_t max_len) {
-  const TopkWork w = topk_work_carve(nullptr, rows, max_len);
-  return (size_t)(reinterpret_cast<uintptr_t>(w.cand) + sizeof(uint64_t) * rows * kCandCap);
+  return (size_t)rows * (size_t)topk_gstride(max_len) * sizeof(uint32_t);
 }
 
 TopkWork topk_work_carve(void* base, int rows, int64_t max_len) {
+  (void)rows;
   TopkWork w;
-  w.mm_tiles = (int)((max_len + kMMTile - 1) / kMMTile);
-  int64_t slice = kPass;
-  while ((max_len + slice - 1) / slice > 256) slice += kPass;
-  w.slice = (int)slice;
-  w.n_slices = (int)((max_len + slice - 1) / slice);
-  auto r256 = [](size_t x) { return (x + 255) & ~size_t(255); };
-  size_t off = 0;
-  char* b = static_cast<char*>(base);
-  auto take = [&](size_t bytes) {
-    char* p = b + off;
-    off += r256(bytes);
-    return p;
-  };
-  w.tile_mm = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 2 * rows * w.mm_tiles));
-  w.hist = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * rows * kTopkBins));
-  w.state = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * rows * kStateWords));
-  w.s_def = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * rows * w.n_slices));
-  w.s_eq = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * rows * w.n_slices));
-  w.s_off = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * rows * w.n_slices));
-  w.s_eqb = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * rows * w.n_slices));
-  w.cand = reinterpret_cast<uint64_t*>(take(0));
+  w.gmax = static_cast<uint32_t*>(base);
+  w.gstride = topk_gstride(max_len);
   return w;
 }
 
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
   if (a.num_rows <= 0) return hipSuccess;
-  if (a.prep) {
-    topk_prep_kernel<<<dim3(a.tw.mm_tiles, a.num_rows), kThreads, 0, s>>>(a);
-    hipError_t e = hipGetLastError();
+  if (a.prep && a.max_len > 2 * a.K) {  // some row may group its positions
+    const int64_t groups = (a.max_len + 1) / 2;
+    topk_group_max_kernel<<<dim3((unsigned)((groups + 255) / 256), a.num_rows), 256, 0, s>>>(a);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const dim3 grid(a.tw.n_slices, a.num_rows);
-  topk_hist_kernel<<<grid, kThreads, 0, s>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  topk_cand_kernel<<<grid, kThreads, 0, s>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  topk_compact_kernel<<<grid, kThreads, 0, s>>>(a);
+  topk_row_kernel<<<a.num_rows, kT, 0, s>>>(a);
   return hipGetLastError();
 }
 

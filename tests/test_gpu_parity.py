@@ -35,6 +35,8 @@ CASES = {
     "h48_d64": dict(lengths=[777, 2500], mode="int", **{**MLA, "H_I": 48, "D_I": 64, "H_q": 80}),
     # 576/512 with a separate V cache (not the latent layout)
     "mla_sepv": dict(lengths=[1, 777, 3000], mode="int", latent=False, **MLA),
+    # histories long enough for the Top-K to group positions by 2, 4 and 8
+    "mla_int_grouped": dict(lengths=[9000, 20000, 40000], mode="int", **MLA),
 }
 
 
@@ -86,7 +88,10 @@ def test_topk_exact_on_oracle_scores(name):
 
 def test_topk_ties_and_special_values():
     # heavy ties, signed zeros, infinities, all-equal rows: exact vs the oracle
-    wl = small_workload("ties", lengths=[5000, 5000, 5000, 5000, 3000, 2049], **MLA)
+    # (the last rows are long enough to group positions, and their ties or
+    # NaNs send them down the streamed path)
+    wl = small_workload("ties", lengths=[5000, 5000, 5000, 5000, 3000, 2049, 20000, 40000,
+                                         40000, 9000], **MLA)
     batch = make_batch(wl, device="cuda", seed=24)
     rng = np.random.default_rng(24)
     ld = 64 * batch.max_blocks
@@ -98,6 +103,13 @@ def test_topk_ties_and_special_values():
     sc[3, :L[3]] = rng.choice(np.array([-np.inf, np.inf, 5.0, -2.0], np.float32), L[3])
     sc[4, :L[4]] = rng.standard_normal(L[4]).astype(np.float32) * 1e-30  # subnormal-ish range
     sc[5, :L[5]] = -np.arange(L[5], dtype=np.float32)              # K+1 distinct, descending
+    sc[6, :L[6]] = rng.integers(0, 3, L[6])                        # 3 distinct values, G = 4
+    sc[7, :L[7]] = 1.5                                              # all equal, G = 8
+    sc[8, :L[8]] = np.where(rng.random(L[8]) < 0.99, np.nan,       # mostly NaN: t = 0
+                            rng.standard_normal(L[8])).astype(np.float32)
+    x = rng.standard_normal(L[9]).astype(np.float32)                # a few exact ties near
+    x[rng.choice(L[9], 300, replace=False)] = np.sort(x)[-2100]     # the threshold, G = 2
+    sc[9, :L[9]] = x
     idx, cnt = gpu_topk(batch, torch.from_numpy(sc).cuda())
     for i in range(batch.rows):
         want, n = oracle.topk_row(sc[i, :L[i]], wl.K)
@@ -143,7 +155,7 @@ def test_sparse_attn_skips_padding_and_handles_empty_rows():
 
 
 @pytest.mark.parametrize("name", ["mla_int", "mla_int_shuffled", "tiny_int", "mla_int_k100",
-                                  "mla_sepv"])
+                                  "mla_sepv", "mla_int_grouped"])
 def test_decode_step_integer_mode(name):
     batch = _batch(name, seed=27)
     arr = oracle_arrays(batch)
