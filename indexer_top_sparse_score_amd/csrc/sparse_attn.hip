@@ -38,6 +38,9 @@
 #ifndef DSA_ATTN_LATENT_DMA
 #define DSA_ATTN_LATENT_DMA 1
 #endif
+#ifndef DSA_ATTN_KDEPTH
+#define DSA_ATTN_KDEPTH 8  // K fragment reads in flight ahead of their MFMAs
+#endif
 #ifndef DSA_ATTN_NBUF
 #define DSA_ATTN_NBUF 4
 #endif
@@ -55,7 +58,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // Split-key partials of a call: (max, sum) as float2 [rows][chunks][H_q],
-// then the chunk's normalised output O / sum as bf16 [rows][chunks][H_q][D_v]
+// then the chunk's unnormalised output O = sum_j 2^(t_j - max) v_j as bf16
+// [rows][chunks][H_q][D_v]
 // (256-byte aligned).
 __host__ __device__ inline size_t part_stats_bytes(int rows, int chunks, int H_q) {
   return ((size_t)rows * chunks * H_q * sizeof(float2) + 255) & ~size_t(255);
@@ -104,7 +108,8 @@ template <int MT>
 __device__ __forceinline__ void write_result(const AttnLaunch& a, int r, int row_local, int chunk,
                                              int head, int grp, const v4f* o, float m2, float lsum) {
   constexpr int DV = 16 * MT;
-  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  // the single chunk's output O / sum; a partial keeps O (see the combine)
+  const float inv = a.n_chunks > 1 ? 1.0f : lsum > 0.0f ? 1.0f / lsum : 0.0f;
   uint16_t* dst = a.n_chunks == 1 ? a.out + ((int64_t)r * a.H_q + head) * DV
                                   : part_out(a, row_local, chunk, DV) + (int64_t)head * DV;
   dst += 4 * grp;
@@ -134,13 +139,23 @@ __device__ __forceinline__ void write_result_staged(const AttnLaunch& a, int r, 
                                                     float m2, float lsum, uint8_t* stage) {
   constexpr int DV = 512, MT = DV / 16, kPitch = 2 * DV + 16;
   const int cidx = lane & 15, grp = lane >> 4;
-  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  if (a.n_chunks == 1) {
+    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    uint2 w;
-    w.x = pack2(o[mt][0] * inv, o[mt][1] * inv);
-    w.y = pack2(o[mt][2] * inv, o[mt][3] * inv);
-    *reinterpret_cast<uint2*>(stage + cidx * kPitch + 2 * (16 * mt + 4 * grp)) = w;
+    for (int mt = 0; mt < MT; ++mt) {
+      uint2 w;
+      w.x = pack2(o[mt][0] * inv, o[mt][1] * inv);
+      w.y = pack2(o[mt][2] * inv, o[mt][3] * inv);
+      *reinterpret_cast<uint2*>(stage + cidx * kPitch + 2 * (16 * mt + 4 * grp)) = w;
+    }
+  } else {  // a partial: O against the chunk's reference, unnormalised
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      uint2 w;
+      w.x = pack2(o[mt][0], o[mt][1]);
+      w.y = pack2(o[mt][2], o[mt][3]);
+      *reinterpret_cast<uint2*>(stage + cidx * kPitch + 2 * (16 * mt + 4 * grp)) = w;
+    }
   }
   uint16_t* dst = a.n_chunks == 1 ? a.out + ((int64_t)r * a.H_q + head0) * DV
                                   : part_out(a, row_local, chunk, DV) + (int64_t)head0 * DV;
@@ -524,35 +539,24 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int cidx = lane & 15, grp = lane >> 4;
 
-  int b = 0, p = -1;
-  if (!resolve_row(a.rows, r, b, p)) {
-    p = -1;
-    if (chunk == 0 && hg == 0 && tid == 0) report(a.err, DSA_DEVERR_ROW);
-  }
   const int slot0 = chunk * g.chunk;
   const int n_slots = max(0, min(a.K, slot0 + g.chunk) - slot0);
   const int nsb = (n_slots + kSB - 1) / kSB;
 
-  // Q^T operand: this lane's head, 8 dims per MFMA step (issued first: the
-  // loads overlap the prologue's dependent index -> block-table loads)
-  const int head = hg * (kHPW * kNW) + wave * kHPW + cidx;
-  const bool head_ok = head < a.H_q;
-  v8s qb[kKS];
-  {
-    const uint16_t* qrow = a.q + ((int64_t)r * a.H_q + (head_ok ? head : 0)) * kDqk + 8 * grp;
-#pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) {
-      const v8s x = *reinterpret_cast<const v8s*>(qrow + 32 * ks);
-      qb[ks] = head_ok ? x : v8s{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-  }
-
-  // ---- prologue: every index of the chunk -> row byte offset (-1: absent);
-  //      ready-made when the Top-K compaction wrote them
+  // ---- prologue: every index of the chunk -> row byte offset (-1: absent).
+  //      Ready-made when the Top-K compaction wrote them (-1 for a row that
+  //      does not resolve, which that kernel has reported): one round trip,
+  //      and nothing else is loaded before it, so the first DMAs go out as
+  //      soon as it is back.
   if (a.rowoff) {
     const int64_t* ro = a.rowoff + (int64_t)row_local * a.K + slot0;
-    for (int i = tid; i < nsb * kSB; i += 64 * kNW) koff[i] = i < n_slots && p >= 0 ? ro[i] : -1;
+    for (int i = tid; i < nsb * kSB; i += 64 * kNW) koff[i] = i < n_slots ? ro[i] : -1;
   } else {
+    int b = 0, p = -1;
+    if (!resolve_row(a.rows, r, b, p)) {
+      p = -1;
+      if (chunk == 0 && hg == 0 && tid == 0) report(a.err, DSA_DEVERR_ROW);
+    }
     const int32_t* idx_row = a.indices + (a.indices_row_offset + row_local) * (int64_t)a.K;
     const int32_t* bt = a.rows.block_table + (int64_t)b * a.rows.max_blocks;
     for (int i = tid; i < nsb * kSB; i += 64 * kNW) {
@@ -592,9 +596,10 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
       const int64_t off = koff[sb * kSB + row];
       src[t] = kbase + (off >= 0 ? off : 0) + 16 * piece;
     }
+    const uint32_t lds0 =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(buf + 1024 * wave * kDmaPerWave));
 #pragma unroll
-    for (int t = 0; t < kDmaPerWave; ++t)
-      dma16(src[t], (uint32_t)(uintptr_t)(buf + 1024 * (wave * kDmaPerWave + t)));
+    for (int t = 0; t < kDmaPerWave; ++t) dma16(src[t], lds0 + 1024 * t);
   };
   auto zero_absent = [&](int sb) {
     uint8_t* buf = tile[sb % NBUF];
@@ -607,6 +612,22 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
     }
   };
 
+  // the first sub-block requested, then Q^T (this lane's head, 8 dims per
+  // MFMA step), then the rest of the prefetch: what the first MFMAs need is
+  // queued ahead of what they do not
+  if (nsb > 0) issue(0);
+  const int head = hg * (kHPW * kNW) + wave * kHPW + cidx;
+  const bool head_ok = head < a.H_q;
+  v8s qb[kKS];
+  {
+    const uint16_t* qrow = a.q + ((int64_t)r * a.H_q + (head_ok ? head : 0)) * kDqk + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      const v8s x = *reinterpret_cast<const v8s*>(qrow + 32 * ks);
+      qb[ks] = head_ok ? x : v8s{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+  for (int x = 1; x < min(NBUF - 1, nsb); ++x) issue(x);
   const float c2 = a.scale * kLog2e;
 
   // Per-lane tile offsets.  Logits: lane (grp, cidx) reads row 16kt + cidx,
@@ -629,10 +650,11 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
   // Softmax reference.  The exponentials are taken against a fixed
   // per-head reference m2, so the accumulators are only ever touched by
   // MFMAs (a rescale would need every accumulator in VGPRs).  First pass:
-  // m2 = the head's max over the first sub-block with a valid key.  Should a
-  // later logit exceed it by more than kSlack (log2 units; exponentials stay
+  // m2 = the head's max over the first sub-block with a valid key (one
+  // cross-lane reduction; the sub-blocks after it need none).  Should a later
+  // logit exceed it by more than kSlack (log2 units; exponentials stay
   // <= 2^kSlack otherwise), the workgroup runs the chunk again with m2 = the
-  // true chunk max, which the first pass has collected by then.  Any
+  // true chunk max, which the first pass has collected lane by lane.  Any
   // reference gives the same softmax; lse uses the same one.
   constexpr float kSlack = 16.0f;
   v4f o[kMT];
@@ -644,12 +666,14 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
     for (int mt = 0; mt < kMT; ++mt) o[mt] = v4f{0.f, 0.f, 0.f, 0.f};
     m2 = m_fix;
     lsum = 0.0f;
-    float m_all = -__builtin_inff();  // the head's max over every logit seen
-    bool over = false;                // (wave) a logit exceeded m2 + kSlack
+    float m_lane = -__builtin_inff();  // max over this lane's logits
+    bool over = false;                 // (wave) a logit exceeded m2 + kSlack
 
-    // NBUF-1 sub-blocks are requested up front; iteration sb requests
-    // sub-block sb+NBUF-1 into the buffer freed by iteration sb-1.
-    for (int x = 0; x < min(NBUF - 1, nsb); ++x) issue(x);
+    // NBUF-1 sub-blocks are requested up front (before the pass loop for the
+    // first pass); iteration sb requests sub-block sb+NBUF-1 into the buffer
+    // freed by iteration sb-1.
+    if (pass > 0)
+      for (int x = 0; x < min(NBUF - 1, nsb); ++x) issue(x);
     for (int sb = 0; sb < nsb; ++sb) {
       wait_vm<kDmaPerWave>(min(nsb - 1 - sb, NBUF - 2));
       const uint32_t valid =
@@ -673,7 +697,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
       // LDS latency is exposed on every step.
       v4f s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
       {
-        constexpr int kSteps = 2 * kKS, kDepth = 8;
+        constexpr int kSteps = 2 * kKS, kDepth = DSA_ATTN_KDEPTH;
         auto frag = [&](int i) {
           const int kk = i >> 1, kt = i & 1;
           return *reinterpret_cast<const v8s*>(buf + ((kk & 1) ? s_odd : s_even) + 128 * (kk >> 1) +
@@ -693,34 +717,47 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // ---- softmax for this lane's head over keys 16kt + 4grp + v
-      float mx = -__builtin_inff();
+      // ---- softmax for this lane's head over keys 16kt + 4grp + v, in log2
+      //      units: t = logit * scale * log2(e) - m2.  Absent keys (only in
+      //      sub-blocks with padding or missing pages) are masked to -inf.
+      if (valid != 0xFFFFFFFFu) {  // wave-uniform
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int key = 16 * kt + 4 * grp + v;
-          const float x = ((valid >> key) & 1u) ? s[kt][v] * c2 : -__builtin_inff();
-          s[kt][v] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));  // -inf only without a valid key
-      m_all = fmaxf(m_all, mx);
-      if (m2 == -__builtin_inff()) m2 = mx;
-      over = over || __ballot(mx > m2 + kSlack) != 0;
-      // past an overrun the pass only collects m_all
+          for (int v = 0; v < 4; ++v)
+            if (!((valid >> (16 * kt + 4 * grp + v)) & 1u)) s[kt][v] = -__builtin_inff();
+      }
+      if (m2 == -__builtin_inff()) {  // wave-uniform: every head sees the same keys
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[kt][v] * c2);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        m2 = fmaxf(mx, __shfl_xor(mx, 32));  // -inf only without a valid key
+      }
       float pv[8];
       float psum = 0.0f;
+      bool hot = false;  // a logit above m2 + kSlack
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float x = s[kt][v];
-          const float e = (over || x == -__builtin_inff()) ? 0.0f : exp2f(x - m2);
-          pv[kt * 4 + v] = e;
-          psum += e;
+          const float t = fmaf(s[kt][v], c2, -m2);  // -inf for masked keys
+          hot = hot || t > kSlack;
+          m_lane = fmaxf(m_lane, s[kt][v] * c2);
+          pv[kt * 4 + v] = t;
         }
+      over = over || __ballot(hot) != 0;
+      // past an overrun the pass only collects the lane maxima; a sub-block
+      // before the first valid key (m2 still -inf, t NaN) adds nothing
+      const bool skip = over || m2 == -__builtin_inff();  // wave-uniform
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float e = skip ? 0.0f : __builtin_amdgcn_exp2f(pv[j]);  // exp2(-inf) = 0
+        pv[j] = e;
+        psum += e;
+      }
       lsum += psum;
       const v8bf pb = __builtin_bit_cast(
           v8bf, (uint4){pack2(pv[0], pv[1]), pack2(pv[2], pv[3]), pack2(pv[4], pv[5]),
@@ -755,7 +792,8 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
     // the last iteration waited for every DMA; the barrier also makes the
     // buffers free for a second pass
     if (!__syncthreads_or(over)) break;
-    m_fix = m_all;
+    m_lane = fmaxf(m_lane, __shfl_xor(m_lane, 16));
+    m_fix = fmaxf(m_lane, __shfl_xor(m_lane, 32));
   }
 
   lsum += __shfl_xor(lsum, 16);
@@ -787,8 +825,8 @@ __device__ __forceinline__ void load_bf16(const uint16_t* p, float* x) {
 
 // Merges the chunks of each (row, head): one wave per head; lane c holds
 // chunk c's (max, sum).  With M the largest max, chunk c weighs
-// w_c = sum_c * 2^(max_c - M); out = sum_c w_c O_c / sum_c w_c, where O_c
-// is the chunk's normalised output.
+// g_c = 2^(max_c - M); out = sum_c g_c O_c / sum_c g_c sum_c, where O_c is
+// the chunk's unnormalised output.
 template <int DV>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   constexpr int PER = DV / 64;  // dims per lane
@@ -809,8 +847,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   for (int i = 0; i < PER; ++i) acc[i] = 0.0f;
   // no branch on M: with every chunk empty all weights are 0, and the
   // output loads below need not wait for the statistics
-  const float f = st.x == -__builtin_inff() ? 0.0f : st.y * exp2f(st.x - M);
-  float Ls = f;
+  const float f = st.x == -__builtin_inff() ? 0.0f : exp2f(st.x - M);
+  float Ls = f * st.y;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) Ls += __shfl_xor(Ls, o);
   // kBatch chunks per round trip: every load of a batch is issued before
