@@ -82,7 +82,8 @@ typedef enum {
 typedef struct {
   const void* base;     /* device address of physical block 0, row 0            */
   int64_t block_stride; /* bytes from one physical block to the next             */
-  int64_t row_stride;   /* bytes from one row (token) to the next inside a block */
+  int64_t row_stride;   /* bytes from one row (token) to the next inside a block;
+                           above 2^24: DSA_ERR_UNSUPPORTED                       */
   int64_t num_blocks;   /* number of physical blocks addressable from base       */
 } dsa_paged;
 

@@ -51,6 +51,8 @@ int check_paged(const dsa_paged& c, int64_t row_bytes) {
   if (c.num_blocks < 1 || c.block_stride <= 0 || c.row_stride <= 0) return DSA_ERR_INVALID;
   if (c.block_stride % 16 || c.row_stride % 16) return DSA_ERR_INVALID;
   if (c.row_stride < row_bytes) return DSA_ERR_INVALID;
+  // kernels address the rows of one block with 32-bit offsets
+  if (c.row_stride > (int64_t(1) << 24)) return DSA_ERR_UNSUPPORTED;
   return DSA_OK;
 }
 

@@ -16,11 +16,13 @@
 // query, so one 16-byte load instruction covers 16 rows x 64 contiguous bytes.
 //
 // Work split.  A workgroup (4 waves) owns a tile of kTile consecutive
-// positions of one row; each wave owns every fourth 16-position sub-tile of
-// it and issues all of their key loads before its first MFMA, so several KiB
-// per wave are in flight.  A sub-tile never straddles a 64-row page; the
-// tile's block ids are fetched once, one per lane.  The query and weights
-// are staged once per workgroup in LDS.
+// positions of one row; each wave owns a quarter of it (kSpan positions, 8
+// sub-tiles of 16) and issues all of their key loads (16 KiB per wave)
+// before its first MFMA.  The tile is sized so that a 4 x 128k decode batch is one round of
+// workgroups at 4 waves per SIMD: every key load is in flight from the start
+// and the memory pipe never drains between rounds.  A sub-tile never
+// straddles a 64-row page; the tile's block ids are fetched once, one per
+// lane.  The query and weights are staged once per workgroup in LDS.
 
 #include "dsa_common.h"
 
@@ -28,64 +30,85 @@ namespace dsa {
 namespace {
 
 #ifndef DSA_IDX_TILE
-#define DSA_IDX_TILE 256
+#define DSA_IDX_TILE 512
 #endif
 constexpr int kTile = DSA_IDX_TILE;  // positions per workgroup
 constexpr int kWaves = 4;
 constexpr int kSub = 16;  // positions per MFMA column block
+constexpr int kSpan = kTile / kWaves;          // consecutive positions per wave
+constexpr int kSubPerWave = kSpan / kSub;      // 8
+static_assert(kSpan % 64 == 0, "a wave's positions are whole 64-position stores");
 
 // This lane's 32-byte K slice of a 128-byte row (D_I = 128): the 16-byte
 // pieces g and g + 4, g = lane / 16.  For D_I = 64 the slice is piece g and
 // 16 zero bytes.  The same rule builds both MFMA operands, so the
 // contraction pairs query and key bytes of the same dimension.
 //
-// `row` must be readable even when `ok` is false (callers point it at valid
-// memory): the load is unconditional and the data is zeroed by a select,
-// which keeps the code free of branches so every wait is exact.
+// `sub` (wave-uniform) points at the first of 16 key rows and `lane_off` is
+// this lane's byte offset in them (its row, plus 16 bytes per slice group).
+// The load is unconditional, which keeps the code free of branches so every
+// wait is exact: callers point `sub` at valid memory even for an absent page
+// and discard such columns afterwards.  A column of the product depends on
+// its own key row alone, so rows past the sequence need no zeroing either.
 template <int NKP>
-__device__ __forceinline__ v8i load_slice(const uint8_t* row, int g, bool ok) {
-  const v4i* src = reinterpret_cast<const v4i*>(row);
-  const v4i lo = src[g];
-  const v4i hi = NKP == 2 ? src[g + 4] : v4i{0, 0, 0, 0};
-  const int m = ok ? -1 : 0;
-  return v8i{lo[0] & m, lo[1] & m, lo[2] & m, lo[3] & m,
-             hi[0] & m, hi[1] & m, hi[2] & m, hi[3] & m};
+__device__ __forceinline__ v8i load_slice(const uint8_t* sub, uint32_t lane_off) {
+  const v4i lo = *reinterpret_cast<const v4i*>(sub + lane_off);
+  const v4i hi = NKP == 2 ? *reinterpret_cast<const v4i*>(sub + lane_off + 64) : v4i{0, 0, 0, 0};
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Sum over the four 16-lane rows of a wave, every lane getting the total.
+// v_permlane16_swap exchanges rows 0<->1 and 2<->3 and v_permlane32_swap the
+// two halves, both in registers; with both operands the same value, the
+// returned pair holds this lane's value and its partner's.
+__device__ __forceinline__ float sum_rows(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// Maximum over aligned groups of G lanes (G = 1, 2, 4 or 8, wave-uniform)
+// with DPP moves: swap neighbours, swap pairs, mirror each half-row.
+__device__ __forceinline__ uint32_t max_lanes(uint32_t k, int G) {
+  if (G >= 2) k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0xB1, 0xF, 0xF, false));
+  if (G >= 4) k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x4E, 0xF, 0xF, false));
+  if (G >= 8) k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x141, 0xF, 0xF, false));
+  return k;
 }
 
 // NKP = D_I / 64 pieces per lane; HT = 16-head tiles (ceil(H_I / 16)).
 template <int NKP, int HT>
-__global__ __launch_bounds__(256) void indexer_scan_kernel(IndexerLaunch a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void indexer_scan_kernel(IndexerLaunch a) {
   const int r = a.row_begin + (int)blockIdx.y;
-  int b, p;
-  if (!resolve_row(a.rows, r, b, p)) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) report(a.err, DSA_DEVERR_ROW);
-    return;
-  }
-  const int L = p + 1;
   const int tile0 = (int)blockIdx.x * kTile;
-  if (tile0 >= L) return;
-
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;  // head row of A, position column of B
   const int g = lane >> 4;    // K slice group
   constexpr int kRowBytes = 64 * NKP;
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[64 * 128];
-  __shared__ float w_lds[64];
+  __shared__ __attribute__((aligned(16))) float w_lds[64];
+  __shared__ float sc_lds[kWaves][kSpan];
+  __shared__ uint32_t gm_lds[kWaves][kSpan / 2];
 
   // Load order matters (vector loads complete in issue order): one round
-  // trip fetches the tile's block ids and the row's query and weights (once
-  // per workgroup, staged in LDS), then every key load is issued, and each
-  // sub-tile is computed as soon as its own keys have landed.
+  // trip fetches the row's length, the tile's block ids and the row's query
+  // and weights (once per workgroup, staged in LDS), then every key load is
+  // issued, and each sub-tile is computed as soon as its own keys have
+  // landed.
 
   // 1. block ids of the tile's pages, one per lane (read back into scalar
-  //    registers per sub-tile); query and weights into LDS, heads past H_I
-  //    as zero
+  //    registers per sub-tile), fetched alongside the row's length rather
+  //    than after it; query and weights into LDS, heads past H_I as zero
   constexpr int kPages = kTile / kBlock;
   static_assert(kPages <= 64, "tile spans more pages than a wave has lanes");
-  const int32_t* bt = a.rows.block_table + (int64_t)b * a.rows.max_blocks;
+  const int b = a.rows.row_seq ? a.rows.row_seq[r] : r;
+  const bool b_ok = b >= 0 && b < a.rows.num_seqs;
+  const int32_t* bt = a.rows.block_table + (int64_t)(b_ok ? b : 0) * a.rows.max_blocks;
   int my_page = -1;
-  if (lane < kPages && tile0 + lane * kBlock < L) my_page = bt[tile0 / kBlock + lane];
+  if (b_ok && lane < kPages && tile0 / kBlock + lane < a.rows.max_blocks)
+    my_page = bt[tile0 / kBlock + lane];
   {
     // the padded query is HT*16 rows of kRowBytes <= 8 KiB: two 16-byte
     // pieces per thread; all loads are issued before any LDS write
@@ -101,69 +124,93 @@ __global__ __launch_bounds__(256) void indexer_scan_kernel(IndexerLaunch a) {
     if (off1 < kQBytes) *reinterpret_cast<v4i*>(&q_lds[off1]) = q1;
     if (threadIdx.x < HT * 16) w_lds[threadIdx.x] = wv;
   }
+  int bb, p;
+  if (!resolve_row(a.rows, r, bb, p)) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) report(a.err, DSA_DEVERR_ROW);
+    return;
+  }
+  const int L = p + 1;
+  if (tile0 >= L) return;
+  if (tile0 + lane * kBlock >= L) my_page = -1;  // pages past the row are not read
 
-  // 2. keys: this wave's sub-tiles j start at tile0 + (wave + kWaves*j)*16.
-  //    Straight-line code lets the compiler wait for each sub-tile alone
-  //    (vmcnt(N)) while the later loads stay in flight.
-  constexpr int kSubPerWave = kTile / (kWaves * kSub);
+  // 2. keys: this wave owns the kSpan positions from w0; sub-tile j starts
+  //    at w0 + 16j.  Straight-line code lets the compiler wait for each
+  //    sub-tile alone (vmcnt(N)) while the later loads stay in flight.
+  const int w0 = tile0 + wave * kSpan;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.kI.base);
+  const uint32_t lane_off = (uint32_t)(col * a.kI.row_stride + 16 * g);
   v8i keys[kSubPerWave];
   bool page_ok[kSubPerWave];
 #pragma unroll
   for (int j = 0; j < kSubPerWave; ++j) {
-    const int s0 = tile0 + (wave + kWaves * j) * kSub;
+    const int s0 = w0 + j * kSub;
     const int phys = __builtin_amdgcn_readlane(my_page, (s0 - tile0) >> 6);
     page_ok[j] = phys >= 0 && (int64_t)phys < a.kI.num_blocks;
-    const uint8_t* row = kbase + (int64_t)(page_ok[j] ? phys : 0) * a.kI.block_stride +
-                         (int64_t)((s0 + col) & 63) * a.kI.row_stride;
-    keys[j] = load_slice<NKP>(row, g, page_ok[j] && s0 + col < L);
+    const uint8_t* sub = kbase + (int64_t)(page_ok[j] ? phys : 0) * a.kI.block_stride +
+                         (int64_t)(s0 & 63) * a.kI.row_stride;
+    keys[j] = load_slice<NKP>(sub, lane_off);
   }
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
-  // A operands (heads 16*ht + col) and the head weights of this lane's
-  // accumulator rows (register v of a 16x16 tile is row 4*g + v)
+  // A operands (heads 16*ht + col); the head weights of this lane's
+  // accumulator rows (register v of a 16x16 tile is row 4*g + v) are read
+  // from LDS per use, which keeps the registers for keys in flight
   v8i aq[HT];
-  float wr[HT][4];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
     const v4i* src = reinterpret_cast<const v4i*>(&q_lds[(16 * ht + col) * kRowBytes]);
     const v4i lo = src[g];
     const v4i hi = NKP == 2 ? src[g + 4] : v4i{0, 0, 0, 0};
     aq[ht] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-    for (int v = 0; v < 4; ++v) wr[ht][v] = w_lds[16 * ht + 4 * g + v];
   }
-  float* out = a.scores + (int64_t)(r - a.row_begin) * a.ld;
-  // Group maxima for the Top-K that follows (groups of G positions, G <= 16
-  // a power of two, so a group never straddles a 16-position sub-tile)
+  // Group maxima for the Top-K that follows: groups of G positions, G <= 8
+  // a power of two, so a group never straddles a 16-position sub-tile
   const int G = a.tw.gmax && L > a.topk_K ? topk_group(L, a.topk_K) : 1;
-  uint32_t* gmax = a.tw.gmax + (int64_t)(r - a.row_begin) * a.tw.gstride;
+  const int lgG = __builtin_ctz(G);
+  // The wave's scores and group maxima are collected in LDS and written
+  // with a few full-width stores at the end, not one narrow store per
+  // sub-tile.
+  float* my_sc = sc_lds[wave];
+  uint32_t* my_gm = gm_lds[wave];
 
+  bool bad_page = false;
 #pragma unroll
   for (int j = 0; j < kSubPerWave; ++j) {
-    const int s0 = tile0 + (wave + kWaves * j) * kSub;
     float part = 0.0f;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       v4f acc = {0.f, 0.f, 0.f, 0.f};
       acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[ht], keys[j], acc, 0, 0, 0, 0,
                                                              0, 0);
+      const v4f wr = *reinterpret_cast<const v4f*>(&w_lds[16 * ht + 4 * g]);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) part += wr[ht][v] * fmaxf(acc[v], 0.0f);
+      for (int v = 0; v < 4; ++v) part += wr[v] * fmaxf(acc[v], 0.0f);
     }
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
-    const int s = s0 + col;
+    part = sum_rows(part);
     // canonical +0 for a zero score; an absent page scores -inf
     const float v = page_ok[j] ? part + 0.0f : -__builtin_inff();
-    if (g == 0 && s < L) out[s] = v;
+    if (g == 0) my_sc[j * kSub + col] = v;
     if (G > 1) {  // wave-uniform
-      uint32_t k = s < L ? score_key(v) : 0u;
-      for (int o = 1; o < G; o <<= 1) k = max(k, (uint32_t)__shfl_xor((int)k, o));
-      if (g == 0 && s < L && (col & (G - 1)) == 0) gmax[s / G] = k;
+      const int s = w0 + j * kSub + col;
+      const uint32_t k = max_lanes(s < L ? score_key(v) : 0u, G);
+      if (g == 0 && (col & (G - 1)) == 0) my_gm[(j * kSub + col) >> lgG] = k;
     }
-    if (s0 < L && !page_ok[j] && lane == 0) report(a.err, DSA_DEVERR_BLOCK);
+    bad_page = bad_page || (w0 + j * kSub < L && !page_ok[j]);
   }
+  // LDS accesses of one wave complete in order; the fence keeps the
+  // compiler from moving the reads above the writes of other lanes
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  float* out = a.scores + (int64_t)(r - a.row_begin) * a.ld;
+#pragma unroll
+  for (int h = 0; h < kSpan / 64; ++h) {
+    const int i = 64 * h + lane;
+    if (w0 + i < L) out[w0 + i] = my_sc[i];
+  }
+  if (G > 1 && lane < (kSpan >> lgG) && w0 + (lane << lgG) < L) {
+    uint32_t* gmax = a.tw.gmax + (int64_t)(r - a.row_begin) * a.tw.gstride;
+    gmax[(w0 >> lgG) + lane] = my_gm[lane];
+  }
+  if (bad_page && lane == 0) report(a.err, DSA_DEVERR_BLOCK);
 }
 
 template <int NKP, int HT>
