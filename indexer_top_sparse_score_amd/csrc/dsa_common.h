@@ -82,12 +82,26 @@ __host__ __device__ inline int64_t topk_gstride(int64_t max_len) {
   return ((max_len + 1) / 2 + 3) & ~int64_t(3);
 }
 
-// The Top-K's work area, carved from the caller's workspace: the maximum
-// key of every group of every row, [rows][gstride] (rows with G = 1 leave
-// theirs unused).
+// The Top-K's work area, carved from the caller's workspace:
+//  - gmax [rows][gstride]: the maximum key of every group of every row (rows
+//    with G = 1 leave theirs unused);
+//  - ckey, cpos [rows][cstride]: the candidate keys and positions that the
+//    workgroups of a row's slices hand to the one that finishes the row
+//    (slice j's entries start at j * kTopkSliceGroups * G);
+//  - ccount [rows][kTopkSlices]: how many candidates each slice left;
+//  - arrive [rows]: slices of the row done so far.  Whichever kernel writes
+//    gmax for a call (the fused indexer, or the standalone group-maximum
+//    pass) zeroes it first.
+constexpr int kTopkSlices = 16;         // workgroups per row, at most
+constexpr int kTopkSliceGroups = 1024;  // groups per slice (one per thread)
 struct TopkWork {
   uint32_t* gmax;
   int64_t gstride;
+  uint32_t* ckey;
+  int32_t* cpos;
+  int64_t cstride;
+  uint32_t* ccount;
+  uint32_t* arrive;
 };
 // bytes of the work area for `rows` rows of history up to max_len
 size_t topk_work_bytes(int rows, int64_t max_len);

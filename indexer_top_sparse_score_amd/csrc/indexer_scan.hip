@@ -82,6 +82,8 @@ template <int NKP, int HT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void indexer_scan_kernel(IndexerLaunch a) {
   const int r = a.row_begin + (int)blockIdx.y;
   const int tile0 = (int)blockIdx.x * kTile;
+  // the Top-K that follows counts its row's finished slices from zero
+  if (a.tw.arrive && blockIdx.x == 0 && threadIdx.x == 0) a.tw.arrive[blockIdx.y] = 0;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;  // head row of A, position column of B

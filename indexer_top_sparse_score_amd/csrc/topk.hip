@@ -58,6 +58,8 @@ constexpr int kKeysPer = 8;               // compacted keys per thread
 constexpr int kMaxKeys = kKeysPer * kT;   // 8192
 constexpr int kBtCache = 2048;            // block-table entries cached in LDS
 constexpr int kScanWords = 4 * kWaves + 1;
+constexpr int kSegRead = kT / kTopkSlices;  // threads reading one slice's candidates (64)
+static_assert(kSegRead * kKeysPer * kTopkSlices == kMaxKeys, "slice-major candidate layout");
 static_assert(kBins == 2 * kT, "find_bin gives each thread two bins");
 
 struct Smem {
@@ -541,36 +543,31 @@ __device__ __forceinline__ bool select_fast(const float* sc, int L, int K, bool 
   }
 }
 
-__global__ __launch_bounds__(kT) void topk_row_kernel(TopkLaunch a) {
-  __shared__ Smem s;
-  const int tid = threadIdx.x;
-  const int r_local = (int)blockIdx.x;
-  const int K = a.K;
-  // independent loads first: this thread's share of the group maxima (the
-  // row's slice is gstride long, whatever the row's length turns out to be)
-  uint32_t gm[kPerThread];
-  {
-    const uint32_t* src = a.tw.gmax + (int64_t)r_local * a.tw.gstride;
-    const int g0 = kPerThread * tid;
-    if (g0 + kPerThread <= a.tw.gstride) {
+// This thread's share of a row's group maxima, 16t .. 16t+15 (the row's
+// slice is gstride long, whatever the row's length turns out to be).
+__device__ __forceinline__ void load_gmax(const TopkLaunch& a, int r_local,
+                                          uint32_t (&gm)[kPerThread]) {
+  const uint32_t* src = a.tw.gmax + (int64_t)r_local * a.tw.gstride;
+  const int g0 = kPerThread * (int)threadIdx.x;
+  if (g0 + kPerThread <= a.tw.gstride) {
 #pragma unroll
-      for (int j = 0; j < kPerThread; j += 4) {
-        const uint4 v = *reinterpret_cast<const uint4*>(src + g0 + j);
-        gm[j] = v.x;
-        gm[j + 1] = v.y;
-        gm[j + 2] = v.z;
-        gm[j + 3] = v.w;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kPerThread; ++j) gm[j] = g0 + j < a.tw.gstride ? src[g0 + j] : 0u;
+    for (int j = 0; j < kPerThread; j += 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src + g0 + j);
+      gm[j] = v.x;
+      gm[j + 1] = v.y;
+      gm[j + 2] = v.z;
+      gm[j + 3] = v.w;
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) gm[j] = g0 + j < a.tw.gstride ? src[g0 + j] : 0u;
   }
-  int b = 0, p;
-  const int L = resolve_row(a.rows, a.row_begin + r_local, b, p) ? p + 1 : 0;
+}
+
+__device__ __forceinline__ Out make_out(const TopkLaunch& a, int r_local, int b) {
   Out o;
-  o.idx = a.indices + (int64_t)r_local * K;
-  o.roff = a.rowoff ? a.rowoff + (int64_t)r_local * K : nullptr;
+  o.idx = a.indices + (int64_t)r_local * a.K;
+  o.roff = a.rowoff ? a.rowoff + (int64_t)r_local * a.K : nullptr;
   o.bt = a.rows.block_table + (int64_t)b * a.rows.max_blocks;
   o.bt_lds = nullptr;
   o.kv_blocks = a.kv.num_blocks;
@@ -578,6 +575,24 @@ __global__ __launch_bounds__(kT) void topk_row_kernel(TopkLaunch a) {
   o.kv_row_stride = a.kv.row_stride;
   o.err = a.err;
   o.pos = nullptr;
+  return o;
+}
+
+// Copies the row's block table to LDS when the KV row offsets are wanted and
+// it fits (read while the selection runs; flush() uses it).
+__device__ __forceinline__ void cache_block_table(int L, Out& o, Smem& s) {
+  const int nblk = (L + kBlock - 1) / kBlock;
+  if (o.roff && nblk <= kBtCache) {
+    for (int i = threadIdx.x; i < nblk; i += kT) s.bt[i] = o.bt[i];
+    o.bt_lds = s.bt;
+  }
+}
+
+// A whole row in one workgroup: every path but the split one.
+__device__ __forceinline__ void row_single(const TopkLaunch& a, int r_local, int L,
+                                           uint32_t (&gm)[kPerThread], Out& o, Smem& s) {
+  const int tid = threadIdx.x;
+  const int K = a.K;
   if (tid == 0 && a.counts) a.counts[r_local] = min(K, L);
   if (L <= K) {  // keep the whole history (nothing for an invalid row)
     for (int j = tid; j < K; j += kT) {
@@ -595,11 +610,7 @@ __global__ __launch_bounds__(kT) void topk_row_kernel(TopkLaunch a) {
     select_streamed<false>(sc, L, K, a.vec, o, s);
     return;
   }
-  const int nblk = (L + kBlock - 1) / kBlock;
-  if (o.roff && nblk <= kBtCache) {  // the row's block table, read while selecting
-    for (int i = tid; i < nblk; i += kT) s.bt[i] = o.bt[i];
-    o.bt_lds = s.bt;
-  }
+  cache_block_table(L, o, s);
   o.pos = s.hist;
   if (!(K <= kMaxCand - kT && select_fast(sc, L, K, a.vec, gm, o, s)))
     select_streamed<true>(sc, L, K, a.vec, o, s);
@@ -607,10 +618,220 @@ __global__ __launch_bounds__(kT) void topk_row_kernel(TopkLaunch a) {
   o.flush(K);
 }
 
+__global__ __launch_bounds__(kT) void topk_row_kernel(TopkLaunch a) {
+  __shared__ Smem s;
+  const int r_local = (int)blockIdx.x;
+  uint32_t gm[kPerThread];
+  load_gmax(a, r_local, gm);  // independent loads first
+  int b = 0, p;
+  const int L = resolve_row(a.rows, a.row_begin + r_local, b, p) ? p + 1 : 0;
+  Out o = make_out(a, r_local, b);
+  row_single(a, r_local, L, gm, o, s);
+}
+
+// ---------------------------------------------------------- split rows
+// A row whose group maxima are known is spread over up to kTopkSlices
+// workgroups, one per slice of kTopkSliceGroups groups:
+//  a. every workgroup computes t from all the row's group maxima (the same
+//     integer arithmetic on the same data, so the same t everywhere);
+//  b. each keeps its slice's keys >= t and writes them, with their
+//     positions and in position order, to its segment of the work area;
+//  c. the last workgroup of the row to finish (a device-scope fence, then a
+//     counter) reads the segments back in slice order -- position order --
+//     selects T and the tie budget exactly and writes the row out.
+// Nothing waits on another workgroup.  Rows that do not take this path run
+// row_single in slice 0's workgroup.
+
+// The G keys of group g (positions past L as 0).
+template <int G>
+__device__ __forceinline__ void group_keys(const float* sc, int g, int L, bool vec,
+                                           uint32_t (&k)[kMaxGroup]) {
+  uint32_t kk[G];
+  load_keys<G>(sc, g * G, L, vec && G >= 4, kk);
+#pragma unroll
+  for (int j = 0; j < kMaxGroup; ++j) k[j] = j < G ? kk[j] : 0u;
+}
+
+__global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
+  __shared__ Smem s;
+  const int tid = threadIdx.x;
+  const int slice = (int)blockIdx.x;
+  const int r_local = (int)blockIdx.y;
+  const int K = a.K;
+  uint32_t gm[kPerThread];
+  load_gmax(a, r_local, gm);  // independent loads first
+  int b = 0, p;
+  const int L = resolve_row(a.rows, a.row_begin + r_local, b, p) ? p + 1 : 0;
+  Out o = make_out(a, r_local, b);
+  const int G = L > 0 ? topk_group(L, K) : 1;
+  const int N = (L + G - 1) / G;
+  if (!(L > K && G > 1 && K <= kBins && K <= kMaxCand - kT && N <= kMaxN)) {
+    if (slice == 0) row_single(a, r_local, L, gm, o, s);
+    return;
+  }
+  const int S = (N + kTopkSliceGroups - 1) / kTopkSliceGroups;
+  if (slice >= S) return;
+
+  // this thread's group of the slice: its keys, loaded now, used after t
+  const float* sc = a.scores + (int64_t)r_local * a.ld;
+  const int g = slice * kTopkSliceGroups + tid;
+  uint32_t k[kMaxGroup];
+  switch (G) {
+    case 2: group_keys<2>(sc, g, L, a.vec, k); break;
+    case 4: group_keys<4>(sc, g, L, a.vec, k); break;
+    default: group_keys<kMaxGroup>(sc, g, L, a.vec, k); break;
+  }
+  if (slice == 0 && tid == 0 && a.counts) a.counts[r_local] = K;
+  // the row's block ids for the KV row offsets: loaded now, staged in LDS
+  // only by the workgroup that writes the row out
+  constexpr int kBtPer = kBtCache / kT;
+  const int nblk = (L + kBlock - 1) / kBlock;
+  const bool bt_cached = o.roff && nblk <= kBtCache;
+  int32_t btv[kBtPer];
+#pragma unroll
+  for (int j = 0; j < kBtPer; ++j) {
+    const int i = tid + j * kT;
+    btv[j] = bt_cached && i < nblk ? o.bt[i] : 0;
+  }
+
+  // a. t = lower edge of the bin holding the K-th largest group maximum
+  const int g0 = kPerThread * tid;
+  const int n_mine = max(0, min(kPerThread, N - g0));
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j)
+    if (j < n_mine) {
+      kmin = min(kmin, gm[j]);
+      kmax = max(kmax, gm[j]);
+    }
+  block_minmax(kmin, kmax, s.red);
+  uint32_t t = kmin;
+  if (kmin < kmax) {
+    auto visit = [&](auto f) {
+#pragma unroll
+      for (int j = 0; j < kPerThread; ++j)
+        if (j < n_mine) f(gm[j]);
+    };
+    const int shift = range_shift(kmin, kmax);
+    histogram_bin(visit, kmin, kmax, shift, (uint32_t)K, s);
+    t = kmin + (s.res[0] << shift);
+  }
+  o.pos = s.hist;
+  if (t == 0) {  // NaN scores at the threshold: the general path, once
+    if (slice == 0) {
+      __syncthreads();
+      select_streamed<true>(sc, L, K, a.vec, o, s);
+      __syncthreads();
+      o.flush(K);
+    }
+    return;
+  }
+
+  // b. this slice's keys >= t (t >= 1: positions past L never count)
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxGroup; ++j) c += (j < G && k[j] >= t) ? 1u : 0u;
+  uint32_t n_slice;
+  uint32_t at = block_scan(c, s.wsum, n_slice);
+  {
+    const int64_t seg = (int64_t)r_local * a.tw.cstride + (int64_t)slice * kTopkSliceGroups * G;
+#pragma unroll
+    for (int j = 0; j < kMaxGroup; ++j)
+      if (j < G && k[j] >= t) {
+        a.tw.ckey[seg + at] = k[j];
+        a.tw.cpos[seg + at] = g * G + j;
+        ++at;
+      }
+    if (tid == 0) a.tw.ccount[r_local * kTopkSlices + slice] = n_slice;
+  }
+
+  // c. the last slice to finish completes the row.  The barrier orders the
+  //    workgroup's stores before thread 0's device-scope release (a
+  //    cumulative fence: one per workgroup, since each writes back the L2)
+  //    and counter update; the last workgroup's thread 0 acquires before
+  //    the barrier that releases its other threads to read.
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    const uint32_t done = atomicAdd(&a.tw.arrive[r_local], 1u);
+    if (done == (uint32_t)(S - 1)) __threadfence();
+    s.res[3] = done == (uint32_t)(S - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (s.res[3] == 0) return;
+  if (bt_cached) {
+#pragma unroll
+    for (int j = 0; j < kBtPer; ++j) s.bt[tid + j * kT] = btv[j];
+    o.bt_lds = s.bt;  // read after the barriers of the selection below
+  }
+  // Thread t reads entries 8 (t mod 64) .. +7 of slice t / 64 together with
+  // the counts (no round trip between them); in thread order that is
+  // position order.  A slice with more than 512 candidates sends the row
+  // to the general path.
+  const int my_slice = tid / kSegRead;
+  const int e0 = kKeysPer * (tid % kSegRead);
+  const int64_t seg = (int64_t)r_local * a.tw.cstride + (int64_t)my_slice * kTopkSliceGroups * G;
+  // A slice's candidates end at or before the row's end of the area, so
+  // entries past it are never wanted (and not read).  Segments start on
+  // 16-byte boundaries: two 16-byte loads each for keys and positions.
+  const int64_t row_end = (int64_t)(r_local + 1) * a.tw.cstride;
+  uint32_t kk[kKeysPer];
+  int32_t pp[kKeysPer];
+  if (my_slice < S && seg + e0 + kKeysPer <= row_end) {
+#pragma unroll
+    for (int j = 0; j < kKeysPer; j += 4) {
+      const uint4 kv = *reinterpret_cast<const uint4*>(a.tw.ckey + seg + e0 + j);
+      const int4 pv = *reinterpret_cast<const int4*>(a.tw.cpos + seg + e0 + j);
+      kk[j] = kv.x; kk[j + 1] = kv.y; kk[j + 2] = kv.z; kk[j + 3] = kv.w;
+      pp[j] = pv.x; pp[j + 1] = pv.y; pp[j + 2] = pv.z; pp[j + 3] = pv.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kKeysPer; ++j) {
+      const bool in = my_slice < S && seg + e0 + j < row_end;
+      kk[j] = in ? a.tw.ckey[seg + e0 + j] : 0u;
+      pp[j] = in ? a.tw.cpos[seg + e0 + j] : 0;
+    }
+  }
+  uint32_t cnt[kTopkSlices];
+  uint32_t n_tot = 0, c_max = 0;
+#pragma unroll
+  for (int j = 0; j < kTopkSlices; ++j) {
+    cnt[j] = j < S ? a.tw.ccount[r_local * kTopkSlices + j] : 0u;
+    n_tot += cnt[j];
+    c_max = max(c_max, cnt[j]);
+  }
+  if (n_tot > (uint32_t)kMaxKeys || c_max > (uint32_t)(kSegRead * kKeysPer)) {
+    // heavy ties at t: the general path
+    select_streamed<true>(sc, L, K, a.vec, o, s);
+  } else {
+    uint32_t c_mine = 0;
+#pragma unroll
+    for (int j = 0; j < kTopkSlices; ++j) c_mine = j == my_slice ? cnt[j] : c_mine;
+    const int n = max(0, min(kKeysPer, (int)c_mine - e0));
+#pragma unroll
+    for (int j = 0; j < kKeysPer; ++j) kk[j] = j < n ? kk[j] : 0u;
+    auto visit = [&](auto f) {
+#pragma unroll
+      for (int j = 0; j < kKeysPer; ++j)
+        if (j < n) f(kk[j]);
+    };
+    uint32_t need = (uint32_t)K;
+    const uint32_t T = select_kth(visit, t, kmax, need, s);
+    uint32_t eq_before = 0, out_before = 0;
+    emit_runs<kKeysPer, true>(kk, n, [&](int j) { return pp[j]; }, T, need, eq_before,
+                              out_before, o, s);
+  }
+  __syncthreads();
+  o.flush(K);
+  if (tid == 0) a.tw.arrive[r_local] = 0;
+}
+
 // Group maxima for a standalone Top-K call: thread -> one group of its row.
 __global__ __launch_bounds__(256) void topk_group_max_kernel(TopkLaunch a) {
   int b, p;
   const int r_local = (int)blockIdx.y;
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.tw.arrive[r_local] = 0;
   if (!resolve_row(a.rows, a.row_begin + r_local, b, p)) return;
   const int L = p + 1;
   if (L <= a.K) return;
@@ -628,15 +849,30 @@ __global__ __launch_bounds__(256) void topk_group_max_kernel(TopkLaunch a) {
 
 }  // namespace
 
+namespace {
+int64_t cstride_of(int64_t max_len) { return (max_len + 63) & ~int64_t(63); }
+}  // namespace
+
 size_t topk_work_bytes(int rows, int64_t max_len) {
-  return (size_t)rows * (size_t)topk_gstride(max_len) * sizeof(uint32_t);
+  const size_t words = (size_t)topk_gstride(max_len) + 2 * (size_t)cstride_of(max_len) +
+                       kTopkSlices + 1;
+  return (size_t)rows * words * sizeof(uint32_t);
 }
 
 TopkWork topk_work_carve(void* base, int rows, int64_t max_len) {
-  (void)rows;
   TopkWork w;
-  w.gmax = static_cast<uint32_t*>(base);
+  uint32_t* p = static_cast<uint32_t*>(base);
   w.gstride = topk_gstride(max_len);
+  w.cstride = cstride_of(max_len);
+  w.gmax = p;
+  p += (size_t)rows * w.gstride;
+  w.ckey = p;
+  p += (size_t)rows * w.cstride;
+  w.cpos = reinterpret_cast<int32_t*>(p);
+  p += (size_t)rows * w.cstride;
+  w.ccount = p;
+  p += (size_t)rows * kTopkSlices;
+  w.arrive = p;
   return w;
 }
 
@@ -648,7 +884,11 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  topk_row_kernel<<<a.num_rows, kT, 0, s>>>(a);
+  if (a.tw.arrive) {
+    topk_split_kernel<<<dim3(kTopkSlices, a.num_rows), kT, 0, s>>>(a);
+  } else {
+    topk_row_kernel<<<a.num_rows, kT, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

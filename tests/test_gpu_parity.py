@@ -91,7 +91,7 @@ def test_topk_ties_and_special_values():
     # (the last rows are long enough to group positions, and their ties or
     # NaNs send them down the streamed path)
     wl = small_workload("ties", lengths=[5000, 5000, 5000, 5000, 3000, 2049, 20000, 40000,
-                                         40000, 9000], **MLA)
+                                         40000, 9000, 131072], **MLA)
     batch = make_batch(wl, device="cuda", seed=24)
     rng = np.random.default_rng(24)
     ld = 64 * batch.max_blocks
@@ -110,6 +110,9 @@ def test_topk_ties_and_special_values():
     x = rng.standard_normal(L[9]).astype(np.float32)                # a few exact ties near
     x[rng.choice(L[9], 300, replace=False)] = np.sort(x)[-2100]     # the threshold, G = 2
     sc[9, :L[9]] = x
+    # 16 slices of 1024 groups of 8: scores on a 1/64 grid tie some 80 ways at
+    # the threshold, so the budget of keys equal to T spans several slices
+    sc[10, :L[10]] = np.round(rng.standard_normal(L[10]) * 64) / 64
     idx, cnt = gpu_topk(batch, torch.from_numpy(sc).cuda())
     for i in range(batch.rows):
         want, n = oracle.topk_row(sc[i, :L[i]], wl.K)
