@@ -1,0 +1,79 @@
+"""GPU parity at the full workload sizes, through dsa_decode_step as the
+benchmark launches it (one call over the whole batch, workspace from
+dsa_workspace_size, the default stream).
+
+Every row is checked for what holds at any size: the count is min(K, L),
+the kept positions are ascending, distinct and inside the history, the
+rest is -1, and the output is finite with no device error.  Sampled rows
+(the first, the last, the longest and shortest history, and a seeded
+random pick) are compared element by element with the oracle: integer
+mode -- indices bit-exact and attention within tolerance; Gaussian mode
+on the benchmark shape -- Top-K recall >= 0.999 and attention within
+tolerance on the rows whose selection matches."""
+
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_helpers import RECALL_MIN, check_attention, gpu_decode, np_, recall, say
+from tests.helpers import run_oracle
+from workloads import BENCH_WORKLOAD, CONFIGS, make_batch, oracle_arrays, row_positions
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_rows(batch, seed):
+    n = batch.rows
+    lens = [p + 1 for _, p in row_positions(batch)]
+    rows = {0, n - 1, int(np.argmax(lens)), int(np.argmin(lens))}
+    if n > 2:
+        rows.add(int(np.random.default_rng(seed).integers(1, n - 1)))
+    return sorted(rows)
+
+
+def _check_every_row(batch, res):
+    K = batch.wl.K
+    gi = np_(res["indices"])
+    cnt = np_(res["counts"])
+    for i, (_, p) in enumerate(row_positions(batch)):
+        n = min(K, p + 1)
+        assert int(cnt[i]) == n, f"row {i}: count {cnt[i]} != {n}"
+        sel = gi[i, :n]
+        assert (np.diff(sel) > 0).all(), f"row {i}: not ascending"
+        assert sel[0] >= 0 and sel[-1] <= p, f"row {i}: outside the history"
+        assert (gi[i, n:] == -1).all(), f"row {i}: padding"
+    assert torch.isfinite(res["out"].float()).all()
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_full_size_integer_mode(name):
+    wl = CONFIGS[name]
+    say(f"full size {name}: {wl.batch} sequences, integer mode, seed {wl.seed}")
+    batch = make_batch(wl, device="cuda", seed=wl.seed, mode="int")
+    res = gpu_decode(batch)
+    _check_every_row(batch, res)
+    rows = _sample_rows(batch, wl.seed)
+    say(f"  oracle rows {rows}")
+    orc = run_oracle(oracle_arrays(batch, rows=rows), keep_scores=False)
+    assert (np_(res["counts"])[rows] == orc["counts"]).all()
+    gi = np_(res["indices"])[rows]
+    for j, r in enumerate(rows):
+        assert (gi[j] == orc["indices"][j]).all(), f"row {r}: indices differ"
+    check_attention(res["out"][rows], res["lse"][rows], orc["out"], orc["lse"])
+
+
+def test_full_size_gaussian_bench_shape():
+    wl = CONFIGS[BENCH_WORKLOAD]
+    say(f"full size {BENCH_WORKLOAD}: Gaussian mode, seed {wl.seed}")
+    batch = make_batch(wl, device="cuda", seed=wl.seed, mode="gauss")
+    res = gpu_decode(batch)
+    _check_every_row(batch, res)
+    rows = list(range(batch.rows))
+    orc = run_oracle(oracle_arrays(batch, rows=rows), keep_scores=False)
+    gi = np_(res["indices"])
+    rec, worst = recall(gi, orc["indices"], orc["counts"])
+    say(f"  recall {rec:.6f} (worst row {worst:.6f})")
+    assert rec >= RECALL_MIN
+    same = [i for i in rows if (gi[i] == orc["indices"][i]).all()]
+    if same:
+        check_attention(res["out"][same], res["lse"][same], orc["out"][same], orc["lse"][same])
