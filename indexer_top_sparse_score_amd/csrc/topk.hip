@@ -199,11 +199,15 @@ __device__ __forceinline__ int range_shift(uint32_t lo, uint32_t hi) {
 // Histogram of the keys in [lo, hi] that visit(f) hands to f, on 2048 bins
 // of width 2^shift from lo, and the bin b holding the need-th largest
 // (res[0] = b, res[1] = keys above b).
-template <class Visit>
+// With kZeroed the caller has already cleared the histogram (and a barrier
+// has passed since).
+template <bool kZeroed = false, class Visit>
 __device__ __forceinline__ void histogram_bin(Visit&& visit, uint32_t lo, uint32_t hi, int shift,
                                               uint32_t need, Smem& s) {
-  for (int i = threadIdx.x; i < kBins; i += kT) s.hist[i] = 0;
-  __syncthreads();
+  if (!kZeroed) {
+    for (int i = threadIdx.x; i < kBins; i += kT) s.hist[i] = 0;
+    __syncthreads();
+  }
   visit([&](uint32_t k) {
     if (k >= lo && k <= hi) atomicAdd(&s.hist[(k - lo) >> shift], 1u);
   });
@@ -642,14 +646,27 @@ __global__ __launch_bounds__(kT) void topk_row_kernel(TopkLaunch a) {
 // Nothing waits on another workgroup.  Rows that do not take this path run
 // row_single in slice 0's workgroup.
 
-// The G keys of group g (positions past L as 0).
+// The G scores of group g as raw bits (positions past L as 0); converted to
+// keys only once they are needed, so nothing waits for them earlier.
 template <int G>
-__device__ __forceinline__ void group_keys(const float* sc, int g, int L, bool vec,
-                                           uint32_t (&k)[kMaxGroup]) {
-  uint32_t kk[G];
-  load_keys<G>(sc, g * G, L, vec && G >= 4, kk);
+__device__ __forceinline__ void group_scores(const float* sc, int g, int L, bool vec,
+                                             uint32_t (&x)[kMaxGroup]) {
+  const int i0 = g * G;
 #pragma unroll
-  for (int j = 0; j < kMaxGroup; ++j) k[j] = j < G ? kk[j] : 0u;
+  for (int j = 0; j < kMaxGroup; ++j) x[j] = 0u;
+  if (vec && G >= 4 && i0 + G <= L) {
+#pragma unroll
+    for (int j = 0; j < G; j += 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(sc + i0 + j);
+      x[j] = v.x;
+      x[j + 1] = v.y;
+      x[j + 2] = v.z;
+      x[j + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < G; ++j) x[j] = i0 + j < L ? __float_as_uint(sc[i0 + j]) : 0u;
+  }
 }
 
 __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
@@ -677,10 +694,12 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
   const int g = slice * kTopkSliceGroups + tid;
   uint32_t k[kMaxGroup];
   switch (G) {
-    case 2: group_keys<2>(sc, g, L, a.vec, k); break;
-    case 4: group_keys<4>(sc, g, L, a.vec, k); break;
-    default: group_keys<kMaxGroup>(sc, g, L, a.vec, k); break;
+    case 2: group_scores<2>(sc, g, L, a.vec, k); break;
+    case 4: group_scores<4>(sc, g, L, a.vec, k); break;
+    default: group_scores<kMaxGroup>(sc, g, L, a.vec, k); break;
   }
+  const int n_valid = max(0, min(G, L - g * G));
+  for (int i = tid; i < kBins; i += kT) s.hist[i] = 0;  // for step a; block_minmax syncs
   if (slice == 0 && tid == 0 && a.counts) a.counts[r_local] = K;
   // the row's block ids for the KV row offsets: loaded now, staged in LDS
   // only by the workgroup that writes the row out
@@ -713,7 +732,7 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
         if (j < n_mine) f(gm[j]);
     };
     const int shift = range_shift(kmin, kmax);
-    histogram_bin(visit, kmin, kmax, shift, (uint32_t)K, s);
+    histogram_bin<true>(visit, kmin, kmax, shift, (uint32_t)K, s);
     t = kmin + (s.res[0] << shift);
   }
   o.pos = s.hist;
@@ -727,7 +746,9 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
     return;
   }
 
-  // b. this slice's keys >= t (t >= 1: positions past L never count)
+  // b. this slice's keys >= t (t >= 1: positions past L, key 0, never count)
+#pragma unroll
+  for (int j = 0; j < kMaxGroup; ++j) k[j] = j < n_valid ? score_key(__uint_as_float(k[j])) : 0u;
   uint32_t c = 0;
 #pragma unroll
   for (int j = 0; j < kMaxGroup; ++j) c += (j < G && k[j] >= t) ? 1u : 0u;
