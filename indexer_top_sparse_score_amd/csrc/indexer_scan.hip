@@ -107,33 +107,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
   static_assert(kPages <= 64, "tile spans more pages than a wave has lanes");
   const int b = a.rows.row_seq ? a.rows.row_seq[r] : r;
   const bool b_ok = b >= 0 && b < a.rows.num_seqs;
+  // Every load of this round trip is unconditional, from a clamped
+  // (always valid) address, and selected afterwards: a branch, or a value
+  // kept in a scalar register, would make the compiler wait for each load
+  // where it is taken.  The row's length and position stay in vector
+  // registers (the empty asm hides their uniformity) until they are checked.
+  typedef __attribute__((address_space(1))) const int32_t gint;  // global, not flat
+  gint* len_at = (gint*)(a.rows.seq_lens + (b_ok ? b : 0));
+  gint* pos_at = (gint*)(a.rows.row_pos ? a.rows.row_pos + r : a.rows.seq_lens);
+  asm volatile("" : "+v"(len_at), "+v"(pos_at));
+  const int len_v = *len_at;
+  const int pos_v = *pos_at;
   const int32_t* bt = a.rows.block_table + (int64_t)(b_ok ? b : 0) * a.rows.max_blocks;
-  int my_page = -1;
-  if (b_ok && lane < kPages && tile0 / kBlock + lane < a.rows.max_blocks)
-    my_page = bt[tile0 / kBlock + lane];
+  // block id of the tile's page `lane` (lanes past the tile's pages, or past
+  // the table's columns, read a valid entry that is never used)
+  const int my_page = bt[min(tile0 / kBlock + lane, a.rows.max_blocks - 1)];
   {
     // the padded query is HT*16 rows of kRowBytes <= 8 KiB: two 16-byte
     // pieces per thread; all loads are issued before any LDS write
     const uint8_t* qrow = a.qI + (int64_t)r * a.H_I * kRowBytes;
-    const int qbytes = a.H_I * kRowBytes;
+    const int qbytes = a.H_I * kRowBytes;  // a multiple of 64
     constexpr int kQBytes = HT * 16 * kRowBytes;
     const int off0 = threadIdx.x * 16, off1 = off0 + 256 * 16;
     const v4i z = v4i{0, 0, 0, 0};
-    const v4i q0 = off0 < qbytes ? *reinterpret_cast<const v4i*>(qrow + off0) : z;
-    const v4i q1 = off1 < qbytes ? *reinterpret_cast<const v4i*>(qrow + off1) : z;
-    const float wv = threadIdx.x < a.H_I ? a.w[(int64_t)r * a.H_I + threadIdx.x] : 0.0f;
+    v4i q0 = *reinterpret_cast<const v4i*>(qrow + min(off0, qbytes - 16));
+    v4i q1 = *reinterpret_cast<const v4i*>(qrow + min(off1, qbytes - 16));
+    float wv = a.w[(int64_t)r * a.H_I + min((int)threadIdx.x, a.H_I - 1)];
+    q0 = off0 < qbytes ? q0 : z;
+    q1 = off1 < qbytes ? q1 : z;
+    wv = (int)threadIdx.x < a.H_I ? wv : 0.0f;
     if (off0 < kQBytes) *reinterpret_cast<v4i*>(&q_lds[off0]) = q0;
     if (off1 < kQBytes) *reinterpret_cast<v4i*>(&q_lds[off1]) = q1;
     if (threadIdx.x < HT * 16) w_lds[threadIdx.x] = wv;
   }
-  int bb, p;
-  if (!resolve_row(a.rows, r, bb, p)) {
+  const int len = __builtin_amdgcn_readfirstlane(len_v);
+  const int pos_given = __builtin_amdgcn_readfirstlane(pos_v);
+  // the same checks as resolve_row, on the values loaded above
+  const int p = a.rows.row_pos ? pos_given : len - 1;
+  if (!b_ok || p < 0 || p >= len || p >= a.rows.max_blocks * kBlock) {
     if (blockIdx.x == 0 && threadIdx.x == 0) report(a.err, DSA_DEVERR_ROW);
     return;
   }
   const int L = p + 1;
   if (tile0 >= L) return;
-  if (tile0 + lane * kBlock >= L) my_page = -1;  // pages past the row are not read
 
   // 2. keys: this wave owns the kSpan positions from w0; sub-tile j starts
   //    at w0 + 16j.  Straight-line code lets the compiler wait for each
@@ -147,7 +163,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
   for (int j = 0; j < kSubPerWave; ++j) {
     const int s0 = w0 + j * kSub;
     const int phys = __builtin_amdgcn_readlane(my_page, (s0 - tile0) >> 6);
-    page_ok[j] = phys >= 0 && (int64_t)phys < a.kI.num_blocks;
+    // a page past the table's columns, or with an id out of range, is absent
+    page_ok[j] = s0 / kBlock < a.rows.max_blocks && phys >= 0 && (int64_t)phys < a.kI.num_blocks;
     const uint8_t* sub = kbase + (int64_t)(page_ok[j] ? phys : 0) * a.kI.block_stride +
                          (int64_t)(s0 & 63) * a.kI.row_stride;
     keys[j] = load_slice<NKP>(sub, lane_off);
