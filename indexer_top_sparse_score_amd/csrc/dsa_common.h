@@ -40,6 +40,37 @@ __device__ __forceinline__ bool resolve_row(const RowMap& m, int r, int& b, int&
   return true;
 }
 
+// Row resolution split in two, for kernels whose first round trip should
+// carry everything: row_issue loads the row's length and position without
+// branches (an absent row_pos reads a valid dummy) and keeps them in vector
+// registers -- the empty asm hides their uniformity, so the compiler does
+// not move them to scalar registers, and wait for them, at once;
+// row_finish applies resolve_row's checks and returns the history length
+// L = p + 1, or 0 for a row that does not resolve.  Only a row_seq lookup
+// (chunked prefill rows) costs a round trip of its own.
+struct RowIssue {
+  int b, len_v, pos_v;
+  bool b_ok;
+};
+__device__ __forceinline__ RowIssue row_issue(const RowMap& m, int r) {
+  typedef __attribute__((address_space(1))) const int32_t gint;  // global, not flat
+  RowIssue q;
+  q.b = m.row_seq ? m.row_seq[r] : r;
+  q.b_ok = q.b >= 0 && q.b < m.num_seqs;
+  gint* len_at = (gint*)(m.seq_lens + (q.b_ok ? q.b : 0));
+  gint* pos_at = (gint*)(m.row_pos ? m.row_pos + r : m.seq_lens);
+  asm volatile("" : "+v"(len_at), "+v"(pos_at));
+  q.len_v = *len_at;
+  q.pos_v = *pos_at;
+  return q;
+}
+__device__ __forceinline__ int row_finish(const RowMap& m, const RowIssue& q) {
+  const int len = __builtin_amdgcn_readfirstlane(q.len_v);
+  const int p = m.row_pos ? __builtin_amdgcn_readfirstlane(q.pos_v) : len - 1;
+  if (!q.b_ok || p < 0 || p >= len || p >= m.max_blocks * kBlock) return 0;
+  return p + 1;
+}
+
 __device__ __forceinline__ void report(uint32_t* err, uint32_t bit) {
   if (err) atomicOr(err, bit);
 }

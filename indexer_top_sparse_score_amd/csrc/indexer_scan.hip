@@ -105,19 +105,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
   //    than after it; query and weights into LDS, heads past H_I as zero
   constexpr int kPages = kTile / kBlock;
   static_assert(kPages <= 64, "tile spans more pages than a wave has lanes");
-  const int b = a.rows.row_seq ? a.rows.row_seq[r] : r;
-  const bool b_ok = b >= 0 && b < a.rows.num_seqs;
   // Every load of this round trip is unconditional, from a clamped
-  // (always valid) address, and selected afterwards: a branch, or a value
-  // kept in a scalar register, would make the compiler wait for each load
-  // where it is taken.  The row's length and position stay in vector
-  // registers (the empty asm hides their uniformity) until they are checked.
-  typedef __attribute__((address_space(1))) const int32_t gint;  // global, not flat
-  gint* len_at = (gint*)(a.rows.seq_lens + (b_ok ? b : 0));
-  gint* pos_at = (gint*)(a.rows.row_pos ? a.rows.row_pos + r : a.rows.seq_lens);
-  asm volatile("" : "+v"(len_at), "+v"(pos_at));
-  const int len_v = *len_at;
-  const int pos_v = *pos_at;
+  // (always valid) address, and selected afterwards: a branch would make
+  // the compiler wait for each load where it merges.
+  const RowIssue ri = row_issue(a.rows, r);
+  const int b = ri.b;
+  const bool b_ok = ri.b_ok;
   const int32_t* bt = a.rows.block_table + (int64_t)(b_ok ? b : 0) * a.rows.max_blocks;
   // block id of the tile's page `lane` (lanes past the tile's pages, or past
   // the table's columns, read a valid entry that is never used)
@@ -140,15 +133,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     if (off1 < kQBytes) *reinterpret_cast<v4i*>(&q_lds[off1]) = q1;
     if (threadIdx.x < HT * 16) w_lds[threadIdx.x] = wv;
   }
-  const int len = __builtin_amdgcn_readfirstlane(len_v);
-  const int pos_given = __builtin_amdgcn_readfirstlane(pos_v);
-  // the same checks as resolve_row, on the values loaded above
-  const int p = a.rows.row_pos ? pos_given : len - 1;
-  if (!b_ok || p < 0 || p >= len || p >= a.rows.max_blocks * kBlock) {
+
+  const int L = row_finish(a.rows, ri);
+  if (L == 0) {
     if (blockIdx.x == 0 && threadIdx.x == 0) report(a.err, DSA_DEVERR_ROW);
     return;
   }
-  const int L = p + 1;
   if (tile0 >= L) return;
 
   // 2. keys: this wave owns the kSpan positions from w0; sub-tile j starts

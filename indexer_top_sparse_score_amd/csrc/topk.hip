@@ -547,24 +547,22 @@ __device__ __forceinline__ bool select_fast(const float* sc, int L, int K, bool 
   }
 }
 
-// This thread's share of a row's group maxima, 16t .. 16t+15 (the row's
-// slice is gstride long, whatever the row's length turns out to be).
+// This thread's share of a row's group maxima, 16t .. 16t+15, whatever the
+// row's length turns out to be.  The loads are unconditional 16-byte ones
+// (no branch, so nothing waits for them before they are used): the work
+// area is padded so that kMaxN entries from any row's start are readable;
+// entries past the row's groups hold other rows' or padding values and are
+// never used.
 __device__ __forceinline__ void load_gmax(const TopkLaunch& a, int r_local,
                                           uint32_t (&gm)[kPerThread]) {
-  const uint32_t* src = a.tw.gmax + (int64_t)r_local * a.tw.gstride;
-  const int g0 = kPerThread * (int)threadIdx.x;
-  if (g0 + kPerThread <= a.tw.gstride) {
+  const uint32_t* src = a.tw.gmax + (int64_t)r_local * a.tw.gstride + kPerThread * threadIdx.x;
 #pragma unroll
-    for (int j = 0; j < kPerThread; j += 4) {
-      const uint4 v = *reinterpret_cast<const uint4*>(src + g0 + j);
-      gm[j] = v.x;
-      gm[j + 1] = v.y;
-      gm[j + 2] = v.z;
-      gm[j + 3] = v.w;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) gm[j] = g0 + j < a.tw.gstride ? src[g0 + j] : 0u;
+  for (int j = 0; j < kPerThread; j += 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(src + j);
+    gm[j] = v.x;
+    gm[j + 1] = v.y;
+    gm[j + 2] = v.z;
+    gm[j + 3] = v.w;
   }
 }
 
@@ -622,17 +620,6 @@ __device__ __forceinline__ void row_single(const TopkLaunch& a, int r_local, int
   o.flush(K);
 }
 
-__global__ __launch_bounds__(kT) void topk_row_kernel(TopkLaunch a) {
-  __shared__ Smem s;
-  const int r_local = (int)blockIdx.x;
-  uint32_t gm[kPerThread];
-  load_gmax(a, r_local, gm);  // independent loads first
-  int b = 0, p;
-  const int L = resolve_row(a.rows, a.row_begin + r_local, b, p) ? p + 1 : 0;
-  Out o = make_out(a, r_local, b);
-  row_single(a, r_local, L, gm, o, s);
-}
-
 // ---------------------------------------------------------- split rows
 // A row whose group maxima are known is spread over up to kTopkSlices
 // workgroups, one per slice of kTopkSliceGroups groups:
@@ -675,11 +662,12 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
   const int slice = (int)blockIdx.x;
   const int r_local = (int)blockIdx.y;
   const int K = a.K;
+  // one round trip: the row's length, then its group maxima
+  const RowIssue ri = row_issue(a.rows, a.row_begin + r_local);
   uint32_t gm[kPerThread];
-  load_gmax(a, r_local, gm);  // independent loads first
-  int b = 0, p;
-  const int L = resolve_row(a.rows, a.row_begin + r_local, b, p) ? p + 1 : 0;
-  Out o = make_out(a, r_local, b);
+  load_gmax(a, r_local, gm);
+  const int L = row_finish(a.rows, ri);
+  Out o = make_out(a, r_local, ri.b_ok ? ri.b : 0);
   const int G = L > 0 ? topk_group(L, K) : 1;
   const int N = (L + G - 1) / G;
   if (!(L > K && G > 1 && K <= kBins && K <= kMaxCand - kT && N <= kMaxN)) {
@@ -875,9 +863,10 @@ int64_t cstride_of(int64_t max_len) { return (max_len + 63) & ~int64_t(63); }
 }  // namespace
 
 size_t topk_work_bytes(int rows, int64_t max_len) {
+  if (rows <= 0) return 0;
   const size_t words = (size_t)topk_gstride(max_len) + 2 * (size_t)cstride_of(max_len) +
                        kTopkSlices + 1;
-  return (size_t)rows * words * sizeof(uint32_t);
+  return ((size_t)rows * words + kMaxN) * sizeof(uint32_t);  // + load_gmax's padding
 }
 
 TopkWork topk_work_carve(void* base, int rows, int64_t max_len) {
@@ -886,7 +875,7 @@ TopkWork topk_work_carve(void* base, int rows, int64_t max_len) {
   w.gstride = topk_gstride(max_len);
   w.cstride = cstride_of(max_len);
   w.gmax = p;
-  p += (size_t)rows * w.gstride;
+  p += (size_t)rows * w.gstride + kMaxN;  // load_gmax reads up to kMaxN past a row's start
   w.ckey = p;
   p += (size_t)rows * w.cstride;
   w.cpos = reinterpret_cast<int32_t*>(p);
@@ -905,11 +894,7 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (a.tw.arrive) {
-    topk_split_kernel<<<dim3(kTopkSlices, a.num_rows), kT, 0, s>>>(a);
-  } else {
-    topk_row_kernel<<<a.num_rows, kT, 0, s>>>(a);
-  }
+  topk_split_kernel<<<dim3(kTopkSlices, a.num_rows), kT, 0, s>>>(a);
   return hipGetLastError();
 }
 
