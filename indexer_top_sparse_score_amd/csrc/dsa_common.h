@@ -85,6 +85,44 @@ __device__ __forceinline__ uint32_t score_key(float x) {
   return mag > 0x7F800000u ? 0u : k;
 }
 
+// ----------------------------------------------------- cross-lane, registers
+// Reductions over lanes without an LDS round trip.  v_permlane16_swap
+// exchanges 16-lane rows 0<->1 and 2<->3, v_permlane32_swap the two wave
+// halves: with both operands the same value the returned pair holds this
+// lane's value and its partner's, so op(pair) is the same in both lanes.
+// Within a row, DPP quad permutes and the half-row and row mirrors pair
+// lanes 1, 2, 4 and 8 apart (each step combines two disjoint groups).
+struct FMax { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct FAdd { __device__ float operator()(float a, float b) const { return a + b; } };
+template <class Op>
+__device__ __forceinline__ float xor16(float x, Op op) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+template <class Op>
+__device__ __forceinline__ float xor32(float x, Op op) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+// op over the four 16-lane rows (lanes l, l^16, l^32, l^48), in every lane
+template <class Op>
+__device__ __forceinline__ float across_rows(float x, Op op) {
+  return xor32(xor16(x, op), op);
+}
+// op over all 64 lanes, in every lane
+template <class Op>
+__device__ __forceinline__ float across_wave(float x, Op op) {
+  x = op(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = op(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = op(x, dpp_f<0x141>(x));  // row_half_mirror
+  x = op(x, dpp_f<0x140>(x));  // row_mirror
+  return across_rows(x, op);
+}
+
 // Number of set bits of `mask` below this lane (wave64).
 __device__ __forceinline__ int lane_prefix(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),

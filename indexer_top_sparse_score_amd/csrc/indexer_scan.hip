@@ -57,17 +57,6 @@ __device__ __forceinline__ v8i load_slice(const uint8_t* sub, uint32_t lane_off)
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Sum over the four 16-lane rows of a wave, every lane getting the total.
-// v_permlane16_swap exchanges rows 0<->1 and 2<->3 and v_permlane32_swap the
-// two halves, both in registers; with both operands the same value, the
-// returned pair holds this lane's value and its partner's.
-__device__ __forceinline__ float sum_rows(float x) {
-  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
-}
-
 // Maximum over aligned groups of G lanes (G = 1, 2, 4 or 8, wave-uniform)
 // with DPP moves: swap neighbours, swap pairs, mirror each half-row.
 __device__ __forceinline__ uint32_t max_lanes(uint32_t k, int G) {
@@ -195,7 +184,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
 #pragma unroll
       for (int v = 0; v < 4; ++v) part += wr[v] * fmaxf(acc[v], 0.0f);
     }
-    part = sum_rows(part);
+    part = across_rows(part, FAdd());
     // canonical +0 for a zero score; an absent page scores -inf
     const float v = page_ok[j] ? part + 0.0f : -__builtin_inff();
     if (g == 0) my_sc[j * kSub + col] = v;

@@ -407,8 +407,7 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
         s[kt][v] = x;
         mx = fmaxf(mx, x);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = across_rows(mx, FMax());
     // Lazy rescaling: the reference max m2 only moves when some head's max
     // exceeds it by more than 8 (log2 units), so the exponentials below stay
     // <= 2^8 and the accumulators are rescaled rarely.  Any reference gives
@@ -450,8 +449,7 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
     }
   }
 
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = across_rows(lsum, FAdd());
   if (!head_ok) return;
 
   write_result<C::MT>(a, r, row_local, chunk, head, grp, o, m2, lsum);
@@ -733,8 +731,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[kt][v] * c2);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        m2 = fmaxf(mx, __shfl_xor(mx, 32));  // -inf only without a valid key
+        m2 = across_rows(mx, FMax());  // -inf only without a valid key
       }
       float pv[8];
       float psum = 0.0f;
@@ -792,12 +789,10 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
     // the last iteration waited for every DMA; the barrier also makes the
     // buffers free for a second pass
     if (!__syncthreads_or(over)) break;
-    m_lane = fmaxf(m_lane, __shfl_xor(m_lane, 16));
-    m_fix = fmaxf(m_lane, __shfl_xor(m_lane, 32));
+    m_fix = across_rows(m_lane, FMax());
   }
 
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = across_rows(lsum, FAdd());
   // every wave is past the last barrier and every DMA has landed: the tile
   // buffers are free for staging (16.25 KB per wave)
   const int head0 = hg * (kHPW * kNW) + wave * kHPW;
@@ -836,33 +831,34 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   const int lane = threadIdx.x & 63;
   if (head >= a.H_q) return;
   const int n = a.n_chunks;  // <= 64
-  const float2 st = lane < n ? part_stats(a, row_local, lane)[head] : float2{-__builtin_inff(), 0.0f};
   const uint16_t* o0 = part_out(a, row_local, 0, DV) + (int64_t)head * DV + lane * PER;
   const int64_t cstride = (int64_t)a.H_q * DV;
-  float M = st.x;
+  // kBatch chunks per round trip; the first batch goes out before the
+  // statistics, so one round trip brings both (chunks past n reload the
+  // last one and get weight 0)
+  constexpr int kBatch = 16;
+  float x[kBatch][PER];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  for (int u = 0; u < kBatch; ++u) load_bf16<PER>(o0 + min(u, n - 1) * cstride, x[u]);
+  const float2 st = lane < n ? part_stats(a, row_local, lane)[head] : float2{-__builtin_inff(), 0.0f};
+  const float M = across_wave(st.x, FMax());
+  // no branch on M: with every chunk empty all weights are 0
+  const float f = st.x == -__builtin_inff() ? 0.0f : exp2f(st.x - M);
+  const float Ls = across_wave(f * st.y, FAdd());
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.0f;
-  // no branch on M: with every chunk empty all weights are 0, and the
-  // output loads below need not wait for the statistics
-  const float f = st.x == -__builtin_inff() ? 0.0f : exp2f(st.x - M);
-  float Ls = f * st.y;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) Ls += __shfl_xor(Ls, o);
-  // kBatch chunks per round trip: every load of a batch is issued before
-  // any is used (chunks past n reload the last one with weight 0)
-  constexpr int kBatch = 16;
   for (int c0 = 0; c0 < n; c0 += kBatch) {
-    float x[kBatch][PER];
+    if (c0 > 0) {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) load_bf16<PER>(o0 + min(c0 + u, n - 1) * cstride, x[u]);
+      for (int u = 0; u < kBatch; ++u) load_bf16<PER>(o0 + min(c0 + u, n - 1) * cstride, x[u]);
+    }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const float fu = c0 + u < n ? __shfl(f, c0 + u) : 0.0f;
+      const float fu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), min(c0 + u, 63)));
+      const float wu = c0 + u < n ? fu : 0.0f;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] += x[u][i] * fu;
+      for (int i = 0; i < PER; ++i) acc[i] += x[u][i] * wu;
     }
   }
   const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
