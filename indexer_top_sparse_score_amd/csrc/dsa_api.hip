@@ -210,6 +210,7 @@ int dsa_topk(const dsa_problem* p, const float* scores, int64_t ld_scores, int32
   a.vec = aligned(scores, 16) && ld_scores % 4 == 0;
   a.rowoff = nullptr;
   a.kv = dsa_paged{};
+  a.kv_row_bytes = 0;
   return status_of(launch_topk(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -333,6 +334,7 @@ int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa
     ta.vec = true;  // 256-byte aligned slab, ld a multiple of 64
     ta.rowoff = use_rowoff ? roff : nullptr;
     ta.kv = k;
+    ta.kv_row_bytes = use_rowoff ? p->D_qk * 2 : 0;
     if ((st = status_of(launch_topk(ta, s))) != DSA_OK) return st;
 
     AttnLaunch aa = attn_launch(p, q, k, v, out, lse, err);

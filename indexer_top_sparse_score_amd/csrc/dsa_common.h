@@ -211,6 +211,10 @@ struct TopkLaunch {
   // positions whose block id is out of range, to rowoff[num_rows][K].
   int64_t* rowoff;
   dsa_paged kv;
+  // With rowoff: bytes of a KV row the attention that follows reads (0: none).
+  // The Top-K then touches every candidate's row once it has handed its
+  // slice over, so that the attention's gather finds them in the caches.
+  int32_t kv_row_bytes;
 };
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
 

@@ -633,6 +633,32 @@ __device__ __forceinline__ void row_single(const TopkLaunch& a, int r_local, int
 // Nothing waits on another workgroup.  Rows that do not take this path run
 // row_single in slice 0's workgroup.
 
+// Loads one dword of every 128-byte line of the KV rows at the positions
+// cp[0..n), through the row's block table in LDS, and waits for them: only
+// their arrival in the caches matters.  At most kPrefetchPer lines per
+// thread (longer lists are cut), all in flight at once.
+constexpr int kPrefetchPer = 8;
+__device__ __forceinline__ void prefetch_rows(const TopkLaunch& a, uint32_t n, const int32_t* cp,
+                                              const int32_t* bt_lds) {
+  const int lines = (a.kv_row_bytes + 127) / 128;
+  const uint32_t total = min(n * (uint32_t)lines, (uint32_t)(kPrefetchPer * kT));
+  const uint8_t* base = static_cast<const uint8_t*>(a.kv.base);
+  uint32_t acc = 0;
+#pragma unroll
+  for (int i = 0; i < kPrefetchPer; ++i) {
+    const uint32_t idx = threadIdx.x + (uint32_t)(i * kT);
+    if (idx < total) {
+      const int c = (int)(idx / (uint32_t)lines), l = (int)(idx % (uint32_t)lines);
+      const int p = cp[c];
+      const int phys = bt_lds[p >> 6];
+      if (phys >= 0 && (int64_t)phys < a.kv.num_blocks)
+        acc ^= *reinterpret_cast<const uint32_t*>(base + (int64_t)phys * a.kv.block_stride +
+                                                  (int64_t)(p & 63) * a.kv.row_stride + 128 * l);
+    }
+  }
+  asm volatile("" : : "v"(acc));  // keeps the loads, waits for them once
+}
+
 // The G scores of group g as raw bits (positions past L as 0); converted to
 // keys only once they are needed, so nothing waits for them earlier.
 template <int G>
@@ -749,9 +775,14 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
       if (j < G && k[j] >= t) {
         a.tw.ckey[seg + at] = k[j];
         a.tw.cpos[seg + at] = g * G + j;
+        if (at < (uint32_t)kMaxKeys) s.cp[at] = g * G + j;  // for the KV prefetch
         ++at;
       }
     if (tid == 0) a.tw.ccount[r_local * kTopkSlices + slice] = n_slice;
+    if (bt_cached) {  // every workgroup: the prefetch below reads it too
+#pragma unroll
+      for (int j = 0; j < kBtPer; ++j) s.bt[tid + j * kT] = btv[j];
+    }
   }
 
   // c. the last slice to finish completes the row.  The barrier orders the
@@ -767,12 +798,15 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
     s.res[3] = done == (uint32_t)(S - 1) ? 1u : 0u;
   }
   __syncthreads();
-  if (s.res[3] == 0) return;
-  if (bt_cached) {
-#pragma unroll
-    for (int j = 0; j < kBtPer; ++j) s.bt[tid + j * kT] = btv[j];
-    o.bt_lds = s.bt;  // read after the barriers of the selection below
+  if (s.res[3] == 0) {
+    // Handed over: touch the KV rows of this slice's candidates (a superset
+    // of what the row keeps), one 4-byte load per 128-byte line, so that
+    // the attention's gather finds them in the caches rather than in HBM.
+    if (a.kv_row_bytes > 0 && bt_cached)
+      prefetch_rows(a, min(n_slice, (uint32_t)kMaxKeys), s.cp, s.bt);
+    return;
   }
+  if (bt_cached) o.bt_lds = s.bt;  // staged by every workgroup above
   // Thread t reads entries 8 (t mod 64) .. +7 of slice t / 64 together with
   // the counts (no round trip between them); in thread order that is
   // position order.  A slice with more than 512 candidates sends the row
