@@ -219,14 +219,20 @@ __device__ __forceinline__ void histogram_bin(Visit&& visit, uint32_t lo, uint32
 // in [lo, hi] that visit(f) hands to f in the threads of the block; there
 // must be at least `need` of them.  On return `need` holds how many keys
 // equal to the result belong to the need largest (the others are larger).
-// Every thread calls it with the same lo, hi and need.
-template <class Visit>
+// Every thread calls it with the same lo, hi and need.  With kZeroed the
+// caller has cleared the histogram (and a barrier has passed since).
+template <bool kZeroed = false, class Visit>
 __device__ __forceinline__ uint32_t select_kth(Visit&& visit, uint32_t lo, uint32_t hi,
                                                uint32_t& need, Smem& s) {
   const int tid = threadIdx.x;
+  bool zeroed = kZeroed;
   while (lo < hi) {
     const int shift = range_shift(lo, hi);
-    histogram_bin(visit, lo, hi, shift, need, s);
+    if (zeroed)
+      histogram_bin<true>(visit, lo, hi, shift, need, s);
+    else
+      histogram_bin<false>(visit, lo, hi, shift, need, s);
+    zeroed = false;
     const uint32_t b = s.res[0];
     need -= s.res[1];
     const uint32_t cnt = s.hist[b];
@@ -356,12 +362,15 @@ __device__ __forceinline__ void emit_runs(const uint32_t (&k)[N], int n, Pos&& p
     gt += (j < n && k[j] > T) ? 1u : 0u;
     eq += (j < n && k[j] == T) ? 1u : 0u;
   }
+  // one scan for both counts (a run holds at most 16384 entries, so each
+  // half of the packed word stays below 2^16)
   uint32_t tot;
-  const uint32_t eqx = eq_before + block_scan(eq, s.wsum, tot);
-  eq_before += tot;
-  const uint32_t take_eq = eqx >= need_eq ? 0u : min(eq, need_eq - eqx);
-  const uint32_t slot0 = out_before + block_scan(gt + take_eq, s.wsum, tot);
-  out_before += tot;
+  const uint32_t ex = block_scan((eq << 16) | gt, s.wsum, tot);
+  const uint32_t eqx = eq_before + (ex >> 16);  // equal keys before this thread
+  // kept so far: every larger key, and equal keys up to the budget
+  const uint32_t slot0 = out_before + (ex & 0xFFFFu) + min(eqx, need_eq) - min(eq_before, need_eq);
+  out_before += (tot & 0xFFFFu) + min(eq_before + (tot >> 16), need_eq) - min(eq_before, need_eq);
+  eq_before += tot >> 16;
   uint32_t slot = slot0, e = eqx;
 #pragma unroll
   for (int j = 0; j < N; ++j) {
@@ -807,6 +816,7 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
     return;
   }
   if (bt_cached) o.bt_lds = s.bt;  // staged by every workgroup above
+  for (int i = tid; i < kBins; i += kT) s.hist[i] = 0;  // for the selection, while loading
   // Thread t reads entries 8 (t mod 64) .. +7 of slice t / 64 together with
   // the counts (no round trip between them); in thread order that is
   // position order.  A slice with more than 512 candidates sends the row
@@ -860,7 +870,8 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
         if (j < n) f(kk[j]);
     };
     uint32_t need = (uint32_t)K;
-    const uint32_t T = select_kth(visit, t, kmax, need, s);
+    __syncthreads();  // the cleared histogram
+    const uint32_t T = select_kth<true>(visit, t, kmax, need, s);
     uint32_t eq_before = 0, out_before = 0;
     emit_runs<kKeysPer, true>(kk, n, [&](int j) { return pp[j]; }, T, need, eq_before,
                               out_before, o, s);
