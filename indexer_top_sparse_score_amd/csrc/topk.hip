@@ -668,6 +668,13 @@ __device__ __forceinline__ void prefetch_rows(const TopkLaunch& a, uint32_t n, c
   asm volatile("" : : "v"(acc));  // keeps the loads, waits for them once
 }
 
+// Device-coherent store for the hand-over between a row's workgroups: an
+// agent-scope atomic store, which the hardware writes through the XCD's L2
+// (nothing dirty is left to write back).
+__device__ __forceinline__ void store_shared(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // The G scores of group g as raw bits (positions past L as 0); converted to
 // keys only once they are needed, so nothing waits for them earlier.
 template <int G>
@@ -782,29 +789,36 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
 #pragma unroll
     for (int j = 0; j < kMaxGroup; ++j)
       if (j < G && k[j] >= t) {
-        a.tw.ckey[seg + at] = k[j];
-        a.tw.cpos[seg + at] = g * G + j;
+        store_shared(a.tw.ckey + seg + at, k[j]);
+        store_shared(reinterpret_cast<uint32_t*>(a.tw.cpos) + seg + at, (uint32_t)(g * G + j));
         if (at < (uint32_t)kMaxKeys) s.cp[at] = g * G + j;  // for the KV prefetch
         ++at;
       }
-    if (tid == 0) a.tw.ccount[r_local * kTopkSlices + slice] = n_slice;
+    if (tid == 0) store_shared(a.tw.ccount + r_local * kTopkSlices + slice, n_slice);
     if (bt_cached) {  // every workgroup: the prefetch below reads it too
 #pragma unroll
       for (int j = 0; j < kBtPer; ++j) s.bt[tid + j * kT] = btv[j];
     }
   }
 
-  // c. the last slice to finish completes the row.  The barrier orders the
-  //    workgroup's stores before thread 0's device-scope release (a
-  //    cumulative fence: one per workgroup, since each writes back the L2)
-  //    and counter update; the last workgroup's thread 0 acquires before
-  //    the barrier that releases its other threads to read.
+  // c. the last slice to finish completes the row.  The segments and counts
+  //    went out as device-coherent stores (written through, nothing dirty
+  //    left in the L2): each wave waits until its own have completed, the
+  //    barrier gathers the waves, and only then does thread 0 count the
+  //    slice in (a device-scope atomic).  So no release fence, whose L2
+  //    write-back cost about a microsecond per workgroup.  The workgroup
+  //    that sees the count reach S invalidates its caches (an acquire fence
+  //    by thread 0, before the barrier that releases the others) and reads
+  //    everything back with ordinary vector loads.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);  // no compiler motion across the wait
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    __threadfence();
-    const uint32_t done = atomicAdd(&a.tw.arrive[r_local], 1u);
-    if (done == (uint32_t)(S - 1)) __threadfence();
-    s.res[3] = done == (uint32_t)(S - 1) ? 1u : 0u;
+    const uint32_t done = __hip_atomic_fetch_add(a.tw.arrive + r_local, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = done == (uint32_t)(S - 1);
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s.res[3] = last ? 1u : 0u;
   }
   __syncthreads();
   if (s.res[3] == 0) {
@@ -824,12 +838,12 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
   const int my_slice = tid / kSegRead;
   const int e0 = kKeysPer * (tid % kSegRead);
   const int64_t seg = (int64_t)r_local * a.tw.cstride + (int64_t)my_slice * kTopkSliceGroups * G;
-  // A slice's candidates end at or before the row's end of the area, so
-  // entries past it are never wanted (and not read).  Segments start on
-  // 16-byte boundaries: two 16-byte loads each for keys and positions.
   const int64_t row_end = (int64_t)(r_local + 1) * a.tw.cstride;
   uint32_t kk[kKeysPer];
   int32_t pp[kKeysPer];
+  // A slice's candidates end at or before the row's end of the area, so
+  // entries past it are never wanted (and not read).  Segments start on
+  // 16-byte boundaries: two 16-byte loads each for keys and positions.
   if (my_slice < S && seg + e0 + kKeysPer <= row_end) {
 #pragma unroll
     for (int j = 0; j < kKeysPer; j += 4) {
