@@ -42,7 +42,7 @@
 #define DSA_ATTN_KDEPTH 8  // K fragment reads in flight ahead of their MFMAs
 #endif
 #ifndef DSA_ATTN_NBUF
-#define DSA_ATTN_NBUF 4
+#define DSA_ATTN_NBUF 3
 #endif
 #ifndef DSA_ATTN_TARGET_WGS
 #define DSA_ATTN_TARGET_WGS 256
