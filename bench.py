@@ -15,6 +15,9 @@ roofline   the dominant kernel (the indexer scan): algorithmic bytes per
            the counter-measured HBM bytes per launch from profiles/ (null
            when the kernel source changed since they were taken)
 cpu_baseline  the oracle timed on the host on a bounded sample of rows
+mxfp8_indexer  the same workload with MXFP8 indexer operands (one E8M0 scale
+           per 32 dims): the fused step and the indexer scan alone, timed the
+           same way over their own rotating input sets (--no-mxfp8 skips it)
 """
 
 import argparse
@@ -41,6 +44,8 @@ def parse():
     ap.add_argument("--graph", type=int, default=1, help="replay captured HIP graphs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mxfp8", action="store_true",
+                    help="skip the MXFP8-indexer leg (same workload, group-32 scales)")
     ap.add_argument("--table", default=None)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain elementwise copy of MIB MiB (float32 in, float32 out) "
@@ -61,10 +66,12 @@ def step_bytes(wl, lengths):
     return total
 
 
-def indexer_bytes(wl, lengths):
+def indexer_bytes(wl, lengths, mx=False):
     """Algorithmic bytes of one indexer-scan launch: index keys, queries,
-    weights, block-table entries, and the float32 scores it writes."""
-    return sum(wl.D_I * L + wl.H_I * wl.D_I + 4 * wl.H_I + 4 * ((L + 63) // 64) + 4 * L
+    weights, block-table entries, and the float32 scores it writes; with
+    MXFP8 operands also one scale byte per 32 dims of every key and query."""
+    per = wl.D_I + (wl.D_I // 32 if mx else 0)
+    return sum(per * L + wl.H_I * per + 4 * wl.H_I + 4 * ((L + 63) // 64) + 4 * L
                for L in lengths)
 
 
@@ -229,6 +236,9 @@ def main():
         "wall_s": round(wall, 4),
     }
 
+    if not args.no_mxfp8:
+        result["mxfp8_indexer"] = mxfp8_leg(args, wl, lengths, stream, rotate_bytes=ib)
+
     if args.copy_calibration:
         n = (args.copy_calibration << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -243,6 +253,62 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(first, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def mxfp8_leg(args, wl, lengths, stream, rotate_bytes):
+    """The same workload with MXFP8 indexer operands (one E8M0 scale per 32
+    dims): the indexer scan timed alone, and the fused step, both with HIP
+    events on the launch stream over input sets that rotate past the
+    Infinity Cache."""
+    import torch
+    from indexer_top_sparse_score_amd import binding as B
+    from workloads import make_batch
+    mwl = wl.with_(indexer_fmt="mxfp8")
+    dev = torch.device("cuda:0")
+    nset = max(1, min(8, -(-4 * MALL_BYTES // rotate_bytes)))
+    sets = [make_batch(mwl, device=dev, seed=mwl.seed + 7000 + 1000 * i, mode=args.mode,
+                       table=args.table) for i in range(nset)]
+    probs = [B.problem_for_batch(s) for s in sets]
+    rows = sets[0].rows
+    ld = 64 * sets[0].max_blocks
+    scores = torch.empty((rows, ld), dtype=torch.float32, device=dev)
+    ws_i = B.workspace(probs[0], B.DSA_OP_INDEXER_SCORES, device=dev)
+    ws = B.workspace(probs[0], B.DSA_OP_DECODE_STEP, device=dev)
+    out = torch.empty((rows, mwl.H_q, mwl.D_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((rows, mwl.H_q), dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        with torch.cuda.stream(stream):
+            for i in range(args.warmup):
+                fn(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(args.steps):
+                fn(i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / args.steps  # us
+
+    def scan(i):
+        s = sets[i % nset]
+        B.dsa_indexer_scores(probs[i % nset], s.qI, s.w, s.kI, scores, ws_i, stream=stream)
+
+    def step(i):
+        s = sets[i % nset]
+        v = s.v if s.v is not None else s.kv
+        B.dsa_decode_step(probs[i % nset], s.qI, s.w, s.kI, s.q, s.kv, v, out, ws, lse=lse,
+                          stream=stream)
+
+    idx_us = timed(scan)
+    step_us = timed(step)
+    assert B.device_errors(ws) == 0 and B.device_errors(ws_i) == 0
+    ib = indexer_bytes(mwl, lengths, mx=True)
+    achieved = ib / (idx_us * 1e-6) / 1e9
+    return {"indexer": f"{mwl.H_I}x{mwl.D_I} e4m3 + e8m0/32", "rotation_sets": nset,
+            "launch": "stream (eager)", "step_us": round(step_us, 3),
+            "tokens_per_s": round(rows / (step_us * 1e-6), 1),
+            "indexer_avg_launch_us": round(idx_us, 3), "indexer_bytes_per_launch": ib,
+            "indexer_achieved": round(achieved, 1), "indexer_frac": round(achieved / HBM_PEAK_GBS, 4)}
 
 
 def cpu_baseline(batch, budget_s):

@@ -62,7 +62,7 @@ extern "C" {
 #define DSA_API
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 #define DSA_BLOCK_SIZE 64
 
 typedef enum {
@@ -104,7 +104,17 @@ typedef struct {
   int32_t D_v;                /* attention v / output dim: 64 (with D_qk 64) or 512     */
   int32_t K;                  /* positions kept per row, >= 1                           */
   float scale;                /* attention logit scale, finite (e.g. 1/sqrt(D_qk))      */
+  int32_t indexer_format;     /* DSA_INDEXER_E4M3 or DSA_INDEXER_MXFP8                  */
+  const uint8_t* qI_scale;    /* MXFP8: [num_rows][H_I][D_I / 32] E8M0 scales of qI;
+                                 NULL for E4M3                                          */
 } dsa_problem;
+
+/* indexer operand formats (dsa_problem.indexer_format) */
+enum {
+  DSA_INDEXER_E4M3 = 0,  /* unscaled E4M3 codes                                         */
+  DSA_INDEXER_MXFP8 = 1  /* E4M3 codes with one E8M0 scale per group of 32 dims (Day0,
+                            section 5.1); see dsa_indexer_scores                        */
+};
 
 /* which call dsa_workspace_size() sizes */
 enum {
@@ -130,6 +140,17 @@ DSA_API size_t dsa_workspace_size(const dsa_problem* p, int op);
  *           Entries s > p_r are neither read nor written.
  * FP8 products are exact and accumulate in float32, so integer-valued inputs
  * whose partial sums stay below 2**24 give exact scores in any order.
+ *
+ * With indexer_format = DSA_INDEXER_MXFP8 (Day0 article, section 5.1: one
+ * shared scale per group of 32 dims of Q and of K), the dims are cut into
+ * groups g of 32 and each group of a query head and of a key row carries an
+ * E8M0 scale byte e (the value 2**(e - 127); e = 255 is not allowed):
+ *   sum_d qI[r, h, d] * kI[s, d]  becomes
+ *   sum_g 2**(eq[r, h, g] + ek[s, g] - 254) * sum_{d in g} qI[r, h, d] * kI[s, d]
+ *   eq      p->qI_scale, [num_rows][H_I][D_I / 32]
+ *   ek      bytes D_I .. D_I + D_I/32 - 1 of each kI row (so the row stride
+ *           must be at least D_I + D_I / 32)
+ * Power-of-two scales keep every product exact.
  */
 DSA_API int dsa_indexer_scores(const dsa_problem* p, const uint8_t* qI, const float* w, dsa_paged kI,
                        float* scores, int64_t ld_scores, void* ws, size_t ws_bytes,

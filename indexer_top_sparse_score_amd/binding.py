@@ -27,7 +27,9 @@ DSA_OP_TOPK = 1
 DSA_OP_SPARSE_ATTN = 2
 DSA_OP_DECODE_STEP = 3
 
-ABI_VERSION = 1
+ABI_VERSION = 2
+DSA_INDEXER_E4M3 = 0
+DSA_INDEXER_MXFP8 = 1
 BLOCK = 64
 
 #: every symbol include/dsa.h declares
@@ -47,7 +49,8 @@ class DsaProblem(ctypes.Structure):
                 ("row_seq", ctypes.c_void_p), ("row_pos", ctypes.c_void_p),
                 ("H_I", ctypes.c_int32), ("D_I", ctypes.c_int32), ("H_q", ctypes.c_int32),
                 ("D_qk", ctypes.c_int32), ("D_v", ctypes.c_int32), ("K", ctypes.c_int32),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("indexer_format", ctypes.c_int32),
+                ("qI_scale", ctypes.c_void_p)]
 
 
 class DsaError(RuntimeError):
@@ -112,8 +115,11 @@ def paged(cache: torch.Tensor) -> DsaPaged:
 
 
 def problem(*, seq_lens, block_table, num_rows=None, row_seq=None, row_pos=None, H_I=64,
-            D_I=128, H_q=128, D_qk=576, D_v=512, K=2048, scale=576 ** -0.5) -> DsaProblem:
-    """Problem descriptor; device tensors are referenced, not copied."""
+            D_I=128, H_q=128, D_qk=576, D_v=512, K=2048, scale=576 ** -0.5,
+            qI_scale=None) -> DsaProblem:
+    """Problem descriptor; device tensors are referenced, not copied.  With
+    ``qI_scale`` (uint8 E8M0 [rows, H_I, D_I/32]) the indexer runs in MXFP8
+    format and the index-key rows carry their scales after the codes."""
     num_seqs = int(seq_lens.shape[0])
     if num_rows is None:
         num_rows = int(row_seq.shape[0]) if row_seq is not None else num_seqs
@@ -121,8 +127,10 @@ def problem(*, seq_lens, block_table, num_rows=None, row_seq=None, row_pos=None,
                    int(block_table.shape[1]), BLOCK,
                    None if row_seq is None else row_seq.data_ptr(),
                    None if row_pos is None else row_pos.data_ptr(),
-                   H_I, D_I, H_q, D_qk, D_v, K, scale)
-    p._keep = (seq_lens, block_table, row_seq, row_pos)  # keep the tensors alive
+                   H_I, D_I, H_q, D_qk, D_v, K, scale,
+                   DSA_INDEXER_E4M3 if qI_scale is None else DSA_INDEXER_MXFP8,
+                   None if qI_scale is None else qI_scale.data_ptr())
+    p._keep = (seq_lens, block_table, row_seq, row_pos, qI_scale)  # keep the tensors alive
     return p
 
 
@@ -133,7 +141,8 @@ def problem_for_batch(batch) -> DsaProblem:
     return problem(seq_lens=batch.seq_lens, block_table=batch.block_table,
                    num_rows=int(batch.qI.shape[0]), row_seq=batch.row_seq,
                    row_pos=batch.row_pos, H_I=wl.H_I, D_I=wl.D_I, H_q=wl.H_q, D_qk=wl.D_qk,
-                   D_v=wl.D_v, K=wl.K, scale=wl.scale)
+                   D_v=wl.D_v, K=wl.K, scale=wl.scale,
+                   qI_scale=getattr(batch, "qI_scale", None))
 
 
 def dsa_workspace_size(prob: DsaProblem, op: int) -> int:

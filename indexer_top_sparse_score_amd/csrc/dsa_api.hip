@@ -33,7 +33,20 @@ int check_indexer_shape(const dsa_problem* p) {
   if (p->H_I < 1 || p->D_I < 1) return DSA_ERR_INVALID;
   if (p->H_I > 64) return DSA_ERR_UNSUPPORTED;
   if (p->D_I != 64 && p->D_I != 128) return DSA_ERR_UNSUPPORTED;
+  if (p->indexer_format == DSA_INDEXER_E4M3) {
+    if (p->qI_scale) return DSA_ERR_INVALID;
+  } else if (p->indexer_format == DSA_INDEXER_MXFP8) {
+    if (!p->qI_scale) return DSA_ERR_INVALID;
+  } else {
+    return DSA_ERR_INVALID;
+  }
   return DSA_OK;
+}
+
+// bytes of an index-key row the indexer reads: the codes, then (MXFP8) one
+// scale byte per 32 dims
+int64_t kI_row_bytes(const dsa_problem* p) {
+  return p->D_I + (p->indexer_format == DSA_INDEXER_MXFP8 ? p->D_I / 32 : 0);
 }
 
 int check_attn_shape(const dsa_problem* p) {
@@ -161,7 +174,7 @@ int dsa_indexer_scores(const dsa_problem* p, const uint8_t* qI, const float* w, 
   if ((st = check_indexer_shape(p)) != DSA_OK) return st;
   if (!qI || !w || !scores) return DSA_ERR_INVALID;
   if (!aligned(qI, 16) || !aligned(w, 4) || !aligned(scores, 4)) return DSA_ERR_INVALID;
-  if ((st = check_paged(kI, p->D_I)) != DSA_OK) return st;
+  if ((st = check_paged(kI, kI_row_bytes(p))) != DSA_OK) return st;
   if (ld_scores < max_len(p)) return DSA_ERR_INVALID;
   if ((st = check_ws(ws, ws_bytes, kHeader)) != DSA_OK) return st;
   if (p->num_rows == 0) return DSA_OK;
@@ -175,6 +188,7 @@ int dsa_indexer_scores(const dsa_problem* p, const uint8_t* qI, const float* w, 
   a.err = static_cast<uint32_t*>(ws);
   a.H_I = p->H_I;
   a.D_I = p->D_I;
+  a.qI_scale = p->qI_scale;
   a.row_begin = 0;
   a.num_rows = p->num_rows;
   a.max_len = (int32_t)max_len(p);
@@ -279,7 +293,7 @@ int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa
   if ((st = check_indexer_shape(p)) != DSA_OK) return st;
   if ((st = check_attn_args(p, q, k, v, out, lse)) != DSA_OK) return st;
   if (!qI || !w || !aligned(qI, 16) || !aligned(w, 4)) return DSA_ERR_INVALID;
-  if ((st = check_paged(kI, p->D_I)) != DSA_OK) return st;
+  if ((st = check_paged(kI, kI_row_bytes(p))) != DSA_OK) return st;
   if ((indices_out && !aligned(indices_out, 4)) || (counts_out && !aligned(counts_out, 4)))
     return DSA_ERR_INVALID;
   if ((st = check_ws(ws, ws_bytes, dsa_workspace_size(p, DSA_OP_DECODE_STEP))) != DSA_OK)
@@ -311,6 +325,7 @@ int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa
     ia.err = err;
     ia.H_I = p->H_I;
     ia.D_I = p->D_I;
+    ia.qI_scale = p->qI_scale;
     ia.row_begin = row0;
     ia.num_rows = nr;
     ia.max_len = (int32_t)ld;

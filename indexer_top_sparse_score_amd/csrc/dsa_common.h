@@ -180,6 +180,7 @@ TopkWork topk_work_carve(void* base, int rows, int64_t max_len);
 struct IndexerLaunch {
   RowMap rows;
   const uint8_t* qI;
+  const uint8_t* qI_scale;  // MXFP8: [rows][H_I][D_I/32] E8M0; NULL: unscaled E4M3
   const float* w;
   dsa_paged kI;
   float* scores;

@@ -57,6 +57,14 @@ __device__ __forceinline__ v8i load_slice(const uint8_t* sub, uint32_t lane_off)
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// 16 heads x 16 positions x 128 dims of E4M3, A scaled by byte kSelA of
+// scale_a and B by byte 0 of scale_b (E8M0; 127 = x1), from zero.
+template <int kSelA>
+__device__ __forceinline__ v4f mfma_scaled(v8i a, v8i b, int scale_a, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0,
+                                                          kSelA, scale_a, 0, scale_b);
+}
+
 // Maximum over aligned groups of G lanes (G = 1, 2, 4 or 8, wave-uniform)
 // with DPP moves: swap neighbours, swap pairs, mirror each half-row.
 __device__ __forceinline__ uint32_t max_lanes(uint32_t k, int G) {
@@ -66,8 +74,18 @@ __device__ __forceinline__ uint32_t max_lanes(uint32_t k, int G) {
   return k;
 }
 
-// NKP = D_I / 64 pieces per lane; HT = 16-head tiles (ceil(H_I / 16)).
-template <int NKP, int HT>
+// NKP = D_I / 64 pieces per lane; HT = 16-head tiles (ceil(H_I / 16)); MX:
+// MXFP8 operands (one E8M0 scale per 32 dims of every query head and key
+// row, Day0 section 5.1), else unscaled E4M3.
+//
+// Scales.  The block-scaled MFMA takes one scale byte per lane for each
+// operand: lane l scales row (A) or column (B) l % 16 over the K block of
+// dims [32 (l / 16), 32 (l / 16) + 32).  That block holds the first halves
+// of lane groups 2j, 2j + 1 (j = l / 16 < 2) or their second halves
+// (j >= 2) in the slice layout above -- a pairing of data and scales the
+// hardware defines, and that this kernel only has to feed: lane (col, g)
+// passes the scale of dims [32g, 32g + 32) of its head or key row.
+template <int NKP, int HT, bool MX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void indexer_scan_kernel(IndexerLaunch a) {
   const int r = a.row_begin + (int)blockIdx.y;
   const int tile0 = (int)blockIdx.x * kTile;
@@ -80,6 +98,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
   constexpr int kRowBytes = 64 * NKP;
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[64 * 128];
   __shared__ __attribute__((aligned(16))) float w_lds[64];
+  constexpr int kNG = 2 * NKP;                 // 32-dim groups of a row (MX)
+  __shared__ uint32_t qs_lds[MX ? 64 * kNG : 1];  // query scales, one per word
   __shared__ float sc_lds[kWaves][kSpan];
   __shared__ uint32_t gm_lds[kWaves][kSpan / 2];
 
@@ -121,6 +141,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     if (off0 < kQBytes) *reinterpret_cast<v4i*>(&q_lds[off0]) = q0;
     if (off1 < kQBytes) *reinterpret_cast<v4i*>(&q_lds[off1]) = q1;
     if (threadIdx.x < HT * 16) w_lds[threadIdx.x] = wv;
+    if (MX) {  // the row's query scales; padding heads get 127 (x1, zero codes)
+      const uint8_t* qsrow = a.qI_scale + (int64_t)r * a.H_I * kNG;
+      const int nqs = a.H_I * kNG;
+      uint32_t qsv = qsrow[min((int)threadIdx.x, nqs - 1)];
+      if ((int)threadIdx.x >= nqs) qsv = 127u;
+      if (threadIdx.x < 64 * kNG) qs_lds[threadIdx.x] = qsv;
+    }
   }
 
   const int L = row_finish(a.rows, ri);
@@ -148,18 +175,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
                          (int64_t)(s0 & 63) * a.kI.row_stride;
     keys[j] = load_slice<NKP>(sub, lane_off);
   }
+  // MX: the scale words of the wave's key rows (the word at byte D_I of a
+  // row, inside it since the row stride is a multiple of 16 and at least
+  // D_I + D_I / 32), two per lane: word h of lane l belongs to sub-tile
+  // 4h + l / 16, row l % 16.  Each sub-tile fetches its rows' words across
+  // lanes when it needs them, so only two registers stay in flight.
+  static_assert(kSubPerWave == 8, "two scale words per lane cover the wave's sub-tiles");
+  uint32_t ksw[MX ? 2 : 1];
+  if (MX) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int s0l = w0 + (4 * h + g) * kSub;
+      const int phys_l = __shfl(my_page, (s0l - tile0) >> 6);
+      const bool ok_l = s0l / kBlock < a.rows.max_blocks && phys_l >= 0 &&
+                        (int64_t)phys_l < a.kI.num_blocks;
+      ksw[h] = *reinterpret_cast<const uint32_t*>(
+          kbase + (int64_t)(ok_l ? phys_l : 0) * a.kI.block_stride +
+          (int64_t)((s0l & 63) + col) * a.kI.row_stride + kRowBytes);
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
   // A operands (heads 16*ht + col); the head weights of this lane's
   // accumulator rows (register v of a 16x16 tile is row 4*g + v) are read
   // from LDS per use, which keeps the registers for keys in flight
   v8i aq[HT];
+  // This lane's A scale for head tile ht (group g of head 16ht + col) sits in
+  // byte ht of one register, and the MFMA's op-select immediate picks the
+  // byte; E4M3 keeps 127 (x1) in every byte.
+  int qscale = 0x7F7F7F7F;
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
     const v4i* src = reinterpret_cast<const v4i*>(&q_lds[(16 * ht + col) * kRowBytes]);
     const v4i lo = src[g];
     const v4i hi = NKP == 2 ? src[g + 4] : v4i{0, 0, 0, 0};
     aq[ht] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    if (MX && g < kNG)
+      qscale = (qscale & ~(0xFF << (8 * ht))) | ((int)qs_lds[(16 * ht + col) * kNG + g] << (8 * ht));
   }
   // Group maxima for the Top-K that follows: groups of G positions, G <= 8
   // a power of two, so a group never straddles a 16-position sub-tile
@@ -175,11 +227,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
 #pragma unroll
   for (int j = 0; j < kSubPerWave; ++j) {
     float part = 0.0f;
+    // B scale: byte g of the key row's scale word (127, i.e. x1, for unused
+    // groups and for E4M3)
+    int ks = 127;
+    if (MX) {
+      const uint32_t word = (uint32_t)__shfl((int)ksw[MX ? j / 4 : 0], 16 * (j % 4) + col);
+      ks = g < kNG ? (int)((word >> (8 * g)) & 0xFFu) : 127;
+    }
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[ht], keys[j], acc, 0, 0, 0, 0,
-                                                             0, 0);
+      v4f acc;
+      switch (ht) {  // the op-select byte must be an immediate (ht is one once unrolled)
+        case 0: acc = mfma_scaled<0>(aq[ht], keys[j], qscale, MX ? ks : 127); break;
+        case 1: acc = mfma_scaled<1>(aq[ht], keys[j], qscale, MX ? ks : 127); break;
+        case 2: acc = mfma_scaled<2>(aq[ht], keys[j], qscale, MX ? ks : 127); break;
+        default: acc = mfma_scaled<3>(aq[ht], keys[j], qscale, MX ? ks : 127); break;
+      }
       const v4f wr = *reinterpret_cast<const v4f*>(&w_lds[16 * ht + 4 * g]);
 #pragma unroll
       for (int v = 0; v < 4; ++v) part += wr[v] * fmaxf(acc[v], 0.0f);
@@ -211,32 +274,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
   if (bad_page && lane == 0) report(a.err, DSA_DEVERR_BLOCK);
 }
 
-template <int NKP, int HT>
+template <int NKP, int HT, bool MX>
 hipError_t launch_t(const IndexerLaunch& a, hipStream_t s) {
   dim3 grid((a.max_len + kTile - 1) / kTile, a.num_rows);
-  indexer_scan_kernel<NKP, HT><<<grid, 256, 0, s>>>(a);
+  indexer_scan_kernel<NKP, HT, MX><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
+}
+
+template <bool MX>
+hipError_t launch_mx(const IndexerLaunch& a, hipStream_t s) {
+  const int ht = (a.H_I + 15) / 16;
+  if (a.D_I == 128) {
+    switch (ht) {
+      case 1: return launch_t<2, 1, MX>(a, s);
+      case 2: return launch_t<2, 2, MX>(a, s);
+      case 3: return launch_t<2, 3, MX>(a, s);
+      default: return launch_t<2, 4, MX>(a, s);
+    }
+  }
+  switch (ht) {
+    case 1: return launch_t<1, 1, MX>(a, s);
+    case 2: return launch_t<1, 2, MX>(a, s);
+    case 3: return launch_t<1, 3, MX>(a, s);
+    default: return launch_t<1, 4, MX>(a, s);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_indexer_scores(const IndexerLaunch& a, hipStream_t s) {
   if (a.num_rows <= 0 || a.max_len <= 0) return hipSuccess;
-  const int ht = (a.H_I + 15) / 16;
-  if (a.D_I == 128) {
-    switch (ht) {
-      case 1: return launch_t<2, 1>(a, s);
-      case 2: return launch_t<2, 2>(a, s);
-      case 3: return launch_t<2, 3>(a, s);
-      default: return launch_t<2, 4>(a, s);
-    }
-  }
-  switch (ht) {
-    case 1: return launch_t<1, 1>(a, s);
-    case 2: return launch_t<1, 2>(a, s);
-    case 3: return launch_t<1, 3>(a, s);
-    default: return launch_t<1, 4>(a, s);
-  }
+  return a.qI_scale ? launch_mx<true>(a, s) : launch_mx<false>(a, s);
 }
 
 }  // namespace dsa

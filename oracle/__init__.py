@@ -23,7 +23,8 @@ numeric example for any step):
     cache from the indexer's position list;
   - section 4.3: the fused call takes the quantised query, the index keys and
     the head weights, ``idx = fused_topk(q8, k, g)``;
-  - section 5.1 / 5.2: FP8 storage for the indexer and the KV cache.
+  - section 5.1 / 5.2: FP8 storage for the indexer and the KV cache; the
+    indexer's MXFP8 format (one shared scale per group of 32).
 * "Bandwidth-Aware LLM Inference on Heterogeneous Many-Core Supercomputers"
   (THInfer), eq. 9: softmax attention softmax(Q K^T / sqrt(d)) V, used here as
   the dense reference; section III.B.4: fp32 (here: fp64) accumulation.
@@ -42,7 +43,7 @@ invariants).  The constants the pages never fix (ReLU gate, K, block size 64,
 head dims, attention scale) are readings, not values the pages confirm.
 """
 
-from .formats import E4M3_TABLE, e4m3_to_f64, bf16_to_f64
+from .formats import E4M3_TABLE, e4m3_to_f64, e8m0_to_f64, bf16_to_f64
 from .dsa import (
     resolve_rows,
     gather_positions,
@@ -56,7 +57,7 @@ from .dsa import (
 )
 
 __all__ = [
-    "E4M3_TABLE", "e4m3_to_f64", "bf16_to_f64",
+    "E4M3_TABLE", "e4m3_to_f64", "e8m0_to_f64", "bf16_to_f64",
     "resolve_rows", "gather_positions", "indexer_scores_row", "score_keys",
     "topk_row", "sparse_attn_row", "masked_dense_attn_row",
     "dense_causal_attn_row", "decode_step",

@@ -24,7 +24,10 @@ Array conventions (raw storage bits, exactly what the GPU reads):
 
 import numpy as np
 
-from .formats import bf16_to_f64, e4m3_to_f64
+from .formats import bf16_to_f64, e4m3_to_f64, e8m0_to_f64
+
+#: dims per shared scale of the MXFP8 indexer format (Day0 article, section 5.1)
+MX_GROUP = 32
 
 #: tokens per page of every paged cache
 BLOCK = 64
@@ -59,7 +62,7 @@ def gather_positions(cache, table_row, positions, block=BLOCK):
     return cache[phys, positions % block]
 
 
-def indexer_scores_row(qI_codes, w, kI_rows):
+def indexer_scores_row(qI_codes, w, kI_rows, qI_scale=None, kI_scale=None):
     """Index score of one query row against the given key rows.
 
     I[s] = sum_h w[h] * max(0, sum_d qI[h, d] * kI[s, d])
@@ -75,10 +78,28 @@ def indexer_scores_row(qI_codes, w, kI_rows):
     hundred of them needs far fewer than 53 bits.  The weighted head sum is
     formed in binary64 and rounded once to float32; a zero score is stored as
     +0.
+
+    MXFP8 (Day0 article, section 5.1: Q and K quantised per group of 32 with
+    one shared scale per group): given ``qI_scale`` [H_I, D_I/32] and
+    ``kI_scale`` [L, D_I/32] E8M0 bytes, each group's partial dot product is
+    multiplied by the two groups' scales before the groups are summed,
+
+    dot[h, s] = sum_g sq[h, g] * sk[s, g] * sum_{d in group g} qI[h, d] * kI[s, d].
+
+    Each group's sum is exact as above and the power-of-two scales keep it
+    exact; the groups are summed in binary64.
     """
     q = e4m3_to_f64(qI_codes)                       # [H_I, D_I]
     k = e4m3_to_f64(kI_rows)                        # [L, D_I]
-    dot = q @ k.T                                   # [H_I, L]
+    if qI_scale is None:
+        dot = q @ k.T                               # [H_I, L]
+    else:
+        sq = e8m0_to_f64(qI_scale)                  # [H_I, D_I / 32]
+        sk = e8m0_to_f64(kI_scale)                  # [L, D_I / 32]
+        dot = np.zeros((q.shape[0], k.shape[0]))
+        for g in range(q.shape[1] // MX_GROUP):
+            dims = slice(MX_GROUP * g, MX_GROUP * (g + 1))
+            dot += (q[:, dims] @ k[:, dims].T) * sq[:, g][:, None] * sk[:, g][None, :]
     gated = np.maximum(dot, 0.0)                    # ReLU gate, per head
     weights = np.asarray(w, dtype=np.float32).astype(np.float64)
     total = weights @ gated                         # head-weighted sum, [L]
@@ -183,11 +204,13 @@ def dense_causal_attn_row(q_bits, k_all_bits, v_all_bits, scale):
 
 def decode_step(*, qI, w, kI_cache, q, k_cache, v_cache, block_table, seq_lens,
                 K, scale, D_v, row_seq=None, row_pos=None, rows=None,
-                keep_scores=True):
+                keep_scores=True, qI_scale=None):
     """The whole step for the chosen query rows (default: all rows).
 
     Row by row: index scores over positions 0..p_r, Top-K, gather of the
-    selected KV rows, sparse softmax attention.  Returns a dict with
+    selected KV rows, sparse softmax attention.  With ``qI_scale`` [rows,
+    H_I, D_I/32] the indexer is MXFP8: each ``kI_cache`` row then holds its
+    D_I codes followed by its D_I/32 scale bytes.  Returns a dict with
     ``scores`` (list of float32 arrays, or None), ``indices`` int32 [R, K],
     ``counts`` int64 [R], ``out`` float64 [R, H_q, D_v], ``lse`` float64
     [R, H_q] and ``rows`` (the row ids, in order).
@@ -204,7 +227,13 @@ def decode_step(*, qI, w, kI_cache, q, k_cache, v_cache, block_table, seq_lens,
     for i, r in enumerate(rows):
         b, p = rs[r], rp[r]
         history = np.arange(p + 1)
-        sc = indexer_scores_row(qI[r], w[r], gather_positions(kI_cache, block_table[b], history))
+        k_index = gather_positions(kI_cache, block_table[b], history)
+        if qI_scale is None:
+            sc = indexer_scores_row(qI[r], w[r], k_index)
+        else:
+            D_I = qI.shape[2]
+            sc = indexer_scores_row(qI[r], w[r], k_index[:, :D_I], qI_scale[r],
+                                    k_index[:, D_I:D_I + D_I // MX_GROUP])
         idx, n = topk_row(sc, K)
         chosen = idx[:n]
         k_rows = gather_positions(k_cache, block_table[b], chosen)

@@ -9,6 +9,10 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
   and mantissa bits are all ones (0x7F and 0xFF) are NaN; there is no
   infinity, so the largest finite magnitude is 1.75 * 2**8 = 448.
 * bfloat16: the upper 16 bits of an IEEE-754 binary32 value.
+* E8M0 scale bytes of the MXFP8 indexer format (Day0 article, section 5.1:
+  one shared scale per group of 32 values).  The page does not state the
+  encoding; the reading taken is the OCP microscaling one: byte e stands for
+  2**(e - 127), and e = 255 is NaN.
 """
 
 import numpy as np
@@ -32,6 +36,15 @@ E4M3_TABLE = np.array([_e4m3_value(c) for c in range(256)], dtype=np.float64)
 def e4m3_to_f64(codes) -> np.ndarray:
     """Decode an array of E4M3 byte codes to binary64 (exact)."""
     return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def e8m0_to_f64(codes) -> np.ndarray:
+    """Decode an array of E8M0 scale bytes to binary64 (exact): 2**(e - 127),
+    NaN for 255."""
+    e = np.asarray(codes, dtype=np.uint8).astype(np.float64)
+    out = np.exp2(e - 127.0)
+    out[np.asarray(codes) == 255] = np.nan
+    return out
 
 
 def bf16_to_f64(bits) -> np.ndarray:

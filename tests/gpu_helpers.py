@@ -99,8 +99,14 @@ def score_bound(arr, i, p):
     import oracle
     b = arr["row_seq"][i]
     q = np.abs(oracle.e4m3_to_f64(arr["qI"][i]))
-    k = np.abs(oracle.e4m3_to_f64(
-        oracle.gather_positions(arr["kI_cache"], arr["block_table"][b], np.arange(p + 1))))
+    rows = oracle.gather_positions(arr["kI_cache"], arr["block_table"][b], np.arange(p + 1))
+    D = q.shape[1]
+    k = np.abs(oracle.e4m3_to_f64(rows[:, :D]))
+    if arr.get("qI_scale") is not None:  # MXFP8: fold each group's scales in
+        G = D // 32
+        sq = np.repeat(oracle.e8m0_to_f64(arr["qI_scale"][i]), 32, axis=1)
+        sk = np.repeat(oracle.e8m0_to_f64(rows[:, D:D + G]), 32, axis=1)
+        q, k = q * sq, k * sk
     mag = np.abs(arr["w"][i].astype(np.float64)) @ (q @ k.T)
     n = q.shape[1] + q.shape[0] + 1
     gamma = n * U32 / (1 - n * U32)

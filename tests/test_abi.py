@@ -106,6 +106,20 @@ def test_indexer_scores_rejections():
                       None) == B.DSA_ERR_INVALID
 
 
+def test_indexer_format_rejections():
+    # MXFP8: scales for qI are required, the key rows must hold the codes and
+    # one scale byte per 32 dims (row stride >= D_I + D_I / 32, a multiple of 16)
+    mx = dict(indexer_format=B.DSA_INDEXER_MXFP8, qI_scale=FAKE + (2 << 30))
+    assert call_scores(prob(num_rows=0, **mx), kI=paged(row=144)) == B.DSA_OK
+    assert call_scores(prob(num_rows=0, D_I=64, **mx), kI=paged(row=80)) == B.DSA_OK
+    assert call_scores(prob(**mx), kI=paged(row=128)) == B.DSA_ERR_INVALID   # no room for scales
+    assert call_scores(prob(indexer_format=B.DSA_INDEXER_MXFP8)) == B.DSA_ERR_INVALID  # no qI_scale
+    assert call_scores(prob(qI_scale=FAKE)) == B.DSA_ERR_INVALID             # E4M3 with scales
+    assert call_scores(prob(indexer_format=2)) == B.DSA_ERR_INVALID          # unknown format
+    assert ws_size(prob(indexer_format=2), B.DSA_OP_INDEXER_SCORES) == 0
+    assert ws_size(prob(**mx), B.DSA_OP_DECODE_STEP) > 0
+
+
 def test_topk_rejections():
     def call(p, scores=FAKE, ld=131072, idx=FAKE, counts=None, ws=FAKE, nbytes=256):
         return B.raw_call("dsa_topk", ctypes.byref(p), ctypes.c_void_p(scores),

@@ -77,3 +77,19 @@ def test_full_size_gaussian_bench_shape():
     same = [i for i in rows if (gi[i] == orc["indices"][i]).all()]
     if same:
         check_attention(res["out"][same], res["lse"][same], orc["out"][same], orc["lse"][same])
+
+
+def test_full_size_mxfp8_indexer_bench_shape():
+    # the 4 x 128k decode step with MXFP8 indexer operands (one E8M0 scale
+    # per 32 dims of every query head and key row), integer mode: every row's
+    # indices bit-exact against the oracle, attention within tolerance
+    wl = CONFIGS[BENCH_WORKLOAD].with_(indexer_fmt="mxfp8")
+    say(f"full size {BENCH_WORKLOAD}: MXFP8 indexer, integer mode, seed {wl.seed}")
+    batch = make_batch(wl, device="cuda", seed=wl.seed, mode="int")
+    res = gpu_decode(batch)
+    _check_every_row(batch, res)
+    rows = list(range(batch.rows))
+    orc = run_oracle(oracle_arrays(batch, rows=rows), keep_scores=False)
+    assert (np_(res["counts"]) == orc["counts"]).all()
+    assert (np_(res["indices"]) == orc["indices"]).all()
+    check_attention(res["out"], res["lse"], orc["out"], orc["lse"])

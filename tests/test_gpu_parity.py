@@ -37,6 +37,10 @@ CASES = {
     "mla_sepv": dict(lengths=[1, 777, 3000], mode="int", latent=False, **MLA),
     # histories long enough for the Top-K to group positions by 2, 4 and 8
     "mla_int_grouped": dict(lengths=[9000, 20000, 40000], mode="int", **MLA),
+    # MXFP8 indexer operands (one E8M0 scale per 32 dims), both head dims
+    "mla_mx_int": dict(lengths=LENGTHS, mode="int", indexer_fmt="mxfp8", **MLA),
+    "h48_d64_mx": dict(lengths=[777, 2500], mode="int", indexer_fmt="mxfp8",
+                       **{**MLA, "H_I": 48, "D_I": 64, "H_q": 80}),
 }
 
 
@@ -57,8 +61,9 @@ def test_scores_exact_integer_mode(name):
     check_scores_exact(gpu_scores(batch), orc, row_positions(batch))
 
 
-def test_scores_gaussian_within_fp32_bound():
-    batch = _batch("mla_int", mode="gauss", seed=22)
+@pytest.mark.parametrize("name", ["mla_int", "mla_mx_int"])
+def test_scores_gaussian_within_fp32_bound(name):
+    batch = _batch(name, mode="gauss", seed=22)
     arr = oracle_arrays(batch)
     orc = run_oracle(arr)
     g = np_(gpu_scores(batch))
@@ -158,7 +163,7 @@ def test_sparse_attn_skips_padding_and_handles_empty_rows():
 
 
 @pytest.mark.parametrize("name", ["mla_int", "mla_int_shuffled", "tiny_int", "mla_int_k100",
-                                  "mla_sepv", "mla_int_grouped"])
+                                  "mla_sepv", "mla_int_grouped", "mla_mx_int"])
 def test_decode_step_integer_mode(name):
     batch = _batch(name, seed=27)
     arr = oracle_arrays(batch)

@@ -155,6 +155,113 @@ def test_scores_gaussian_close_to_float64_reference():
     assert (np.abs(got.astype(np.float64) - ref.numpy()) <= 0.5 * ulp + 1e-300).all()
 
 
+# ----------------------------------------------------- MXFP8 index scores
+
+def test_e8m0_closed_form_codes():
+    # E8M0 scale byte e stands for 2**(e - 127) (OCP microscaling reading)
+    cases = {0: 2.0 ** -127, 1: 2.0 ** -126, 126: 0.5, 127: 1.0, 128: 2.0, 130: 8.0,
+             254: 2.0 ** 127}
+    for code, val in cases.items():
+        assert oracle.e8m0_to_f64([code])[0] == val, code
+    assert np.isnan(oracle.e8m0_to_f64([255])[0])
+    # doubling per code step, over the whole finite range
+    v = oracle.e8m0_to_f64(np.arange(255, dtype=np.uint8))
+    assert (v[1:] == 2 * v[:-1]).all()
+
+
+def _mx_case(rng, H=6, D=128, L=50):
+    q = rng.integers(-4, 5, (H, D))
+    k = rng.integers(-4, 5, (L, D))
+    sq = rng.integers(125, 130, (H, D // 32)).astype(np.uint8)
+    sk = rng.integers(125, 130, (L, D // 32)).astype(np.uint8)
+    w = rng.integers(0, 4, H).astype(np.float32)
+    return q, k, sq, sk, w
+
+
+def test_mx_scores_unit_scales_reduce_to_e4m3():
+    # every scale 127 (x1): the MXFP8 score is the pinned unscaled score
+    rng = np.random.default_rng(11)
+    q, k, _, _, w = _mx_case(rng)
+    ones_q = np.full((q.shape[0], q.shape[1] // 32), 127, np.uint8)
+    ones_k = np.full((k.shape[0], k.shape[1] // 32), 127, np.uint8)
+    got = oracle.indexer_scores_row(_e4m3(q), w, _e4m3(k), ones_q, ones_k)
+    assert (got == oracle.indexer_scores_row(_e4m3(q), w, _e4m3(k))).all()
+
+
+def test_mx_scores_one_hot_keys_closed_form():
+    # key s = c_s * e_{d_s} with scale byte b on the group of d_s: the head's
+    # dot product is c_s * q[h, d_s] * 2**(eq[h, d_s // 32] + b - 254)
+    rng = np.random.default_rng(12)
+    H, D, L = 5, 128, 40
+    q = rng.integers(-4, 5, (H, D))
+    sq = rng.integers(124, 131, (H, D // 32)).astype(np.uint8)
+    w = rng.integers(0, 4, H).astype(np.float32)
+    d_s = rng.integers(0, D, L)
+    c_s = rng.choice([-3, -1, 1, 2, 4], L)
+    k = np.zeros((L, D))
+    k[np.arange(L), d_s] = c_s
+    sk = rng.integers(124, 131, (L, D // 32)).astype(np.uint8)
+    got = oracle.indexer_scores_row(_e4m3(q), w, _e4m3(k), sq, sk)
+    for s in range(L):
+        g = d_s[s] // 32
+        want = 0.0
+        for h in range(H):
+            scale = 2.0 ** (int(sq[h, g]) + int(sk[s, g]) - 254)
+            want += float(w[h]) * max(0.0, float(c_s[s]) * float(q[h, d_s[s]]) * scale)
+        assert got[s] == np.float32(want), s
+
+
+def test_mx_scores_code_scale_trade_and_group_locality():
+    rng = np.random.default_rng(13)
+    q, k, sq, sk, w = _mx_case(rng)
+    base = oracle.indexer_scores_row(_e4m3(q), w, _e4m3(k), sq, sk)
+    # halving a group's codes (kept even so halves stay integers) while
+    # raising that group's scale by one step leaves every score unchanged;
+    # the trade only holds if the scale multiplies exactly its own 32 dims
+    q2, sq2 = 2 * (q // 2), sq.copy()
+    base2 = oracle.indexer_scores_row(_e4m3(q2), w, _e4m3(k), sq2, sk)
+    for g in range(q.shape[1] // 32):
+        qh, sqh = q2.copy(), sq2.copy()
+        qh[:, 32 * g:32 * (g + 1)] //= 2
+        sqh[:, g] += 1
+        assert (oracle.indexer_scores_row(_e4m3(qh), w, _e4m3(k), sqh, sk) == base2).all(), g
+    # a key group's scale one step up doubles exactly that group's share of
+    # every head's dot product: check through the linear identity of the gate
+    # (I(q) - I(-q) = sum_h w_h dot_h), group by group with integer arithmetic
+    lin = lambda qq, sk_: (oracle.indexer_scores_row(_e4m3(qq), w, _e4m3(k), sq, sk_).astype(np.float64)
+                           - oracle.indexer_scores_row(_e4m3(-qq), w, _e4m3(k), sq, sk_).astype(np.float64))
+    d0 = lin(q, sk)
+    for g in range(q.shape[1] // 32):
+        sk_up = sk.copy()
+        sk_up[:, g] += 1
+        dims = slice(32 * g, 32 * (g + 1))
+        share = sum(float(w[h]) * (q[h, dims] * k[:, dims]).sum(axis=1).astype(np.float64)
+                    * 2.0 ** (sq[h, g].astype(np.int64) + sk[:, g].astype(np.int64) - 254)
+                    for h in range(q.shape[0]))
+        assert (lin(q, sk_up) - d0 == share).all(), g
+    assert base.dtype == np.float32
+
+
+def test_mx_scores_integer_mode_exact():
+    # integer codes in [-4, 4], scales 2**-2 .. 2**2: exact rational
+    # arithmetic (Python ints over a common 2**-8 denominator) as the route
+    rng = np.random.default_rng(14)
+    q, k, sq, sk, w = _mx_case(rng, H=16, L=60)
+    s = oracle.indexer_scores_row(_e4m3(q), w, _e4m3(k), sq, sk)
+    H, L = q.shape[0], k.shape[0]
+    want = []
+    for j in range(L):
+        tot = 0
+        for h in range(H):
+            dot = 0  # in units of 2**-8
+            for g in range(q.shape[1] // 32):
+                part = int((q[h, 32 * g:32 * (g + 1)] * k[j, 32 * g:32 * (g + 1)]).sum())
+                dot += part * 2 ** (int(sq[h, g]) + int(sk[j, g]) - 254 + 8)
+            tot += int(w[h]) * max(0, dot)
+        want.append(tot / 256.0)
+    assert (s.astype(np.float64) == np.array(want)).all()
+
+
 # ------------------------------------------------------------------ Top-K
 
 def test_score_keys_order():

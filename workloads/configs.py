@@ -29,6 +29,9 @@ class Workload:
     latent: bool = True             # V = first D_v columns of the K row
     table: str = "identity"         # "identity" or "shuffled" block table
     seed: int = 0
+    # indexer operands: "e4m3" unscaled codes, or "mxfp8" codes with one E8M0
+    # scale per 32 dims (integer mode: codes in [-4, 4], scales 2**-1 .. 2**1)
+    indexer_fmt: str = "e4m3"
 
     @property
     def rows(self) -> int:

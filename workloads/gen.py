@@ -32,10 +32,12 @@ class Batch:
     row_pos: Optional[torch.Tensor]
     qI: torch.Tensor         # uint8 E4M3 [rows, H_I, D_I]
     w: torch.Tensor          # float32 [rows, H_I]
-    kI: torch.Tensor         # uint8 E4M3 [num_blocks, 64, D_I]
+    kI: torch.Tensor         # uint8 E4M3 [num_blocks, 64, D_I] (MXFP8: D_I + 16, the
+                             # row's D_I/32 E8M0 scales right after its codes)
     q: torch.Tensor          # bfloat16 [rows, H_q, D_qk]
     kv: torch.Tensor         # bfloat16 [num_blocks, 64, D_qk]
     v: Optional[torch.Tensor] = None   # bfloat16 [num_blocks, 64, D_v] (separate V)
+    qI_scale: Optional[torch.Tensor] = None  # MXFP8: uint8 E8M0 [rows, H_I, D_I/32]
     extra: dict = field(default_factory=dict)
 
     @property
@@ -63,6 +65,41 @@ def _fp8_codes(shape, mode, gen, device):
             x = torch.randn(n, generator=gen, device=device, dtype=torch.float32)
             return x.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
     return _fill(out, draw)
+
+
+MX_GROUP = 32
+
+
+def _mx_codes_scales(shape, mode, gen, device):
+    """MXFP8 operands of the given shape (last dim a multiple of 32): E4M3
+    codes and one E8M0 scale byte per group of 32.  Integer mode: codes are
+    integers in [-4, 4] and scales 2**-1, 1 or 2**1 (every score stays exact
+    in float32).  Gaussian mode: N(0, 1) values quantised the OCP way, shared
+    exponent floor(log2(max |x|)) - 8 per group, codes saturated to +-448."""
+    *lead, D = shape
+    codes = torch.empty(shape, dtype=torch.uint8, device=device)
+    scales = torch.empty((*lead, D // MX_GROUP), dtype=torch.uint8, device=device)
+    flat_c = codes.view(-1, D)
+    flat_s = scales.view(-1, D // MX_GROUP)
+    rows = flat_c.shape[0]
+    step = max(1, _CHUNK // D)
+    for i in range(0, rows, step):
+        j = min(rows, i + step)
+        n = j - i
+        if mode == "int":
+            x = torch.randint(-4, 5, (n, D), generator=gen, device=device, dtype=torch.int32)
+            flat_c[i:j] = x.to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)
+            flat_s[i:j] = torch.randint(126, 129, (n, D // MX_GROUP), generator=gen,
+                                        device=device, dtype=torch.int32).to(torch.uint8)
+        else:
+            x = torch.randn(n, D // MX_GROUP, MX_GROUP, generator=gen, device=device,
+                            dtype=torch.float32)
+            amax = x.abs().amax(dim=2, keepdim=True).clamp_min(2.0 ** -100)
+            e = torch.floor(torch.log2(amax)) - 8.0
+            y = (x * torch.exp2(-e)).clamp_(-448.0, 448.0)
+            flat_c[i:j] = y.to(torch.float8_e4m3fn).view(torch.uint8).view(n, D)
+            flat_s[i:j] = (e.view(n, -1) + 127.0).to(torch.int32).to(torch.uint8)
+    return codes, scales
 
 
 def _bf16_normal(shape, gen, device):
@@ -134,9 +171,19 @@ def make_batch(wl: Workload, device="cpu", seed=None, mode=None, table=None,
         row_pos_h = [L - 1 for L in lens]
         row_seq = row_pos = None
 
-    qI = _fp8_codes((R, wl.H_I, wl.D_I), mode, gd, device)
-    w = _weights((R, wl.H_I), mode, gd, device)
-    kI = _fp8_codes((num_blocks, BLOCK, wl.D_I), mode, gd, device)
+    qI_scale = None
+    if wl.indexer_fmt == "mxfp8":
+        qI, qI_scale = _mx_codes_scales((R, wl.H_I, wl.D_I), mode, gd, device)
+        w = _weights((R, wl.H_I), mode, gd, device)
+        k_codes, k_scales = _mx_codes_scales((num_blocks, BLOCK, wl.D_I), mode, gd, device)
+        kI = torch.zeros((num_blocks, BLOCK, wl.D_I + 16), dtype=torch.uint8, device=device)
+        kI[..., :wl.D_I] = k_codes
+        kI[..., wl.D_I:wl.D_I + wl.D_I // MX_GROUP] = k_scales
+        del k_codes, k_scales
+    else:
+        qI = _fp8_codes((R, wl.H_I, wl.D_I), mode, gd, device)
+        w = _weights((R, wl.H_I), mode, gd, device)
+        kI = _fp8_codes((num_blocks, BLOCK, wl.D_I), mode, gd, device)
     q = _bf16_normal((R, wl.H_q, wl.D_qk), gd, device)
     kv = _bf16_normal((num_blocks, BLOCK, wl.D_qk), gd, device)
     v = None if wl.latent else _bf16_normal((num_blocks, BLOCK, wl.D_v), gd, device)
@@ -145,7 +192,7 @@ def make_batch(wl: Workload, device="cpu", seed=None, mode=None, table=None,
                  max_blocks=max_blocks, num_blocks=num_blocks,
                  seq_lens=torch.tensor(lens, dtype=torch.int32, device=device),
                  block_table=bt.to(device), row_seq=row_seq, row_pos=row_pos,
-                 qI=qI, w=w, kI=kI, q=q, kv=kv, v=v)
+                 qI=qI, w=w, kI=kI, q=q, kv=kv, v=v, qI_scale=qI_scale)
 
 
 def row_positions(batch: Batch):
@@ -195,6 +242,7 @@ def oracle_arrays(batch: Batch, rows=None) -> dict:
             off += nb
     sel = torch.as_tensor(rows, dtype=torch.int64).to(batch.qI.device)
     return {
+        "qI_scale": None if batch.qI_scale is None else _np(batch.qI_scale.index_select(0, sel)),
         "qI": _np(batch.qI.index_select(0, sel)),
         "w": _np(batch.w.index_select(0, sel)),
         "q": _np(batch.q.index_select(0, sel).view(torch.int16)).view(np.uint16),
