@@ -636,9 +636,10 @@ __device__ __forceinline__ void row_single(const TopkLaunch& a, int r_local, int
 //     integer arithmetic on the same data, so the same t everywhere);
 //  b. each keeps its slice's keys >= t and writes them, with their
 //     positions and in position order, to its segment of the work area;
-//  c. the last workgroup of the row to finish (a device-scope fence, then a
-//     counter) reads the segments back in slice order -- position order --
-//     selects T and the tie budget exactly and writes the row out.
+//  c. the last workgroup of the row to count itself in (a device-scope
+//     counter, once its stores have completed) reads the segments back in
+//     slice order -- position order -- selects T and the tie budget exactly
+//     and writes the row out; the others warm the caches for the attention.
 // Nothing waits on another workgroup.  Rows that do not take this path run
 // row_single in slice 0's workgroup.
 
