@@ -62,7 +62,7 @@ extern "C" {
 #define DSA_API
 #endif
 
-#define DSA_ABI_VERSION 2
+#define DSA_ABI_VERSION 3
 #define DSA_BLOCK_SIZE 64
 
 typedef enum {
@@ -148,8 +148,13 @@ DSA_API size_t dsa_workspace_size(const dsa_problem* p, int op);
  *   sum_d qI[r, h, d] * kI[s, d]  becomes
  *   sum_g 2**(eq[r, h, g] + ek[s, g] - 254) * sum_{d in g} qI[r, h, d] * kI[s, d]
  *   eq      p->qI_scale, [num_rows][H_I][D_I / 32]
- *   ek      bytes D_I .. D_I + D_I/32 - 1 of each kI row (so the row stride
- *           must be at least D_I + D_I / 32)
+ *   ek      the scale area of each kI block, after its 64 rows of codes:
+ *           ek[s, g] of the position s in row i of block b is the byte at
+ *           b * block_stride + 64 * row_stride + i * (D_I / 32) + g, so a
+ *           block holds 64 * row_stride bytes of codes and then 2 * D_I
+ *           bytes of scales (block_stride >= 64 * row_stride + 2 * D_I,
+ *           else DSA_ERR_INVALID).  The code rows keep their alignment and
+ *           the scales of 64 positions are one contiguous run.
  * Power-of-two scales keep every product exact.
  */
 DSA_API int dsa_indexer_scores(const dsa_problem* p, const uint8_t* qI, const float* w, dsa_paged kI,

@@ -27,7 +27,7 @@ DSA_OP_TOPK = 1
 DSA_OP_SPARSE_ATTN = 2
 DSA_OP_DECODE_STEP = 3
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 DSA_INDEXER_E4M3 = 0
 DSA_INDEXER_MXFP8 = 1
 BLOCK = 64
@@ -107,9 +107,12 @@ def _stream(stream):
 
 
 def paged(cache: torch.Tensor) -> DsaPaged:
-    """Descriptor of a [num_blocks, 64, ...] cache tensor (any row stride)."""
-    if cache.dim() < 3 or cache.shape[1] != BLOCK:
-        raise ValueError("paged cache must be [num_blocks, 64, row]")
+    """Descriptor of a [num_blocks, 64, ...] cache tensor (any row stride).
+    An MXFP8 index-key cache is [num_blocks, 66, D_I]: two more D_I-byte rows
+    per block hold the 64 rows' scales."""
+    if cache.dim() < 3 or cache.shape[1] not in (BLOCK, BLOCK + 2):
+        raise ValueError("paged cache must be [num_blocks, 64, row] ([num_blocks, 66, D_I] "
+                         "for MXFP8 index keys)")
     es = cache.element_size()
     return DsaPaged(cache.data_ptr(), cache.stride(0) * es, cache.stride(1) * es, cache.shape[0])
 
@@ -119,7 +122,7 @@ def problem(*, seq_lens, block_table, num_rows=None, row_seq=None, row_pos=None,
             qI_scale=None) -> DsaProblem:
     """Problem descriptor; device tensors are referenced, not copied.  With
     ``qI_scale`` (uint8 E8M0 [rows, H_I, D_I/32]) the indexer runs in MXFP8
-    format and the index-key rows carry their scales after the codes."""
+    format and each index-key block carries its rows' scales after the code rows."""
     num_seqs = int(seq_lens.shape[0])
     if num_rows is None:
         num_rows = int(row_seq.shape[0]) if row_seq is not None else num_seqs

@@ -43,12 +43,6 @@ int check_indexer_shape(const dsa_problem* p) {
   return DSA_OK;
 }
 
-// bytes of an index-key row the indexer reads: the codes, then (MXFP8) one
-// scale byte per 32 dims
-int64_t kI_row_bytes(const dsa_problem* p) {
-  return p->D_I + (p->indexer_format == DSA_INDEXER_MXFP8 ? p->D_I / 32 : 0);
-}
-
 int check_attn_shape(const dsa_problem* p) {
   if (p->H_q < 1 || p->D_qk < 1 || p->D_v < 1 || p->K < 1) return DSA_ERR_INVALID;
   if (!std::isfinite(p->scale)) return DSA_ERR_INVALID;
@@ -66,6 +60,17 @@ int check_paged(const dsa_paged& c, int64_t row_bytes) {
   if (c.row_stride < row_bytes) return DSA_ERR_INVALID;
   // kernels address the rows of one block with 32-bit offsets
   if (c.row_stride > (int64_t(1) << 24)) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
+}
+
+// The index-key cache: D_I code bytes per row; MXFP8 blocks also hold the
+// 64 rows' scales (D_I / 32 bytes each) after the code rows.
+int check_kI(const dsa_problem* p, const dsa_paged& kI) {
+  int st = check_paged(kI, p->D_I);
+  if (st != DSA_OK) return st;
+  if (p->indexer_format == DSA_INDEXER_MXFP8 &&
+      kI.block_stride < 64 * kI.row_stride + 2 * (int64_t)p->D_I)
+    return DSA_ERR_INVALID;
   return DSA_OK;
 }
 
@@ -174,7 +179,7 @@ int dsa_indexer_scores(const dsa_problem* p, const uint8_t* qI, const float* w, 
   if ((st = check_indexer_shape(p)) != DSA_OK) return st;
   if (!qI || !w || !scores) return DSA_ERR_INVALID;
   if (!aligned(qI, 16) || !aligned(w, 4) || !aligned(scores, 4)) return DSA_ERR_INVALID;
-  if ((st = check_paged(kI, kI_row_bytes(p))) != DSA_OK) return st;
+  if ((st = check_kI(p, kI)) != DSA_OK) return st;
   if (ld_scores < max_len(p)) return DSA_ERR_INVALID;
   if ((st = check_ws(ws, ws_bytes, kHeader)) != DSA_OK) return st;
   if (p->num_rows == 0) return DSA_OK;
@@ -293,7 +298,7 @@ int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa
   if ((st = check_indexer_shape(p)) != DSA_OK) return st;
   if ((st = check_attn_args(p, q, k, v, out, lse)) != DSA_OK) return st;
   if (!qI || !w || !aligned(qI, 16) || !aligned(w, 4)) return DSA_ERR_INVALID;
-  if ((st = check_paged(kI, kI_row_bytes(p))) != DSA_OK) return st;
+  if ((st = check_kI(p, kI)) != DSA_OK) return st;
   if ((indices_out && !aligned(indices_out, 4)) || (counts_out && !aligned(counts_out, 4)))
     return DSA_ERR_INVALID;
   if ((st = check_ws(ws, ws_bytes, dsa_workspace_size(p, DSA_OP_DECODE_STEP))) != DSA_OK)

@@ -76,7 +76,8 @@ __device__ __forceinline__ uint32_t max_lanes(uint32_t k, int G) {
 
 // NKP = D_I / 64 pieces per lane; HT = 16-head tiles (ceil(H_I / 16)); MX:
 // MXFP8 operands (one E8M0 scale per 32 dims of every query head and key
-// row, Day0 section 5.1), else unscaled E4M3.
+// row, Day0 section 5.1; a key block's 64 rows of scales follow its 64 code
+// rows), else unscaled E4M3.
 //
 // Scales.  The block-scaled MFMA takes one scale byte per lane for each
 // operand: lane l scales row (A) or column (B) l % 16 over the K block of
@@ -175,23 +176,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
                          (int64_t)(s0 & 63) * a.kI.row_stride;
     keys[j] = load_slice<NKP>(sub, lane_off);
   }
-  // MX: the scale words of the wave's key rows (the word at byte D_I of a
-  // row, inside it since the row stride is a multiple of 16 and at least
-  // D_I + D_I / 32), two per lane: word h of lane l belongs to sub-tile
-  // 4h + l / 16, row l % 16.  Each sub-tile fetches its rows' words across
-  // lanes when it needs them, so only two registers stay in flight.
-  static_assert(kSubPerWave == 8, "two scale words per lane cover the wave's sub-tiles");
+  // MX: the scale words of the wave's key rows.  The wave's 128 positions
+  // are two whole blocks (w0 is a multiple of 128), and a block keeps its
+  // 64 rows' scales together after its code rows: lane l takes row l's
+  // scales from block h, so word h of lane l belongs to sub-tile 4h + l / 16,
+  // row l % 16, and each load is one contiguous run.  Each sub-tile fetches
+  // its rows' words across lanes when it needs them, so only two registers
+  // stay in flight.
+  static_assert(kSubPerWave == 8 && kSpan == 2 * kBlock, "two scale words per lane cover the wave");
   uint32_t ksw[MX ? 2 : 1];
   if (MX) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int s0l = w0 + (4 * h + g) * kSub;
-      const int phys_l = __shfl(my_page, (s0l - tile0) >> 6);
-      const bool ok_l = s0l / kBlock < a.rows.max_blocks && phys_l >= 0 &&
-                        (int64_t)phys_l < a.kI.num_blocks;
-      ksw[h] = *reinterpret_cast<const uint32_t*>(
-          kbase + (int64_t)(ok_l ? phys_l : 0) * a.kI.block_stride +
-          (int64_t)((s0l & 63) + col) * a.kI.row_stride + kRowBytes);
+      const int phys = __builtin_amdgcn_readlane(my_page, ((w0 - tile0) >> 6) + h);
+      const uint8_t* area = kbase + (int64_t)(page_ok[4 * h] ? phys : 0) * a.kI.block_stride +
+                            (int64_t)kBlock * a.kI.row_stride;
+      if constexpr (kNG == 4)
+        ksw[h] = *reinterpret_cast<const uint32_t*>(area + 4 * lane);
+      else
+        ksw[h] = *reinterpret_cast<const uint16_t*>(area + 2 * lane);
     }
   }
   __builtin_amdgcn_sched_barrier(0);

@@ -204,13 +204,13 @@ def dense_causal_attn_row(q_bits, k_all_bits, v_all_bits, scale):
 
 def decode_step(*, qI, w, kI_cache, q, k_cache, v_cache, block_table, seq_lens,
                 K, scale, D_v, row_seq=None, row_pos=None, rows=None,
-                keep_scores=True, qI_scale=None):
+                keep_scores=True, qI_scale=None, kI_scale_cache=None):
     """The whole step for the chosen query rows (default: all rows).
 
     Row by row: index scores over positions 0..p_r, Top-K, gather of the
     selected KV rows, sparse softmax attention.  With ``qI_scale`` [rows,
-    H_I, D_I/32] the indexer is MXFP8: each ``kI_cache`` row then holds its
-    D_I codes followed by its D_I/32 scale bytes.  Returns a dict with
+    H_I, D_I/32] and ``kI_scale_cache`` [num_blocks, 64, D_I/32] (paged like
+    ``kI_cache``) the indexer is MXFP8.  Returns a dict with
     ``scores`` (list of float32 arrays, or None), ``indices`` int32 [R, K],
     ``counts`` int64 [R], ``out`` float64 [R, H_q, D_v], ``lse`` float64
     [R, H_q] and ``rows`` (the row ids, in order).
@@ -231,9 +231,8 @@ def decode_step(*, qI, w, kI_cache, q, k_cache, v_cache, block_table, seq_lens,
         if qI_scale is None:
             sc = indexer_scores_row(qI[r], w[r], k_index)
         else:
-            D_I = qI.shape[2]
-            sc = indexer_scores_row(qI[r], w[r], k_index[:, :D_I], qI_scale[r],
-                                    k_index[:, D_I:D_I + D_I // MX_GROUP])
+            k_scale = gather_positions(kI_scale_cache, block_table[b], history)
+            sc = indexer_scores_row(qI[r], w[r], k_index, qI_scale[r], k_scale)
         idx, n = topk_row(sc, K)
         chosen = idx[:n]
         k_rows = gather_positions(k_cache, block_table[b], chosen)

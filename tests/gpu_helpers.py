@@ -105,7 +105,9 @@ def score_bound(arr, i, p):
     if arr.get("qI_scale") is not None:  # MXFP8: fold each group's scales in
         G = D // 32
         sq = np.repeat(oracle.e8m0_to_f64(arr["qI_scale"][i]), 32, axis=1)
-        sk = np.repeat(oracle.e8m0_to_f64(rows[:, D:D + G]), 32, axis=1)
+        srows = oracle.gather_positions(arr["kI_scale_cache"], arr["block_table"][b],
+                                        np.arange(p + 1))
+        sk = np.repeat(oracle.e8m0_to_f64(srows[:, :G]), 32, axis=1)
         q, k = q * sq, k * sk
     mag = np.abs(arr["w"][i].astype(np.float64)) @ (q @ k.T)
     n = q.shape[1] + q.shape[0] + 1

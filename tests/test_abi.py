@@ -107,12 +107,15 @@ def test_indexer_scores_rejections():
 
 
 def test_indexer_format_rejections():
-    # MXFP8: scales for qI are required, the key rows must hold the codes and
-    # one scale byte per 32 dims (row stride >= D_I + D_I / 32, a multiple of 16)
+    # MXFP8: scales for qI are required, and each key block must hold its 64
+    # code rows and then 2 * D_I bytes of row scales
     mx = dict(indexer_format=B.DSA_INDEXER_MXFP8, qI_scale=FAKE + (2 << 30))
-    assert call_scores(prob(num_rows=0, **mx), kI=paged(row=144)) == B.DSA_OK
-    assert call_scores(prob(num_rows=0, D_I=64, **mx), kI=paged(row=80)) == B.DSA_OK
-    assert call_scores(prob(**mx), kI=paged(row=128)) == B.DSA_ERR_INVALID   # no room for scales
+    kb = lambda row, extra: B.DsaPaged(FAKE + (1 << 30), 64 * row + extra, row, 8192)
+    assert call_scores(prob(num_rows=0, **mx), kI=kb(128, 256)) == B.DSA_OK
+    assert call_scores(prob(num_rows=0, D_I=64, **mx), kI=kb(64, 128)) == B.DSA_OK
+    assert call_scores(prob(num_rows=0, **mx), kI=kb(144, 256)) == B.DSA_OK  # padded rows
+    assert call_scores(prob(**mx), kI=kb(128, 0)) == B.DSA_ERR_INVALID     # no room for scales
+    assert call_scores(prob(**mx), kI=kb(128, 240)) == B.DSA_ERR_INVALID   # too little room
     assert call_scores(prob(indexer_format=B.DSA_INDEXER_MXFP8)) == B.DSA_ERR_INVALID  # no qI_scale
     assert call_scores(prob(qI_scale=FAKE)) == B.DSA_ERR_INVALID             # E4M3 with scales
     assert call_scores(prob(indexer_format=2)) == B.DSA_ERR_INVALID          # unknown format

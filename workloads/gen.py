@@ -32,8 +32,9 @@ class Batch:
     row_pos: Optional[torch.Tensor]
     qI: torch.Tensor         # uint8 E4M3 [rows, H_I, D_I]
     w: torch.Tensor          # float32 [rows, H_I]
-    kI: torch.Tensor         # uint8 E4M3 [num_blocks, 64, D_I] (MXFP8: D_I + 16, the
-                             # row's D_I/32 E8M0 scales right after its codes)
+    kI: torch.Tensor         # uint8 E4M3 [num_blocks, 64, D_I] (MXFP8: [num_blocks, 66,
+                             # D_I], the 64 rows' D_I/32 E8M0 scales each, in row order,
+                             # in the last two D_I-byte rows of the block)
     q: torch.Tensor          # bfloat16 [rows, H_q, D_qk]
     kv: torch.Tensor         # bfloat16 [num_blocks, 64, D_qk]
     v: Optional[torch.Tensor] = None   # bfloat16 [num_blocks, 64, D_v] (separate V)
@@ -176,9 +177,9 @@ def make_batch(wl: Workload, device="cpu", seed=None, mode=None, table=None,
         qI, qI_scale = _mx_codes_scales((R, wl.H_I, wl.D_I), mode, gd, device)
         w = _weights((R, wl.H_I), mode, gd, device)
         k_codes, k_scales = _mx_codes_scales((num_blocks, BLOCK, wl.D_I), mode, gd, device)
-        kI = torch.zeros((num_blocks, BLOCK, wl.D_I + 16), dtype=torch.uint8, device=device)
-        kI[..., :wl.D_I] = k_codes
-        kI[..., wl.D_I:wl.D_I + wl.D_I // MX_GROUP] = k_scales
+        kI = torch.empty((num_blocks, BLOCK + 2, wl.D_I), dtype=torch.uint8, device=device)
+        kI[:, :BLOCK] = k_codes
+        kI[:, BLOCK:] = k_scales.reshape(num_blocks, 2, wl.D_I)
         del k_codes, k_scales
     else:
         qI = _fp8_codes((R, wl.H_I, wl.D_I), mode, gd, device)
@@ -241,8 +242,13 @@ def oracle_arrays(batch: Batch, rows=None) -> dict:
             bt[b, :nb] = np.arange(off, off + nb, dtype=np.int32)
             off += nb
     sel = torch.as_tensor(rows, dtype=torch.int64).to(batch.qI.device)
+    kI_scale = None
+    if batch.qI_scale is not None:  # MXFP8: split each block into code rows and row scales
+        kI_scale = np.ascontiguousarray(kI[:, BLOCK:]).reshape(kI.shape[0], BLOCK, -1)
+        kI = kI[:, :BLOCK]
     return {
         "qI_scale": None if batch.qI_scale is None else _np(batch.qI_scale.index_select(0, sel)),
+        "kI_scale_cache": kI_scale,
         "qI": _np(batch.qI.index_select(0, sel)),
         "w": _np(batch.w.index_select(0, sel)),
         "q": _np(batch.q.index_select(0, sel).view(torch.int16)).view(np.uint16),
