@@ -134,38 +134,78 @@ __device__ __forceinline__ int lane_prefix(uint64_t mask) {
 // the front end before these run.
 
 // ------------------------------------------------------ Top-K work area
-// Positions per group whose maximum key the Top-K pre-selects on, for a row
-// of L positions keeping K: the largest power of two up to kMaxGroup that
-// leaves at least 2K groups, or 1 (no grouping).  The fused indexer and the
-// Top-K kernels call the same function, so they agree on every row's
-// grouping.
-constexpr int kMaxGroup = 8;
-__host__ __device__ inline int topk_group(int L, int K) {
-  int g = 1;
-  while (g < kMaxGroup && (int64_t)L >= (int64_t)4 * K * g) g <<= 1;
-  return g;
+// The Top-K's pre-selection.  A row's positions are cut into segments of
+// kSumSeg (one indexer wave's span); the m = topk_sum_m(L) largest keys of
+// each segment form the row's summary, at most kSumMax keys.  The summary's
+// keys sit at distinct positions, so its K-th largest is a lower bound on
+// the row's K-th largest score; the segments' top keys hold nearly all of
+// the row's top K, so the bound is close.  With at least 128 segments
+// (topk_split_row) the summary holds at least 2048 >= K keys.  The fused
+// indexer and the standalone summary pass call the same functions, so they
+// agree on every row.
+constexpr int kSumSeg = 128;            // positions per segment
+constexpr int kSumMax = 4096;           // summary keys per row, at most
+constexpr int kSumCap = 16;             // keys per segment, at most
+__host__ __device__ inline int topk_sum_m(int L) {
+  const int nseg = (L + kSumSeg - 1) / kSumSeg;
+  if (nseg <= 0) return 0;
+  const int m = kSumMax / nseg;
+  return m < kSumCap ? m : kSumCap;
 }
-// Row stride (elements) of the group maxima: rows that group at all hold
-// at most ceil(max_len / 2) groups; a multiple of 4 for 16-byte loads.
-__host__ __device__ inline int64_t topk_gstride(int64_t max_len) {
-  return ((max_len + 1) / 2 + 3) & ~int64_t(3);
+constexpr int kTopkSlices = 16;         // workgroups per row, at most
+constexpr int kTopkSliceLen = 8192;     // positions per slice
+constexpr int kTopkSplitMaxK = 2048;
+// Rows that the Top-K spreads over slices (and that get a summary).
+__host__ __device__ inline bool topk_split_row(int L, int K) {
+  return K <= kTopkSplitMaxK && L >= 128 * kSumSeg && L <= kTopkSlices * kTopkSliceLen;
+}
+
+// Maximum of an unsigned value over the 64 lanes, in every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false));  // row_mirror
+  auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = max((uint32_t)p[0], (uint32_t)p[1]);
+  p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max((uint32_t)p[0], (uint32_t)p[1]);
+}
+
+// The m largest of the wave's 128 keys (two per lane), with multiplicity:
+// m rounds of a wave maximum, each taking out one instance (the lowest lane
+// that holds it).  Lane i < m returns the (i+1)-th largest.  m is
+// wave-uniform.
+__device__ __forceinline__ uint32_t segment_top(uint32_t ka, uint32_t kb, int m) {
+  const int lane = (int)(threadIdx.x & 63);
+  uint32_t mine = 0;
+  for (int i = 0; i < m; ++i) {
+    const uint32_t v = max(ka, kb);
+    const uint32_t M = wave_max_u32(v);
+    const uint64_t hit = __ballot(v == M);
+    if (lane == (int)__builtin_ctzll(hit)) {
+      if (ka == M)
+        ka = 0u;
+      else
+        kb = 0u;
+    }
+    mine = lane == i ? M : mine;
+  }
+  return mine;
 }
 
 // The Top-K's work area, carved from the caller's workspace:
-//  - gmax [rows][gstride]: the maximum key of every group of every row (rows
-//    with G = 1 leave theirs unused);
+//  - summ [rows][kSumMax]: each row's summary (segment s's keys at
+//    s * m .. s * m + m - 1);
 //  - ckey, cpos [rows][cstride]: the candidate keys and positions that the
 //    workgroups of a row's slices hand to the one that finishes the row
-//    (slice j's entries start at j * kTopkSliceGroups * G);
+//    (slice j's entries start at j * kTopkSliceLen);
 //  - ccount [rows][kTopkSlices]: how many candidates each slice left;
 //  - arrive [rows]: slices of the row done so far.  Whichever kernel writes
-//    gmax for a call (the fused indexer, or the standalone group-maximum
+//    the summary for a call (the fused indexer, or the standalone summary
 //    pass) zeroes it first.
-constexpr int kTopkSlices = 16;         // workgroups per row, at most
-constexpr int kTopkSliceGroups = 1024;  // groups per slice (one per thread)
 struct TopkWork {
-  uint32_t* gmax;
-  int64_t gstride;
+  uint32_t* summ;
   uint32_t* ckey;
   int32_t* cpos;
   int64_t cstride;
@@ -189,8 +229,8 @@ struct IndexerLaunch {
   int32_t H_I, D_I;
   int32_t row_begin, num_rows;  // rows [row_begin, row_begin + num_rows)
   int32_t max_len;              // upper bound of any row's history length
-  TopkWork tw;                  // group maxima for a Top-K of topk_K that follows,
-  int32_t topk_K;               // or nothing when tw.gmax is NULL
+  TopkWork tw;                  // summaries for a Top-K of topk_K that follows,
+  int32_t topk_K;               // or nothing when tw.summ is NULL
 };
 hipError_t launch_indexer_scores(const IndexerLaunch& a, hipStream_t s);
 
@@ -205,7 +245,7 @@ struct TopkLaunch {
   int32_t row_begin, num_rows;
   int32_t max_len;
   TopkWork tw;
-  bool prep;            // compute the group maxima here (no fused indexer before)
+  bool prep;            // compute the summaries here (no fused indexer before)
   bool vec;             // every score row is 16-byte aligned (ld % 4 == 0)
   // Optional: also write each kept position's byte offset in the paged KV
   // cache `kv` (block table -> physical block), -1 for padding and for

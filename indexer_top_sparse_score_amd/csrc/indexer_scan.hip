@@ -65,15 +65,6 @@ __device__ __forceinline__ v4f mfma_scaled(v8i a, v8i b, int scale_a, int scale_
                                                           kSelA, scale_a, 0, scale_b);
 }
 
-// Maximum over aligned groups of G lanes (G = 1, 2, 4 or 8, wave-uniform)
-// with DPP moves: swap neighbours, swap pairs, mirror each half-row.
-__device__ __forceinline__ uint32_t max_lanes(uint32_t k, int G) {
-  if (G >= 2) k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0xB1, 0xF, 0xF, false));
-  if (G >= 4) k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x4E, 0xF, 0xF, false));
-  if (G >= 8) k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x141, 0xF, 0xF, false));
-  return k;
-}
-
 // NKP = D_I / 64 pieces per lane; HT = 16-head tiles (ceil(H_I / 16)); MX:
 // MXFP8 operands (one E8M0 scale per 32 dims of every query head and key
 // row, Day0 section 5.1; a key block's 64 rows of scales follow its 64 code
@@ -102,7 +93,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
   constexpr int kNG = 2 * NKP;                 // 32-dim groups of a row (MX)
   __shared__ uint32_t qs_lds[MX ? 64 * kNG : 1];  // query scales, one per word
   __shared__ float sc_lds[kWaves][kSpan];
-  __shared__ uint32_t gm_lds[kWaves][kSpan / 2];
 
   // Load order matters (vector loads complete in issue order): one round
   // trip fetches the row's length, the tile's block ids and the row's query
@@ -216,15 +206,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     if (MX && g < kNG)
       qscale = (qscale & ~(0xFF << (8 * ht))) | ((int)qs_lds[(16 * ht + col) * kNG + g] << (8 * ht));
   }
-  // Group maxima for the Top-K that follows: groups of G positions, G <= 8
-  // a power of two, so a group never straddles a 16-position sub-tile
-  const int G = a.tw.gmax && L > a.topk_K ? topk_group(L, a.topk_K) : 1;
-  const int lgG = __builtin_ctz(G);
-  // The wave's scores and group maxima are collected in LDS and written
-  // with a few full-width stores at the end, not one narrow store per
-  // sub-tile.
+  // The wave's scores are collected in LDS and written with a few
+  // full-width stores at the end, not one narrow store per sub-tile.
   float* my_sc = sc_lds[wave];
-  uint32_t* my_gm = gm_lds[wave];
 
   bool bad_page = false;
 #pragma unroll
@@ -254,11 +238,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     // canonical +0 for a zero score; an absent page scores -inf
     const float v = page_ok[j] ? part + 0.0f : -__builtin_inff();
     if (g == 0) my_sc[j * kSub + col] = v;
-    if (G > 1) {  // wave-uniform
-      const int s = w0 + j * kSub + col;
-      const uint32_t k = max_lanes(s < L ? score_key(v) : 0u, G);
-      if (g == 0 && (col & (G - 1)) == 0) my_gm[(j * kSub + col) >> lgG] = k;
-    }
     bad_page = bad_page || (w0 + j * kSub < L && !page_ok[j]);
   }
   // LDS accesses of one wave complete in order; the fence keeps the
@@ -270,9 +249,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     const int i = 64 * h + lane;
     if (w0 + i < L) out[w0 + i] = my_sc[i];
   }
-  if (G > 1 && lane < (kSpan >> lgG) && w0 + (lane << lgG) < L) {
-    uint32_t* gmax = a.tw.gmax + (int64_t)(r - a.row_begin) * a.tw.gstride;
-    gmax[(w0 >> lgG) + lane] = my_gm[lane];
+  // The Top-K's summary of this wave's segment (its m largest keys; the
+  // wave spans exactly one segment)
+  static_assert(kSpan == kSumSeg, "one summary segment per wave");
+  if (a.tw.summ && w0 < L && topk_split_row(L, a.topk_K)) {  // wave-uniform
+    const uint32_t ka = w0 + lane < L ? score_key(my_sc[lane]) : 0u;
+    const uint32_t kb = w0 + 64 + lane < L ? score_key(my_sc[64 + lane]) : 0u;
+    const int m = topk_sum_m(L);
+    const uint32_t mine = segment_top(ka, kb, m);
+    if (lane < m)
+      a.tw.summ[(int64_t)(r - a.row_begin) * kSumMax + (w0 / kSumSeg) * m + lane] = mine;
   }
   if (bad_page && lane == 0) report(a.err, DSA_DEVERR_BLOCK);
 }

@@ -6,21 +6,20 @@
 // the kept positions are written in ascending order, -1 pads to K.
 //
 // Scores are compared through an order-preserving 32-bit key (score_key);
-// the selection is exact.  A row's history is cut into groups of G
-// consecutive positions (topk_group: a power of two up to 8 that leaves at
-// least 2K groups), and the maximum key of every group is known before this
-// kernel runs -- the fused indexer writes it in its epilogue; the standalone
-// entry point runs topk_group_max_kernel first.
+// the selection is exact.  Rows of 16384 to 131072 positions (K <= 2048,
+// topk_split_row) are spread over up to 16 workgroups, one per slice of 8192
+// positions, and pre-select on the row's summary: the m largest keys of each
+// 128-position segment (topk_sum_m), written by the fused indexer's epilogue
+// or, for the standalone entry point, by topk_summary_kernel.
 //
-//  1. A lower bound t on the row's K-th largest key T: one 2048-bin histogram
-//     of the group maxima over their range, and t = the lower edge of the bin
-//     that holds the K-th largest maximum.  At least K groups have a maximum
-//     >= t, so at least K keys are >= t and T >= t; every kept position lies
-//     in a group whose maximum is >= t (a candidate group).  Without heavy
-//     ties there are about K candidate groups holding some 1.1-1.4 K keys
-//     >= t.
-//  2. The candidate groups' keys are loaded and those >= t are compacted, in
-//     position order, into LDS with their positions.
+//  1. A lower bound t on the row's K-th largest key T: the summary's keys
+//     sit at distinct positions, so its own K-th largest is at most T.  One
+//     2048-bin histogram of the summary over its range gives t = the lower
+//     edge of the bin that holds its K-th largest key.  The segments' top
+//     keys hold nearly every one of the row's top K, so t is close to T:
+//     about 1.04 K keys are >= t.
+//  2. Each slice compacts its keys >= t, in position order, into its
+//     segment of the work area; the last slice to finish reads them all.
 //  3. T is selected exactly among them, together with the number of keys
 //     equal to T that are kept (the first ones in position order).
 //  4. The kept positions are written in ascending order: block-wide prefix
@@ -28,11 +27,11 @@
 //     coalesced pass (with the KV row offsets, from a copy of the row's block
 //     table in LDS).
 //
-// With G = 1 the keys themselves are loaded and step 3 runs on them
-// directly.  Rows with L <= K keep every position.  A row that does not fit
-// these buffers (K > 2048, more than 16384 groups, more than 4096 candidate
-// groups or 8192 keys >= t because of ties, or t = 0 because of NaN scores)
-// runs the same selection over its keys streamed from memory.
+// Rows of at most 16384 positions run steps 3-4 on their keys in one
+// workgroup; rows with L <= K keep every position.  A row that does not fit
+// these buffers (K > 2048, more than 8192 keys >= t or more than a slice's
+// share of them because of ties, or t = 0 because of NaN scores) runs the
+// same selection over its keys streamed from memory.
 //
 // Selection (select_kth): histograms of 2048 bins laid over the current key
 // range [lo, hi] narrow the range to the bin that holds the wanted rank,
@@ -50,28 +49,25 @@ constexpr int kWaves = kT / 64;           // 16
 constexpr int kBinBits = 11;
 constexpr int kBins = 1 << kBinBits;      // 2048
 constexpr int kSmall = 64;                // bin size ranked directly by one wave
-constexpr int kPerThread = 16;            // group maxima (or keys) per thread
+constexpr int kPerThread = 16;            // keys per thread of a one-workgroup row
 constexpr int kMaxN = kPerThread * kT;    // 16384
-constexpr int kCandPer = 4;               // candidate groups per thread
-constexpr int kMaxCand = kCandPer * kT;   // 4096
-constexpr int kKeysPer = 8;               // compacted keys per thread
+constexpr int kKeysPer = 8;               // a slice's keys (and compacted keys) per thread
 constexpr int kMaxKeys = kKeysPer * kT;   // 8192
+constexpr int kSumPer = kSumMax / kT;     // summary keys per thread (4)
+static_assert(kKeysPer * kT == kTopkSliceLen, "a slice is one key run per thread");
+static_assert(kTopkSplitMaxK <= kBins, "split rows select within one staged pass");
 constexpr int kBtCache = 2048;            // block-table entries cached in LDS
 constexpr int kScanWords = 4 * kWaves + 1;
-constexpr int kSegRead = kT / kTopkSlices;  // threads reading one slice's candidates (64)
-static_assert(kSegRead * kKeysPer * kTopkSlices == kMaxKeys, "slice-major candidate layout");
 static_assert(kBins == 2 * kT, "find_bin gives each thread two bins");
 
 struct Smem {
   uint32_t hist[kBins];    // histograms; afterwards slot -> kept position
-  uint32_t list[kMaxCand]; // candidate group ids, in position order
-  uint32_t ck[kMaxKeys];   // compacted keys >= t, in position order
-  int32_t cp[kMaxKeys];    // and their positions
+  int32_t cp[kMaxKeys];    // a slice's compacted positions (for the KV prefetch)
   int32_t bt[kBtCache];    // the row's block table (rows of <= 2048 blocks)
   uint32_t buf[kSmall];
   uint32_t res[4];
-  uint32_t wsum[kScanWords];
-  uint32_t red[2 * kWaves];
+  alignas(16) uint32_t wsum[kScanWords];
+  alignas(16) uint32_t red[3 * kWaves];
 };
 
 __device__ __forceinline__ int bitlen32(uint32_t x) { return x ? 32 - __clz(x) : 0; }
@@ -101,25 +97,37 @@ struct Add { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { retu
 struct Min { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); } };
 struct Max { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); } };
 
+// Sum of the 16 words at w (16-byte aligned) before index `upto`, and of
+// all of them: four broadcast reads.
+__device__ __forceinline__ uint32_t sum_words(const uint32_t* w, int upto, uint32_t& all) {
+  const uint4* w4 = reinterpret_cast<const uint4*>(w);
+  uint32_t before = 0;
+  all = 0;
+#pragma unroll
+  for (int v = 0; v < kWaves / 4; ++v) {
+    const uint4 q = w4[v];
+    const int i = 4 * v;
+    all += (q.x + q.y) + (q.z + q.w);
+    before += (i < upto ? q.x : 0u) + (i + 1 < upto ? q.y : 0u) + (i + 2 < upto ? q.z : 0u) +
+              (i + 3 < upto ? q.w : 0u);
+  }
+  return before;
+}
+
 // Exclusive prefix sum over the block in thread order; `tot` receives the
-// total.  Starts and ends with a barrier, so `wsum` may be reused at once.
+// total.  Each wave's total goes to LDS and, after one barrier, every wave
+// adds up those before it.  kFree: a second barrier at the end, so `wsum`
+// may be rewritten at once; without it the caller must pass a barrier
+// before `wsum` is written again.
+template <bool kFree = true>
 __device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t* wsum, uint32_t& tot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t inc = wave_scan(x, 0u, Add());
-  __syncthreads();
   if (lane == 63) wsum[wave] = inc;
   __syncthreads();
-  if (wave == 0) {
-    const uint32_t v = lane < kWaves ? wsum[lane] : 0u;
-    const uint32_t c = wave_scan(v, 0u, Add());
-    if (lane < kWaves) wsum[lane] = c - v;
-    if (lane == 63) wsum[kWaves] = c;
-  }
-  __syncthreads();
-  const uint32_t ex = wsum[wave] + inc - x;
-  tot = wsum[kWaves];
-  __syncthreads();
-  return ex;
+  const uint32_t before = sum_words(wsum, wave, tot);
+  if (kFree) __syncthreads();
+  return before + inc - x;
 }
 
 // Exclusive prefix sums of N sequences of one value per thread, taken one
@@ -154,40 +162,50 @@ __device__ __forceinline__ uint32_t block_scan_n(const uint32_t (&x)[N], uint32_
   return total;
 }
 
-// Min and max over the block (results in every thread).
-__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_t* red) {
+// Min, max and sum over the block (results in every thread).  One barrier;
+// `red` (3 x 16 words) must not be in use.
+__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_t& sum,
+                                             uint32_t* red) {
   mn = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan(mn, 0xFFFFFFFFu, Min()), 63);
   mx = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan(mx, 0u, Max()), 63);
+  sum = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan(sum, 0u, Add()), 63);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
   if (lane == 0) {
     red[wave] = mn;
     red[kWaves + wave] = mx;
+    red[2 * kWaves + wave] = sum;
   }
   __syncthreads();
+  const uint4* r4 = reinterpret_cast<const uint4*>(red);
+  sum = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    mn = min(mn, red[w]);
-    mx = max(mx, red[kWaves + w]);
+  for (int v = 0; v < kWaves / 4; ++v) {
+    const uint4 a = r4[v], b = r4[kWaves / 4 + v], c = r4[kWaves / 2 + v];
+    mn = min(min(min(mn, a.x), min(a.y, a.z)), a.w);
+    mx = max(max(max(mx, b.x), max(b.y, b.z)), b.w);
+    sum += (c.x + c.y) + (c.z + c.w);
   }
 }
 
 // Over the 2048-bin histogram h, the bin b with above(b) < need <=
 // above(b) + h[b], where above(b) counts the keys in bins above b; thread t
-// owns bins 2047 - 2t and 2046 - 2t.  Results: res[0] = b, res[1] = above(b).
-// Requires 1 <= need <= sum of h.  Ends with a barrier.
+// owns bins 2047 - 2t and 2046 - 2t.  Results: res[0] = b, res[1] = above(b);
+// res[2] is cleared (select_kth counts with it).  Requires 1 <= need <= sum
+// of h.  Two barriers, the last at the end.
 __device__ __forceinline__ void find_bin(const uint32_t* h, uint32_t need, uint32_t* res,
                                          uint32_t* wsum) {
   const int top = kBins - 1 - 2 * (int)threadIdx.x;
   const uint32_t c0 = h[top], c1 = h[top - 1];
   uint32_t tot;
-  const uint32_t above = block_scan(c0 + c1, wsum, tot);
+  const uint32_t above = block_scan<false>(c0 + c1, wsum, tot);
   if (above < need && need <= above + c0) {
     res[0] = (uint32_t)top;
     res[1] = above;
+    res[2] = 0;
   } else if (above + c0 < need && need <= above + c0 + c1) {
     res[0] = (uint32_t)(top - 1);
     res[1] = above + c0;
+    res[2] = 0;
   }
   __syncthreads();
 }
@@ -240,11 +258,10 @@ __device__ __forceinline__ uint32_t select_kth(Visit&& visit, uint32_t lo, uint3
     const uint32_t span = (1u << shift) - 1u;
     hi = (hi - nlo <= span) ? hi : nlo + span;
     lo = nlo;
-    __syncthreads();  // hist and res are rewritten below
     if (lo < hi && cnt <= (uint32_t)kSmall) {
-      // rank the bin's keys directly: wave 0, one key per lane
-      if (tid == 0) s.res[2] = 0;
-      __syncthreads();
+      // rank the bin's keys directly: wave 0, one key per lane.  find_bin
+      // cleared the counter res[2]; res[0..1] are rewritten only after the
+      // next barrier, which every thread reaches after reading them.
       visit([&](uint32_t k) {
         if (k >= lo && k <= hi) s.buf[atomicAdd(&s.res[2], 1u)] = k;
       });
@@ -269,6 +286,7 @@ __device__ __forceinline__ uint32_t select_kth(Visit&& visit, uint32_t lo, uint3
       __syncthreads();
       return T;
     }
+    __syncthreads();  // the next pass rewrites hist and res
   }
   return lo;
 }
@@ -351,8 +369,9 @@ __device__ __forceinline__ void load_keys(const float* sc, int i0, int L, bool v
 // Emits one run of N entries per thread (threads in order, entry j of a
 // thread at position pos(j)), masked to the first `n`, given T and the
 // budget of keys equal to T.  `eq_before` / `out_before` carry the counts of
-// earlier runs and are advanced past this one.
-template <int N, bool kStaged, class Pos>
+// earlier runs and are advanced past this one.  kLast: no other emission
+// follows before a barrier (its scan then skips the trailing one).
+template <int N, bool kStaged, bool kLast = false, class Pos>
 __device__ __forceinline__ void emit_runs(const uint32_t (&k)[N], int n, Pos&& pos, uint32_t T,
                                           uint32_t need_eq, uint32_t& eq_before,
                                           uint32_t& out_before, const Out& o, Smem& s) {
@@ -365,7 +384,7 @@ __device__ __forceinline__ void emit_runs(const uint32_t (&k)[N], int n, Pos&& p
   // one scan for both counts (a run holds at most 16384 entries, so each
   // half of the packed word stays below 2^16)
   uint32_t tot;
-  const uint32_t ex = block_scan((eq << 16) | gt, s.wsum, tot);
+  const uint32_t ex = block_scan<!kLast>((eq << 16) | gt, s.wsum, tot);
   const uint32_t eqx = eq_before + (ex >> 16);  // equal keys before this thread
   // kept so far: every larger key, and equal keys up to the budget
   const uint32_t slot0 = out_before + (ex & 0xFFFFu) + min(eqx, need_eq) - min(eq_before, need_eq);
@@ -413,166 +432,33 @@ __device__ __forceinline__ void select_streamed(const float* sc, int L, int K, b
   }
 }
 
-// Steps 2-4 for groups of G positions.  The candidate groups' keys are
-// loaded in pieces of P = G/4 (at least 1) float4 or float2 loads, lane-
-// adjacent within a group so that one cache line serves its pieces: piece q
-// of list entry e is taken by thread (e P + q) mod 1024 in round
-// (e P + q) / 1024.  The keys >= t are compacted in (round, thread) order,
-// which is position order.  Returns false, having written nothing, when
-// more than kMaxKeys keys are >= t.
-template <int G>
-__device__ __forceinline__ bool select_groups(const float* sc, int L, int K, uint32_t t,
-                                              uint32_t kmax, uint32_t n_cg, bool vec,
-                                              const Out& o, Smem& s) {
-  constexpr int W = G < 4 ? G : 4;      // keys per piece
-  constexpr int P = G / W;              // pieces per group
-  constexpr int R = kCandPer * P;       // rounds (pieces per thread)
-  const int tid = threadIdx.x;
-  uint32_t n_c;
-  {
-    int base[R];  // first position of the piece, L: none
-#pragma unroll
-    for (int m = 0; m < R; ++m) {
-      const uint32_t q = (uint32_t)(m * kT + tid);
-      const uint32_t e = q / P;
-      base[m] = e < n_cg ? (int)s.list[e] * G + (int)(q % P) * W : L;
-    }
-    uint32_t k[R][W];
-#pragma unroll
-    for (int m = 0; m < R; ++m) load_keys<W>(sc, base[m], L, vec, k[m]);
-    uint32_t c[R], at[R];
-#pragma unroll
-    for (int m = 0; m < R; ++m) {
-      c[m] = 0;
-#pragma unroll
-      for (int j = 0; j < W; ++j) c[m] += k[m][j] >= t ? 1u : 0u;  // t >= 1: absent keys never count
-    }
-    static_assert(R <= 8, "rounds");
-    if constexpr (R <= 4) {
-      n_c = block_scan_n<R>(c, at, s.wsum);
-    } else {  // two scans of four rounds
-      uint32_t c0[4], c1[4], a0[4], a1[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        c0[m] = c[m];
-        c1[m] = c[m + 4];
-      }
-      const uint32_t n0 = block_scan_n<4>(c0, a0, s.wsum);
-      n_c = n0 + block_scan_n<4>(c1, a1, s.wsum);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        at[m] = a0[m];
-        at[m + 4] = n0 + a1[m];
-      }
-    }
-    if (n_c > (uint32_t)kMaxKeys) return false;
-#pragma unroll
-    for (int m = 0; m < R; ++m)
-#pragma unroll
-      for (int j = 0; j < W; ++j)
-        if (k[m][j] >= t) {
-          s.ck[at[m]] = k[m][j];
-          s.cp[at[m]] = base[m] + j;
-          ++at[m];
-        }
-  }
-  __syncthreads();
-  const int c0 = kKeysPer * tid;
-  const int n = max(0, min(kKeysPer, (int)n_c - c0));
-  uint32_t k[kKeysPer];
-#pragma unroll
-  for (int j = 0; j < kKeysPer; ++j) k[j] = j < n ? s.ck[c0 + j] : 0u;
-  auto visit = [&](auto f) {
-#pragma unroll
-    for (int j = 0; j < kKeysPer; ++j)
-      if (j < n) f(k[j]);
-  };
-  uint32_t need = (uint32_t)K;
-  const uint32_t T = select_kth(visit, t, kmax, need, s);
-  uint32_t eq_before = 0, out_before = 0;
-  emit_runs<kKeysPer, true>(k, n, [&](int j) { return s.cp[c0 + j]; }, T, need, eq_before,
-                            out_before, o, s);
-  return true;
-}
-
-// Steps 1-4.  `gm` holds the thread's group maxima 16t .. 16t+15 (loaded
-// before the row was resolved).  Returns false, having written nothing, when
-// the row needs the streamed path.
-__device__ __forceinline__ bool select_fast(const float* sc, int L, int K, bool vec,
-                                            uint32_t (&gm)[kPerThread], const Out& o, Smem& s) {
-  const int tid = threadIdx.x;
-  const int G = topk_group(L, K);
-  const int N = (L + G - 1) / G;
-  if (N > kMaxN) return false;
-  const int g0 = kPerThread * tid;
-  if (G == 1) load_keys<kPerThread>(sc, g0, L, vec, gm);
-  const int n_mine = max(0, min(kPerThread, N - g0));
+// Steps 3-4 on the row's keys themselves, 16 per thread (rows of at most
+// kMaxN positions).
+__device__ __forceinline__ void select_keys(const float* sc, int L, int K, bool vec, const Out& o,
+                                            Smem& s) {
+  const int g0 = kPerThread * (int)threadIdx.x;
+  uint32_t k[kPerThread];
+  load_keys<kPerThread>(sc, g0, L, vec, k);
+  const int n_mine = max(0, min(kPerThread, L - g0));
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j)
     if (j < n_mine) {
-      kmin = min(kmin, gm[j]);
-      kmax = max(kmax, gm[j]);
+      kmin = min(kmin, k[j]);
+      kmax = max(kmax, k[j]);
     }
-  block_minmax(kmin, kmax, s.red);
+  uint32_t unused = 0;
+  block_minmax(kmin, kmax, unused, s.red);
   auto visit = [&](auto f) {
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j)
-      if (j < n_mine) f(gm[j]);
+      if (j < n_mine) f(k[j]);
   };
-
-  if (G == 1) {  // the keys themselves: select T and emit
-    uint32_t need = (uint32_t)K;
-    const uint32_t T = select_kth(visit, kmin, kmax, need, s);
-    uint32_t eq_before = 0, out_before = 0;
-    emit_runs<kPerThread, true>(gm, n_mine, [&](int j) { return g0 + j; }, T, need, eq_before,
-                                out_before, o, s);
-    return true;
-  }
-
-  // 1. t = lower edge of the bin holding the K-th largest group maximum
-  uint32_t t = kmin;
-  if (kmin < kmax) {
-    const int shift = range_shift(kmin, kmax);
-    histogram_bin(visit, kmin, kmax, shift, (uint32_t)K, s);
-    t = kmin + (s.res[0] << shift);
-  }
-  // candidate groups: maxima >= t, listed in position order
-  uint32_t c = 0;
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j) c += (j < n_mine && gm[j] >= t) ? 1u : 0u;
-  uint32_t n_cg;
-  uint32_t at = block_scan(c, s.wsum, n_cg);
-  // heavy ties at t, or t = 0 (NaN scores at the threshold)
-  if (n_cg > (uint32_t)kMaxCand || t == 0) return false;
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j)
-    if (j < n_mine && gm[j] >= t) s.list[at++] = (uint32_t)(g0 + j);
-  __syncthreads();
-  switch (G) {
-    case 2: return select_groups<2>(sc, L, K, t, kmax, n_cg, vec, o, s);
-    case 4: return select_groups<4>(sc, L, K, t, kmax, n_cg, vec, o, s);
-    default: return select_groups<kMaxGroup>(sc, L, K, t, kmax, n_cg, vec, o, s);
-  }
-}
-
-// This thread's share of a row's group maxima, 16t .. 16t+15, whatever the
-// row's length turns out to be.  The loads are unconditional 16-byte ones
-// (no branch, so nothing waits for them before they are used): the work
-// area is padded so that kMaxN entries from any row's start are readable;
-// entries past the row's groups hold other rows' or padding values and are
-// never used.
-__device__ __forceinline__ void load_gmax(const TopkLaunch& a, int r_local,
-                                          uint32_t (&gm)[kPerThread]) {
-  const uint32_t* src = a.tw.gmax + (int64_t)r_local * a.tw.gstride + kPerThread * threadIdx.x;
-#pragma unroll
-  for (int j = 0; j < kPerThread; j += 4) {
-    const uint4 v = *reinterpret_cast<const uint4*>(src + j);
-    gm[j] = v.x;
-    gm[j + 1] = v.y;
-    gm[j + 2] = v.z;
-    gm[j + 3] = v.w;
-  }
+  uint32_t need = (uint32_t)K;
+  const uint32_t T = select_kth(visit, kmin, kmax, need, s);
+  uint32_t eq_before = 0, out_before = 0;
+  emit_runs<kPerThread, true, true>(k, n_mine, [&](int j) { return g0 + j; }, T, need, eq_before,
+                                    out_before, o, s);
 }
 
 __device__ __forceinline__ Out make_out(const TopkLaunch& a, int r_local, int b) {
@@ -600,8 +486,8 @@ __device__ __forceinline__ void cache_block_table(int L, Out& o, Smem& s) {
 }
 
 // A whole row in one workgroup: every path but the split one.
-__device__ __forceinline__ void row_single(const TopkLaunch& a, int r_local, int L,
-                                           uint32_t (&gm)[kPerThread], Out& o, Smem& s) {
+__device__ __forceinline__ void row_single(const TopkLaunch& a, int r_local, int L, Out& o,
+                                           Smem& s) {
   const int tid = threadIdx.x;
   const int K = a.K;
   if (tid == 0 && a.counts) a.counts[r_local] = min(K, L);
@@ -623,16 +509,18 @@ __device__ __forceinline__ void row_single(const TopkLaunch& a, int r_local, int
   }
   cache_block_table(L, o, s);
   o.pos = s.hist;
-  if (!(K <= kMaxCand - kT && select_fast(sc, L, K, a.vec, gm, o, s)))
+  if (L <= kMaxN)
+    select_keys(sc, L, K, a.vec, o, s);
+  else
     select_streamed<true>(sc, L, K, a.vec, o, s);
   __syncthreads();
   o.flush(K);
 }
 
 // ---------------------------------------------------------- split rows
-// A row whose group maxima are known is spread over up to kTopkSlices
-// workgroups, one per slice of kTopkSliceGroups groups:
-//  a. every workgroup computes t from all the row's group maxima (the same
+// A split row (topk_split_row) is spread over up to kTopkSlices workgroups,
+// one per slice of kTopkSliceLen positions:
+//  a. every workgroup computes t from the row's whole summary (the same
 //     integer arithmetic on the same data, so the same t everywhere);
 //  b. each keeps its slice's keys >= t and writes them, with their
 //     positions and in position order, to its segment of the work area;
@@ -676,17 +564,14 @@ __device__ __forceinline__ void store_shared(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The G scores of group g as raw bits (positions past L as 0); converted to
-// keys only once they are needed, so nothing waits for them earlier.
-template <int G>
-__device__ __forceinline__ void group_scores(const float* sc, int g, int L, bool vec,
-                                             uint32_t (&x)[kMaxGroup]) {
-  const int i0 = g * G;
+// The kKeysPer scores from position i0 as raw bits (positions past L as 0);
+// converted to keys only once they are needed, so nothing waits for them
+// earlier.
+__device__ __forceinline__ void run_scores(const float* sc, int i0, int L, bool vec,
+                                           uint32_t (&x)[kKeysPer]) {
+  if (vec && i0 + kKeysPer <= L) {
 #pragma unroll
-  for (int j = 0; j < kMaxGroup; ++j) x[j] = 0u;
-  if (vec && G >= 4 && i0 + G <= L) {
-#pragma unroll
-    for (int j = 0; j < G; j += 4) {
+    for (int j = 0; j < kKeysPer; j += 4) {
       const uint4 v = *reinterpret_cast<const uint4*>(sc + i0 + j);
       x[j] = v.x;
       x[j + 1] = v.y;
@@ -695,7 +580,7 @@ __device__ __forceinline__ void group_scores(const float* sc, int g, int L, bool
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < G; ++j) x[j] = i0 + j < L ? __float_as_uint(sc[i0 + j]) : 0u;
+    for (int j = 0; j < kKeysPer; ++j) x[j] = i0 + j < L ? __float_as_uint(sc[i0 + j]) : 0u;
   }
 }
 
@@ -705,31 +590,29 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
   const int slice = (int)blockIdx.x;
   const int r_local = (int)blockIdx.y;
   const int K = a.K;
-  // one round trip: the row's length, then its group maxima
+  // one round trip: the row's length, its summary (kSumPer keys per thread,
+  // unconditional 16-byte loads: the summary area holds kSumMax per row)
   const RowIssue ri = row_issue(a.rows, a.row_begin + r_local);
-  uint32_t gm[kPerThread];
-  load_gmax(a, r_local, gm);
+  uint32_t sm[kSumPer];
+  {
+    const uint4 v =
+        *reinterpret_cast<const uint4*>(a.tw.summ + (int64_t)r_local * kSumMax + kSumPer * tid);
+    sm[0] = v.x; sm[1] = v.y; sm[2] = v.z; sm[3] = v.w;
+  }
   const int L = row_finish(a.rows, ri);
   Out o = make_out(a, r_local, ri.b_ok ? ri.b : 0);
-  const int G = L > 0 ? topk_group(L, K) : 1;
-  const int N = (L + G - 1) / G;
-  if (!(L > K && G > 1 && K <= kBins && K <= kMaxCand - kT && N <= kMaxN)) {
-    if (slice == 0) row_single(a, r_local, L, gm, o, s);
+  if (!topk_split_row(L, K)) {
+    if (slice == 0) row_single(a, r_local, L, o, s);
     return;
   }
-  const int S = (N + kTopkSliceGroups - 1) / kTopkSliceGroups;
+  const int S = (L + kTopkSliceLen - 1) / kTopkSliceLen;
   if (slice >= S) return;
 
-  // this thread's group of the slice: its keys, loaded now, used after t
+  // this thread's run of the slice: its scores, loaded now, used after t
   const float* sc = a.scores + (int64_t)r_local * a.ld;
-  const int g = slice * kTopkSliceGroups + tid;
-  uint32_t k[kMaxGroup];
-  switch (G) {
-    case 2: group_scores<2>(sc, g, L, a.vec, k); break;
-    case 4: group_scores<4>(sc, g, L, a.vec, k); break;
-    default: group_scores<kMaxGroup>(sc, g, L, a.vec, k); break;
-  }
-  const int n_valid = max(0, min(G, L - g * G));
+  const int p0 = slice * kTopkSliceLen + kKeysPer * tid;
+  uint32_t k[kKeysPer];
+  run_scores(sc, p0, L, a.vec, k);
   for (int i = tid; i < kBins; i += kT) s.hist[i] = 0;  // for step a; block_minmax syncs
   if (slice == 0 && tid == 0 && a.counts) a.counts[r_local] = K;
   // the row's block ids for the KV row offsets: loaded now, staged in LDS
@@ -744,27 +627,33 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
     btv[j] = bt_cached && i < nblk ? o.bt[i] : 0;
   }
 
-  // a. t = lower edge of the bin holding the K-th largest group maximum
-  const int g0 = kPerThread * tid;
-  const int n_mine = max(0, min(kPerThread, N - g0));
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  // a. t = lower edge of the bin holding the summary's K-th largest key
+  //    (key 0, NaN or no position, does not count)
+  const int n_sum = ((L + kSumSeg - 1) / kSumSeg) * topk_sum_m(L);
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, n_nz = 0;
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j)
-    if (j < n_mine) {
-      kmin = min(kmin, gm[j]);
-      kmax = max(kmax, gm[j]);
+  for (int j = 0; j < kSumPer; ++j) {
+    sm[j] = kSumPer * tid + j < n_sum ? sm[j] : 0u;
+    if (sm[j] != 0u) {
+      kmin = min(kmin, sm[j]);
+      kmax = max(kmax, sm[j]);
+      ++n_nz;
     }
-  block_minmax(kmin, kmax, s.red);
-  uint32_t t = kmin;
-  if (kmin < kmax) {
-    auto visit = [&](auto f) {
+  }
+  block_minmax(kmin, kmax, n_nz, s.red);
+  uint32_t t = 0;
+  if (n_nz >= (uint32_t)K) {  // else too few keys for a bound (NaN): t = 0
+    t = kmin;
+    if (kmin < kmax) {
+      auto visit = [&](auto f) {
 #pragma unroll
-      for (int j = 0; j < kPerThread; ++j)
-        if (j < n_mine) f(gm[j]);
-    };
-    const int shift = range_shift(kmin, kmax);
-    histogram_bin<true>(visit, kmin, kmax, shift, (uint32_t)K, s);
-    t = kmin + (s.res[0] << shift);
+        for (int j = 0; j < kSumPer; ++j)
+          if (sm[j] != 0u) f(sm[j]);
+      };
+      const int shift = range_shift(kmin, kmax);
+      histogram_bin<true>(visit, kmin, kmax, shift, (uint32_t)K, s);
+      t = kmin + (s.res[0] << shift);
+    }
   }
   o.pos = s.hist;
   if (t == 0) {  // NaN scores at the threshold: the general path, once
@@ -779,20 +668,20 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
 
   // b. this slice's keys >= t (t >= 1: positions past L, key 0, never count)
 #pragma unroll
-  for (int j = 0; j < kMaxGroup; ++j) k[j] = j < n_valid ? score_key(__uint_as_float(k[j])) : 0u;
+  for (int j = 0; j < kKeysPer; ++j) k[j] = p0 + j < L ? score_key(__uint_as_float(k[j])) : 0u;
   uint32_t c = 0;
 #pragma unroll
-  for (int j = 0; j < kMaxGroup; ++j) c += (j < G && k[j] >= t) ? 1u : 0u;
+  for (int j = 0; j < kKeysPer; ++j) c += k[j] >= t ? 1u : 0u;
   uint32_t n_slice;
-  uint32_t at = block_scan(c, s.wsum, n_slice);
+  uint32_t at = block_scan<false>(c, s.wsum, n_slice);  // the hand-over's barriers follow
   {
-    const int64_t seg = (int64_t)r_local * a.tw.cstride + (int64_t)slice * kTopkSliceGroups * G;
+    const int64_t seg = (int64_t)r_local * a.tw.cstride + (int64_t)slice * kTopkSliceLen;
 #pragma unroll
-    for (int j = 0; j < kMaxGroup; ++j)
-      if (j < G && k[j] >= t) {
+    for (int j = 0; j < kKeysPer; ++j)
+      if (k[j] >= t) {
         store_shared(a.tw.ckey + seg + at, k[j]);
-        store_shared(reinterpret_cast<uint32_t*>(a.tw.cpos) + seg + at, (uint32_t)(g * G + j));
-        if (at < (uint32_t)kMaxKeys) s.cp[at] = g * G + j;  // for the KV prefetch
+        store_shared(reinterpret_cast<uint32_t*>(a.tw.cpos) + seg + at, (uint32_t)(p0 + j));
+        if (at < (uint32_t)kMaxKeys) s.cp[at] = p0 + j;  // for the KV prefetch
         ++at;
       }
     if (tid == 0) store_shared(a.tw.ccount + r_local * kTopkSlices + slice, n_slice);
@@ -832,13 +721,14 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
   }
   if (bt_cached) o.bt_lds = s.bt;  // staged by every workgroup above
   for (int i = tid; i < kBins; i += kT) s.hist[i] = 0;  // for the selection, while loading
-  // Thread t reads entries 8 (t mod 64) .. +7 of slice t / 64 together with
-  // the counts (no round trip between them); in thread order that is
-  // position order.  A slice with more than 512 candidates sends the row
-  // to the general path.
-  const int my_slice = tid / kSegRead;
-  const int e0 = kKeysPer * (tid % kSegRead);
-  const int64_t seg = (int64_t)r_local * a.tw.cstride + (int64_t)my_slice * kTopkSliceGroups * G;
+  // Thread t reads entries kKeysPer (t mod P) .. +kKeysPer-1 of slice t / P,
+  // P = kT / S threads per slice, together with the counts (no round trip
+  // between them); in thread order that is position order.  A slice with
+  // more than P kKeysPer candidates sends the row to the general path.
+  const int P = kT / S;
+  const int my_slice = tid / P;
+  const int e0 = kKeysPer * (tid % P);
+  const int64_t seg = (int64_t)r_local * a.tw.cstride + (int64_t)my_slice * kTopkSliceLen;
   const int64_t row_end = (int64_t)(r_local + 1) * a.tw.cstride;
   uint32_t kk[kKeysPer];
   int32_t pp[kKeysPer];
@@ -869,14 +759,14 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
     n_tot += cnt[j];
     c_max = max(c_max, cnt[j]);
   }
-  if (n_tot > (uint32_t)kMaxKeys || c_max > (uint32_t)(kSegRead * kKeysPer)) {
+  if (n_tot > (uint32_t)kMaxKeys || c_max > (uint32_t)(P * kKeysPer)) {
     // heavy ties at t: the general path
     select_streamed<true>(sc, L, K, a.vec, o, s);
   } else {
     uint32_t c_mine = 0;
 #pragma unroll
     for (int j = 0; j < kTopkSlices; ++j) c_mine = j == my_slice ? cnt[j] : c_mine;
-    const int n = max(0, min(kKeysPer, (int)c_mine - e0));
+    const int n = my_slice < S ? max(0, min(kKeysPer, (int)c_mine - e0)) : 0;
 #pragma unroll
     for (int j = 0; j < kKeysPer; ++j) kk[j] = j < n ? kk[j] : 0u;
     auto visit = [&](auto f) {
@@ -888,32 +778,33 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
     __syncthreads();  // the cleared histogram
     const uint32_t T = select_kth<true>(visit, t, kmax, need, s);
     uint32_t eq_before = 0, out_before = 0;
-    emit_runs<kKeysPer, true>(kk, n, [&](int j) { return pp[j]; }, T, need, eq_before,
-                              out_before, o, s);
+    emit_runs<kKeysPer, true, true>(kk, n, [&](int j) { return pp[j]; }, T, need, eq_before,
+                                    out_before, o, s);
   }
   __syncthreads();
   o.flush(K);
   if (tid == 0) a.tw.arrive[r_local] = 0;
 }
 
-// Group maxima for a standalone Top-K call: thread -> one group of its row.
-__global__ __launch_bounds__(256) void topk_group_max_kernel(TopkLaunch a) {
+// The summary for a standalone Top-K call: one wave per 128-position
+// segment keeps its m largest keys (segment_top).
+__global__ __launch_bounds__(256) void topk_summary_kernel(TopkLaunch a) {
   int b, p;
   const int r_local = (int)blockIdx.y;
   if (blockIdx.x == 0 && threadIdx.x == 0) a.tw.arrive[r_local] = 0;
   if (!resolve_row(a.rows, a.row_begin + r_local, b, p)) return;
   const int L = p + 1;
-  if (L <= a.K) return;
-  const int G = topk_group(L, a.K);
-  if (G == 1) return;
-  const int g = (int)(blockIdx.x * 256 + threadIdx.x);
-  const int N = (L + G - 1) / G;
-  if (g >= N) return;
-  const float* sc = a.scores + (int64_t)r_local * a.ld + (int64_t)g * G;
-  const int n = min(G, L - g * G);
-  uint32_t m = 0;
-  for (int j = 0; j < n; ++j) m = max(m, score_key(sc[j]));
-  a.tw.gmax[(int64_t)r_local * a.tw.gstride + g] = m;
+  if (!topk_split_row(L, a.K)) return;
+  const int lane = (int)(threadIdx.x & 63);
+  const int seg = (int)(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int w0 = seg * kSumSeg;
+  if (w0 >= L) return;
+  const float* sc = a.scores + (int64_t)r_local * a.ld;
+  const uint32_t ka = w0 + lane < L ? score_key(sc[w0 + lane]) : 0u;
+  const uint32_t kb = w0 + 64 + lane < L ? score_key(sc[w0 + 64 + lane]) : 0u;
+  const int m = topk_sum_m(L);
+  const uint32_t mine = segment_top(ka, kb, m);
+  if (lane < m) a.tw.summ[(int64_t)r_local * kSumMax + seg * m + lane] = mine;
 }
 
 }  // namespace
@@ -924,18 +815,16 @@ int64_t cstride_of(int64_t max_len) { return (max_len + 63) & ~int64_t(63); }
 
 size_t topk_work_bytes(int rows, int64_t max_len) {
   if (rows <= 0) return 0;
-  const size_t words = (size_t)topk_gstride(max_len) + 2 * (size_t)cstride_of(max_len) +
-                       kTopkSlices + 1;
-  return ((size_t)rows * words + kMaxN) * sizeof(uint32_t);  // + load_gmax's padding
+  const size_t words = (size_t)kSumMax + 2 * (size_t)cstride_of(max_len) + kTopkSlices + 1;
+  return (size_t)rows * words * sizeof(uint32_t);
 }
 
 TopkWork topk_work_carve(void* base, int rows, int64_t max_len) {
   TopkWork w;
   uint32_t* p = static_cast<uint32_t*>(base);
-  w.gstride = topk_gstride(max_len);
   w.cstride = cstride_of(max_len);
-  w.gmax = p;
-  p += (size_t)rows * w.gstride + kMaxN;  // load_gmax reads up to kMaxN past a row's start
+  w.summ = p;
+  p += (size_t)rows * kSumMax;
   w.ckey = p;
   p += (size_t)rows * w.cstride;
   w.cpos = reinterpret_cast<int32_t*>(p);
@@ -948,9 +837,9 @@ TopkWork topk_work_carve(void* base, int rows, int64_t max_len) {
 
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
   if (a.num_rows <= 0) return hipSuccess;
-  if (a.prep && a.max_len > 2 * a.K) {  // some row may group its positions
-    const int64_t groups = (a.max_len + 1) / 2;
-    topk_group_max_kernel<<<dim3((unsigned)((groups + 255) / 256), a.num_rows), 256, 0, s>>>(a);
+  if (a.prep) {  // the rows' summaries (and the arrival counters cleared)
+    const int64_t segs = (a.max_len + kSumSeg - 1) / kSumSeg;
+    topk_summary_kernel<<<dim3((unsigned)((segs + 3) / 4), a.num_rows), 256, 0, s>>>(a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
