@@ -152,8 +152,8 @@ __host__ __device__ inline int topk_sum_m(int L) {
   const int m = kSumMax / nseg;
   return m < kSumCap ? m : kSumCap;
 }
-constexpr int kTopkSlices = 16;         // workgroups per row, at most
-constexpr int kTopkSliceLen = 8192;     // positions per slice
+constexpr int kTopkSlices = 32;         // workgroups per row, at most
+constexpr int kTopkSliceLen = 4096;     // positions per slice
 constexpr int kTopkSplitMaxK = 2048;
 // Rows that the Top-K spreads over slices (and that get a summary).
 __host__ __device__ inline bool topk_split_row(int L, int K) {

@@ -51,10 +51,12 @@ constexpr int kBins = 1 << kBinBits;      // 2048
 constexpr int kSmall = 64;                // bin size ranked directly by one wave
 constexpr int kPerThread = 16;            // keys per thread of a one-workgroup row
 constexpr int kMaxN = kPerThread * kT;    // 16384
-constexpr int kKeysPer = 8;               // a slice's keys (and compacted keys) per thread
+constexpr int kKeysPer = 8;               // compacted keys per thread (the finish)
 constexpr int kMaxKeys = kKeysPer * kT;   // 8192
 constexpr int kSumPer = kSumMax / kT;     // summary keys per thread (4)
-static_assert(kKeysPer * kT == kTopkSliceLen, "a slice is one key run per thread");
+constexpr int kRunPer = kTopkSliceLen / kT;  // a slice's positions per thread (4)
+static_assert(kRunPer * kT == kTopkSliceLen && kRunPer % 4 == 0, "a slice is one run per thread");
+static_assert(kTopkSlices <= 64, "one wave holds the slice counts");
 static_assert(kTopkSplitMaxK <= kBins, "split rows select within one staged pass");
 constexpr int kBtCache = 2048;            // block-table entries cached in LDS
 constexpr int kScanWords = 4 * kWaves + 1;
@@ -564,14 +566,14 @@ __device__ __forceinline__ void store_shared(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The kKeysPer scores from position i0 as raw bits (positions past L as 0);
+// The kRunPer scores from position i0 as raw bits (positions past L as 0);
 // converted to keys only once they are needed, so nothing waits for them
 // earlier.
 __device__ __forceinline__ void run_scores(const float* sc, int i0, int L, bool vec,
-                                           uint32_t (&x)[kKeysPer]) {
-  if (vec && i0 + kKeysPer <= L) {
+                                           uint32_t (&x)[kRunPer]) {
+  if (vec && i0 + kRunPer <= L) {
 #pragma unroll
-    for (int j = 0; j < kKeysPer; j += 4) {
+    for (int j = 0; j < kRunPer; j += 4) {
       const uint4 v = *reinterpret_cast<const uint4*>(sc + i0 + j);
       x[j] = v.x;
       x[j + 1] = v.y;
@@ -580,7 +582,7 @@ __device__ __forceinline__ void run_scores(const float* sc, int i0, int L, bool 
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < kKeysPer; ++j) x[j] = i0 + j < L ? __float_as_uint(sc[i0 + j]) : 0u;
+    for (int j = 0; j < kRunPer; ++j) x[j] = i0 + j < L ? __float_as_uint(sc[i0 + j]) : 0u;
   }
 }
 
@@ -610,8 +612,8 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
 
   // this thread's run of the slice: its scores, loaded now, used after t
   const float* sc = a.scores + (int64_t)r_local * a.ld;
-  const int p0 = slice * kTopkSliceLen + kKeysPer * tid;
-  uint32_t k[kKeysPer];
+  const int p0 = slice * kTopkSliceLen + kRunPer * tid;
+  uint32_t k[kRunPer];
   run_scores(sc, p0, L, a.vec, k);
   for (int i = tid; i < kBins; i += kT) s.hist[i] = 0;  // for step a; block_minmax syncs
   if (slice == 0 && tid == 0 && a.counts) a.counts[r_local] = K;
@@ -668,16 +670,16 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
 
   // b. this slice's keys >= t (t >= 1: positions past L, key 0, never count)
 #pragma unroll
-  for (int j = 0; j < kKeysPer; ++j) k[j] = p0 + j < L ? score_key(__uint_as_float(k[j])) : 0u;
+  for (int j = 0; j < kRunPer; ++j) k[j] = p0 + j < L ? score_key(__uint_as_float(k[j])) : 0u;
   uint32_t c = 0;
 #pragma unroll
-  for (int j = 0; j < kKeysPer; ++j) c += k[j] >= t ? 1u : 0u;
+  for (int j = 0; j < kRunPer; ++j) c += k[j] >= t ? 1u : 0u;
   uint32_t n_slice;
   uint32_t at = block_scan<false>(c, s.wsum, n_slice);  // the hand-over's barriers follow
   {
     const int64_t seg = (int64_t)r_local * a.tw.cstride + (int64_t)slice * kTopkSliceLen;
 #pragma unroll
-    for (int j = 0; j < kKeysPer; ++j)
+    for (int j = 0; j < kRunPer; ++j)
       if (k[j] >= t) {
         store_shared(a.tw.ckey + seg + at, k[j]);
         store_shared(reinterpret_cast<uint32_t*>(a.tw.cpos) + seg + at, (uint32_t)(p0 + j));
@@ -751,21 +753,16 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
       pp[j] = in ? a.tw.cpos[seg + e0 + j] : 0;
     }
   }
-  uint32_t cnt[kTopkSlices];
-  uint32_t n_tot = 0, c_max = 0;
-#pragma unroll
-  for (int j = 0; j < kTopkSlices; ++j) {
-    cnt[j] = j < S ? a.tw.ccount[r_local * kTopkSlices + j] : 0u;
-    n_tot += cnt[j];
-    c_max = max(c_max, cnt[j]);
-  }
+  // the slices' counts, lane j of every wave holding slice j's
+  const int lane = tid & 63;
+  const uint32_t cnt_lane = lane < S ? a.tw.ccount[r_local * kTopkSlices + lane] : 0u;
+  const uint32_t n_tot = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan(cnt_lane, 0u, Add()), 63);
+  const uint32_t c_max = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan(cnt_lane, 0u, Max()), 63);
   if (n_tot > (uint32_t)kMaxKeys || c_max > (uint32_t)(P * kKeysPer)) {
     // heavy ties at t: the general path
     select_streamed<true>(sc, L, K, a.vec, o, s);
   } else {
-    uint32_t c_mine = 0;
-#pragma unroll
-    for (int j = 0; j < kTopkSlices; ++j) c_mine = j == my_slice ? cnt[j] : c_mine;
+    const uint32_t c_mine = (uint32_t)__shfl((int)cnt_lane, my_slice & 63);
     const int n = my_slice < S ? max(0, min(kKeysPer, (int)c_mine - e0)) : 0;
 #pragma unroll
     for (int j = 0; j < kKeysPer; ++j) kk[j] = j < n ? kk[j] : 0u;
@@ -843,7 +840,11 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  topk_split_kernel<<<dim3(kTopkSlices, a.num_rows), kT, 0, s>>>(a);
+  // as many slices as the longest row can use (a row that splits has at
+  // most that many; the others run in slice 0)
+  const int64_t slices = (a.max_len + kTopkSliceLen - 1) / kTopkSliceLen;
+  const unsigned gx = (unsigned)(slices < 1 ? 1 : slices > kTopkSlices ? kTopkSlices : slices);
+  topk_split_kernel<<<dim3(gx, a.num_rows), kT, 0, s>>>(a);
   return hipGetLastError();
 }
 
