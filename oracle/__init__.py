@@ -25,6 +25,8 @@ numeric example for any step):
     the head weights, ``idx = fused_topk(q8, k, g)``;
   - section 5.1 / 5.2: FP8 storage for the indexer and the KV cache; the
     indexer's MXFP8 format (one shared scale per group of 32).
+* vLLM's DeepSeek-V4.1-Flash article, "Kernels": later indexer layers score
+  only a fixed set of candidate positions and take their top-k from it.
 * "Bandwidth-Aware LLM Inference on Heterogeneous Many-Core Supercomputers"
   (THInfer), eq. 9: softmax attention softmax(Q K^T / sqrt(d)) V, used here as
   the dense reference; section III.B.4: fp32 (here: fp64) accumulation.
@@ -47,6 +49,7 @@ from .formats import E4M3_TABLE, e4m3_to_f64, e8m0_to_f64, bf16_to_f64
 from .dsa import (
     resolve_rows,
     gather_positions,
+    row_history,
     indexer_scores_row,
     score_keys,
     topk_row,
@@ -58,7 +61,7 @@ from .dsa import (
 
 __all__ = [
     "E4M3_TABLE", "e4m3_to_f64", "e8m0_to_f64", "bf16_to_f64",
-    "resolve_rows", "gather_positions", "indexer_scores_row", "score_keys",
+    "resolve_rows", "gather_positions", "row_history", "indexer_scores_row", "score_keys",
     "topk_row", "sparse_attn_row", "masked_dense_attn_row",
     "dense_causal_attn_row", "decode_step",
 ]

@@ -20,6 +20,8 @@ Array conventions (raw storage bits, exactly what the GPU reads):
 * ``v_cache`` uint16 bf16    [num_blocks, 64, D_v] or None (latent layout:
   V is the first D_v columns of the K row)
 * ``block_table`` int32 [num_seqs, max_blocks]; ``seq_lens`` int32 [num_seqs]
+* ``cand`` int32 [rows, n_cand], ``cand_len`` int32 [rows] (optional): a
+  row's candidate positions, ascending, the first cand_len[r] entries valid
 """
 
 import numpy as np
@@ -202,15 +204,36 @@ def dense_causal_attn_row(q_bits, k_all_bits, v_all_bits, scale):
     return p @ v
 
 
+def row_history(p, cand_row=None, cand_len=None):
+    """Positions a row's indexer scores.
+
+    Without candidates: every position 0 .. p (Day0 article, section 2.2).
+    With a candidate list (vLLM's DeepSeek-V4.1-Flash article, "Kernels":
+    later indexer layers choose their top-k from a fixed set of candidate
+    positions and score only those): the first cand_len entries of the
+    row's list, which the caller gives in ascending order, each in 0 .. p.
+    """
+    if cand_row is None:
+        return np.arange(p + 1)
+    h = np.asarray(cand_row[:int(cand_len)], dtype=np.int64)
+    if len(h) and (h[0] < 0 or h[-1] > p or (np.diff(h) <= 0).any()):
+        raise ValueError("candidates must be ascending positions in 0..p")
+    return h
+
+
 def decode_step(*, qI, w, kI_cache, q, k_cache, v_cache, block_table, seq_lens,
                 K, scale, D_v, row_seq=None, row_pos=None, rows=None,
-                keep_scores=True, qI_scale=None, kI_scale_cache=None):
+                keep_scores=True, qI_scale=None, kI_scale_cache=None,
+                cand=None, cand_len=None):
     """The whole step for the chosen query rows (default: all rows).
 
     Row by row: index scores over positions 0..p_r, Top-K, gather of the
     selected KV rows, sparse softmax attention.  With ``qI_scale`` [rows,
     H_I, D_I/32] and ``kI_scale_cache`` [num_blocks, 64, D_I/32] (paged like
-    ``kI_cache``) the indexer is MXFP8.  Returns a dict with
+    ``kI_cache``) the indexer is MXFP8.  With ``cand`` / ``cand_len`` each
+    row scores only its candidate positions (row_history) and keeps the
+    Top-K among them; ``scores`` then holds one entry per candidate.
+    Returns a dict with
     ``scores`` (list of float32 arrays, or None), ``indices`` int32 [R, K],
     ``counts`` int64 [R], ``out`` float64 [R, H_q, D_v], ``lse`` float64
     [R, H_q] and ``rows`` (the row ids, in order).
@@ -226,7 +249,8 @@ def decode_step(*, qI, w, kI_cache, q, k_cache, v_cache, block_table, seq_lens,
     scores = [] if keep_scores else None
     for i, r in enumerate(rows):
         b, p = rs[r], rp[r]
-        history = np.arange(p + 1)
+        history = row_history(p, None if cand is None else cand[r],
+                              None if cand is None else cand_len[r])
         k_index = gather_positions(kI_cache, block_table[b], history)
         if qI_scale is None:
             sc = indexer_scores_row(qI[r], w[r], k_index)
@@ -234,6 +258,10 @@ def decode_step(*, qI, w, kI_cache, q, k_cache, v_cache, block_table, seq_lens,
             k_scale = gather_positions(kI_scale_cache, block_table[b], history)
             sc = indexer_scores_row(qI[r], w[r], k_index, qI_scale[r], k_scale)
         idx, n = topk_row(sc, K)
+        # candidate slots are in position order: ties to the lower slot are
+        # ties to the lower position, and ascending slots ascending positions
+        idx = idx.copy()
+        idx[:n] = history[idx[:n]]
         chosen = idx[:n]
         k_rows = gather_positions(k_cache, block_table[b], chosen)
         if v_cache is None:

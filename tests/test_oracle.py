@@ -426,3 +426,72 @@ def test_decode_step_row_alone_equals_row_in_batch_and_prefill_rows():
     for i in range(16):
         assert len(res["scores"][i]) == arr["row_pos"][i] + 1
         assert res["indices"][i].max() <= arr["row_pos"][i]
+
+
+# ----------------------------------------------------- candidate-restricted
+def _with_cand(arr, cand_rows):
+    """arr with explicit candidate lists (ascending, -1 padded)."""
+    n = max(1, max(len(c) for c in cand_rows))
+    cand = np.full((len(cand_rows), n), -1, dtype=np.int32)
+    for i, c in enumerate(cand_rows):
+        cand[i, :len(c)] = c
+    out = dict(arr)
+    out["cand"] = cand
+    out["cand_len"] = np.array([len(c) for c in cand_rows], dtype=np.int32)
+    return out
+
+
+def test_candidates_covering_the_history_reduce_to_the_full_step():
+    wl = small_workload("t", lengths=[37, 200, 700], **_tiny(K=50))
+    arr = oracle_arrays(make_batch(wl, seed=21))
+    full = run_oracle(arr)
+    cand = run_oracle(_with_cand(arr, [np.arange(L) for L in (37, 200, 700)]))
+    assert (full["indices"] == cand["indices"]).all()
+    assert (full["counts"] == cand["counts"]).all()
+    assert np.array_equal(full["out"], cand["out"]) and np.array_equal(full["lse"], cand["lse"])
+    for a, b in zip(full["scores"], cand["scores"]):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("seed", [3, 4, 5])
+def test_candidate_scores_and_top_k_by_brute_force(seed):
+    # scores at the candidates are the full scores at those positions; the
+    # kept set is the K best candidates (score, then lower position), written
+    # ascending, by a plain sort over the candidate list
+    wl = small_workload("t", lengths=[900, 333], **_tiny(K=40, mode="gauss"))
+    arr = oracle_arrays(make_batch(wl, seed=seed))
+    rng = np.random.default_rng(seed)
+    rows = [np.sort(rng.choice(900, 150, replace=False)), np.sort(rng.choice(333, 30, replace=False))]
+    full = run_oracle(arr)
+    got = run_oracle(_with_cand(arr, rows))
+    for i, c in enumerate(rows):
+        sc = np.asarray(full["scores"][i])[c]
+        assert np.array_equal(np.asarray(got["scores"][i]), sc)
+        best = sorted(range(len(c)), key=lambda j: (-float(sc[j]), int(c[j])))[:40]
+        want = np.sort(c[best])
+        n = min(40, len(c))
+        assert got["counts"][i] == n
+        assert (got["indices"][i][:n] == want).all() and (got["indices"][i][n:] == -1).all()
+
+
+def test_candidates_outside_the_kept_set_do_not_matter():
+    # dropping candidates that are not kept leaves the selection and the
+    # attention unchanged; an empty list keeps nothing
+    wl = small_workload("t", lengths=[500], **_tiny(K=20, mode="gauss"))
+    arr = oracle_arrays(make_batch(wl, seed=8))
+    c = np.arange(0, 500, 3)
+    a = run_oracle(_with_cand(arr, [c]))
+    kept = a["indices"][0][:20]
+    b = run_oracle(_with_cand(arr, [np.union1d(kept, c[::5])]))
+    assert (a["indices"] == b["indices"]).all()
+    assert np.allclose(a["out"], b["out"], rtol=0, atol=1e-12)
+    e = run_oracle(_with_cand(arr, [np.array([], dtype=np.int64)]))
+    assert e["counts"][0] == 0 and (e["indices"][0] == -1).all() and (e["out"][0] == 0).all()
+
+
+def test_candidates_must_be_ascending_positions_of_the_history():
+    with pytest.raises(ValueError):
+        oracle.row_history(10, np.array([3, 2]), 2)
+    with pytest.raises(ValueError):
+        oracle.row_history(10, np.array([3, 11]), 2)
+    assert (oracle.row_history(10, np.array([3, 7, -1]), 2) == [3, 7]).all()

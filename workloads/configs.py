@@ -32,6 +32,10 @@ class Workload:
     # indexer operands: "e4m3" unscaled codes, or "mxfp8" codes with one E8M0
     # scale per 32 dims (integer mode: codes in [-4, 4], scales 2**-1 .. 2**1)
     indexer_fmt: str = "e4m3"
+    # candidate-restricted indexer: each row scores only n_cand of its
+    # positions (a seeded uniform subset, ascending; rows shorter than n_cand
+    # take every position); 0: the whole history
+    n_cand: int = 0
 
     @property
     def rows(self) -> int:

@@ -39,6 +39,8 @@ class Batch:
     kv: torch.Tensor         # bfloat16 [num_blocks, 64, D_qk]
     v: Optional[torch.Tensor] = None   # bfloat16 [num_blocks, 64, D_v] (separate V)
     qI_scale: Optional[torch.Tensor] = None  # MXFP8: uint8 E8M0 [rows, H_I, D_I/32]
+    cand: Optional[torch.Tensor] = None      # int32 [rows, n_cand]: candidate positions, -1 past
+    cand_len: Optional[torch.Tensor] = None  # int32 [rows]: valid candidates of each row
     extra: dict = field(default_factory=dict)
 
     @property
@@ -189,11 +191,25 @@ def make_batch(wl: Workload, device="cpu", seed=None, mode=None, table=None,
     kv = _bf16_normal((num_blocks, BLOCK, wl.D_qk), gd, device)
     v = None if wl.latent else _bf16_normal((num_blocks, BLOCK, wl.D_v), gd, device)
 
+    cand = cand_len = None
+    if wl.n_cand:
+        # each row's candidates: a uniform subset of its history, ascending
+        C = wl.n_cand
+        ch = torch.full((R, C), -1, dtype=torch.int32)
+        cl = torch.zeros(R, dtype=torch.int32)
+        for i, p in enumerate(row_pos_h):
+            n = min(C, p + 1)
+            pick = torch.randperm(p + 1, generator=gs)[:n] if n < p + 1 else torch.arange(p + 1)
+            ch[i, :n] = torch.sort(pick).values.to(torch.int32)
+            cl[i] = n
+        cand, cand_len = ch.to(device), cl.to(device)
+
     return Batch(wl=wl, lengths=lens, row_seq_host=row_seq_h, row_pos_host=row_pos_h,
                  max_blocks=max_blocks, num_blocks=num_blocks,
                  seq_lens=torch.tensor(lens, dtype=torch.int32, device=device),
                  block_table=bt.to(device), row_seq=row_seq, row_pos=row_pos,
-                 qI=qI, w=w, kI=kI, q=q, kv=kv, v=v, qI_scale=qI_scale)
+                 qI=qI, w=w, kI=kI, q=q, kv=kv, v=v, qI_scale=qI_scale,
+                 cand=cand, cand_len=cand_len)
 
 
 def row_positions(batch: Batch):
@@ -249,6 +265,8 @@ def oracle_arrays(batch: Batch, rows=None) -> dict:
     return {
         "qI_scale": None if batch.qI_scale is None else _np(batch.qI_scale.index_select(0, sel)),
         "kI_scale_cache": kI_scale,
+        "cand": None if batch.cand is None else _np(batch.cand.index_select(0, sel)),
+        "cand_len": None if batch.cand is None else _np(batch.cand_len.index_select(0, sel)),
         "qI": _np(batch.qI.index_select(0, sel)),
         "w": _np(batch.w.index_select(0, sel)),
         "q": _np(batch.q.index_select(0, sel).view(torch.int16)).view(np.uint16),
