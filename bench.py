@@ -18,6 +18,9 @@ cpu_baseline  the oracle timed on the host on a bounded sample of rows
 mxfp8_indexer  the same workload with MXFP8 indexer operands (one E8M0 scale
            per 32 dims): the fused step and the indexer scan alone, timed the
            same way over their own rotating input sets (--no-mxfp8 skips it)
+candidate_indexer  the same workload with a candidate-restricted indexer
+           (16384 candidate positions per row): the fused step and the scan
+           alone, timed the same way (--no-cand skips it)
 """
 
 import argparse
@@ -44,6 +47,8 @@ def parse():
     ap.add_argument("--graph", type=int, default=1, help="replay captured HIP graphs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cand", action="store_true",
+                    help="skip the candidate-restricted indexer leg")
     ap.add_argument("--no-mxfp8", action="store_true",
                     help="skip the MXFP8-indexer leg (same workload, group-32 scales)")
     ap.add_argument("--table", default=None)
@@ -238,6 +243,8 @@ def main():
 
     if not args.no_mxfp8:
         result["mxfp8_indexer"] = mxfp8_leg(args, wl, lengths, stream, rotate_bytes=ib)
+    if not args.no_cand:
+        result["candidate_indexer"] = cand_leg(args, wl, lengths, stream)
 
     if args.copy_calibration:
         n = (args.copy_calibration << 20) // 4
@@ -309,6 +316,70 @@ def mxfp8_leg(args, wl, lengths, stream, rotate_bytes):
             "tokens_per_s": round(rows / (step_us * 1e-6), 1),
             "indexer_avg_launch_us": round(idx_us, 3), "indexer_bytes_per_launch": ib,
             "indexer_achieved": round(achieved, 1), "indexer_frac": round(achieved / HBM_PEAK_GBS, 4)}
+
+
+def cand_bytes(wl, lengths, n_cand):
+    """Algorithmic bytes of one candidate-restricted indexer launch: per row,
+    each candidate's key row, list entry and score, at most one block id per
+    candidate, the row's queries and weights."""
+    tot = 0
+    for L in lengths:
+        C = min(n_cand, L)
+        tot += C * (wl.D_I + 4 + 4) + 4 * min(C, -(-L // 64)) + wl.H_I * wl.D_I + 4 * wl.H_I
+    return tot
+
+
+def cand_leg(args, wl, lengths, stream, n_cand=16384):
+    """The same workload with a candidate-restricted indexer (16384 candidate
+    positions per row): the indexer timed alone and the fused step (stream
+    launches), with HIP events on the launch stream over input sets that
+    rotate past the Infinity Cache."""
+    import torch
+    from indexer_top_sparse_score_amd import binding as B
+    from workloads import make_batch
+    cwl = wl.with_(n_cand=n_cand)
+    dev = torch.device("cuda:0")
+    nset = 4  # each set's KV (576 MiB at 4 x 128k) already exceeds the cache
+    sets = [make_batch(cwl, device=dev, seed=cwl.seed + 9000 + 1000 * i, mode=args.mode,
+                       table=args.table) for i in range(nset)]
+    probs = [B.problem_for_batch(s) for s in sets]
+    rows = sets[0].rows
+    scores = torch.empty((rows, n_cand), dtype=torch.float32, device=dev)
+    ws_i = B.workspace(probs[0], B.DSA_OP_INDEXER_SCORES, device=dev)
+    ws = B.workspace(probs[0], B.DSA_OP_DECODE_STEP, device=dev)
+    out = torch.empty((rows, cwl.H_q, cwl.D_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((rows, cwl.H_q), dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        with torch.cuda.stream(stream):
+            for i in range(args.warmup):
+                fn(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(args.steps):
+                fn(i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / args.steps  # us
+
+    def scan(i):
+        s = sets[i % nset]
+        B.dsa_indexer_scores(probs[i % nset], s.qI, s.w, s.kI, scores, ws_i, stream=stream)
+
+    def step(i):
+        s = sets[i % nset]
+        v = s.v if s.v is not None else s.kv
+        B.dsa_decode_step(probs[i % nset], s.qI, s.w, s.kI, s.q, s.kv, v, out, ws, lse=lse,
+                          stream=stream)
+
+    idx_us = timed(scan)
+    step_us = timed(step)
+    assert B.device_errors(ws) == 0 and B.device_errors(ws_i) == 0
+    cb = cand_bytes(cwl, lengths, n_cand)
+    return {"candidates_per_row": n_cand, "rotation_sets": nset, "launch": "stream (eager)",
+            "step_us": round(step_us, 3), "tokens_per_s": round(rows / (step_us * 1e-6), 1),
+            "indexer_avg_launch_us": round(idx_us, 3), "indexer_bytes_per_launch": cb,
+            "indexer_achieved": round(cb / (idx_us * 1e-6) / 1e9, 1)}
 
 
 def cpu_baseline(batch, budget_s):

@@ -62,7 +62,7 @@ extern "C" {
 #define DSA_API
 #endif
 
-#define DSA_ABI_VERSION 3
+#define DSA_ABI_VERSION 4
 #define DSA_BLOCK_SIZE 64
 
 typedef enum {
@@ -107,6 +107,14 @@ typedef struct {
   int32_t indexer_format;     /* DSA_INDEXER_E4M3 or DSA_INDEXER_MXFP8                  */
   const uint8_t* qI_scale;    /* MXFP8: [num_rows][H_I][D_I / 32] E8M0 scales of qI;
                                  NULL for E4M3                                          */
+  /* Candidate-restricted indexer (vLLM's DeepSeek-V4.1-Flash article,
+     "Kernels": later indexer layers score only a fixed set of candidate
+     positions).  NULL cand: every row scores its whole history.          */
+  const int32_t* cand;        /* [num_rows][n_cand] candidate positions of each row,
+                                 ascending, each in 0 .. p_r                            */
+  const int32_t* cand_len;    /* [num_rows] valid leading entries of each list, clamped
+                                 to 0 .. n_cand; entries past it are not read           */
+  int32_t n_cand;             /* row length of cand (>= 1 with cand)                    */
 } dsa_problem;
 
 /* indexer operand formats (dsa_problem.indexer_format) */
@@ -156,6 +164,13 @@ DSA_API size_t dsa_workspace_size(const dsa_problem* p, int op);
  *           else DSA_ERR_INVALID).  The code rows keep their alignment and
  *           the scales of 64 positions are one contiguous run.
  * Power-of-two scales keep every product exact.
+ *
+ * With candidates (p->cand), row r scores its list instead: for slots
+ * c = 0 .. cand_len[r] - 1, scores[r * ld_scores + c] is the score of
+ * position cand[r][c], and ld_scores >= n_cand.  A list that is not
+ * ascending inside 0 .. p_r gives unspecified scores for the offending
+ * slots (a position outside the history sets DSA_DEVERR_ROW), never an
+ * access outside the caches.
  */
 DSA_API int dsa_indexer_scores(const dsa_problem* p, const uint8_t* qI, const float* w, dsa_paged kI,
                        float* scores, int64_t ld_scores, void* ws, size_t ws_bytes,
@@ -168,6 +183,10 @@ DSA_API int dsa_indexer_scores(const dsa_problem* p, const uint8_t* qI, const fl
  *   indices  int32 [num_rows][K]: the kept positions in ascending order,
  *            then -1 up to K
  *   counts   int32 [num_rows] = min(K, L_r), or NULL
+ * With candidates (p->cand) a row's scores are per slot (as
+ * dsa_indexer_scores writes them), L_r = cand_len[r], and the kept slots are
+ * written as their positions cand[r][c]: ascending, ties to the lower
+ * position.
  */
 DSA_API int dsa_topk(const dsa_problem* p, const float* scores, int64_t ld_scores, int32_t* indices,
              int32_t* counts, void* ws, size_t ws_bytes, void* stream);

@@ -27,7 +27,7 @@ DSA_OP_TOPK = 1
 DSA_OP_SPARSE_ATTN = 2
 DSA_OP_DECODE_STEP = 3
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 DSA_INDEXER_E4M3 = 0
 DSA_INDEXER_MXFP8 = 1
 BLOCK = 64
@@ -50,7 +50,8 @@ class DsaProblem(ctypes.Structure):
                 ("H_I", ctypes.c_int32), ("D_I", ctypes.c_int32), ("H_q", ctypes.c_int32),
                 ("D_qk", ctypes.c_int32), ("D_v", ctypes.c_int32), ("K", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("indexer_format", ctypes.c_int32),
-                ("qI_scale", ctypes.c_void_p)]
+                ("qI_scale", ctypes.c_void_p),
+                ("cand", ctypes.c_void_p), ("cand_len", ctypes.c_void_p), ("n_cand", ctypes.c_int32)]
 
 
 class DsaError(RuntimeError):
@@ -119,10 +120,12 @@ def paged(cache: torch.Tensor) -> DsaPaged:
 
 def problem(*, seq_lens, block_table, num_rows=None, row_seq=None, row_pos=None, H_I=64,
             D_I=128, H_q=128, D_qk=576, D_v=512, K=2048, scale=576 ** -0.5,
-            qI_scale=None) -> DsaProblem:
+            qI_scale=None, cand=None, cand_len=None) -> DsaProblem:
     """Problem descriptor; device tensors are referenced, not copied.  With
     ``qI_scale`` (uint8 E8M0 [rows, H_I, D_I/32]) the indexer runs in MXFP8
-    format and each index-key block carries its rows' scales after the code rows."""
+    format and each index-key block carries its rows' scales after the code rows.
+    With ``cand`` (int32 [rows, n_cand], ascending positions) and ``cand_len``
+    (int32 [rows]) each row scores only its candidate positions."""
     num_seqs = int(seq_lens.shape[0])
     if num_rows is None:
         num_rows = int(row_seq.shape[0]) if row_seq is not None else num_seqs
@@ -132,8 +135,11 @@ def problem(*, seq_lens, block_table, num_rows=None, row_seq=None, row_pos=None,
                    None if row_pos is None else row_pos.data_ptr(),
                    H_I, D_I, H_q, D_qk, D_v, K, scale,
                    DSA_INDEXER_E4M3 if qI_scale is None else DSA_INDEXER_MXFP8,
-                   None if qI_scale is None else qI_scale.data_ptr())
-    p._keep = (seq_lens, block_table, row_seq, row_pos, qI_scale)  # keep the tensors alive
+                   None if qI_scale is None else qI_scale.data_ptr(),
+                   None if cand is None else cand.data_ptr(),
+                   None if cand_len is None else cand_len.data_ptr(),
+                   0 if cand is None else int(cand.shape[1]))
+    p._keep = (seq_lens, block_table, row_seq, row_pos, qI_scale, cand, cand_len)  # keep alive
     return p
 
 
@@ -145,7 +151,8 @@ def problem_for_batch(batch) -> DsaProblem:
                    num_rows=int(batch.qI.shape[0]), row_seq=batch.row_seq,
                    row_pos=batch.row_pos, H_I=wl.H_I, D_I=wl.D_I, H_q=wl.H_q, D_qk=wl.D_qk,
                    D_v=wl.D_v, K=wl.K, scale=wl.scale,
-                   qI_scale=getattr(batch, "qI_scale", None))
+                   qI_scale=getattr(batch, "qI_scale", None), cand=getattr(batch, "cand", None),
+                   cand_len=getattr(batch, "cand_len", None))
 
 
 def dsa_workspace_size(prob: DsaProblem, op: int) -> int:

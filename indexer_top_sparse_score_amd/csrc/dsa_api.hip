@@ -26,6 +26,10 @@ int check_rows(const dsa_problem* p) {
     return DSA_ERR_INVALID;
   if (p->block_size != DSA_BLOCK_SIZE) return DSA_ERR_UNSUPPORTED;
   if (p->max_blocks > (1 << 24)) return DSA_ERR_UNSUPPORTED;
+  if (!p->cand != !p->cand_len) return DSA_ERR_INVALID;  // both or neither
+  if (p->cand && (p->n_cand < 1 || !aligned(p->cand, 16) || !aligned(p->cand_len, 4)))
+    return DSA_ERR_INVALID;
+  if (p->cand && p->n_cand > (1 << 24)) return DSA_ERR_UNSUPPORTED;
   return DSA_OK;
 }
 
@@ -88,13 +92,25 @@ RowMap row_map(const dsa_problem* p) {
   m.row_pos = p->row_pos;
   m.num_seqs = p->num_seqs;
   m.max_blocks = p->max_blocks;
+  m.cand = p->cand;
+  m.cand_len = p->cand_len;
+  m.n_cand = p->cand ? p->n_cand : 0;
   return m;
 }
 
-int64_t max_len(const dsa_problem* p) { return (int64_t)p->max_blocks * DSA_BLOCK_SIZE; }
+// Length of a score row: the candidate list's, or the longest history.
+int64_t max_len(const dsa_problem* p) {
+  return p->cand ? (int64_t)p->n_cand : (int64_t)p->max_blocks * DSA_BLOCK_SIZE;
+}
+
+// Row stride of the fused step's score slab: a multiple of 64 floats, so
+// every row is 256-byte aligned.
+int64_t slab_ld(const dsa_problem* p) { return (max_len(p) + 63) & ~int64_t(63); }
+
+bool cand_vec(const dsa_problem* p) { return p->cand && p->n_cand % 4 == 0; }
 
 int rows_per_pass(const dsa_problem* p) {
-  const size_t per_row = (size_t)max_len(p) * sizeof(float) + topk_work_bytes(1, max_len(p));
+  const size_t per_row = (size_t)slab_ld(p) * sizeof(float) + topk_work_bytes(1, max_len(p));
   size_t rp = kScoresBudget / per_row;
   if (rp < 1) rp = 1;
   if (rp > (size_t)p->num_rows) rp = (size_t)p->num_rows;
@@ -123,7 +139,7 @@ DecodeLayout decode_layout(const dsa_problem* p) {
   d.idx_off = kHeader;
   d.roff_off = d.idx_off + round256((size_t)d.rp * p->K * sizeof(int32_t));
   d.scores_off = d.roff_off + round256((size_t)d.rp * p->K * sizeof(int64_t));
-  d.topk_off = d.scores_off + round256((size_t)d.rp * max_len(p) * sizeof(float));
+  d.topk_off = d.scores_off + round256((size_t)d.rp * slab_ld(p) * sizeof(float));
   d.part_off = d.topk_off + round256(topk_work_bytes(d.rp, max_len(p)));
   d.total = d.part_off + round256(attn_partial_bytes(d.rp, p->H_q, p->D_v, nc));
   return d;
@@ -227,6 +243,7 @@ int dsa_topk(const dsa_problem* p, const float* scores, int64_t ld_scores, int32
   a.tw = topk_work_carve(static_cast<char*>(ws) + kHeader, p->num_rows, max_len(p));
   a.prep = true;
   a.vec = aligned(scores, 16) && ld_scores % 4 == 0;
+  a.cvec = cand_vec(p);
   a.rowoff = nullptr;
   a.kv = dsa_paged{};
   a.kv_row_bytes = 0;
@@ -310,8 +327,8 @@ int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa
   char* base = static_cast<char*>(ws);
   uint32_t* err = reinterpret_cast<uint32_t*>(base);
   float* scores = reinterpret_cast<float*>(base + d.scores_off);
-  const int64_t ld = max_len(p);
-  const TopkWork tw = topk_work_carve(base + d.topk_off, d.rp, ld);
+  const int64_t ld = slab_ld(p);
+  const TopkWork tw = topk_work_carve(base + d.topk_off, d.rp, max_len(p));
   const bool use_rowoff = is_latent(k, v) && p->D_qk == 576;
   int64_t* roff = reinterpret_cast<int64_t*>(base + d.roff_off);
 
@@ -333,7 +350,7 @@ int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa
     ia.qI_scale = p->qI_scale;
     ia.row_begin = row0;
     ia.num_rows = nr;
-    ia.max_len = (int32_t)ld;
+    ia.max_len = (int32_t)max_len(p);
     ia.tw = tw;
     ia.topk_K = p->K;
     if ((st = status_of(launch_indexer_scores(ia, s))) != DSA_OK) return st;
@@ -348,10 +365,11 @@ int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa
     ta.K = p->K;
     ta.row_begin = row0;
     ta.num_rows = nr;
-    ta.max_len = (int32_t)ld;
+    ta.max_len = (int32_t)max_len(p);
     ta.tw = tw;
     ta.prep = false;
     ta.vec = true;  // 256-byte aligned slab, ld a multiple of 64
+    ta.cvec = cand_vec(p);
     ta.rowoff = use_rowoff ? roff : nullptr;
     ta.kv = k;
     ta.kv_row_bytes = use_rowoff ? p->D_qk * 2 : 0;

@@ -26,6 +26,11 @@ struct RowMap {
   const int32_t* row_pos;  // NULL: position seq_lens[b] - 1
   int32_t num_seqs;
   int32_t max_blocks;
+  // Candidate-restricted rows: row r scores only the positions
+  // cand[r * n_cand + c], c < cand_len[r] (ascending); NULL: every position.
+  const int32_t* cand;
+  const int32_t* cand_len;
+  int32_t n_cand;
 };
 
 // Resolves row r.  Returns false (and leaves b, p unspecified) when the
@@ -49,7 +54,7 @@ __device__ __forceinline__ bool resolve_row(const RowMap& m, int r, int& b, int&
 // L = p + 1, or 0 for a row that does not resolve.  Only a row_seq lookup
 // (chunked prefill rows) costs a round trip of its own.
 struct RowIssue {
-  int b, len_v, pos_v;
+  int b, len_v, pos_v, clen_v;
   bool b_ok;
 };
 __device__ __forceinline__ RowIssue row_issue(const RowMap& m, int r) {
@@ -59,9 +64,11 @@ __device__ __forceinline__ RowIssue row_issue(const RowMap& m, int r) {
   q.b_ok = q.b >= 0 && q.b < m.num_seqs;
   gint* len_at = (gint*)(m.seq_lens + (q.b_ok ? q.b : 0));
   gint* pos_at = (gint*)(m.row_pos ? m.row_pos + r : m.seq_lens);
-  asm volatile("" : "+v"(len_at), "+v"(pos_at));
+  gint* clen_at = (gint*)(m.cand_len ? m.cand_len + r : m.seq_lens);
+  asm volatile("" : "+v"(len_at), "+v"(pos_at), "+v"(clen_at));
   q.len_v = *len_at;
   q.pos_v = *pos_at;
+  q.clen_v = *clen_at;
   return q;
 }
 __device__ __forceinline__ int row_finish(const RowMap& m, const RowIssue& q) {
@@ -69,6 +76,14 @@ __device__ __forceinline__ int row_finish(const RowMap& m, const RowIssue& q) {
   const int p = m.row_pos ? __builtin_amdgcn_readfirstlane(q.pos_v) : len - 1;
   if (!q.b_ok || p < 0 || p >= len || p >= m.max_blocks * kBlock) return 0;
   return p + 1;
+}
+// Length of the row's score row: its candidate count (clamped to
+// 0 .. n_cand) for a candidate-restricted row, else its history length L
+// (0 for a row that does not resolve).
+__device__ __forceinline__ int row_slots(const RowMap& m, const RowIssue& q, int L) {
+  if (!m.cand || L == 0) return L;
+  const int c = __builtin_amdgcn_readfirstlane(q.clen_v);
+  return c < 0 ? 0 : c > m.n_cand ? m.n_cand : c;
 }
 
 __device__ __forceinline__ void report(uint32_t* err, uint32_t bit) {
@@ -247,6 +262,7 @@ struct TopkLaunch {
   TopkWork tw;
   bool prep;            // compute the summaries here (no fused indexer before)
   bool vec;             // every score row is 16-byte aligned (ld % 4 == 0)
+  bool cvec;            // every candidate row is 16-byte aligned (n_cand % 4 == 0)
   // Optional: also write each kept position's byte offset in the paged KV
   // cache `kv` (block table -> physical block), -1 for padding and for
   // positions whose block id is out of range, to rowoff[num_rows][K].

@@ -77,7 +77,12 @@ __device__ __forceinline__ v4f mfma_scaled(v8i a, v8i b, int scale_a, int scale_
 // (j >= 2) in the slice layout above -- a pairing of data and scales the
 // hardware defines, and that this kernel only has to feed: lane (col, g)
 // passes the scale of dims [32g, 32g + 32) of its head or key row.
-template <int NKP, int HT, bool MX>
+//
+// CAND: candidate-restricted rows (vLLM's DeepSeek-V4.1-Flash article,
+// "Kernels"): the tile covers 512 slots of the row's candidate list rather
+// than 512 consecutive positions, and every lane gathers its own key row
+// (position cand[slot], block id from the table), one more round trip.
+template <int NKP, int HT, bool MX, bool CAND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void indexer_scan_kernel(IndexerLaunch a) {
   const int r = a.row_begin + (int)blockIdx.y;
   const int tile0 = (int)blockIdx.x * kTile;
@@ -114,7 +119,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
   const int32_t* bt = a.rows.block_table + (int64_t)(b_ok ? b : 0) * a.rows.max_blocks;
   // block id of the tile's page `lane` (lanes past the tile's pages, or past
   // the table's columns, read a valid entry that is never used)
-  const int my_page = bt[min(tile0 / kBlock + lane, a.rows.max_blocks - 1)];
+  const int my_page = CAND ? 0 : bt[min(tile0 / kBlock + lane, a.rows.max_blocks - 1)];
+  // candidate rows: position of the slot of each of the wave's sub-tiles
+  // that this lane's column covers (clamped reads; checked after L is known)
+  int cpos[CAND ? kSubPerWave : 1];
+  if constexpr (CAND) {
+    const int32_t* crow = a.rows.cand + (int64_t)r * a.rows.n_cand;
+#pragma unroll
+    for (int j = 0; j < kSubPerWave; ++j)
+      cpos[j] = crow[min(tile0 + wave * kSpan + j * kSub + col, a.rows.n_cand - 1)];
+  }
   {
     // the padded query is HT*16 rows of kRowBytes <= 8 KiB: two 16-byte
     // pieces per thread; all loads are issued before any LDS write
@@ -146,7 +160,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     if (blockIdx.x == 0 && threadIdx.x == 0) report(a.err, DSA_DEVERR_ROW);
     return;
   }
-  if (tile0 >= L) return;
+  // slots of the score row: L positions, or the candidate count
+  const int S = CAND ? row_slots(a.rows, ri, L) : L;
+  if (tile0 >= S) return;
 
   // 2. keys: this wave owns the kSpan positions from w0; sub-tile j starts
   //    at w0 + 16j.  Straight-line code lets the compiler wait for each
@@ -156,15 +172,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
   const uint32_t lane_off = (uint32_t)(col * a.kI.row_stride + 16 * g);
   v8i keys[kSubPerWave];
   bool page_ok[kSubPerWave];
+  uint32_t csw[CAND && MX ? kSubPerWave : 1];  // candidate rows: this lane's key scale word
+  bool bad_pos = false, bad_blk = false;
+  if constexpr (CAND) {
+    // each lane's own row: a slot inside the list whose position lies in
+    // the history; its block id comes from the table (one more round trip)
+    int cphys[kSubPerWave];
+    bool inside[kSubPerWave];
 #pragma unroll
-  for (int j = 0; j < kSubPerWave; ++j) {
-    const int s0 = w0 + j * kSub;
-    const int phys = __builtin_amdgcn_readlane(my_page, (s0 - tile0) >> 6);
-    // a page past the table's columns, or with an id out of range, is absent
-    page_ok[j] = s0 / kBlock < a.rows.max_blocks && phys >= 0 && (int64_t)phys < a.kI.num_blocks;
-    const uint8_t* sub = kbase + (int64_t)(page_ok[j] ? phys : 0) * a.kI.block_stride +
-                         (int64_t)(s0 & 63) * a.kI.row_stride;
-    keys[j] = load_slice<NKP>(sub, lane_off);
+    for (int j = 0; j < kSubPerWave; ++j) {
+      const bool in_list = w0 + j * kSub + col < S;
+      inside[j] = in_list && cpos[j] >= 0 && cpos[j] < L;
+      bad_pos = bad_pos || (in_list && !inside[j]);
+      cpos[j] = inside[j] ? cpos[j] : 0;
+      cphys[j] = bt[cpos[j] >> 6];
+    }
+#pragma unroll
+    for (int j = 0; j < kSubPerWave; ++j) {
+      page_ok[j] = inside[j] && cphys[j] >= 0 && (int64_t)cphys[j] < a.kI.num_blocks;
+      bad_blk = bad_blk || (inside[j] && !page_ok[j]);
+      const uint8_t* blk = kbase + (int64_t)(page_ok[j] ? cphys[j] : 0) * a.kI.block_stride;
+      const int rr = page_ok[j] ? (cpos[j] & 63) : 0;
+      keys[j] = load_slice<NKP>(blk + (int64_t)rr * a.kI.row_stride, (uint32_t)(16 * g));
+      if constexpr (MX) {
+        const uint8_t* sw = blk + (int64_t)kBlock * a.kI.row_stride + rr * kNG;
+        if constexpr (kNG == 4)
+          csw[j] = *reinterpret_cast<const uint32_t*>(sw);
+        else
+          csw[j] = *reinterpret_cast<const uint16_t*>(sw);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kSubPerWave; ++j) {
+      const int s0 = w0 + j * kSub;
+      const int phys = __builtin_amdgcn_readlane(my_page, (s0 - tile0) >> 6);
+      // a page past the table's columns, or with an id out of range, is absent
+      page_ok[j] = s0 / kBlock < a.rows.max_blocks && phys >= 0 && (int64_t)phys < a.kI.num_blocks;
+      const uint8_t* sub = kbase + (int64_t)(page_ok[j] ? phys : 0) * a.kI.block_stride +
+                           (int64_t)(s0 & 63) * a.kI.row_stride;
+      keys[j] = load_slice<NKP>(sub, lane_off);
+    }
   }
   // MX: the scale words of the wave's key rows.  The wave's 128 positions
   // are two whole blocks (w0 is a multiple of 128), and a block keeps its
@@ -175,7 +223,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
   // stay in flight.
   static_assert(kSubPerWave == 8 && kSpan == 2 * kBlock, "two scale words per lane cover the wave");
   uint32_t ksw[MX ? 2 : 1];
-  if (MX) {
+  if (MX && !CAND) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int phys = __builtin_amdgcn_readlane(my_page, ((w0 - tile0) >> 6) + h);
@@ -218,7 +266,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     // groups and for E4M3)
     int ks = 127;
     if (MX) {
-      const uint32_t word = (uint32_t)__shfl((int)ksw[MX ? j / 4 : 0], 16 * (j % 4) + col);
+      const uint32_t word = CAND ? csw[CAND ? j : 0]
+                                 : (uint32_t)__shfl((int)ksw[MX ? j / 4 : 0], 16 * (j % 4) + col);
       ks = g < kNG ? (int)((word >> (8 * g)) & 0xFFu) : 127;
     }
 #pragma unroll
@@ -238,7 +287,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     // canonical +0 for a zero score; an absent page scores -inf
     const float v = page_ok[j] ? part + 0.0f : -__builtin_inff();
     if (g == 0) my_sc[j * kSub + col] = v;
-    bad_page = bad_page || (w0 + j * kSub < L && !page_ok[j]);
+    if (!CAND) bad_page = bad_page || (w0 + j * kSub < L && !page_ok[j]);
   }
   // LDS accesses of one wave complete in order; the fence keeps the
   // compiler from moving the reads above the writes of other lanes
@@ -247,26 +296,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
 #pragma unroll
   for (int h = 0; h < kSpan / 64; ++h) {
     const int i = 64 * h + lane;
-    if (w0 + i < L) out[w0 + i] = my_sc[i];
+    if (w0 + i < S) out[w0 + i] = my_sc[i];
   }
   // The Top-K's summary of this wave's segment (its m largest keys; the
   // wave spans exactly one segment)
   static_assert(kSpan == kSumSeg, "one summary segment per wave");
-  if (a.tw.summ && w0 < L && topk_split_row(L, a.topk_K)) {  // wave-uniform
-    const uint32_t ka = w0 + lane < L ? score_key(my_sc[lane]) : 0u;
-    const uint32_t kb = w0 + 64 + lane < L ? score_key(my_sc[64 + lane]) : 0u;
-    const int m = topk_sum_m(L);
+  if (a.tw.summ && w0 < S && topk_split_row(S, a.topk_K)) {  // wave-uniform
+    const uint32_t ka = w0 + lane < S ? score_key(my_sc[lane]) : 0u;
+    const uint32_t kb = w0 + 64 + lane < S ? score_key(my_sc[64 + lane]) : 0u;
+    const int m = topk_sum_m(S);
     const uint32_t mine = segment_top(ka, kb, m);
     if (lane < m)
       a.tw.summ[(int64_t)(r - a.row_begin) * kSumMax + (w0 / kSumSeg) * m + lane] = mine;
   }
-  if (bad_page && lane == 0) report(a.err, DSA_DEVERR_BLOCK);
+  if (__builtin_amdgcn_ballot_w64(bad_page || bad_blk) && lane == 0) report(a.err, DSA_DEVERR_BLOCK);
+  if (CAND && __builtin_amdgcn_ballot_w64(bad_pos) && lane == 0) report(a.err, DSA_DEVERR_ROW);
 }
 
 template <int NKP, int HT, bool MX>
 hipError_t launch_t(const IndexerLaunch& a, hipStream_t s) {
   dim3 grid((a.max_len + kTile - 1) / kTile, a.num_rows);
-  indexer_scan_kernel<NKP, HT, MX><<<grid, 256, 0, s>>>(a);
+  if (a.rows.cand)
+    indexer_scan_kernel<NKP, HT, MX, true><<<grid, 256, 0, s>>>(a);
+  else
+    indexer_scan_kernel<NKP, HT, MX, false><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

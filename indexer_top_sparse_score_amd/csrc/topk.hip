@@ -308,6 +308,18 @@ struct Out {
   int64_t kv_blocks, kv_block_stride, kv_row_stride;
   uint32_t* err;
   uint32_t* pos;       // LDS staging of the selection, or NULL
+  // Candidate rows: the selection is over slots of the row's list, written
+  // as their positions cand[slot] (NULL: slots are positions).  A position
+  // outside the history (0 .. hist-1) is reported and written as 0.
+  const int32_t* cand;
+  int hist;
+  __device__ __forceinline__ int position(int slot) const {
+    if (!cand) return slot;
+    const int p = cand[slot];
+    if (p >= 0 && p < hist) return p;
+    report(err, DSA_DEVERR_ROW);
+    return 0;
+  }
   __device__ __forceinline__ int64_t row_offset(int p, int phys) const {
     if (phys >= 0 && (int64_t)phys < kv_blocks)
       return (int64_t)phys * kv_block_stride + (int64_t)(p & 63) * kv_row_stride;
@@ -324,6 +336,7 @@ struct Out {
       pos[slot] = (uint32_t)p;
       return;
     }
+    p = position(p);
     idx[slot] = p;
     if (roff) roff[slot] = row_offset(p, bt[p >> 6]);
   }
@@ -334,7 +347,7 @@ struct Out {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int slot = (int)threadIdx.x + i * kT;
-      p[i] = slot < K ? (int)pos[slot] : 0;
+      p[i] = slot < K ? position((int)pos[slot]) : 0;
       if (slot < K) idx[slot] = p[i];
     }
     if (!roff) return;
@@ -474,6 +487,8 @@ __device__ __forceinline__ Out make_out(const TopkLaunch& a, int r_local, int b)
   o.kv_row_stride = a.kv.row_stride;
   o.err = a.err;
   o.pos = nullptr;
+  o.cand = nullptr;
+  o.hist = 0;
   return o;
 }
 
@@ -487,9 +502,10 @@ __device__ __forceinline__ void cache_block_table(int L, Out& o, Smem& s) {
   }
 }
 
-// A whole row in one workgroup: every path but the split one.
-__device__ __forceinline__ void row_single(const TopkLaunch& a, int r_local, int L, Out& o,
-                                           Smem& s) {
+// A whole row in one workgroup: every path but the split one.  L: the score
+// row's length (slots), Lh: the history's (whose block ids are cached).
+__device__ __forceinline__ void row_single(const TopkLaunch& a, int r_local, int L, int Lh,
+                                           Out& o, Smem& s) {
   const int tid = threadIdx.x;
   const int K = a.K;
   if (tid == 0 && a.counts) a.counts[r_local] = min(K, L);
@@ -509,7 +525,7 @@ __device__ __forceinline__ void row_single(const TopkLaunch& a, int r_local, int
     select_streamed<false>(sc, L, K, a.vec, o, s);
     return;
   }
-  cache_block_table(L, o, s);
+  cache_block_table(Lh, o, s);
   o.pos = s.hist;
   if (L <= kMaxN)
     select_keys(sc, L, K, a.vec, o, s);
@@ -601,10 +617,15 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
         *reinterpret_cast<const uint4*>(a.tw.summ + (int64_t)r_local * kSumMax + kSumPer * tid);
     sm[0] = v.x; sm[1] = v.y; sm[2] = v.z; sm[3] = v.w;
   }
-  const int L = row_finish(a.rows, ri);
+  const int Lh = row_finish(a.rows, ri);      // history length
+  const int L = row_slots(a.rows, ri, Lh);    // score row length (candidate count)
   Out o = make_out(a, r_local, ri.b_ok ? ri.b : 0);
+  const int32_t* crow =
+      a.rows.cand ? a.rows.cand + (int64_t)(a.row_begin + r_local) * a.rows.n_cand : nullptr;
+  o.cand = crow;
+  o.hist = Lh;
   if (!topk_split_row(L, K)) {
-    if (slice == 0) row_single(a, r_local, L, o, s);
+    if (slice == 0) row_single(a, r_local, L, Lh, o, s);
     return;
   }
   const int S = (L + kTopkSliceLen - 1) / kTopkSliceLen;
@@ -615,12 +636,29 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
   const int p0 = slice * kTopkSliceLen + kRunPer * tid;
   uint32_t k[kRunPer];
   run_scores(sc, p0, L, a.vec, k);
+  // and their positions (candidate rows: the list's entries, checked)
+  int32_t cp[kRunPer];
+  if (crow) {
+    if (a.cvec && p0 + kRunPer <= L) {
+#pragma unroll
+      for (int j = 0; j < kRunPer; j += 4) {
+        const int4 v = *reinterpret_cast<const int4*>(crow + p0 + j);
+        cp[j] = v.x; cp[j + 1] = v.y; cp[j + 2] = v.z; cp[j + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kRunPer; ++j) cp[j] = p0 + j < L ? crow[p0 + j] : 0;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kRunPer; ++j) cp[j] = p0 + j;
+  }
   for (int i = tid; i < kBins; i += kT) s.hist[i] = 0;  // for step a; block_minmax syncs
   if (slice == 0 && tid == 0 && a.counts) a.counts[r_local] = K;
   // the row's block ids for the KV row offsets: loaded now, staged in LDS
   // only by the workgroup that writes the row out
   constexpr int kBtPer = kBtCache / kT;
-  const int nblk = (L + kBlock - 1) / kBlock;
+  const int nblk = (Lh + kBlock - 1) / kBlock;
   const bool bt_cached = o.roff && nblk <= kBtCache;
   int32_t btv[kBtPer];
 #pragma unroll
@@ -669,8 +707,16 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
   }
 
   // b. this slice's keys >= t (t >= 1: positions past L, key 0, never count)
+  bool bad_pos = false;
 #pragma unroll
-  for (int j = 0; j < kRunPer; ++j) k[j] = p0 + j < L ? score_key(__uint_as_float(k[j])) : 0u;
+  for (int j = 0; j < kRunPer; ++j) {
+    k[j] = p0 + j < L ? score_key(__uint_as_float(k[j])) : 0u;
+    if (crow && p0 + j < L && (cp[j] < 0 || cp[j] >= Lh)) {  // a list entry outside the history
+      bad_pos = true;
+      cp[j] = 0;
+    }
+  }
+  if (bad_pos) report(a.err, DSA_DEVERR_ROW);
   uint32_t c = 0;
 #pragma unroll
   for (int j = 0; j < kRunPer; ++j) c += k[j] >= t ? 1u : 0u;
@@ -682,8 +728,8 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
     for (int j = 0; j < kRunPer; ++j)
       if (k[j] >= t) {
         store_shared(a.tw.ckey + seg + at, k[j]);
-        store_shared(reinterpret_cast<uint32_t*>(a.tw.cpos) + seg + at, (uint32_t)(p0 + j));
-        if (at < (uint32_t)kMaxKeys) s.cp[at] = p0 + j;  // for the KV prefetch
+        store_shared(reinterpret_cast<uint32_t*>(a.tw.cpos) + seg + at, (uint32_t)cp[j]);
+        if (at < (uint32_t)kMaxKeys) s.cp[at] = cp[j];  // for the KV prefetch
         ++at;
       }
     if (tid == 0) store_shared(a.tw.ccount + r_local * kTopkSlices + slice, n_slice);
@@ -774,6 +820,7 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
     uint32_t need = (uint32_t)K;
     __syncthreads();  // the cleared histogram
     const uint32_t T = select_kth<true>(visit, t, kmax, need, s);
+    o.cand = nullptr;  // the segments hold positions already
     uint32_t eq_before = 0, out_before = 0;
     emit_runs<kKeysPer, true, true>(kk, n, [&](int j) { return pp[j]; }, T, need, eq_before,
                                     out_before, o, s);
@@ -790,7 +837,11 @@ __global__ __launch_bounds__(256) void topk_summary_kernel(TopkLaunch a) {
   const int r_local = (int)blockIdx.y;
   if (blockIdx.x == 0 && threadIdx.x == 0) a.tw.arrive[r_local] = 0;
   if (!resolve_row(a.rows, a.row_begin + r_local, b, p)) return;
-  const int L = p + 1;
+  int L = p + 1;
+  if (a.rows.cand) {  // the score row is the candidate list
+    const int c = a.rows.cand_len[a.row_begin + r_local];
+    L = c < 0 ? 0 : c > a.rows.n_cand ? a.rows.n_cand : c;
+  }
   if (!topk_split_row(L, a.K)) return;
   const int lane = (int)(threadIdx.x & 63);
   const int seg = (int)(blockIdx.x * 4 + (threadIdx.x >> 6));

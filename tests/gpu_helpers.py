@@ -24,15 +24,20 @@ def kv_and_v(batch):
 
 
 def gpu_scores(batch):
-    """dsa_indexer_scores into a NaN-filled [rows, 64 * max_blocks] buffer."""
+    """dsa_indexer_scores into a NaN-filled [rows, ld] buffer (ld: the longest
+    history, or the candidate lists' length)."""
     prob = B.problem_for_batch(batch)
-    ld = 64 * batch.max_blocks
+    ld = score_ld(batch)
     scores = torch.full((batch.rows, ld), float("nan"), dtype=torch.float32, device="cuda")
     ws = B.workspace(prob, B.DSA_OP_INDEXER_SCORES)
     B.dsa_indexer_scores(prob, batch.qI, batch.w, batch.kI, scores, ws)
     torch.cuda.synchronize()
     assert B.device_errors(ws) == 0
     return scores
+
+
+def score_ld(batch):
+    return batch.cand.shape[1] if batch.cand is not None else 64 * batch.max_blocks
 
 
 def gpu_topk(batch, scores):
@@ -83,13 +88,15 @@ def np_(t):
 
 
 def check_scores_exact(gpu_scores_t, orc, rows_pos):
+    # the oracle's row holds one score per position (or per candidate)
     g = np_(gpu_scores_t)
-    for i, (_, p) in enumerate(rows_pos):
+    for i, _ in enumerate(rows_pos):
         want = orc["scores"][i]
-        got = g[i, :p + 1]
+        n = len(want)
+        got = g[i, :n]
         assert (got.view(np.uint32) == want.view(np.uint32)).all(), \
             f"row {i}: {int((got != want).sum())} score mismatches"
-        assert np.isnan(g[i, p + 1:]).all(), f"row {i}: wrote past its history"
+        assert np.isnan(g[i, n:]).all(), f"row {i}: wrote past its score row"
 
 
 def score_bound(arr, i, p):

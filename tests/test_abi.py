@@ -123,6 +123,21 @@ def test_indexer_format_rejections():
     assert ws_size(prob(**mx), B.DSA_OP_DECODE_STEP) > 0
 
 
+def test_candidate_list_rejections():
+    # candidates need both arrays, a row length >= 1, 16-byte aligned lists;
+    # the score rows are then n_cand long
+    cand = dict(cand=FAKE + (3 << 30), cand_len=FAKE + (3 << 30) + 4096, n_cand=16384)
+    assert call_scores(prob(num_rows=0, **cand), ld=16384) == B.DSA_OK
+    assert call_scores(prob(**cand), ld=16383) == B.DSA_ERR_INVALID        # ld < n_cand
+    assert call_scores(prob(cand=FAKE), ld=16384) == B.DSA_ERR_INVALID     # no cand_len
+    assert call_scores(prob(cand_len=FAKE), ld=16384) == B.DSA_ERR_INVALID # no cand
+    assert call_scores(prob(**{**cand, "n_cand": 0})) == B.DSA_ERR_INVALID
+    assert call_scores(prob(**{**cand, "cand": FAKE + 4}), ld=16384) == B.DSA_ERR_INVALID
+    small = ws_size(prob(**cand), B.DSA_OP_TOPK)
+    assert 0 < small < ws_size(prob(), B.DSA_OP_TOPK)  # 16384 slots, not 131072 positions
+    assert ws_size(prob(**cand), B.DSA_OP_DECODE_STEP) > 0
+
+
 def test_topk_rejections():
     def call(p, scores=FAKE, ld=131072, idx=FAKE, counts=None, ws=FAKE, nbytes=256):
         return B.raw_call("dsa_topk", ctypes.byref(p), ctypes.c_void_p(scores),

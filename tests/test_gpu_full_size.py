@@ -93,3 +93,19 @@ def test_full_size_mxfp8_indexer_bench_shape():
     assert (np_(res["counts"]) == orc["counts"]).all()
     assert (np_(res["indices"]) == orc["indices"]).all()
     check_attention(res["out"], res["lse"], orc["out"], orc["lse"])
+
+
+def test_full_size_candidates_bench_shape():
+    # the 4 x 128k decode step scoring 16384 candidate positions per row
+    # (the candidate-restricted indexer), integer mode: every row's indices
+    # bit-exact against the oracle, attention within tolerance
+    wl = CONFIGS[BENCH_WORKLOAD].with_(n_cand=16384)
+    say(f"full size {BENCH_WORKLOAD}: 16384 candidates per row, integer mode, seed {wl.seed}")
+    batch = make_batch(wl, device="cuda", seed=wl.seed, mode="int")
+    res = gpu_decode(batch)
+    _check_every_row(batch, res)
+    rows = list(range(batch.rows))
+    orc = run_oracle(oracle_arrays(batch, rows=rows), keep_scores=False)
+    assert (np_(res["counts"]) == orc["counts"]).all()
+    assert (np_(res["indices"]) == orc["indices"]).all()
+    check_attention(res["out"], res["lse"], orc["out"], orc["lse"])

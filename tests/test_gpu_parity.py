@@ -13,7 +13,8 @@ import torch
 
 import oracle
 from tests.gpu_helpers import (RECALL_MIN, check_attention, check_scores_exact, gpu_attn,
-                               gpu_decode, gpu_scores, gpu_topk, np_, recall, say, score_bound)
+                               gpu_decode, gpu_scores, gpu_topk, np_, recall, say, score_bound,
+                               score_ld)
 from tests.helpers import run_oracle
 from workloads import CONFIGS, make_batch, oracle_arrays, row_positions, small_workload
 
@@ -41,6 +42,14 @@ CASES = {
     "mla_mx_int": dict(lengths=LENGTHS, mode="int", indexer_fmt="mxfp8", **MLA),
     "h48_d64_mx": dict(lengths=[777, 2500], mode="int", indexer_fmt="mxfp8",
                        **{**MLA, "H_I": 48, "D_I": 64, "H_q": 80}),
+    # candidate-restricted rows: short lists (one workgroup per row; rows up
+    # to 1500 positions take every position), lists long enough to split
+    # (a length that is not a multiple of 4, then one that is, with MXFP8)
+    "mla_cand_int": dict(lengths=LENGTHS, mode="int", n_cand=1500, **MLA),
+    "mla_cand_split": dict(lengths=[20000, 70000, 131072], mode="int", n_cand=17001, **MLA),
+    "mla_mx_cand": dict(lengths=[5000, 40000], mode="int", indexer_fmt="mxfp8", n_cand=16384,
+                        **MLA),
+    "tiny_cand": dict(lengths=[1, 50, 64, 1024, 3000], mode="int", n_cand=700, **TINY),
 }
 
 
@@ -82,7 +91,7 @@ def test_topk_exact_on_oracle_scores(name):
     batch = _batch(name, mode="gauss", seed=23)
     arr = oracle_arrays(batch)
     orc = run_oracle(arr)
-    ld = 64 * batch.max_blocks
+    ld = score_ld(batch)
     sc = np.full((batch.rows, ld), np.nan, np.float32)
     for i, s in enumerate(orc["scores"]):
         sc[i, :len(s)] = s
@@ -163,7 +172,8 @@ def test_sparse_attn_skips_padding_and_handles_empty_rows():
 
 
 @pytest.mark.parametrize("name", ["mla_int", "mla_int_shuffled", "tiny_int", "mla_int_k100",
-                                  "mla_sepv", "mla_int_grouped", "mla_mx_int"])
+                                  "mla_sepv", "mla_int_grouped", "mla_mx_int", "mla_cand_int",
+                                  "mla_cand_split", "mla_mx_cand", "tiny_cand"])
 def test_decode_step_integer_mode(name):
     batch = _batch(name, seed=27)
     arr = oracle_arrays(batch)
