@@ -772,7 +772,7 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
   // Thread t reads entries kKeysPer (t mod P) .. +kKeysPer-1 of slice t / P,
   // P = kT / S threads per slice, together with the counts (no round trip
   // between them); in thread order that is position order.  A slice with
-  // more than P kKeysPer candidates sends the row to the general path.
+  // more than P kKeysPer candidates makes every thread reload densely.
   const int P = kT / S;
   const int my_slice = tid / P;
   const int e0 = kKeysPer * (tid % P);
@@ -804,12 +804,41 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
   const uint32_t cnt_lane = lane < S ? a.tw.ccount[r_local * kTopkSlices + lane] : 0u;
   const uint32_t n_tot = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan(cnt_lane, 0u, Add()), 63);
   const uint32_t c_max = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan(cnt_lane, 0u, Max()), 63);
-  if (n_tot > (uint32_t)kMaxKeys || c_max > (uint32_t)(P * kKeysPer)) {
+  if (n_tot > (uint32_t)kMaxKeys) {
     // heavy ties at t: the general path
     select_streamed<true>(sc, L, K, a.vec, o, s);
   } else {
-    const uint32_t c_mine = (uint32_t)__shfl((int)cnt_lane, my_slice & 63);
-    const int n = my_slice < S ? max(0, min(kKeysPer, (int)c_mine - e0)) : 0;
+    int n;
+    if (c_max <= (uint32_t)(P * kKeysPer)) {  // every slice fit its share: loaded above
+      const uint32_t c_mine = (uint32_t)__shfl((int)cnt_lane, my_slice & 63);
+      n = my_slice < S ? max(0, min(kKeysPer, (int)c_mine - e0)) : 0;
+    } else {
+      // A slice overflowed its share (the row's top keys cluster): reload
+      // densely.  Thread t takes entries kKeysPer t .. +kKeysPer-1 of the
+      // slices' lists laid end to end (still position order), finding each
+      // entry's slice from the slices' running totals in LDS -- one more
+      // round trip, on this path only.
+      const uint32_t incl = wave_scan(cnt_lane, 0u, Add());  // lanes >= S: n_tot
+      uint32_t* ends = s.wsum;  // ends[q] = entries in slices 0 .. q
+      if (tid < kTopkSlices) ends[tid] = incl;
+      __syncthreads();
+      const int g0 = kKeysPer * tid;
+      n = max(0, min(kKeysPer, (int)n_tot - g0));
+      int q = 0;
+      for (int step = kTopkSlices / 2; step >= 1; step >>= 1)  // last q with ends[q-1] <= g0
+        if (q + step < kTopkSlices && (int)ends[q + step - 1] <= g0) q += step;
+#pragma unroll
+      for (int j = 0; j < kKeysPer; ++j) {
+        const int e = g0 + j;
+        if (j < n) {
+          while ((int)ends[q] <= e) ++q;
+          const int64_t at = (int64_t)r_local * a.tw.cstride + (int64_t)q * kTopkSliceLen +
+                             (e - (q > 0 ? (int)ends[q - 1] : 0));
+          kk[j] = a.tw.ckey[at];
+          pp[j] = a.tw.cpos[at];
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < kKeysPer; ++j) kk[j] = j < n ? kk[j] : 0u;
     auto visit = [&](auto f) {

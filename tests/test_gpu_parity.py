@@ -105,7 +105,7 @@ def test_topk_ties_and_special_values():
     # (the last rows are long enough to group positions, and their ties or
     # NaNs send them down the streamed path)
     wl = small_workload("ties", lengths=[5000, 5000, 5000, 5000, 3000, 2049, 20000, 40000,
-                                         40000, 9000, 131072], **MLA)
+                                         40000, 9000, 131072, 131072, 70000], **MLA)
     batch = make_batch(wl, device="cuda", seed=24)
     rng = np.random.default_rng(24)
     ld = 64 * batch.max_blocks
@@ -127,6 +127,15 @@ def test_topk_ties_and_special_values():
     # 16 slices of 1024 groups of 8: scores on a 1/64 grid tie some 80 ways at
     # the threshold, so the budget of keys equal to T spans several slices
     sc[10, :L[10]] = np.round(rng.standard_normal(L[10]) * 64) / 64
+    # the best keys packed into a few thousand recent positions: one slice
+    # holds far more candidates than its share, and the finish reloads
+    # them densely
+    x = rng.standard_normal(L[11]).astype(np.float32)
+    x[-3000:] += 10.0
+    sc[11, :L[11]] = x
+    x = rng.standard_normal(L[12]).astype(np.float32)
+    x[30000:32500] += 6.0
+    sc[12, :L[12]] = x
     idx, cnt = gpu_topk(batch, torch.from_numpy(sc).cuda())
     for i in range(batch.rows):
         want, n = oracle.topk_row(sc[i, :L[i]], wl.K)
