@@ -102,8 +102,9 @@ def test_topk_exact_on_oracle_scores(name):
 
 def test_topk_ties_and_special_values():
     # heavy ties, signed zeros, infinities, all-equal rows: exact vs the oracle
-    # (the last rows are long enough to group positions, and their ties or
-    # NaNs send them down the streamed path)
+    # (rows of 16384 positions and more split over slices unless their ties
+    # or NaNs send them down the streamed path; shorter rows select on their
+    # keys in one workgroup)
     wl = small_workload("ties", lengths=[5000, 5000, 5000, 5000, 3000, 2049, 20000, 40000,
                                          40000, 9000, 131072, 131072, 70000], **MLA)
     batch = make_batch(wl, device="cuda", seed=24)
@@ -117,14 +118,14 @@ def test_topk_ties_and_special_values():
     sc[3, :L[3]] = rng.choice(np.array([-np.inf, np.inf, 5.0, -2.0], np.float32), L[3])
     sc[4, :L[4]] = rng.standard_normal(L[4]).astype(np.float32) * 1e-30  # subnormal-ish range
     sc[5, :L[5]] = -np.arange(L[5], dtype=np.float32)              # K+1 distinct, descending
-    sc[6, :L[6]] = rng.integers(0, 3, L[6])                        # 3 distinct values, G = 4
-    sc[7, :L[7]] = 1.5                                              # all equal, G = 8
+    sc[6, :L[6]] = rng.integers(0, 3, L[6])                        # 3 distinct values: streamed
+    sc[7, :L[7]] = 1.5                                              # all equal: streamed
     sc[8, :L[8]] = np.where(rng.random(L[8]) < 0.99, np.nan,       # mostly NaN: t = 0
                             rng.standard_normal(L[8])).astype(np.float32)
     x = rng.standard_normal(L[9]).astype(np.float32)                # a few exact ties near
-    x[rng.choice(L[9], 300, replace=False)] = np.sort(x)[-2100]     # the threshold, G = 2
+    x[rng.choice(L[9], 300, replace=False)] = np.sort(x)[-2100]     # the threshold (one workgroup)
     sc[9, :L[9]] = x
-    # 16 slices of 1024 groups of 8: scores on a 1/64 grid tie some 80 ways at
+    # 32 slices of 4096 positions: scores on a 1/64 grid tie some 80 ways at
     # the threshold, so the budget of keys equal to T spans several slices
     sc[10, :L[10]] = np.round(rng.standard_normal(L[10]) * 64) / 64
     # the best keys packed into a few thousand recent positions: one slice
@@ -219,6 +220,21 @@ def test_decode_step_prefill_rows():
     arr = oracle_arrays(batch)
     orc = run_oracle(arr, keep_scores=False)
     res = gpu_decode(batch)
+    assert (np_(res["indices"]) == orc["indices"]).all()
+    check_attention(res["out"], res["lse"], orc["out"], orc["lse"])
+
+
+@pytest.mark.parametrize("table", ["identity", "shuffled"])
+def test_decode_step_prefill_rows_with_candidates(table):
+    # chunked-prefill rows (one sequence, 48 consecutive positions) each with
+    # its own candidate list, through a shuffled table too
+    wl = small_workload("prefill_cand", lengths=[24000], prefill_rows=48, mode="int",
+                        n_cand=16500, table=table, **MLA)
+    batch = make_batch(wl, device="cuda", seed=31)
+    arr = oracle_arrays(batch)
+    orc = run_oracle(arr, keep_scores=False)
+    res = gpu_decode(batch)
+    assert (np_(res["counts"]) == orc["counts"]).all()
     assert (np_(res["indices"]) == orc["indices"]).all()
     check_attention(res["out"], res["lse"], orc["out"], orc["lse"])
 
