@@ -18,6 +18,9 @@ cpu_baseline  the oracle timed on the host on a bounded sample of rows
 mxfp8_indexer  the same workload with MXFP8 indexer operands (one E8M0 scale
            per 32 dims): the fused step and the indexer scan alone, timed the
            same way over their own rotating input sets (--no-mxfp8 skips it)
+step_us_spread  p10 / p50 / p90 of the step time over graph replays timed one by one
+stream_launch  the same steps launched one by one on the stream (no graph)
+read_reference a library streaming read (torch.sum over 1 GiB) as a reference for HBM reads
 candidate_indexer  the same workload with a candidate-restricted indexer
            (16384 candidate positions per row): the fused step and the scan
            alone, timed the same way (--no-cand skips it)
@@ -241,6 +244,7 @@ def main():
         "wall_s": round(wall, 4),
     }
 
+    result.update(spread_legs(args, graphs, rotate, step, stream, rows))
     if not args.no_mxfp8:
         result["mxfp8_indexer"] = mxfp8_leg(args, wl, lengths, stream, rotate_bytes=ib)
     if not args.no_cand:
@@ -316,6 +320,51 @@ def mxfp8_leg(args, wl, lengths, stream, rotate_bytes):
             "tokens_per_s": round(rows / (step_us * 1e-6), 1),
             "indexer_avg_launch_us": round(idx_us, 3), "indexer_bytes_per_launch": ib,
             "indexer_achieved": round(achieved, 1), "indexer_frac": round(achieved / HBM_PEAK_GBS, 4)}
+
+
+def spread_legs(args, graphs, rotate, step, stream, rows):
+    """After the timed region: the spread of the step time (graph replays
+    timed one by one with HIP events, per step = replay / steps per replay),
+    the same steps launched one by one on the stream, and a plain streaming
+    read (torch.sum over 1 GiB) as a reference ceiling for HBM reads."""
+    import torch
+    out = {}
+    if graphs:
+        n = max(8, args.steps // rotate)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+        with torch.cuda.stream(stream):
+            for k in range(n):
+                evs[2 * k].record(stream)
+                graphs[rotate].replay()
+                evs[2 * k + 1].record(stream)
+        torch.cuda.synchronize()
+        per = sorted(1e3 * evs[2 * k].elapsed_time(evs[2 * k + 1]) / rotate for k in range(n))
+        pick = lambda q: round(per[min(n - 1, int(q * n))], 3)
+        out["step_us_spread"] = {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9),
+                                 "replays": n, "steps_per_replay": rotate}
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            step(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / args.steps
+    out["stream_launch"] = {"step_us": round(us, 3), "tokens_per_s": round(rows / (us * 1e-6), 1)}
+    buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(stream):
+        torch.sum(buf)
+        e0.record(stream)
+        for _ in range(5):
+            torch.sum(buf)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    rd = 5 * buf.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    out["read_reference"] = {"kernel": "torch.sum over 1 GiB of float32", "gbs": round(rd, 1)}
+    del buf
+    return out
 
 
 def cand_bytes(wl, lengths, n_cand):
