@@ -149,20 +149,28 @@ __device__ __forceinline__ int lane_prefix(uint64_t mask) {
 // the front end before these run.
 
 // ------------------------------------------------------ Top-K work area
-// The Top-K's pre-selection.  A row's positions are cut into segments of
-// kSumSeg (one indexer wave's span); the m = topk_sum_m(L) largest keys of
-// each segment form the row's summary, at most kSumMax keys.  The summary's
-// keys sit at distinct positions, so its K-th largest is a lower bound on
-// the row's K-th largest score; the segments' top keys hold nearly all of
-// the row's top K, so the bound is close.  With at least 128 segments
-// (topk_split_row) the summary holds at least 2048 >= K keys.  The fused
-// indexer and the standalone summary pass call the same functions, so they
-// agree on every row.
-constexpr int kSumSeg = 128;            // positions per segment
+// The Top-K's pre-selection.  A row's positions are cut into segments of G
+// = topk_sum_seg(L) positions (16 to 128, at most 1024 segments up to
+// 131072 positions); the m = topk_sum_m(L) largest keys of each segment
+// form the row's summary, between 2048 and kSumMax keys for the rows that
+// use it (topk_split_row).  The summary's keys sit at distinct positions,
+// so its K-th largest is a lower bound on the row's K-th largest score;
+// with about two summary keys per row key kept, and about two kept keys per
+// segment, the segments' top keys hold nearly all of the row's top K and
+// the bound is close.  The fused indexer and the standalone summary pass
+// call the same functions, so they agree on every row.
+constexpr int kSumSpan = 128;           // positions per indexer wave (one or more segments)
+constexpr int kSumSegs = 1024;          // segments per row, at most (up to 131072 positions)
 constexpr int kSumMax = 4096;           // summary keys per row, at most
-constexpr int kSumCap = 16;             // keys per segment, at most
+constexpr int kSumCap = 8;              // keys per segment, at most
+__host__ __device__ inline int topk_sum_seg(int L) {
+  int G = 16;
+  while (G < kSumSpan && (L + G - 1) / G > kSumSegs) G <<= 1;
+  return G;
+}
 __host__ __device__ inline int topk_sum_m(int L) {
-  const int nseg = (L + kSumSeg - 1) / kSumSeg;
+  const int G = topk_sum_seg(L);
+  const int nseg = (L + G - 1) / G;
   if (nseg <= 0) return 0;
   const int m = kSumMax / nseg;
   return m < kSumCap ? m : kSumCap;
@@ -170,43 +178,80 @@ __host__ __device__ inline int topk_sum_m(int L) {
 constexpr int kTopkSlices = 32;         // workgroups per row, at most
 constexpr int kTopkSliceLen = 4096;     // positions per slice
 constexpr int kTopkSplitMaxK = 2048;
-// Rows that the Top-K spreads over slices (and that get a summary).
+// Rows that the Top-K spreads over slices (and that get a summary): at
+// least 512 segments of m >= 4 keys, so more than 2048 >= K summary keys.
 __host__ __device__ inline bool topk_split_row(int L, int K) {
-  return K <= kTopkSplitMaxK && L >= 128 * kSumSeg && L <= kTopkSlices * kTopkSliceLen;
+  return K <= kTopkSplitMaxK && L >= 16384 && L <= kTopkSlices * kTopkSliceLen;
 }
 
-// Maximum of an unsigned value over the 64 lanes, in every lane.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+// Maximum of an unsigned value over aligned groups of G lanes (16, 32 or
+// 64, wave-uniform), in every lane of the group.
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t x, int G) {
   x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
   x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
   x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));  // row_half_mirror
   x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false));  // row_mirror
-  auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  x = max((uint32_t)p[0], (uint32_t)p[1]);
-  p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  return max((uint32_t)p[0], (uint32_t)p[1]);
+  if (G >= 32) {
+    const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = max((uint32_t)p[0], (uint32_t)p[1]);
+  }
+  if (G >= 64) {
+    const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    x = max((uint32_t)p[0], (uint32_t)p[1]);
+  }
+  return x;
 }
 
-// The m largest of the wave's 128 keys (two per lane), with multiplicity:
-// m rounds of a wave maximum, each taking out one instance (the lowest lane
-// that holds it).  Lane i < m returns the (i+1)-th largest.  m is
-// wave-uniform.
-__device__ __forceinline__ uint32_t segment_top(uint32_t ka, uint32_t kb, int m) {
+// The m largest keys of each segment of G positions of a wave's 128 (key a
+// of lane l: position l, key b: position 64 + l), with multiplicity: m
+// rounds of a group maximum, each taking out one instance (the lowest lane
+// of the group that holds it).  G = 128: one segment over both keys, lane
+// i < m gets its (i+1)-th largest in out_a.  G <= 64: segments of G lanes
+// in each key; lane G s + i, i < m, gets segment s's (i+1)-th largest of
+// the a keys in out_a and of the b keys in out_b.  G and m are wave-uniform.
+__device__ __forceinline__ void segment_top(uint32_t ka, uint32_t kb, int m, int G, uint32_t& out_a,
+                                            uint32_t& out_b) {
   const int lane = (int)(threadIdx.x & 63);
-  uint32_t mine = 0;
-  for (int i = 0; i < m; ++i) {
-    const uint32_t v = max(ka, kb);
-    const uint32_t M = wave_max_u32(v);
-    const uint64_t hit = __ballot(v == M);
-    if (lane == (int)__builtin_ctzll(hit)) {
-      if (ka == M)
-        ka = 0u;
-      else
-        kb = 0u;
+  out_a = out_b = 0u;
+  if (G >= kSumSpan) {
+    for (int i = 0; i < m; ++i) {
+      const uint32_t v = max(ka, kb);
+      const uint32_t M = group_max_u32(v, 64);
+      const uint64_t hit = __ballot(v == M);
+      if (lane == (int)__builtin_ctzll(hit)) {
+        if (ka == M)
+          ka = 0u;
+        else
+          kb = 0u;
+      }
+      out_a = lane == i ? M : out_a;
     }
-    mine = lane == i ? M : mine;
+    return;
   }
-  return mine;
+  const int base = lane & ~(G - 1);
+  const uint64_t gmask = G == 64 ? ~0ull : ((1ull << G) - 1ull) << base;
+  for (int i = 0; i < m; ++i) {
+    const uint32_t Ma = group_max_u32(ka, G), Mb = group_max_u32(kb, G);
+    const uint64_t ha = __ballot(ka == Ma) & gmask, hb = __ballot(kb == Mb) & gmask;
+    if (lane == (int)__builtin_ctzll(ha)) ka = 0u;
+    if (lane == (int)__builtin_ctzll(hb)) kb = 0u;
+    out_a = lane - base == i ? Ma : out_a;
+    out_b = lane - base == i ? Mb : out_b;
+  }
+}
+
+// Writes a wave's summary keys (segment_top's results for the 128 positions
+// from w0, of a score row of S positions) into the row's summary `summ`.
+__device__ __forceinline__ void store_segment_top(uint32_t* summ, int w0, int S, int m, int G,
+                                                  uint32_t out_a, uint32_t out_b) {
+  const int lane = (int)(threadIdx.x & 63);
+  if (G >= kSumSpan) {
+    if (lane < m && w0 < S) summ[(w0 / G) * m + lane] = out_a;
+    return;
+  }
+  const int i = lane & (G - 1), s_lane = lane / G;
+  if (i < m && w0 + G * s_lane < S) summ[(w0 / G + s_lane) * m + i] = out_a;
+  if (i < m && w0 + 64 + G * s_lane < S) summ[((w0 + 64) / G + s_lane) * m + i] = out_b;
 }
 
 // The Top-K's work area, carved from the caller's workspace:

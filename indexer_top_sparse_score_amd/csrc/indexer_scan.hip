@@ -298,16 +298,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     const int i = 64 * h + lane;
     if (w0 + i < S) out[w0 + i] = my_sc[i];
   }
-  // The Top-K's summary of this wave's segment (its m largest keys; the
-  // wave spans exactly one segment)
-  static_assert(kSpan == kSumSeg, "one summary segment per wave");
+  // The Top-K's summary of this wave's positions (the m largest keys of
+  // each of its segments)
+  static_assert(kSpan == kSumSpan, "the summary's wave span");
   if (a.tw.summ && w0 < S && topk_split_row(S, a.topk_K)) {  // wave-uniform
     const uint32_t ka = w0 + lane < S ? score_key(my_sc[lane]) : 0u;
     const uint32_t kb = w0 + 64 + lane < S ? score_key(my_sc[64 + lane]) : 0u;
-    const int m = topk_sum_m(S);
-    const uint32_t mine = segment_top(ka, kb, m);
-    if (lane < m)
-      a.tw.summ[(int64_t)(r - a.row_begin) * kSumMax + (w0 / kSumSeg) * m + lane] = mine;
+    const int m = topk_sum_m(S), G = topk_sum_seg(S);
+    uint32_t out_a, out_b;
+    segment_top(ka, kb, m, G, out_a, out_b);
+    store_segment_top(a.tw.summ + (int64_t)(r - a.row_begin) * kSumMax, w0, S, m, G, out_a, out_b);
   }
   if (__builtin_amdgcn_ballot_w64(bad_page || bad_blk) && lane == 0) report(a.err, DSA_DEVERR_BLOCK);
   if (CAND && __builtin_amdgcn_ballot_w64(bad_pos) && lane == 0) report(a.err, DSA_DEVERR_ROW);

@@ -9,8 +9,9 @@
 // the selection is exact.  Rows of 16384 to 131072 positions (K <= 2048,
 // topk_split_row) are spread over up to 32 workgroups, one per slice of 4096
 // positions, and pre-select on the row's summary: the m largest keys of each
-// 128-position segment (topk_sum_m), written by the fused indexer's epilogue
-// or, for the standalone entry point, by topk_summary_kernel.
+// segment of 16 to 128 positions (topk_sum_seg, topk_sum_m), written by the
+// fused indexer's epilogue or, for the standalone entry point, by
+// topk_summary_kernel.
 //
 //  1. A lower bound t on the row's K-th largest key T: the summary's keys
 //     sit at distinct positions, so its own K-th largest is at most T.  One
@@ -669,7 +670,7 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
 
   // a. t = lower edge of the bin holding the summary's K-th largest key
   //    (key 0, NaN or no position, does not count)
-  const int n_sum = ((L + kSumSeg - 1) / kSumSeg) * topk_sum_m(L);
+  const int n_sum = ((L + topk_sum_seg(L) - 1) / topk_sum_seg(L)) * topk_sum_m(L);
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, n_nz = 0;
 #pragma unroll
   for (int j = 0; j < kSumPer; ++j) {
@@ -859,8 +860,8 @@ __global__ __launch_bounds__(kT) void topk_split_kernel(TopkLaunch a) {
   if (tid == 0) a.tw.arrive[r_local] = 0;
 }
 
-// The summary for a standalone Top-K call: one wave per 128-position
-// segment keeps its m largest keys (segment_top).
+// The summary for a standalone Top-K call: one wave per 128 positions keeps
+// the m largest keys of each of their segments (segment_top).
 __global__ __launch_bounds__(256) void topk_summary_kernel(TopkLaunch a) {
   int b, p;
   const int r_local = (int)blockIdx.y;
@@ -874,14 +875,15 @@ __global__ __launch_bounds__(256) void topk_summary_kernel(TopkLaunch a) {
   if (!topk_split_row(L, a.K)) return;
   const int lane = (int)(threadIdx.x & 63);
   const int seg = (int)(blockIdx.x * 4 + (threadIdx.x >> 6));
-  const int w0 = seg * kSumSeg;
+  const int w0 = seg * kSumSpan;
   if (w0 >= L) return;
   const float* sc = a.scores + (int64_t)r_local * a.ld;
   const uint32_t ka = w0 + lane < L ? score_key(sc[w0 + lane]) : 0u;
   const uint32_t kb = w0 + 64 + lane < L ? score_key(sc[w0 + 64 + lane]) : 0u;
-  const int m = topk_sum_m(L);
-  const uint32_t mine = segment_top(ka, kb, m);
-  if (lane < m) a.tw.summ[(int64_t)r_local * kSumMax + seg * m + lane] = mine;
+  const int m = topk_sum_m(L), G = topk_sum_seg(L);
+  uint32_t out_a, out_b;
+  segment_top(ka, kb, m, G, out_a, out_b);
+  store_segment_top(a.tw.summ + (int64_t)r_local * kSumMax, w0, L, m, G, out_a, out_b);
 }
 
 }  // namespace
@@ -915,7 +917,7 @@ TopkWork topk_work_carve(void* base, int rows, int64_t max_len) {
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
   if (a.num_rows <= 0) return hipSuccess;
   if (a.prep) {  // the rows' summaries (and the arrival counters cleared)
-    const int64_t segs = (a.max_len + kSumSeg - 1) / kSumSeg;
+    const int64_t segs = (a.max_len + kSumSpan - 1) / kSumSpan;
     topk_summary_kernel<<<dim3((unsigned)((segs + 3) / 4), a.num_rows), 256, 0, s>>>(a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
