@@ -150,11 +150,12 @@ __device__ __forceinline__ int lane_prefix(uint64_t mask) {
 
 // ------------------------------------------------------ Top-K work area
 // The Top-K's pre-selection.  A row's positions are cut into segments of G
-// = topk_sum_seg(L) positions (16 to 128, at most 1024 segments up to
+// = topk_sum_seg(L) positions (32 to 128, at most 1024 segments up to
 // 131072 positions); the m = topk_sum_m(L) largest keys of each segment
-// form the row's summary, between 2048 and kSumMax keys for the rows that
-// use it (topk_split_row).  The summary's keys sit at distinct positions,
-// so its K-th largest is a lower bound on the row's K-th largest score;
+// form the row's summary, 3072 to kSumMax keys for the rows that use it
+// (topk_split_row: more than 16384 positions, so more than 512 segments).
+// The summary's keys sit at distinct positions, so its K-th largest is a
+// lower bound on the row's K-th largest score;
 // with about two summary keys per row key kept, and about two kept keys per
 // segment, the segments' top keys hold nearly all of the row's top K and
 // the bound is close.  The fused indexer and the standalone summary pass
@@ -164,7 +165,7 @@ constexpr int kSumSegs = 1024;          // segments per row, at most (up to 1310
 constexpr int kSumMax = 4096;           // summary keys per row, at most
 constexpr int kSumCap = 8;              // keys per segment, at most
 __host__ __device__ inline int topk_sum_seg(int L) {
-  int G = 16;
+  int G = 32;
   while (G < kSumSpan && (L + G - 1) / G > kSumSegs) G <<= 1;
   return G;
 }
@@ -178,10 +179,11 @@ __host__ __device__ inline int topk_sum_m(int L) {
 constexpr int kTopkSlices = 32;         // workgroups per row, at most
 constexpr int kTopkSliceLen = 4096;     // positions per slice
 constexpr int kTopkSplitMaxK = 2048;
-// Rows that the Top-K spreads over slices (and that get a summary): at
-// least 512 segments of m >= 4 keys, so more than 2048 >= K summary keys.
+// Rows that the Top-K spreads over slices (and that get a summary).  Rows
+// of up to 16384 positions are faster in one workgroup, which holds 16 keys
+// per thread.
 __host__ __device__ inline bool topk_split_row(int L, int K) {
-  return K <= kTopkSplitMaxK && L >= 16384 && L <= kTopkSlices * kTopkSliceLen;
+  return K <= kTopkSplitMaxK && L > 16384 && L <= kTopkSlices * kTopkSliceLen;
 }
 
 // Maximum of an unsigned value over aligned groups of G lanes (16, 32 or

@@ -6,10 +6,10 @@
 // the kept positions are written in ascending order, -1 pads to K.
 //
 // Scores are compared through an order-preserving 32-bit key (score_key);
-// the selection is exact.  Rows of 16384 to 131072 positions (K <= 2048,
+// the selection is exact.  Rows of 16385 to 131072 positions (K <= 2048,
 // topk_split_row) are spread over up to 32 workgroups, one per slice of 4096
 // positions, and pre-select on the row's summary: the m largest keys of each
-// segment of 16 to 128 positions (topk_sum_seg, topk_sum_m), written by the
+// segment of 32 to 128 positions (topk_sum_seg, topk_sum_m), written by the
 // fused indexer's epilogue or, for the standalone entry point, by
 // topk_summary_kernel.
 //

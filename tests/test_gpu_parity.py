@@ -36,8 +36,10 @@ CASES = {
     "h48_d64": dict(lengths=[777, 2500], mode="int", **{**MLA, "H_I": 48, "D_I": 64, "H_q": 80}),
     # 576/512 with a separate V cache (not the latent layout)
     "mla_sepv": dict(lengths=[1, 777, 3000], mode="int", latent=False, **MLA),
-    # histories long enough for the Top-K to group positions by 2, 4 and 8
-    "mla_int_grouped": dict(lengths=[9000, 20000, 40000], mode="int", **MLA),
+    # histories on both sides of the Top-K's split threshold (16384 in one
+    # workgroup, 16385 over slices) and long enough for summary segments of
+    # 32 and 64 positions
+    "mla_int_grouped": dict(lengths=[9000, 16384, 16385, 20000, 40000], mode="int", **MLA),
     # MXFP8 indexer operands (one E8M0 scale per 32 dims), both head dims
     "mla_mx_int": dict(lengths=LENGTHS, mode="int", indexer_fmt="mxfp8", **MLA),
     "h48_d64_mx": dict(lengths=[777, 2500], mode="int", indexer_fmt="mxfp8",
@@ -47,7 +49,7 @@ CASES = {
     # (a length that is not a multiple of 4, then one that is, with MXFP8)
     "mla_cand_int": dict(lengths=LENGTHS, mode="int", n_cand=1500, **MLA),
     "mla_cand_split": dict(lengths=[20000, 70000, 131072], mode="int", n_cand=17001, **MLA),
-    "mla_mx_cand": dict(lengths=[5000, 40000], mode="int", indexer_fmt="mxfp8", n_cand=16384,
+    "mla_mx_cand": dict(lengths=[5000, 40000], mode="int", indexer_fmt="mxfp8", n_cand=16388,
                         **MLA),
     "tiny_cand": dict(lengths=[1, 50, 64, 1024, 3000], mode="int", n_cand=700, **TINY),
 }
@@ -102,7 +104,7 @@ def test_topk_exact_on_oracle_scores(name):
 
 def test_topk_ties_and_special_values():
     # heavy ties, signed zeros, infinities, all-equal rows: exact vs the oracle
-    # (rows of 16384 positions and more split over slices unless their ties
+    # (rows of more than 16384 positions split over slices unless their ties
     # or NaNs send them down the streamed path; shorter rows select on their
     # keys in one workgroup)
     wl = small_workload("ties", lengths=[5000, 5000, 5000, 5000, 3000, 2049, 20000, 40000,
