@@ -19,7 +19,8 @@ mxfp8_indexer  the same workload with MXFP8 indexer operands (one E8M0 scale
            per 32 dims): the fused step and the indexer scan alone, timed the
            same way over their own rotating input sets (--no-mxfp8 skips it)
 step_us_spread  p10 / p50 / p90 of the step time over graph replays timed one by one
-stream_launch  the same steps launched one by one on the stream (no graph)
+stream_launch  the same steps launched one by one on the stream (graph_replay
+           instead when --graph 0 times stream launches for the headline)
 read_reference a library streaming read (torch.sum over 1 GiB) as a reference for HBM reads
 candidate_indexer  the same workload with a candidate-restricted indexer
            (16384 candidate positions per row): the fused step and the scan
@@ -47,7 +48,12 @@ def parse():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--mode", default=None, help="int or gauss (default: the workload's)")
     ap.add_argument("--rotate", type=int, default=0, help="input sets (0: auto)")
-    ap.add_argument("--graph", type=int, default=1, help="replay captured HIP graphs")
+    ap.add_argument("--graph", type=int, default=1,
+                    help="time graph replays (1) or stream launches (0); the two run within about "
+                         "1 us per step of each other, but stream launches fall behind when the "
+                         "host is slowed (under a profiler)")
+    ap.add_argument("--no-graph-legs", action="store_true",
+                    help="with --graph 0, capture no graphs (skips step_us_spread, graph_replay)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cand", action="store_true",
@@ -151,7 +157,7 @@ def main():
 
     launch = "stream"
     graphs = {}
-    if args.graph:
+    if args.graph or not args.no_graph_legs:
         # one graph holds `rotate` consecutive steps (one per input set), the
         # way a decode graph holds every layer of a step; a second graph holds
         # the remainder so that exactly `steps` steps are timed
@@ -166,7 +172,8 @@ def main():
                 for g in graphs.values():
                     g.replay()
             torch.cuda.synchronize()
-            launch = f"graph ({rotate} steps per replay)"
+            if args.graph:
+                launch = f"graph ({rotate} steps per replay)"
         except Exception as e:  # capture unsupported: fall back to stream launches
             print(f"bench.py: graph capture failed ({e}); timing stream launches",
                   file=sys.stderr)
@@ -178,7 +185,7 @@ def main():
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         ev0.record(stream)
-        if graphs:
+        if args.graph and graphs:
             for _ in range(args.steps // rotate):
                 graphs[rotate].replay()
             if args.steps % rotate:
@@ -325,7 +332,8 @@ def mxfp8_leg(args, wl, lengths, stream, rotate_bytes):
 def spread_legs(args, graphs, rotate, step, stream, rows):
     """After the timed region: the spread of the step time (graph replays
     timed one by one with HIP events, per step = replay / steps per replay),
-    the same steps launched one by one on the stream, and a plain streaming
+    the same steps in the launch mode that the headline did not time (graph
+    replays, or stream launches under --graph 1), and a plain streaming
     read (torch.sum over 1 GiB) as a reference ceiling for HBM reads."""
     import torch
     out = {}
@@ -342,18 +350,32 @@ def spread_legs(args, graphs, rotate, step, stream, rows):
         pick = lambda q: round(per[min(n - 1, int(q * n))], 3)
         out["step_us_spread"] = {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9),
                                  "replays": n, "steps_per_replay": rotate}
-    with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            step(i)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(args.steps):
-            step(i)
-        e1.record(stream)
-    torch.cuda.synchronize()
-    us = 1e3 * e0.elapsed_time(e1) / args.steps
-    out["stream_launch"] = {"step_us": round(us, 3), "tokens_per_s": round(rows / (us * 1e-6), 1)}
+    # the launch mode that the headline did not time
+    replay = graphs and not args.graph
+    if replay or args.graph:
+        with torch.cuda.stream(stream):
+            for i in range(args.warmup):
+                step(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if replay:
+                for _ in range(args.steps // rotate):
+                    graphs[rotate].replay()
+                if args.steps % rotate:
+                    graphs[args.steps % rotate].replay()
+            else:
+                for i in range(args.steps):
+                    step(i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / args.steps
+        leg = {"step_us": round(us, 3), "tokens_per_s": round(rows / (us * 1e-6), 1)}
+        if replay:
+            out["graph_replay"] = {**leg, "steps_per_replay": rotate}
+        else:
+            out["stream_launch"] = leg
     buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         torch.sum(buf)
         e0.record(stream)
