@@ -10,7 +10,7 @@
  * indexer reads the paged K cache directly (section 4.1); the attention core
  * gathers the selected rows of the main KV cache from the indexer's position
  * list (section 4.2); the fused call takes the FP8 indexer query, the index
- * keys and the head weights (section 4.3, "idx = fused_topk(q8, k, g)").
+ * keys and the head weights and returns positions (section 4.3).
  * One KV latent row is shared by every query head ("SPLASH: Switching
  * Parallel Layouts of Attention with Seamless Handoff for LLM Serving",
  * section 2).
@@ -64,6 +64,7 @@ extern "C" {
 
 #define DSA_ABI_VERSION 4
 #define DSA_BLOCK_SIZE 64
+#define DSA_MAX_ATTN_K 16384 /* largest K of dsa_sparse_attn / dsa_decode_step */
 
 typedef enum {
   DSA_OK = 0,
@@ -102,7 +103,8 @@ typedef struct {
   int32_t H_q;                /* attention query heads, 1..128                          */
   int32_t D_qk;               /* attention q/k dim: 64 or 576                           */
   int32_t D_v;                /* attention v / output dim: 64 (with D_qk 64) or 512     */
-  int32_t K;                  /* positions kept per row, >= 1                           */
+  int32_t K;                  /* positions kept per row, >= 1 (attention: at most
+                                 DSA_MAX_ATTN_K, else DSA_ERR_UNSUPPORTED)               */
   float scale;                /* attention logit scale, finite (e.g. 1/sqrt(D_qk))      */
   int32_t indexer_format;     /* DSA_INDEXER_E4M3 or DSA_INDEXER_MXFP8                  */
   const uint8_t* qI_scale;    /* MXFP8: [num_rows][H_I][D_I / 32] E8M0 scales of qI;

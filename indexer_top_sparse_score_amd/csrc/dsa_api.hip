@@ -11,7 +11,10 @@ namespace dsa {
 namespace {
 
 constexpr size_t kHeader = 256;                    // error word + reserved
-constexpr size_t kScoresBudget = size_t(512) << 20;  // fused step: scores kept per pass
+// Fused step: score rows (and summaries) kept per pass of rows.  Chunked
+// prefill batches of thousands of rows are cut into passes whose score slab
+// stays within the 256 MB Infinity Cache.
+constexpr size_t kScoresBudget = size_t(128) << 20;
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -51,6 +54,8 @@ int check_attn_shape(const dsa_problem* p) {
   if (p->H_q < 1 || p->D_qk < 1 || p->D_v < 1 || p->K < 1) return DSA_ERR_INVALID;
   if (!std::isfinite(p->scale)) return DSA_ERR_INVALID;
   if (p->H_q > 128) return DSA_ERR_UNSUPPORTED;
+  // a row's index list is split into at most 64 chunks of at most 256 slots
+  if (p->K > DSA_MAX_ATTN_K) return DSA_ERR_UNSUPPORTED;
   const bool small = p->D_qk == 64 && p->D_v == 64;
   const bool mla = p->D_qk == 576 && p->D_v == 512;
   if (!small && !mla) return DSA_ERR_UNSUPPORTED;
@@ -107,10 +112,13 @@ int64_t max_len(const dsa_problem* p) {
 // every row is 256-byte aligned.
 int64_t slab_ld(const dsa_problem* p) { return (max_len(p) + 63) & ~int64_t(63); }
 
-bool cand_vec(const dsa_problem* p) { return p->cand && p->n_cand % 4 == 0; }
+
+// Whether any row of the problem can have a summary (more than 16384 slots).
+bool needs_summary(const dsa_problem* p) { return max_len(p) >= kSumMinLen && p->K <= kSumMaxK; }
 
 int rows_per_pass(const dsa_problem* p) {
-  const size_t per_row = (size_t)slab_ld(p) * sizeof(float) + topk_work_bytes(1, max_len(p));
+  const size_t per_row = (size_t)slab_ld(p) * sizeof(float) +
+                         (needs_summary(p) ? (size_t)kSumEntries * 5 : 0);
   size_t rp = kScoresBudget / per_row;
   if (rp < 1) rp = 1;
   if (rp > (size_t)p->num_rows) rp = (size_t)p->num_rows;
@@ -125,13 +133,14 @@ int status_of(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
 
 struct DecodeLayout {
   int rp;
-  size_t idx_off, roff_off, scores_off, topk_off, part_off, total;
+  size_t idx_off, roff_off, scores_off, sum_off, part_off, total;
 };
 
-// The fused step hands the attention kernel the selected rows' byte offsets
-// (written by the Top-K compaction) for the latent 576-wide rows; the
-// workspace reserves them for every shape so its size does not depend on
-// the caches' strides.
+// Workspace of the fused step, per pass of rows: the selection, the selected
+// rows' byte offsets in the KV cache (for the latent layout; reserved for
+// every shape so that the size does not depend on the caches' strides), the
+// float32 score slab, the rows' Top-K summaries and the attention's
+// split-key partials.
 DecodeLayout decode_layout(const dsa_problem* p) {
   DecodeLayout d;
   d.rp = rows_per_pass(p);
@@ -139,8 +148,8 @@ DecodeLayout decode_layout(const dsa_problem* p) {
   d.idx_off = kHeader;
   d.roff_off = d.idx_off + round256((size_t)d.rp * p->K * sizeof(int32_t));
   d.scores_off = d.roff_off + round256((size_t)d.rp * p->K * sizeof(int64_t));
-  d.topk_off = d.scores_off + round256((size_t)d.rp * slab_ld(p) * sizeof(float));
-  d.part_off = d.topk_off + round256(topk_work_bytes(d.rp, max_len(p)));
+  d.sum_off = d.scores_off + round256((size_t)d.rp * slab_ld(p) * sizeof(float));
+  d.part_off = d.sum_off + round256(needs_summary(p) ? summary_bytes(d.rp) : 0);
   d.total = d.part_off + round256(attn_partial_bytes(d.rp, p->H_q, p->D_v, nc));
   return d;
 }
@@ -172,7 +181,7 @@ size_t dsa_workspace_size(const dsa_problem* p, int op) {
       return check_indexer_shape(p) == DSA_OK ? kHeader : 0;
     case DSA_OP_TOPK:
       if (p->K < 1) return 0;
-      return kHeader + round256(topk_work_bytes(p->num_rows, max_len(p)));
+      return kHeader + round256(needs_summary(p) ? summary_bytes(p->num_rows) : 0);
     case DSA_OP_SPARSE_ATTN: {
       if (check_attn_shape(p) != DSA_OK) return 0;
       const int nc = attn_chunks_max(p->num_rows, p->H_q, p->D_qk, p->K);
@@ -213,7 +222,7 @@ int dsa_indexer_scores(const dsa_problem* p, const uint8_t* qI, const float* w, 
   a.row_begin = 0;
   a.num_rows = p->num_rows;
   a.max_len = (int32_t)max_len(p);
-  a.tw = TopkWork{};
+  a.sum = Summary{nullptr, nullptr};
   a.topk_K = 0;
   return status_of(launch_indexer_scores(a, static_cast<hipStream_t>(stream)));
 }
@@ -240,13 +249,12 @@ int dsa_topk(const dsa_problem* p, const float* scores, int64_t ld_scores, int32
   a.row_begin = 0;
   a.num_rows = p->num_rows;
   a.max_len = (int32_t)max_len(p);
-  a.tw = topk_work_carve(static_cast<char*>(ws) + kHeader, p->num_rows, max_len(p));
-  a.prep = true;
+  a.sum = needs_summary(p) ? summary_carve(static_cast<char*>(ws) + kHeader, p->num_rows)
+                           : Summary{nullptr, nullptr};
+  a.prep = a.sum.key != nullptr;
   a.vec = aligned(scores, 16) && ld_scores % 4 == 0;
-  a.cvec = cand_vec(p);
   a.rowoff = nullptr;
   a.kv = dsa_paged{};
-  a.kv_row_bytes = 0;
   return status_of(launch_topk(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -328,10 +336,13 @@ int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa
   uint32_t* err = reinterpret_cast<uint32_t*>(base);
   float* scores = reinterpret_cast<float*>(base + d.scores_off);
   const int64_t ld = slab_ld(p);
-  const TopkWork tw = topk_work_carve(base + d.topk_off, d.rp, max_len(p));
-  const bool use_rowoff = is_latent(k, v) && p->D_qk == 576;
+  const Summary sum = needs_summary(p) ? summary_carve(base + d.sum_off, d.rp)
+                                       : Summary{nullptr, nullptr};
+  const bool use_rowoff = attn_uses_rowoff(p->D_qk, p->D_v, is_latent(k, v));
   int64_t* roff = reinterpret_cast<int64_t*>(base + d.roff_off);
 
+  // Four launches per pass of rows: indexer scan (scores and summaries),
+  // Top-K selection, sparse attention, split-key merge.
   for (int row0 = 0; row0 < p->num_rows; row0 += d.rp) {
     const int nr = p->num_rows - row0 < d.rp ? p->num_rows - row0 : d.rp;
     int32_t* idx = indices_out ? indices_out + (int64_t)row0 * p->K
@@ -351,7 +362,7 @@ int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa
     ia.row_begin = row0;
     ia.num_rows = nr;
     ia.max_len = (int32_t)max_len(p);
-    ia.tw = tw;
+    ia.sum = sum;
     ia.topk_K = p->K;
     if ((st = status_of(launch_indexer_scores(ia, s))) != DSA_OK) return st;
 
@@ -366,13 +377,11 @@ int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa
     ta.row_begin = row0;
     ta.num_rows = nr;
     ta.max_len = (int32_t)max_len(p);
-    ta.tw = tw;
-    ta.prep = false;
-    ta.vec = true;  // 256-byte aligned slab, ld a multiple of 64
-    ta.cvec = cand_vec(p);
+    ta.sum = sum;
+    ta.prep = false;  // the indexer wrote the summaries
+    ta.vec = true;    // 256-byte aligned slab, ld a multiple of 64
     ta.rowoff = use_rowoff ? roff : nullptr;
     ta.kv = k;
-    ta.kv_row_bytes = use_rowoff ? p->D_qk * 2 : 0;
     if ((st = status_of(launch_topk(ta, s))) != DSA_OK) return st;
 
     AttnLaunch aa = attn_launch(p, q, k, v, out, lse, err);

@@ -91,13 +91,14 @@ __device__ __forceinline__ void report(uint32_t* err, uint32_t bit) {
 }
 
 // Order-preserving 32-bit key of a float32 score: larger score, larger key;
-// -0 and +0 share a key; NaN gets 0 and ranks below every number.
+// -0 and +0 share a key; NaN gets 1 and ranks below every number (the keys
+// of numbers are at least 0x007FFFFF).  Key 0 stands for "no slot".
 __device__ __forceinline__ uint32_t score_key(float x) {
   uint32_t u = __float_as_uint(x);
   const uint32_t mag = u & 0x7FFFFFFFu;
   if (mag == 0) u = 0;
   uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return mag > 0x7F800000u ? 0u : k;
+  return mag > 0x7F800000u ? 1u : k;
 }
 
 // ----------------------------------------------------- cross-lane, registers
@@ -148,43 +149,40 @@ __device__ __forceinline__ int lane_prefix(uint64_t mask) {
 // Each returns hipSuccess or the launch error.  Arguments are validated by
 // the front end before these run.
 
-// ------------------------------------------------------ Top-K work area
-// The Top-K's pre-selection.  A row's positions are cut into segments of G
-// = topk_sum_seg(L) positions (32 to 128, at most 1024 segments up to
-// 131072 positions); the m = topk_sum_m(L) largest keys of each segment
-// form the row's summary, 3072 to kSumMax keys for the rows that use it
-// (topk_split_row: more than 16384 positions, so more than 512 segments).
-// The summary's keys sit at distinct positions, so its K-th largest is a
-// lower bound on the row's K-th largest score;
-// with about two summary keys per row key kept, and about two kept keys per
-// segment, the segments' top keys hold nearly all of the row's top K and
-// the bound is close.  The fused indexer and the standalone summary pass
-// call the same functions, so they agree on every row.
-constexpr int kSumSpan = 128;           // positions per indexer wave (one or more segments)
-constexpr int kSumSegs = 1024;          // segments per row, at most (up to 131072 positions)
-constexpr int kSumMax = 4096;           // summary keys per row, at most
-constexpr int kSumCap = 8;              // keys per segment, at most
-__host__ __device__ inline int topk_sum_seg(int L) {
-  int G = 32;
-  while (G < kSumSpan && (L + G - 1) / G > kSumSegs) G <<= 1;
+// ------------------------------------------------------ Top-K summaries
+// A row of more than 16384 and at most 131072 slots (with K <= 2048) gets a
+// summary from the indexer's epilogue, or from the standalone summary pass:
+// its slots are cut into segments of G = sum_seg(L) slots (16, 32 or 64;
+// at most 2048 segments), and for each segment the kSumM largest keys are
+// kept with their offsets in the segment, in slot order; key 0 fills the
+// entries of a segment shorter than kSumM.  The selection (topk_select.h)
+// works from it.  With K <= 2048 a segment holds on average at most two of
+// the row's K largest keys (one at the segment counts' upper ends, 32768,
+// 65536 and 131072 slots), so eight per segment rarely miss one; when they
+// might, the selection re-reads that segment's scores.
+constexpr int kSumM = 8;                        // entries per segment
+constexpr int kSumSegMax = 2048;                // segments per row, at most
+constexpr int kSumEntries = kSumM * kSumSegMax; // 16384 per row
+constexpr int kSumMinLen = 16385;
+constexpr int kSumMaxLen = 131072;
+constexpr int kSumMaxK = 2048;
+__host__ __device__ inline int sum_seg(int L) {
+  int G = 16;
+  while (G < 64 && (L + G - 1) / G > kSumSegMax) G <<= 1;
   return G;
 }
-__host__ __device__ inline int topk_sum_m(int L) {
-  const int G = topk_sum_seg(L);
-  const int nseg = (L + G - 1) / G;
-  if (nseg <= 0) return 0;
-  const int m = kSumMax / nseg;
-  return m < kSumCap ? m : kSumCap;
+__host__ __device__ inline bool sum_row(int L, int K) {
+  return K <= kSumMaxK && L >= kSumMinLen && L <= kSumMaxLen;
 }
-constexpr int kTopkSlices = 32;         // workgroups per row, at most
-constexpr int kTopkSliceLen = 4096;     // positions per slice
-constexpr int kTopkSplitMaxK = 2048;
-// Rows that the Top-K spreads over slices (and that get a summary).  Rows
-// of up to 16384 positions are faster in one workgroup, which holds 16 keys
-// per thread.
-__host__ __device__ inline bool topk_split_row(int L, int K) {
-  return K <= kTopkSplitMaxK && L > 16384 && L <= kTopkSlices * kTopkSliceLen;
-}
+
+// The summaries of a pass of rows: keys [rows][kSumEntries] (uint32) and
+// offsets [rows][kSumEntries] (uint8), carved from a workspace.
+struct Summary {
+  uint32_t* key;
+  uint8_t* off;
+};
+size_t summary_bytes(int rows);
+Summary summary_carve(void* base, int rows);
 
 // Maximum of an unsigned value over aligned groups of G lanes (16, 32 or
 // 64, wave-uniform), in every lane of the group.
@@ -204,80 +202,68 @@ __device__ __forceinline__ uint32_t group_max_u32(uint32_t x, int G) {
   return x;
 }
 
-// The m largest keys of each segment of G positions of a wave's 128 (key a
-// of lane l: position l, key b: position 64 + l), with multiplicity: m
-// rounds of a group maximum, each taking out one instance (the lowest lane
-// of the group that holds it).  G = 128: one segment over both keys, lane
-// i < m gets its (i+1)-th largest in out_a.  G <= 64: segments of G lanes
-// in each key; lane G s + i, i < m, gets segment s's (i+1)-th largest of
-// the a keys in out_a and of the b keys in out_b.  G and m are wave-uniform.
-__device__ __forceinline__ void segment_top(uint32_t ka, uint32_t kb, int m, int G, uint32_t& out_a,
-                                            uint32_t& out_b) {
+// Writes the summary entries of a wave's 128 slots w0 .. w0 + 127 (w0 a
+// multiple of 128, w0 < S) of a row of S slots: ka is the key of slot
+// w0 + lane, kb of slot w0 + 64 + lane (0 past the row; keys of slots are
+// at least 1).  G = sum_seg(S) lanes form a segment, within ka and within kb.
+// Up to kSumM rounds each take one largest remaining key per segment (the
+// lowest lane holding it; the order among equal keys does not matter: a
+// segment whose kSumM-th key ties the threshold is re-read whole); the taken
+// keys are then written in slot order.
+__device__ __forceinline__ void summary_write(uint32_t ka, uint32_t kb, int w0, int S, int G,
+                                              uint32_t* skey, uint8_t* soff) {
   const int lane = (int)(threadIdx.x & 63);
-  out_a = out_b = 0u;
-  if (G >= kSumSpan) {
-    for (int i = 0; i < m; ++i) {
-      const uint32_t v = max(ka, kb);
-      const uint32_t M = group_max_u32(v, 64);
-      const uint64_t hit = __ballot(v == M);
-      if (lane == (int)__builtin_ctzll(hit)) {
-        if (ka == M)
-          ka = 0u;
-        else
-          kb = 0u;
-      }
-      out_a = lane == i ? M : out_a;
-    }
-    return;
-  }
+  bool ta = false, tb = false;
+  uint32_t va = ka, vb = kb;
   const int base = lane & ~(G - 1);
   const uint64_t gmask = G == 64 ? ~0ull : ((1ull << G) - 1ull) << base;
-  for (int i = 0; i < m; ++i) {
-    const uint32_t Ma = group_max_u32(ka, G), Mb = group_max_u32(kb, G);
-    const uint64_t ha = __ballot(ka == Ma) & gmask, hb = __ballot(kb == Mb) & gmask;
-    if (lane == (int)__builtin_ctzll(ha)) ka = 0u;
-    if (lane == (int)__builtin_ctzll(hb)) kb = 0u;
-    out_a = lane - base == i ? Ma : out_a;
-    out_b = lane - base == i ? Mb : out_b;
+#pragma unroll
+  for (int i = 0; i < kSumM; ++i) {
+    const uint32_t Ma = group_max_u32(va, G), Mb = group_max_u32(vb, G);
+    if (__ballot(Ma != 0u || Mb != 0u) == 0) break;  // nothing left in any segment
+    const uint64_t ha = __ballot(va == Ma && Ma != 0u) & gmask;
+    const uint64_t hb = __ballot(vb == Mb && Mb != 0u) & gmask;
+    if (ha != 0 && lane == (int)__builtin_ctzll(ha)) {
+      ta = true;
+      va = 0u;
+    }
+    if (hb != 0 && lane == (int)__builtin_ctzll(hb)) {
+      tb = true;
+      vb = 0u;
+    }
+  }
+  const uint64_t ma = __ballot(ta) & gmask, mb = __ballot(tb) & gmask;
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int ra = __popcll(ma & below), rb = __popcll(mb & below);
+  const int ca = __popcll(ma), cb = __popcll(mb);
+  const int i = lane - base;  // offset in the segment
+  if (w0 + base < S) {
+    const int sg = (w0 + base) / G;
+    uint32_t* kd = skey + sg * kSumM;
+    uint8_t* od = soff + sg * kSumM;
+    if (ta) {
+      kd[ra] = ka;
+      od[ra] = (uint8_t)i;
+    }
+    if (i >= ca && i < kSumM) {
+      kd[i] = 0u;
+      od[i] = 0;
+    }
+  }
+  if (w0 + 64 + base < S) {
+    const int sg = (w0 + 64 + base) / G;
+    uint32_t* kd = skey + sg * kSumM;
+    uint8_t* od = soff + sg * kSumM;
+    if (tb) {
+      kd[rb] = kb;
+      od[rb] = (uint8_t)i;
+    }
+    if (i >= cb && i < kSumM) {
+      kd[i] = 0u;
+      od[i] = 0;
+    }
   }
 }
-
-// Writes a wave's summary keys (segment_top's results for the 128 positions
-// from w0, of a score row of S positions) into the row's summary `summ`.
-__device__ __forceinline__ void store_segment_top(uint32_t* summ, int w0, int S, int m, int G,
-                                                  uint32_t out_a, uint32_t out_b) {
-  const int lane = (int)(threadIdx.x & 63);
-  if (G >= kSumSpan) {
-    if (lane < m && w0 < S) summ[(w0 / G) * m + lane] = out_a;
-    return;
-  }
-  const int i = lane & (G - 1), s_lane = lane / G;
-  if (i < m && w0 + G * s_lane < S) summ[(w0 / G + s_lane) * m + i] = out_a;
-  if (i < m && w0 + 64 + G * s_lane < S) summ[((w0 + 64) / G + s_lane) * m + i] = out_b;
-}
-
-// The Top-K's work area, carved from the caller's workspace:
-//  - summ [rows][kSumMax]: each row's summary (segment s's keys at
-//    s * m .. s * m + m - 1);
-//  - ckey, cpos [rows][cstride]: the candidate keys and positions that the
-//    workgroups of a row's slices hand to the one that finishes the row
-//    (slice j's entries start at j * kTopkSliceLen);
-//  - ccount [rows][kTopkSlices]: how many candidates each slice left;
-//  - arrive [rows]: slices of the row done so far.  Whichever kernel writes
-//    the summary for a call (the fused indexer, or the standalone summary
-//    pass) zeroes it first.
-struct TopkWork {
-  uint32_t* summ;
-  uint32_t* ckey;
-  int32_t* cpos;
-  int64_t cstride;
-  uint32_t* ccount;
-  uint32_t* arrive;
-};
-// bytes of the work area for `rows` rows of history up to max_len
-size_t topk_work_bytes(int rows, int64_t max_len);
-// carves the work area out of `base` (256-byte aligned)
-TopkWork topk_work_carve(void* base, int rows, int64_t max_len);
 
 struct IndexerLaunch {
   RowMap rows;
@@ -291,8 +277,8 @@ struct IndexerLaunch {
   int32_t H_I, D_I;
   int32_t row_begin, num_rows;  // rows [row_begin, row_begin + num_rows)
   int32_t max_len;              // upper bound of any row's history length
-  TopkWork tw;                  // summaries for a Top-K of topk_K that follows,
-  int32_t topk_K;               // or nothing when tw.summ is NULL
+  Summary sum;                  // summaries for a Top-K of topk_K that follows,
+  int32_t topk_K;               // or nothing when sum.key is NULL
 };
 hipError_t launch_indexer_scores(const IndexerLaunch& a, hipStream_t s);
 
@@ -306,19 +292,14 @@ struct TopkLaunch {
   int32_t K;
   int32_t row_begin, num_rows;
   int32_t max_len;
-  TopkWork tw;
-  bool prep;            // compute the summaries here (no fused indexer before)
+  Summary sum;          // the rows' summaries
+  bool prep;            // write the summaries here (no fused indexer before)
   bool vec;             // every score row is 16-byte aligned (ld % 4 == 0)
-  bool cvec;            // every candidate row is 16-byte aligned (n_cand % 4 == 0)
   // Optional: also write each kept position's byte offset in the paged KV
   // cache `kv` (block table -> physical block), -1 for padding and for
   // positions whose block id is out of range, to rowoff[num_rows][K].
   int64_t* rowoff;
   dsa_paged kv;
-  // With rowoff: bytes of a KV row the attention that follows reads (0: none).
-  // The Top-K then touches every candidate's row once it has handed its
-  // slice over, so that the attention's gather finds them in the caches.
-  int32_t kv_row_bytes;
 };
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
 
@@ -327,11 +308,13 @@ struct AttnLaunch {
   const uint16_t* q;
   dsa_paged k, v;
   bool latent;  // v aliases k (same base and strides)
+  // The selection: indices [.][K] (row row_begin + i at row indices_row_offset
+  // + i); or, for the latent layout, the kept rows' byte offsets in the KV
+  // cache as the Top-K wrote them (rowoff [num_rows][K], -1 = absent),
+  // which replace the index -> block table lookup.
   const int32_t* indices;
-  int64_t indices_row_offset;  // indices row of row_begin
-  const int64_t* rowoff;       // optional [num_rows][K] byte offsets of the selected
-                               // rows (latent layout), -1 = absent; replaces the
-                               // index -> block table lookup
+  int64_t indices_row_offset;
+  const int64_t* rowoff;
   uint16_t* out;
   float* lse;
   void* partial;   // workspace for split-key partials, or NULL when n_chunks == 1
@@ -347,6 +330,9 @@ struct AttnLaunch {
 int attn_chunks(int num_rows, int H_q, int D_qk, int K, bool latent);
 int attn_chunks_max(int num_rows, int H_q, int D_qk, int K);
 size_t attn_partial_bytes(int num_rows, int H_q, int D_v, int n_chunks);
+// whether launch_sparse_attn reads row offsets (AttnLaunch.rowoff) for this
+// shape and layout
+bool attn_uses_rowoff(int D_qk, int D_v, bool latent);
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s);
 
 }  // namespace dsa

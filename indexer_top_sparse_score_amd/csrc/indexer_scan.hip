@@ -86,8 +86,6 @@ template <int NKP, int HT, bool MX, bool CAND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void indexer_scan_kernel(IndexerLaunch a) {
   const int r = a.row_begin + (int)blockIdx.y;
   const int tile0 = (int)blockIdx.x * kTile;
-  // the Top-K that follows counts its row's finished slices from zero
-  if (a.tw.arrive && blockIdx.x == 0 && threadIdx.x == 0) a.tw.arrive[blockIdx.y] = 0;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;  // head row of A, position column of B
@@ -298,16 +296,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     const int i = 64 * h + lane;
     if (w0 + i < S) out[w0 + i] = my_sc[i];
   }
-  // The Top-K's summary of this wave's positions (the m largest keys of
-  // each of its segments)
-  static_assert(kSpan == kSumSpan, "the summary's wave span");
-  if (a.tw.summ && w0 < S && topk_split_row(S, a.topk_K)) {  // wave-uniform
+  // The Top-K's summary of this wave's slots: the kSumM largest keys of each
+  // of their segments, with their offsets
+  static_assert(kSpan == 128, "a wave's summary covers 128 slots");
+  if (a.sum.key && w0 < S && sum_row(S, a.topk_K)) {  // wave-uniform
     const uint32_t ka = w0 + lane < S ? score_key(my_sc[lane]) : 0u;
     const uint32_t kb = w0 + 64 + lane < S ? score_key(my_sc[64 + lane]) : 0u;
-    const int m = topk_sum_m(S), G = topk_sum_seg(S);
-    uint32_t out_a, out_b;
-    segment_top(ka, kb, m, G, out_a, out_b);
-    store_segment_top(a.tw.summ + (int64_t)(r - a.row_begin) * kSumMax, w0, S, m, G, out_a, out_b);
+    const int64_t ro = (int64_t)(r - a.row_begin) * kSumEntries;
+    summary_write(ka, kb, w0, S, sum_seg(S), a.sum.key + ro, a.sum.off + ro);
   }
   if (__builtin_amdgcn_ballot_w64(bad_page || bad_blk) && lane == 0) report(a.err, DSA_DEVERR_BLOCK);
   if (CAND && __builtin_amdgcn_ballot_w64(bad_pos) && lane == 0) report(a.err, DSA_DEVERR_ROW);

@@ -27,8 +27,8 @@
 // exactly the 8 logits its S^T accumulators already hold; the V^T operand is
 // read with the same permutation.
 // When a row's index list is split over several chunks, each chunk writes
-// its (max, sum, unnormalised O) and a second kernel merges them by
-// log-sum-exp.
+// its (max, sum, unnormalised O) in float32 and a second kernel merges them
+// by log-sum-exp.
 
 #include "dsa_common.h"
 
@@ -53,24 +53,49 @@ namespace {
 
 constexpr int kSB = 32;        // keys per sub-block
 constexpr int kHPW = 16;       // heads per wave
-constexpr int kMaxChunk = 256; // index slots per workgroup
+constexpr int kMaxChunk = 256; // index slots per workgroup (staged kernel)
+constexpr int kMaxChunkLat = 2048;  // index slots per workgroup (latent kernel)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Split-key partials of a call: (max, sum) as float2 [rows][chunks][H_q],
-// then the chunk's unnormalised output O = sum_j 2^(t_j - max) v_j as bf16
-// [rows][chunks][H_q][D_v]
-// (256-byte aligned).
+// Split-key partials of a call, float32:
+//  - (max, sum) as float2 [rows][chunks][H_q]: the chunk's reference max of
+//    the log2-scaled logits (-inf for an empty chunk) and its sum of
+//    exponentials against it;
+//  - the chunk's unnormalised output O = sum_j 2^(t_j - max) v_j, per
+//    (row, chunk) in blocks of 16 heads: [HB][DV/16][16 heads][16 dims], HB =
+//    ceil(H_q / 16).  This is the order in which a wave's O^T accumulators
+//    sit in its lanes, so each 16-dim tile of a wave is one contiguous 1 KB
+//    store.
 __host__ __device__ inline size_t part_stats_bytes(int rows, int chunks, int H_q) {
   return ((size_t)rows * chunks * H_q * sizeof(float2) + 255) & ~size_t(255);
+}
+__host__ __device__ inline int64_t part_block_floats(int H_q, int DV) {
+  return (int64_t)((H_q + 15) / 16) * 16 * DV;
 }
 __device__ __forceinline__ float2* part_stats(const AttnLaunch& a, int row_local, int chunk) {
   return reinterpret_cast<float2*>(a.partial) + ((int64_t)row_local * a.n_chunks + chunk) * a.H_q;
 }
-__device__ __forceinline__ uint16_t* part_out(const AttnLaunch& a, int row_local, int chunk, int DV) {
-  return reinterpret_cast<uint16_t*>(static_cast<char*>(a.partial) +
-                                     part_stats_bytes(a.num_rows, a.n_chunks, a.H_q)) +
-         ((int64_t)row_local * a.n_chunks + chunk) * a.H_q * DV;
+__device__ __forceinline__ float* part_out(const AttnLaunch& a, int row_local, int chunk, int DV) {
+  return reinterpret_cast<float*>(static_cast<char*>(a.partial) +
+                                  part_stats_bytes(a.num_rows, a.n_chunks, a.H_q)) +
+         ((int64_t)row_local * a.n_chunks + chunk) * part_block_floats(a.H_q, DV);
+}
+
+// A wave's partial: lane (grp, cidx) holds O^T[16mt + 4grp + v][head0 + cidx]
+// in o[mt][v]; lsum is the head's whole sum (reduced across the lane groups).
+template <int MT>
+__device__ __forceinline__ void write_partial(const AttnLaunch& a, int row_local, int chunk,
+                                              int head0, int lane, const v4f* o, float m2,
+                                              float lsum) {
+  const int cidx = lane & 15, grp = lane >> 4;
+  float* dst = part_out(a, row_local, chunk, 16 * MT) + (int64_t)(head0 / 16) * (MT * 256) +
+               cidx * 16 + 4 * grp;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<v4f*>(dst + mt * 256) = o[mt];
+  if (grp == 0 && head0 + cidx < a.H_q)
+    part_stats(a, row_local, chunk)[head0 + cidx] =
+        float2{lsum > 0.0f ? m2 : -__builtin_inff(), lsum};
 }
 
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
@@ -103,16 +128,18 @@ __device__ __forceinline__ uint32_t word(const uint4& x, int c) {
 // Epilogue of one wave: lane (grp, cidx) holds O^T[16mt + 4grp + v][head]
 // in o[mt][v], the head's reference max m2 (log2 units) and its sum of
 // exponentials.  One chunk: out = O / sum (bf16) and lse; several: the
-// chunk's (max, sum) and O / sum as bf16 partials.
+// chunk's float32 partial.
 template <int MT>
 __device__ __forceinline__ void write_result(const AttnLaunch& a, int r, int row_local, int chunk,
                                              int head, int grp, const v4f* o, float m2, float lsum) {
   constexpr int DV = 16 * MT;
-  // the single chunk's output O / sum; a partial keeps O (see the combine)
-  const float inv = a.n_chunks > 1 ? 1.0f : lsum > 0.0f ? 1.0f / lsum : 0.0f;
-  uint16_t* dst = a.n_chunks == 1 ? a.out + ((int64_t)r * a.H_q + head) * DV
-                                  : part_out(a, row_local, chunk, DV) + (int64_t)head * DV;
-  dst += 4 * grp;
+  if (a.n_chunks > 1) {
+    write_partial<MT>(a, row_local, chunk, head - (head & 15), (int)(threadIdx.x & 63), o, m2,
+                      lsum);
+    return;
+  }
+  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  uint16_t* dst = a.out + ((int64_t)r * a.H_q + head) * DV + 4 * grp;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     uint2 w;
@@ -120,45 +147,29 @@ __device__ __forceinline__ void write_result(const AttnLaunch& a, int r, int row
     w.y = pack2(o[mt][2] * inv, o[mt][3] * inv);
     *reinterpret_cast<uint2*>(dst + 16 * mt) = w;
   }
-  if (grp != 0) return;
-  if (a.n_chunks == 1) {
-    if (a.lse)
-      a.lse[(int64_t)r * a.H_q + head] = lsum > 0.0f ? (m2 + log2f(lsum)) * kLn2 : -__builtin_inff();
-  } else {
-    part_stats(a, row_local, chunk)[head] = float2{lsum > 0.0f ? m2 : -__builtin_inff(), lsum};
-  }
+  if (grp == 0 && a.lse)
+    a.lse[(int64_t)r * a.H_q + head] = lsum > 0.0f ? (m2 + log2f(lsum)) * kLn2 : -__builtin_inff();
 }
 
-// The same results written through LDS, so that every global store is a
-// whole 1 KB head row (64 lanes x 16 B) rather than 16 scattered 32-byte
+// The single-chunk result written through LDS, so that every global store
+// is a whole 1 KB head row (64 lanes x 16 B) rather than 16 scattered 32-byte
 // pieces: the wave's 16 x 512 bf16 go to `stage` (16 rows, pitch 1040 B to
 // spread the banks) and come back one head row per instruction.  `stage` is
 // this wave's own 16.25 KB of LDS; nothing else may use it meanwhile.
-__device__ __forceinline__ void write_result_staged(const AttnLaunch& a, int r, int row_local,
-                                                    int chunk, int head0, int lane, const v4f* o,
-                                                    float m2, float lsum, uint8_t* stage) {
+__device__ __forceinline__ void write_out_staged(const AttnLaunch& a, int r, int head0, int lane,
+                                                 const v4f* o, float m2, float lsum,
+                                                 uint8_t* stage) {
   constexpr int DV = 512, MT = DV / 16, kPitch = 2 * DV + 16;
   const int cidx = lane & 15, grp = lane >> 4;
-  if (a.n_chunks == 1) {
-    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      uint2 w;
-      w.x = pack2(o[mt][0] * inv, o[mt][1] * inv);
-      w.y = pack2(o[mt][2] * inv, o[mt][3] * inv);
-      *reinterpret_cast<uint2*>(stage + cidx * kPitch + 2 * (16 * mt + 4 * grp)) = w;
-    }
-  } else {  // a partial: O against the chunk's reference, unnormalised
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      uint2 w;
-      w.x = pack2(o[mt][0], o[mt][1]);
-      w.y = pack2(o[mt][2], o[mt][3]);
-      *reinterpret_cast<uint2*>(stage + cidx * kPitch + 2 * (16 * mt + 4 * grp)) = w;
-    }
+  for (int mt = 0; mt < MT; ++mt) {
+    uint2 w;
+    w.x = pack2(o[mt][0] * inv, o[mt][1] * inv);
+    w.y = pack2(o[mt][2] * inv, o[mt][3] * inv);
+    *reinterpret_cast<uint2*>(stage + cidx * kPitch + 2 * (16 * mt + 4 * grp)) = w;
   }
-  uint16_t* dst = a.n_chunks == 1 ? a.out + ((int64_t)r * a.H_q + head0) * DV
-                                  : part_out(a, row_local, chunk, DV) + (int64_t)head0 * DV;
+  uint16_t* dst = a.out + ((int64_t)r * a.H_q + head0) * DV;
   const int nh = min(kHPW, a.H_q - head0);
 #pragma unroll
   for (int h = 0; h < kHPW; ++h)
@@ -167,12 +178,8 @@ __device__ __forceinline__ void write_result_staged(const AttnLaunch& a, int r, 
           *reinterpret_cast<const uint4*>(stage + h * kPitch + 16 * lane);
   const int head = head0 + cidx;
   if (grp != 0 || cidx >= nh) return;
-  if (a.n_chunks == 1) {
-    if (a.lse)
-      a.lse[(int64_t)r * a.H_q + head] = lsum > 0.0f ? (m2 + log2f(lsum)) * kLn2 : -__builtin_inff();
-  } else {
-    part_stats(a, row_local, chunk)[head] = float2{lsum > 0.0f ? m2 : -__builtin_inff(), lsum};
-  }
+  if (a.lse)
+    a.lse[(int64_t)r * a.H_q + head] = lsum > 0.0f ? (m2 + log2f(lsum)) * kLn2 : -__builtin_inff();
 }
 
 struct AttnGrid {
@@ -521,12 +528,13 @@ __device__ __forceinline__ void wait_vm(int groups) {
 template <int NBUF, int kNW>
 __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLaunch a, AttnGrid g) {
   using namespace lat;
+  constexpr int NT = 64 * kNW;
   constexpr int kDmaPerWave = kDmaPerSB / kNW;
   static_assert(kDmaPerSB % kNW == 0, "DMA instructions per wave");
   static_assert(NBUF >= 2 && NBUF <= 4, "vmcnt cases");
   static_assert(kNW * 16 * (2 * kDv + 16) <= NBUF * kTileBytes, "epilogue staging fits the tiles");
   __shared__ __attribute__((aligned(16))) uint8_t tile[NBUF][kTileBytes];
-  __shared__ int64_t koff[kMaxChunk];
+  __shared__ int64_t koff[kMaxChunkLat];
 
   int unit, hg;
   if (!decode_wg(g, unit, hg)) return;
@@ -541,14 +549,14 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
   const int n_slots = max(0, min(a.K, slot0 + g.chunk) - slot0);
   const int nsb = (n_slots + kSB - 1) / kSB;
 
-  // ---- prologue: every index of the chunk -> row byte offset (-1: absent).
-  //      Ready-made when the Top-K compaction wrote them (-1 for a row that
+  // ---- prologue: every index slot of the chunk -> row byte offset (-1:
+  //      absent).  Ready-made when the Top-K wrote them (-1 for a row that
   //      does not resolve, which that kernel has reported): one round trip,
   //      and nothing else is loaded before it, so the first DMAs go out as
   //      soon as it is back.
   if (a.rowoff) {
     const int64_t* ro = a.rowoff + (int64_t)row_local * a.K + slot0;
-    for (int i = tid; i < nsb * kSB; i += 64 * kNW) koff[i] = i < n_slots ? ro[i] : -1;
+    for (int i = tid; i < nsb * kSB; i += NT) koff[i] = i < n_slots ? ro[i] : -1;
   } else {
     int b = 0, p = -1;
     if (!resolve_row(a.rows, r, b, p)) {
@@ -557,7 +565,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
     }
     const int32_t* idx_row = a.indices + (a.indices_row_offset + row_local) * (int64_t)a.K;
     const int32_t* bt = a.rows.block_table + (int64_t)b * a.rows.max_blocks;
-    for (int i = tid; i < nsb * kSB; i += 64 * kNW) {
+    for (int i = tid; i < nsb * kSB; i += NT) {
       int64_t ko = -1;
       if (i < n_slots && p >= 0) {
         const int idx = idx_row[slot0 + i];
@@ -716,8 +724,14 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
         }
       }
       // ---- softmax for this lane's head over keys 16kt + 4grp + v, in log2
-      //      units: t = logit * scale * log2(e) - m2.  Absent keys (only in
-      //      sub-blocks with padding or missing pages) are masked to -inf.
+      //      units: x = logit * scale * log2(e), t = x - m2.  Absent keys
+      //      (only in sub-blocks with padding or missing pages) are masked to
+      //      -inf after the scaling, so any finite scale (zero and negative
+      //      included) leaves them out.
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s[kt][v] *= c2;
       if (valid != 0xFFFFFFFFu) {  // wave-uniform
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -730,7 +744,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[kt][v] * c2);
+          for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[kt][v]);
         m2 = across_rows(mx, FMax());  // -inf only without a valid key
       }
       float pv[8];
@@ -740,9 +754,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float t = fmaf(s[kt][v], c2, -m2);  // -inf for masked keys
+          const float t = s[kt][v] - m2;  // -inf for masked keys
           hot = hot || t > kSlack;
-          m_lane = fmaxf(m_lane, s[kt][v] * c2);
+          m_lane = fmaxf(m_lane, s[kt][v]);
           pv[kt * 4 + v] = t;
         }
       over = over || __ballot(hot) != 0;
@@ -793,88 +807,90 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
   }
 
   lsum = across_rows(lsum, FAdd());
-  // every wave is past the last barrier and every DMA has landed: the tile
-  // buffers are free for staging (16.25 KB per wave)
   const int head0 = hg * (kHPW * kNW) + wave * kHPW;
   if (head0 >= a.H_q) return;
-  write_result_staged(a, r, row_local, chunk, head0, lane, o, m2, lsum,
-                      &tile[0][0] + wave * (16 * (2 * kDv + 16)));
-}
-
-// PER consecutive bf16 values as floats (16-byte load when PER == 8)
-template <int PER>
-__device__ __forceinline__ void load_bf16(const uint16_t* p, float* x) {
-  if constexpr (PER == 8) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __uint_as_float(w[i] << 16);
-      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) x[i] = __uint_as_float((uint32_t)p[i] << 16);
+  if (a.n_chunks > 1) {
+    write_partial<kMT>(a, row_local, chunk, head0, lane, o, m2, lsum);
+    return;
   }
+  // every wave is past the last barrier and every DMA has landed: the tile
+  // buffers are free for staging (16.25 KB per wave)
+  write_out_staged(a, r, head0, lane, o, m2, lsum, &tile[0][0] + wave * (16 * (2 * kDv + 16)));
 }
 
-// Merges the chunks of each (row, head): one wave per head; lane c holds
-// chunk c's (max, sum).  With M the largest max, chunk c weighs
-// g_c = 2^(max_c - M); out = sum_c g_c O_c / sum_c g_c sum_c, where O_c is
-// the chunk's unnormalised output.
+// Merges the chunks of each (row, head) by log-sum-exp: with M the largest
+// chunk max, chunk c weighs g_c = 2^(max_c - M), and out = sum_c g_c O_c /
+// sum_c g_c sum_c.  A workgroup takes one row, one block of 16 heads and up
+// to 8 of its 16-dim tiles; thread t holds 8 consecutive floats of that
+// slice of every chunk's partial (tile t / 32, head (t / 2) % 16, dims
+// 8 (t % 2) .. +7), loaded kBatch chunks per round trip.
 template <int DV>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
-  constexpr int PER = DV / 64;  // dims per lane
-  const int row_local = blockIdx.x;
-  const int r = a.row_begin + row_local;
-  const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (head >= a.H_q) return;
-  const int n = a.n_chunks;  // <= 64
-  const uint16_t* o0 = part_out(a, row_local, 0, DV) + (int64_t)head * DV + lane * PER;
-  const int64_t cstride = (int64_t)a.H_q * DV;
-  // kBatch chunks per round trip; the first batch goes out before the
-  // statistics, so one round trip brings both (chunks past n reload the
-  // last one and get weight 0)
+  constexpr int MT = DV / 16;
+  constexpr int MTW = MT < 8 ? MT : 8;  // tiles per workgroup
   constexpr int kBatch = 16;
-  float x[kBatch][PER];
+  const int row_local = (int)blockIdx.x;
+  const int r = a.row_begin + row_local;
+  const int hb = (int)blockIdx.y;
+  const int tid = (int)threadIdx.x;
+  const int mt_l = tid >> 5, hl = (tid >> 1) & 15, d0 = (tid & 1) * 8;
+  if (mt_l >= MTW) return;
+  const int mt = (int)blockIdx.z * MTW + mt_l;
+  const int head = hb * 16 + hl;
+  const bool head_ok = head < a.H_q;
+  const int n = a.n_chunks;
+  const int64_t cstride = part_block_floats(a.H_q, DV);
+  const float* p0 = part_out(a, row_local, 0, DV) + (int64_t)hb * (MT * 256) + mt * 256 + hl * 16 + d0;
+  const float2* st0 = part_stats(a, row_local, 0) + (head_ok ? head : 0);
+  // one round trip per batch of chunks (partials and statistics together);
+  // the running max M moves batch by batch, rescaling what has accumulated
+  float M = -__builtin_inff();
+  float acc[8];
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u) load_bf16<PER>(o0 + min(u, n - 1) * cstride, x[u]);
-  const float2 st = lane < n ? part_stats(a, row_local, lane)[head] : float2{-__builtin_inff(), 0.0f};
-  const float M = across_wave(st.x, FMax());
-  // no branch on M: with every chunk empty all weights are 0
-  const float f = st.x == -__builtin_inff() ? 0.0f : exp2f(st.x - M);
-  const float Ls = across_wave(f * st.y, FAdd());
-  float acc[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.0f;
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  float Ls = 0.0f;
   for (int c0 = 0; c0 < n; c0 += kBatch) {
-    if (c0 > 0) {
+    v4f x[kBatch][2];
+    float2 st[kBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) load_bf16<PER>(o0 + min(c0 + u, n - 1) * cstride, x[u]);
+    for (int u = 0; u < kBatch; ++u) {
+      const int c = min(c0 + u, n - 1);
+      x[u][0] = *reinterpret_cast<const v4f*>(p0 + c * cstride);
+      x[u][1] = *reinterpret_cast<const v4f*>(p0 + c * cstride + 4);
+      st[u] = st0[(int64_t)c * a.H_q];
+    }
+    float Mb = M;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (c0 + u < n) Mb = fmaxf(Mb, st[u].x);
+    if (Mb > M) {  // (never true while every chunk so far is empty)
+      const float f = M == -__builtin_inff() ? 0.0f : exp2f(M - Mb);
+      Ls *= f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= f;
+      M = Mb;
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const float fu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), min(c0 + u, 63)));
-      const float wu = c0 + u < n ? fu : 0.0f;
+      // empty chunks (max -inf) and chunks past n weigh 0
+      const float wu = (c0 + u < n && st[u].x != -__builtin_inff()) ? exp2f(st[u].x - M) : 0.0f;
+      Ls += wu * st[u].y;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] += x[u][i] * wu;
+      for (int i = 0; i < 4; ++i) {
+        acc[i] += x[u][0][i] * wu;
+        acc[4 + i] += x[u][1][i] * wu;
+      }
     }
   }
+  if (!head_ok) return;
   const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-  uint16_t* orow = a.out + ((int64_t)r * a.H_q + head) * DV + lane * PER;
-  if constexpr (PER == 8) {
-    uint4 w;
-    w.x = pack2(acc[0] * inv, acc[1] * inv);
-    w.y = pack2(acc[2] * inv, acc[3] * inv);
-    w.z = pack2(acc[4] * inv, acc[5] * inv);
-    w.w = pack2(acc[6] * inv, acc[7] * inv);
-    *reinterpret_cast<uint4*>(orow) = w;
-  } else {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) orow[i] = bf16_bits(acc[i] * inv);
-  }
-  if (a.lse && lane == 0)
+  uint4 w;
+  w.x = pack2(acc[0] * inv, acc[1] * inv);
+  w.y = pack2(acc[2] * inv, acc[3] * inv);
+  w.z = pack2(acc[4] * inv, acc[5] * inv);
+  w.w = pack2(acc[6] * inv, acc[7] * inv);
+  *reinterpret_cast<uint4*>(a.out + ((int64_t)r * a.H_q + head) * DV + 16 * mt + d0) = w;
+  if (a.lse && blockIdx.z == 0 && mt_l == 0 && d0 == 0)
     a.lse[(int64_t)r * a.H_q + head] = Ls > 0.0f ? (M + log2f(Ls)) * kLn2 : -__builtin_inff();
 }
 
@@ -890,6 +906,10 @@ int waves_for(int H_q, int D_qk, bool latent) {
   return (H_q > kHPW || D_qk > 64) ? 4 : 1;
 }
 
+bool uses_latent_kernel(int D_qk, bool latent) {
+  return D_qk == 576 && latent && DSA_ATTN_LATENT_DMA;
+}
+
 template <int DQK, int DV, int NW>
 hipError_t launch_t(const AttnLaunch& a, hipStream_t s) {
   AttnGrid g;
@@ -900,20 +920,24 @@ hipError_t launch_t(const AttnLaunch& a, hipStream_t s) {
   const int grid = (g.n_units + 7) / 8 * 8 * g.n_hg;
   bool done = false;
   if constexpr (DQK == lat::kDqk && NW > 1) {
-    if (DSA_ATTN_LATENT_DMA && a.latent) {
+    if (uses_latent_kernel(DQK, a.latent)) {
       sparse_attn_latent_kernel<DSA_ATTN_NBUF, NW><<<grid, 64 * NW, 0, s>>>(a, g);
       done = true;
     }
   }
-  if (!done) {
-    if (a.latent)
-      sparse_attn_kernel<DQK, DV, true, NW><<<grid, 64 * NW, 0, s>>>(a, g);
-    else
-      sparse_attn_kernel<DQK, DV, false, NW><<<grid, 64 * NW, 0, s>>>(a, g);
+  // (the 576-wide staged kernel only ever runs with four waves)
+  if constexpr (DQK != lat::kDqk || NW == 4) {
+    if (!done) {
+      if (a.latent)
+        sparse_attn_kernel<DQK, DV, true, NW><<<grid, 64 * NW, 0, s>>>(a, g);
+      else
+        sparse_attn_kernel<DQK, DV, false, NW><<<grid, 64 * NW, 0, s>>>(a, g);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks == 1) return e;
-  attn_combine_kernel<DV><<<dim3(a.num_rows, (a.H_q + 3) / 4), 256, 0, s>>>(a);
+  constexpr int MT = DV / 16, MTW = MT < 8 ? MT : 8;
+  attn_combine_kernel<DV><<<dim3(a.num_rows, (a.H_q + 15) / 16, MT / MTW), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -924,18 +948,24 @@ int attn_chunks(int num_rows, int H_q, int D_qk, int K, bool latent) {
   const int hpw = kHPW * waves_for(H_q, D_qk, latent);
   const int n_hg = (H_q + hpw - 1) / hpw;
   const int want = (DSA_ATTN_TARGET_WGS + num_rows * n_hg - 1) / (num_rows * n_hg);
-  const int least = (K + kMaxChunk - 1) / kMaxChunk;  // chunks must fit kMaxChunk slots
+  const int cap = uses_latent_kernel(D_qk, latent) ? kMaxChunkLat : kMaxChunk;
+  const int least = (K + cap - 1) / cap;  // chunks must fit the kernel's slots
   const int most = max(least, min(DSA_ATTN_MAX_CHUNKS, (K + kSB - 1) / kSB));
   return min(64, max(least, min(want, most)));
 }
 
 size_t attn_partial_bytes(int num_rows, int H_q, int D_v, int n_chunks) {
   if (n_chunks <= 1) return 0;
-  return part_stats_bytes(num_rows, n_chunks, H_q) + (size_t)num_rows * n_chunks * H_q * D_v * 2;
+  return part_stats_bytes(num_rows, n_chunks, H_q) +
+         (size_t)num_rows * n_chunks * part_block_floats(H_q, D_v) * sizeof(float);
 }
 
 int attn_chunks_max(int num_rows, int H_q, int D_qk, int K) {
   return max(attn_chunks(num_rows, H_q, D_qk, K, true), attn_chunks(num_rows, H_q, D_qk, K, false));
+}
+
+bool attn_uses_rowoff(int D_qk, int D_v, bool latent) {
+  return D_v == lat::kDv && uses_latent_kernel(D_qk, latent);
 }
 
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s) {

@@ -1,0 +1,591 @@
+// Exact per-row Top-K selection by one workgroup of NT threads.
+//
+// Method: Baidu AI Cloud, "Day0 Inference Support and Performance
+// Optimization for New Architecture LLMs", section 2.2 (keep the Top-K most
+// relevant historical positions).  Readings: ties go to the lower position,
+// the kept positions are written in ascending order, -1 pads to K.
+//
+// Scores are compared through score_key (order-preserving, NaN below every
+// number).  The selection is exact.  A row takes one of these routes:
+//  - at most K slots: keep every slot;
+//  - at most NT * kPer slots: select on all of its keys, held in registers;
+//  - a summary row (sum_row: more than 16384 and at most kSumMaxLen slots,
+//    K <= kSumMaxK): select on the row's summary, the kSumM largest keys of
+//    each segment of G slots with their offsets, which the indexer's
+//    epilogue (or the standalone summary pass) wrote:
+//      1. T1 = the K-th largest summary key.  The summary keys sit at distinct
+//         slots, so the row holds at least K keys >= T1.
+//      2. A segment whose smallest summary key is >= T1 (and that has more
+//         than kSumM slots) may hide further keys >= T1: it is saturated.
+//         Every other segment keeps all of its keys >= T1 in the summary
+//         (they exceed its kSumM-th largest key).
+//      3. Nothing saturated (the usual case): the summary's keys >= T1 are
+//         exactly the row's, T = T1, and the summary itself is emitted.
+//      4. Otherwise the candidates -- summary keys >= T1 of unsaturated
+//         segments and the saturated segments' keys >= T1, re-read from the
+//         score row -- are exactly the row's keys >= T1.  They are staged in
+//         LDS in slot order, T is their K-th largest, and they are emitted.
+//         Too many of them for the staging falls back to the streamed route.
+//  - otherwise (streamed): histogram passes over the row's keys read from
+//    memory narrow the range to T, then one pass emits.
+//
+// The kept slots are staged in LDS (slot -> position) and written out at the
+// end in one coalesced pass, with the KV row offsets when wanted.
+//
+// Selection of the K-th largest key (select_kth): histograms of 2048 bins
+// laid over the current key range [lo, hi] narrow the range to the bin that
+// holds the wanted rank, until one key value remains or the bin holds at
+// most kSmall keys, which one wave then ranks directly.
+//
+// The code is kept small on purpose: a selection runs once per row, so its
+// instructions are fetched cold, and a long unrolled body costs more in
+// instruction fetch than it saves in issue.  Loops over LDS stay loops.
+#pragma once
+
+#include "dsa_common.h"
+
+namespace dsa {
+namespace sel {
+
+constexpr int kBinBits = 11;
+constexpr int kBins = 1 << kBinBits;   // 2048
+constexpr int kSmall = 64;             // bin size ranked directly by one wave
+constexpr int kPer = 16;               // keys per thread on the register routes
+constexpr int kCandMax = 8192;         // candidates staged in LDS (saturated summary rows)
+constexpr int kStageK = 2048;          // largest K whose selection is staged in LDS
+
+// LDS of one selection.  hist doubles as the histogram of every pass.
+template <int NT>
+struct Smem {
+  static constexpr int kWaves = NT / 64;
+  uint32_t hist[kBins];
+  uint32_t ckey[kCandMax];
+  int32_t cpos[kCandMax];
+  int32_t pos[kStageK];  // kept slot -> position
+  uint32_t buf[kSmall];
+  uint32_t res[4];
+  alignas(16) uint32_t wsum[kWaves < 4 ? 4 : kWaves];
+  alignas(16) uint32_t red[3 * (kWaves < 4 ? 4 : kWaves)];
+};
+
+// ------------------------------------------------------------ wave / block
+// DPP controls: row_shr:n = 0x110 + n; row_bcast:15 = 0x142; row_bcast:31 =
+// 0x143.  A lane whose DPP source is absent (or whose row is masked off)
+// receives `id`, the identity of the operation.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp(uint32_t id, uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, kCtrl, kRowMask, 0xF, false);
+}
+
+// Inclusive prefix over the 64 lanes of a wave, for an associative op with
+// identity id.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x, uint32_t id, Op op) {
+  x = op(x, dpp<0x111, 0xF>(id, x));
+  x = op(x, dpp<0x112, 0xF>(id, x));
+  x = op(x, dpp<0x114, 0xF>(id, x));
+  x = op(x, dpp<0x118, 0xF>(id, x));
+  x = op(x, dpp<0x142, 0xA>(id, x));
+  x = op(x, dpp<0x143, 0xC>(id, x));
+  return x;
+}
+struct Add { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
+struct Min { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); } };
+struct Max { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); } };
+
+// Exclusive prefix sum over the block in thread order; `tot` receives the
+// total.  Starts with no barrier and ends with one: wsum is free afterwards.
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t* wsum, uint32_t& tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t inc = wave_scan(x, 0u, Add());
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0;
+  tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    const uint32_t v = wsum[i];
+    tot += v;
+    before += i < wave ? v : 0u;
+  }
+  __syncthreads();
+  return before + inc - x;
+}
+
+// Min, max and sum over the block (results in every thread).  Ends with a
+// barrier after which `red` is free.
+template <int NT>
+__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_t& sum,
+                                             uint32_t* red) {
+  constexpr int W = NT / 64;
+  mn = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan(mn, 0xFFFFFFFFu, Min()), 63);
+  mx = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan(mx, 0u, Max()), 63);
+  sum = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan(sum, 0u, Add()), 63);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    red[wave] = mn;
+    red[W + wave] = mx;
+    red[2 * W + wave] = sum;
+  }
+  __syncthreads();
+  sum = 0;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    mn = min(mn, red[i]);
+    mx = max(mx, red[W + i]);
+    sum += red[2 * W + i];
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ int bitlen32(uint32_t x) { return x ? 32 - __clz(x) : 0; }
+
+// The need-th largest key (1-based, with multiplicity) among the keys in
+// [lo, hi] that visit(f) hands to f in the threads of the block; there must
+// be at least `need` of them.  On return `need` holds how many keys equal to
+// the result belong to the need largest (the others are larger).  Every
+// thread calls it with the same lo, hi and need; it starts and ends with
+// every thread past a barrier.
+template <int NT, class Visit>
+__device__ __forceinline__ uint32_t select_kth(Visit visit, uint32_t lo, uint32_t hi,
+                                               uint32_t& need, Smem<NT>& s) {
+  constexpr int BPT = kBins / NT;  // bins per thread of the scan, from the top
+  const int tid = threadIdx.x;
+  while (lo < hi) {
+    const int shift = max(0, bitlen32(hi - lo) - kBinBits);
+    for (int i = tid; i < kBins; i += NT) s.hist[i] = 0;
+    __syncthreads();
+    visit([&](uint32_t k) {
+      if (k >= lo && k <= hi) atomicAdd(&s.hist[(k - lo) >> shift], 1u);
+    });
+    __syncthreads();
+    // the bin b with above(b) < need <= above(b) + hist[b]
+    {
+      const int top = kBins - 1 - BPT * tid;
+      uint32_t mine = 0;
+      for (int i = 0; i < BPT; ++i) mine += s.hist[top - i];
+      uint32_t tot;
+      uint32_t above = block_scan<NT>(mine, s.wsum, tot);
+      for (int i = 0; i < BPT; ++i) {
+        const uint32_t c = s.hist[top - i];
+        if (above < need && need <= above + c) {
+          s.res[0] = (uint32_t)(top - i);
+          s.res[1] = above;
+          s.res[2] = 0;
+        }
+        above += c;
+      }
+      __syncthreads();
+    }
+    const uint32_t b = s.res[0];
+    need -= s.res[1];
+    const uint32_t cnt = s.hist[b];
+    const uint32_t nlo = lo + (b << shift);
+    const uint32_t span = (1u << shift) - 1u;
+    hi = (hi - nlo <= span) ? hi : nlo + span;
+    lo = nlo;
+    if (lo < hi && cnt <= (uint32_t)kSmall) {
+      // rank the bin's keys directly: wave 0, one key per lane
+      visit([&](uint32_t k) {
+        if (k >= lo && k <= hi) s.buf[atomicAdd(&s.res[2], 1u)] = k;
+      });
+      __syncthreads();
+      if (tid < 64) {
+        const uint32_t m = s.res[2];
+        const uint32_t x = (uint32_t)tid < m ? s.buf[tid] : 0u;
+        uint32_t gt = 0, ge = 0;
+        for (uint32_t i = 0; i < m; ++i) {
+          const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, (int)i);
+          gt += y > x ? 1u : 0u;
+          ge += y >= x ? 1u : 0u;
+        }
+        if ((uint32_t)tid < m && gt < need && need <= ge) {  // equal keys write equal values
+          s.res[0] = x;
+          s.res[1] = need - gt;
+        }
+      }
+      __syncthreads();
+      const uint32_t T = s.res[0];
+      need = s.res[1];
+      __syncthreads();
+      return T;
+    }
+    __syncthreads();  // the next pass rewrites hist and res
+  }
+  return lo;
+}
+
+// Emission bookkeeping: every key larger than T is kept, and the first
+// need_eq keys equal to T in slot order.  After one block scan of each
+// thread's counts (emit_begin), keep() walks the thread's keys in order.
+struct Emit {
+  uint32_t T, need_eq;
+  uint32_t slot, eq;  // this thread's next output slot, equal keys before it
+  __device__ __forceinline__ bool keep(uint32_t k) {
+    const bool is_eq = k == T;
+    const bool kp = k > T || (is_eq && eq < need_eq);
+    eq += is_eq ? 1u : 0u;
+    return kp;
+  }
+};
+// Sets e.slot / e.eq for this thread from its counts of larger and equal
+// keys (each total below 2^16).  Ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void emit_begin(Emit& e, uint32_t gt, uint32_t eq, Smem<NT>& s) {
+  uint32_t tot;
+  const uint32_t ex = block_scan<NT>((eq << 16) | gt, s.wsum, tot);
+  e.eq = ex >> 16;
+  e.slot = (ex & 0xFFFFu) + min(e.eq, e.need_eq);
+}
+
+// ------------------------------------------------------------------ output
+// The selection is staged as slot -> position in s.pos (K <= kStageK) and
+// written out by flush(): indices, and with `roff` the byte offset of each
+// kept position's row in a paged KV cache (block id from the row's block
+// table `bt`, or its LDS copy `bt_lds`; -1, and DSA_DEVERR_BLOCK, for a
+// block id out of range).  Slots are written as positions: the slot itself,
+// or cand[slot] for a candidate-restricted row (checked against the history;
+// an entry outside it is reported and written as 0).
+struct Out {
+  int32_t* gidx;
+  int64_t* roff;
+  const int32_t* cand;
+  int hist;
+  uint32_t* err;
+  const int32_t* bt;
+  const int32_t* bt_lds;
+  int64_t kv_blocks, kv_block_stride, kv_row_stride;
+};
+__device__ __forceinline__ int out_position(const Out& o, int slot) {
+  if (!o.cand) return slot;
+  const int p = o.cand[slot];
+  if (p >= 0 && p < o.hist) return p;
+  report(o.err, DSA_DEVERR_ROW);
+  return 0;
+}
+__device__ __forceinline__ int64_t out_row_offset(const Out& o, int p) {
+  const int phys = o.bt_lds ? o.bt_lds[p >> 6] : o.bt[p >> 6];
+  if (phys >= 0 && (int64_t)phys < o.kv_blocks)
+    return (int64_t)phys * o.kv_block_stride + (int64_t)(p & 63) * o.kv_row_stride;
+  report(o.err, DSA_DEVERR_BLOCK);
+  return -1;
+}
+// Writes slots [0, K): the staged selection's first `count`, then -1.
+template <int NT>
+__device__ __forceinline__ void flush(const Out& o, int K, int count, const int32_t* staged) {
+  for (int j = threadIdx.x; j < K; j += NT) {
+    const int p = j < count ? out_position(o, staged[j]) : -1;
+    o.gidx[j] = p;
+    if (o.roff) o.roff[j] = p >= 0 ? out_row_offset(o, p) : -1;
+  }
+}
+// Direct write of one kept slot (selections too large to stage).
+__device__ __forceinline__ void put_direct(const Out& o, uint32_t slot, int s) {
+  const int p = out_position(o, s);
+  o.gidx[slot] = p;
+  if (o.roff) o.roff[slot] = out_row_offset(o, p);
+}
+
+// ------------------------------------------------------------------ routes
+
+// Keys of one route in registers: kPer per thread, entry j of thread t at
+// slot p[j]; threads and entries in slot order; key 0 = no entry.
+struct Regs {
+  uint32_t k[kPer];
+  int32_t p[kPer];
+};
+
+// Emits the register keys given T and its budget, into s.pos.
+template <int NT>
+__device__ __forceinline__ void regs_emit(const Regs& r, uint32_t T, uint32_t need_eq, Smem<NT>& s) {
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    gt += r.k[j] > T ? 1u : 0u;
+    eq += r.k[j] == T ? 1u : 0u;
+  }
+  Emit e;
+  e.T = T;
+  e.need_eq = need_eq;
+  emit_begin<NT>(e, gt, eq, s);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (e.keep(r.k[j])) s.pos[e.slot++] = r.p[j];
+}
+
+// Streamed: histogram passes over the keys read from memory, then one
+// emission pass (staged when K allows, else straight to memory).
+template <int NT>
+__device__ __forceinline__ void select_streamed(const float* sc, int L, int K, const Out& o,
+                                                int count, Smem<NT>& s) {
+  auto visit = [&](auto f) {
+    for (int i = threadIdx.x; i < L; i += NT) f(score_key(sc[i]));
+  };
+  uint32_t need = (uint32_t)K;
+  const uint32_t T = select_kth<NT>(visit, 1u, 0xFFFFFFFFu, need, s);
+  // runs of NT * R slots, R consecutive per thread
+  constexpr int R = 8;
+  uint32_t out_before = 0, eq_before = 0;
+  for (int i0 = 0; i0 < L && out_before < (uint32_t)K; i0 += NT * R) {
+    const int p0 = i0 + R * (int)threadIdx.x;
+    uint32_t gt = 0, eq = 0;
+    for (int j = 0; j < R; ++j) {
+      const uint32_t k = p0 + j < L ? score_key(sc[p0 + j]) : 0u;
+      gt += k > T ? 1u : 0u;
+      eq += k == T ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t ex = block_scan<NT>((eq << 16) | gt, s.wsum, tot);
+    Emit e;
+    e.T = T;
+    e.need_eq = need;
+    e.eq = eq_before + (ex >> 16);
+    e.slot = out_before + (ex & 0xFFFFu) + min(e.eq, need) - min(eq_before, need);
+    for (int j = 0; j < R; ++j) {
+      const uint32_t k = p0 + j < L ? score_key(sc[p0 + j]) : 0u;
+      if (k != 0u && e.keep(k)) {
+        if (K <= kStageK)
+          s.pos[e.slot] = p0 + j;
+        else
+          put_direct(o, e.slot, p0 + j);
+        ++e.slot;
+      }
+    }
+    out_before += (tot & 0xFFFFu) + min(eq_before + (tot >> 16), need) - min(eq_before, need);
+    eq_before += tot >> 16;
+  }
+  __syncthreads();
+  if (K <= kStageK) flush<NT>(o, K, count, s.pos);
+}
+
+// Whether segment q of this thread's share of a summary row is saturated.
+__device__ __forceinline__ bool seg_saturated(const Regs& r, int q, int sg, int L, int G, uint32_t T1) {
+  uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+  for (int j = 0; j < kSumM; ++j) mn = min(mn, r.k[q * kSumM + j]);
+  return sg * G < L && min(G, L - sg * G) > kSumM && mn >= T1;
+}
+
+// A saturated summary row: candidates in LDS (step 4 above) into s.pos.
+// Returns false when they do not fit.
+template <int NT>
+__device__ __forceinline__ bool summary_saturated(const float* sc, int L, int G, const Regs& r,
+                                                  uint32_t T1, uint32_t kmax, int K, Smem<NT>& s) {
+  // per thread, in slot order: summary keys >= T1 of unsaturated segments,
+  // every key >= T1 of saturated ones (re-read)
+  constexpr int SPT = kPer / kSumM;
+  const int tid = threadIdx.x;
+  uint32_t c = 0;
+#pragma unroll
+  for (int q = 0; q < SPT; ++q) {
+    const int sg = tid * SPT + q;
+    if (seg_saturated(r, q, sg, L, G, T1)) {
+      for (int i = sg * G; i < min(L, sg * G + G); ++i) c += score_key(sc[i]) >= T1 ? 1u : 0u;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSumM; ++j) c += r.k[q * kSumM + j] >= T1 ? 1u : 0u;
+    }
+  }
+  uint32_t n_cand;
+  uint32_t b = block_scan<NT>(c, s.wsum, n_cand);
+  if (n_cand > (uint32_t)kCandMax) return false;
+#pragma unroll
+  for (int q = 0; q < SPT; ++q) {
+    const int sg = tid * SPT + q;
+    if (seg_saturated(r, q, sg, L, G, T1)) {
+      for (int i = sg * G; i < min(L, sg * G + G); ++i) {
+        const uint32_t k = score_key(sc[i]);
+        if (k >= T1) {
+          s.ckey[b] = k;
+          s.cpos[b] = i;
+          ++b;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSumM; ++j)
+        if (r.k[q * kSumM + j] >= T1) {
+          s.ckey[b] = r.k[q * kSumM + j];
+          s.cpos[b] = r.p[q * kSumM + j];
+          ++b;
+        }
+    }
+  }
+  __syncthreads();
+  uint32_t need = (uint32_t)K;
+  const uint32_t T = select_kth<NT>(
+      [&](auto f) {
+        for (int i = threadIdx.x; i < (int)n_cand; i += NT) f(s.ckey[i]);
+      },
+      T1, kmax, need, s);
+  // emission: thread t takes candidates qn t .. qn t + qn - 1
+  const int qn = ((int)n_cand + NT - 1) / NT;
+  const int i0 = min((int)n_cand, qn * tid), i1 = min((int)n_cand, i0 + qn);
+  uint32_t gt = 0, eq = 0;
+  for (int i = i0; i < i1; ++i) {
+    gt += s.ckey[i] > T ? 1u : 0u;
+    eq += s.ckey[i] == T ? 1u : 0u;
+  }
+  Emit e;
+  e.T = T;
+  e.need_eq = need;
+  emit_begin<NT>(e, gt, eq, s);
+  for (int i = i0; i < i1; ++i)
+    if (e.keep(s.ckey[i])) s.pos[e.slot++] = s.cpos[i];
+  return true;
+}
+
+// A thread's share of a row's summary: its kPer / kSumM segments, loaded
+// before the row's length is known (the summary area always holds
+// kSumSegMax segments per row; entries of segments past the row are masked
+// by summary_positions once it is).  The offsets stay packed in p[] until
+// then.
+template <int NT>
+__device__ __forceinline__ void load_summary(const uint32_t* skey, const uint8_t* soff, Regs& r) {
+  constexpr int SPT = kPer / kSumM;
+  static_assert(SPT * NT == kSumSegMax, "segments per thread");
+#pragma unroll
+  for (int q = 0; q < SPT; ++q) {
+    const int sg = (int)threadIdx.x * SPT + q;
+    const uint4 a = *reinterpret_cast<const uint4*>(skey + sg * kSumM);
+    const uint4 b = *reinterpret_cast<const uint4*>(skey + sg * kSumM + 4);
+    const uint2 c = *reinterpret_cast<const uint2*>(soff + sg * kSumM);
+    r.k[q * 8 + 0] = a.x; r.k[q * 8 + 1] = a.y; r.k[q * 8 + 2] = a.z; r.k[q * 8 + 3] = a.w;
+    r.k[q * 8 + 4] = b.x; r.k[q * 8 + 5] = b.y; r.k[q * 8 + 6] = b.z; r.k[q * 8 + 7] = b.w;
+    r.p[q * 8] = (int32_t)c.x;
+    r.p[q * 8 + 1] = (int32_t)c.y;
+  }
+}
+// Turns the loaded summary's offsets into slots and masks segments past
+// the row.
+template <int NT>
+__device__ __forceinline__ void summary_positions(Regs& r, int L, int G) {
+  constexpr int SPT = kPer / kSumM;
+  const int nseg = (L + G - 1) / G;
+#pragma unroll
+  for (int q = 0; q < SPT; ++q) {
+    const int sg = (int)threadIdx.x * SPT + q;
+    const uint32_t w0 = (uint32_t)r.p[q * 8], w1 = (uint32_t)r.p[q * 8 + 1];
+    const bool in = sg < nseg;
+#pragma unroll
+    for (int j = 0; j < kSumM; ++j) {
+      const uint32_t w = j < 4 ? w0 : w1;
+      r.p[q * 8 + j] = sg * G + (int)((w >> (8 * (j & 3))) & 0xFFu);
+      r.k[q * 8 + j] = in ? r.k[q * 8 + j] : 0u;  // (a select, not a conditional store)
+    }
+  }
+}
+
+// The whole selection of one row, written through `o` (every slot of
+// [0, K): kept positions ascending, then -1).  `sc` is the row's score row
+// (L slots, 16-byte aligned when vec); `r` holds this thread's preloaded
+// share of the row's summary when has_sum (it is overwritten).  Returns
+// min(K, L).  All threads of the block call it; it ends with every thread
+// past a barrier.
+template <int NT>
+__device__ __forceinline__ int select_row(const float* sc, bool vec, int L, int K, Regs& r,
+                                          bool has_sum, const Out& o, Smem<NT>& s) {
+  const int tid = threadIdx.x;
+  const int count = max(0, min(K, L));
+  if (L <= K) {  // keep every slot
+    if (K <= kStageK) {
+      for (int j = tid; j < count; j += NT) s.pos[j] = j;
+      __syncthreads();
+      flush<NT>(o, K, count, s.pos);
+    } else {
+      for (int j = tid; j < K; j += NT) {
+        if (j < count) {
+          put_direct(o, (uint32_t)j, j);
+        } else {
+          o.gidx[j] = -1;
+          if (o.roff) o.roff[j] = -1;
+        }
+      }
+    }
+    __syncthreads();
+    return count;
+  }
+  const bool full = L <= NT * kPer && K <= kStageK;
+  const bool summ = !full && has_sum && sum_row(L, K);
+  if (full || summ) {
+    int G = 0;
+    if (full) {
+      const int g0 = kPer * tid;
+#pragma unroll
+      for (int j = 0; j < kPer; j += 4) {
+        float4 v;
+        if (vec && g0 + j + 4 <= L) {
+          v = *reinterpret_cast<const float4*>(sc + g0 + j);
+        } else {
+          v.x = g0 + j < L ? sc[g0 + j] : 0.0f;
+          v.y = g0 + j + 1 < L ? sc[g0 + j + 1] : 0.0f;
+          v.z = g0 + j + 2 < L ? sc[g0 + j + 2] : 0.0f;
+          v.w = g0 + j + 3 < L ? sc[g0 + j + 3] : 0.0f;
+        }
+        r.k[j] = g0 + j < L ? score_key(v.x) : 0u;
+        r.k[j + 1] = g0 + j + 1 < L ? score_key(v.y) : 0u;
+        r.k[j + 2] = g0 + j + 2 < L ? score_key(v.z) : 0u;
+        r.k[j + 3] = g0 + j + 3 < L ? score_key(v.w) : 0u;
+        r.p[j] = g0 + j;
+        r.p[j + 1] = g0 + j + 1;
+        r.p[j + 2] = g0 + j + 2;
+        r.p[j + 3] = g0 + j + 3;
+      }
+    } else {
+      G = sum_seg(L);
+      summary_positions<NT>(r, L, G);
+    }
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, n = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (r.k[j] != 0u) {
+        kmin = min(kmin, r.k[j]);
+        kmax = max(kmax, r.k[j]);
+        ++n;
+      }
+    block_minmax<NT>(kmin, kmax, n, s.red);
+    if (n >= (uint32_t)K) {  // always, for every row that takes these routes
+      uint32_t need = (uint32_t)K;
+      const uint32_t T1 = select_kth<NT>(
+          [&](auto f) {
+#pragma unroll
+            for (int j = 0; j < kPer; ++j)
+              if (r.k[j] != 0u) f(r.k[j]);
+          },
+          kmin, kmax, need, s);
+      bool done = true;
+      uint32_t n_sat = 0;
+      if (summ) {
+        constexpr int SPT = kPer / kSumM;
+        uint32_t sat = 0;
+#pragma unroll
+        for (int q = 0; q < SPT; ++q) sat += seg_saturated(r, q, tid * SPT + q, L, G, T1) ? 1u : 0u;
+        block_scan<NT>(sat, s.wsum, n_sat);
+      }
+      if (n_sat > 0)
+        done = summary_saturated<NT>(sc, L, G, r, T1, kmax, K, s);
+      else
+        regs_emit<NT>(r, T1, need, s);
+      if (done) {
+        __syncthreads();
+        flush<NT>(o, K, count, s.pos);
+        __syncthreads();
+        return count;
+      }
+    }
+    __syncthreads();
+  }
+  select_streamed<NT>(sc, L, K, o, count, s);
+  if (K > kStageK) {  // padding of an unstaged selection
+    for (int j = count + tid; j < K; j += NT) {
+      o.gidx[j] = -1;
+      if (o.roff) o.roff[j] = -1;
+    }
+  }
+  __syncthreads();
+  return count;
+}
+
+}  // namespace sel
+}  // namespace dsa

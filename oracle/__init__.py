@@ -22,7 +22,7 @@ numeric example for any step):
   - section 4.2: the attention core gathers the selected rows of the main KV
     cache from the indexer's position list;
   - section 4.3: the fused call takes the quantised query, the index keys and
-    the head weights, ``idx = fused_topk(q8, k, g)``;
+    the head weights and returns the selected positions;
   - section 5.1 / 5.2: FP8 storage for the indexer and the KV cache; the
     indexer's MXFP8 format (one shared scale per group of 32).
 * vLLM's DeepSeek-V4.1-Flash article, "Kernels": later indexer layers score

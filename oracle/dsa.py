@@ -70,9 +70,9 @@ def indexer_scores_row(qI_codes, w, kI_rows, qI_scale=None, kI_scale=None):
     I[s] = sum_h w[h] * max(0, sum_d qI[h, d] * kI[s, d])
 
     Scoring against every historical position, then aggregating the per-head
-    scores with head weights (Day0 article, section 2.2; the fused call
-    ``fused_topk(q8, k, g)`` of section 4.3 takes exactly these three
-    inputs).  Readings: the per-head score passes a ReLU gate before the
+    scores with head weights (Day0 article, section 2.2; the fused call of
+    section 4.3 takes exactly these three inputs: the quantised query, the
+    index keys and the head weights).  Readings: the per-head score passes a ReLU gate before the
     weighting; one shared index key per position serves every indexer head.
 
     The per-head dot products are exact in binary64: E4M3 products carry at

@@ -158,6 +158,8 @@ def test_sparse_attn_rejections():
                           ctypes.c_void_p(out), ctypes.c_void_p(lse), ctypes.c_void_p(ws),
                           ctypes.c_size_t(nbytes), None)
     assert call(prob(D_qk=128, D_v=128)) == B.DSA_ERR_UNSUPPORTED
+    assert call(prob(K=16385)) == B.DSA_ERR_UNSUPPORTED              # above DSA_MAX_ATTN_K
+    assert call(prob(K=16384), nbytes=0) == B.DSA_ERR_WORKSPACE      # shape accepted
     assert call(prob(scale=float("nan"))) == B.DSA_ERR_INVALID
     assert call(prob(), k=paged(row=1024)) == B.DSA_ERR_INVALID      # K row < 576 bf16
     assert call(prob(), q=FAKE + 4) == B.DSA_ERR_INVALID
