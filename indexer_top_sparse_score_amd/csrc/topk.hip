@@ -13,7 +13,10 @@
 namespace dsa {
 namespace {
 
-constexpr int kNT = 1024;  // threads of a selecting workgroup
+#ifndef DSA_TOPK_THREADS
+#define DSA_TOPK_THREADS 1024
+#endif
+constexpr int kNT = DSA_TOPK_THREADS;  // threads of a selecting workgroup
 constexpr int kBtCache = 2048;  // block-table entries cached in LDS
 
 // One wave per 128 slots of a summary row writes that span's summary entries.
@@ -36,14 +39,14 @@ __global__ __launch_bounds__(256) void topk_summary_kernel(TopkLaunch a) {
 // One row per workgroup.  The first round trip brings the row's length, its
 // summary (whatever the length turns out to be) and, for row offsets, its
 // block table; the selection then runs on-chip.
-__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(1, 4))) void topk_select_kernel(TopkLaunch a) {
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(1, kNT >= 1024 ? 4 : kNT >= 512 ? 2 : 1))) void topk_select_kernel(TopkLaunch a) {
   __shared__ sel::Smem<kNT> s;
   __shared__ int32_t bt_lds[kBtCache];
   const int r_local = (int)blockIdx.x;
   const int r = a.row_begin + r_local;
   const int tid = (int)threadIdx.x;
   const RowIssue ri = row_issue(a.rows, r);
-  sel::Regs regs;
+  sel::Regs<kNT> regs;
   const int64_t ro = (int64_t)r_local * kSumEntries;
   if (a.sum.key) sel::load_summary<kNT>(a.sum.key + ro, a.sum.off + ro, regs);
   const int32_t* bt = a.rows.block_table + (int64_t)(ri.b_ok ? ri.b : 0) * a.rows.max_blocks;

@@ -8,7 +8,7 @@
 // Scores are compared through score_key (order-preserving, NaN below every
 // number).  The selection is exact.  A row takes one of these routes:
 //  - at most K slots: keep every slot;
-//  - at most NT * kPer slots: select on all of its keys, held in registers;
+//  - at most kRegKeys slots: select on all of its keys, held in registers;
 //  - a summary row (sum_row: more than 16384 and at most kSumMaxLen slots,
 //    K <= kSumMaxK): select on the row's summary, the kSumM largest keys of
 //    each segment of G slots with their offsets, which the indexer's
@@ -50,7 +50,7 @@ namespace sel {
 constexpr int kBinBits = 11;
 constexpr int kBins = 1 << kBinBits;   // 2048
 constexpr int kSmall = 64;             // bin size ranked directly by one wave
-constexpr int kPer = 16;               // keys per thread on the register routes
+constexpr int kRegKeys = 16384;        // keys held in registers by a workgroup (both routes)
 constexpr int kCandMax = 8192;         // candidates staged in LDS (saturated summary rows)
 constexpr int kStageK = 2048;          // largest K whose selection is staged in LDS
 
@@ -64,7 +64,7 @@ struct Smem {
   int32_t pos[kStageK];  // kept slot -> position
   uint32_t buf[kSmall];
   uint32_t res[4];
-  alignas(16) uint32_t wsum[kWaves < 4 ? 4 : kWaves];
+  alignas(16) uint32_t wsum[2 * kWaves];
   alignas(16) uint32_t red[3 * (kWaves < 4 ? 4 : kWaves)];
 };
 
@@ -94,27 +94,33 @@ struct Min { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { retu
 struct Max { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); } };
 
 // Exclusive prefix sum over the block in thread order; `tot` receives the
-// total.  Starts with no barrier and ends with one: wsum is free afterwards.
+// total.  One barrier.  Consecutive scans alternate between the two halves
+// of wsum (ph counts the scans of this thread), so a scan may start while
+// slower waves still read the previous one's totals: the half it writes was
+// last read before the previous scan's barrier.
 template <int NT>
-__device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t* wsum, uint32_t& tot) {
+__device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t* wsum, uint32_t& ph,
+                                               uint32_t& tot) {
+  constexpr int W = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t* w = wsum + (ph & 1u) * W;
+  ++ph;
   const uint32_t inc = wave_scan(x, 0u, Add());
-  if (lane == 63) wsum[wave] = inc;
+  if (lane == 63) w[wave] = inc;
   __syncthreads();
   uint32_t before = 0;
   tot = 0;
 #pragma unroll
-  for (int i = 0; i < NT / 64; ++i) {
-    const uint32_t v = wsum[i];
+  for (int i = 0; i < W; ++i) {
+    const uint32_t v = w[i];
     tot += v;
     before += i < wave ? v : 0u;
   }
-  __syncthreads();
   return before + inc - x;
 }
 
-// Min, max and sum over the block (results in every thread).  Ends with a
-// barrier after which `red` is free.
+// Min, max and sum over the block (results in every thread).  One barrier;
+// `red` is written once per selection.
 template <int NT>
 __device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_t& sum,
                                              uint32_t* red) {
@@ -136,7 +142,6 @@ __device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_
     mx = max(mx, red[W + i]);
     sum += red[2 * W + i];
   }
-  __syncthreads();
 }
 
 __device__ __forceinline__ int bitlen32(uint32_t x) { return x ? 32 - __clz(x) : 0; }
@@ -149,7 +154,7 @@ __device__ __forceinline__ int bitlen32(uint32_t x) { return x ? 32 - __clz(x) :
 // every thread past a barrier.
 template <int NT, class Visit>
 __device__ __forceinline__ uint32_t select_kth(Visit visit, uint32_t lo, uint32_t hi,
-                                               uint32_t& need, Smem<NT>& s) {
+                                               uint32_t& need, Smem<NT>& s, uint32_t& ph) {
   constexpr int BPT = kBins / NT;  // bins per thread of the scan, from the top
   const int tid = threadIdx.x;
   while (lo < hi) {
@@ -166,7 +171,7 @@ __device__ __forceinline__ uint32_t select_kth(Visit visit, uint32_t lo, uint32_
       uint32_t mine = 0;
       for (int i = 0; i < BPT; ++i) mine += s.hist[top - i];
       uint32_t tot;
-      uint32_t above = block_scan<NT>(mine, s.wsum, tot);
+      uint32_t above = block_scan<NT>(mine, s.wsum, ph, tot);
       for (int i = 0; i < BPT; ++i) {
         const uint32_t c = s.hist[top - i];
         if (above < need && need <= above + c) {
@@ -230,11 +235,12 @@ struct Emit {
   }
 };
 // Sets e.slot / e.eq for this thread from its counts of larger and equal
-// keys (each total below 2^16).  Ends with a barrier.
+// keys (each total below 2^16).
 template <int NT>
-__device__ __forceinline__ void emit_begin(Emit& e, uint32_t gt, uint32_t eq, Smem<NT>& s) {
+__device__ __forceinline__ void emit_begin(Emit& e, uint32_t gt, uint32_t eq, Smem<NT>& s,
+                                           uint32_t& ph) {
   uint32_t tot;
-  const uint32_t ex = block_scan<NT>((eq << 16) | gt, s.wsum, tot);
+  const uint32_t ex = block_scan<NT>((eq << 16) | gt, s.wsum, ph, tot);
   e.eq = ex >> 16;
   e.slot = (ex & 0xFFFFu) + min(e.eq, e.need_eq);
 }
@@ -289,41 +295,54 @@ __device__ __forceinline__ void put_direct(const Out& o, uint32_t slot, int s) {
 
 // ------------------------------------------------------------------ routes
 
-// Keys of one route in registers: kPer per thread, entry j of thread t at
-// slot p[j]; threads and entries in slot order; key 0 = no entry.
+// Keys of one register route, P = kRegKeys / NT per thread, in slot order
+// (threads in order, entries in order); key 0 = no entry.  Full rows: entry
+// j of thread t is slot P t + j.  Summary rows: thread t holds segments
+// SPT t .. SPT t + SPT - 1 (kSumM entries each) and w[] their packed
+// offsets; a slot is worked out only for the entries that are kept.
+template <int NT>
 struct Regs {
-  uint32_t k[kPer];
-  int32_t p[kPer];
+  static constexpr int P = kRegKeys / NT;
+  static constexpr int SPT = P / kSumM;
+  static_assert(SPT * kSumM == P && SPT * NT == kSumSegMax, "summary segments per thread");
+  uint32_t k[P];
+  uint32_t w[2 * SPT];
+  __device__ __forceinline__ int slot(int j, int G) const {  // j a constant once unrolled
+    if (G == 0) return P * (int)threadIdx.x + j;
+    const int q = j / kSumM, e = j % kSumM;
+    return ((int)threadIdx.x * SPT + q) * G + (int)((w[2 * q + (e >> 2)] >> (8 * (e & 3))) & 0xFFu);
+  }
 };
 
 // Emits the register keys given T and its budget, into s.pos.
 template <int NT>
-__device__ __forceinline__ void regs_emit(const Regs& r, uint32_t T, uint32_t need_eq, Smem<NT>& s) {
+__device__ __forceinline__ void regs_emit(const Regs<NT>& r, int G, uint32_t T, uint32_t need_eq,
+                                          Smem<NT>& s, uint32_t& ph) {
   uint32_t gt = 0, eq = 0;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
+  for (int j = 0; j < Regs<NT>::P; ++j) {
     gt += r.k[j] > T ? 1u : 0u;
     eq += r.k[j] == T ? 1u : 0u;
   }
   Emit e;
   e.T = T;
   e.need_eq = need_eq;
-  emit_begin<NT>(e, gt, eq, s);
+  emit_begin<NT>(e, gt, eq, s, ph);
 #pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    if (e.keep(r.k[j])) s.pos[e.slot++] = r.p[j];
+  for (int j = 0; j < Regs<NT>::P; ++j)
+    if (e.keep(r.k[j])) s.pos[e.slot++] = r.slot(j, G);
 }
 
 // Streamed: histogram passes over the keys read from memory, then one
 // emission pass (staged when K allows, else straight to memory).
 template <int NT>
 __device__ __forceinline__ void select_streamed(const float* sc, int L, int K, const Out& o,
-                                                int count, Smem<NT>& s) {
+                                                int count, Smem<NT>& s, uint32_t& ph) {
   auto visit = [&](auto f) {
     for (int i = threadIdx.x; i < L; i += NT) f(score_key(sc[i]));
   };
   uint32_t need = (uint32_t)K;
-  const uint32_t T = select_kth<NT>(visit, 1u, 0xFFFFFFFFu, need, s);
+  const uint32_t T = select_kth<NT>(visit, 1u, 0xFFFFFFFFu, need, s, ph);
   // runs of NT * R slots, R consecutive per thread
   constexpr int R = 8;
   uint32_t out_before = 0, eq_before = 0;
@@ -336,7 +355,7 @@ __device__ __forceinline__ void select_streamed(const float* sc, int L, int K, c
       eq += k == T ? 1u : 0u;
     }
     uint32_t tot;
-    const uint32_t ex = block_scan<NT>((eq << 16) | gt, s.wsum, tot);
+    const uint32_t ex = block_scan<NT>((eq << 16) | gt, s.wsum, ph, tot);
     Emit e;
     e.T = T;
     e.need_eq = need;
@@ -359,28 +378,31 @@ __device__ __forceinline__ void select_streamed(const float* sc, int L, int K, c
   if (K <= kStageK) flush<NT>(o, K, count, s.pos);
 }
 
-// Whether segment q of this thread's share of a summary row is saturated.
-__device__ __forceinline__ bool seg_saturated(const Regs& r, int q, int sg, int L, int G, uint32_t T1) {
+// Whether summary segment q of this thread is saturated.
+template <int NT>
+__device__ __forceinline__ bool seg_saturated(const Regs<NT>& r, int q, int L, int G, uint32_t T1) {
   uint32_t mn = 0xFFFFFFFFu;
 #pragma unroll
   for (int j = 0; j < kSumM; ++j) mn = min(mn, r.k[q * kSumM + j]);
+  const int sg = (int)threadIdx.x * Regs<NT>::SPT + q;
   return sg * G < L && min(G, L - sg * G) > kSumM && mn >= T1;
 }
 
 // A saturated summary row: candidates in LDS (step 4 above) into s.pos.
 // Returns false when they do not fit.
 template <int NT>
-__device__ __forceinline__ bool summary_saturated(const float* sc, int L, int G, const Regs& r,
-                                                  uint32_t T1, uint32_t kmax, int K, Smem<NT>& s) {
+__device__ __forceinline__ bool summary_saturated(const float* sc, int L, int G, const Regs<NT>& r,
+                                                  uint32_t T1, uint32_t kmax, int K, Smem<NT>& s,
+                                                  uint32_t& ph) {
   // per thread, in slot order: summary keys >= T1 of unsaturated segments,
   // every key >= T1 of saturated ones (re-read)
-  constexpr int SPT = kPer / kSumM;
+  constexpr int kSPT = Regs<NT>::SPT;
   const int tid = threadIdx.x;
   uint32_t c = 0;
 #pragma unroll
-  for (int q = 0; q < SPT; ++q) {
-    const int sg = tid * SPT + q;
-    if (seg_saturated(r, q, sg, L, G, T1)) {
+  for (int q = 0; q < kSPT; ++q) {
+    const int sg = tid * kSPT + q;
+    if (seg_saturated<NT>(r, q, L, G, T1)) {
       for (int i = sg * G; i < min(L, sg * G + G); ++i) c += score_key(sc[i]) >= T1 ? 1u : 0u;
     } else {
 #pragma unroll
@@ -388,12 +410,12 @@ __device__ __forceinline__ bool summary_saturated(const float* sc, int L, int G,
     }
   }
   uint32_t n_cand;
-  uint32_t b = block_scan<NT>(c, s.wsum, n_cand);
+  uint32_t b = block_scan<NT>(c, s.wsum, ph, n_cand);
   if (n_cand > (uint32_t)kCandMax) return false;
 #pragma unroll
-  for (int q = 0; q < SPT; ++q) {
-    const int sg = tid * SPT + q;
-    if (seg_saturated(r, q, sg, L, G, T1)) {
+  for (int q = 0; q < kSPT; ++q) {
+    const int sg = tid * kSPT + q;
+    if (seg_saturated<NT>(r, q, L, G, T1)) {
       for (int i = sg * G; i < min(L, sg * G + G); ++i) {
         const uint32_t k = score_key(sc[i]);
         if (k >= T1) {
@@ -407,7 +429,7 @@ __device__ __forceinline__ bool summary_saturated(const float* sc, int L, int G,
       for (int j = 0; j < kSumM; ++j)
         if (r.k[q * kSumM + j] >= T1) {
           s.ckey[b] = r.k[q * kSumM + j];
-          s.cpos[b] = r.p[q * kSumM + j];
+          s.cpos[b] = r.slot(q * kSumM + j, G);
           ++b;
         }
     }
@@ -418,7 +440,7 @@ __device__ __forceinline__ bool summary_saturated(const float* sc, int L, int G,
       [&](auto f) {
         for (int i = threadIdx.x; i < (int)n_cand; i += NT) f(s.ckey[i]);
       },
-      T1, kmax, need, s);
+      T1, kmax, need, s, ph);
   // emission: thread t takes candidates qn t .. qn t + qn - 1
   const int qn = ((int)n_cand + NT - 1) / NT;
   const int i0 = min((int)n_cand, qn * tid), i1 = min((int)n_cand, i0 + qn);
@@ -430,50 +452,28 @@ __device__ __forceinline__ bool summary_saturated(const float* sc, int L, int G,
   Emit e;
   e.T = T;
   e.need_eq = need;
-  emit_begin<NT>(e, gt, eq, s);
+  emit_begin<NT>(e, gt, eq, s, ph);
   for (int i = i0; i < i1; ++i)
     if (e.keep(s.ckey[i])) s.pos[e.slot++] = s.cpos[i];
   return true;
 }
 
-// A thread's share of a row's summary: its kPer / kSumM segments, loaded
-// before the row's length is known (the summary area always holds
-// kSumSegMax segments per row; entries of segments past the row are masked
-// by summary_positions once it is).  The offsets stay packed in p[] until
-// then.
+// A thread's share of a row's summary: its SPT segments, loaded before the
+// row's length is known (the summary area always holds kSumSegMax segments
+// per row; entries of segments past the row are masked once it is).
 template <int NT>
-__device__ __forceinline__ void load_summary(const uint32_t* skey, const uint8_t* soff, Regs& r) {
-  constexpr int SPT = kPer / kSumM;
-  static_assert(SPT * NT == kSumSegMax, "segments per thread");
+__device__ __forceinline__ void load_summary(const uint32_t* skey, const uint8_t* soff, Regs<NT>& r) {
+  constexpr int kSPT = Regs<NT>::SPT;
 #pragma unroll
-  for (int q = 0; q < SPT; ++q) {
-    const int sg = (int)threadIdx.x * SPT + q;
+  for (int q = 0; q < kSPT; ++q) {
+    const int sg = (int)threadIdx.x * kSPT + q;
     const uint4 a = *reinterpret_cast<const uint4*>(skey + sg * kSumM);
     const uint4 b = *reinterpret_cast<const uint4*>(skey + sg * kSumM + 4);
     const uint2 c = *reinterpret_cast<const uint2*>(soff + sg * kSumM);
     r.k[q * 8 + 0] = a.x; r.k[q * 8 + 1] = a.y; r.k[q * 8 + 2] = a.z; r.k[q * 8 + 3] = a.w;
     r.k[q * 8 + 4] = b.x; r.k[q * 8 + 5] = b.y; r.k[q * 8 + 6] = b.z; r.k[q * 8 + 7] = b.w;
-    r.p[q * 8] = (int32_t)c.x;
-    r.p[q * 8 + 1] = (int32_t)c.y;
-  }
-}
-// Turns the loaded summary's offsets into slots and masks segments past
-// the row.
-template <int NT>
-__device__ __forceinline__ void summary_positions(Regs& r, int L, int G) {
-  constexpr int SPT = kPer / kSumM;
-  const int nseg = (L + G - 1) / G;
-#pragma unroll
-  for (int q = 0; q < SPT; ++q) {
-    const int sg = (int)threadIdx.x * SPT + q;
-    const uint32_t w0 = (uint32_t)r.p[q * 8], w1 = (uint32_t)r.p[q * 8 + 1];
-    const bool in = sg < nseg;
-#pragma unroll
-    for (int j = 0; j < kSumM; ++j) {
-      const uint32_t w = j < 4 ? w0 : w1;
-      r.p[q * 8 + j] = sg * G + (int)((w >> (8 * (j & 3))) & 0xFFu);
-      r.k[q * 8 + j] = in ? r.k[q * 8 + j] : 0u;  // (a select, not a conditional store)
-    }
+    r.w[2 * q] = c.x;
+    r.w[2 * q + 1] = c.y;
   }
 }
 
@@ -484,10 +484,11 @@ __device__ __forceinline__ void summary_positions(Regs& r, int L, int G) {
 // min(K, L).  All threads of the block call it; it ends with every thread
 // past a barrier.
 template <int NT>
-__device__ __forceinline__ int select_row(const float* sc, bool vec, int L, int K, Regs& r,
+__device__ __forceinline__ int select_row(const float* sc, bool vec, int L, int K, Regs<NT>& r,
                                           bool has_sum, const Out& o, Smem<NT>& s) {
   const int tid = threadIdx.x;
   const int count = max(0, min(K, L));
+  uint32_t ph = 0;  // block scans so far
   if (L <= K) {  // keep every slot
     if (K <= kStageK) {
       for (int j = tid; j < count; j += NT) s.pos[j] = j;
@@ -506,7 +507,8 @@ __device__ __forceinline__ int select_row(const float* sc, bool vec, int L, int 
     __syncthreads();
     return count;
   }
-  const bool full = L <= NT * kPer && K <= kStageK;
+  constexpr int kPer = Regs<NT>::P, kSPT = Regs<NT>::SPT;
+  const bool full = L <= kRegKeys && K <= kStageK;
   const bool summ = !full && has_sum && sum_row(L, K);
   if (full || summ) {
     int G = 0;
@@ -527,23 +529,24 @@ __device__ __forceinline__ int select_row(const float* sc, bool vec, int L, int 
         r.k[j + 1] = g0 + j + 1 < L ? score_key(v.y) : 0u;
         r.k[j + 2] = g0 + j + 2 < L ? score_key(v.z) : 0u;
         r.k[j + 3] = g0 + j + 3 < L ? score_key(v.w) : 0u;
-        r.p[j] = g0 + j;
-        r.p[j + 1] = g0 + j + 1;
-        r.p[j + 2] = g0 + j + 2;
-        r.p[j + 3] = g0 + j + 3;
       }
     } else {
       G = sum_seg(L);
-      summary_positions<NT>(r, L, G);
+      const int nseg = (L + G - 1) / G;
+#pragma unroll
+      for (int q = 0; q < kSPT; ++q) {
+        const bool in = tid * kSPT + q < nseg;
+#pragma unroll
+        for (int j = 0; j < kSumM; ++j) r.k[q * 8 + j] = in ? r.k[q * 8 + j] : 0u;  // a select
+      }
     }
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, n = 0;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      if (r.k[j] != 0u) {
-        kmin = min(kmin, r.k[j]);
-        kmax = max(kmax, r.k[j]);
-        ++n;
-      }
+    for (int j = 0; j < kPer; ++j) {
+      kmin = min(kmin, r.k[j] != 0u ? r.k[j] : 0xFFFFFFFFu);
+      kmax = max(kmax, r.k[j]);
+      n += r.k[j] != 0u ? 1u : 0u;
+    }
     block_minmax<NT>(kmin, kmax, n, s.red);
     if (n >= (uint32_t)K) {  // always, for every row that takes these routes
       uint32_t need = (uint32_t)K;
@@ -553,20 +556,19 @@ __device__ __forceinline__ int select_row(const float* sc, bool vec, int L, int 
             for (int j = 0; j < kPer; ++j)
               if (r.k[j] != 0u) f(r.k[j]);
           },
-          kmin, kmax, need, s);
+          kmin, kmax, need, s, ph);
       bool done = true;
       uint32_t n_sat = 0;
       if (summ) {
-        constexpr int SPT = kPer / kSumM;
         uint32_t sat = 0;
 #pragma unroll
-        for (int q = 0; q < SPT; ++q) sat += seg_saturated(r, q, tid * SPT + q, L, G, T1) ? 1u : 0u;
-        block_scan<NT>(sat, s.wsum, n_sat);
+        for (int q = 0; q < kSPT; ++q) sat += seg_saturated<NT>(r, q, L, G, T1) ? 1u : 0u;
+        block_scan<NT>(sat, s.wsum, ph, n_sat);
       }
       if (n_sat > 0)
-        done = summary_saturated<NT>(sc, L, G, r, T1, kmax, K, s);
+        done = summary_saturated<NT>(sc, L, G, r, T1, kmax, K, s, ph);
       else
-        regs_emit<NT>(r, T1, need, s);
+        regs_emit<NT>(r, G, T1, need, s, ph);
       if (done) {
         __syncthreads();
         flush<NT>(o, K, count, s.pos);
@@ -576,7 +578,7 @@ __device__ __forceinline__ int select_row(const float* sc, bool vec, int L, int 
     }
     __syncthreads();
   }
-  select_streamed<NT>(sc, L, K, o, count, s);
+  select_streamed<NT>(sc, L, K, o, count, s, ph);
   if (K > kStageK) {  // padding of an unstaged selection
     for (int j = count + tid; j < K; j += NT) {
       o.gidx[j] = -1;
