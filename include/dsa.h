@@ -62,9 +62,10 @@ extern "C" {
 #define DSA_API
 #endif
 
-#define DSA_ABI_VERSION 4
+#define DSA_ABI_VERSION 5
 #define DSA_BLOCK_SIZE 64
 #define DSA_MAX_ATTN_K 16384 /* largest K of dsa_sparse_attn / dsa_decode_step */
+#define DSA_STATIC_SCRATCH_BYTES (64u << 20) /* scratch of dsa_decode_step_static, per GPU */
 
 typedef enum {
   DSA_OK = 0,
@@ -227,6 +228,30 @@ DSA_API int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float
                     const uint16_t* q, dsa_paged k, dsa_paged v, uint16_t* out, float* lse,
                     int32_t* indices_out, int32_t* counts_out, void* ws, size_t ws_bytes,
                     void* stream);
+
+/*
+ * The fused step without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Results are those of dsa_decode_step.
+ * The call itself allocates nothing: the library keeps one scratch array of
+ * DSA_STATIC_SCRATCH_BYTES on every GPU it runs on (reserved when the library
+ * is loaded, held until the process ends) and lays the step out in it,
+ * cutting the rows into smaller passes when needed.  A problem whose layout
+ * does not fit even one row per pass returns DSA_ERR_WORKSPACE and nothing
+ * runs.  The first call on a device looks the array's address up (a HIP
+ * runtime query, no allocation).
+ *   err  optional device pointer to a caller-owned uint32 into which the
+ *        DSA_DEVERR_* bits are OR-ed (sticky, as the workspace error word of
+ *        dsa_decode_step; the caller zeroes it); NULL: not reported
+ * Every call on a GPU shares that GPU's scratch, and the scratch keeps the
+ * last call's contents (nothing in it needs to start at zero): calls that
+ * overlap in time on one GPU -- on different streams, or from different
+ * threads -- race and give undefined results.  Serialise them.
+ */
+DSA_API int dsa_decode_step_static(const dsa_problem* p, const uint8_t* qI, const float* w,
+                                   dsa_paged kI, const uint16_t* q, dsa_paged k, dsa_paged v,
+                                   uint16_t* out, float* lse, int32_t* indices_out,
+                                   int32_t* counts_out, uint32_t* err, void* stream);
 
 /* Static text for a dsa_status value ("unknown status" otherwise). */
 DSA_API const char* dsa_status_string(int status);

@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "dsa_common.h"
 
@@ -116,10 +117,10 @@ int64_t slab_ld(const dsa_problem* p) { return (max_len(p) + 63) & ~int64_t(63);
 // Whether any row of the problem can have a summary (more than 16384 slots).
 bool needs_summary(const dsa_problem* p) { return max_len(p) >= kSumMinLen && p->K <= kSumMaxK; }
 
-int rows_per_pass(const dsa_problem* p) {
+int rows_per_pass(const dsa_problem* p, size_t budget = kScoresBudget) {
   const size_t per_row = (size_t)slab_ld(p) * sizeof(float) +
                          (needs_summary(p) ? (size_t)kSumEntries * 5 : 0);
-  size_t rp = kScoresBudget / per_row;
+  size_t rp = budget / per_row;
   if (rp < 1) rp = 1;
   if (rp > (size_t)p->num_rows) rp = (size_t)p->num_rows;
   return (int)rp;
@@ -141,9 +142,9 @@ struct DecodeLayout {
 // every shape so that the size does not depend on the caches' strides), the
 // float32 score slab, the rows' Top-K summaries and the attention's
 // split-key partials.
-DecodeLayout decode_layout(const dsa_problem* p) {
+DecodeLayout decode_layout(const dsa_problem* p, size_t budget = kScoresBudget) {
   DecodeLayout d;
-  d.rp = rows_per_pass(p);
+  d.rp = rows_per_pass(p, budget);
   const int nc = attn_chunks_max(d.rp, p->H_q, p->D_qk, p->K);
   d.idx_off = kHeader;
   d.roff_off = d.idx_off + round256((size_t)d.rp * p->K * sizeof(int32_t));
@@ -152,6 +153,171 @@ DecodeLayout decode_layout(const dsa_problem* p) {
   d.part_off = d.sum_off + round256(needs_summary(p) ? summary_bytes(d.rp) : 0);
   d.total = d.part_off + round256(attn_partial_bytes(d.rp, p->H_q, p->D_v, nc));
   return d;
+}
+
+int check_attn_args(const dsa_problem* p, const uint16_t* q, const dsa_paged& k,
+                           const dsa_paged& v, uint16_t* out, float* lse) {
+  int st = check_attn_shape(p);
+  if (st != DSA_OK) return st;
+  if (!q || !out) return DSA_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(out, 16) || (lse && !aligned(lse, 4))) return DSA_ERR_INVALID;
+  if ((st = check_paged(k, 2 * (int64_t)p->D_qk)) != DSA_OK) return st;
+  if ((st = check_paged(v, 2 * (int64_t)p->D_v)) != DSA_OK) return st;
+  return DSA_OK;
+}
+
+AttnLaunch attn_launch(const dsa_problem* p, const uint16_t* q, dsa_paged k, dsa_paged v,
+                              uint16_t* out, float* lse, uint32_t* err) {
+  AttnLaunch a;
+  a.rows = row_map(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.latent = is_latent(k, v);
+  a.indices = nullptr;
+  a.indices_row_offset = 0;
+  a.rowoff = nullptr;
+  a.out = out;
+  a.lse = lse;
+  a.partial = nullptr;
+  a.err = err;
+  a.H_q = p->H_q;
+  a.D_qk = p->D_qk;
+  a.D_v = p->D_v;
+  a.K = p->K;
+  a.scale = p->scale;
+  a.row_begin = 0;
+  a.num_rows = p->num_rows;
+  a.n_chunks = 1;
+  return a;
+}
+
+// Validation shared by both fused-step entry points (everything but the
+// workspace).
+int check_decode_args(const dsa_problem* p, const uint8_t* qI, const float* w,
+                      const dsa_paged& kI, const uint16_t* q, const dsa_paged& k,
+                      const dsa_paged& v, uint16_t* out, float* lse, int32_t* indices_out,
+                      int32_t* counts_out) {
+  int st = check_rows(p);
+  if (st != DSA_OK) return st;
+  if ((st = check_indexer_shape(p)) != DSA_OK) return st;
+  if ((st = check_attn_args(p, q, k, v, out, lse)) != DSA_OK) return st;
+  if (!qI || !w || !aligned(qI, 16) || !aligned(w, 4)) return DSA_ERR_INVALID;
+  if ((st = check_kI(p, kI)) != DSA_OK) return st;
+  if ((indices_out && !aligned(indices_out, 4)) || (counts_out && !aligned(counts_out, 4)))
+    return DSA_ERR_INVALID;
+  return DSA_OK;
+}
+
+// The fused step itself, on a workspace `base` laid out as `d`; device-side
+// errors are OR-ed into *err.
+int decode_run(const dsa_problem* p, const uint8_t* qI, const float* w, dsa_paged kI,
+               const uint16_t* q, dsa_paged k, dsa_paged v, uint16_t* out, float* lse,
+               int32_t* indices_out, int32_t* counts_out, char* base, const DecodeLayout& d,
+               uint32_t* err, hipStream_t s) {
+  int st = DSA_OK;
+  float* scores = reinterpret_cast<float*>(base + d.scores_off);
+  const int64_t ld = slab_ld(p);
+  const Summary sum = needs_summary(p) ? summary_carve(base + d.sum_off, d.rp)
+                                       : Summary{nullptr, nullptr};
+  const bool use_rowoff = attn_uses_rowoff(p->D_qk, p->D_v, is_latent(k, v));
+  int64_t* roff = reinterpret_cast<int64_t*>(base + d.roff_off);
+
+  // Four launches per pass of rows: indexer scan (scores and summaries),
+  // Top-K selection, sparse attention, split-key merge.
+  for (int row0 = 0; row0 < p->num_rows; row0 += d.rp) {
+    const int nr = p->num_rows - row0 < d.rp ? p->num_rows - row0 : d.rp;
+    int32_t* idx = indices_out ? indices_out + (int64_t)row0 * p->K
+                               : reinterpret_cast<int32_t*>(base + d.idx_off);
+
+    IndexerLaunch ia;
+    ia.rows = row_map(p);
+    ia.qI = qI;
+    ia.w = w;
+    ia.kI = kI;
+    ia.scores = scores;
+    ia.ld = ld;
+    ia.err = err;
+    ia.H_I = p->H_I;
+    ia.D_I = p->D_I;
+    ia.qI_scale = p->qI_scale;
+    ia.row_begin = row0;
+    ia.num_rows = nr;
+    ia.max_len = (int32_t)max_len(p);
+    ia.sum = sum;
+    ia.topk_K = p->K;
+    if ((st = status_of(launch_indexer_scores(ia, s))) != DSA_OK) return st;
+
+    TopkLaunch ta;
+    ta.rows = row_map(p);
+    ta.scores = scores;
+    ta.ld = ld;
+    ta.indices = idx;
+    ta.counts = counts_out ? counts_out + row0 : nullptr;
+    ta.err = err;
+    ta.K = p->K;
+    ta.row_begin = row0;
+    ta.num_rows = nr;
+    ta.max_len = (int32_t)max_len(p);
+    ta.sum = sum;
+    ta.prep = false;  // the indexer wrote the summaries
+    ta.vec = true;    // 256-byte aligned slab, ld a multiple of 64
+    ta.rowoff = use_rowoff ? roff : nullptr;
+    ta.kv = k;
+    if ((st = status_of(launch_topk(ta, s))) != DSA_OK) return st;
+
+    AttnLaunch aa = attn_launch(p, q, k, v, out, lse, err);
+    aa.indices = idx;
+    aa.indices_row_offset = 0;
+    aa.rowoff = use_rowoff ? roff : nullptr;
+    aa.row_begin = row0;
+    aa.num_rows = nr;
+    // the workspace holds partials for the larger of the two layouts' counts
+    aa.n_chunks = attn_chunks(d.rp, p->H_q, p->D_qk, p->K, aa.latent);
+    aa.partial = aa.n_chunks > 1 ? static_cast<void*>(base + d.part_off) : nullptr;
+    if ((st = status_of(launch_sparse_attn(aa, s))) != DSA_OK) return st;
+  }
+  return DSA_OK;
+}
+
+
+// ------------------------------------------------- allocation-free entry point
+// The library's own scratch for dsa_decode_step_static: a file-scope device
+// array, one copy on every GPU the library runs on, held until the process
+// ends.  Host code never uses the array's name as an address: its device
+// address on the current GPU comes from hipGetSymbolAddress, once per
+// device.
+static __device__ __align__(256) uint8_t scratch[DSA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DSA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (dev >= 0 && dev < kMaxDevices && g_scratch_ptr[dev]) {
+    *out = g_scratch_ptr[dev];
+    return DSA_OK;
+  }
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return DSA_ERR_HIP;
+  if (dev >= 0 && dev < kMaxDevices) g_scratch_ptr[dev] = static_cast<char*>(ptr);
+  *out = static_cast<char*>(ptr);
+  return DSA_OK;
+}
+
+// The fused step's layout with a score budget small enough that the whole
+// workspace fits the scratch (fewer rows per pass), or false when even one
+// row per pass does not fit.
+bool static_layout(const dsa_problem* p, DecodeLayout& d) {
+  for (size_t budget = kScoresBudget; budget >= 4096; budget /= 2) {
+    d = decode_layout(p, budget);
+    if (d.total <= (size_t)DSA_STATIC_SCRATCH_BYTES) return true;
+    if (d.rp == 1) break;
+  }
+  return false;
 }
 
 }  // namespace
@@ -258,43 +424,6 @@ int dsa_topk(const dsa_problem* p, const float* scores, int64_t ld_scores, int32
   return status_of(launch_topk(a, static_cast<hipStream_t>(stream)));
 }
 
-static int check_attn_args(const dsa_problem* p, const uint16_t* q, const dsa_paged& k,
-                           const dsa_paged& v, uint16_t* out, float* lse) {
-  int st = check_attn_shape(p);
-  if (st != DSA_OK) return st;
-  if (!q || !out) return DSA_ERR_INVALID;
-  if (!aligned(q, 16) || !aligned(out, 16) || (lse && !aligned(lse, 4))) return DSA_ERR_INVALID;
-  if ((st = check_paged(k, 2 * (int64_t)p->D_qk)) != DSA_OK) return st;
-  if ((st = check_paged(v, 2 * (int64_t)p->D_v)) != DSA_OK) return st;
-  return DSA_OK;
-}
-
-static AttnLaunch attn_launch(const dsa_problem* p, const uint16_t* q, dsa_paged k, dsa_paged v,
-                              uint16_t* out, float* lse, uint32_t* err) {
-  AttnLaunch a;
-  a.rows = row_map(p);
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.latent = is_latent(k, v);
-  a.indices = nullptr;
-  a.indices_row_offset = 0;
-  a.rowoff = nullptr;
-  a.out = out;
-  a.lse = lse;
-  a.partial = nullptr;
-  a.err = err;
-  a.H_q = p->H_q;
-  a.D_qk = p->D_qk;
-  a.D_v = p->D_v;
-  a.K = p->K;
-  a.scale = p->scale;
-  a.row_begin = 0;
-  a.num_rows = p->num_rows;
-  a.n_chunks = 1;
-  return a;
-}
-
 int dsa_sparse_attn(const dsa_problem* p, const uint16_t* q, dsa_paged k, dsa_paged v,
                     const int32_t* indices, uint16_t* out, float* lse, void* ws,
                     size_t ws_bytes, void* stream) {
@@ -318,84 +447,35 @@ int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa
                     const uint16_t* q, dsa_paged k, dsa_paged v, uint16_t* out, float* lse,
                     int32_t* indices_out, int32_t* counts_out, void* ws, size_t ws_bytes,
                     void* stream) {
-  int st = check_rows(p);
+  int st = check_decode_args(p, qI, w, kI, q, k, v, out, lse, indices_out, counts_out);
   if (st != DSA_OK) return st;
-  if ((st = check_indexer_shape(p)) != DSA_OK) return st;
-  if ((st = check_attn_args(p, q, k, v, out, lse)) != DSA_OK) return st;
-  if (!qI || !w || !aligned(qI, 16) || !aligned(w, 4)) return DSA_ERR_INVALID;
-  if ((st = check_kI(p, kI)) != DSA_OK) return st;
-  if ((indices_out && !aligned(indices_out, 4)) || (counts_out && !aligned(counts_out, 4)))
-    return DSA_ERR_INVALID;
   if ((st = check_ws(ws, ws_bytes, dsa_workspace_size(p, DSA_OP_DECODE_STEP))) != DSA_OK)
     return st;
   if (p->num_rows == 0) return DSA_OK;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const DecodeLayout d = decode_layout(p);
   char* base = static_cast<char*>(ws);
-  uint32_t* err = reinterpret_cast<uint32_t*>(base);
-  float* scores = reinterpret_cast<float*>(base + d.scores_off);
-  const int64_t ld = slab_ld(p);
-  const Summary sum = needs_summary(p) ? summary_carve(base + d.sum_off, d.rp)
-                                       : Summary{nullptr, nullptr};
-  const bool use_rowoff = attn_uses_rowoff(p->D_qk, p->D_v, is_latent(k, v));
-  int64_t* roff = reinterpret_cast<int64_t*>(base + d.roff_off);
+  return decode_run(p, qI, w, kI, q, k, v, out, lse, indices_out, counts_out, base,
+                    decode_layout(p), reinterpret_cast<uint32_t*>(base),
+                    static_cast<hipStream_t>(stream));
+}
 
-  // Four launches per pass of rows: indexer scan (scores and summaries),
-  // Top-K selection, sparse attention, split-key merge.
-  for (int row0 = 0; row0 < p->num_rows; row0 += d.rp) {
-    const int nr = p->num_rows - row0 < d.rp ? p->num_rows - row0 : d.rp;
-    int32_t* idx = indices_out ? indices_out + (int64_t)row0 * p->K
-                               : reinterpret_cast<int32_t*>(base + d.idx_off);
-
-    IndexerLaunch ia;
-    ia.rows = row_map(p);
-    ia.qI = qI;
-    ia.w = w;
-    ia.kI = kI;
-    ia.scores = scores;
-    ia.ld = ld;
-    ia.err = err;
-    ia.H_I = p->H_I;
-    ia.D_I = p->D_I;
-    ia.qI_scale = p->qI_scale;
-    ia.row_begin = row0;
-    ia.num_rows = nr;
-    ia.max_len = (int32_t)max_len(p);
-    ia.sum = sum;
-    ia.topk_K = p->K;
-    if ((st = status_of(launch_indexer_scores(ia, s))) != DSA_OK) return st;
-
-    TopkLaunch ta;
-    ta.rows = row_map(p);
-    ta.scores = scores;
-    ta.ld = ld;
-    ta.indices = idx;
-    ta.counts = counts_out ? counts_out + row0 : nullptr;
-    ta.err = err;
-    ta.K = p->K;
-    ta.row_begin = row0;
-    ta.num_rows = nr;
-    ta.max_len = (int32_t)max_len(p);
-    ta.sum = sum;
-    ta.prep = false;  // the indexer wrote the summaries
-    ta.vec = true;    // 256-byte aligned slab, ld a multiple of 64
-    ta.rowoff = use_rowoff ? roff : nullptr;
-    ta.kv = k;
-    if ((st = status_of(launch_topk(ta, s))) != DSA_OK) return st;
-
-    AttnLaunch aa = attn_launch(p, q, k, v, out, lse, err);
-    aa.indices = idx;
-    aa.indices_row_offset = 0;
-    aa.rowoff = use_rowoff ? roff : nullptr;
-    aa.row_begin = row0;
-    aa.num_rows = nr;
-    // the workspace holds partials for the larger of the two layouts' counts
-    aa.n_chunks = attn_chunks(d.rp, p->H_q, p->D_qk, p->K, aa.latent);
-    aa.partial = aa.n_chunks > 1 ? static_cast<void*>(base + d.part_off) : nullptr;
-    if ((st = status_of(launch_sparse_attn(aa, s))) != DSA_OK) return st;
-  }
-  return DSA_OK;
+int dsa_decode_step_static(const dsa_problem* p, const uint8_t* qI, const float* w,
+                           dsa_paged kI, const uint16_t* q, dsa_paged k, dsa_paged v,
+                           uint16_t* out, float* lse, int32_t* indices_out, int32_t* counts_out,
+                           uint32_t* err, void* stream) {
+  int st = check_decode_args(p, qI, w, kI, q, k, v, out, lse, indices_out, counts_out);
+  if (st != DSA_OK) return st;
+  if (err && !aligned(err, 4)) return DSA_ERR_INVALID;
+  if (p->num_rows == 0) return DSA_OK;
+  // the fused step's layout with passes of rows small enough for the scratch
+  DecodeLayout d;
+  if (!static_layout(p, d)) return DSA_ERR_WORKSPACE;
+  char* base = nullptr;
+  if ((st = static_scratch(&base)) != DSA_OK) return st;
+  // with no error word of the caller's, device-side errors go to the
+  // scratch's header word, which nothing reads
+  return decode_run(p, qI, w, kI, q, k, v, out, lse, indices_out, counts_out, base, d,
+                    err ? err : reinterpret_cast<uint32_t*>(base),
+                    static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -27,7 +27,7 @@ def lib():
 
 def test_exports_every_header_symbol(lib):
     syms = header_symbols()
-    assert len(syms) == 7 and sorted(B.EXPORTS) == syms
+    assert len(syms) == 8 and sorted(B.EXPORTS) == syms
     for s in syms:
         assert getattr(lib, s) is not None
     assert lib.dsa_abi_version() == B.ABI_VERSION
@@ -183,3 +183,21 @@ def test_decode_step_rejections():
     assert call(prob(), nbytes=1024) == B.DSA_ERR_WORKSPACE
     assert call(prob(), indices=FAKE + 2) == B.DSA_ERR_INVALID
     assert call(prob(num_rows=0), nbytes=256) == B.DSA_OK
+
+
+def test_decode_step_static_rejections():
+    # validation runs before the scratch is looked up, so every case here
+    # returns without touching a GPU
+    def call(p, kI=None, k=None, indices=None, err=None):
+        return B.raw_call("dsa_decode_step_static", ctypes.byref(p), ctypes.c_void_p(FAKE),
+                          ctypes.c_void_p(FAKE), kI or paged(), ctypes.c_void_p(FAKE),
+                          k or paged(row=1152), k or paged(row=1152), ctypes.c_void_p(FAKE),
+                          None, ctypes.c_void_p(indices), None, ctypes.c_void_p(err), None)
+    assert call(prob(H_I=100)) == B.DSA_ERR_UNSUPPORTED
+    assert call(prob(), kI=paged(row=16)) == B.DSA_ERR_INVALID
+    assert call(prob(), indices=FAKE + 2) == B.DSA_ERR_INVALID
+    assert call(prob(), err=FAKE + 2) == B.DSA_ERR_INVALID
+    assert call(prob(num_rows=0)) == B.DSA_OK
+    # a layout that cannot fit DSA_STATIC_SCRATCH_BYTES even one row per pass:
+    # a history of 2^24 blocks needs a 4 GiB score row
+    assert call(prob(max_blocks=1 << 24)) == B.DSA_ERR_WORKSPACE
