@@ -54,7 +54,7 @@ def parse():
                          "host is slowed (under a profiler)")
     ap.add_argument("--no-graph-legs", action="store_true",
                     help="with --graph 0, capture no graphs (skips step_us_spread, graph_replay)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cand", action="store_true",
                     help="skip the candidate-restricted indexer leg")
@@ -454,37 +454,42 @@ def cand_leg(args, wl, lengths, stream, n_cand=16384):
 
 
 def cpu_baseline(batch, budget_s):
-    """The oracle, as it stands, on whole rows of the first input set, in
-    passes over the batch, until about budget_s seconds of host time are
-    spent (at least one row)."""
-    import numpy as np
-    from threadpoolctl import threadpool_info
-
-    import oracle
+    """The plain C++ oracle, as it stands, on whole rows of the first input
+    set: once on one host thread, then on every core this process may run on
+    (os.sched_getaffinity), each for about budget_s / 2 seconds of wall time
+    (at least one row)."""
+    import oracle.cpp
     from workloads import oracle_arrays
 
     t_copy = time.perf_counter()
     arr = oracle_arrays(batch, rows=list(range(batch.rows)))
     t_copy = time.perf_counter() - t_copy
-    done = 0
-    t0 = time.perf_counter()
-    while done == 0 or time.perf_counter() - t0 < budget_s:
-        r = done % batch.rows
-        one = {k: (v[r:r + 1] if k in ("qI", "w", "q", "row_seq", "row_pos") else v)
-               for k, v in arr.items()}
-        oracle.decode_step(qI=one["qI"], w=one["w"], kI_cache=one["kI_cache"], q=one["q"],
-                           k_cache=one["k_cache"], v_cache=one["v_cache"],
-                           block_table=one["block_table"], seq_lens=one["seq_lens"],
-                           K=one["K"], scale=one["scale"], D_v=one["D_v"],
-                           row_seq=one["row_seq"], row_pos=one["row_pos"], keep_scores=False)
-        done += 1
-    el = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(done / el, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} row evaluations ({done / batch.rows:.1f} passes over the "
-                      f"{batch.rows} rows of {batch.wl.name}, full history each), {el:.1f} s; "
-                      f"host copy {t_copy:.1f} s not timed",
-            "numpy_threads": threads, "host_cpus": os.cpu_count()}
+    oracle.cpp.lib()
+
+    def run(threads, seconds):
+        done = 0
+        t0 = time.perf_counter()
+        while done == 0 or time.perf_counter() - t0 < seconds:
+            oracle.cpp.decode_step(
+                qI=arr["qI"], w=arr["w"], kI_cache=arr["kI_cache"], q=arr["q"],
+                k_cache=arr["k_cache"], v_cache=arr["v_cache"], block_table=arr["block_table"],
+                seq_lens=arr["seq_lens"], K=arr["K"], scale=arr["scale"], D_v=arr["D_v"],
+                row_seq=arr["row_seq"], row_pos=arr["row_pos"], rows=[done % batch.rows],
+                keep_scores=False, qI_scale=arr.get("qI_scale"),
+                kI_scale_cache=arr.get("kI_scale_cache"), threads=threads)
+            done += 1
+        return done, time.perf_counter() - t0
+
+    cores = len(os.sched_getaffinity(0))
+    n1, t1 = run(1, budget_s / 2)
+    nc, tc = run(cores, budget_s / 2)
+    return {"value": round(nc / tc, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"plain C++ oracle (binary64), whole rows of {batch.wl.name} "
+                      f"(full history each), cycling over its {batch.rows} rows: {nc} rows in "
+                      f"{tc:.1f} s on {cores} threads; host copy {t_copy:.1f} s not timed",
+            "single_thread": {"value": round(n1 / t1, 4), "unit": "tokens/s", "cores": 1,
+                              "sample": f"{n1} rows in {t1:.1f} s on 1 thread"},
+            "affinity_cores": cores, "host_cpus": os.cpu_count()}
 
 
 if __name__ == "__main__":

@@ -39,6 +39,11 @@ Readings of points the pages leave open (ReLU gate, tie rule, output order,
 latent V = leading D_v columns of the K row, history inclusive of the current
 token) are stated where each function uses them.
 
+Two routes state the same definitions: this numpy package, and the plain C++
+file ``cpp/dsa_oracle.cpp`` (its own decoders, binary64 loops, a full sort,
+the softmax definition), loaded through ``oracle.cpp``.  They share no code;
+the tests pin each against the other and run every closed-form pin on both.
+
 Parity status: every function here is pinned by tests under ``tests/`` that do
 not re-type its formula (closed forms, brute force, library routines,
 invariants).  The constants the pages never fix (ReLU gate, K, block size 64,

@@ -1,0 +1,318 @@
+// CPU oracle of the indexer -> Top-K -> sparse-attention step, in plain C++.
+//
+// TEST INFRASTRUCTURE ONLY.  This is the slow, obviously correct statement of
+// what the hot path computes.  Only the test-suite, the package smoke check
+// and the CPU-baseline leg of the benchmark load it (through oracle/cpp.py).
+// It shares no code, header, table or constant with the HIP library, and
+// neither one includes the other.
+//
+// Each step follows Baidu AI Cloud's "Day0 Inference Support and Performance
+// Optimization for New Architecture LLMs", section 2.2 (score every
+// historical position, aggregate the per-head scores with head weights, keep
+// the Top-K positions, attend over only those rows), with the paged caches of
+// sections 4.1-4.2 and the MXFP8 indexer format of section 5.1.  Readings of
+// what the pages leave open (ReLU gate, tie rule, ascending output, latent V,
+// history inclusive of the current token) are stated where they are used.
+//
+// Arithmetic is binary64.  The per-head dot products of E4M3 codes are exact
+// (products of 4-bit-mantissa values summed over at most a few hundred terms
+// fit in 53 bits; power-of-two group scales keep them exact); the weighted
+// head sum runs in ascending head order and is rounded once to binary32.
+// Top-K is a full sort.  Attention is the softmax definition over the
+// gathered rows (THInfer, eq. 9, restricted to the selected set).
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <numeric>
+#include <thread>
+#include <vector>
+
+namespace {
+
+// ------------------------------------------------------------------ formats
+// OCP E4M3 "FN": sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0
+// holds subnormals m * 2^-9; 0x7F and 0xFF are NaN; no infinities.
+double e4m3_value(uint8_t code) {
+  const double sign = (code & 0x80) ? -1.0 : 1.0;
+  const int e = (code >> 3) & 0xF, m = code & 0x7;
+  if (e == 0xF && m == 0x7) return std::nan("");
+  if (e == 0) return sign * m * std::ldexp(1.0, -9);
+  return sign * (1.0 + m / 8.0) * std::ldexp(1.0, e - 7);
+}
+
+struct E4M3Table {
+  double v[256];
+  E4M3Table() {
+    for (int c = 0; c < 256; ++c) v[c] = e4m3_value((uint8_t)c);
+  }
+};
+const E4M3Table& e4m3() {
+  static const E4M3Table t;
+  return t;
+}
+
+// E8M0 scale byte (OCP microscaling): 2^(e - 127); 255 is NaN.
+double e8m0_value(uint8_t e) { return e == 255 ? std::nan("") : std::ldexp(1.0, (int)e - 127); }
+
+// bfloat16: the upper half of a binary32.
+double bf16_value(uint16_t bits) {
+  const uint32_t u = (uint32_t)bits << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+// Order-preserving key of a binary32 score: larger score, larger key; -0 and
+// +0 share a key; NaN gets 0 and ranks below every number.
+uint32_t score_key(float s) {
+  if (std::isnan(s)) return 0u;
+  if (s == 0.0f) s = 0.0f;
+  uint32_t u;
+  std::memcpy(&u, &s, 4);
+  return (u >> 31) ? ~u : (u | 0x80000000u);
+}
+
+// Runs fn(i) for i in [0, n) on up to `threads` host threads.
+template <class F>
+void parallel_for(int64_t n, int threads, F fn) {
+  if (threads <= 1 || n <= 1) {
+    for (int64_t i = 0; i < n; ++i) fn(i);
+    return;
+  }
+  const int t = (int)std::min<int64_t>(threads, n);
+  std::vector<std::thread> pool;
+  for (int k = 0; k < t; ++k)
+    pool.emplace_back([&, k] {
+      for (int64_t i = k; i < n; i += t) fn(i);
+    });
+  for (auto& th : pool) th.join();
+}
+
+}  // namespace
+
+extern "C" {
+
+// Value of every E4M3 code (for pins against other decoders).
+void orc_e4m3_table(double* out) {
+  for (int c = 0; c < 256; ++c) out[c] = e4m3().v[c];
+}
+
+void orc_score_keys(const float* s, int64_t n, uint32_t* keys) {
+  for (int64_t i = 0; i < n; ++i) keys[i] = score_key(s[i]);
+}
+
+// Index scores of one query row against n key rows (Day0 article, section
+// 2.2): I[s] = sum_h w[h] * max(0, dot_h[s]), dot_h[s] = sum_d qI[h,d] kI[s,d].
+//   qI [H][D] E4M3 codes, w [H] binary32, kI [n][D] E4M3 codes (gathered).
+//   MXFP8 (qs, ks non-NULL; section 5.1): dims in groups of 32 share an E8M0
+//   scale, qs [H][D/32], ks [n][D/32]; each group's partial dot is scaled by
+//   both groups' scales before the groups are summed.
+// Reading: the ReLU gate acts per head before the weighting.  One shared key
+// row per position serves every head.  A zero score is stored as +0.
+void orc_indexer_scores(const uint8_t* qI, const float* w, const uint8_t* kI, const uint8_t* qs,
+                        const uint8_t* ks, int H, int D, int64_t n, float* out, int threads) {
+  const double* t = e4m3().v;
+  const int G = D / 32;
+  std::vector<double> q((size_t)H * D);
+  for (size_t i = 0; i < q.size(); ++i) q[i] = t[qI[i]];
+  const int64_t chunk = 256;
+  parallel_for((n + chunk - 1) / chunk, threads, [&](int64_t c) {
+    std::vector<double> k(D);
+    for (int64_t s = c * chunk; s < std::min(n, (c + 1) * chunk); ++s) {
+      for (int d = 0; d < D; ++d) k[d] = t[kI[s * D + d]];
+      double total = 0.0;
+      for (int h = 0; h < H; ++h) {
+        double dot = 0.0;
+        if (!qs) {
+          for (int d = 0; d < D; ++d) dot += q[(size_t)h * D + d] * k[d];
+        } else {
+          for (int g = 0; g < G; ++g) {
+            double part = 0.0;
+            for (int d = 32 * g; d < 32 * g + 32; ++d) part += q[(size_t)h * D + d] * k[d];
+            dot += part * e8m0_value(qs[h * G + g]) * e8m0_value(ks[s * G + g]);
+          }
+        }
+        total += (double)w[h] * std::max(0.0, dot);
+      }
+      out[s] = (float)total + 0.0f;
+    }
+  });
+}
+
+// Top-K of one row's n scores (Day0 article, section 2.2): the min(K, n)
+// slots with the largest score; readings: equal scores go to the lower slot,
+// NaN ranks last, the kept slots are written in ascending order and -1 pads
+// to K.  A full sort by (key descending, slot ascending).  Returns the count.
+int64_t orc_topk(const float* scores, int64_t n, int64_t K, int32_t* idx) {
+  std::vector<int64_t> order(n);
+  std::iota(order.begin(), order.end(), 0);
+  std::vector<uint32_t> key(n);
+  for (int64_t i = 0; i < n; ++i) key[i] = score_key(scores[i]);
+  std::sort(order.begin(), order.end(), [&](int64_t a, int64_t b) {
+    return key[a] != key[b] ? key[a] > key[b] : a < b;
+  });
+  const int64_t count = std::min(K, n);
+  std::vector<int64_t> kept(order.begin(), order.begin() + count);
+  std::sort(kept.begin(), kept.end());
+  for (int64_t j = 0; j < K; ++j) idx[j] = j < count ? (int32_t)kept[j] : -1;
+  return count;
+}
+
+// Softmax attention of one query row (H heads, bf16 q [H][Dqk]) over n
+// gathered rows: logit[h,j] = scale sum_d q[h,d] k[j,d]; o[h] = sum_j
+// exp(logit - m) v[j] / sum_j exp(logit - m); lse[h] = m + ln(sum).  With
+// no rows: o = 0 and lse = -inf.  k [n][Dqk], v [n][Dv] (bf16 bits).
+void orc_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n, int H,
+                   int Dqk, int Dv, double scale, double* o, double* lse, int threads) {
+  parallel_for(H, threads, [&](int64_t h) {
+    double* oh = o + h * Dv;
+    for (int d = 0; d < Dv; ++d) oh[d] = 0.0;
+    if (n == 0) {
+      lse[h] = -INFINITY;
+      return;
+    }
+    std::vector<double> logit(n);
+    for (int64_t j = 0; j < n; ++j) {
+      double dot = 0.0;
+      for (int d = 0; d < Dqk; ++d) dot += bf16_value(q[h * Dqk + d]) * bf16_value(k[j * Dqk + d]);
+      logit[j] = scale * dot;
+    }
+    const double m = *std::max_element(logit.begin(), logit.end());
+    double l = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+      const double p = std::exp(logit[j] - m);
+      l += p;
+      for (int d = 0; d < Dv; ++d) oh[d] += p * bf16_value(v[j * Dv + d]);
+    }
+    for (int d = 0; d < Dv; ++d) oh[d] /= l;
+    lse[h] = m + std::log(l);
+  });
+}
+
+// The same attention by brute force over every one of the n rows of a
+// history, with the unselected ones masked to -inf before the softmax
+// (selected: n flags).  A different route to orc_attention's result.
+void orc_masked_dense_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const uint8_t* selected, int64_t n, int H, int Dqk, int Dv,
+                                double scale, double* o, double* lse) {
+  for (int h = 0; h < H; ++h) {
+    std::vector<double> s(n);
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) {
+      double dot = 0.0;
+      for (int d = 0; d < Dqk; ++d) dot += bf16_value(q[h * Dqk + d]) * bf16_value(k[j * Dqk + d]);
+      s[j] = selected[j] ? scale * dot : -INFINITY;
+      m = std::max(m, s[j]);
+    }
+    double l = 0.0;
+    for (int d = 0; d < Dv; ++d) o[h * Dv + d] = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+      const double e = std::isinf(s[j]) ? 0.0 : std::exp(s[j] - m);
+      l += e;
+      for (int d = 0; d < Dv; ++d) o[h * Dv + d] += e * bf16_value(v[j * Dv + d]);
+    }
+    for (int d = 0; d < Dv; ++d) o[h * Dv + d] /= l;
+    lse[h] = m + std::log(l);
+  }
+}
+
+// The inputs of a whole step, in the layouts of the caches (raw bits).
+struct OrcStep {
+  int32_t num_rows, num_seqs, max_blocks, num_blocks;
+  const int32_t* seq_lens;     // [num_seqs]
+  const int32_t* block_table;  // [num_seqs][max_blocks]
+  const int32_t* row_seq;      // [num_rows] or NULL: row r -> sequence r
+  const int32_t* row_pos;      // [num_rows] or NULL: seq_lens[b] - 1
+  int32_t H_I, D_I;
+  const uint8_t* qI;           // [num_rows][H_I][D_I]
+  const float* w;              // [num_rows][H_I]
+  const uint8_t* kI;           // [num_blocks][64][D_I]
+  const uint8_t* qI_scale;     // [num_rows][H_I][D_I/32] or NULL
+  const uint8_t* kI_scale;     // [num_blocks][64][D_I/32] or NULL
+  const int32_t* cand;         // [num_rows][n_cand] or NULL
+  const int32_t* cand_len;     // [num_rows]
+  int32_t n_cand;
+  int32_t H_q, D_qk, D_v, K;
+  double scale;
+  const uint16_t* q;           // [num_rows][H_q][D_qk]
+  const uint16_t* k;           // [num_blocks][64][D_qk]
+  const uint16_t* v;           // [num_blocks][64][D_v] or NULL: V = the first D_v of each K row
+};
+
+// The step for the rows listed (n_sel of them, row ids), in order:
+//   indices [n_sel][K], counts [n_sel], out [n_sel][H_q][D_v], lse [n_sel][H_q],
+//   scores  [n_sel][ld] (or NULL; NaN past each row's history).
+// Row r's history is positions 0 .. p_r inclusive (reading: the current
+// token's key is already in the cache); position s lives in block
+// block_table[b][s / 64], row s % 64 (Day0 article, sections 4.1-4.2).  A
+// candidate-restricted row scores only its list's first cand_len[r] entries
+// (vLLM's DeepSeek-V4.1-Flash article, "Kernels") and keeps the Top-K slots
+// of the list, written as their positions.  Returns 0, or -1 for a row whose
+// sequence or position is out of range.
+int orc_decode_step(const OrcStep* p, const int32_t* rows, int n_sel, int32_t* indices,
+                    int64_t* counts, double* out, double* lse, float* scores, int64_t ld,
+                    int threads) {
+  const int B = 64;
+  for (int i = 0; i < n_sel; ++i) {
+    const int r = rows[i];
+    const int b = p->row_seq ? p->row_seq[r] : r;
+    if (b < 0 || b >= p->num_seqs) return -1;
+    const int pos = p->row_pos ? p->row_pos[r] : p->seq_lens[b] - 1;
+    if (pos < 0 || pos >= p->seq_lens[b] || pos >= p->max_blocks * B) return -1;
+    const int32_t* bt = p->block_table + (int64_t)b * p->max_blocks;
+    // the history this row scores
+    std::vector<int64_t> hist;
+    if (p->cand) {
+      const int32_t* c = p->cand + (int64_t)r * p->n_cand;
+      const int n = std::max(0, std::min(p->cand_len[r], p->n_cand));
+      for (int j = 0; j < n; ++j) {
+        if (c[j] < 0 || c[j] > pos || (j > 0 && c[j] <= c[j - 1])) return -1;
+        hist.push_back(c[j]);
+      }
+    } else {
+      hist.resize(pos + 1);
+      std::iota(hist.begin(), hist.end(), 0);
+    }
+    const int64_t n = (int64_t)hist.size();
+    // gather the index keys (and their scales) of the history
+    const int D = p->D_I, G = D / 32;
+    std::vector<uint8_t> kI((size_t)n * D), ks(p->kI_scale ? (size_t)n * G : 0);
+    for (int64_t j = 0; j < n; ++j) {
+      const int64_t row = (int64_t)bt[hist[j] / B] * B + hist[j] % B;
+      std::memcpy(&kI[(size_t)j * D], p->kI + row * D, D);
+      if (p->kI_scale) std::memcpy(&ks[(size_t)j * G], p->kI_scale + row * G, G);
+    }
+    std::vector<float> sc(n);
+    orc_indexer_scores(p->qI + (int64_t)r * p->H_I * D, p->w + (int64_t)r * p->H_I, kI.data(),
+                       p->qI_scale ? p->qI_scale + (int64_t)r * p->H_I * G : nullptr,
+                       p->kI_scale ? ks.data() : nullptr, p->H_I, D, n, sc.data(), threads);
+    if (scores) {
+      float* srow = scores + (int64_t)i * ld;
+      for (int64_t j = 0; j < ld; ++j) srow[j] = j < n ? sc[j] : std::nanf("");
+    }
+    int32_t* idx = indices + (int64_t)i * p->K;
+    counts[i] = orc_topk(sc.data(), n, p->K, idx);
+    // slots -> positions (candidate slots are in position order, so the
+    // order and the tie rule carry over)
+    for (int64_t j = 0; j < counts[i]; ++j) idx[j] = (int32_t)hist[idx[j]];
+    // gather the selected KV rows and attend
+    const int64_t m = counts[i];
+    std::vector<uint16_t> kr((size_t)m * p->D_qk), vr((size_t)m * p->D_v);
+    for (int64_t j = 0; j < m; ++j) {
+      const int64_t row = (int64_t)bt[idx[j] / B] * B + idx[j] % B;
+      std::memcpy(&kr[(size_t)j * p->D_qk], p->k + row * p->D_qk, 2 * (size_t)p->D_qk);
+      if (p->v)
+        std::memcpy(&vr[(size_t)j * p->D_v], p->v + row * p->D_v, 2 * (size_t)p->D_v);
+      else  // latent layout (reading): V is the first D_v elements of the K row
+        std::memcpy(&vr[(size_t)j * p->D_v], p->k + row * p->D_qk, 2 * (size_t)p->D_v);
+    }
+    orc_attention(p->q + (int64_t)r * p->H_q * p->D_qk, kr.data(), vr.data(), m, p->H_q, p->D_qk,
+                  p->D_v, p->scale, out + (int64_t)i * p->H_q * p->D_v, lse + (int64_t)i * p->H_q,
+                  threads);
+  }
+  return 0;
+}
+
+}  // extern "C"

@@ -8,6 +8,7 @@ gate, a wrong tie rule) breaks.
 """
 
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -16,8 +17,15 @@ import torch
 
 import oracle
 from oracle.formats import E4M3_TABLE
-from tests.helpers import run_oracle
+from tests.helpers import ORACLES, run_oracle
 from workloads import make_batch, oracle_arrays, small_workload
+
+
+@pytest.fixture(params=sorted(ORACLES))
+def orc(request):
+    """Each pin runs on both oracle routes: the numpy statement and the plain
+    C++ one (written separately; neither calls the other)."""
+    return ORACLES[request.param]
 
 
 # ----------------------------------------------------------------- formats
@@ -74,7 +82,7 @@ def _e4m3(x):
     return torch.tensor(x, dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
-def test_scores_one_hot_keys_closed_form():
+def test_scores_one_hot_keys_closed_form(orc):
     # key s = c_s * e_{d_s}: the dot product collapses to c_s * q[h, d_s], so
     # I[s] = sum_h w_h * max(0, c_s * q[h, d_s]).  H_I != D_I so a transposed
     # operand cannot pass.
@@ -86,7 +94,7 @@ def test_scores_one_hot_keys_closed_form():
     c_s = rng.choice([-3, -1, 1, 2, 4], L)
     k = np.zeros((L, D))
     k[np.arange(L), d_s] = c_s
-    got = oracle.indexer_scores_row(_e4m3(q), w, _e4m3(k))
+    got = orc.indexer_scores_row(_e4m3(q), w, _e4m3(k))
     for s in range(L):
         want = 0.0
         for h in range(H):
@@ -94,20 +102,20 @@ def test_scores_one_hot_keys_closed_form():
         assert got[s] == np.float32(want), s
 
 
-def test_scores_gate_is_per_head():
+def test_scores_gate_is_per_head(orc):
     # two heads of opposite sign on one key: a gate applied after the head sum
     # would give max(0, 3*4 - 2*4) = 4; the per-head gate gives 3*4 = 12.
     q = np.zeros((2, 4)); q[0, 0] = 4; q[1, 0] = -4
     k = np.zeros((1, 4)); k[0, 0] = 1
     w = np.array([3.0, 2.0], np.float32)
-    assert oracle.indexer_scores_row(_e4m3(q), w, _e4m3(k))[0] == 12.0
+    assert orc.indexer_scores_row(_e4m3(q), w, _e4m3(k))[0] == 12.0
     # every head gated off, with a negative weight: the score is +0
     w2 = np.array([-1.0, -2.0], np.float32)
-    z = oracle.indexer_scores_row(_e4m3(-np.abs(q)), w2, _e4m3(k))[0]
+    z = orc.indexer_scores_row(_e4m3(-np.abs(q)), w2, _e4m3(k))[0]
     assert z == 0 and not np.signbit(z)
 
 
-def test_scores_linear_identity():
+def test_scores_linear_identity(orc):
     # max(0, x) - max(0, -x) = x, so I(q) - I(-q) = sum_h w_h q_h . k_s
     # = k_s . (sum_h w_h q_h): weights folded into the query first, a
     # different association than the oracle's (per-head dots, then weights).
@@ -116,43 +124,72 @@ def test_scores_linear_identity():
     q = rng.integers(-8, 9, (H, D)).astype(np.float64)
     k = rng.integers(-8, 9, (L, D)).astype(np.float64)
     w = rng.integers(0, 4, H).astype(np.float32)
-    plus = oracle.indexer_scores_row(_e4m3(q), w, _e4m3(k)).astype(np.float64)
-    minus = oracle.indexer_scores_row(_e4m3(-q), w, _e4m3(k)).astype(np.float64)
+    plus = orc.indexer_scores_row(_e4m3(q), w, _e4m3(k)).astype(np.float64)
+    minus = orc.indexer_scores_row(_e4m3(-q), w, _e4m3(k)).astype(np.float64)
     folded = (w.astype(np.float64)[:, None] * q).sum(axis=0)      # [D]
     want = (k * folded[None, :]).sum(axis=1)
     assert (plus - minus == want).all()
 
 
-def test_scores_integer_mode_exact_and_invariant():
+def test_scores_integer_mode_exact_and_invariant(orc):
     rng = np.random.default_rng(3)
     H, D, L = 64, 128, 200
     q = rng.integers(-8, 9, (H, D))
     k = rng.integers(-8, 9, (L, D))
     w = rng.integers(0, 4, H).astype(np.float32)
-    s = oracle.indexer_scores_row(_e4m3(q), w, _e4m3(k))
+    s = orc.indexer_scores_row(_e4m3(q), w, _e4m3(k))
     assert (s == np.round(s)).all()
     # exact integer arithmetic as an independent route
     dots = [[sum(int(a) * int(b) for a, b in zip(q[h], k[j])) for j in range(L)] for h in range(H)]
     want = [sum(int(w[h]) * max(0, dots[h][j]) for h in range(H)) for j in range(L)]
     assert (s.astype(np.int64) == np.array(want)).all()
     # doubling every weight doubles every score exactly
-    assert (oracle.indexer_scores_row(_e4m3(q), 2 * w, _e4m3(k)) == 2 * s).all()
+    assert (orc.indexer_scores_row(_e4m3(q), 2 * w, _e4m3(k)) == 2 * s).all()
     # permuting heads together with their weights changes nothing
     perm = rng.permutation(H)
-    assert (oracle.indexer_scores_row(_e4m3(q[perm]), w[perm], _e4m3(k)) == s).all()
+    assert (orc.indexer_scores_row(_e4m3(q[perm]), w[perm], _e4m3(k)) == s).all()
 
 
-def test_scores_gaussian_close_to_float64_reference():
-    # Gaussian E4M3 inputs: the float32 score is the binary64 value rounded
-    # once; compare with torch's float64 route at half an ulp.
+def _f32_nearest(x):
+    """float32 nearest to the rational x, ties to even (exact arithmetic)."""
+    c = np.float32(float(x))
+    cands = [np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))]
+    best = min(cands, key=lambda f: (abs(Fraction(float(f)) - x),
+                                     int(np.array(f, np.float32).view(np.uint32)) & 1))
+    return np.float32(best)
+
+
+def test_scores_gaussian_are_the_exact_value_rounded_once(orc):
+    # Every E4M3 value is an integer multiple of 2**-9, so with integer codes
+    # Q = 512 q and Kc = 512 k each head's dot product is (Q @ Kc^T) / 2**18
+    # exactly, in int64.  The weighted head sum is then formed in exact
+    # rational arithmetic and rounded to the nearest float32.  The oracle
+    # rounds a binary64 sum once, so it must give the same float32 unless the
+    # exact value sits within binary64 noise of a float32 rounding boundary.
     g = torch.Generator().manual_seed(4)
     qc = torch.randn(64, 128, generator=g).to(torch.float8_e4m3fn)
-    kc = torch.randn(500, 128, generator=g).to(torch.float8_e4m3fn)
-    w = torch.rand(64, generator=g) * 3
-    ref = (w.double()[:, None] * torch.relu(qc.double() @ kc.double().T)).sum(0)
-    got = oracle.indexer_scores_row(qc.view(torch.uint8).numpy(), w.numpy(), kc.view(torch.uint8).numpy())
-    ulp = np.spacing(np.abs(got).astype(np.float32)).astype(np.float64)
-    assert (np.abs(got.astype(np.float64) - ref.numpy()) <= 0.5 * ulp + 1e-300).all()
+    kc = torch.randn(300, 128, generator=g).to(torch.float8_e4m3fn)
+    w = (torch.rand(64, generator=g) * 3).numpy()
+    qv = qc.view(torch.uint8).numpy()
+    kv = kc.view(torch.uint8).numpy()
+    Qi = (E4M3_TABLE[qv] * 512).astype(np.int64)
+    Ki = (E4M3_TABLE[kv] * 512).astype(np.int64)
+    assert (Qi == E4M3_TABLE[qv] * 512).all() and (Ki == E4M3_TABLE[kv] * 512).all()
+    dots = Qi @ Ki.T                                        # [64, 300], units of 2**-18
+    wf = [Fraction(float(x)) for x in w]
+    got = orc.indexer_scores_row(qv, w, kv)
+    near_boundary = 0
+    for s in range(kv.shape[0]):
+        exact = sum(wf[h] * int(dots[h, s]) for h in range(64) if dots[h, s] > 0) / 2 ** 18
+        want = _f32_nearest(exact)
+        if got[s] != want:
+            # only allowed next to a rounding boundary, one ulp away
+            lo, hi = sorted([float(got[s]), float(want)])
+            mid = (Fraction(lo) + Fraction(hi)) / 2
+            assert np.nextafter(np.float32(lo), np.float32(np.inf)) == np.float32(hi)
+            assert abs(exact - mid) <= abs(exact) * Fraction(1, 2 ** 45), s
+            near_boundary += 1
+    assert near_boundary <= 1
 
 
 # ----------------------------------------------------- MXFP8 index scores
@@ -178,17 +215,17 @@ def _mx_case(rng, H=6, D=128, L=50):
     return q, k, sq, sk, w
 
 
-def test_mx_scores_unit_scales_reduce_to_e4m3():
+def test_mx_scores_unit_scales_reduce_to_e4m3(orc):
     # every scale 127 (x1): the MXFP8 score is the pinned unscaled score
     rng = np.random.default_rng(11)
     q, k, _, _, w = _mx_case(rng)
     ones_q = np.full((q.shape[0], q.shape[1] // 32), 127, np.uint8)
     ones_k = np.full((k.shape[0], k.shape[1] // 32), 127, np.uint8)
-    got = oracle.indexer_scores_row(_e4m3(q), w, _e4m3(k), ones_q, ones_k)
-    assert (got == oracle.indexer_scores_row(_e4m3(q), w, _e4m3(k))).all()
+    got = orc.indexer_scores_row(_e4m3(q), w, _e4m3(k), ones_q, ones_k)
+    assert (got == orc.indexer_scores_row(_e4m3(q), w, _e4m3(k))).all()
 
 
-def test_mx_scores_one_hot_keys_closed_form():
+def test_mx_scores_one_hot_keys_closed_form(orc):
     # key s = c_s * e_{d_s} with scale byte b on the group of d_s: the head's
     # dot product is c_s * q[h, d_s] * 2**(eq[h, d_s // 32] + b - 254)
     rng = np.random.default_rng(12)
@@ -201,7 +238,7 @@ def test_mx_scores_one_hot_keys_closed_form():
     k = np.zeros((L, D))
     k[np.arange(L), d_s] = c_s
     sk = rng.integers(124, 131, (L, D // 32)).astype(np.uint8)
-    got = oracle.indexer_scores_row(_e4m3(q), w, _e4m3(k), sq, sk)
+    got = orc.indexer_scores_row(_e4m3(q), w, _e4m3(k), sq, sk)
     for s in range(L):
         g = d_s[s] // 32
         want = 0.0
@@ -211,25 +248,25 @@ def test_mx_scores_one_hot_keys_closed_form():
         assert got[s] == np.float32(want), s
 
 
-def test_mx_scores_code_scale_trade_and_group_locality():
+def test_mx_scores_code_scale_trade_and_group_locality(orc):
     rng = np.random.default_rng(13)
     q, k, sq, sk, w = _mx_case(rng)
-    base = oracle.indexer_scores_row(_e4m3(q), w, _e4m3(k), sq, sk)
+    base = orc.indexer_scores_row(_e4m3(q), w, _e4m3(k), sq, sk)
     # halving a group's codes (kept even so halves stay integers) while
     # raising that group's scale by one step leaves every score unchanged;
     # the trade only holds if the scale multiplies exactly its own 32 dims
     q2, sq2 = 2 * (q // 2), sq.copy()
-    base2 = oracle.indexer_scores_row(_e4m3(q2), w, _e4m3(k), sq2, sk)
+    base2 = orc.indexer_scores_row(_e4m3(q2), w, _e4m3(k), sq2, sk)
     for g in range(q.shape[1] // 32):
         qh, sqh = q2.copy(), sq2.copy()
         qh[:, 32 * g:32 * (g + 1)] //= 2
         sqh[:, g] += 1
-        assert (oracle.indexer_scores_row(_e4m3(qh), w, _e4m3(k), sqh, sk) == base2).all(), g
+        assert (orc.indexer_scores_row(_e4m3(qh), w, _e4m3(k), sqh, sk) == base2).all(), g
     # a key group's scale one step up doubles exactly that group's share of
     # every head's dot product: check through the linear identity of the gate
     # (I(q) - I(-q) = sum_h w_h dot_h), group by group with integer arithmetic
-    lin = lambda qq, sk_: (oracle.indexer_scores_row(_e4m3(qq), w, _e4m3(k), sq, sk_).astype(np.float64)
-                           - oracle.indexer_scores_row(_e4m3(-qq), w, _e4m3(k), sq, sk_).astype(np.float64))
+    lin = lambda qq, sk_: (orc.indexer_scores_row(_e4m3(qq), w, _e4m3(k), sq, sk_).astype(np.float64)
+                           - orc.indexer_scores_row(_e4m3(-qq), w, _e4m3(k), sq, sk_).astype(np.float64))
     d0 = lin(q, sk)
     for g in range(q.shape[1] // 32):
         sk_up = sk.copy()
@@ -242,12 +279,12 @@ def test_mx_scores_code_scale_trade_and_group_locality():
     assert base.dtype == np.float32
 
 
-def test_mx_scores_integer_mode_exact():
+def test_mx_scores_integer_mode_exact(orc):
     # integer codes in [-4, 4], scales 2**-2 .. 2**2: exact rational
     # arithmetic (Python ints over a common 2**-8 denominator) as the route
     rng = np.random.default_rng(14)
     q, k, sq, sk, w = _mx_case(rng, H=16, L=60)
-    s = oracle.indexer_scores_row(_e4m3(q), w, _e4m3(k), sq, sk)
+    s = orc.indexer_scores_row(_e4m3(q), w, _e4m3(k), sq, sk)
     H, L = q.shape[0], k.shape[0]
     want = []
     for j in range(L):
@@ -264,17 +301,17 @@ def test_mx_scores_integer_mode_exact():
 
 # ------------------------------------------------------------------ Top-K
 
-def test_score_keys_order():
+def test_score_keys_order(orc):
     vals = np.array([-np.inf, -3.4e38, -1.0, -1e-40, -0.0, 0.0, 1e-45, 1e-40, 1.0, 2.0,
                      3.4e38, np.inf], dtype=np.float32)
-    keys = oracle.score_keys(vals).astype(np.int64)
+    keys = orc.score_keys(vals).astype(np.int64)
     assert (np.diff(keys)[[0, 1, 2, 3]] > 0).all()
     assert keys[4] == keys[5]                                # -0 and +0 tie
     assert (np.diff(keys)[5:] > 0).all()
-    assert oracle.score_keys(np.array([np.nan], np.float32))[0] == 0
+    assert orc.score_keys(np.array([np.nan], np.float32))[0] == 0
     rng = np.random.default_rng(5)
     x = (rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000)).astype(np.float32)
-    kx = oracle.score_keys(x).astype(np.int64)
+    kx = orc.score_keys(x).astype(np.int64)
     i, j = rng.integers(0, len(x), (2, 20000))
     assert ((x[i] < x[j]) == (kx[i] < kx[j])).all()
 
@@ -287,7 +324,7 @@ def _topk_brute(values, K):
 
 
 @pytest.mark.parametrize("seed", range(12))
-def test_topk_brute_force(seed):
+def test_topk_brute_force(seed, orc):
     rng = np.random.default_rng(100 + seed)
     L = int(rng.integers(1, 400))
     K = int(rng.integers(1, 80))
@@ -297,23 +334,23 @@ def test_topk_brute_force(seed):
         vals = rng.standard_normal(L).astype(np.float32)
     else:
         vals = rng.choice(np.array([-np.inf, -2.0, -0.0, 0.0, 1.0, 7.0, np.inf], np.float32), L)
-    idx, n = oracle.topk_row(vals, K)
+    idx, n = orc.topk_row(vals, K)
     assert n == min(K, L)
     assert idx.tolist() == _topk_brute(vals, K)
 
 
-def test_topk_closed_forms():
-    idx, n = oracle.topk_row(np.full(100, 3.0, np.float32), 10)
+def test_topk_closed_forms(orc):
+    idx, n = orc.topk_row(np.full(100, 3.0, np.float32), 10)
     assert n == 10 and idx.tolist() == list(range(10))             # all equal: lowest positions
-    idx, n = oracle.topk_row(np.arange(5, dtype=np.float32), 8)
+    idx, n = orc.topk_row(np.arange(5, dtype=np.float32), 8)
     assert n == 5 and idx.tolist() == [0, 1, 2, 3, 4, -1, -1, -1]  # K >= L: everything
     vals = np.zeros(1000, np.float32)
     planted = [3, 77, 500, 999]
     vals[planted] = [5, 9, 7, 6]
-    idx, n = oracle.topk_row(vals, 4)
+    idx, n = orc.topk_row(vals, 4)
     assert idx.tolist() == planted                                  # ascending positions
     vals[[10, 20]] = -0.0                                           # -0 ties +0: lower positions win
-    idx, _ = oracle.topk_row(vals, 6)
+    idx, _ = orc.topk_row(vals, 6)
     assert idx.tolist() == [0, 1, 3, 77, 500, 999]
 
 
@@ -323,36 +360,36 @@ def _bf16(x):
     return torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-def test_attention_sparse_equals_masked_dense():
+def test_attention_sparse_equals_masked_dense(orc):
     rng = np.random.default_rng(6)
     H, D, Dv, L = 8, 64, 48, 90
     q, k, v = _bf16(rng.standard_normal((H, D))), _bf16(rng.standard_normal((L, D))), \
         _bf16(rng.standard_normal((L, Dv)))
     sel = np.sort(rng.choice(L, 30, replace=False))
-    o, lse = oracle.sparse_attn_row(q, k[sel], v[sel], 0.125)
+    o, lse = orc.sparse_attn_row(q, k[sel], v[sel], 0.125)
     mask = np.zeros(L, bool); mask[sel] = True
-    o2, lse2 = oracle.masked_dense_attn_row(q, k, v, mask, 0.125)
+    o2, lse2 = orc.masked_dense_attn_row(q, k, v, mask, 0.125)
     assert np.allclose(o, o2, rtol=1e-13, atol=1e-13) and np.allclose(lse, lse2, rtol=1e-13)
     logits = 0.125 * oracle.bf16_to_f64(q) @ oracle.bf16_to_f64(k[sel]).T
     assert np.allclose(lse, scipy.special.logsumexp(logits, axis=1), rtol=1e-13)
 
 
-def test_attention_closed_forms():
+def test_attention_closed_forms(orc):
     rng = np.random.default_rng(7)
     H, D, Dv, n = 4, 32, 16, 12
     q, k, v = _bf16(rng.standard_normal((H, D))), _bf16(rng.standard_normal((n, D))), \
         _bf16(rng.standard_normal((n, Dv)))
     vf = oracle.bf16_to_f64(v)
-    o, lse = oracle.sparse_attn_row(q, k[5:6], v[5:6], 0.3)         # one row: o = v_s
+    o, lse = orc.sparse_attn_row(q, k[5:6], v[5:6], 0.3)         # one row: o = v_s
     assert np.allclose(o, np.broadcast_to(vf[5], o.shape), rtol=0, atol=1e-15)
     assert np.allclose(lse, 0.3 * oracle.bf16_to_f64(q) @ oracle.bf16_to_f64(k[5]), rtol=1e-14)
     const = _bf16(np.full((n, Dv), 1.5))
-    o, _ = oracle.sparse_attn_row(q, k, const, 0.3)                 # constant V
+    o, _ = orc.sparse_attn_row(q, k, const, 0.3)                 # constant V
     assert np.allclose(o, 1.5, rtol=0, atol=1e-14)
-    o, lse = oracle.sparse_attn_row(_bf16(np.zeros((H, D))), k, v, 0.3)   # q = 0: mean of V
+    o, lse = orc.sparse_attn_row(_bf16(np.zeros((H, D))), k, v, 0.3)   # q = 0: mean of V
     assert np.allclose(o, np.broadcast_to(vf.mean(axis=0), o.shape), atol=1e-14)
     assert np.allclose(lse, math.log(n))
-    o, lse = oracle.sparse_attn_row(q, k[:0], v[:0], 0.3)
+    o, lse = orc.sparse_attn_row(q, k[:0], v[:0], 0.3)
     assert (o == 0).all() and np.isneginf(lse).all()
 
 
@@ -378,11 +415,11 @@ def _tiny(**kw):
     return base
 
 
-def test_decode_step_K_at_least_L_is_dense_causal():
+def test_decode_step_K_at_least_L_is_dense_causal(orc):
     # with K >= every history length the sparse step is dense causal attention
     wl = small_workload("t", lengths=[1, 37, 64, 65, 130], latent=True, **_tiny(K=256, D_qk=96))
     arr = oracle_arrays(make_batch(wl, seed=9))
-    res = run_oracle(arr)
+    res = run_oracle(arr, impl=orc)
     for i in range(5):
         b, p = arr["row_seq"][i], arr["row_pos"][i]
         hist = np.arange(p + 1)
@@ -393,7 +430,7 @@ def test_decode_step_K_at_least_L_is_dense_causal():
         assert np.allclose(res["out"][i], dense, rtol=1e-12, atol=1e-12)
 
 
-def test_decode_step_block_table_shuffle_invariance():
+def test_decode_step_block_table_shuffle_invariance(orc):
     wl = small_workload("t", lengths=[300, 129, 700], latent=False, **_tiny(K=40))
     a = oracle_arrays(make_batch(wl, seed=10, table="identity"))
     b = oracle_arrays(make_batch(wl, seed=10, table="shuffled"))
@@ -405,23 +442,23 @@ def test_decode_step_block_table_shuffle_invariance():
             nb = (a["seq_lens"][s] + 63) // 64
             moved[b["block_table"][s, :nb]] = a[key][a["block_table"][s, :nb]]
         b[key] = moved
-    ra, rb = run_oracle(a), run_oracle(b)
+    ra, rb = run_oracle(a, impl=orc), run_oracle(b, impl=orc)
     assert (ra["indices"] == rb["indices"]).all()
     assert all((x == y).all() for x, y in zip(ra["scores"], rb["scores"]))
     assert (ra["out"] == rb["out"]).all()
 
 
-def test_decode_step_row_alone_equals_row_in_batch_and_prefill_rows():
+def test_decode_step_row_alone_equals_row_in_batch_and_prefill_rows(orc):
     wl = small_workload("t", lengths=[500, 260, 900], **_tiny(K=32, D_qk=96, latent=True))
     batch = make_batch(wl, seed=11)
-    full = run_oracle(oracle_arrays(batch))
-    one = run_oracle(oracle_arrays(batch, rows=[2]))
+    full = run_oracle(oracle_arrays(batch), impl=orc)
+    one = run_oracle(oracle_arrays(batch, rows=[2]), impl=orc)
     assert (one["indices"][0] == full["indices"][2]).all()
     assert (one["out"][0] == full["out"][2]).all()
     # a chunked-prefill row at position p sees exactly positions 0..p
     pre = small_workload("p", lengths=[400], prefill_rows=16, **_tiny(K=32))
     arr = oracle_arrays(make_batch(pre, seed=12))
-    res = run_oracle(arr)
+    res = run_oracle(arr, impl=orc)
     assert arr["row_pos"].tolist() == list(range(384, 400))
     for i in range(16):
         assert len(res["scores"][i]) == arr["row_pos"][i] + 1
@@ -441,11 +478,11 @@ def _with_cand(arr, cand_rows):
     return out
 
 
-def test_candidates_covering_the_history_reduce_to_the_full_step():
+def test_candidates_covering_the_history_reduce_to_the_full_step(orc):
     wl = small_workload("t", lengths=[37, 200, 700], **_tiny(K=50))
     arr = oracle_arrays(make_batch(wl, seed=21))
-    full = run_oracle(arr)
-    cand = run_oracle(_with_cand(arr, [np.arange(L) for L in (37, 200, 700)]))
+    full = run_oracle(arr, impl=orc)
+    cand = run_oracle(_with_cand(arr, [np.arange(L) for L in (37, 200, 700)]), impl=orc)
     assert (full["indices"] == cand["indices"]).all()
     assert (full["counts"] == cand["counts"]).all()
     assert np.array_equal(full["out"], cand["out"]) and np.array_equal(full["lse"], cand["lse"])
@@ -454,7 +491,7 @@ def test_candidates_covering_the_history_reduce_to_the_full_step():
 
 
 @pytest.mark.parametrize("seed", [3, 4, 5])
-def test_candidate_scores_and_top_k_by_brute_force(seed):
+def test_candidate_scores_and_top_k_by_brute_force(seed, orc):
     # scores at the candidates are the full scores at those positions; the
     # kept set is the K best candidates (score, then lower position), written
     # ascending, by a plain sort over the candidate list
@@ -462,8 +499,8 @@ def test_candidate_scores_and_top_k_by_brute_force(seed):
     arr = oracle_arrays(make_batch(wl, seed=seed))
     rng = np.random.default_rng(seed)
     rows = [np.sort(rng.choice(900, 150, replace=False)), np.sort(rng.choice(333, 30, replace=False))]
-    full = run_oracle(arr)
-    got = run_oracle(_with_cand(arr, rows))
+    full = run_oracle(arr, impl=orc)
+    got = run_oracle(_with_cand(arr, rows), impl=orc)
     for i, c in enumerate(rows):
         sc = np.asarray(full["scores"][i])[c]
         assert np.array_equal(np.asarray(got["scores"][i]), sc)
@@ -474,18 +511,18 @@ def test_candidate_scores_and_top_k_by_brute_force(seed):
         assert (got["indices"][i][:n] == want).all() and (got["indices"][i][n:] == -1).all()
 
 
-def test_candidates_outside_the_kept_set_do_not_matter():
+def test_candidates_outside_the_kept_set_do_not_matter(orc):
     # dropping candidates that are not kept leaves the selection and the
     # attention unchanged; an empty list keeps nothing
     wl = small_workload("t", lengths=[500], **_tiny(K=20, mode="gauss"))
     arr = oracle_arrays(make_batch(wl, seed=8))
     c = np.arange(0, 500, 3)
-    a = run_oracle(_with_cand(arr, [c]))
+    a = run_oracle(_with_cand(arr, [c]), impl=orc)
     kept = a["indices"][0][:20]
-    b = run_oracle(_with_cand(arr, [np.union1d(kept, c[::5])]))
+    b = run_oracle(_with_cand(arr, [np.union1d(kept, c[::5])]), impl=orc)
     assert (a["indices"] == b["indices"]).all()
     assert np.allclose(a["out"], b["out"], rtol=0, atol=1e-12)
-    e = run_oracle(_with_cand(arr, [np.array([], dtype=np.int64)]))
+    e = run_oracle(_with_cand(arr, [np.array([], dtype=np.int64)]), impl=orc)
     assert e["counts"][0] == 0 and (e["indices"][0] == -1).all() and (e["out"][0] == 0).all()
 
 
