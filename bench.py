@@ -9,12 +9,25 @@ resident in HBM before timing starts; R independent input sets rotate so the
 bytes touched per rotation exceed the 256 MB Infinity Cache several times.
 
 value      decode tokens/s = rows * steps / timed seconds (whole GPU)
-roofline   the dominant kernel (the indexer scan): algorithmic bytes per
-           launch / its average launch time, measured here with HIP events
-           on the launch stream, against the 8 TB/s HBM peak; `traffic` is
-           the counter-measured HBM bytes per launch from profiles/ (null
-           when the kernel source changed since they were taken)
-cpu_baseline  the oracle timed on the host on a bounded sample of rows
+roofline   the dominant kernel, the indexer scan as the fused step launches
+           it: the algorithmic bytes of its launch (index keys, queries,
+           weights, block-table entries; no score matrix) over its average
+           duration, from HIP events that the kernel's own dispatch stamps
+           on the launch stream (dsa_decode_step_timed), against
+           the 8 TB/s HBM peak; `traffic` is the counter-measured HBM bytes per
+           launch from profiles/ (null when the kernel source changed since)
+stages     average duration of each stage of the fused step (scan, Top-K
+           selection, attention, split-key merge) from the same events, and
+           the gaps between them, with
+           the attention's own HBM and bf16-MFMA roofline fractions
+indexer_scores_launch  the scan launched alone by dsa_indexer_scores (it
+           also writes the float32 score rows), timed with HIP events
+cpu_baseline  the plain C++ oracle on the host: whole rows, on one thread
+           and on every affinity core
+workloads  the other workload shapes (decode 32 x 32k, ragged 64 x
+           U[1k, 128k] with a shuffled table, chunked prefill of 4096 rows on
+           a 61440-token prefix): step time, tokens/s, HBM fraction, and for
+           the prefill the fraction of the FP8 + bf16 MFMA roofline
 mxfp8_indexer  the same workload with MXFP8 indexer operands (one E8M0 scale
            per 32 dims): the fused step and the indexer scan alone, timed the
            same way over their own rotating input sets (--no-mxfp8 skips it)
@@ -37,7 +50,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFS = 5000.0    # dense FP8 MFMA, TFLOP/s
+BF16_PEAK_TFS = 2500.0   # dense bf16 MFMA, TFLOP/s
 MALL_BYTES = 256 << 20
+OTHER_WORKLOADS = "decode_32x32k,ragged_64_1k_128k,prefill_4096_on_61440"
 
 
 def parse():
@@ -61,10 +77,19 @@ def parse():
     ap.add_argument("--no-mxfp8", action="store_true",
                     help="skip the MXFP8-indexer leg (same workload, group-32 scales)")
     ap.add_argument("--table", default=None)
+    ap.add_argument("--legs", default=OTHER_WORKLOADS,
+                    help="comma-separated other workloads to time after the headline ('none')")
+    ap.add_argument("--no-scan-leg", action="store_true",
+                    help="skip timing the scan launched alone by dsa_indexer_scores")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain elementwise copy of MIB MiB (float32 in, float32 out) "
                          "so that hardware byte counters can be scaled against known traffic")
     return ap.parse_args()
+
+
+def log(msg):
+    """Progress line on stderr (the JSON result alone goes to stdout)."""
+    print(f"bench.py: {msg}", file=sys.stderr, flush=True)
 
 
 def step_bytes(wl, lengths):
@@ -80,13 +105,29 @@ def step_bytes(wl, lengths):
     return total
 
 
-def indexer_bytes(wl, lengths, mx=False):
+def indexer_bytes(wl, lengths, mx=False, scores=False):
     """Algorithmic bytes of one indexer-scan launch: index keys, queries,
-    weights, block-table entries, and the float32 scores it writes; with
-    MXFP8 operands also one scale byte per 32 dims of every key and query."""
+    weights and block-table entries; with MXFP8 operands also one scale byte
+    per 32 dims of every key and query; with ``scores`` the float32 score
+    rows that dsa_indexer_scores writes (the fused step needs none)."""
     per = wl.D_I + (wl.D_I // 32 if mx else 0)
-    return sum(per * L + wl.H_I * per + 4 * wl.H_I + 4 * ((L + 63) // 64) + 4 * L
+    return sum(per * L + wl.H_I * per + 4 * wl.H_I + 4 * ((L + 63) // 64)
+               + (4 * L if scores else 0) for L in lengths)
+
+
+def attention_bytes(wl, lengths):
+    """Algorithmic bytes of the attention stage: the gathered KV rows, the
+    queries and the output (the selection it reads is a few KiB)."""
+    row_kv = 2 * (wl.D_qk if wl.latent else wl.D_qk + wl.D_v)
+    return sum(row_kv * min(wl.K, L) + 2 * wl.H_q * wl.D_qk + 2 * wl.H_q * wl.D_v
                for L in lengths)
+
+
+def step_flops(wl, lengths):
+    """(FP8 indexer flops, bf16 attention flops) of one step."""
+    fp8 = sum(2 * wl.H_I * wl.D_I * L for L in lengths)
+    bf16 = sum(2 * wl.H_q * (wl.D_qk + wl.D_v) * min(wl.K, L) for L in lengths)
+    return fp8, bf16
 
 
 def recorded_traffic(workload):
@@ -201,24 +242,19 @@ def main():
     ms_per_step = 1e3 * gpu_s / args.steps
     value = rows * args.steps / gpu_s
 
-    # ---- dominant kernel: the indexer scan, timed alone on the same stream
-    ld = 64 * first.max_blocks
-    scores = torch.empty((rows, ld), dtype=torch.float32, device=dev)
-    ws_i = B.workspace(probs[0], B.DSA_OP_INDEXER_SCORES, device=dev)
-    with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            s = sets[i % rotate]
-            B.dsa_indexer_scores(probs[i % rotate], s.qI, s.w, s.kI, scores, ws_i, stream=stream)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(args.steps):
-            s = sets[i % rotate]
-            B.dsa_indexer_scores(probs[i % rotate], s.qI, s.w, s.kI, scores, ws_i, stream=stream)
-        e1.record(stream)
-    torch.cuda.synchronize()
-    idx_us = 1e3 * e0.elapsed_time(e1) / args.steps
+    # ---- per-stage times of the fused step, from HIP events recorded between
+    # its kernels on the launch stream; the dominant kernel is the scan
+    log(f"headline {name}: {ms_per_step * 1e3:.2f} us per step; stage times")
+    st = stage_times(args, sets, probs, outs, ws, stream)
     ib = indexer_bytes(wl, lengths)
-    achieved = ib / (idx_us * 1e-6) / 1e9
+    achieved = ib / (st["indexer_us"] * 1e-6) / 1e9
+    ab = attention_bytes(wl, lengths)
+    _, attn_flops = step_flops(wl, lengths)
+    st["attention_gbs"] = round(ab / (st["attention_us"] * 1e-6) / 1e9, 1)
+    st["attention_hbm_frac"] = round(st["attention_gbs"] / HBM_PEAK_GBS, 4)
+    st["attention_bytes"] = ab
+    st["attention_bf16_mfma_frac"] = round(
+        attn_flops / (st["attention_us"] * 1e-6) / 1e12 / BF16_PEAK_TFS, 4)
     traffic = recorded_traffic(name)
 
     result = {
@@ -244,18 +280,30 @@ def main():
         "step_hbm_frac": round(sb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_bytes": sb,
         "roofline": {
-            "bound": "hbm", "kernel": "indexer_scan_kernel", "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic, "bytes_per_launch": ib, "avg_launch_us": round(idx_us, 3),
+            "bound": "hbm", "kernel": "indexer_scan_kernel (fused step)",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "bytes_per_launch": ib, "avg_launch_us": st["indexer_us"],
         },
+        "stages": st,
         "wall_s": round(wall, 4),
     }
+    if not args.no_scan_leg:
+        result["indexer_scores_launch"] = scan_leg(args, wl, lengths, sets, probs, stream)
 
     result.update(spread_legs(args, graphs, rotate, step, stream, rows))
     if not args.no_mxfp8:
-        result["mxfp8_indexer"] = mxfp8_leg(args, wl, lengths, stream, rotate_bytes=ib)
+        log("mxfp8 indexer leg")
+        result["mxfp8_indexer"] = guarded(mxfp8_leg, args, wl, lengths, stream, rotate_bytes=ib)
     if not args.no_cand:
-        result["candidate_indexer"] = cand_leg(args, wl, lengths, stream)
+        log("candidate indexer leg")
+        result["candidate_indexer"] = guarded(cand_leg, args, wl, lengths, stream)
+    legs = [x for x in args.legs.split(",") if x and x != "none" and x != name]
+    if legs:
+        del sets, probs, outs, graphs
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        result["workloads"] = {x: guarded(workload_leg, args, x, stream) for x in legs}
 
     if args.copy_calibration:
         n = (args.copy_calibration << 20) // 4
@@ -269,8 +317,192 @@ def main():
                                       "read_bytes": 4 * n, "write_bytes": 4 * n, "launches": 3}
 
     if not args.no_cpu_baseline:
+        log("cpu baseline")
         result["cpu_baseline"] = cpu_baseline(first, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def guarded(fn, *a, **kw):
+    """A side leg: its result, or the error that stopped it (the headline
+    line is still printed)."""
+    try:
+        return fn(*a, **kw)
+    except Exception as e:  # reported in the JSON line, not hidden
+        log(f"{fn.__name__} failed: {e!r}")
+        return {"error": repr(e)}
+
+
+def stage_times(args, sets, probs, outs, ws, stream):
+    """Average duration of each stage of the fused step over `steps` eager
+    launches of dsa_decode_step_timed on the stream, rotating the input
+    sets: each kernel's dispatch stamps HIP events with its own start and
+    end, so the figures are kernel durations; the gaps between stages are
+    reported apart."""
+    import torch
+    from indexer_top_sparse_score_amd import binding as B
+    nset = len(sets)
+    names = ("indexer_us", "topk_us", "attention_us", "merge_us")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            for e in evs[i]:
+                e.record(stream)  # torch creates its events on first record
+        torch.cuda.synchronize()
+
+        def one(i, ev):
+            s, p = sets[i % nset], probs[i % nset]
+            out, lse = outs[i % nset]
+            v = s.v if s.v is not None else s.kv
+            B.dsa_decode_step_timed(p, s.qI, s.w, s.kI, s.q, s.kv, v, out, ws, ev, lse=lse,
+                                    stream=stream)
+        for i in range(args.warmup):
+            one(i, evs[i % args.steps])
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            one(i, evs[i])
+    torch.cuda.synchronize()
+    assert B.device_errors(ws) == 0
+    out = {}
+    for k, nm in enumerate(names):
+        t = sorted(1e3 * evs[i][2 * k].elapsed_time(evs[i][2 * k + 1]) for i in range(args.steps))
+        out[nm] = round(sum(t) / len(t), 3)
+        out[nm.replace("_us", "_p50_us")] = round(t[len(t) // 2], 3)
+    gaps = [sum(1e3 * evs[i][2 * k + 1].elapsed_time(evs[i][2 * k + 2]) for i in range(args.steps))
+            / args.steps for k in range(3)]
+    out["gaps_us"] = [round(g, 3) for g in gaps]
+    out["sum_us"] = round(sum(out[nm] for nm in names) + sum(gaps), 3)
+    out["launch"] = "stream (eager), kernel start/end stamped by the dispatches"
+    return out
+
+
+def scan_leg(args, wl, lengths, sets, probs, stream):
+    """The indexer scan launched alone by dsa_indexer_scores over the same
+    rotating input sets, timed with HIP events on the stream; its bytes
+    include the float32 score rows it writes."""
+    import torch
+    from indexer_top_sparse_score_amd import binding as B
+    nset = len(sets)
+    rows = sets[0].rows
+    scores = torch.empty((rows, 64 * sets[0].max_blocks), dtype=torch.float32, device="cuda")
+    ws_i = B.workspace(probs[0], B.DSA_OP_INDEXER_SCORES, device="cuda")
+
+    def scan(i):
+        s = sets[i % nset]
+        B.dsa_indexer_scores(probs[i % nset], s.qI, s.w, s.kI, scores, ws_i, stream=stream)
+
+    us = timed_eager(args, scan, stream)
+    assert B.device_errors(ws_i) == 0
+    ib = indexer_bytes(wl, lengths, scores=True)
+    ach = ib / (us * 1e-6) / 1e9
+    return {"avg_launch_us": round(us, 3), "bytes_per_launch": ib, "achieved": round(ach, 1),
+            "frac": round(ach / HBM_PEAK_GBS, 4)}
+
+
+def timed_eager(args, fn, stream, steps=None):
+    """Average microseconds of fn(i) over `steps` eager launches on the
+    stream after the warm-up, with HIP events on that stream."""
+    import torch
+    steps = steps or args.steps
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            fn(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            fn(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / steps
+
+
+def workload_leg(args, name, stream):
+    """One of the other workload shapes: the fused step over input sets that
+    rotate past the Infinity Cache (graph replays of one step per set, as
+    the headline), its stage times, tokens/s and HBM fraction; for a
+    prefill, also the fraction of the FP8 + bf16 MFMA roofline."""
+    import torch
+    from indexer_top_sparse_score_amd import binding as B
+    from workloads import CONFIGS, make_batch, row_positions
+    wl = CONFIGS[name]
+    log(f"workload leg {name}")
+    dev = torch.device("cuda:0")
+    first = make_batch(wl, device=dev, seed=wl.seed, mode=args.mode)
+    lengths = [first.lengths[b] if not wl.prefill_rows else p + 1
+               for b, p in row_positions(first)]
+    rows = first.rows
+    sb = step_bytes(wl, lengths)
+    fp8, bf16 = step_flops(wl, lengths)
+    nset = max(1, min(8, -(-4 * MALL_BYTES // sb)))
+    if wl.prefill_rows:
+        nset = 1  # compute-bound: nothing to gain from rotation
+    # every set has the first one's lengths (ragged shapes: the same mix)
+    sets = [first] + [make_batch(wl, device=dev, seed=wl.seed + 1000 * i, mode=args.mode,
+                                 lengths=first.lengths) for i in range(1, nset)]
+    probs = [B.problem_for_batch(s) for s in sets]
+    outs = [(torch.empty((rows, wl.H_q, wl.D_v), dtype=torch.bfloat16, device=dev),
+             torch.empty((rows, wl.H_q), dtype=torch.float32, device=dev)) for _ in sets]
+    ws = B.workspace(max(probs, key=lambda p: B.dsa_workspace_size(p, B.DSA_OP_DECODE_STEP)),
+                     B.DSA_OP_DECODE_STEP, device=dev)
+
+    def step(i):
+        s, p = sets[i % nset], probs[i % nset]
+        out, lse = outs[i % nset]
+        v = s.v if s.v is not None else s.kv
+        B.dsa_decode_step(p, s.qI, s.w, s.kI, s.q, s.kv, v, out, ws, lse=lse, stream=stream)
+
+    steps = args.steps if not wl.prefill_rows else max(5, min(args.steps, 20))
+    with torch.cuda.stream(stream):
+        for i in range(max(1, args.warmup)):
+            step(i)
+    torch.cuda.synchronize()
+    launch = "stream (eager)"
+    us = None
+    if args.graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(nset):
+                    step(i)
+            reps = max(1, steps // nset)
+            with torch.cuda.stream(stream):
+                g.replay()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    g.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            us = 1e3 * e0.elapsed_time(e1) / (reps * nset)
+            steps = reps * nset
+            launch = f"graph ({nset} steps per replay)"
+            del g
+        except Exception as e:  # capture unsupported: stream launches
+            print(f"bench.py: graph capture failed for {name} ({e})", file=sys.stderr)
+    if us is None:
+        us = timed_eager(args, step, stream, steps)
+    assert B.device_errors(ws) == 0
+    sargs = argparse.Namespace(**{**vars(args), "steps": min(steps, 20), "warmup": 2})
+    st = stage_times(sargs, sets, probs, outs, ws, stream)
+    leg = {"rows": rows, "context_max": max(lengths), "rotation_sets": nset, "launch": launch,
+           "steps": steps, "step_us": round(us, 3), "tokens_per_s": round(rows / (us * 1e-6), 1),
+           "step_bytes": sb, "step_gbs": round(sb / (us * 1e-6) / 1e9, 1),
+           "hbm_frac": round(sb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "stages_last_pass": st}
+    if not wl.prefill_rows:
+        # decode shapes run in one pass of rows: the stages cover the step
+        leg["indexer_frac"] = round(indexer_bytes(wl, lengths) / (st["indexer_us"] * 1e-6)
+                                    / 1e9 / HBM_PEAK_GBS, 4)
+        leg["attention_hbm_frac"] = round(attention_bytes(wl, lengths) / (st["attention_us"]
+                                          * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    else:
+        ideal_us = 1e6 * (fp8 / (FP8_PEAK_TFS * 1e12) + bf16 / (BF16_PEAK_TFS * 1e12))
+        leg.update({"fp8_tflop": round(fp8 / 1e12, 4), "bf16_tflop": round(bf16 / 1e12, 4),
+                    "mfma_ideal_us": round(ideal_us, 1),
+                    "mfma_roofline_frac": round(ideal_us / us, 4)})
+    del sets, probs, outs, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return leg
 
 
 def mxfp8_leg(args, wl, lengths, stream, rotate_bytes):

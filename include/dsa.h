@@ -62,7 +62,7 @@ extern "C" {
 #define DSA_API
 #endif
 
-#define DSA_ABI_VERSION 5
+#define DSA_ABI_VERSION 6
 #define DSA_BLOCK_SIZE 64
 #define DSA_MAX_ATTN_K 16384 /* largest K of dsa_sparse_attn / dsa_decode_step */
 #define DSA_STATIC_SCRATCH_BYTES (64u << 20) /* scratch of dsa_decode_step_static, per GPU */
@@ -228,6 +228,25 @@ DSA_API int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float
                     const uint16_t* q, dsa_paged k, dsa_paged v, uint16_t* out, float* lse,
                     int32_t* indices_out, int32_t* counts_out, void* ws, size_t ws_bytes,
                     void* stream);
+
+/*
+ * dsa_decode_step with per-stage timing, for benchmarks: the same launches
+ * and results, plus eight caller-created HIP events (hipEvent_t, passed as
+ * void*) that the last pass of rows stamps with the start and end times of
+ * its stages, taken by the kernel dispatches themselves:
+ *   events[0], [1]  indexer scan        events[2], [3]  Top-K selection
+ *   events[4], [5]  sparse attention    events[6], [7]  split-key merge
+ * (with no merge kernel, [6] and [7] are recorded right after the attention),
+ * so hipEventElapsedTime(events[2i], events[2i + 1]) is the duration of
+ * stage i.  Not meant for graph capture.  events NULL, or any of the eight
+ * NULL: DSA_ERR_INVALID and nothing runs.  Other arguments and errors as
+ * dsa_decode_step.
+ */
+DSA_API int dsa_decode_step_timed(const dsa_problem* p, const uint8_t* qI, const float* w,
+                                  dsa_paged kI, const uint16_t* q, dsa_paged k, dsa_paged v,
+                                  uint16_t* out, float* lse, int32_t* indices_out,
+                                  int32_t* counts_out, void* ws, size_t ws_bytes,
+                                  void* const* events, void* stream);
 
 /*
  * The fused step without a workspace argument, for callers that cannot

@@ -27,14 +27,15 @@ DSA_OP_TOPK = 1
 DSA_OP_SPARSE_ATTN = 2
 DSA_OP_DECODE_STEP = 3
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 DSA_INDEXER_E4M3 = 0
 DSA_INDEXER_MXFP8 = 1
 BLOCK = 64
 
 #: every symbol include/dsa.h declares
 EXPORTS = ("dsa_workspace_size", "dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn",
-           "dsa_decode_step", "dsa_decode_step_static", "dsa_status_string", "dsa_abi_version")
+           "dsa_decode_step", "dsa_decode_step_timed", "dsa_decode_step_static",
+           "dsa_status_string", "dsa_abi_version")
 
 
 class DsaPaged(ctypes.Structure):
@@ -81,10 +82,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_sparse_attn.argtypes = [prob, P, DsaPaged, DsaPaged, P, P, P, P, sz, P]
     lib.dsa_decode_step.argtypes = [prob, P, P, DsaPaged, P, DsaPaged, DsaPaged, P, P, P, P, P,
                                     sz, P]
+    lib.dsa_decode_step_timed.argtypes = [prob, P, P, DsaPaged, P, DsaPaged, DsaPaged, P, P, P,
+                                          P, P, sz, ctypes.POINTER(P), P]
     lib.dsa_decode_step_static.argtypes = [prob, P, P, DsaPaged, P, DsaPaged, DsaPaged, P, P, P,
                                            P, P, P]
     for f in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_decode_step",
-              "dsa_decode_step_static"):
+              "dsa_decode_step_timed", "dsa_decode_step_static"):
         getattr(lib, f).restype = ctypes.c_int
     lib.dsa_status_string.argtypes = [ctypes.c_int]
     lib.dsa_status_string.restype = ctypes.c_char_p
@@ -207,6 +210,26 @@ def dsa_decode_step(prob, qI, w, kI, q, k, v, out, ws, lse=None, indices=None, c
                                   paged(k), paged(v), _ptr(out), _ptr(lse), _ptr(indices),
                                   _ptr(counts), _ptr(ws), ws.numel(), _stream(stream)),
            "dsa_decode_step")
+
+
+def dsa_decode_step_timed(prob, qI, w, kI, q, k, v, out, ws, events, lse=None, indices=None,
+                          counts=None, stream=None):
+    """dsa_decode_step, stamping eight torch.cuda.Event objects with the start
+    and end of its stages (scan, selection, attention, merge).  Each event is
+    recorded once first if it has no HIP event yet (torch creates them
+    lazily)."""
+    if len(events) != 8:
+        raise ValueError("eight events")
+    handles = []
+    for e in events:
+        if not e.cuda_event:
+            e.record()
+        handles.append(e.cuda_event)
+    arr = (ctypes.c_void_p * 8)(*handles)
+    _check(load().dsa_decode_step_timed(ctypes.byref(prob), _ptr(qI), _ptr(w), paged(kI), _ptr(q),
+                                        paged(k), paged(v), _ptr(out), _ptr(lse), _ptr(indices),
+                                        _ptr(counts), _ptr(ws), ws.numel(), arr,
+                                        _stream(stream)), "dsa_decode_step_timed")
 
 
 def dsa_decode_step_static(prob, qI, w, kI, q, k, v, out, lse=None, indices=None, counts=None,

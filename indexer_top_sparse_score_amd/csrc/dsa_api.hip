@@ -210,11 +210,13 @@ int check_decode_args(const dsa_problem* p, const uint8_t* qI, const float* w,
 }
 
 // The fused step itself, on a workspace `base` laid out as `d`; device-side
-// errors are OR-ed into *err.
+// errors are OR-ed into *err.  With `ev` (eight events), the last pass of
+// rows stamps the start and end of its scan (ev[0], ev[1]), selection
+// (ev[2], ev[3]), attention (ev[4], ev[5]) and merge (ev[6], ev[7]).
 int decode_run(const dsa_problem* p, const uint8_t* qI, const float* w, dsa_paged kI,
                const uint16_t* q, dsa_paged k, dsa_paged v, uint16_t* out, float* lse,
                int32_t* indices_out, int32_t* counts_out, char* base, const DecodeLayout& d,
-               uint32_t* err, hipStream_t s) {
+               uint32_t* err, hipStream_t s, const hipEvent_t* ev = nullptr) {
   int st = DSA_OK;
   float* scores = reinterpret_cast<float*>(base + d.scores_off);
   const int64_t ld = slab_ld(p);
@@ -229,6 +231,12 @@ int decode_run(const dsa_problem* p, const uint8_t* qI, const float* w, dsa_page
     const int nr = p->num_rows - row0 < d.rp ? p->num_rows - row0 : d.rp;
     int32_t* idx = indices_out ? indices_out + (int64_t)row0 * p->K
                                : reinterpret_cast<int32_t*>(base + d.idx_off);
+    const hipEvent_t* tev = ev && row0 + nr >= p->num_rows ? ev : nullptr;
+    auto stage = [&](int i) {
+      StageEvents e;
+      if (tev) e = StageEvents{tev[2 * i], tev[2 * i + 1]};
+      return e;
+    };
 
     IndexerLaunch ia;
     ia.rows = row_map(p);
@@ -246,7 +254,7 @@ int decode_run(const dsa_problem* p, const uint8_t* qI, const float* w, dsa_page
     ia.max_len = (int32_t)max_len(p);
     ia.sum = sum;
     ia.topk_K = p->K;
-    if ((st = status_of(launch_indexer_scores(ia, s))) != DSA_OK) return st;
+    if ((st = status_of(launch_indexer_scores(ia, s, stage(0)))) != DSA_OK) return st;
 
     TopkLaunch ta;
     ta.rows = row_map(p);
@@ -264,7 +272,7 @@ int decode_run(const dsa_problem* p, const uint8_t* qI, const float* w, dsa_page
     ta.vec = true;    // 256-byte aligned slab, ld a multiple of 64
     ta.rowoff = use_rowoff ? roff : nullptr;
     ta.kv = k;
-    if ((st = status_of(launch_topk(ta, s))) != DSA_OK) return st;
+    if ((st = status_of(launch_topk(ta, s, stage(1)))) != DSA_OK) return st;
 
     AttnLaunch aa = attn_launch(p, q, k, v, out, lse, err);
     aa.indices = idx;
@@ -275,7 +283,7 @@ int decode_run(const dsa_problem* p, const uint8_t* qI, const float* w, dsa_page
     // the workspace holds partials for the larger of the two layouts' counts
     aa.n_chunks = attn_chunks(d.rp, p->H_q, p->D_qk, p->K, aa.latent);
     aa.partial = aa.n_chunks > 1 ? static_cast<void*>(base + d.part_off) : nullptr;
-    if ((st = status_of(launch_sparse_attn(aa, s))) != DSA_OK) return st;
+    if ((st = status_of(launch_sparse_attn(aa, s, stage(2), stage(3)))) != DSA_OK) return st;
   }
   return DSA_OK;
 }
@@ -456,6 +464,27 @@ int dsa_decode_step(const dsa_problem* p, const uint8_t* qI, const float* w, dsa
   return decode_run(p, qI, w, kI, q, k, v, out, lse, indices_out, counts_out, base,
                     decode_layout(p), reinterpret_cast<uint32_t*>(base),
                     static_cast<hipStream_t>(stream));
+}
+
+int dsa_decode_step_timed(const dsa_problem* p, const uint8_t* qI, const float* w, dsa_paged kI,
+                          const uint16_t* q, dsa_paged k, dsa_paged v, uint16_t* out, float* lse,
+                          int32_t* indices_out, int32_t* counts_out, void* ws, size_t ws_bytes,
+                          void* const* events, void* stream) {
+  if (!events) return DSA_ERR_INVALID;
+  hipEvent_t ev[8];
+  for (int i = 0; i < 8; ++i) {
+    if (!events[i]) return DSA_ERR_INVALID;
+    ev[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  int st = check_decode_args(p, qI, w, kI, q, k, v, out, lse, indices_out, counts_out);
+  if (st != DSA_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, dsa_workspace_size(p, DSA_OP_DECODE_STEP))) != DSA_OK)
+    return st;
+  if (p->num_rows == 0) return DSA_OK;
+  char* base = static_cast<char*>(ws);
+  return decode_run(p, qI, w, kI, q, k, v, out, lse, indices_out, counts_out, base,
+                    decode_layout(p), reinterpret_cast<uint32_t*>(base),
+                    static_cast<hipStream_t>(stream), ev);
 }
 
 int dsa_decode_step_static(const dsa_problem* p, const uint8_t* qI, const float* w,

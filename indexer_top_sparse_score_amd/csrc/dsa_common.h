@@ -2,6 +2,7 @@
 // Nothing here is exported.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -280,7 +281,28 @@ struct IndexerLaunch {
   Summary sum;                  // summaries for a Top-K of topk_K that follows,
   int32_t topk_K;               // or nothing when sum.key is NULL
 };
-hipError_t launch_indexer_scores(const IndexerLaunch& a, hipStream_t s);
+// Optional timing of a launch: `start` takes the time its (first) kernel
+// begins and `stop` the time its (last) kernel ends, stamped by the
+// dispatch itself (hipExtLaunchKernel), so no marker sits between kernels.
+struct StageEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+// kernel<<<g, b, 0, s>>>(args...), through hipExtLaunchKernel when either
+// event is set.
+template <class... A>
+hipError_t launch_kernel(void (*kernel)(A...), dim3 g, dim3 b, hipStream_t s, hipEvent_t start,
+                         hipEvent_t stop, A... args) {
+  if (!start && !stop) {
+    kernel<<<g, b, 0, s>>>(args...);
+    return hipGetLastError();
+  }
+  void* argv[] = {static_cast<void*>(&args)...};
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), g, b, argv, 0, s, start, stop,
+                            0);
+}
+
+hipError_t launch_indexer_scores(const IndexerLaunch& a, hipStream_t s, StageEvents ev = {});
 
 struct TopkLaunch {
   RowMap rows;
@@ -301,7 +323,7 @@ struct TopkLaunch {
   int64_t* rowoff;
   dsa_paged kv;
 };
-hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
+hipError_t launch_topk(const TopkLaunch& a, hipStream_t s, StageEvents ev = {});
 
 struct AttnLaunch {
   RowMap rows;
@@ -333,6 +355,10 @@ size_t attn_partial_bytes(int num_rows, int H_q, int D_v, int n_chunks);
 // whether launch_sparse_attn reads row offsets (AttnLaunch.rowoff) for this
 // shape and layout
 bool attn_uses_rowoff(int D_qk, int D_v, bool latent);
-hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s);
+// `ev` times the attention kernel, `merge` the split-key merge (with one
+// chunk per row there is no merge kernel: both its events are recorded on
+// the stream right after the attention)
+hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s, StageEvents ev = {},
+                              StageEvents merge = {});
 
 }  // namespace dsa

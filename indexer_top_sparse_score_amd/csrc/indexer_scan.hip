@@ -310,39 +310,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
 }
 
 template <int NKP, int HT, bool MX>
-hipError_t launch_t(const IndexerLaunch& a, hipStream_t s) {
+hipError_t launch_t(const IndexerLaunch& a, hipStream_t s, StageEvents ev) {
   dim3 grid((a.max_len + kTile - 1) / kTile, a.num_rows);
-  if (a.rows.cand)
-    indexer_scan_kernel<NKP, HT, MX, true><<<grid, 256, 0, s>>>(a);
-  else
-    indexer_scan_kernel<NKP, HT, MX, false><<<grid, 256, 0, s>>>(a);
-  return hipGetLastError();
+  return launch_kernel(a.rows.cand ? indexer_scan_kernel<NKP, HT, MX, true>
+                                   : indexer_scan_kernel<NKP, HT, MX, false>,
+                       grid, dim3(256), s, ev.start, ev.stop, a);
 }
 
 template <bool MX>
-hipError_t launch_mx(const IndexerLaunch& a, hipStream_t s) {
+hipError_t launch_mx(const IndexerLaunch& a, hipStream_t s, StageEvents ev) {
   const int ht = (a.H_I + 15) / 16;
   if (a.D_I == 128) {
     switch (ht) {
-      case 1: return launch_t<2, 1, MX>(a, s);
-      case 2: return launch_t<2, 2, MX>(a, s);
-      case 3: return launch_t<2, 3, MX>(a, s);
-      default: return launch_t<2, 4, MX>(a, s);
+      case 1: return launch_t<2, 1, MX>(a, s, ev);
+      case 2: return launch_t<2, 2, MX>(a, s, ev);
+      case 3: return launch_t<2, 3, MX>(a, s, ev);
+      default: return launch_t<2, 4, MX>(a, s, ev);
     }
   }
   switch (ht) {
-    case 1: return launch_t<1, 1, MX>(a, s);
-    case 2: return launch_t<1, 2, MX>(a, s);
-    case 3: return launch_t<1, 3, MX>(a, s);
-    default: return launch_t<1, 4, MX>(a, s);
+    case 1: return launch_t<1, 1, MX>(a, s, ev);
+    case 2: return launch_t<1, 2, MX>(a, s, ev);
+    case 3: return launch_t<1, 3, MX>(a, s, ev);
+    default: return launch_t<1, 4, MX>(a, s, ev);
   }
 }
 
 }  // namespace
 
-hipError_t launch_indexer_scores(const IndexerLaunch& a, hipStream_t s) {
+hipError_t launch_indexer_scores(const IndexerLaunch& a, hipStream_t s, StageEvents ev) {
   if (a.num_rows <= 0 || a.max_len <= 0) return hipSuccess;
-  return a.qI_scale ? launch_mx<true>(a, s) : launch_mx<false>(a, s);
+  return a.qI_scale ? launch_mx<true>(a, s, ev) : launch_mx<false>(a, s, ev);
 }
 
 }  // namespace dsa

@@ -911,34 +911,33 @@ bool uses_latent_kernel(int D_qk, bool latent) {
 }
 
 template <int DQK, int DV, int NW>
-hipError_t launch_t(const AttnLaunch& a, hipStream_t s) {
+hipError_t launch_t(const AttnLaunch& a, hipStream_t s, StageEvents ev, StageEvents merge) {
   AttnGrid g;
   g.n_hg = (a.H_q + kHPW * NW - 1) / (kHPW * NW);
   g.n_units = a.num_rows * a.n_chunks;
   const int per = (a.K + a.n_chunks - 1) / a.n_chunks;
   g.chunk = (per + kSB - 1) / kSB * kSB;
   const int grid = (g.n_units + 7) / 8 * 8 * g.n_hg;
-  bool done = false;
+  void (*kernel)(AttnLaunch, AttnGrid) = nullptr;
   if constexpr (DQK == lat::kDqk && NW > 1) {
-    if (uses_latent_kernel(DQK, a.latent)) {
-      sparse_attn_latent_kernel<DSA_ATTN_NBUF, NW><<<grid, 64 * NW, 0, s>>>(a, g);
-      done = true;
-    }
+    if (uses_latent_kernel(DQK, a.latent)) kernel = sparse_attn_latent_kernel<DSA_ATTN_NBUF, NW>;
   }
   // (the 576-wide staged kernel only ever runs with four waves)
   if constexpr (DQK != lat::kDqk || NW == 4) {
-    if (!done) {
-      if (a.latent)
-        sparse_attn_kernel<DQK, DV, true, NW><<<grid, 64 * NW, 0, s>>>(a, g);
-      else
-        sparse_attn_kernel<DQK, DV, false, NW><<<grid, 64 * NW, 0, s>>>(a, g);
-    }
+    if (!kernel)
+      kernel = a.latent ? sparse_attn_kernel<DQK, DV, true, NW> : sparse_attn_kernel<DQK, DV, false, NW>;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_chunks == 1) return e;
+  if (!kernel) return hipErrorInvalidConfiguration;
+  hipError_t e = launch_kernel(kernel, dim3(grid), dim3(64 * NW), s, ev.start, ev.stop, a, g);
+  if (e != hipSuccess) return e;
+  if (a.n_chunks == 1) {
+    if (merge.start && (e = hipEventRecord(merge.start, s)) != hipSuccess) return e;
+    if (merge.stop && (e = hipEventRecord(merge.stop, s)) != hipSuccess) return e;
+    return hipSuccess;
+  }
   constexpr int MT = DV / 16, MTW = MT < 8 ? MT : 8;
-  attn_combine_kernel<DV><<<dim3(a.num_rows, (a.H_q + 15) / 16, MT / MTW), 256, 0, s>>>(a);
-  return hipGetLastError();
+  return launch_kernel(attn_combine_kernel<DV>, dim3(a.num_rows, (a.H_q + 15) / 16, MT / MTW),
+                       dim3(256), s, merge.start, merge.stop, a);
 }
 
 }  // namespace
@@ -968,13 +967,14 @@ bool attn_uses_rowoff(int D_qk, int D_v, bool latent) {
   return D_v == lat::kDv && uses_latent_kernel(D_qk, latent);
 }
 
-hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s) {
+hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s, StageEvents ev,
+                              StageEvents merge) {
   if (a.num_rows <= 0) return hipSuccess;
   switch (waves_for(a.H_q, a.D_qk, a.latent) * 1000 + a.D_qk) {
-    case 2576: return launch_t<576, 512, 2>(a, s);
-    case 4576: return launch_t<576, 512, 4>(a, s);
-    case 4064: return launch_t<64, 64, 4>(a, s);
-    default: return launch_t<64, 64, 1>(a, s);
+    case 2576: return launch_t<576, 512, 2>(a, s, ev, merge);
+    case 4576: return launch_t<576, 512, 4>(a, s, ev, merge);
+    case 4064: return launch_t<64, 64, 4>(a, s, ev, merge);
+    default: return launch_t<64, 64, 1>(a, s, ev, merge);
   }
 }
 

@@ -99,16 +99,17 @@ Summary summary_carve(void* base, int rows) {
   return m;
 }
 
-hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
+hipError_t launch_topk(const TopkLaunch& a, hipStream_t s, StageEvents ev) {
   if (a.num_rows <= 0) return hipSuccess;
   if (a.prep) {
     const int64_t spans = (a.max_len + 127) / 128;
-    topk_summary_kernel<<<dim3((unsigned)((spans + 3) / 4), a.num_rows), 256, 0, s>>>(a);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e =
+        launch_kernel(topk_summary_kernel, dim3((unsigned)((spans + 3) / 4), a.num_rows),
+                      dim3(256), s, ev.start, nullptr, a);
     if (e != hipSuccess) return e;
+    ev.start = nullptr;
   }
-  topk_select_kernel<<<dim3(a.num_rows), kNT, 0, s>>>(a);
-  return hipGetLastError();
+  return launch_kernel(topk_select_kernel, dim3(a.num_rows), dim3(kNT), s, ev.start, ev.stop, a);
 }
 
 }  // namespace dsa

@@ -153,3 +153,29 @@ def check_attention(out_t, lse_t, orc_out, orc_lse, rows=None):
 
 def log2ceil(x):
     return int(math.ceil(math.log2(max(1, x))))
+
+
+def oracle_attention_on(arr, indices, counts, threads=None):
+    """The oracle's sparse attention of every row held in ``arr`` over the
+    positions the GPU selected for it (indices [rows, K], counts [rows]):
+    the selected rows are gathered through the block table and attended by
+    the C++ oracle.  Returns (out [rows, H_q, D_v], lse [rows, H_q])."""
+    import oracle
+    import oracle.cpp
+    from tests.helpers import HOST_THREADS
+
+    D_v = int(arr["D_v"])
+    outs, lses = [], []
+    for i in range(len(arr["qI"])):
+        b = arr["row_seq"][i]
+        sel = np.asarray(indices[i][:int(counts[i])], dtype=np.int64)
+        k_rows = oracle.gather_positions(arr["k_cache"], arr["block_table"][b], sel)
+        if arr["v_cache"] is None:
+            v_rows = k_rows[:, :D_v]
+        else:
+            v_rows = oracle.gather_positions(arr["v_cache"], arr["block_table"][b], sel)
+        o, l = oracle.cpp.sparse_attn_row(arr["q"][i], k_rows, v_rows, arr["scale"],
+                                          threads=threads or HOST_THREADS)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)

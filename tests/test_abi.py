@@ -27,7 +27,7 @@ def lib():
 
 def test_exports_every_header_symbol(lib):
     syms = header_symbols()
-    assert len(syms) == 8 and sorted(B.EXPORTS) == syms
+    assert len(syms) == 9 and sorted(B.EXPORTS) == syms
     for s in syms:
         assert getattr(lib, s) is not None
     assert lib.dsa_abi_version() == B.ABI_VERSION
@@ -201,3 +201,20 @@ def test_decode_step_static_rejections():
     # a layout that cannot fit DSA_STATIC_SCRATCH_BYTES even one row per pass:
     # a history of 2^24 blocks needs a 4 GiB score row
     assert call(prob(max_blocks=1 << 24)) == B.DSA_ERR_WORKSPACE
+
+
+def test_decode_step_timed_rejections():
+    # the events are checked first, then everything dsa_decode_step checks;
+    # no case here reaches a launch
+    def call(p, events, ws_bytes=1 << 40):
+        ev = None if events is None else (ctypes.c_void_p * 8)(*events)
+        return B.raw_call("dsa_decode_step_timed", ctypes.byref(p), ctypes.c_void_p(FAKE),
+                          ctypes.c_void_p(FAKE), paged(), ctypes.c_void_p(FAKE),
+                          paged(row=1152), paged(row=1152), ctypes.c_void_p(FAKE), None, None,
+                          None, ctypes.c_void_p(FAKE), ws_bytes, ev, None)
+    eight = [FAKE + 256 * i for i in range(8)]
+    assert call(prob(), None) == B.DSA_ERR_INVALID
+    assert call(prob(), eight[:7] + [None]) == B.DSA_ERR_INVALID
+    assert call(prob(H_I=100), eight) == B.DSA_ERR_UNSUPPORTED
+    assert call(prob(), eight, ws_bytes=0) == B.DSA_ERR_WORKSPACE
+    assert call(prob(num_rows=0), eight) == B.DSA_OK

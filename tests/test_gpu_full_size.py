@@ -8,14 +8,15 @@ rest is -1, and the output is finite with no device error.  Sampled rows
 (the first, the last, the longest and shortest history, and a seeded
 random pick) are compared element by element with the oracle: integer
 mode -- indices bit-exact and attention within tolerance; Gaussian mode
-on the benchmark shape -- Top-K recall >= 0.999 and attention within
-tolerance on the rows whose selection matches."""
+(every workload shape) -- Top-K recall >= 0.999 and attention within
+tolerance against the oracle's attention over the GPU's own indices."""
 
 import numpy as np
 import pytest
 import torch
 
-from tests.gpu_helpers import RECALL_MIN, check_attention, gpu_decode, np_, recall, say
+from tests.gpu_helpers import (RECALL_MIN, check_attention, gpu_decode, np_,
+                               oracle_attention_on, recall, say)
 from tests.helpers import run_oracle
 from workloads import BENCH_WORKLOAD, CONFIGS, make_batch, oracle_arrays, row_positions
 
@@ -62,21 +63,39 @@ def test_full_size_integer_mode(name):
     check_attention(res["out"][rows], res["lse"][rows], orc["out"], orc["lse"])
 
 
-def test_full_size_gaussian_bench_shape():
-    wl = CONFIGS[BENCH_WORKLOAD]
-    say(f"full size {BENCH_WORKLOAD}: Gaussian mode, seed {wl.seed}")
+# Gaussian mode: the GPU's fp32 scores may order near-equal positions
+# differently from the binary64 oracle, so the selection is held to a recall
+# bound, and every checked row's attention is compared with the oracle's
+# attention over the positions the GPU itself selected.
+GAUSS = [(BENCH_WORKLOAD, None), ("decode_32x32k", 8), ("ragged_64_1k_128k", 8),
+         ("prefill_4096_on_61440", 6)]
+
+
+@pytest.mark.parametrize("name,n_rows", GAUSS, ids=[g[0] for g in GAUSS])
+def test_full_size_gaussian(name, n_rows):
+    wl = CONFIGS[name]
+    say(f"full size {name}: Gaussian mode, seed {wl.seed}")
     batch = make_batch(wl, device="cuda", seed=wl.seed, mode="gauss")
     res = gpu_decode(batch)
     _check_every_row(batch, res)
-    rows = list(range(batch.rows))
-    orc = run_oracle(oracle_arrays(batch, rows=rows), keep_scores=False)
-    gi = np_(res["indices"])
+    if n_rows is None:
+        rows = list(range(batch.rows))
+    else:
+        rows = set(_sample_rows(batch, wl.seed))
+        pick = np.random.default_rng(wl.seed + 1).permutation(batch.rows)
+        rows = sorted(rows | set(int(x) for x in pick[:max(0, n_rows - len(rows))]))
+    say(f"  oracle rows {rows}")
+    arr = oracle_arrays(batch, rows=rows)
+    orc = run_oracle(arr, keep_scores=False)
+    gi = np_(res["indices"])[rows]
+    gc = np_(res["counts"])[rows]
+    assert (gc == orc["counts"]).all()
     rec, worst = recall(gi, orc["indices"], orc["counts"])
     say(f"  recall {rec:.6f} (worst row {worst:.6f})")
     assert rec >= RECALL_MIN
-    same = [i for i in rows if (gi[i] == orc["indices"][i]).all()]
-    if same:
-        check_attention(res["out"][same], res["lse"][same], orc["out"][same], orc["lse"][same])
+    o_ref, l_ref = oracle_attention_on(arr, gi, gc)
+    e_max, e_mean = check_attention(res["out"][rows], res["lse"][rows], o_ref, l_ref)
+    say(f"  attention on the GPU's own indices: max {e_max:.3g} mean {e_mean:.3g}")
 
 
 def test_full_size_mxfp8_indexer_bench_shape():

@@ -12,9 +12,10 @@ import pytest
 import torch
 
 import oracle
+from indexer_top_sparse_score_amd import binding as B
 from tests.gpu_helpers import (RECALL_MIN, check_attention, check_scores_exact, gpu_attn,
-                               gpu_decode, gpu_scores, gpu_topk, np_, recall, say, score_bound,
-                               score_ld)
+                               gpu_decode, gpu_scores, gpu_topk, np_, oracle_attention_on,
+                               recall, say, score_bound, score_ld)
 from tests.helpers import run_oracle
 from workloads import CONFIGS, make_batch, oracle_arrays, row_positions, small_workload
 
@@ -208,6 +209,9 @@ def test_decode_step_gaussian_mode():
     same = [i for i in range(batch.rows) if (gi[i] == orc["indices"][i]).all()]
     assert len(same) >= batch.rows - 1
     check_attention(res["out"], res["lse"], orc["out"], orc["lse"], rows=same)
+    # every row, against the oracle's attention over the GPU's own selection
+    o_ref, l_ref = oracle_attention_on(arr, gi, np_(res["counts"]))
+    check_attention(res["out"], res["lse"], o_ref, l_ref)
     # every selection is valid: ascending, distinct, inside the history, -1 padded
     for i, (_, p) in enumerate(row_positions(batch)):
         n = int(orc["counts"][i])
@@ -268,3 +272,30 @@ def test_tiny_workload_matches_golden_fixture():
     res = gpu_decode(batch)
     assert np_(res["indices"])[0].tolist() == want["indices"]
     assert int(np_(res["counts"])[0]) == want["count"]
+
+
+def test_decode_step_timed_matches_decode_step():
+    # the timed entry launches the same kernels: identical results, and the
+    # eight events it stamps give ordered, non-negative stage times
+    batch = _batch("mla_int", seed=29)
+    prob = B.problem_for_batch(batch)
+    ref = gpu_decode(batch)
+    wl = batch.wl
+    out = torch.full_like(ref["out"], float("nan"))
+    lse = torch.full_like(ref["lse"], float("nan"))
+    idx = torch.full_like(ref["indices"], -7)
+    cnt = torch.full_like(ref["counts"], -7)
+    ws = B.workspace(prob, B.DSA_OP_DECODE_STEP)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    v = batch.v if batch.v is not None else batch.kv
+    B.dsa_decode_step_timed(prob, batch.qI, batch.w, batch.kI, batch.q, batch.kv, v, out, ws, ev,
+                            lse=lse, indices=idx, counts=cnt)
+    torch.cuda.synchronize()
+    assert B.device_errors(ws) == 0
+    assert torch.equal(idx, ref["indices"]) and torch.equal(cnt, ref["counts"])
+    assert torch.equal(out.view(torch.int16), ref["out"].view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), ref["lse"].view(torch.int32))
+    t = [ev[i].elapsed_time(ev[i + 1]) for i in range(7)]
+    say(f"stage times and gaps (ms) {t}")
+    assert all(x >= 0 for x in t) and t[0] > 0 and t[2] > 0 and t[4] > 0
+    assert wl.K == idx.shape[1]
