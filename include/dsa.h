@@ -207,7 +207,9 @@ DSA_API int dsa_topk(const dsa_problem* p, const float* scores, int64_t ld_score
  *   k        paged cache of bf16 rows of D_qk elements
  *   v        paged cache of bf16 rows whose first D_v elements are V; pass
  *            the k descriptor again for the latent layout (V = the leading
- *            D_v columns of each K row)
+ *            D_v columns of each K row; the cache, num_blocks * block
+ *            stride bytes, may then span at most 64 GiB, else
+ *            DSA_ERR_UNSUPPORTED)
  *   indices  int32 [num_rows][K]
  *   out      bf16 [num_rows][H_q][D_v]; lse float32 [num_rows][H_q] or NULL
  * Products are bf16 x bf16 with float32 accumulation; softmax in float32.

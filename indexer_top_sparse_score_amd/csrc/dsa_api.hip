@@ -163,6 +163,10 @@ int check_attn_args(const dsa_problem* p, const uint16_t* q, const dsa_paged& k,
   if (!aligned(q, 16) || !aligned(out, 16) || (lse && !aligned(lse, 4))) return DSA_ERR_INVALID;
   if ((st = check_paged(k, 2 * (int64_t)p->D_qk)) != DSA_OK) return st;
   if ((st = check_paged(v, 2 * (int64_t)p->D_v)) != DSA_OK) return st;
+  // the latent kernel keeps each gathered row's offset in 32 bits of 16-byte
+  // units: its cache spans at most 64 GiB
+  if (is_latent(k, v) && (int64_t)k.num_blocks * k.block_stride > (int64_t(1) << 36))
+    return DSA_ERR_UNSUPPORTED;
   return DSA_OK;
 }
 
@@ -221,7 +225,7 @@ int decode_run(const dsa_problem* p, const uint8_t* qI, const float* w, dsa_page
   float* scores = reinterpret_cast<float*>(base + d.scores_off);
   const int64_t ld = slab_ld(p);
   const Summary sum = needs_summary(p) ? summary_carve(base + d.sum_off, d.rp)
-                                       : Summary{nullptr, nullptr};
+                                       : Summary{nullptr, nullptr, nullptr};
   const bool use_rowoff = attn_uses_rowoff(p->D_qk, p->D_v, is_latent(k, v));
   int64_t* roff = reinterpret_cast<int64_t*>(base + d.roff_off);
 
@@ -396,7 +400,7 @@ int dsa_indexer_scores(const dsa_problem* p, const uint8_t* qI, const float* w, 
   a.row_begin = 0;
   a.num_rows = p->num_rows;
   a.max_len = (int32_t)max_len(p);
-  a.sum = Summary{nullptr, nullptr};
+  a.sum = Summary{nullptr, nullptr, nullptr};
   a.topk_K = 0;
   return status_of(launch_indexer_scores(a, static_cast<hipStream_t>(stream)));
 }
@@ -424,7 +428,7 @@ int dsa_topk(const dsa_problem* p, const float* scores, int64_t ld_scores, int32
   a.num_rows = p->num_rows;
   a.max_len = (int32_t)max_len(p);
   a.sum = needs_summary(p) ? summary_carve(static_cast<char*>(ws) + kHeader, p->num_rows)
-                           : Summary{nullptr, nullptr};
+                           : Summary{nullptr, nullptr, nullptr};
   a.prep = a.sum.key != nullptr;
   a.vec = aligned(scores, 16) && ld_scores % 4 == 0;
   a.rowoff = nullptr;

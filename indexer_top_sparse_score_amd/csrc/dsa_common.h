@@ -153,14 +153,15 @@ __device__ __forceinline__ int lane_prefix(uint64_t mask) {
 // ------------------------------------------------------ Top-K summaries
 // A row of more than 16384 and at most 131072 slots (with K <= 2048) gets a
 // summary from the indexer's epilogue, or from the standalone summary pass:
-// its slots are cut into segments of G = sum_seg(L) slots (16, 32 or 64;
-// at most 2048 segments), and for each segment the kSumM largest keys are
-// kept with their offsets in the segment, in slot order; key 0 fills the
-// entries of a segment shorter than kSumM.  The selection (topk_select.h)
-// works from it.  With K <= 2048 a segment holds on average at most two of
-// the row's K largest keys (one at the segment counts' upper ends, 32768,
-// 65536 and 131072 slots), so eight per segment rarely miss one; when they
-// might, the selection re-reads that segment's scores.
+// its slots are cut into segments of G = sum_seg(L) slots (16, 32 or 64:
+// the smallest that makes at most 2048 segments), and for each segment
+//  - the kSumM largest keys with their offsets in the segment, in slot
+//    order (key 0 fills the entries of a segment shorter than kSumM), and
+//  - the largest key not among them (the segment's next key; 0 if none).
+// The selection (topk_select.h) works from it.  With K <= 2048 a segment
+// holds on average G K / L <= 2 of the row's K largest keys, so its next key
+// seldom reaches the selection threshold; when it does, the selection
+// re-reads that segment's scores.
 constexpr int kSumM = 8;                        // entries per segment
 constexpr int kSumSegMax = 2048;                // segments per row, at most
 constexpr int kSumEntries = kSumM * kSumSegMax; // 16384 per row
@@ -176,11 +177,13 @@ __host__ __device__ inline bool sum_row(int L, int K) {
   return K <= kSumMaxK && L >= kSumMinLen && L <= kSumMaxLen;
 }
 
-// The summaries of a pass of rows: keys [rows][kSumEntries] (uint32) and
-// offsets [rows][kSumEntries] (uint8), carved from a workspace.
+// The summaries of a pass of rows, carved from a workspace: keys
+// [rows][kSumEntries] (uint32), offsets [rows][kSumEntries] (uint8), next
+// keys [rows][kSumSegMax] (uint32).
 struct Summary {
   uint32_t* key;
   uint8_t* off;
+  uint32_t* next;
 };
 size_t summary_bytes(int rows);
 Summary summary_carve(void* base, int rows);
@@ -203,67 +206,65 @@ __device__ __forceinline__ uint32_t group_max_u32(uint32_t x, int G) {
   return x;
 }
 
-// Writes the summary entries of a wave's 128 slots w0 .. w0 + 127 (w0 a
-// multiple of 128, w0 < S) of a row of S slots: ka is the key of slot
-// w0 + lane, kb of slot w0 + 64 + lane (0 past the row; keys of slots are
-// at least 1).  G = sum_seg(S) lanes form a segment, within ka and within kb.
-// Up to kSumM rounds each take one largest remaining key per segment (the
-// lowest lane holding it; the order among equal keys does not matter: a
-// segment whose kSumM-th key ties the threshold is re-read whole); the taken
-// keys are then written in slot order.
-__device__ __forceinline__ void summary_write(uint32_t ka, uint32_t kb, int w0, int S, int G,
-                                              uint32_t* skey, uint8_t* soff) {
+// The summary of one half of a wave's 128 slots (64 slots, one per lane),
+// as this lane's share: whether its key is taken, its rank among the taken
+// keys of its segment, how many were taken there, and the segment's next
+// key.  k is the key of the lane's slot (0 past the row; keys of slots are
+// at least 1); G = sum_seg(S) lanes form a segment.  Up to kSumM rounds
+// each take one largest remaining key per segment (the lowest lane holding
+// it; the order among equal keys does not matter: a segment whose next key
+// ties the threshold is re-read whole).  Registers only: it can run while
+// the wave still waits for its other loads.
+struct HalfSummary {
+  bool taken;
+  int rank, count;
+  uint32_t next;
+};
+__device__ __forceinline__ HalfSummary summary_half(uint32_t k, int G) {
   const int lane = (int)(threadIdx.x & 63);
-  bool ta = false, tb = false;
-  uint32_t va = ka, vb = kb;
   const int base = lane & ~(G - 1);
   const uint64_t gmask = G == 64 ? ~0ull : ((1ull << G) - 1ull) << base;
+  bool t = false;
+  uint32_t v = k;
 #pragma unroll
   for (int i = 0; i < kSumM; ++i) {
-    const uint32_t Ma = group_max_u32(va, G), Mb = group_max_u32(vb, G);
-    if (__ballot(Ma != 0u || Mb != 0u) == 0) break;  // nothing left in any segment
-    const uint64_t ha = __ballot(va == Ma && Ma != 0u) & gmask;
-    const uint64_t hb = __ballot(vb == Mb && Mb != 0u) & gmask;
-    if (ha != 0 && lane == (int)__builtin_ctzll(ha)) {
-      ta = true;
-      va = 0u;
-    }
-    if (hb != 0 && lane == (int)__builtin_ctzll(hb)) {
-      tb = true;
-      vb = 0u;
+    const uint32_t M = group_max_u32(v, G);
+    if (__ballot(M != 0u) == 0) break;  // nothing left in any segment
+    const uint64_t h = __ballot(v == M && M != 0u) & gmask;
+    if (h != 0 && lane == (int)__builtin_ctzll(h)) {
+      t = true;
+      v = 0u;
     }
   }
-  const uint64_t ma = __ballot(ta) & gmask, mb = __ballot(tb) & gmask;
-  const uint64_t below = (1ull << lane) - 1ull;
-  const int ra = __popcll(ma & below), rb = __popcll(mb & below);
-  const int ca = __popcll(ma), cb = __popcll(mb);
-  const int i = lane - base;  // offset in the segment
-  if (w0 + base < S) {
-    const int sg = (w0 + base) / G;
-    uint32_t* kd = skey + sg * kSumM;
-    uint8_t* od = soff + sg * kSumM;
-    if (ta) {
-      kd[ra] = ka;
-      od[ra] = (uint8_t)i;
-    }
-    if (i >= ca && i < kSumM) {
-      kd[i] = 0u;
-      od[i] = 0;
-    }
+  HalfSummary hs;
+  hs.next = group_max_u32(v, G);
+  const uint64_t m = __ballot(t) & gmask;
+  hs.taken = t;
+  hs.rank = __popcll(m & ((1ull << lane) - 1ull));
+  hs.count = __popcll(m);
+  return hs;
+}
+
+// Writes a half's summary: slots h0 .. h0 + 63 (h0 a multiple of 64, the
+// half's first slot) of row `row` of a row of S slots, this lane's key k.
+// The taken keys go out in slot order, then zero entries up to kSumM.
+__device__ __forceinline__ void summary_store(const HalfSummary& hs, uint32_t k, int h0, int S,
+                                              int G, const Summary& sum, int64_t row) {
+  const int lane = (int)(threadIdx.x & 63);
+  const int base = lane & ~(G - 1), i = lane - base;
+  if (h0 + base >= S) return;
+  const int sg = (h0 + base) / G;
+  uint32_t* kd = sum.key + row * kSumEntries + sg * kSumM;
+  uint8_t* od = sum.off + row * kSumEntries + sg * kSumM;
+  if (hs.taken) {
+    kd[hs.rank] = k;
+    od[hs.rank] = (uint8_t)i;
   }
-  if (w0 + 64 + base < S) {
-    const int sg = (w0 + 64 + base) / G;
-    uint32_t* kd = skey + sg * kSumM;
-    uint8_t* od = soff + sg * kSumM;
-    if (tb) {
-      kd[rb] = kb;
-      od[rb] = (uint8_t)i;
-    }
-    if (i >= cb && i < kSumM) {
-      kd[i] = 0u;
-      od[i] = 0;
-    }
+  if (i >= hs.count && i < kSumM) {
+    kd[i] = 0u;
+    od[i] = 0;
   }
+  if (i == 0) sum.next[row * kSumSegMax + sg] = hs.next;
 }
 
 struct IndexerLaunch {

@@ -255,10 +255,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
   // The wave's scores are collected in LDS and written with a few
   // full-width stores at the end, not one narrow store per sub-tile.
   float* my_sc = sc_lds[wave];
+  // The Top-K's summary of this wave's slots (the kSumM largest keys of each
+  // segment, with their offsets, and the segment's next key): the first
+  // half's is worked out as soon as its four sub-tiles are scored, while
+  // the second half's keys are still loading; both are stored at the end.
+  static_assert(kSpan == 128 && kSubPerWave == 8, "a wave's summary covers two halves of 64");
+  const bool summ = a.sum.key && w0 < S && sum_row(S, a.topk_K);  // wave-uniform
+  const int G = sum_seg(S);
+  uint32_t ka = 0u;
+  HalfSummary ha{};
 
   bool bad_page = false;
 #pragma unroll
   for (int j = 0; j < kSubPerWave; ++j) {
+    if (j == kSubPerWave / 2 && summ) {
+      // LDS accesses of one wave complete in order; the fence keeps the
+      // compiler from moving the reads above the writes of other lanes
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      ka = w0 + lane < S ? score_key(my_sc[lane]) : 0u;
+      ha = summary_half(ka, G);
+    }
     float part = 0.0f;
     // B scale: byte g of the key row's scale word (127, i.e. x1, for unused
     // groups and for E4M3)
@@ -296,14 +312,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     const int i = 64 * h + lane;
     if (w0 + i < S) out[w0 + i] = my_sc[i];
   }
-  // The Top-K's summary of this wave's slots: the kSumM largest keys of each
-  // of their segments, with their offsets
-  static_assert(kSpan == 128, "a wave's summary covers 128 slots");
-  if (a.sum.key && w0 < S && sum_row(S, a.topk_K)) {  // wave-uniform
-    const uint32_t ka = w0 + lane < S ? score_key(my_sc[lane]) : 0u;
+  if (summ) {
     const uint32_t kb = w0 + 64 + lane < S ? score_key(my_sc[64 + lane]) : 0u;
-    const int64_t ro = (int64_t)(r - a.row_begin) * kSumEntries;
-    summary_write(ka, kb, w0, S, sum_seg(S), a.sum.key + ro, a.sum.off + ro);
+    const HalfSummary hb = summary_half(kb, G);
+    summary_store(ha, ka, w0, S, G, a.sum, r - a.row_begin);
+    summary_store(hb, kb, w0 + 64, S, G, a.sum, r - a.row_begin);
   }
   if (__builtin_amdgcn_ballot_w64(bad_page || bad_blk) && lane == 0) report(a.err, DSA_DEVERR_BLOCK);
   if (CAND && __builtin_amdgcn_ballot_w64(bad_pos) && lane == 0) report(a.err, DSA_DEVERR_ROW);

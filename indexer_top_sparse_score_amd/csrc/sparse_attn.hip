@@ -47,6 +47,9 @@
 #ifndef DSA_ATTN_TARGET_WGS
 #define DSA_ATTN_TARGET_WGS 256
 #endif
+#ifndef DSA_ATTN_MERGE_TILES
+#define DSA_ATTN_MERGE_TILES 4  // 16-dim tiles per merge workgroup (32 threads each)
+#endif
 
 namespace dsa {
 namespace {
@@ -534,7 +537,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
   static_assert(NBUF >= 2 && NBUF <= 4, "vmcnt cases");
   static_assert(kNW * 16 * (2 * kDv + 16) <= NBUF * kTileBytes, "epilogue staging fits the tiles");
   __shared__ __attribute__((aligned(16))) uint8_t tile[NBUF][kTileBytes];
-  __shared__ int64_t koff[kMaxChunkLat];
+  // each slot's row offset in the cache in 16-byte units (the front end
+  // keeps the cache below 64 GiB for this kernel), ~0u for an absent row
+  __shared__ uint32_t koff[kMaxChunkLat];
 
   int unit, hg;
   if (!decode_wg(g, unit, hg)) return;
@@ -556,7 +561,10 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
   //      soon as it is back.
   if (a.rowoff) {
     const int64_t* ro = a.rowoff + (int64_t)row_local * a.K + slot0;
-    for (int i = tid; i < nsb * kSB; i += NT) koff[i] = i < n_slots ? ro[i] : -1;
+    for (int i = tid; i < nsb * kSB; i += NT) {
+      const int64_t o = i < n_slots ? ro[i] : -1;
+      koff[i] = o >= 0 ? (uint32_t)(o >> 4) : ~0u;
+    }
   } else {
     int b = 0, p = -1;
     if (!resolve_row(a.rows, r, b, p)) {
@@ -579,7 +587,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
           report(a.err, DSA_DEVERR_INDEX);
         }
       }
-      koff[i] = ko;
+      koff[i] = ko >= 0 ? (uint32_t)(ko >> 4) : ~0u;
     }
   }
 
@@ -599,8 +607,8 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
       const int sl = 64 * (wave * kDmaPerWave + t) + lane;
       const int row = sl / kPieces;
       const int piece = (sl - row * kPieces) ^ (row & 7);
-      const int64_t off = koff[sb * kSB + row];
-      src[t] = kbase + (off >= 0 ? off : 0) + 16 * piece;
+      const uint32_t o16 = koff[sb * kSB + row];
+      src[t] = kbase + (o16 != ~0u ? (int64_t)o16 << 4 : 0) + 16 * piece;
     }
     const uint32_t lds0 =
         __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(buf + 1024 * wave * kDmaPerWave));
@@ -613,7 +621,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
     for (int t = 0; t < kDmaPerWave; ++t) {
       const int i = wave * kDmaPerWave + t;
       const int sl = 64 * i + lane;
-      if (koff[sb * kSB + sl / kPieces] < 0)
+      if (koff[sb * kSB + sl / kPieces] == ~0u)
         *reinterpret_cast<uint4*>(buf + 16 * sl) = uint4{0u, 0u, 0u, 0u};
     }
   };
@@ -683,7 +691,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
     for (int sb = 0; sb < nsb; ++sb) {
       wait_vm<kDmaPerWave>(min(nsb - 1 - sb, NBUF - 2));
       const uint32_t valid =
-          (uint32_t)__ballot(lane < kSB && koff[sb * kSB + (lane & (kSB - 1))] >= 0);
+          (uint32_t)__ballot(lane < kSB && koff[sb * kSB + (lane & (kSB - 1))] != ~0u);
       if (valid != 0xFFFFFFFFu) zero_absent(sb);
       // every wave's DMAs of sb have landed, and every wave is done with the
       // buffer the next DMA overwrites (last read in sub-block sb-1)
@@ -820,14 +828,15 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
 
 // Merges the chunks of each (row, head) by log-sum-exp: with M the largest
 // chunk max, chunk c weighs g_c = 2^(max_c - M), and out = sum_c g_c O_c /
-// sum_c g_c sum_c.  A workgroup takes one row, one block of 16 heads and up
-// to 8 of its 16-dim tiles; thread t holds 8 consecutive floats of that
-// slice of every chunk's partial (tile t / 32, head (t / 2) % 16, dims
-// 8 (t % 2) .. +7), loaded kBatch chunks per round trip.
-template <int DV>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
+// sum_c g_c sum_c.  A workgroup of 32 MTW threads takes one row, one block
+// of 16 heads and MTW of its 16-dim tiles; thread t holds 8 consecutive
+// floats of that slice of every chunk's partial (tile t / 32, head
+// (t / 2) % 16, dims 8 (t % 2) .. +7), loaded kBatch chunks per round trip.
+// Small workgroups make many of them: the merge is a streaming read.
+template <int DV, int MTW>
+__global__ __launch_bounds__(32 * MTW) void attn_combine_kernel(AttnLaunch a) {
   constexpr int MT = DV / 16;
-  constexpr int MTW = MT < 8 ? MT : 8;  // tiles per workgroup
+  static_assert(MT % MTW == 0, "tiles per workgroup");
   constexpr int kBatch = 16;
   const int row_local = (int)blockIdx.x;
   const int r = a.row_begin + row_local;
@@ -935,9 +944,10 @@ hipError_t launch_t(const AttnLaunch& a, hipStream_t s, StageEvents ev, StageEve
     if (merge.stop && (e = hipEventRecord(merge.stop, s)) != hipSuccess) return e;
     return hipSuccess;
   }
-  constexpr int MT = DV / 16, MTW = MT < 8 ? MT : 8;
-  return launch_kernel(attn_combine_kernel<DV>, dim3(a.num_rows, (a.H_q + 15) / 16, MT / MTW),
-                       dim3(256), s, merge.start, merge.stop, a);
+  constexpr int MT = DV / 16, MTW = MT < DSA_ATTN_MERGE_TILES ? MT : DSA_ATTN_MERGE_TILES;
+  return launch_kernel(attn_combine_kernel<DV, MTW>,
+                       dim3(a.num_rows, (a.H_q + 15) / 16, MT / MTW), dim3(32 * MTW), s,
+                       merge.start, merge.stop, a);
 }
 
 }  // namespace

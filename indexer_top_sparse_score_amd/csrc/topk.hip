@@ -32,8 +32,10 @@ __global__ __launch_bounds__(256) void topk_summary_kernel(TopkLaunch a) {
   const float* sc = a.scores + (int64_t)r_local * a.ld;
   const uint32_t ka = w0 + lane < L ? score_key(sc[w0 + lane]) : 0u;
   const uint32_t kb = w0 + 64 + lane < L ? score_key(sc[w0 + 64 + lane]) : 0u;
-  const int64_t ro = (int64_t)r_local * kSumEntries;
-  summary_write(ka, kb, w0, L, sum_seg(L), a.sum.key + ro, a.sum.off + ro);
+  const int G = sum_seg(L);
+  const HalfSummary ha = summary_half(ka, G), hb = summary_half(kb, G);
+  summary_store(ha, ka, w0, L, G, a.sum, r_local);
+  summary_store(hb, kb, w0 + 64, L, G, a.sum, r_local);
 }
 
 // One row per workgroup.  The first round trip brings the row's length, its
@@ -48,7 +50,9 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(1, kNT >= 1
   const RowIssue ri = row_issue(a.rows, r);
   sel::Regs<kNT> regs;
   const int64_t ro = (int64_t)r_local * kSumEntries;
-  if (a.sum.key) sel::load_summary<kNT>(a.sum.key + ro, a.sum.off + ro, regs);
+  if (a.sum.key)
+    sel::load_summary<kNT>(a.sum.key + ro, a.sum.off + ro, a.sum.next + (int64_t)r_local * kSumSegMax,
+                           regs);
   const int32_t* bt = a.rows.block_table + (int64_t)(ri.b_ok ? ri.b : 0) * a.rows.max_blocks;
   constexpr int kBtPer = kBtCache / kNT;
   int32_t btv[kBtPer];
@@ -85,17 +89,25 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(1, kNT >= 1
 
 }  // namespace
 
+namespace {
+size_t round_up256(size_t x) { return (x + 255) & ~size_t(255); }
+}  // namespace
+
 size_t summary_bytes(int rows) {
   if (rows <= 0) return 0;
-  const size_t keys = ((size_t)rows * kSumEntries * sizeof(uint32_t) + 255) & ~size_t(255);
-  return keys + (((size_t)rows * kSumEntries + 255) & ~size_t(255));
+  return round_up256((size_t)rows * kSumEntries * sizeof(uint32_t)) +
+         round_up256((size_t)rows * kSumEntries) +
+         round_up256((size_t)rows * kSumSegMax * sizeof(uint32_t));
 }
 
 Summary summary_carve(void* base, int rows) {
   Summary m;
-  m.key = static_cast<uint32_t*>(base);
-  m.off = static_cast<uint8_t*>(base) +
-          (((size_t)rows * kSumEntries * sizeof(uint32_t) + 255) & ~size_t(255));
+  uint8_t* p = static_cast<uint8_t*>(base);
+  m.key = reinterpret_cast<uint32_t*>(p);
+  p += round_up256((size_t)rows * kSumEntries * sizeof(uint32_t));
+  m.off = p;
+  p += round_up256((size_t)rows * kSumEntries);
+  m.next = reinterpret_cast<uint32_t*>(p);
   return m;
 }
 

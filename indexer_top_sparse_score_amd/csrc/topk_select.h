@@ -10,22 +10,24 @@
 //  - at most K slots: keep every slot;
 //  - at most kRegKeys slots: select on all of its keys, held in registers;
 //  - a summary row (sum_row: more than 16384 and at most kSumMaxLen slots,
-//    K <= kSumMaxK): select on the row's summary, the kSumM largest keys of
-//    each segment of G slots with their offsets, which the indexer's
-//    epilogue (or the standalone summary pass) wrote:
+//    K <= kSumMaxK): select on the row's summary -- the kSumM largest keys
+//    of each segment of G slots with their offsets, and the segment's next
+//    key -- which the indexer's epilogue (or the standalone summary pass)
+//    wrote:
 //      1. T1 = the K-th largest summary key.  The summary keys sit at distinct
 //         slots, so the row holds at least K keys >= T1.
-//      2. A segment whose smallest summary key is >= T1 (and that has more
-//         than kSumM slots) may hide further keys >= T1: it is saturated.
-//         Every other segment keeps all of its keys >= T1 in the summary
-//         (they exceed its kSumM-th largest key).
+//      2. A segment whose next key is >= T1 hides further keys >= T1: it is
+//         saturated.  Every other segment keeps all of its keys >= T1 in the
+//         summary.
 //      3. Nothing saturated (the usual case): the summary's keys >= T1 are
 //         exactly the row's, T = T1, and the summary itself is emitted.
 //      4. Otherwise the candidates -- summary keys >= T1 of unsaturated
-//         segments and the saturated segments' keys >= T1, re-read from the
-//         score row -- are exactly the row's keys >= T1.  They are staged in
-//         LDS in slot order, T is their K-th largest, and they are emitted.
-//         Too many of them for the staging falls back to the streamed route.
+//         segments and the saturated segments' keys >= T1, which the waves
+//         re-read from the score row, one segment per wave at a time -- are
+//         exactly the row's keys >= T1.  They are staged in LDS in slot
+//         order, T is their K-th largest, and they are emitted.  Too many of
+//         them (or too many saturated segments) falls back to the streamed
+//         route.
 //  - otherwise (streamed): histogram passes over the row's keys read from
 //    memory narrow the range to T, then one pass emits.
 //
@@ -42,6 +44,8 @@
 // instruction fetch than it saves in issue.  Loops over LDS stay loops.
 #pragma once
 
+#include <type_traits>
+
 #include "dsa_common.h"
 
 namespace dsa {
@@ -50,9 +54,10 @@ namespace sel {
 constexpr int kBinBits = 11;
 constexpr int kBins = 1 << kBinBits;   // 2048
 constexpr int kSmall = 64;             // bin size ranked directly by one wave
-constexpr int kRegKeys = 16384;        // keys held in registers by a workgroup (both routes)
+constexpr int kRegKeys = kSumEntries;  // keys held in registers by a workgroup (both routes)
 constexpr int kCandMax = 8192;         // candidates staged in LDS (saturated summary rows)
 constexpr int kStageK = 2048;          // largest K whose selection is staged in LDS
+constexpr int kSatMax = 512;           // saturated segments re-read by the waves
 
 // LDS of one selection.  hist doubles as the histogram of every pass.
 template <int NT>
@@ -62,7 +67,10 @@ struct Smem {
   uint32_t ckey[kCandMax];
   int32_t cpos[kCandMax];
   int32_t pos[kStageK];  // kept slot -> position
-  uint32_t buf[kSmall];
+  uint32_t sat_seg[kSatMax];  // saturated segments, in slot order
+  uint32_t sat_cnt[kSatMax];  // their keys >= T1
+  uint32_t sat_off[kSatMax];  // their first candidate
+  alignas(16) uint32_t buf[kSmall];
   uint32_t res[4];
   alignas(16) uint32_t wsum[2 * kWaves];
   alignas(16) uint32_t red[3 * (kWaves < 4 ? 4 : kWaves)];
@@ -154,13 +162,17 @@ __device__ __forceinline__ int bitlen32(uint32_t x) { return x ? 32 - __clz(x) :
 // every thread past a barrier.
 template <int NT, class Visit>
 __device__ __forceinline__ uint32_t select_kth(Visit visit, uint32_t lo, uint32_t hi,
-                                               uint32_t& need, Smem<NT>& s, uint32_t& ph) {
+                                               uint32_t& need, Smem<NT>& s, uint32_t& ph,
+                                               bool zeroed = false) {
   constexpr int BPT = kBins / NT;  // bins per thread of the scan, from the top
   const int tid = threadIdx.x;
   while (lo < hi) {
     const int shift = max(0, bitlen32(hi - lo) - kBinBits);
-    for (int i = tid; i < kBins; i += NT) s.hist[i] = 0;
-    __syncthreads();
+    if (!zeroed) {  // (the caller may have cleared hist before a barrier of its own)
+      for (int i = tid; i < kBins; i += NT) s.hist[i] = 0;
+      __syncthreads();
+    }
+    zeroed = false;
     visit([&](uint32_t k) {
       if (k >= lo && k <= hi) atomicAdd(&s.hist[(k - lo) >> shift], 1u);
     });
@@ -200,10 +212,22 @@ __device__ __forceinline__ uint32_t select_kth(Visit visit, uint32_t lo, uint32_
         const uint32_t m = s.res[2];
         const uint32_t x = (uint32_t)tid < m ? s.buf[tid] : 0u;
         uint32_t gt = 0, ge = 0;
-        for (uint32_t i = 0; i < m; ++i) {
-          const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, (int)i);
-          gt += y > x ? 1u : 0u;
-          ge += y >= x ? 1u : 0u;
+        // every lane reads the bin's keys, sixteen at a time (LDS
+        // broadcasts, issued together before their compares)
+        for (uint32_t h = 0; h < m; h += 16) {
+          uint4 y[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) y[i] = *reinterpret_cast<const uint4*>(&s.buf[h + 4 * i]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t v[4] = {y[i].x, y[i].y, y[i].z, y[i].w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const bool in = h + (uint32_t)(4 * i + u) < m;
+              gt += in && v[u] > x ? 1u : 0u;
+              ge += in && v[u] >= x ? 1u : 0u;
+            }
+          }
         }
         if ((uint32_t)tid < m && gt < need && need <= ge) {  // equal keys write equal values
           s.res[0] = x;
@@ -305,32 +329,72 @@ struct Regs {
   static constexpr int P = kRegKeys / NT;
   static constexpr int SPT = P / kSumM;
   static_assert(SPT * kSumM == P && SPT * NT == kSumSegMax, "summary segments per thread");
+  static_assert(P <= 64, "one bit per key in a 64-bit mask");
+  using Mask = typename std::conditional<(P > 32), uint64_t, uint32_t>::type;
   uint32_t k[P];
   uint32_t w[2 * SPT];
-  __device__ __forceinline__ int slot(int j, int G) const {  // j a constant once unrolled
+  uint32_t nx[SPT];  // next key of each segment
+  // slot of entry j
+  __device__ __forceinline__ int slot(int j, int G) const {
     if (G == 0) return P * (int)threadIdx.x + j;
-    const int q = j / kSumM, e = j % kSumM;
-    return ((int)threadIdx.x * SPT + q) * G + (int)((w[2 * q + (e >> 2)] >> (8 * (e & 3))) & 0xFFu);
+    const int q = j / kSumM, e = j % kSumM, wi = 2 * q + (e >> 2);
+    uint32_t word = w[0];
+#pragma unroll
+    for (int i = 1; i < 2 * SPT; ++i) word = i == wi ? w[i] : word;
+    return ((int)threadIdx.x * SPT + q) * G + (int)((word >> (8 * (e & 3))) & 0xFFu);
   }
 };
 
-// Emits the register keys given T and its budget, into s.pos.
+__device__ __forceinline__ uint32_t popc_any(uint32_t m) { return __popc(m); }
+__device__ __forceinline__ uint32_t popc_any(uint64_t m) { return __popcll(m); }
+
+// Emits the register keys given T and the number of keys equal to T to
+// keep (the first ones in slot order), into s.pos: every thread sets one
+// bit per kept key, and after one block scan of the counts writes only
+// those.
 template <int NT>
 __device__ __forceinline__ void regs_emit(const Regs<NT>& r, int G, uint32_t T, uint32_t need_eq,
                                           Smem<NT>& s, uint32_t& ph) {
-  uint32_t gt = 0, eq = 0;
+  using Mask = typename Regs<NT>::Mask;
+  Mask gtm = 0, eqm = 0;
 #pragma unroll
   for (int j = 0; j < Regs<NT>::P; ++j) {
-    gt += r.k[j] > T ? 1u : 0u;
-    eq += r.k[j] == T ? 1u : 0u;
+    gtm |= (Mask)(r.k[j] > T ? 1u : 0u) << j;
+    eqm |= (Mask)(r.k[j] == T ? 1u : 0u) << j;
   }
-  Emit e;
-  e.T = T;
-  e.need_eq = need_eq;
-  emit_begin<NT>(e, gt, eq, s, ph);
+  const uint32_t ngt = popc_any(gtm), neq = popc_any(eqm);
+  uint32_t tot;
+  const uint32_t ex = block_scan<NT>((neq << 16) | ngt, s.wsum, ph, tot);
+  const uint32_t eq_before = ex >> 16;
+  // equal keys this thread keeps, as a difference of two minima (the
+  // conditional-subtract form of it lost its condition in compilation)
+  const uint32_t take = min(eq_before + neq, need_eq) - min(eq_before, need_eq);
+  Mask rest = eqm;
+  for (uint32_t i = 0; i < take; ++i) rest &= rest - 1;  // drop the first `take` equal keys
+  Mask keep = gtm | (eqm & ~rest);
+  uint32_t slot = (ex & 0xFFFFu) + min(eq_before, need_eq);
+  // a loop over the kept keys only, with the offsets copied to scalars first
+  // (indexing the register arrays by a variable would move them to scratch)
+  constexpr int SPT = Regs<NT>::SPT;
+  uint32_t wv[2 * SPT];
 #pragma unroll
-  for (int j = 0; j < Regs<NT>::P; ++j)
-    if (e.keep(r.k[j])) s.pos[e.slot++] = r.slot(j, G);
+  for (int i = 0; i < 2 * SPT; ++i) wv[i] = r.w[i];
+  const int seg0 = (int)threadIdx.x * SPT;
+  while (keep != 0) {
+    const int j = (int)popc_any((keep & (0 - keep)) - 1);  // lowest set bit
+    keep &= keep - 1;
+    int p;
+    if (G == 0) {
+      p = Regs<NT>::P * (int)threadIdx.x + j;
+    } else {
+      const int wi = j >> 2;
+      uint32_t word = wv[0];
+#pragma unroll
+      for (int i = 1; i < 2 * SPT; ++i) word = i == wi ? wv[i] : word;
+      p = (seg0 + (j >> 3)) * G + (int)((word >> (8 * (j & 3))) & 0xFFu);
+    }
+    s.pos[slot++] = p;
+  }
 }
 
 // Streamed: histogram passes over the keys read from memory, then one
@@ -378,61 +442,107 @@ __device__ __forceinline__ void select_streamed(const float* sc, int L, int K, c
   if (K <= kStageK) flush<NT>(o, K, count, s.pos);
 }
 
-// Whether summary segment q of this thread is saturated.
+// Whether summary segment q of this thread is saturated: its next key (the
+// largest outside the summary) is >= T1.
 template <int NT>
 __device__ __forceinline__ bool seg_saturated(const Regs<NT>& r, int q, int L, int G, uint32_t T1) {
-  uint32_t mn = 0xFFFFFFFFu;
-#pragma unroll
-  for (int j = 0; j < kSumM; ++j) mn = min(mn, r.k[q * kSumM + j]);
   const int sg = (int)threadIdx.x * Regs<NT>::SPT + q;
-  return sg * G < L && min(G, L - sg * G) > kSumM && mn >= T1;
+  return sg * G < L && r.nx[q] >= T1;
+}
+
+// Keys of saturated segment sg that are >= T1, visited by one wave in slot
+// order: f(lane mask of the round, key, slot) for rounds of 64 slots.
+template <class F>
+__device__ __forceinline__ void sat_segment_keys(const float* sc, int L, int G, int sg, uint32_t T1,
+                                                 F f) {
+  const int lane = threadIdx.x & 63;
+  const int s0 = sg * G, end = min(L, s0 + G);
+  for (int b = s0; b < end; b += 64) {
+    const int i = b + lane;
+    const bool in = lane < G && i < end;
+    const uint32_t k = in ? score_key(sc[i]) : 0u;
+    const bool hit = in && k >= T1;
+    f(__ballot(hit), hit, k, i);
+  }
 }
 
 // A saturated summary row: candidates in LDS (step 4 above) into s.pos.
-// Returns false when they do not fit.
+// `satm` marks this thread's saturated segments.  Returns false when they
+// do not fit (the block agrees).
 template <int NT>
 __device__ __forceinline__ bool summary_saturated(const float* sc, int L, int G, const Regs<NT>& r,
-                                                  uint32_t T1, uint32_t kmax, int K, Smem<NT>& s,
-                                                  uint32_t& ph) {
-  // per thread, in slot order: summary keys >= T1 of unsaturated segments,
-  // every key >= T1 of saturated ones (re-read)
-  constexpr int kSPT = Regs<NT>::SPT;
-  const int tid = threadIdx.x;
+                                                  uint32_t satm, uint32_t T1, uint32_t kmax, int K,
+                                                  Smem<NT>& s, uint32_t& ph) {
+  constexpr int kSPT = Regs<NT>::SPT, W = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t below = (1ull << lane) - 1ull;
+  // 1. the saturated segments, listed in slot order
+  uint32_t n_sat;
+  const uint32_t sat_before = block_scan<NT>(__popc(satm), s.wsum, ph, n_sat);
+  if (n_sat > (uint32_t)kSatMax) return false;
+  {
+    uint32_t i = sat_before;
+#pragma unroll
+    for (int q = 0; q < kSPT; ++q)
+      if (satm >> q & 1u) s.sat_seg[i++] = (uint32_t)(tid * kSPT + q);
+  }
+  __syncthreads();
+  // 2. each wave counts the keys >= T1 of its share of them
+  for (uint32_t i = wave; i < n_sat; i += W) {
+    uint32_t c = 0;
+    sat_segment_keys(sc, L, G, (int)s.sat_seg[i], T1,
+                     [&](uint64_t m, bool, uint32_t, int) { c += (uint32_t)__popcll(m); });
+    if (lane == 0) s.sat_cnt[i] = c;
+  }
+  __syncthreads();
+  // 3. candidate counts per thread, in slot order, and their offsets
   uint32_t c = 0;
+  {
+    uint32_t i = sat_before;
 #pragma unroll
-  for (int q = 0; q < kSPT; ++q) {
-    const int sg = tid * kSPT + q;
-    if (seg_saturated<NT>(r, q, L, G, T1)) {
-      for (int i = sg * G; i < min(L, sg * G + G); ++i) c += score_key(sc[i]) >= T1 ? 1u : 0u;
-    } else {
+    for (int q = 0; q < kSPT; ++q) {
+      if (satm >> q & 1u) {
+        c += s.sat_cnt[i++];
+      } else {
 #pragma unroll
-      for (int j = 0; j < kSumM; ++j) c += r.k[q * kSumM + j] >= T1 ? 1u : 0u;
+        for (int j = 0; j < kSumM; ++j) c += r.k[q * kSumM + j] >= T1 ? 1u : 0u;
+      }
     }
   }
   uint32_t n_cand;
   uint32_t b = block_scan<NT>(c, s.wsum, ph, n_cand);
   if (n_cand > (uint32_t)kCandMax) return false;
+  {
+    uint32_t i = sat_before;
 #pragma unroll
-  for (int q = 0; q < kSPT; ++q) {
-    const int sg = tid * kSPT + q;
-    if (seg_saturated<NT>(r, q, L, G, T1)) {
-      for (int i = sg * G; i < min(L, sg * G + G); ++i) {
-        const uint32_t k = score_key(sc[i]);
-        if (k >= T1) {
-          s.ckey[b] = k;
-          s.cpos[b] = i;
-          ++b;
-        }
+    for (int q = 0; q < kSPT; ++q) {
+      if (satm >> q & 1u) {
+        s.sat_off[i] = b;
+        b += s.sat_cnt[i++];
+      } else {
+#pragma unroll
+        for (int j = 0; j < kSumM; ++j)
+          if (r.k[q * kSumM + j] >= T1) {
+            s.ckey[b] = r.k[q * kSumM + j];
+            s.cpos[b] = r.slot(q * kSumM + j, G);
+            ++b;
+          }
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kSumM; ++j)
-        if (r.k[q * kSumM + j] >= T1) {
-          s.ckey[b] = r.k[q * kSumM + j];
-          s.cpos[b] = r.slot(q * kSumM + j, G);
-          ++b;
-        }
     }
+  }
+  __syncthreads();
+  // 4. the waves write the saturated segments' candidates at their offsets
+  for (uint32_t i = wave; i < n_sat; i += W) {
+    uint32_t o = s.sat_off[i];
+    sat_segment_keys(sc, L, G, (int)s.sat_seg[i], T1,
+                     [&](uint64_t m, bool hit, uint32_t k, int slot) {
+                       if (hit) {
+                         const uint32_t at = o + (uint32_t)__popcll(m & below);
+                         s.ckey[at] = k;
+                         s.cpos[at] = slot;
+                       }
+                       o += (uint32_t)__popcll(m);
+                     });
   }
   __syncthreads();
   uint32_t need = (uint32_t)K;
@@ -462,7 +572,8 @@ __device__ __forceinline__ bool summary_saturated(const float* sc, int L, int G,
 // row's length is known (the summary area always holds kSumSegMax segments
 // per row; entries of segments past the row are masked once it is).
 template <int NT>
-__device__ __forceinline__ void load_summary(const uint32_t* skey, const uint8_t* soff, Regs<NT>& r) {
+__device__ __forceinline__ void load_summary(const uint32_t* skey, const uint8_t* soff,
+                                             const uint32_t* snext, Regs<NT>& r) {
   constexpr int kSPT = Regs<NT>::SPT;
 #pragma unroll
   for (int q = 0; q < kSPT; ++q) {
@@ -474,6 +585,7 @@ __device__ __forceinline__ void load_summary(const uint32_t* skey, const uint8_t
     r.k[q * 8 + 4] = b.x; r.k[q * 8 + 5] = b.y; r.k[q * 8 + 6] = b.z; r.k[q * 8 + 7] = b.w;
     r.w[2 * q] = c.x;
     r.w[2 * q + 1] = c.y;
+    r.nx[q] = snext[sg];
   }
 }
 
@@ -547,6 +659,7 @@ __device__ __forceinline__ int select_row(const float* sc, bool vec, int L, int 
       kmax = max(kmax, r.k[j]);
       n += r.k[j] != 0u ? 1u : 0u;
     }
+    for (int i = tid; i < kBins; i += NT) s.hist[i] = 0;  // for select_kth's first pass
     block_minmax<NT>(kmin, kmax, n, s.red);
     if (n >= (uint32_t)K) {  // always, for every row that takes these routes
       uint32_t need = (uint32_t)K;
@@ -556,17 +669,15 @@ __device__ __forceinline__ int select_row(const float* sc, bool vec, int L, int 
             for (int j = 0; j < kPer; ++j)
               if (r.k[j] != 0u) f(r.k[j]);
           },
-          kmin, kmax, need, s, ph);
+          kmin, kmax, need, s, ph, true);
       bool done = true;
-      uint32_t n_sat = 0;
+      uint32_t satm = 0;
       if (summ) {
-        uint32_t sat = 0;
 #pragma unroll
-        for (int q = 0; q < kSPT; ++q) sat += seg_saturated<NT>(r, q, L, G, T1) ? 1u : 0u;
-        block_scan<NT>(sat, s.wsum, ph, n_sat);
+        for (int q = 0; q < kSPT; ++q) satm |= (seg_saturated<NT>(r, q, L, G, T1) ? 1u : 0u) << q;
       }
-      if (n_sat > 0)
-        done = summary_saturated<NT>(sc, L, G, r, T1, kmax, K, s, ph);
+      if (__syncthreads_or(satm != 0u))
+        done = summary_saturated<NT>(sc, L, G, r, satm, T1, kmax, K, s, ph);
       else
         regs_emit<NT>(r, G, T1, need, s, ph);
       if (done) {

@@ -133,8 +133,10 @@ def test_candidate_list_rejections():
     assert call_scores(prob(cand_len=FAKE), ld=16384) == B.DSA_ERR_INVALID # no cand
     assert call_scores(prob(**{**cand, "n_cand": 0})) == B.DSA_ERR_INVALID
     assert call_scores(prob(**{**cand, "cand": FAKE + 4}), ld=16384) == B.DSA_ERR_INVALID
-    small = ws_size(prob(**cand), B.DSA_OP_TOPK)
-    assert 0 < small < ws_size(prob(), B.DSA_OP_TOPK)  # 16384 slots, not 131072 positions
+    # sized by slots, not positions: 8192 candidates need no summary, a
+    # 131072-position history does
+    small = ws_size(prob(**{**cand, "n_cand": 8192}), B.DSA_OP_TOPK)
+    assert 0 < small < ws_size(prob(), B.DSA_OP_TOPK)
     assert ws_size(prob(**cand), B.DSA_OP_DECODE_STEP) > 0
 
 
@@ -168,6 +170,13 @@ def test_sparse_attn_rejections():
     need = ws_size(prob(), B.DSA_OP_SPARSE_ATTN)
     assert call(prob(), nbytes=need - 256) == B.DSA_ERR_WORKSPACE
     assert call(prob(num_rows=0)) == B.DSA_OK
+    # a latent cache (v aliases k) may span at most 64 GiB; separate V may not
+    big = paged(row=1152, nb=1 << 20)                                 # 72 GiB
+    assert call(prob(), k=big, v=big) == B.DSA_ERR_UNSUPPORTED
+    sep_v = paged(base=FAKE + (1 << 40), row=1024, nb=1 << 20)
+    assert call(prob(), k=big, v=sep_v, nbytes=0) == B.DSA_ERR_WORKSPACE
+    edge = paged(row=1152, nb=(1 << 36) // (64 * 1152))               # just below 64 GiB
+    assert call(prob(), k=edge, v=edge, nbytes=0) == B.DSA_ERR_WORKSPACE
 
 
 def test_decode_step_rejections():
