@@ -47,6 +47,9 @@
 #ifndef DSA_ATTN_TARGET_WGS
 #define DSA_ATTN_TARGET_WGS 256
 #endif
+#ifndef DSA_ATTN_KSPLIT
+#define DSA_ATTN_KSPLIT 2  // key halves per latent workgroup when rows are split into chunks
+#endif
 #ifndef DSA_ATTN_MERGE_TILES
 #define DSA_ATTN_MERGE_TILES 4  // 16-dim tiles per merge workgroup (32 threads each)
 #endif
@@ -528,14 +531,27 @@ __device__ __forceinline__ void wait_vm(int groups) {
   }
 }
 
-template <int NBUF, int kNW>
+// KSPLIT: the key halves of a workgroup.  With KSPLIT = 2 the kNW waves are
+// kNW / 2 head waves (16 heads each) times two key halves: both halves share
+// every staged sub-block, half 0 takes the even sub-blocks of the chunk and
+// half 1 the odd ones, and at the end half 1 hands its accumulators to half
+// 0 through LDS, which merges them by log-sum-exp.  Twice the waves per
+// staged byte, and the same partial per workgroup.
+template <int NBUF, int kNW, int KSPLIT>
 __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLaunch a, AttnGrid g) {
   using namespace lat;
   constexpr int NT = 64 * kNW;
+  constexpr int kHW = kNW / KSPLIT;  // head waves
   constexpr int kDmaPerWave = kDmaPerSB / kNW;
+  constexpr int kPerStep = KSPLIT * kDmaPerWave;  // DMA instructions per wave per step
+  constexpr int kAhead = NBUF / KSPLIT;           // steps staged at once
   static_assert(kDmaPerSB % kNW == 0, "DMA instructions per wave");
-  static_assert(NBUF >= 2 && NBUF <= 4, "vmcnt cases");
-  static_assert(kNW * 16 * (2 * kDv + 16) <= NBUF * kTileBytes, "epilogue staging fits the tiles");
+  static_assert(KSPLIT == 1 || KSPLIT == 2, "key halves");
+  static_assert(NBUF % KSPLIT == 0 && kAhead >= 2 && (kAhead - 1) * kPerStep <= 63, "vmcnt");
+  // epilogue staging of the head waves, after the merge area (KSPLIT = 2)
+  constexpr int kMergeBytes = KSPLIT == 2 ? kHW * 64 * (kMT * 16 + 8) : 0;
+  static_assert(kMergeBytes + kHW * 16 * (2 * kDv + 16) <= NBUF * kTileBytes,
+                "merge and epilogue staging fit the tiles");
   __shared__ __attribute__((aligned(16))) uint8_t tile[NBUF][kTileBytes];
   // each slot's row offset in the cache in 16-byte units (the front end
   // keeps the cache below 64 GiB for this kernel), ~0u for an absent row
@@ -548,11 +564,15 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
   const int row_local = r - a.row_begin;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hw = wave % kHW, kh = wave / kHW;  // head wave, key half
   const int cidx = lane & 15, grp = lane >> 4;
 
   const int slot0 = chunk * g.chunk;
   const int n_slots = max(0, min(a.K, slot0 + g.chunk) - slot0);
-  const int nsb = (n_slots + kSB - 1) / kSB;
+  // sub-blocks, rounded up to whole steps (a padding sub-block is all
+  // absent rows and adds nothing)
+  const int nsb = (n_slots + kSB * KSPLIT - 1) / (kSB * KSPLIT) * KSPLIT;
+  const int nst = nsb / KSPLIT;
 
   // ---- prologue: every index slot of the chunk -> row byte offset (-1:
   //      absent).  Ready-made when the Top-K wrote them (-1 for a row that
@@ -626,11 +646,15 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
     }
   };
 
-  // the first sub-block requested, then Q^T (this lane's head, 8 dims per
-  // MFMA step), then the rest of the prefetch: what the first MFMAs need is
-  // queued ahead of what they do not
-  if (nsb > 0) issue(0);
-  const int head = hg * (kHPW * kNW) + wave * kHPW + cidx;
+  // the first step's sub-blocks requested, then Q^T (this lane's head, 8
+  // dims per MFMA step), then the rest of the lookahead: what the first
+  // MFMAs need is queued ahead of what they do not
+  auto issue_step = [&](int st) {
+#pragma unroll
+    for (int x = 0; x < KSPLIT; ++x) issue(st * KSPLIT + x);
+  };
+  if (nst > 0) issue_step(0);
+  const int head = hg * (kHPW * kHW) + hw * kHPW + cidx;
   const bool head_ok = head < a.H_q;
   v8s qb[kKS];
   {
@@ -641,7 +665,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
       qb[ks] = head_ok ? x : v8s{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
-  for (int x = 1; x < min(NBUF - 1, nsb); ++x) issue(x);
+  for (int x = 1; x < min(kAhead, nst); ++x) issue_step(x);
   const float c2 = a.scale * kLog2e;
 
   // Per-lane tile offsets.  Logits: lane (grp, cidx) reads row 16kt + cidx,
@@ -683,20 +707,30 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
     float m_lane = -__builtin_inff();  // max over this lane's logits
     bool over = false;                 // (wave) a logit exceeded m2 + kSlack
 
-    // NBUF-1 sub-blocks are requested up front (before the pass loop for the
-    // first pass); iteration sb requests sub-block sb+NBUF-1 into the buffer
-    // freed by iteration sb-1.
+    // Steps of KSPLIT sub-blocks (one per key half).  kAhead steps are
+    // requested up front (before the pass loop for the first pass); step st
+    // >= 1 requests step st + kAhead - 1 into the buffers freed by step st-1.
     if (pass > 0)
-      for (int x = 0; x < min(NBUF - 1, nsb); ++x) issue(x);
-    for (int sb = 0; sb < nsb; ++sb) {
-      wait_vm<kDmaPerWave>(min(nsb - 1 - sb, NBUF - 2));
+      for (int x = 0; x < min(kAhead, nst); ++x) issue_step(x);
+    for (int st = 0; st < nst; ++st) {
+      // steps requested after this one: all but the first kAhead were
+      // requested one step ahead
+      const int issued_to = st == 0 ? min(kAhead, nst) - 1 : min(nst - 1, st + kAhead - 2);
+      wait_vm<kPerStep>(issued_to - st);
+#pragma unroll
+      for (int x = 0; x < KSPLIT; ++x) {
+        const int sbx = st * KSPLIT + x;
+        const bool any_absent =
+            __ballot(lane < kSB && koff[sbx * kSB + (lane & (kSB - 1))] == ~0u) != 0;
+        if (any_absent) zero_absent(sbx);
+      }
+      // every wave's DMAs of this step have landed, and every wave is done
+      // with the buffers the next DMAs overwrite (last read in step st-1)
+      __syncthreads();
+      if (st >= 1 && st + kAhead - 1 < nst) issue_step(st + kAhead - 1);
+      const int sb = st * KSPLIT + kh;  // this wave's sub-block
       const uint32_t valid =
           (uint32_t)__ballot(lane < kSB && koff[sb * kSB + (lane & (kSB - 1))] != ~0u);
-      if (valid != 0xFFFFFFFFu) zero_absent(sb);
-      // every wave's DMAs of sb have landed, and every wave is done with the
-      // buffer the next DMA overwrites (last read in sub-block sb-1)
-      __syncthreads();
-      if (sb + NBUF - 1 < nsb) issue(sb + NBUF - 1);
 
       // No early exit below: every sub-block runs its MFMAs (a sub-block
       // without a valid key, or after an overrun, adds P = 0), so the
@@ -815,15 +849,43 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
   }
 
   lsum = across_rows(lsum, FAdd());
-  const int head0 = hg * (kHPW * kNW) + wave * kHPW;
+  // every wave is past the last barrier and every DMA has landed: the tile
+  // buffers are free for the merge and the epilogue staging
+  if constexpr (KSPLIT == 2) {
+    // half 1 -> LDS: lane-major v4f per 16-dim tile, then (m2, lsum)
+    uint8_t* mbase = &tile[0][0] + hw * (64 * (kMT * 16 + 8));
+    v4f* mo = reinterpret_cast<v4f*>(mbase);
+    float2* mls = reinterpret_cast<float2*>(mbase + 64 * kMT * 16);
+    if (kh == 1) {
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) mo[mt * 64 + lane] = o[mt];
+      mls[lane] = float2{m2, lsum};
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    // half 0 merges: each half's exponentials are against its own reference
+    const float2 other = mls[lane];
+    const float M = fmaxf(m2, other.x);
+    const float f0 = m2 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m2 - M);
+    const float f1 = other.x == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(other.x - M);
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) {
+      const v4f b = mo[mt * 64 + lane];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[mt][v] = o[mt][v] * f0 + b[v] * f1;
+    }
+    lsum = lsum * f0 + other.y * f1;
+    m2 = M;
+  }
+  const int head0 = hg * (kHPW * kHW) + hw * kHPW;
   if (head0 >= a.H_q) return;
   if (a.n_chunks > 1) {
     write_partial<kMT>(a, row_local, chunk, head0, lane, o, m2, lsum);
     return;
   }
-  // every wave is past the last barrier and every DMA has landed: the tile
-  // buffers are free for staging (16.25 KB per wave)
-  write_out_staged(a, r, head0, lane, o, m2, lsum, &tile[0][0] + wave * (16 * (2 * kDv + 16)));
+  // the head waves' staging (16.25 KB each) sits after the merge area
+  write_out_staged(a, r, head0, lane, o, m2, lsum,
+                   &tile[0][0] + kMergeBytes + hw * (16 * (2 * kDv + 16)));
 }
 
 // Merges the chunks of each (row, head) by log-sum-exp: with M the largest
@@ -928,8 +990,19 @@ hipError_t launch_t(const AttnLaunch& a, hipStream_t s, StageEvents ev, StageEve
   g.chunk = (per + kSB - 1) / kSB * kSB;
   const int grid = (g.n_units + 7) / 8 * 8 * g.n_hg;
   void (*kernel)(AttnLaunch, AttnGrid) = nullptr;
+  int threads = 64 * NW;
   if constexpr (DQK == lat::kDqk && NW > 1) {
-    if (uses_latent_kernel(DQK, a.latent)) kernel = sparse_attn_latent_kernel<DSA_ATTN_NBUF, NW>;
+    if (uses_latent_kernel(DQK, a.latent)) {
+      // split rows (few workgroups, short chunks): two key halves per
+      // workgroup; whole rows: one, with the deeper prefetch
+      kernel = sparse_attn_latent_kernel<DSA_ATTN_NBUF, NW, 1>;
+      if constexpr (NW == 2) {
+        if (DSA_ATTN_KSPLIT == 2 && a.n_chunks > 1) {
+          kernel = sparse_attn_latent_kernel<4, 4, 2>;
+          threads = 256;
+        }
+      }
+    }
   }
   // (the 576-wide staged kernel only ever runs with four waves)
   if constexpr (DQK != lat::kDqk || NW == 4) {
@@ -937,7 +1010,7 @@ hipError_t launch_t(const AttnLaunch& a, hipStream_t s, StageEvents ev, StageEve
       kernel = a.latent ? sparse_attn_kernel<DQK, DV, true, NW> : sparse_attn_kernel<DQK, DV, false, NW>;
   }
   if (!kernel) return hipErrorInvalidConfiguration;
-  hipError_t e = launch_kernel(kernel, dim3(grid), dim3(64 * NW), s, ev.start, ev.stop, a, g);
+  hipError_t e = launch_kernel(kernel, dim3(grid), dim3(threads), s, ev.start, ev.stop, a, g);
   if (e != hipSuccess) return e;
   if (a.n_chunks == 1) {
     if (merge.start && (e = hipEventRecord(merge.start, s)) != hipSuccess) return e;
