@@ -158,6 +158,9 @@ __device__ __forceinline__ int lane_prefix(uint64_t mask) {
 //  - the kSumM largest keys with their offsets in the segment, in slot
 //    order (key 0 fills the entries of a segment shorter than kSumM), and
 //  - the largest key not among them (the segment's next key; 0 if none).
+// Equal keys are taken together, so ties can put more than kSumM keys among
+// the largest; such a segment keeps its first kSumM of them and gets the
+// largest key value as its next key, which makes the selection re-read it.
 // The selection (topk_select.h) works from it.  With K <= 2048 a segment
 // holds on average G K / L <= 2 of the row's K largest keys, so its next key
 // seldom reaches the selection threshold; when it does, the selection
@@ -188,66 +191,96 @@ struct Summary {
 size_t summary_bytes(int rows);
 Summary summary_carve(void* base, int rows);
 
-// Maximum of an unsigned value over aligned groups of G lanes (16, 32 or
-// 64, wave-uniform), in every lane of the group.
-__device__ __forceinline__ uint32_t group_max_u32(uint32_t x, int G) {
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));  // row_half_mirror
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false));  // row_mirror
-  if (G >= 32) {
-    const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    x = max((uint32_t)p[0], (uint32_t)p[1]);
+// Maximum over aligned groups of G lanes (16, 32 or 64) of two values at
+// once, x and y, each in every lane of its group.  Within a row of 16 lanes
+// four DPP steps per value, interleaved so that each fills the other's wait
+// states.  Across rows one v_permlane16_swap of x with y leaves, after a
+// max, x's pair-of-rows maxima in the even rows and y's in the odd rows (row
+// 2i + v holds the max of rows 2i, 2i + 1 of value v); for G = 64 a
+// v_permlane32_swap folds the two halves of the wave the same way.  A last
+// v_permlane16_swap spreads the even rows to every lane (x) and the odd rows
+// (y).
+template <int G>
+__device__ __forceinline__ void group_max2_u32(uint32_t& x, uint32_t& y) {
+  static_assert(G == 16 || G == 32 || G == 64, "segment size");
+#define DSA_GMAX_DPP(ctrl)                                                                   \
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, ctrl, 0xF, 0xF, false));     \
+  y = max(y, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)y, ctrl, 0xF, 0xF, false));
+  DSA_GMAX_DPP(0xB1)   // quad_perm [1,0,3,2]
+  DSA_GMAX_DPP(0x4E)   // quad_perm [2,3,0,1]
+  DSA_GMAX_DPP(0x141)  // row_half_mirror
+  DSA_GMAX_DPP(0x140)  // row_mirror
+#undef DSA_GMAX_DPP
+  if constexpr (G >= 32) {
+    const auto p = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+    uint32_t c = max((uint32_t)p[0], (uint32_t)p[1]);
+    if constexpr (G == 64) {
+      const auto q = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+      c = max((uint32_t)q[0], (uint32_t)q[1]);
+    }
+    const auto r = __builtin_amdgcn_permlane16_swap(c, c, false, false);
+    x = (uint32_t)r[0];
+    y = (uint32_t)r[1];
   }
-  if (G >= 64) {
-    const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    x = max((uint32_t)p[0], (uint32_t)p[1]);
-  }
-  return x;
 }
 
 // The summary of one half of a wave's 128 slots (64 slots, one per lane),
 // as this lane's share: whether its key is taken, its rank among the taken
 // keys of its segment, how many were taken there, and the segment's next
-// key.  k is the key of the lane's slot (0 past the row; keys of slots are
-// at least 1); G = sum_seg(S) lanes form a segment.  Up to kSumM rounds
-// each take one largest remaining key per segment (the lowest lane holding
-// it; the order among equal keys does not matter: a segment whose next key
-// ties the threshold is re-read whole).  Registers only: it can run while
-// the wave still waits for its other loads.
+// key.  G = sum_seg(S) lanes form a segment.
 struct HalfSummary {
   bool taken;
   int rank, count;
   uint32_t next;
 };
-__device__ __forceinline__ HalfSummary summary_half(uint32_t k, int G) {
+__device__ __forceinline__ HalfSummary summary_finish(bool t, uint32_t rest_max, int G) {
   const int lane = (int)(threadIdx.x & 63);
   const int base = lane & ~(G - 1);
   const uint64_t gmask = G == 64 ? ~0ull : ((1ull << G) - 1ull) << base;
-  bool t = false;
-  uint32_t v = k;
+  const uint64_t m = __ballot(t) & gmask;
+  HalfSummary hs;
+  hs.taken = t;
+  hs.rank = lane_prefix(m);
+  hs.count = __popcll(m);
+  hs.next = hs.count > kSumM ? ~0u : rest_max;
+  return hs;
+}
+// Both halves' summaries; ka and kb are the keys of this lane's slot in
+// each half (0 past the row; keys of slots are at least 1).  kSumM rounds
+// each take, in every segment, all keys equal to the largest key left;
+// then the next key is the largest key not taken.  Registers only.
+template <int G>
+__device__ __forceinline__ void summary_halves_g(uint32_t ka, uint32_t kb, HalfSummary& ha,
+                                                 HalfSummary& hb) {
+  bool ta = false, tb = false;
 #pragma unroll
   for (int i = 0; i < kSumM; ++i) {
-    const uint32_t M = group_max_u32(v, G);
-    if (__ballot(M != 0u) == 0) break;  // nothing left in any segment
-    const uint64_t h = __ballot(v == M && M != 0u) & gmask;
-    if (h != 0 && lane == (int)__builtin_ctzll(h)) {
-      t = true;
-      v = 0u;
-    }
+    uint32_t ma = ka, mb = kb;
+    group_max2_u32<G>(ma, mb);
+    const bool ea = ka != 0u && ka == ma, eb = kb != 0u && kb == mb;
+    ta = ta || ea;
+    tb = tb || eb;
+    ka = ea ? 0u : ka;
+    kb = eb ? 0u : kb;
   }
-  HalfSummary hs;
-  hs.next = group_max_u32(v, G);
-  const uint64_t m = __ballot(t) & gmask;
-  hs.taken = t;
-  hs.rank = __popcll(m & ((1ull << lane) - 1ull));
-  hs.count = __popcll(m);
-  return hs;
+  group_max2_u32<G>(ka, kb);
+  ha = summary_finish(ta, ka, G);
+  hb = summary_finish(tb, kb, G);
+}
+__device__ __forceinline__ void summary_halves(uint32_t ka, uint32_t kb, int G, HalfSummary& ha,
+                                               HalfSummary& hb) {
+  if (G == 64)
+    summary_halves_g<64>(ka, kb, ha, hb);
+  else if (G == 32)
+    summary_halves_g<32>(ka, kb, ha, hb);
+  else
+    summary_halves_g<16>(ka, kb, ha, hb);
 }
 
 // Writes a half's summary: slots h0 .. h0 + 63 (h0 a multiple of 64, the
 // half's first slot) of row `row` of a row of S slots, this lane's key k.
-// The taken keys go out in slot order, then zero entries up to kSumM.
+// The taken keys go out in slot order (the first kSumM of them), then zero
+// entries up to kSumM.
 __device__ __forceinline__ void summary_store(const HalfSummary& hs, uint32_t k, int h0, int S,
                                               int G, const Summary& sum, int64_t row) {
   const int lane = (int)(threadIdx.x & 63);
@@ -256,7 +289,7 @@ __device__ __forceinline__ void summary_store(const HalfSummary& hs, uint32_t k,
   const int sg = (h0 + base) / G;
   uint32_t* kd = sum.key + row * kSumEntries + sg * kSumM;
   uint8_t* od = sum.off + row * kSumEntries + sg * kSumM;
-  if (hs.taken) {
+  if (hs.taken && hs.rank < kSumM) {
     kd[hs.rank] = k;
     od[hs.rank] = (uint8_t)i;
   }

@@ -256,25 +256,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
   // full-width stores at the end, not one narrow store per sub-tile.
   float* my_sc = sc_lds[wave];
   // The Top-K's summary of this wave's slots (the kSumM largest keys of each
-  // segment, with their offsets, and the segment's next key): the first
-  // half's is worked out as soon as its four sub-tiles are scored, while
-  // the second half's keys are still loading; both are stored at the end.
+  // segment, with their offsets, and the segment's next key) is worked out
+  // for both halves at once after the last sub-tile: the last workgroups to
+  // get their keys end the kernel, and the two halves' interleaved rounds
+  // take about the time of one.
   static_assert(kSpan == 128 && kSubPerWave == 8, "a wave's summary covers two halves of 64");
   const bool summ = a.sum.key && w0 < S && sum_row(S, a.topk_K);  // wave-uniform
-  const int G = sum_seg(S);
-  uint32_t ka = 0u;
-  HalfSummary ha{};
 
   bool bad_page = false;
 #pragma unroll
   for (int j = 0; j < kSubPerWave; ++j) {
-    if (j == kSubPerWave / 2 && summ) {
-      // LDS accesses of one wave complete in order; the fence keeps the
-      // compiler from moving the reads above the writes of other lanes
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      ka = w0 + lane < S ? score_key(my_sc[lane]) : 0u;
-      ha = summary_half(ka, G);
-    }
     float part = 0.0f;
     // B scale: byte g of the key row's scale word (127, i.e. x1, for unused
     // groups and for E4M3)
@@ -313,8 +304,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     if (w0 + i < S) out[w0 + i] = my_sc[i];
   }
   if (summ) {
+    const int G = sum_seg(S);
+    const uint32_t ka = w0 + lane < S ? score_key(my_sc[lane]) : 0u;
     const uint32_t kb = w0 + 64 + lane < S ? score_key(my_sc[64 + lane]) : 0u;
-    const HalfSummary hb = summary_half(kb, G);
+    HalfSummary ha, hb;
+    summary_halves(ka, kb, G, ha, hb);
     summary_store(ha, ka, w0, S, G, a.sum, r - a.row_begin);
     summary_store(hb, kb, w0 + 64, S, G, a.sum, r - a.row_begin);
   }

@@ -33,7 +33,8 @@ __global__ __launch_bounds__(256) void topk_summary_kernel(TopkLaunch a) {
   const uint32_t ka = w0 + lane < L ? score_key(sc[w0 + lane]) : 0u;
   const uint32_t kb = w0 + 64 + lane < L ? score_key(sc[w0 + 64 + lane]) : 0u;
   const int G = sum_seg(L);
-  const HalfSummary ha = summary_half(ka, G), hb = summary_half(kb, G);
+  HalfSummary ha, hb;
+  summary_halves(ka, kb, G, ha, hb);
   summary_store(ha, ka, w0, L, G, a.sum, r_local);
   summary_store(hb, kb, w0 + 64, L, G, a.sum, r_local);
 }
