@@ -555,7 +555,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
   __shared__ __attribute__((aligned(16))) uint8_t tile[NBUF][kTileBytes];
   // each slot's row offset in the cache in 16-byte units (the front end
   // keeps the cache below 64 GiB for this kernel), ~0u for an absent row
-  __shared__ uint32_t koff[kMaxChunkLat];
+  __shared__ __attribute__((aligned(16))) uint32_t koff[kMaxChunkLat];
 
   int unit, hg;
   if (!decode_wg(g, unit, hg)) return;
@@ -619,15 +619,32 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
   // 0 (which always exists) and are zeroed after they land.
   // (All row offsets are read before the first DMA: the DMA's asm is a
   // compiler memory barrier, so reads interleaved with it would each wait.)
+  // A wave's DMAs of a sub-block cover its rows kRowsPW * wave .. + kRowsPW
+  // - 1 (kRowsPW rows x 72 pieces = kDmaPerWave x 64 slots): their offsets
+  // come in with a few broadcast LDS reads, and instruction t, whose lanes
+  // span at most two of those rows (64 slots < 72 pieces), picks its row's
+  // offset with one select.
+  constexpr int kRowsPW = kSB / kNW;
+  static_assert(kRowsPW * kPieces == kDmaPerWave * 64 && kRowsPW % 4 == 0, "rows per wave");
   auto issue = [&](int sb) {
     uint8_t* buf = tile[sb % NBUF];
+    uint32_t kr[kRowsPW];
+#pragma unroll
+    for (int i = 0; i < kRowsPW; i += 4) {
+      const uint4 x = *reinterpret_cast<const uint4*>(&koff[sb * kSB + kRowsPW * wave + i]);
+      kr[i] = x.x;
+      kr[i + 1] = x.y;
+      kr[i + 2] = x.z;
+      kr[i + 3] = x.w;
+    }
     const uint8_t* src[kDmaPerWave];
 #pragma unroll
     for (int t = 0; t < kDmaPerWave; ++t) {
-      const int sl = 64 * (wave * kDmaPerWave + t) + lane;
-      const int row = sl / kPieces;
-      const int piece = (sl - row * kPieces) ^ (row & 7);
-      const uint32_t o16 = koff[sb * kSB + row];
+      const int sl = 64 * t + lane;  // slot within this wave's rows
+      const int j = sl / kPieces;    // a_t or a_t + 1
+      const int at = 64 * t / kPieces;
+      const int piece = (sl - j * kPieces) ^ ((kRowsPW * wave + j) & 7);
+      const uint32_t o16 = (at + 1 < kRowsPW && j > at) ? kr[at + 1 < kRowsPW ? at + 1 : at] : kr[at];
       src[t] = kbase + (o16 != ~0u ? (int64_t)o16 << 4 : 0) + 16 * piece;
     }
     const uint32_t lds0 =
@@ -653,19 +670,53 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
 #pragma unroll
     for (int x = 0; x < KSPLIT; ++x) issue(st * KSPLIT + x);
   };
-  if (nst > 0) issue_step(0);
-  const int head = hg * (kHPW * kHW) + hw * kHPW + cidx;
+  // Q of the workgroup's heads is one contiguous run of rows, staged once
+  // per workgroup by DMA into the last kQT tile buffers (as sub-blocks of
+  // keys are, same swizzle) and read from there as each wave's Q^T operand;
+  // the steps that fill those buffers are requested after the reads.
+  // Loading Q^T per wave straight from memory instead would fetch it once
+  // per key half, in 16-row gathers.
+  constexpr int kHG = kHPW * kHW;  // heads per workgroup
+  constexpr int kQT = kHG / kSB;   // tile buffers they take
+  static_assert(kHG % kSB == 0 && kQT < NBUF, "the workgroup's heads fill whole tiles");
+  constexpr int kStepQ = (NBUF - kQT) / KSPLIT;  // first step that writes a Q buffer
+  const int head0_wg = hg * kHG;
+  for (int x = 0; x < min(kStepQ, nst); ++x) issue_step(x);
+  {
+    const uint8_t* qbase = reinterpret_cast<const uint8_t*>(a.q + (int64_t)r * a.H_q * kDqk);
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) {
+      const uint8_t* src[kDmaPerWave];
+#pragma unroll
+      for (int t = 0; t < kDmaPerWave; ++t) {
+        const int sl = 64 * (wave * kDmaPerWave + t) + lane;
+        const int row = sl / kPieces;
+        const int piece = (sl - row * kPieces) ^ (row & 7);
+        const int h = head0_wg + kSB * qt + row;
+        src[t] = qbase + (int64_t)(h < a.H_q ? h : 0) * (2 * kDqk) + 16 * piece;  // (rows past H_q go unused)
+      }
+      const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+          (uint32_t)(uintptr_t)(tile[NBUF - kQT + qt] + 1024 * wave * kDmaPerWave));
+#pragma unroll
+      for (int t = 0; t < kDmaPerWave; ++t) dma16(src[t], lds0 + 1024 * t);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const int head = head0_wg + hw * kHPW + cidx;
   const bool head_ok = head < a.H_q;
   v8s qb[kKS];
   {
-    const uint16_t* qrow = a.q + ((int64_t)r * a.H_q + (head_ok ? head : 0)) * kDqk + 8 * grp;
+    const int qr = hw * kHPW + cidx;  // row among the workgroup's heads
+    const uint8_t* qrow = tile[NBUF - kQT + qr / kSB] + 16 * ((qr % kSB) * kPieces);
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
-      const v8s x = *reinterpret_cast<const v8s*>(qrow + 32 * ks);
+      const v8s x = *reinterpret_cast<const v8s*>(qrow + 16 * ((grp + 4 * ks) ^ (qr & 7)));
       qb[ks] = head_ok ? x : v8s{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
-  for (int x = 1; x < min(kAhead, nst); ++x) issue_step(x);
+  __syncthreads();  // every wave holds its Q^T: the buffers are free
+  for (int x = kStepQ; x < min(kAhead, nst); ++x) issue_step(x);
   const float c2 = a.scale * kLog2e;
 
   // Per-lane tile offsets.  Logits: lane (grp, cidx) reads row 16kt + cidx,
