@@ -73,6 +73,7 @@ struct Smem {
   alignas(16) uint32_t buf[kSmall];
   uint32_t res[4];
   alignas(16) uint32_t wsum[2 * kWaves];
+  alignas(16) uint32_t wflag[2 * kWaves];  // per-wave flags of block_scan_flag
   alignas(16) uint32_t red[3 * (kWaves < 4 ? 4 : kWaves)];
 };
 
@@ -124,6 +125,37 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t* wsum, uint3
     tot += v;
     before += i < wave ? v : 0u;
   }
+  return before + inc - x;
+}
+
+// block_scan that also ORs a per-thread flag over the block, through the
+// same barrier (the result in every thread).
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan_flag(uint32_t x, bool flag, uint32_t* wsum,
+                                                    uint32_t* wflag, uint32_t& ph, uint32_t& tot,
+                                                    bool& any) {
+  constexpr int W = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t* w = wsum + (ph & 1u) * W;
+  uint32_t* f = wflag + (ph & 1u) * W;
+  ++ph;
+  const uint32_t inc = wave_scan(x, 0u, Add());
+  const bool wf = __ballot(flag) != 0;
+  if (lane == 63) {
+    w[wave] = inc;
+    f[wave] = wf ? 1u : 0u;
+  }
+  __syncthreads();
+  uint32_t before = 0, fl = 0;
+  tot = 0;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    const uint32_t v = w[i];
+    tot += v;
+    before += i < wave ? v : 0u;
+    fl |= f[i];
+  }
+  any = fl != 0u;
   return before + inc - x;
 }
 
@@ -351,10 +383,14 @@ __device__ __forceinline__ uint32_t popc_any(uint64_t m) { return __popcll(m); }
 // Emits the register keys given T and the number of keys equal to T to
 // keep (the first ones in slot order), into s.pos: every thread sets one
 // bit per kept key, and after one block scan of the counts writes only
-// those.
+// those.  `sat`: this thread holds a saturated summary segment; the scan ORs
+// it over the block, and when any is set nothing is written and false is
+// returned (the same in every thread).  (Writing the kept keys straight to
+// the output instead of staging them costs more: one narrow store per kept
+// key and lane, against a few full-width ones.)
 template <int NT>
-__device__ __forceinline__ void regs_emit(const Regs<NT>& r, int G, uint32_t T, uint32_t need_eq,
-                                          Smem<NT>& s, uint32_t& ph) {
+__device__ __forceinline__ bool regs_emit(const Regs<NT>& r, int G, uint32_t T, uint32_t need_eq,
+                                          bool sat, Smem<NT>& s, uint32_t& ph) {
   using Mask = typename Regs<NT>::Mask;
   Mask gtm = 0, eqm = 0;
 #pragma unroll
@@ -364,7 +400,10 @@ __device__ __forceinline__ void regs_emit(const Regs<NT>& r, int G, uint32_t T, 
   }
   const uint32_t ngt = popc_any(gtm), neq = popc_any(eqm);
   uint32_t tot;
-  const uint32_t ex = block_scan<NT>((neq << 16) | ngt, s.wsum, ph, tot);
+  bool any_sat;
+  const uint32_t ex =
+      block_scan_flag<NT>((neq << 16) | ngt, sat, s.wsum, s.wflag, ph, tot, any_sat);
+  if (any_sat) return false;
   const uint32_t eq_before = ex >> 16;
   // equal keys this thread keeps, as a difference of two minima (the
   // conditional-subtract form of it lost its condition in compilation)
@@ -395,6 +434,7 @@ __device__ __forceinline__ void regs_emit(const Regs<NT>& r, int G, uint32_t T, 
     }
     s.pos[slot++] = p;
   }
+  return true;
 }
 
 // Streamed: histogram passes over the keys read from memory, then one
@@ -670,17 +710,13 @@ __device__ __forceinline__ int select_row(const float* sc, bool vec, int L, int 
               if (r.k[j] != 0u) f(r.k[j]);
           },
           kmin, kmax, need, s, ph, true);
-      bool done = true;
       uint32_t satm = 0;
       if (summ) {
 #pragma unroll
         for (int q = 0; q < kSPT; ++q) satm |= (seg_saturated<NT>(r, q, L, G, T1) ? 1u : 0u) << q;
       }
-      if (__syncthreads_or(satm != 0u))
-        done = summary_saturated<NT>(sc, L, G, r, satm, T1, kmax, K, s, ph);
-      else
-        regs_emit<NT>(r, G, T1, need, s, ph);
-      if (done) {
+      if (regs_emit<NT>(r, G, T1, need, satm != 0u, s, ph) ||
+          summary_saturated<NT>(sc, L, G, r, satm, T1, kmax, K, s, ph)) {
         __syncthreads();
         flush<NT>(o, K, count, s.pos);
         __syncthreads();
