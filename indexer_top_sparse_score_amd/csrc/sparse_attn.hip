@@ -98,7 +98,7 @@ __device__ __forceinline__ void write_partial(const AttnLaunch& a, int row_local
   float* dst = part_out(a, row_local, chunk, 16 * MT) + (int64_t)(head0 / 16) * (MT * 256) +
                cidx * 16 + 4 * grp;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<v4f*>(dst + mt * 256) = o[mt];
+  for (int mt = 0; mt < MT; ++mt) __builtin_nontemporal_store(o[mt], reinterpret_cast<v4f*>(dst + mt * 256));
   if (grp == 0 && head0 + cidx < a.H_q)
     part_stats(a, row_local, chunk)[head0 + cidx] =
         float2{lsum > 0.0f ? m2 : -__builtin_inff(), lsum};
