@@ -181,8 +181,18 @@ __host__ __device__ inline bool sum_row(int L, int K) {
 }
 
 // The summaries of a pass of rows, carved from a workspace: keys
-// [rows][kSumEntries] (uint32), offsets [rows][kSumEntries] (uint8), next
-// keys [rows][kSumSegMax] (uint32).
+// [rows][kSumEntries] (uint32, laid out by sum_key_index), offsets
+// [rows][kSumSegMax][kSumM] (uint8), next keys [rows][kSumSegMax] (uint32).
+//
+// Key layout within a row: segments go in pairs (2p, 2p + 1), whose 16
+// entries j = 8 (sg & 1) + e form four chunks of four keys; chunk c of pair
+// p sits at (c * kSumSegMax / 2 + p) * 4.  A selecting workgroup of 1024
+// threads holds one pair per thread, so each of its four key loads reads
+// 16 contiguous bytes per lane, a kilobyte per wave.
+__host__ __device__ inline int sum_key_index(int sg, int e) {
+  const int j = ((sg & 1) << 3) | e;
+  return (((j >> 2) * (kSumSegMax / 2) + (sg >> 1)) << 2) | (j & 3);
+}
 struct Summary {
   uint32_t* key;
   uint8_t* off;
@@ -287,14 +297,14 @@ __device__ __forceinline__ void summary_store(const HalfSummary& hs, uint32_t k,
   const int base = lane & ~(G - 1), i = lane - base;
   if (h0 + base >= S) return;
   const int sg = (h0 + base) / G;
-  uint32_t* kd = sum.key + row * kSumEntries + sg * kSumM;
+  uint32_t* kd = sum.key + row * kSumEntries;
   uint8_t* od = sum.off + row * kSumEntries + sg * kSumM;
   if (hs.taken && hs.rank < kSumM) {
-    kd[hs.rank] = k;
+    kd[sum_key_index(sg, hs.rank)] = k;
     od[hs.rank] = (uint8_t)i;
   }
   if (i >= hs.count && i < kSumM) {
-    kd[i] = 0u;
+    kd[sum_key_index(sg, i)] = 0u;
     od[i] = 0;
   }
   if (i == 0) sum.next[row * kSumSegMax + sg] = hs.next;

@@ -608,24 +608,35 @@ __device__ __forceinline__ bool summary_saturated(const float* sc, int L, int G,
   return true;
 }
 
-// A thread's share of a row's summary: its SPT segments, loaded before the
-// row's length is known (the summary area always holds kSumSegMax segments
-// per row; entries of segments past the row are masked once it is).
+// A thread's share of a row's summary: its SPT segments (SPT / 2 segment
+// pairs), loaded before the row's length is known (the summary area always
+// holds kSumSegMax segments per row; entries of segments past the row are
+// masked once it is).  With 1024 threads each load instruction of a wave
+// reads one contiguous kilobyte (sum_key_index lays the keys out so).
 template <int NT>
 __device__ __forceinline__ void load_summary(const uint32_t* skey, const uint8_t* soff,
                                              const uint32_t* snext, Regs<NT>& r) {
   constexpr int kSPT = Regs<NT>::SPT;
+  static_assert(kSPT % 2 == 0, "whole segment pairs per thread");
 #pragma unroll
-  for (int q = 0; q < kSPT; ++q) {
-    const int sg = (int)threadIdx.x * kSPT + q;
-    const uint4 a = *reinterpret_cast<const uint4*>(skey + sg * kSumM);
-    const uint4 b = *reinterpret_cast<const uint4*>(skey + sg * kSumM + 4);
-    const uint2 c = *reinterpret_cast<const uint2*>(soff + sg * kSumM);
-    r.k[q * 8 + 0] = a.x; r.k[q * 8 + 1] = a.y; r.k[q * 8 + 2] = a.z; r.k[q * 8 + 3] = a.w;
-    r.k[q * 8 + 4] = b.x; r.k[q * 8 + 5] = b.y; r.k[q * 8 + 6] = b.z; r.k[q * 8 + 7] = b.w;
-    r.w[2 * q] = c.x;
-    r.w[2 * q + 1] = c.y;
-    r.nx[q] = snext[sg];
+  for (int i = 0; i < kSPT / 2; ++i) {
+    const int pair = (int)threadIdx.x * (kSPT / 2) + i;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 a = *reinterpret_cast<const uint4*>(skey + sum_key_index(2 * pair, 4 * c));
+      r.k[16 * i + 4 * c + 0] = a.x;
+      r.k[16 * i + 4 * c + 1] = a.y;
+      r.k[16 * i + 4 * c + 2] = a.z;
+      r.k[16 * i + 4 * c + 3] = a.w;
+    }
+    const uint4 o = *reinterpret_cast<const uint4*>(soff + pair * 2 * kSumM);
+    r.w[4 * i + 0] = o.x;
+    r.w[4 * i + 1] = o.y;
+    r.w[4 * i + 2] = o.z;
+    r.w[4 * i + 3] = o.w;
+    const uint2 n = *reinterpret_cast<const uint2*>(snext + 2 * pair);
+    r.nx[2 * i] = n.x;
+    r.nx[2 * i + 1] = n.y;
   }
 }
 
