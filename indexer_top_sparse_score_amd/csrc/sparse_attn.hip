@@ -1044,11 +1044,11 @@ hipError_t launch_t(const AttnLaunch& a, hipStream_t s, StageEvents ev, StageEve
   int threads = 64 * NW;
   if constexpr (DQK == lat::kDqk && NW > 1) {
     if (uses_latent_kernel(DQK, a.latent)) {
-      // split rows (few workgroups, short chunks): two key halves per
-      // workgroup; whole rows: one, with the deeper prefetch
+      // two key halves per workgroup (four waves: every SIMD of the CU
+      // busy), for split and whole rows alike
       kernel = sparse_attn_latent_kernel<DSA_ATTN_NBUF, NW, 1>;
       if constexpr (NW == 2) {
-        if (DSA_ATTN_KSPLIT == 2 && a.n_chunks > 1) {
+        if (DSA_ATTN_KSPLIT == 2) {
           kernel = sparse_attn_latent_kernel<4, 4, 2>;
           threads = 256;
         }
