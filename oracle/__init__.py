@@ -24,7 +24,8 @@ numeric example for any step):
   - section 4.3: the fused call takes the quantised query, the index keys and
     the head weights and returns the selected positions;
   - section 5.1 / 5.2: FP8 storage for the indexer and the KV cache; the
-    indexer's MXFP8 format (one shared scale per group of 32).
+    indexer's MXFP8 format (one shared scale per group of 32); the KV cache's
+    per-token tiles of 128 elements with one scale each.
 * vLLM's DeepSeek-V4.1-Flash article, "Kernels": later indexer layers score
   only a fixed set of candidate positions and take their top-k from it.
 * "Bandwidth-Aware LLM Inference on Heterogeneous Many-Core Supercomputers"
@@ -50,7 +51,7 @@ invariants).  The constants the pages never fix (ReLU gate, K, block size 64,
 head dims, attention scale) are readings, not values the pages confirm.
 """
 
-from .formats import E4M3_TABLE, e4m3_to_f64, e8m0_to_f64, bf16_to_f64
+from .formats import E4M3_TABLE, KV_TILE, e4m3_to_f64, e8m0_to_f64, bf16_to_f64, kv_fp8_to_f64, kv_tiles
 from .dsa import (
     resolve_rows,
     gather_positions,
@@ -59,14 +60,15 @@ from .dsa import (
     score_keys,
     topk_row,
     sparse_attn_row,
+    sparse_attn_values,
     masked_dense_attn_row,
     dense_causal_attn_row,
     decode_step,
 )
 
 __all__ = [
-    "E4M3_TABLE", "e4m3_to_f64", "e8m0_to_f64", "bf16_to_f64",
-    "resolve_rows", "gather_positions", "row_history", "indexer_scores_row", "score_keys",
-    "topk_row", "sparse_attn_row", "masked_dense_attn_row",
+    "E4M3_TABLE", "KV_TILE", "e4m3_to_f64", "e8m0_to_f64", "bf16_to_f64", "kv_fp8_to_f64",
+    "kv_tiles", "resolve_rows", "gather_positions", "row_history", "indexer_scores_row",
+    "score_keys", "topk_row", "sparse_attn_row", "sparse_attn_values", "masked_dense_attn_row",
     "dense_causal_attn_row", "decode_step",
 ]

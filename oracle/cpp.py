@@ -45,7 +45,7 @@ class _Step(ctypes.Structure):
         ("cand", _i32p), ("cand_len", _i32p), ("n_cand", ctypes.c_int32),
         ("H_q", ctypes.c_int32), ("D_qk", ctypes.c_int32), ("D_v", ctypes.c_int32),
         ("K", ctypes.c_int32), ("scale", ctypes.c_double),
-        ("q", _u16p), ("k", _u16p), ("v", _u16p),
+        ("q", _u16p), ("k", _u16p), ("v", _u16p), ("k8", _u8p), ("k8_scale", _f32p),
     ]
 
 
@@ -84,6 +84,7 @@ def lib():
                                           _i64p, _f64p, _f64p, _f32p, ctypes.c_int64,
                                           ctypes.c_int]
             L.orc_decode_step.restype = ctypes.c_int
+            L.orc_kv_fp8_decode.argtypes = [_u8p, _f32p, ctypes.c_int64, ctypes.c_int, _f64p]
             _lib = L
     return _lib
 
@@ -146,6 +147,21 @@ def sparse_attn_row(q_bits, k_rows_bits, v_rows_bits, scale, threads=1):
     return o, lse
 
 
+def kv_fp8_to_f64(codes, scales):
+    """Decoded FP8 KV rows (codes uint8 [..., D], scales float32 [..., ceil(D/128)])
+    -> float64 [..., D]; the C++ route's counterpart of ``oracle.kv_fp8_to_f64``."""
+    c = _arr(codes, np.uint8)
+    D = c.shape[-1]
+    n = c.size // D if D else 0
+    s = _arr(scales, np.float32)
+    if s.shape[-1] != (D + 127) // 128 or s.size != n * s.shape[-1]:
+        raise ValueError("one scale per tile of 128 elements")
+    out = np.empty(c.shape, np.float64)
+    lib().orc_kv_fp8_decode(_ptr(c, ctypes.c_uint8), _ptr(s, ctypes.c_float), n, D,
+                            _ptr(out, ctypes.c_double))
+    return out
+
+
 def masked_dense_attn_row(q_bits, k_all_bits, v_all_bits, selected, scale):
     q = _arr(q_bits, np.uint16)
     k = _arr(k_all_bits, np.uint16).reshape(-1, q.shape[1])
@@ -164,7 +180,7 @@ def masked_dense_attn_row(q_bits, k_all_bits, v_all_bits, selected, scale):
 
 def decode_step(*, qI, w, kI_cache, q, k_cache, v_cache, block_table, seq_lens, K, scale,
                 D_v, row_seq=None, row_pos=None, rows=None, keep_scores=True, qI_scale=None,
-                kI_scale_cache=None, cand=None, cand_len=None, threads=1):
+                kI_scale_cache=None, cand=None, cand_len=None, k_scale_cache=None, threads=1):
     """The whole step for the chosen rows; same contract and result dict as
     the numpy oracle's ``decode_step``, plus ``threads`` host threads."""
     keep = {}
@@ -200,8 +216,14 @@ def decode_step(*, qI, w, kI_cache, q, k_cache, v_cache, block_table, seq_lens, 
         st.cand_len = _ptr(hold(cand_len, np.int32), ctypes.c_int32)
     st.H_q, st.D_qk, st.D_v, st.K, st.scale = H_q, D_qk, int(D_v), int(K), float(scale)
     st.q = _ptr(q_a, ctypes.c_uint16)
-    st.k = _ptr(hold(k_cache, np.uint16), ctypes.c_uint16)
-    st.v = _ptr(hold(v_cache, np.uint16), ctypes.c_uint16)
+    if k_scale_cache is not None:  # FP8 KV cache: E4M3 codes and tile scales, latent layout
+        if v_cache is not None:
+            raise ValueError("the FP8 KV cache takes the latent layout")
+        st.k8 = _ptr(hold(k_cache, np.uint8), ctypes.c_uint8)
+        st.k8_scale = _ptr(hold(k_scale_cache, np.float32), ctypes.c_float)
+    else:
+        st.k = _ptr(hold(k_cache, np.uint16), ctypes.c_uint16)
+        st.v = _ptr(hold(v_cache, np.uint16), ctypes.c_uint16)
 
     rows = np.arange(num_rows) if rows is None else np.asarray(rows, np.int64)
     rows32 = _arr(rows, np.int32)

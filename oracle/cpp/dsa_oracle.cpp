@@ -64,6 +64,14 @@ double bf16_value(uint16_t bits) {
   return (double)f;
 }
 
+// FP8 KV cache (Day0 article, section 5.2: FP8, quantised per token and head
+// in tiles of 128 elements).  Readings: E4M3 codes, one binary32 scale per
+// tile, value = code value * scale; a row of D elements has ceil(D / 128)
+// tiles, the last one shorter when 128 does not divide D.
+constexpr int kKvTile = 128;
+int kv_tiles(int D) { return (D + kKvTile - 1) / kKvTile; }
+double kv_fp8_value(uint8_t code, float scale) { return e4m3().v[code] * (double)scale; }
+
 // Order-preserving key of a binary32 score: larger score, larger key; -0 and
 // +0 share a key; NaN gets 0 and ranks below every number.
 uint32_t score_key(float s) {
@@ -161,11 +169,11 @@ int64_t orc_topk(const float* scores, int64_t n, int64_t K, int32_t* idx) {
 }
 
 // Softmax attention of one query row (H heads, bf16 q [H][Dqk]) over n
-// gathered rows: logit[h,j] = scale sum_d q[h,d] k[j,d]; o[h] = sum_j
-// exp(logit - m) v[j] / sum_j exp(logit - m); lse[h] = m + ln(sum).  With
-// no rows: o = 0 and lse = -inf.  k [n][Dqk], v [n][Dv] (bf16 bits).
-void orc_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n, int H,
-                   int Dqk, int Dv, double scale, double* o, double* lse, int threads) {
+// gathered rows of decoded values: logit[h,j] = scale sum_d q[h,d] k[j,d];
+// o[h] = sum_j exp(logit - m) v[j] / sum_j exp(logit - m); lse[h] = m +
+// ln(sum).  With no rows: o = 0 and lse = -inf.  k [n][Dqk], v [n][Dv].
+static void attention_values(const uint16_t* q, const double* k, const double* v, int64_t n,
+                             int H, int Dqk, int Dv, double scale, double* o, double* lse, int threads) {
   parallel_for(H, threads, [&](int64_t h) {
     double* oh = o + h * Dv;
     for (int d = 0; d < Dv; ++d) oh[d] = 0.0;
@@ -176,7 +184,7 @@ void orc_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int6
     std::vector<double> logit(n);
     for (int64_t j = 0; j < n; ++j) {
       double dot = 0.0;
-      for (int d = 0; d < Dqk; ++d) dot += bf16_value(q[h * Dqk + d]) * bf16_value(k[j * Dqk + d]);
+      for (int d = 0; d < Dqk; ++d) dot += bf16_value(q[h * Dqk + d]) * k[j * Dqk + d];
       logit[j] = scale * dot;
     }
     const double m = *std::max_element(logit.begin(), logit.end());
@@ -184,11 +192,29 @@ void orc_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int6
     for (int64_t j = 0; j < n; ++j) {
       const double p = std::exp(logit[j] - m);
       l += p;
-      for (int d = 0; d < Dv; ++d) oh[d] += p * bf16_value(v[j * Dv + d]);
+      for (int d = 0; d < Dv; ++d) oh[d] += p * v[j * Dv + d];
     }
     for (int d = 0; d < Dv; ++d) oh[d] /= l;
     lse[h] = m + std::log(l);
   });
+}
+
+// attention_values with bf16 rows: k [n][Dqk], v [n][Dv] (bf16 bits).
+void orc_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n, int H,
+                   int Dqk, int Dv, double scale, double* o, double* lse, int threads) {
+  std::vector<double> kd((size_t)n * Dqk), vd((size_t)n * Dv);
+  for (size_t i = 0; i < kd.size(); ++i) kd[i] = bf16_value(k[i]);
+  for (size_t i = 0; i < vd.size(); ++i) vd[i] = bf16_value(v[i]);
+  attention_values(q, kd.data(), vd.data(), n, H, Dqk, Dv, scale, o, lse, threads);
+}
+
+// Decoded values of n FP8 KV rows: codes [n][D] (E4M3), scales
+// [n][ceil(D / 128)] -> out [n][D].
+void orc_kv_fp8_decode(const uint8_t* codes, const float* scales, int64_t n, int D, double* out) {
+  const int T = kv_tiles(D);
+  for (int64_t j = 0; j < n; ++j)
+    for (int d = 0; d < D; ++d)
+      out[j * D + d] = kv_fp8_value(codes[j * D + d], scales[j * T + d / kKvTile]);
 }
 
 // The same attention by brute force over every one of the n rows of a
@@ -237,8 +263,11 @@ struct OrcStep {
   int32_t H_q, D_qk, D_v, K;
   double scale;
   const uint16_t* q;           // [num_rows][H_q][D_qk]
-  const uint16_t* k;           // [num_blocks][64][D_qk]
+  const uint16_t* k;           // [num_blocks][64][D_qk] (bf16 KV cache)
   const uint16_t* v;           // [num_blocks][64][D_v] or NULL: V = the first D_v of each K row
+  const uint8_t* k8;           // FP8 KV cache instead of k, v: [num_blocks][64][D_qk] E4M3
+  const float* k8_scale;       //   codes and [num_blocks][64][ceil(D_qk/128)] tile scales;
+                               //   latent layout (V = the first D_v of each decoded row)
 };
 
 // The step for the rows listed (n_sel of them, row ids), in order:
@@ -299,6 +328,22 @@ int orc_decode_step(const OrcStep* p, const int32_t* rows, int n_sel, int32_t* i
     for (int64_t j = 0; j < counts[i]; ++j) idx[j] = (int32_t)hist[idx[j]];
     // gather the selected KV rows and attend
     const int64_t m = counts[i];
+    const uint16_t* qr = p->q + (int64_t)r * p->H_q * p->D_qk;
+    double* o_r = out + (int64_t)i * p->H_q * p->D_v;
+    double* lse_r = lse + (int64_t)i * p->H_q;
+    if (p->k8) {  // FP8 cache: decode each gathered row, V = its first D_v values
+      const int T = kv_tiles(p->D_qk);
+      std::vector<double> kd((size_t)m * p->D_qk), vd((size_t)m * p->D_v);
+      for (int64_t j = 0; j < m; ++j) {
+        const int64_t row = (int64_t)bt[idx[j] / B] * B + idx[j] % B;
+        orc_kv_fp8_decode(p->k8 + row * p->D_qk, p->k8_scale + row * T, 1, p->D_qk,
+                          &kd[(size_t)j * p->D_qk]);
+        for (int d = 0; d < p->D_v; ++d) vd[(size_t)j * p->D_v + d] = kd[(size_t)j * p->D_qk + d];
+      }
+      attention_values(qr, kd.data(), vd.data(), m, p->H_q, p->D_qk, p->D_v, p->scale, o_r, lse_r,
+                       threads);
+      continue;
+    }
     std::vector<uint16_t> kr((size_t)m * p->D_qk), vr((size_t)m * p->D_v);
     for (int64_t j = 0; j < m; ++j) {
       const int64_t row = (int64_t)bt[idx[j] / B] * B + idx[j] % B;
@@ -308,8 +353,7 @@ int orc_decode_step(const OrcStep* p, const int32_t* rows, int n_sel, int32_t* i
       else  // latent layout (reading): V is the first D_v elements of the K row
         std::memcpy(&vr[(size_t)j * p->D_v], p->k + row * p->D_qk, 2 * (size_t)p->D_v);
     }
-    orc_attention(p->q + (int64_t)r * p->H_q * p->D_qk, kr.data(), vr.data(), m, p->H_q, p->D_qk,
-                  p->D_v, p->scale, out + (int64_t)i * p->H_q * p->D_v, lse + (int64_t)i * p->H_q,
+    orc_attention(qr, kr.data(), vr.data(), m, p->H_q, p->D_qk, p->D_v, p->scale, o_r, lse_r,
                   threads);
   }
   return 0;

@@ -26,7 +26,7 @@ Array conventions (raw storage bits, exactly what the GPU reads):
 
 import numpy as np
 
-from .formats import bf16_to_f64, e4m3_to_f64, e8m0_to_f64
+from .formats import bf16_to_f64, e4m3_to_f64, e8m0_to_f64, kv_fp8_to_f64
 
 #: dims per shared scale of the MXFP8 indexer format (Day0 article, section 5.1)
 MX_GROUP = 32
@@ -154,9 +154,13 @@ def sparse_attn_row(q_bits, k_rows_bits, v_rows_bits, scale):
     With no rows selected the output is 0 and lse is -inf.
     Returns (o float64 [H_q, D_v], lse float64 [H_q]).
     """
-    q = bf16_to_f64(q_bits)
-    k = bf16_to_f64(k_rows_bits)
-    v = bf16_to_f64(v_rows_bits)
+    return sparse_attn_values(bf16_to_f64(q_bits), bf16_to_f64(k_rows_bits),
+                              bf16_to_f64(v_rows_bits), scale)
+
+
+def sparse_attn_values(q, k, v, scale):
+    """``sparse_attn_row`` on decoded values: q [H_q, D_qk], k [n, D_qk],
+    v [n, D_v], all binary64."""
     H_q, D_v = q.shape[0], v.shape[1]
     if k.shape[0] == 0:
         return np.zeros((H_q, D_v)), np.full(H_q, -np.inf)
@@ -224,7 +228,7 @@ def row_history(p, cand_row=None, cand_len=None):
 def decode_step(*, qI, w, kI_cache, q, k_cache, v_cache, block_table, seq_lens,
                 K, scale, D_v, row_seq=None, row_pos=None, rows=None,
                 keep_scores=True, qI_scale=None, kI_scale_cache=None,
-                cand=None, cand_len=None):
+                cand=None, cand_len=None, k_scale_cache=None):
     """The whole step for the chosen query rows (default: all rows).
 
     Row by row: index scores over positions 0..p_r, Top-K, gather of the
@@ -232,7 +236,11 @@ def decode_step(*, qI, w, kI_cache, q, k_cache, v_cache, block_table, seq_lens,
     H_I, D_I/32] and ``kI_scale_cache`` [num_blocks, 64, D_I/32] (paged like
     ``kI_cache``) the indexer is MXFP8.  With ``cand`` / ``cand_len`` each
     row scores only its candidate positions (row_history) and keeps the
-    Top-K among them; ``scores`` then holds one entry per candidate.
+    Top-K among them; ``scores`` then holds one entry per candidate.  With
+    ``k_scale_cache`` float32 [num_blocks, 64, ceil(D_qk / 128)] the KV cache
+    is FP8 (Day0 article, section 5.2): ``k_cache`` holds E4M3 codes
+    [num_blocks, 64, D_qk] in the latent layout (``v_cache`` None) and each
+    gathered row is decoded by ``kv_fp8_to_f64``.
     Returns a dict with
     ``scores`` (list of float32 arrays, or None), ``indices`` int32 [R, K],
     ``counts`` int64 [R], ``out`` float64 [R, H_q, D_v], ``lse`` float64
@@ -264,11 +272,17 @@ def decode_step(*, qI, w, kI_cache, q, k_cache, v_cache, block_table, seq_lens,
         idx[:n] = history[idx[:n]]
         chosen = idx[:n]
         k_rows = gather_positions(k_cache, block_table[b], chosen)
-        if v_cache is None:
-            v_rows = k_rows[:, :D_v]
+        if k_scale_cache is not None:
+            if v_cache is not None:
+                raise ValueError("the FP8 KV cache takes the latent layout")
+            k_vals = kv_fp8_to_f64(k_rows, gather_positions(k_scale_cache, block_table[b], chosen))
+            out[i], lse[i] = sparse_attn_values(bf16_to_f64(q[r]), k_vals, k_vals[:, :D_v], scale)
         else:
-            v_rows = gather_positions(v_cache, block_table[b], chosen)
-        out[i], lse[i] = sparse_attn_row(q[r], k_rows, v_rows, scale)
+            if v_cache is None:
+                v_rows = k_rows[:, :D_v]
+            else:
+                v_rows = gather_positions(v_cache, block_table[b], chosen)
+            out[i], lse[i] = sparse_attn_row(q[r], k_rows, v_rows, scale)
         indices[i], counts[i] = idx, n
         if keep_scores:
             scores.append(sc)

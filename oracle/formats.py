@@ -13,6 +13,11 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
   one shared scale per group of 32 values).  The page does not state the
   encoding; the reading taken is the OCP microscaling one: byte e stands for
   2**(e - 127), and e = 255 is NaN.
+* The FP8 KV cache (Day0 article, section 5.2: FP8 storage quantised per
+  token, per head, in tiles of 128 elements).  Readings: the codes are E4M3;
+  each tile carries one binary32 scale and an element's value is its code's
+  value times its tile's scale; a row of D elements has ceil(D / 128) tiles,
+  the last one shorter when 128 does not divide D (576 = 4 * 128 + 64).
 """
 
 import numpy as np
@@ -51,3 +56,25 @@ def bf16_to_f64(bits) -> np.ndarray:
     """Decode an array of bfloat16 bit patterns (uint16) to binary64 (exact)."""
     wide = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return wide.view(np.float32).astype(np.float64)
+
+
+#: elements per scale tile of the FP8 KV cache (Day0 article, section 5.2)
+KV_TILE = 128
+
+
+def kv_tiles(dim: int) -> int:
+    """Scale tiles of an FP8 KV row of ``dim`` elements."""
+    return (int(dim) + KV_TILE - 1) // KV_TILE
+
+
+def kv_fp8_to_f64(codes, scales) -> np.ndarray:
+    """Decode FP8 KV rows to binary64 (exact): codes uint8 [..., D] (E4M3),
+    scales float32 [..., kv_tiles(D)]; element d is e4m3(code[d]) times the
+    scale of tile d // 128."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    d = codes.shape[-1]
+    if scales.shape[-1] != kv_tiles(d):
+        raise ValueError("one scale per tile of 128 elements")
+    per_elem = np.repeat(scales, KV_TILE, axis=-1)[..., :d]
+    return e4m3_to_f64(codes) * per_elem

@@ -26,7 +26,7 @@ def run_oracle(arr, keep_scores=True, impl=None, rows=None):
         seq_lens=arr["seq_lens"], K=arr["K"], scale=arr["scale"], D_v=arr["D_v"],
         row_seq=arr["row_seq"], row_pos=arr["row_pos"], keep_scores=keep_scores, rows=rows,
         qI_scale=arr.get("qI_scale"), kI_scale_cache=arr.get("kI_scale_cache"),
-        cand=arr.get("cand"), cand_len=arr.get("cand_len"))
+        cand=arr.get("cand"), cand_len=arr.get("cand_len"), k_scale_cache=arr.get("k_scale_cache"))
     if impl is oracle.cpp:
         kw["threads"] = HOST_THREADS
     return impl.decode_step(**kw)

@@ -407,6 +407,64 @@ def test_dense_causal_matches_torch_sdpa():
     assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
 
 
+# ------------------------------------------------------------ FP8 KV cache
+# Day0 article, section 5.2: FP8 KV rows quantised per token in tiles of 128
+# elements, one scale per tile; 576 = 4 * 128 + 64 gives a shorter last tile.
+
+_KV_TILES = [(0, 128), (128, 256), (256, 384), (384, 512), (512, 576)]
+
+
+def test_kv_fp8_decode_closed_forms(orc):
+    D = 576
+    codes = np.zeros((2, D), np.uint8)
+    codes[0, :] = 0x38                      # 1.0 everywhere
+    codes[1, 0], codes[1, 127] = 0x7E, 0xB8    # 448, -1.0: first and last of tile 0
+    codes[1, 128], codes[1, 511] = 0x40, 0x01  # 2.0 (tile 1), 2**-9 (last of tile 3)
+    codes[1, 512], codes[1, 575] = 0x3C, 0xC0  # 1.5, -2.0: first and last of the 64-wide tile
+    scales = np.array([[1, 2, 4, 8, 16], [0.5, 3.0, 0.25, 1024.0, 0.125]], np.float32)
+    got = orc.kv_fp8_to_f64(codes, scales)
+    row0 = np.concatenate([np.full(hi - lo, 2.0 ** t) for t, (lo, hi) in enumerate(_KV_TILES)])
+    assert np.array_equal(got[0], row0)
+    row1 = np.zeros(D)
+    row1[0], row1[127], row1[128], row1[511] = 224.0, -0.5, 6.0, 2.0
+    row1[512], row1[575] = 0.1875, -0.25
+    assert np.array_equal(got[1], row1)
+
+
+def test_kv_fp8_scale_of_one_tile_moves_only_its_elements(orc):
+    rng = np.random.default_rng(13)
+    codes = rng.integers(0, 0x7E, size=(4, 576)).astype(np.uint8)   # finite codes
+    codes[:, ::2] |= 0x80                                             # and negative ones
+    sc = rng.uniform(0.5, 2.0, size=(4, 5)).astype(np.float32)
+    base = orc.kv_fp8_to_f64(codes, sc)
+    for t, (lo, hi) in enumerate(_KV_TILES):
+        sc2 = sc.copy()
+        sc2[:, t] *= 2
+        got = orc.kv_fp8_to_f64(codes, sc2)
+        assert np.array_equal(got[:, lo:hi], 2 * base[:, lo:hi])
+        rest = np.ones(576, bool)
+        rest[lo:hi] = False
+        assert np.array_equal(got[:, rest], base[:, rest])
+
+
+def test_kv_fp8_step_equals_the_bf16_step_on_the_same_values(orc):
+    # power-of-two tile scales keep every decoded value exact in bfloat16:
+    # the FP8 step must then match the already pinned bf16 step bit for bit
+    wl = small_workload("f", lengths=[5, 300, 2100], mode="int", K=128, kv_fmt="fp8",
+                        table="shuffled")
+    arr = oracle_arrays(make_batch(wl, seed=11))
+    rng = np.random.default_rng(12)
+    sc = np.exp2(rng.integers(-8, 3, size=arr["k_scale_cache"].shape)).astype(np.float32)
+    vals = orc.kv_fp8_to_f64(arr["k_cache"], sc)
+    f32 = vals.astype(np.float32)
+    bits = (f32.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(oracle.bf16_to_f64(bits), vals)
+    r8 = run_oracle(dict(arr, k_scale_cache=sc), impl=orc)
+    r16 = run_oracle(dict(arr, k_cache=bits, k_scale_cache=None), impl=orc)
+    assert np.array_equal(r8["indices"], r16["indices"])
+    assert np.array_equal(r8["out"], r16["out"]) and np.array_equal(r8["lse"], r16["lse"])
+
+
 # ------------------------------------------------------------- end to end
 
 def _tiny(**kw):

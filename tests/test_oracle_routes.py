@@ -28,6 +28,8 @@ CASES = [
     small_workload("prefill", lengths=[3000], prefill_rows=5, seed=15, K=256),
     small_workload("separate_v", lengths=[100, 3000], seed=16, K=64, latent=False, D_qk=64,
                    D_v=64, H_q=8, table="shuffled", mode="int"),
+    small_workload("fp8_kv", lengths=[100, 3000], seed=18, K=256, kv_fmt="fp8", mode="int",
+                   table="shuffled"),
 ]
 
 

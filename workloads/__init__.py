@@ -12,7 +12,7 @@ DeepSeek-V4.1-Flash post); none of those suites' items is reproduced.
 """
 
 from .configs import Workload, CONFIGS, BENCH_WORKLOAD, small_workload
-from .gen import Batch, make_batch, oracle_arrays, row_positions
+from .gen import Batch, make_batch, oracle_arrays, row_positions, kv_fp8_split, kv_scale_rows
 
-__all__ = ["Workload", "CONFIGS", "BENCH_WORKLOAD", "small_workload",
+__all__ = ["Workload", "CONFIGS", "BENCH_WORKLOAD", "small_workload", "kv_fp8_split", "kv_scale_rows",
            "Batch", "make_batch", "oracle_arrays", "row_positions"]

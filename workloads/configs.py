@@ -36,6 +36,9 @@ class Workload:
     # positions (a seeded uniform subset, ascending; rows shorter than n_cand
     # take every position); 0: the whole history
     n_cand: int = 0
+    # KV cache: "bf16" rows, or "fp8": E4M3 codes with one float32 scale per
+    # tile of 128 elements of each row (latent layout only)
+    kv_fmt: str = "bf16"
 
     @property
     def rows(self) -> int:

@@ -36,7 +36,9 @@ class Batch:
                              # D_I], the 64 rows' D_I/32 E8M0 scales each, in row order,
                              # in the last two D_I-byte rows of the block)
     q: torch.Tensor          # bfloat16 [rows, H_q, D_qk]
-    kv: torch.Tensor         # bfloat16 [num_blocks, 64, D_qk]
+    kv: torch.Tensor         # bfloat16 [num_blocks, 64, D_qk] (FP8 KV: uint8 [num_blocks,
+                             # 64 + KV_SCALE_ROWS, D_qk], E4M3 code rows, then the 64 rows'
+                             # float32 tile scales, row after row, from row 64 on)
     v: Optional[torch.Tensor] = None   # bfloat16 [num_blocks, 64, D_v] (separate V)
     qI_scale: Optional[torch.Tensor] = None  # MXFP8: uint8 E8M0 [rows, H_I, D_I/32]
     cand: Optional[torch.Tensor] = None      # int32 [rows, n_cand]: candidate positions, -1 past
@@ -102,6 +104,53 @@ def _mx_codes_scales(shape, mode, gen, device):
             y = (x * torch.exp2(-e)).clamp_(-448.0, 448.0)
             flat_c[i:j] = y.to(torch.float8_e4m3fn).view(torch.uint8).view(n, D)
             flat_s[i:j] = (e.view(n, -1) + 127.0).to(torch.int32).to(torch.uint8)
+    return codes, scales
+
+
+KV_TILE = 128
+
+
+def kv_scale_rows(D):
+    """Rows of D bytes after a block's 64 FP8 KV code rows that hold the 64
+    rows' float32 tile scales (4 * ceil(D / 128) bytes per row)."""
+    tiles = (D + KV_TILE - 1) // KV_TILE
+    return (BLOCK * 4 * tiles + D - 1) // D
+
+
+def _kv_fp8_pages(num_blocks, D, gen, device):
+    """FP8 KV pages of N(0, 1) rows: every tile of 128 elements (the last one
+    shorter when 128 does not divide D) is scaled by amax / 448 and rounded
+    to E4M3; the float32 scales follow the block's code rows."""
+    tiles = (D + KV_TILE - 1) // KV_TILE
+    srows = kv_scale_rows(D)
+    pages = torch.zeros((num_blocks, BLOCK + srows, D), dtype=torch.uint8, device=device)
+    step = max(1, _CHUNK // (BLOCK * D))
+    for i in range(0, num_blocks, step):
+        j = min(num_blocks, i + step)
+        n = j - i
+        x = torch.randn(n, BLOCK, D, generator=gen, device=device, dtype=torch.float32)
+        pad = torch.zeros(n, BLOCK, tiles * KV_TILE, device=device, dtype=torch.float32)
+        pad[..., :D] = x
+        t = pad.view(n, BLOCK, tiles, KV_TILE)
+        scale = (t.abs().amax(dim=3) / 448.0).clamp_min(2.0 ** -100)      # [n, 64, tiles]
+        codes = (t / scale[..., None]).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
+        pages[i:j, :BLOCK] = codes.view(torch.uint8).view(n, BLOCK, tiles * KV_TILE)[..., :D]
+        sb = scale.contiguous().view(torch.uint8).view(n, BLOCK * 4 * tiles)
+        pages[i:j, BLOCK:].view(n, srows * D)[:, :BLOCK * 4 * tiles] = sb
+    return pages
+
+
+def kv_fp8_split(pages, D):
+    """(codes uint8 [..., 64, D], scales float32 [..., 64, ceil(D / 128)]) of
+    FP8 KV pages laid out by ``_kv_fp8_pages`` (any leading dims)."""
+    tiles = (D + KV_TILE - 1) // KV_TILE
+    lead = pages.shape[:-2]
+    codes = pages[..., :BLOCK, :]
+    tail = pages[..., BLOCK:, :].reshape(*lead, -1)[..., :BLOCK * 4 * tiles]
+    if isinstance(tail, torch.Tensor):
+        scales = tail.contiguous().view(torch.float32).view(*lead, BLOCK, tiles)
+    else:
+        scales = np.ascontiguousarray(tail).view(np.float32).reshape(*lead, BLOCK, tiles)
     return codes, scales
 
 
@@ -188,7 +237,12 @@ def make_batch(wl: Workload, device="cpu", seed=None, mode=None, table=None,
         w = _weights((R, wl.H_I), mode, gd, device)
         kI = _fp8_codes((num_blocks, BLOCK, wl.D_I), mode, gd, device)
     q = _bf16_normal((R, wl.H_q, wl.D_qk), gd, device)
-    kv = _bf16_normal((num_blocks, BLOCK, wl.D_qk), gd, device)
+    if wl.kv_fmt == "fp8":
+        if not wl.latent:
+            raise ValueError("the FP8 KV cache takes the latent layout")
+        kv = _kv_fp8_pages(num_blocks, wl.D_qk, gd, device)
+    else:
+        kv = _bf16_normal((num_blocks, BLOCK, wl.D_qk), gd, device)
     v = None if wl.latent else _bf16_normal((num_blocks, BLOCK, wl.D_v), gd, device)
 
     cand = cand_len = None
@@ -221,6 +275,12 @@ def _np(t):
     return t.detach().cpu().numpy()
 
 
+def _kv_host(kv):
+    if kv.dtype == torch.uint8:  # FP8 KV pages
+        return _np(kv)
+    return _np(kv.view(torch.int16)).view(np.uint16)
+
+
 def oracle_arrays(batch: Batch, rows=None) -> dict:
     """The batch as plain numpy arrays of raw storage bits.
 
@@ -234,7 +294,7 @@ def oracle_arrays(batch: Batch, rows=None) -> dict:
     if rows is None:
         rows = np.arange(batch.rows)
         bt = _np(batch.block_table)
-        kI, kv = _np(batch.kI), _np(batch.kv.view(torch.int16)).view(np.uint16)
+        kI, kv = _np(batch.kI), _kv_host(batch.kv)
         v = None if batch.v is None else _np(batch.v.view(torch.int16)).view(np.uint16)
         seqs = None
     else:
@@ -248,7 +308,7 @@ def oracle_arrays(batch: Batch, rows=None) -> dict:
         ids_t = torch.cat(ids)
         idx_dev = ids_t.to(batch.kI.device)
         kI = _np(batch.kI.index_select(0, idx_dev))
-        kv = _np(batch.kv.index_select(0, idx_dev).view(torch.int16)).view(np.uint16)
+        kv = _kv_host(batch.kv.index_select(0, idx_dev))
         v = None if batch.v is None else \
             _np(batch.v.index_select(0, idx_dev).view(torch.int16)).view(np.uint16)
         bt = np.full(_np(bt_full).shape, -1, dtype=np.int32)
@@ -258,6 +318,10 @@ def oracle_arrays(batch: Batch, rows=None) -> dict:
             bt[b, :nb] = np.arange(off, off + nb, dtype=np.int32)
             off += nb
     sel = torch.as_tensor(rows, dtype=torch.int64).to(batch.qI.device)
+    k_scale = None
+    if wl.kv_fmt == "fp8":  # FP8 KV: E4M3 code rows and their float32 tile scales
+        kv, k_scale = kv_fp8_split(kv, wl.D_qk)
+        kv = np.ascontiguousarray(kv)
     kI_scale = None
     if batch.qI_scale is not None:  # MXFP8: split each block into code rows and row scales
         kI_scale = np.ascontiguousarray(kI[:, BLOCK:]).reshape(kI.shape[0], BLOCK, -1)
@@ -270,7 +334,7 @@ def oracle_arrays(batch: Batch, rows=None) -> dict:
         "qI": _np(batch.qI.index_select(0, sel)),
         "w": _np(batch.w.index_select(0, sel)),
         "q": _np(batch.q.index_select(0, sel).view(torch.int16)).view(np.uint16),
-        "kI_cache": kI, "k_cache": kv, "v_cache": v,
+        "kI_cache": kI, "k_cache": kv, "v_cache": v, "k_scale_cache": k_scale,
         "block_table": bt, "seq_lens": np.asarray(batch.lengths, np.int32),
         "row_seq": np.asarray(batch.row_seq_host, np.int64)[rows],
         "row_pos": np.asarray(batch.row_pos_host, np.int64)[rows],
