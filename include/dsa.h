@@ -62,7 +62,7 @@ extern "C" {
 #define DSA_API
 #endif
 
-#define DSA_ABI_VERSION 6
+#define DSA_ABI_VERSION 7
 #define DSA_BLOCK_SIZE 64
 #define DSA_MAX_ATTN_K 16384 /* largest K of dsa_sparse_attn / dsa_decode_step */
 #define DSA_STATIC_SCRATCH_BYTES (64u << 20) /* scratch of dsa_decode_step_static, per GPU */
@@ -118,6 +118,7 @@ typedef struct {
   const int32_t* cand_len;    /* [num_rows] valid leading entries of each list, clamped
                                  to 0 .. n_cand; entries past it are not read           */
   int32_t n_cand;             /* row length of cand (>= 1 with cand)                    */
+  int32_t kv_format;          /* DSA_KV_BF16 or DSA_KV_FP8 (see dsa_sparse_attn)        */
 } dsa_problem;
 
 /* indexer operand formats (dsa_problem.indexer_format) */
@@ -125,6 +126,13 @@ enum {
   DSA_INDEXER_E4M3 = 0,  /* unscaled E4M3 codes                                         */
   DSA_INDEXER_MXFP8 = 1  /* E4M3 codes with one E8M0 scale per group of 32 dims (Day0,
                             section 5.1); see dsa_indexer_scores                        */
+};
+
+/* KV cache formats (dsa_problem.kv_format) */
+enum {
+  DSA_KV_BF16 = 0, /* bf16 rows                                                          */
+  DSA_KV_FP8 = 1   /* E4M3 rows with one float32 scale per tile of 128 elements (Day0,
+                      section 5.2); latent 576/512 layout only; see dsa_sparse_attn     */
 };
 
 /* which call dsa_workspace_size() sizes */
@@ -213,6 +221,17 @@ DSA_API int dsa_topk(const dsa_problem* p, const float* scores, int64_t ld_score
  *   indices  int32 [num_rows][K]
  *   out      bf16 [num_rows][H_q][D_v]; lse float32 [num_rows][H_q] or NULL
  * Products are bf16 x bf16 with float32 accumulation; softmax in float32.
+ *
+ * With kv_format = DSA_KV_FP8 (Day0 article, section 5.2: FP8 KV quantised
+ * per token in tiles of 128 elements), D_qk = 576, D_v = 512, and k and v
+ * are the same descriptor (the latent layout, else DSA_ERR_INVALID).  A row
+ * holds 576 E4M3 (OCP FN) codes at row_stride; the 64 rows of a block are
+ * followed by their float32 tile scales, row i's five at
+ * b * block_stride + 64 * row_stride + 20 * i (block_stride >= 64 *
+ * row_stride + 1280, else DSA_ERR_INVALID).  Element d of a row has the
+ * value code[d] * scale[d / 128]: four tiles of 128 and a last one of 64.
+ * The kernel decodes each gathered element to bf16 (rounded to nearest
+ * even) before the bf16 products.  NaN codes are not valid input.
  */
 DSA_API int dsa_sparse_attn(const dsa_problem* p, const uint16_t* q, dsa_paged k, dsa_paged v,
                     const int32_t* indices, uint16_t* out, float* lse, void* ws,

@@ -27,9 +27,11 @@ DSA_OP_TOPK = 1
 DSA_OP_SPARSE_ATTN = 2
 DSA_OP_DECODE_STEP = 3
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 DSA_INDEXER_E4M3 = 0
 DSA_INDEXER_MXFP8 = 1
+DSA_KV_BF16 = 0
+DSA_KV_FP8 = 1
 BLOCK = 64
 
 #: every symbol include/dsa.h declares
@@ -52,7 +54,8 @@ class DsaProblem(ctypes.Structure):
                 ("D_qk", ctypes.c_int32), ("D_v", ctypes.c_int32), ("K", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("indexer_format", ctypes.c_int32),
                 ("qI_scale", ctypes.c_void_p),
-                ("cand", ctypes.c_void_p), ("cand_len", ctypes.c_void_p), ("n_cand", ctypes.c_int32)]
+                ("cand", ctypes.c_void_p), ("cand_len", ctypes.c_void_p), ("n_cand", ctypes.c_int32),
+                ("kv_format", ctypes.c_int32)]
 
 
 class DsaError(RuntimeError):
@@ -116,22 +119,26 @@ def _stream(stream):
 def paged(cache: torch.Tensor) -> DsaPaged:
     """Descriptor of a [num_blocks, 64, ...] cache tensor (any row stride).
     An MXFP8 index-key cache is [num_blocks, 66, D_I]: two more D_I-byte rows
-    per block hold the 64 rows' scales."""
-    if cache.dim() < 3 or cache.shape[1] not in (BLOCK, BLOCK + 2):
-        raise ValueError("paged cache must be [num_blocks, 64, row] ([num_blocks, 66, D_I] "
-                         "for MXFP8 index keys)")
+    per block hold the 64 rows' scales.  An FP8 KV cache is uint8
+    [num_blocks, 64 + n, D_qk]: the rows after the 64 code rows hold the 64
+    rows' float32 tile scales."""
+    if cache.dim() < 3 or cache.shape[1] < BLOCK or (cache.shape[1] > BLOCK and
+                                                     cache.dtype != torch.uint8):
+        raise ValueError("paged cache must be [num_blocks, 64, row] (uint8 [num_blocks, 64 + n, "
+                         "row] with the block's scales in the extra rows)")
     es = cache.element_size()
     return DsaPaged(cache.data_ptr(), cache.stride(0) * es, cache.stride(1) * es, cache.shape[0])
 
 
 def problem(*, seq_lens, block_table, num_rows=None, row_seq=None, row_pos=None, H_I=64,
             D_I=128, H_q=128, D_qk=576, D_v=512, K=2048, scale=576 ** -0.5,
-            qI_scale=None, cand=None, cand_len=None) -> DsaProblem:
+            qI_scale=None, cand=None, cand_len=None, kv_format=DSA_KV_BF16) -> DsaProblem:
     """Problem descriptor; device tensors are referenced, not copied.  With
     ``qI_scale`` (uint8 E8M0 [rows, H_I, D_I/32]) the indexer runs in MXFP8
     format and each index-key block carries its rows' scales after the code rows.
     With ``cand`` (int32 [rows, n_cand], ascending positions) and ``cand_len``
-    (int32 [rows]) each row scores only its candidate positions."""
+    (int32 [rows]) each row scores only its candidate positions.  ``kv_format``
+    DSA_KV_FP8: the KV cache holds E4M3 rows with float32 tile scales."""
     num_seqs = int(seq_lens.shape[0])
     if num_rows is None:
         num_rows = int(row_seq.shape[0]) if row_seq is not None else num_seqs
@@ -144,7 +151,7 @@ def problem(*, seq_lens, block_table, num_rows=None, row_seq=None, row_pos=None,
                    None if qI_scale is None else qI_scale.data_ptr(),
                    None if cand is None else cand.data_ptr(),
                    None if cand_len is None else cand_len.data_ptr(),
-                   0 if cand is None else int(cand.shape[1]))
+                   0 if cand is None else int(cand.shape[1]), int(kv_format))
     p._keep = (seq_lens, block_table, row_seq, row_pos, qI_scale, cand, cand_len)  # keep alive
     return p
 
@@ -158,7 +165,8 @@ def problem_for_batch(batch) -> DsaProblem:
                    row_pos=batch.row_pos, H_I=wl.H_I, D_I=wl.D_I, H_q=wl.H_q, D_qk=wl.D_qk,
                    D_v=wl.D_v, K=wl.K, scale=wl.scale,
                    qI_scale=getattr(batch, "qI_scale", None), cand=getattr(batch, "cand", None),
-                   cand_len=getattr(batch, "cand_len", None))
+                   cand_len=getattr(batch, "cand_len", None),
+                   kv_format=DSA_KV_FP8 if getattr(wl, "kv_fmt", "bf16") == "fp8" else DSA_KV_BF16)
 
 
 def dsa_workspace_size(prob: DsaProblem, op: int) -> int:

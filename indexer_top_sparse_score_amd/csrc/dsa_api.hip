@@ -60,6 +60,8 @@ int check_attn_shape(const dsa_problem* p) {
   const bool small = p->D_qk == 64 && p->D_v == 64;
   const bool mla = p->D_qk == 576 && p->D_v == 512;
   if (!small && !mla) return DSA_ERR_UNSUPPORTED;
+  if (p->kv_format != DSA_KV_BF16 && p->kv_format != DSA_KV_FP8) return DSA_ERR_INVALID;
+  if (p->kv_format == DSA_KV_FP8 && !mla) return DSA_ERR_UNSUPPORTED;  // latent 576/512 only
   return DSA_OK;
 }
 
@@ -161,6 +163,17 @@ int check_attn_args(const dsa_problem* p, const uint16_t* q, const dsa_paged& k,
   if (st != DSA_OK) return st;
   if (!q || !out) return DSA_ERR_INVALID;
   if (!aligned(q, 16) || !aligned(out, 16) || (lse && !aligned(lse, 4))) return DSA_ERR_INVALID;
+  if (p->kv_format == DSA_KV_FP8) {
+    // E4M3 rows of D_qk codes serving as K and V (the latent layout), each
+    // block's 64 rows of float32 tile scales after its code rows
+    if (p->D_qk != 576 || p->D_v != 512) return DSA_ERR_UNSUPPORTED;
+    if (!is_latent(k, v)) return DSA_ERR_INVALID;
+    if ((st = check_paged(k, p->D_qk)) != DSA_OK) return st;
+    const int64_t tiles = (p->D_qk + 127) / 128;
+    if (k.block_stride < 64 * k.row_stride + 64 * 4 * tiles) return DSA_ERR_INVALID;
+    return DSA_OK;
+  }
+  if (p->kv_format != DSA_KV_BF16) return DSA_ERR_INVALID;
   if ((st = check_paged(k, 2 * (int64_t)p->D_qk)) != DSA_OK) return st;
   if ((st = check_paged(v, 2 * (int64_t)p->D_v)) != DSA_OK) return st;
   // the latent kernel keeps each gathered row's offset in 32 bits of 16-byte
@@ -168,6 +181,12 @@ int check_attn_args(const dsa_problem* p, const uint16_t* q, const dsa_paged& k,
   if (is_latent(k, v) && (int64_t)k.num_blocks * k.block_stride > (int64_t(1) << 36))
     return DSA_ERR_UNSUPPORTED;
   return DSA_OK;
+}
+
+// The layout the attention kernels see as "latent" (bf16 rows shared by K
+// and V, gathered by DMA); an FP8 cache is staged like a separate V cache.
+bool dma_latent(const dsa_problem* p, const dsa_paged& k, const dsa_paged& v) {
+  return is_latent(k, v) && p->kv_format != DSA_KV_FP8;
 }
 
 AttnLaunch attn_launch(const dsa_problem* p, const uint16_t* q, dsa_paged k, dsa_paged v,
@@ -178,6 +197,7 @@ AttnLaunch attn_launch(const dsa_problem* p, const uint16_t* q, dsa_paged k, dsa
   a.k = k;
   a.v = v;
   a.latent = is_latent(k, v);
+  a.kv8 = p->kv_format == DSA_KV_FP8;
   a.indices = nullptr;
   a.indices_row_offset = 0;
   a.rowoff = nullptr;
@@ -226,7 +246,7 @@ int decode_run(const dsa_problem* p, const uint8_t* qI, const float* w, dsa_page
   const int64_t ld = slab_ld(p);
   const Summary sum = needs_summary(p) ? summary_carve(base + d.sum_off, d.rp)
                                        : Summary{nullptr, nullptr, nullptr};
-  const bool use_rowoff = attn_uses_rowoff(p->D_qk, p->D_v, is_latent(k, v));
+  const bool use_rowoff = attn_uses_rowoff(p->D_qk, p->D_v, dma_latent(p, k, v));
   int64_t* roff = reinterpret_cast<int64_t*>(base + d.roff_off);
 
   // Four launches per pass of rows: indexer scan (scores and summaries),
@@ -285,7 +305,7 @@ int decode_run(const dsa_problem* p, const uint8_t* qI, const float* w, dsa_page
     aa.row_begin = row0;
     aa.num_rows = nr;
     // the workspace holds partials for the larger of the two layouts' counts
-    aa.n_chunks = attn_chunks(d.rp, p->H_q, p->D_qk, p->K, aa.latent);
+    aa.n_chunks = attn_chunks(d.rp, p->H_q, p->D_qk, p->K, aa.latent && !aa.kv8);
     aa.partial = aa.n_chunks > 1 ? static_cast<void*>(base + d.part_off) : nullptr;
     if ((st = status_of(launch_sparse_attn(aa, s, stage(2), stage(3)))) != DSA_OK) return st;
   }
@@ -448,7 +468,7 @@ int dsa_sparse_attn(const dsa_problem* p, const uint16_t* q, dsa_paged k, dsa_pa
   if (p->num_rows == 0) return DSA_OK;
   AttnLaunch a = attn_launch(p, q, k, v, out, lse, static_cast<uint32_t*>(ws));
   a.indices = indices;
-  a.n_chunks = attn_chunks(p->num_rows, p->H_q, p->D_qk, p->K, a.latent);
+  a.n_chunks = attn_chunks(p->num_rows, p->H_q, p->D_qk, p->K, a.latent && !a.kv8);
   a.partial = a.n_chunks > 1
                   ? static_cast<void*>(static_cast<char*>(ws) + kHeader)
                   : nullptr;

@@ -374,6 +374,7 @@ struct AttnLaunch {
   const uint16_t* q;
   dsa_paged k, v;
   bool latent;  // v aliases k (same base and strides)
+  bool kv8;     // the (latent) cache holds E4M3 rows with tile scales (DSA_KV_FP8)
   // The selection: indices [.][K] (row row_begin + i at row indices_row_offset
   // + i); or, for the latent layout, the kept rows' byte offsets in the KV
   // cache as the Top-K wrote them (rowoff [num_rows][K], -1 = absent),

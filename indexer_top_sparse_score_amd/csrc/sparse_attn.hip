@@ -227,19 +227,63 @@ struct Cfg {
   static constexpr int kVtElems = DV * VP;
 };
 
-template <class C>
+// A staging job's raw data: 8 bf16 elements (16 bytes), or with KV8 their 8
+// E4M3 codes (8 bytes) and the float32 scale of their tile.
+template <bool KV8>
+struct Raw8 {
+  uint4 x;
+};
+template <>
+struct Raw8<true> {
+  uint2 x;
+  float s;
+};
+template <class C, bool KV8>
 struct Staged {
-  uint4 v[C::kVJ > 0 ? C::kVJ : 1][4];
-  uint4 k[C::kKJ > 0 ? C::kKJ : 1];
+  Raw8<KV8> v[C::kVJ > 0 ? C::kVJ : 1][4];
+  Raw8<KV8> k[C::kKJ > 0 ? C::kKJ : 1];
 };
 
-template <int DQK, int DV, bool LATENT, int NW>
+// Eight elements as packed bf16: raw bf16 as they are; KV8 codes decoded
+// (the hardware conversion is the OCP E4M3 one), times the tile's scale and
+// rounded to bf16.  `keep` false gives zeros (an absent row).
+__device__ __forceinline__ uint4 raw_bf16x8(const Raw8<false>& r, bool keep) {
+  return keep_or_zero(r.x, keep);
+}
+__device__ __forceinline__ uint4 raw_bf16x8(const Raw8<true>& r, bool keep) {
+  float f[8];
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const int word = (int)(w ? r.x.y : r.x.x);
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+    f[4 * w + 0] = lo[0];
+    f[4 * w + 1] = lo[1];
+    f[4 * w + 2] = hi[0];
+    f[4 * w + 3] = hi[1];
+  }
+  const float sc = keep ? r.s : 0.0f;
+  return uint4{pack2(f[0] * sc, f[1] * sc), pack2(f[2] * sc, f[3] * sc),
+               pack2(f[4] * sc, f[5] * sc), pack2(f[6] * sc, f[7] * sc)};
+}
+
+// KV8: the latent cache holds E4M3 code rows, and a block keeps its 64 rows'
+// float32 tile scales after its code rows (row i's kKvTiles scales at
+// 64 * row_stride + 4 * kKvTiles * i); element d belongs to tile d / 128.
+constexpr int kKvTile = 128;
+constexpr int kKvDim = 576;  // the FP8 cache's rows: the 576-wide latent
+constexpr int kKvTiles = (kKvDim + kKvTile - 1) / kKvTile;  // 5
+
+template <int DQK, int DV, bool LATENT, int NW, bool KV8 = false>
 __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, AttnGrid g) {
   using C = Cfg<DQK, DV, LATENT, NW>;
+  static_assert(!KV8 || (LATENT && DQK == kKvDim && DV == 512), "FP8 KV: latent 576/512");
+  constexpr int kEB = KV8 ? 1 : 2;  // bytes per stored element
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::kKsElems];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][C::kVtElems];
   __shared__ int64_t koff[kMaxChunk];
-  __shared__ int64_t voff[LATENT ? 1 : kMaxChunk];
+  // separate V: V row offsets; KV8: tile scale offsets of the rows
+  __shared__ int64_t voff[(LATENT && !KV8) ? 1 : kMaxChunk];
 
   int unit, hg;
   if (!decode_wg(g, unit, hg)) return;
@@ -272,7 +316,9 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
           const bool okv = LATENT || (phys >= 0 && (int64_t)phys < a.v.num_blocks);
           if (okk && okv) {
             ko = (int64_t)phys * a.k.block_stride + (int64_t)(idx & 63) * a.k.row_stride;
-            vo = (int64_t)phys * a.v.block_stride + (int64_t)(idx & 63) * a.v.row_stride;
+            vo = KV8 ? (int64_t)phys * a.k.block_stride + 64 * a.k.row_stride +
+                           (int64_t)(idx & 63) * (4 * kKvTiles)
+                     : (int64_t)phys * a.v.block_stride + (int64_t)(idx & 63) * a.v.row_stride;
           } else {
             report(a.err, DSA_DEVERR_BLOCK);
           }
@@ -281,7 +327,7 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
         }
       }
       koff[i] = ko;
-      if (!LATENT) voff[i] = vo;
+      if (!LATENT || KV8) voff[i] = vo;
     }
   }
 
@@ -306,7 +352,19 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
   // Loads are unconditional (an absent row reads row 0 of block 0, which
   // always exists) and raw; rows that are absent are zeroed only when they
   // land, so nothing waits on the loads while the previous sub-block runs.
-  auto issue = [&](int sb, Staged<C>& st) {
+  // (KV8: an absent row reads the scales of row 0 of block 0 too; the
+  // scale area of a block lies inside it, since block_stride >= 64 *
+  // row_stride + 4 * kKvTiles * 64)
+  const int64_t scale0 = 64 * a.k.row_stride;
+  auto load8 = [&](Raw8<KV8>& r, const uint8_t* p, int64_t soff, int d0) {
+    if constexpr (KV8) {
+      r.x = *reinterpret_cast<const uint2*>(p);
+      r.s = *reinterpret_cast<const float*>(kbase + (soff >= 0 ? soff : scale0) + 4 * (d0 / kKvTile));
+    } else {
+      r.x = *reinterpret_cast<const uint4*>(p);
+    }
+  };
+  auto issue = [&](int sb, Staged<C, KV8>& st) {
     const int base = sb * kSB;
 #pragma unroll
     for (int i = 0; i < C::kVJ; ++i) {
@@ -315,8 +373,8 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t off = (LATENT ? koff : voff)[base + 4 * kq + j];
-        st.v[i][j] = *reinterpret_cast<const uint4*>((LATENT ? kbase : vbase) +
-                                                     (off >= 0 ? off : 0) + dg * 16);
+        load8(st.v[i][j], (LATENT ? kbase : vbase) + (off >= 0 ? off : 0) + dg * 8 * kEB,
+              KV8 ? voff[base + 4 * kq + j] : 0, 8 * dg);
       }
     }
 #pragma unroll
@@ -325,10 +383,10 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
       const int key = (job / C::kKPieces) % kSB, piece = job % C::kKPieces;
       const int64_t off = koff[base + key];
       const int d0 = (LATENT ? DV : 0) + 8 * piece;
-      st.k[i] = *reinterpret_cast<const uint4*>(kbase + (off >= 0 ? off : 0) + d0 * 2);
+      load8(st.k[i], kbase + (off >= 0 ? off : 0) + d0 * kEB, KV8 ? voff[base + key] : 0, d0);
     }
   };
-  auto land = [&](Staged<C>& st, int sb, int buf) {
+  auto land = [&](Staged<C, KV8>& st, int sb, int buf) {
     const int base = sb * kSB;
     uint16_t* ks = Ks[buf];
     uint16_t* vt = Vt[buf];
@@ -338,21 +396,22 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
       // every thread owns a job when the jobs divide evenly: no guard
       const bool mine = C::kVJ * C::kThreads == C::kVJobs || job < C::kVJobs;
       const int dg = job % (DV / 8), kq = (job / (DV / 8)) % (kSB / 4);
+      uint4 vv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        st.v[i][j] = keep_or_zero(st.v[i][j], (LATENT ? koff : voff)[base + 4 * kq + j] >= 0);
+        vv[j] = raw_bf16x8(st.v[i][j], (LATENT ? koff : voff)[base + 4 * kq + j] >= 0);
       if (mine) {
       if (LATENT) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<uint4*>(&ks[(4 * kq + j) * C::KP + 8 * dg]) = st.v[i][j];
+          *reinterpret_cast<uint4*>(&ks[(4 * kq + j) * C::KP + 8 * dg]) = vv[j];
       }
-      // transpose: st.v[i][j] holds dims 8dg..8dg+7 of key 4kq+j; row
-      // 8dg+dd of V^T takes element dd of each of the 4 keys
+      // transpose: vv[j] holds dims 8dg..8dg+7 of key 4kq+j; row 8dg+dd of
+      // V^T takes element dd of each of the 4 keys
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
-        const uint32_t a0 = word(st.v[i][0], dd >> 1), a1 = word(st.v[i][1], dd >> 1);
-        const uint32_t a2 = word(st.v[i][2], dd >> 1), a3 = word(st.v[i][3], dd >> 1);
+        const uint32_t a0 = word(vv[0], dd >> 1), a1 = word(vv[1], dd >> 1);
+        const uint32_t a2 = word(vv[2], dd >> 1), a3 = word(vv[3], dd >> 1);
         uint2 t;
         t.x = (dd & 1) ? (a0 >> 16) | (a1 & 0xFFFF0000u) : (a0 & 0xFFFFu) | (a1 << 16);
         t.y = (dd & 1) ? (a2 >> 16) | (a3 & 0xFFFF0000u) : (a2 & 0xFFFFu) | (a3 << 16);
@@ -367,8 +426,7 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
       const bool mine = C::kKJ * C::kThreads == C::kKJobs || job < C::kKJobs;
       const int key = (job / C::kKPieces) % kSB, piece = job % C::kKPieces;
       const int d0 = (LATENT ? DV : 0) + 8 * piece;
-      if (mine)
-        *reinterpret_cast<uint4*>(&ks[key * C::KP + d0]) = keep_or_zero(st.k[i], koff[base + key] >= 0);
+      if (mine) *reinterpret_cast<uint4*>(&ks[key * C::KP + d0]) = raw_bf16x8(st.k[i], koff[base + key] >= 0);
     }
   };
 
@@ -379,7 +437,7 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
   float lsum = 0.0f;             // this lane's share of the running sum
   const float c2 = a.scale * kLog2e;
 
-  Staged<C> st;
+  Staged<C, KV8> st;
   if (nsb > 0) issue(0, st);
   for (int sb = 0; sb < nsb; ++sb) {
     const int buf = sb & 1;
@@ -1055,10 +1113,14 @@ hipError_t launch_t(const AttnLaunch& a, hipStream_t s, StageEvents ev, StageEve
       }
     }
   }
-  // (the 576-wide staged kernel only ever runs with four waves)
+  // (the 576-wide staged kernel only ever runs with four waves; it also
+  // serves the FP8 latent cache, decoding rows as it stages them)
   if constexpr (DQK != lat::kDqk || NW == 4) {
     if (!kernel)
       kernel = a.latent ? sparse_attn_kernel<DQK, DV, true, NW> : sparse_attn_kernel<DQK, DV, false, NW>;
+    if constexpr (DQK == kKvDim && DV == 512) {
+      if (a.kv8) kernel = a.latent ? sparse_attn_kernel<DQK, DV, true, NW, true> : nullptr;
+    }
   }
   if (!kernel) return hipErrorInvalidConfiguration;
   hipError_t e = launch_kernel(kernel, dim3(grid), dim3(threads), s, ev.start, ev.stop, a, g);
@@ -1104,7 +1166,8 @@ bool attn_uses_rowoff(int D_qk, int D_v, bool latent) {
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s, StageEvents ev,
                               StageEvents merge) {
   if (a.num_rows <= 0) return hipSuccess;
-  switch (waves_for(a.H_q, a.D_qk, a.latent) * 1000 + a.D_qk) {
+  // the FP8 cache takes the staged kernel (as a separate V cache does)
+  switch (waves_for(a.H_q, a.D_qk, a.latent && !a.kv8) * 1000 + a.D_qk) {
     case 2576: return launch_t<576, 512, 2>(a, s, ev, merge);
     case 4576: return launch_t<576, 512, 4>(a, s, ev, merge);
     case 4064: return launch_t<64, 64, 4>(a, s, ev, merge);

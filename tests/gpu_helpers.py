@@ -134,19 +134,27 @@ def recall(gpu_idx, orc_idx, counts):
     return hit / max(1, tot), min(per_row) if per_row else 1.0
 
 
-def check_attention(out_t, lse_t, orc_out, orc_lse, rows=None):
+def check_attention(out_t, lse_t, orc_out, orc_lse, rows=None, lse_slack=None):
+    """Attention within ATT_MAX_ABS / ATT_MEAN_ABS on the output and lse to
+    rtol 1e-4 + atol 1e-3, plus ``lse_slack`` [rows, H_q] where the kernel's
+    arithmetic adds a derived error (see fp8_kv_lse_slack)."""
     o = np_(out_t.float()).astype(np.float64)
     l = np_(lse_t).astype(np.float64)
     if rows is not None:
         o, l = o[rows], l[rows]
         orc_out, orc_lse = orc_out[rows], orc_lse[rows]
+        if lse_slack is not None and len(lse_slack) != len(rows):
+            lse_slack = lse_slack[rows]
     err = np.abs(o - orc_out)
     assert np.isfinite(o).all()
     assert err.max() <= ATT_MAX_ABS, f"max abs error {err.max():.3g}"
     assert err.mean() <= ATT_MEAN_ABS, f"mean abs error {err.mean():.3g}"
     fin = np.isfinite(orc_lse)
     assert (np.isfinite(l) == fin).all()
-    assert np.allclose(l[fin], orc_lse[fin], rtol=1e-4, atol=1e-3), \
+    tol = 1e-3 + 1e-4 * np.abs(orc_lse[fin])
+    if lse_slack is not None:
+        tol = tol + lse_slack[fin]
+    assert (np.abs(l[fin] - orc_lse[fin]) <= tol).all(), \
         f"lse error {np.abs(l[fin] - orc_lse[fin]).max():.3g}"
     return float(err.max()), float(err.mean())
 
@@ -170,6 +178,14 @@ def oracle_attention_on(arr, indices, counts, threads=None):
         b = arr["row_seq"][i]
         sel = np.asarray(indices[i][:int(counts[i])], dtype=np.int64)
         k_rows = oracle.gather_positions(arr["k_cache"], arr["block_table"][b], sel)
+        if arr.get("k_scale_cache") is not None:  # FP8 KV: decode the rows (C++ route)
+            kv = oracle.cpp.kv_fp8_to_f64(
+                k_rows, oracle.gather_positions(arr["k_scale_cache"], arr["block_table"][b], sel))
+            o, l = oracle.sparse_attn_values(oracle.bf16_to_f64(arr["q"][i]), kv, kv[:, :D_v],
+                                             arr["scale"])
+            outs.append(o)
+            lses.append(l)
+            continue
         if arr["v_cache"] is None:
             v_rows = k_rows[:, :D_v]
         else:
@@ -179,3 +195,24 @@ def oracle_attention_on(arr, indices, counts, threads=None):
         outs.append(o)
         lses.append(l)
     return np.stack(outs), np.stack(lses)
+
+
+def fp8_kv_lse_slack(arr, indices, counts):
+    """Added lse tolerance for an FP8 KV cache [rows, H_q].  The kernel rounds
+    each decoded element (code * tile scale) to bf16 before the bf16 products:
+    a relative change of at most 2**-9 per K element, so each logit moves by at
+    most scale * 2**-9 * sum_d |q[h, d]| |k[j, d]|, and lse (a smooth maximum
+    of the logits) by at most the largest of those over the selected rows."""
+    import oracle
+    out = np.zeros((len(arr["qI"]), arr["q"].shape[1]))
+    for i in range(len(arr["qI"])):
+        b = arr["row_seq"][i]
+        sel = np.asarray(indices[i][:int(counts[i])], dtype=np.int64)
+        if len(sel) == 0:
+            continue
+        k = oracle.kv_fp8_to_f64(
+            oracle.gather_positions(arr["k_cache"], arr["block_table"][b], sel),
+            oracle.gather_positions(arr["k_scale_cache"], arr["block_table"][b], sel))
+        q = np.abs(oracle.bf16_to_f64(arr["q"][i]))
+        out[i] = abs(arr["scale"]) * 2.0 ** -9 * (q @ np.abs(k).T).max(axis=1)
+    return out

@@ -179,6 +179,29 @@ def test_sparse_attn_rejections():
     assert call(prob(), k=edge, v=edge, nbytes=0) == B.DSA_ERR_WORKSPACE
 
 
+def test_fp8_kv_rejections():
+    def call(p, k=None, v=None, nbytes=0):
+        k = k or fp8()
+        return B.raw_call("dsa_sparse_attn", ctypes.byref(p), ctypes.c_void_p(FAKE), k, v or k,
+                          ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None,
+                          ctypes.c_void_p(FAKE), ctypes.c_size_t(nbytes), None)
+
+    def fp8(row=576, extra=1280, nb=8192, base=FAKE + (1 << 30)):
+        return B.DsaPaged(base, 64 * row + extra, row, nb)
+
+    fp8p = prob(kv_format=B.DSA_KV_FP8)
+    assert call(fp8p) == B.DSA_ERR_WORKSPACE                          # accepted up to the workspace
+    assert ws_size(fp8p, B.DSA_OP_SPARSE_ATTN) == ws_size(prob(), B.DSA_OP_SPARSE_ATTN)
+    assert ws_size(prob(kv_format=2), B.DSA_OP_SPARSE_ATTN) == 0
+    assert call(prob(kv_format=2)) == B.DSA_ERR_INVALID
+    assert call(prob(kv_format=B.DSA_KV_FP8, D_qk=64, D_v=64, H_q=8)) == B.DSA_ERR_UNSUPPORTED
+    assert call(fp8p, k=fp8(extra=1264)) == B.DSA_ERR_INVALID          # no room for the scales
+    assert call(fp8p, k=fp8(row=560)) == B.DSA_ERR_INVALID             # row < 576 codes
+    assert call(fp8p, k=fp8(), v=fp8(base=FAKE + (1 << 31))) == B.DSA_ERR_INVALID  # not latent
+    # the 64 GiB limit of the bf16 latent kernel does not apply
+    assert call(fp8p, k=fp8(nb=1 << 22)) == B.DSA_ERR_WORKSPACE
+
+
 def test_decode_step_rejections():
     def call(p, kI=None, k=None, nbytes=None, ws=FAKE, indices=None):
         nbytes = ws_size(prob(), 3) if nbytes is None else nbytes

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 import torch
 
-from tests.gpu_helpers import (RECALL_MIN, check_attention, gpu_decode, np_,
+from tests.gpu_helpers import (RECALL_MIN, check_attention, fp8_kv_lse_slack, gpu_decode, np_,
                                oracle_attention_on, recall, say)
 from tests.helpers import run_oracle
 from workloads import BENCH_WORKLOAD, CONFIGS, make_batch, oracle_arrays, row_positions
@@ -128,3 +128,23 @@ def test_full_size_candidates_bench_shape():
     assert (np_(res["counts"]) == orc["counts"]).all()
     assert (np_(res["indices"]) == orc["indices"]).all()
     check_attention(res["out"], res["lse"], orc["out"], orc["lse"])
+
+
+def test_full_size_fp8_kv_bench_shape():
+    # the 4 x 128k decode step over an FP8 KV cache (E4M3 latent rows, one
+    # float32 scale per tile of 128 elements), integer-mode indexer: every
+    # row's indices bit-exact against the oracle, attention within tolerance
+    wl = CONFIGS[BENCH_WORKLOAD].with_(kv_fmt="fp8")
+    say(f"full size {BENCH_WORKLOAD}: FP8 KV cache, integer mode, seed {wl.seed}")
+    batch = make_batch(wl, device="cuda", seed=wl.seed, mode="int")
+    res = gpu_decode(batch)
+    _check_every_row(batch, res)
+    rows = list(range(batch.rows))
+    arr = oracle_arrays(batch, rows=rows)
+    orc = run_oracle(arr, keep_scores=False)
+    assert (np_(res["counts"]) == orc["counts"]).all()
+    assert (np_(res["indices"]) == orc["indices"]).all()
+    slack = fp8_kv_lse_slack(arr, orc["indices"], orc["counts"])
+    e_max, e_mean = check_attention(res["out"], res["lse"], orc["out"], orc["lse"],
+                                    lse_slack=slack)
+    say(f"  attention: max {e_max:.3g} mean {e_mean:.3g}; lse slack up to {slack.max():.3g}")

@@ -13,9 +13,9 @@ import torch
 
 import oracle
 from indexer_top_sparse_score_amd import binding as B
-from tests.gpu_helpers import (RECALL_MIN, check_attention, check_scores_exact, gpu_attn,
-                               gpu_decode, gpu_scores, gpu_topk, np_, oracle_attention_on,
-                               recall, say, score_bound, score_ld)
+from tests.gpu_helpers import (RECALL_MIN, check_attention, check_scores_exact, fp8_kv_lse_slack,
+                               gpu_attn, gpu_decode, gpu_scores, gpu_topk, np_,
+                               oracle_attention_on, recall, say, score_bound, score_ld)
 from tests.helpers import run_oracle
 from workloads import CONFIGS, make_batch, oracle_arrays, row_positions, small_workload
 
@@ -53,6 +53,8 @@ CASES = {
     "mla_mx_cand": dict(lengths=[5000, 40000], mode="int", indexer_fmt="mxfp8", n_cand=16388,
                         **MLA),
     "tiny_cand": dict(lengths=[1, 50, 64, 1024, 3000], mode="int", n_cand=700, **TINY),
+    # FP8 KV cache: E4M3 latent rows with one float32 scale per tile of 128
+    "mla_fp8kv": dict(lengths=LENGTHS, mode="int", kv_fmt="fp8", table="shuffled", **MLA),
 }
 
 
@@ -147,18 +149,23 @@ def test_topk_ties_and_special_values():
         assert (np_(idx)[i] == want).all(), f"row {i}"
 
 
-@pytest.mark.parametrize("name", ["mla_int", "tiny_int", "mla_int_k100", "h48_d64", "mla_sepv"])
+@pytest.mark.parametrize("name", ["mla_int", "tiny_int", "mla_int_k100", "h48_d64", "mla_sepv",
+                                  "mla_fp8kv"])
 def test_sparse_attn_on_oracle_indices(name):
     batch = _batch(name, mode="gauss", seed=25)
     arr = oracle_arrays(batch)
     orc = run_oracle(arr)
     out, lse = gpu_attn(batch, torch.from_numpy(orc["indices"]).cuda())
-    mx, mean = check_attention(out, lse, orc["out"], orc["lse"])
+    slack = None
+    if batch.wl.kv_fmt == "fp8":
+        slack = fp8_kv_lse_slack(arr, orc["indices"], orc["counts"])
+    mx, mean = check_attention(out, lse, orc["out"], orc["lse"], lse_slack=slack)
     say(f"attention {name}: max {mx:.3g} mean {mean:.3g}")
 
 
-def test_sparse_attn_skips_padding_and_handles_empty_rows():
-    batch = _batch("mla_int", mode="gauss", seed=26)
+@pytest.mark.parametrize("name", ["mla_int", "mla_fp8kv"])
+def test_sparse_attn_skips_padding_and_handles_empty_rows(name):
+    batch = _batch(name, mode="gauss", seed=26)
     arr = oracle_arrays(batch)
     K = batch.wl.K
     rng = np.random.default_rng(26)
@@ -178,15 +185,29 @@ def test_sparse_attn_skips_padding_and_handles_empty_rows():
         if len(sel) == 0:
             continue
         k_rows = oracle.gather_positions(arr["k_cache"], arr["block_table"][b], sel)
-        want_o[i], want_l[i] = oracle.sparse_attn_row(arr["q"][i], k_rows, k_rows[:, :512],
-                                                      batch.wl.scale)
-    check_attention(out, lse, want_o, want_l)
+        if arr["k_scale_cache"] is not None:
+            kv = oracle.kv_fp8_to_f64(
+                k_rows, oracle.gather_positions(arr["k_scale_cache"], arr["block_table"][b], sel))
+            want_o[i], want_l[i] = oracle.sparse_attn_values(
+                oracle.bf16_to_f64(arr["q"][i]), kv, kv[:, :512], batch.wl.scale)
+        else:
+            want_o[i], want_l[i] = oracle.sparse_attn_row(arr["q"][i], k_rows, k_rows[:, :512],
+                                                          batch.wl.scale)
+    slack = None
+    if batch.wl.kv_fmt == "fp8":
+        packed = np.full_like(idx, -1)
+        cnt = np.zeros(batch.rows, np.int64)
+        for i in range(batch.rows):
+            sel = np.sort(idx[i][idx[i] >= 0])
+            packed[i, :len(sel)], cnt[i] = sel, len(sel)
+        slack = fp8_kv_lse_slack(arr, packed, cnt)
+    check_attention(out, lse, want_o, want_l, lse_slack=slack)
     assert (np_(out.float())[2] == 0).all() and np.isneginf(np_(lse)[2]).all()
 
 
 @pytest.mark.parametrize("name", ["mla_int", "mla_int_shuffled", "tiny_int", "mla_int_k100",
                                   "mla_sepv", "mla_int_grouped", "mla_mx_int", "mla_cand_int",
-                                  "mla_cand_split", "mla_mx_cand", "tiny_cand"])
+                                  "mla_cand_split", "mla_mx_cand", "tiny_cand", "mla_fp8kv"])
 def test_decode_step_integer_mode(name):
     batch = _batch(name, seed=27)
     arr = oracle_arrays(batch)
@@ -194,7 +215,10 @@ def test_decode_step_integer_mode(name):
     res = gpu_decode(batch)
     assert (np_(res["counts"]) == orc["counts"]).all()
     assert (np_(res["indices"]) == orc["indices"]).all()
-    check_attention(res["out"], res["lse"], orc["out"], orc["lse"])
+    slack = None
+    if batch.wl.kv_fmt == "fp8":
+        slack = fp8_kv_lse_slack(arr, orc["indices"], orc["counts"])
+    check_attention(res["out"], res["lse"], orc["out"], orc["lse"], lse_slack=slack)
 
 
 def test_decode_step_gaussian_mode():
