@@ -38,6 +38,9 @@ read_reference a library streaming read (torch.sum over 1 GiB) as a reference fo
 candidate_indexer  the same workload with a candidate-restricted indexer
            (16384 candidate positions per row): the fused step and the scan
            alone, timed the same way (--no-cand skips it)
+fp8_kv_cache  the same workload over an FP8 KV cache (E4M3 latent rows, one
+           float32 scale per tile of 128 elements): the fused step and its
+           stage times, with the attention's HBM fraction (--no-fp8-kv skips it)
 """
 
 import argparse
@@ -76,6 +79,8 @@ def parse():
                     help="skip the candidate-restricted indexer leg")
     ap.add_argument("--no-mxfp8", action="store_true",
                     help="skip the MXFP8-indexer leg (same workload, group-32 scales)")
+    ap.add_argument("--no-fp8-kv", action="store_true",
+                    help="skip the FP8-KV-cache leg (same workload, E4M3 rows, tile-128 scales)")
     ap.add_argument("--table", default=None)
     ap.add_argument("--legs", default=OTHER_WORKLOADS,
                     help="comma-separated other workloads to time after the headline ('none')")
@@ -97,7 +102,7 @@ def step_bytes(wl, lengths):
     the gathered KV rows, the queries, weights, block-table entries and the
     output (no score matrix: the fused step need not materialise one)."""
     total = 0
-    row_kv = 2 * (wl.D_qk if wl.latent else wl.D_qk + wl.D_v)
+    row_kv = kv_row_bytes(wl)
     for L in lengths:
         n = min(wl.K, L)
         total += (wl.D_I * L + row_kv * n + wl.H_I * wl.D_I + 4 * wl.H_I
@@ -118,9 +123,17 @@ def indexer_bytes(wl, lengths, mx=False, scores=False):
 def attention_bytes(wl, lengths):
     """Algorithmic bytes of the attention stage: the gathered KV rows, the
     queries and the output (the selection it reads is a few KiB)."""
-    row_kv = 2 * (wl.D_qk if wl.latent else wl.D_qk + wl.D_v)
+    row_kv = kv_row_bytes(wl)
     return sum(row_kv * min(wl.K, L) + 2 * wl.H_q * wl.D_qk + 2 * wl.H_q * wl.D_v
                for L in lengths)
+
+
+def kv_row_bytes(wl):
+    """Bytes of one gathered KV row: bf16 K (and V), or FP8 codes plus one
+    float32 scale per tile of 128 elements."""
+    if getattr(wl, "kv_fmt", "bf16") == "fp8":
+        return wl.D_qk + 4 * ((wl.D_qk + 127) // 128)
+    return 2 * (wl.D_qk if wl.latent else wl.D_qk + wl.D_v)
 
 
 def step_flops(wl, lengths):
@@ -298,6 +311,9 @@ def main():
     if not args.no_cand:
         log("candidate indexer leg")
         result["candidate_indexer"] = guarded(cand_leg, args, wl, lengths, stream)
+    if not args.no_fp8_kv:
+        log("fp8 kv leg")
+        result["fp8_kv_cache"] = guarded(fp8_kv_leg, args, wl, lengths, stream)
     legs = [x for x in args.legs.split(",") if x and x != "none" and x != name]
     if legs:
         del sets, probs, outs, graphs
@@ -630,6 +646,54 @@ def cand_bytes(wl, lengths, n_cand):
         C = min(n_cand, L)
         tot += C * (wl.D_I + 4 + 4) + 4 * min(C, -(-L // 64)) + wl.H_I * wl.D_I + 4 * wl.H_I
     return tot
+
+
+def fp8_kv_leg(args, wl, lengths, stream):
+    """The same workload over an FP8 KV cache (E4M3 latent rows, one float32
+    scale per tile of 128 elements): the fused step (stream launches, HIP
+    events) and its stage times, over input sets that rotate past the
+    Infinity Cache."""
+    import torch
+    from indexer_top_sparse_score_amd import binding as B
+    from workloads import make_batch
+    fwl = wl.with_(kv_fmt="fp8")
+    dev = torch.device("cuda:0")
+    nset = 8
+    sets = [make_batch(fwl, device=dev, seed=fwl.seed + 9000 + 1000 * i, mode=args.mode,
+                       table=args.table, lengths=lengths) for i in range(nset)]
+    probs = [B.problem_for_batch(s) for s in sets]
+    rows = sets[0].rows
+    ws = B.workspace(probs[0], B.DSA_OP_DECODE_STEP, device=dev)
+    outs = [(torch.empty((rows, fwl.H_q, fwl.D_v), dtype=torch.bfloat16, device=dev),
+             torch.empty((rows, fwl.H_q), dtype=torch.float32, device=dev)) for _ in range(nset)]
+
+    def step(i):
+        s = sets[i % nset]
+        out, lse = outs[i % nset]
+        B.dsa_decode_step(probs[i % nset], s.qI, s.w, s.kI, s.q, s.kv, s.kv, out, ws, lse=lse,
+                          stream=stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            step(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    step_us = 1e3 * e0.elapsed_time(e1) / args.steps
+    st = stage_times(args, sets, probs, outs, ws, stream)
+    assert B.device_errors(ws) == 0
+    ab = attention_bytes(fwl, lengths)
+    return {"kv_cache": f"e4m3 rows of {fwl.D_qk} + float32 scale per 128", "rotation_sets": nset,
+            "launch": "stream (eager)", "step_us": round(step_us, 3),
+            "tokens_per_s": round(rows / (step_us * 1e-6), 1),
+            "kv_row_bytes": kv_row_bytes(fwl), "attention_bytes": ab,
+            "attention_us": st["attention_us"], "merge_us": st["merge_us"],
+            "attention_gbs": round(ab / (st["attention_us"] * 1e-6) / 1e9, 1),
+            "attention_hbm_frac": round(ab / (st["attention_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "stages": st}
 
 
 def cand_leg(args, wl, lengths, stream, n_cand=16384):
