@@ -22,7 +22,9 @@ numeric example for any step):
   - section 4.2: the attention core gathers the selected rows of the main KV
     cache from the indexer's position list;
   - section 4.3: the fused call takes the quantised query, the index keys and
-    the head weights and returns the selected positions;
+    the head weights and returns the selected positions; before it, the
+    indexer prolog projects q and the head weights, normalises the new key
+    and quantises q per group (``prolog.py``);
   - section 5.1 / 5.2: FP8 storage for the indexer and the KV cache; the
     indexer's MXFP8 format (one shared scale per group of 32); the KV cache's
     per-token tiles of 128 elements with one scale each.
@@ -65,10 +67,20 @@ from .dsa import (
     dense_causal_attn_row,
     decode_step,
 )
+from .prolog import (
+    MX_GROUP,
+    bf16_round,
+    e4m3_round,
+    mx_quantize,
+    mx_dequantize,
+    rms_norm,
+    indexer_prolog,
+)
 
 __all__ = [
     "E4M3_TABLE", "KV_TILE", "e4m3_to_f64", "e8m0_to_f64", "bf16_to_f64", "kv_fp8_to_f64",
     "kv_tiles", "resolve_rows", "gather_positions", "row_history", "indexer_scores_row",
     "score_keys", "topk_row", "sparse_attn_row", "sparse_attn_values", "masked_dense_attn_row",
-    "dense_causal_attn_row", "decode_step",
+    "dense_causal_attn_row", "decode_step", "MX_GROUP", "bf16_round", "e4m3_round",
+    "mx_quantize", "mx_dequantize", "rms_norm", "indexer_prolog",
 ]

@@ -85,6 +85,13 @@ def lib():
                                           ctypes.c_int]
             L.orc_decode_step.restype = ctypes.c_int
             L.orc_kv_fp8_decode.argtypes = [_u8p, _f32p, ctypes.c_int64, ctypes.c_int, _f64p]
+            L.orc_bf16_round.argtypes = [_f64p, ctypes.c_int64, _u16p]
+            L.orc_e4m3_round.argtypes = [_f64p, ctypes.c_int64, _u8p]
+            L.orc_mx_quantize.argtypes = [_f64p, ctypes.c_int64, ctypes.c_int, _u8p, _u8p]
+            L.orc_prolog.argtypes = [_u16p, _u16p, _u16p, _u16p, _u16p, ctypes.c_double,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     _f64p, _u16p, _u8p, _u8p, _f32p, _u16p, _u8p, _u8p,
+                                     ctypes.c_int]
             _lib = L
     return _lib
 
@@ -160,6 +167,70 @@ def kv_fp8_to_f64(codes, scales):
     lib().orc_kv_fp8_decode(_ptr(c, ctypes.c_uint8), _ptr(s, ctypes.c_float), n, D,
                             _ptr(out, ctypes.c_double))
     return out
+
+
+def bf16_round(values):
+    """bf16 bits of binary64 values, nearest even (the C++ route)."""
+    v = _arr(values, np.float64)
+    out = np.empty(v.shape, np.uint16)
+    lib().orc_bf16_round(_ptr(v, ctypes.c_double), v.size, _ptr(out, ctypes.c_uint16))
+    return out
+
+
+def e4m3_round(values):
+    """E4M3 codes of binary64 values (the C++ route): nearest, ties to even,
+    saturated at 448, sign kept."""
+    v = _arr(values, np.float64)
+    out = np.empty(v.shape, np.uint8)
+    lib().orc_e4m3_round(_ptr(v, ctypes.c_double), v.size, _ptr(out, ctypes.c_uint8))
+    return out
+
+
+def mx_quantize(values, group=32):
+    """MXFP8 codes and E8M0 scales along the last axis (the C++ route)."""
+    if group != 32:
+        raise ValueError("groups of 32")
+    v = _arr(values, np.float64)
+    n = v.shape[-1]
+    if n % 32:
+        raise ValueError("length must be a multiple of the group")
+    rows = v.size // n if n else 0
+    codes = np.empty(v.shape, np.uint8)
+    scales = np.empty(v.shape[:-1] + (n // 32,), np.uint8)
+    lib().orc_mx_quantize(_ptr(v, ctypes.c_double), rows, n, _ptr(codes, ctypes.c_uint8),
+                          _ptr(scales, ctypes.c_uint8))
+    return codes, scales
+
+
+def indexer_prolog(*, x, w_q, w_g, k_new, k_gamma, eps, H_I, D_I, threads=1):
+    """The indexer prolog; same contract and result dict as
+    ``oracle.indexer_prolog`` (the numpy route)."""
+    xa = _arr(x, np.uint16)
+    rows, D_x = xa.shape
+    wq = _arr(w_q, np.uint16)
+    wg = _arr(w_g, np.uint16)
+    kn = _arr(k_new, np.uint16)
+    ga = _arr(k_gamma, np.uint16)
+    F = H_I * D_I
+    if wq.shape != (F, D_x) or wg.shape != (H_I, D_x) or kn.shape != (rows, D_I) \
+            or ga.shape != (D_I,) or D_I % 32:
+        raise ValueError("prolog shapes")
+    q = np.empty((rows, F), np.float64)
+    q16 = np.empty((rows, F), np.uint16)
+    qI = np.empty((rows, F), np.uint8)
+    qs = np.empty((rows, F // 32), np.uint8)
+    w = np.empty((rows, H_I), np.float32)
+    k16 = np.empty((rows, D_I), np.uint16)
+    kI = np.empty((rows, D_I), np.uint8)
+    ks = np.empty((rows, D_I // 32), np.uint8)
+    P = ctypes.c_uint16, ctypes.c_uint8
+    lib().orc_prolog(_ptr(xa, P[0]), _ptr(wq, P[0]), _ptr(wg, P[0]), _ptr(kn, P[0]),
+                     _ptr(ga, P[0]), float(eps), rows, D_x, H_I, D_I, _ptr(q, ctypes.c_double),
+                     _ptr(q16, P[0]), _ptr(qI, P[1]), _ptr(qs, P[1]), _ptr(w, ctypes.c_float),
+                     _ptr(k16, P[0]), _ptr(kI, P[1]), _ptr(ks, P[1]), int(threads))
+    return {"q": q, "q_bf16": q16, "qI": qI.reshape(rows, H_I, D_I),
+            "qI_scale": qs.reshape(rows, H_I, D_I // 32), "w": w,
+            "k_bf16": k16, "kI": kI, "kI_scale": ks}
 
 
 def masked_dense_attn_row(q_bits, k_all_bits, v_all_bits, selected, scale):

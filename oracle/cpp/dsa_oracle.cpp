@@ -82,6 +82,81 @@ uint32_t score_key(float s) {
   return (u >> 31) ? ~u : (u | 0x80000000u);
 }
 
+// ------------------------------------------------------------ indexer prolog
+// Day0 article, section 4.3 (Q projection, K normalisation, per-group Q
+// quantisation, head-weight projection), with the MXFP8 format of section
+// 5.1 and bf16 projections (section 5.3).  Readings: the prolog's tensors (q,
+// the normalised key, g) are bf16 activations, each the exact value rounded
+// once to nearest even; the K normalisation is RMS normalisation with a bf16
+// weight; the group scale follows the OCP microscaling conversion.
+
+// Nearest-even rounding of v to bfloat16 (8 significant bits; below 2^-126
+// the fixed 2^-133 grid of the subnormals).  std::nearbyint rounds half to
+// even in the default rounding mode.
+uint16_t bf16_round_bits(double v) {
+  int e;
+  std::frexp(v, &e);  // v = f 2^e, 0.5 <= |f| < 1
+  const int qe = std::max(e, -125) - 8;
+  const double r = std::ldexp(std::nearbyint(std::ldexp(v, -qe)), qe);
+  const float f = (float)r;  // exact: r has at most 8 significant bits
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return (uint16_t)(u >> 16);
+}
+
+// E4M3 code of v: the magnitude (saturated at 448) is split into exponent and
+// a 3-bit mantissa rounded half to even; subnormals are multiples of 2^-9.
+// The sign bit is v's own, also when the magnitude rounds to zero.
+uint8_t e4m3_round_code(double v) {
+  const double a = std::min(std::fabs(v), 448.0);
+  int code;
+  if (a < std::ldexp(1.0, -6)) {
+    code = (int)std::nearbyint(std::ldexp(a, 9));  // 0..8; 8 is 2^-6, code 0x08
+  } else {
+    int E;
+    std::frexp(a, &E);
+    int e = E - 1;  // 2^e <= a < 2^(e+1)
+    int m = (int)std::nearbyint((std::ldexp(a, -e) - 1.0) * 8.0);
+    if (m == 8) {
+      m = 0;
+      ++e;
+    }
+    code = ((e + 7) << 3) | m;
+    if (code > 0x7E) code = 0x7E;
+  }
+  return (uint8_t)(code | (std::signbit(v) ? 0x80 : 0));
+}
+
+// One group of n values: the shared scale byte and the codes.  The scale is
+// 2^(floor(log2 max|v|) - 8), 8 being E4M3's largest exponent, clamped to
+// E8M0's 2^-127 .. 2^127 (2^-127 for an all-zero group).
+void mx_quantize_group(const double* v, int n, uint8_t* codes, uint8_t* scale) {
+  double amax = 0.0;
+  for (int i = 0; i < n; ++i) amax = std::max(amax, std::fabs(v[i]));
+  int shared = -127;
+  if (amax > 0.0) {
+    int E;
+    std::frexp(amax, &E);
+    shared = std::min(127, std::max(-127, E - 1 - 8));
+  }
+  *scale = (uint8_t)(shared + 127);
+  for (int i = 0; i < n; ++i) codes[i] = e4m3_round_code(std::ldexp(v[i], -shared));
+}
+
+// Sum of products of two bf16 rows in binary64 with Neumaier's compensation,
+// so the rounding of the result to bf16 sees the exact sum in all but
+// pathological cases (integer inputs are exact either way).
+double dot_bf16(const uint16_t* a, const uint16_t* b, int n) {
+  double s = 0.0, c = 0.0;
+  for (int i = 0; i < n; ++i) {
+    const double t = bf16_value(a[i]) * bf16_value(b[i]);  // exact
+    const double u = s + t;
+    c += std::fabs(s) >= std::fabs(t) ? (s - u) + t : (t - u) + s;
+    s = u;
+  }
+  return s + c;
+}
+
 // Runs fn(i) for i in [0, n) on up to `threads` host threads.
 template <class F>
 void parallel_for(int64_t n, int threads, F fn) {
@@ -357,6 +432,62 @@ int orc_decode_step(const OrcStep* p, const int32_t* rows, int n_sel, int32_t* i
                   threads);
   }
   return 0;
+}
+
+// Bit-level pieces of the prolog, for pins against other routines.
+void orc_bf16_round(const double* v, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = bf16_round_bits(v[i]);
+}
+void orc_e4m3_round(const double* v, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_round_code(v[i]);
+}
+// MXFP8 quantisation of rows of n values (n a multiple of 32).
+void orc_mx_quantize(const double* v, int64_t rows, int n, uint8_t* codes, uint8_t* scales) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int g = 0; g < n / 32; ++g)
+      mx_quantize_group(v + r * n + 32 * g, 32, codes + r * n + 32 * g, scales + r * (n / 32) + g);
+}
+
+// The indexer prolog for `rows` rows (Day0 article, section 4.3):
+//   q = W_q x            x [rows][D_x] bf16, w_q [H_I * D_I][D_x] bf16
+//   qI, qs = MXFP8(bf16(q)) per head and group of 32
+//   g = W_g x            w_g [H_I][D_x] bf16; w = bf16(g) stored as binary32
+//   y = gamma * k / sqrt(mean(k^2) + eps), k [rows][D_I] bf16, gamma [D_I]
+//   kI, ks = MXFP8(bf16(y))
+// Outputs: q binary64 [rows][H_I * D_I], q_bf16, qI [rows][H_I * D_I],
+// qs [rows][H_I * D_I / 32], w [rows][H_I], k_bf16 [rows][D_I], kI
+// [rows][D_I], ks [rows][D_I / 32].
+void orc_prolog(const uint16_t* x, const uint16_t* w_q, const uint16_t* w_g, const uint16_t* k,
+                const uint16_t* gamma, double eps, int rows, int D_x, int H_I, int D_I, double* q,
+                uint16_t* q_bf16, uint8_t* qI, uint8_t* qs, float* w, uint16_t* k_bf16,
+                uint8_t* kI, uint8_t* ks, int threads) {
+  const int F = H_I * D_I;
+  parallel_for(rows, threads, [&](int64_t r) {
+    const uint16_t* xr = x + r * D_x;
+    std::vector<double> qv(F);
+    for (int f = 0; f < F; ++f) {
+      q[r * F + f] = dot_bf16(w_q + (int64_t)f * D_x, xr, D_x);
+      q_bf16[r * F + f] = bf16_round_bits(q[r * F + f]);
+      qv[f] = bf16_value(q_bf16[r * F + f]);
+    }
+    for (int gi = 0; gi < F / 32; ++gi)
+      mx_quantize_group(&qv[32 * gi], 32, qI + r * F + 32 * gi, qs + r * (F / 32) + gi);
+    for (int h = 0; h < H_I; ++h)
+      w[r * H_I + h] = (float)bf16_value(bf16_round_bits(dot_bf16(w_g + (int64_t)h * D_x, xr, D_x)));
+    double ss = 0.0;
+    for (int d = 0; d < D_I; ++d) {
+      const double kd = bf16_value(k[r * D_I + d]);
+      ss += kd * kd;
+    }
+    const double inv = 1.0 / std::sqrt(ss / D_I + eps);
+    std::vector<double> yv(D_I);
+    for (int d = 0; d < D_I; ++d) {
+      k_bf16[r * D_I + d] = bf16_round_bits(bf16_value(gamma[d]) * bf16_value(k[r * D_I + d]) * inv);
+      yv[d] = bf16_value(k_bf16[r * D_I + d]);
+    }
+    for (int gi = 0; gi < D_I / 32; ++gi)
+      mx_quantize_group(&yv[32 * gi], 32, kI + r * D_I + 32 * gi, ks + r * (D_I / 32) + gi);
+  });
 }
 
 }  // extern "C"

@@ -13,6 +13,8 @@ DeepSeek-V4.1-Flash post); none of those suites' items is reproduced.
 
 from .configs import Workload, CONFIGS, BENCH_WORKLOAD, small_workload
 from .gen import Batch, make_batch, oracle_arrays, row_positions, kv_fp8_split, kv_scale_rows
+from .prolog import PROLOG_D_X, PrologInputs, make_prolog_inputs, prolog_arrays
 
 __all__ = ["Workload", "CONFIGS", "BENCH_WORKLOAD", "small_workload", "kv_fp8_split", "kv_scale_rows",
-           "Batch", "make_batch", "oracle_arrays", "row_positions"]
+           "Batch", "make_batch", "oracle_arrays", "row_positions", "PROLOG_D_X", "PrologInputs",
+           "make_prolog_inputs", "prolog_arrays"]
