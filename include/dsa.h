@@ -62,7 +62,7 @@ extern "C" {
 #define DSA_API
 #endif
 
-#define DSA_ABI_VERSION 7
+#define DSA_ABI_VERSION 8
 #define DSA_BLOCK_SIZE 64
 #define DSA_MAX_ATTN_K 16384 /* largest K of dsa_sparse_attn / dsa_decode_step */
 #define DSA_STATIC_SCRATCH_BYTES (64u << 20) /* scratch of dsa_decode_step_static, per GPU */
@@ -140,7 +140,8 @@ enum {
   DSA_OP_INDEXER_SCORES = 0,
   DSA_OP_TOPK = 1,
   DSA_OP_SPARSE_ATTN = 2,
-  DSA_OP_DECODE_STEP = 3
+  DSA_OP_DECODE_STEP = 3,
+  DSA_OP_INDEXER_PROLOG = 4
 };
 
 /* Bytes of workspace `op` needs for problem `p` (a multiple of 256, at least
@@ -292,6 +293,47 @@ DSA_API int dsa_decode_step_static(const dsa_problem* p, const uint8_t* qI, cons
                                    dsa_paged kI, const uint16_t* q, dsa_paged k, dsa_paged v,
                                    uint16_t* out, float* lse, int32_t* indices_out,
                                    int32_t* counts_out, uint32_t* err, void* stream);
+
+/*
+ * The indexer prolog (Day0 article, section 4.3: Q projection, K
+ * normalisation, per-group Q quantisation and head-weight projection ahead
+ * of the fused call), producing the MXFP8 operands of section 5.1 with bf16
+ * projections (section 5.3).  For every row r, in one launch:
+ *   q[r]  = W_q x[r]          x bf16 [num_rows][D_x], w_q bf16 [H_I * D_I][D_x]
+ *                             (row h * D_I + d gives head h, dim d)
+ *   qI, qI_scale = MXFP8(q[r]) per head and group of 32 dims:
+ *                             qI E4M3 [num_rows][H_I][D_I],
+ *                             qI_scale E8M0 [num_rows][H_I][D_I / 32]
+ *   w[r]  = W_g x[r]          w_g bf16 [H_I][D_x]; w float32 [num_rows][H_I]
+ *   y     = k_gamma * k_new[r] / sqrt(mean(k_new[r]^2) + eps)
+ *                             k_new bf16 [num_rows][D_I] (the row's own index
+ *                             key before normalisation), k_gamma bf16 [D_I]
+ *   MXFP8(y) is written into kI at the row's position p_r of sequence b_r:
+ *   codes at row p_r % 64 of block block_table[b_r][p_r / 64], scales in
+ *   that block's scale area (the MXFP8 page layout of dsa_indexer_scores).
+ * Products are bf16 x bf16 with float32 accumulation.  Readings: q, y and w
+ * are bf16 tensors (the float32 result rounded to nearest even; w holds its
+ * bf16 values); a group of 32 values v shares the scale
+ * 2^(floor(log2 max|v|) - 8) (OCP microscaling; 2^-127 for an all-zero
+ * group) and each code is v over the scale rounded to nearest even in E4M3,
+ * saturated at +-448, keeping v's sign.
+ *   p        shapes, rows and block table as for the other calls;
+ *            indexer_format must be DSA_INDEXER_MXFP8 (else DSA_ERR_INVALID);
+ *            the attention fields and K are not read
+ *   D_x      input width, a multiple of 32 in 32 .. 65536
+ *            (else DSA_ERR_INVALID / DSA_ERR_UNSUPPORTED above 65536)
+ *   eps      finite, >= 0
+ *   kI       the index-key cache, written (its base is cast to writable)
+ * Alignment: x, w_q, w_g, qI 16 bytes; k_new, k_gamma, w 4 bytes.
+ * Workspace: dsa_workspace_size(p, DSA_OP_INDEXER_PROLOG) bytes (the error
+ * word).  A row that does not resolve or whose block id is out of range
+ * writes nothing to kI and sets DSA_DEVERR_ROW / DSA_DEVERR_BLOCK; its qI,
+ * qI_scale and w are still written.
+ */
+DSA_API int dsa_indexer_prolog(const dsa_problem* p, int32_t D_x, float eps, const uint16_t* x,
+                               const uint16_t* w_q, const uint16_t* w_g, const uint16_t* k_new,
+                               const uint16_t* k_gamma, uint8_t* qI, uint8_t* qI_scale,
+                               float* w, dsa_paged kI, void* ws, size_t ws_bytes, void* stream);
 
 /* Static text for a dsa_status value ("unknown status" otherwise). */
 DSA_API const char* dsa_status_string(int status);

@@ -26,8 +26,9 @@ DSA_OP_INDEXER_SCORES = 0
 DSA_OP_TOPK = 1
 DSA_OP_SPARSE_ATTN = 2
 DSA_OP_DECODE_STEP = 3
+DSA_OP_INDEXER_PROLOG = 4
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 DSA_INDEXER_E4M3 = 0
 DSA_INDEXER_MXFP8 = 1
 DSA_KV_BF16 = 0
@@ -37,7 +38,7 @@ BLOCK = 64
 #: every symbol include/dsa.h declares
 EXPORTS = ("dsa_workspace_size", "dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn",
            "dsa_decode_step", "dsa_decode_step_timed", "dsa_decode_step_static",
-           "dsa_status_string", "dsa_abi_version")
+           "dsa_indexer_prolog", "dsa_status_string", "dsa_abi_version")
 
 
 class DsaPaged(ctypes.Structure):
@@ -89,8 +90,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                           P, P, sz, ctypes.POINTER(P), P]
     lib.dsa_decode_step_static.argtypes = [prob, P, P, DsaPaged, P, DsaPaged, DsaPaged, P, P, P,
                                            P, P, P]
+    lib.dsa_indexer_prolog.argtypes = [prob, i32, ctypes.c_float, P, P, P, P, P, P, P, P,
+                                       DsaPaged, P, sz, P]
     for f in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_decode_step",
-              "dsa_decode_step_timed", "dsa_decode_step_static"):
+              "dsa_decode_step_timed", "dsa_decode_step_static", "dsa_indexer_prolog"):
         getattr(lib, f).restype = ctypes.c_int
     lib.dsa_status_string.argtypes = [ctypes.c_int]
     lib.dsa_status_string.restype = ctypes.c_char_p
@@ -132,13 +135,16 @@ def paged(cache: torch.Tensor) -> DsaPaged:
 
 def problem(*, seq_lens, block_table, num_rows=None, row_seq=None, row_pos=None, H_I=64,
             D_I=128, H_q=128, D_qk=576, D_v=512, K=2048, scale=576 ** -0.5,
-            qI_scale=None, cand=None, cand_len=None, kv_format=DSA_KV_BF16) -> DsaProblem:
+            qI_scale=None, cand=None, cand_len=None, kv_format=DSA_KV_BF16,
+            indexer_format=None) -> DsaProblem:
     """Problem descriptor; device tensors are referenced, not copied.  With
     ``qI_scale`` (uint8 E8M0 [rows, H_I, D_I/32]) the indexer runs in MXFP8
     format and each index-key block carries its rows' scales after the code rows.
     With ``cand`` (int32 [rows, n_cand], ascending positions) and ``cand_len``
     (int32 [rows]) each row scores only its candidate positions.  ``kv_format``
-    DSA_KV_FP8: the KV cache holds E4M3 rows with float32 tile scales."""
+    DSA_KV_FP8: the KV cache holds E4M3 rows with float32 tile scales.
+    ``indexer_format`` overrides the format ``qI_scale`` implies (the prolog
+    writes MXFP8 operands and takes no ``qI_scale`` here)."""
     num_seqs = int(seq_lens.shape[0])
     if num_rows is None:
         num_rows = int(row_seq.shape[0]) if row_seq is not None else num_seqs
@@ -147,7 +153,8 @@ def problem(*, seq_lens, block_table, num_rows=None, row_seq=None, row_pos=None,
                    None if row_seq is None else row_seq.data_ptr(),
                    None if row_pos is None else row_pos.data_ptr(),
                    H_I, D_I, H_q, D_qk, D_v, K, scale,
-                   DSA_INDEXER_E4M3 if qI_scale is None else DSA_INDEXER_MXFP8,
+                   (DSA_INDEXER_E4M3 if qI_scale is None else DSA_INDEXER_MXFP8)
+                   if indexer_format is None else int(indexer_format),
                    None if qI_scale is None else qI_scale.data_ptr(),
                    None if cand is None else cand.data_ptr(),
                    None if cand_len is None else cand_len.data_ptr(),
@@ -247,6 +254,18 @@ def dsa_decode_step_static(prob, qI, w, kI, q, k, v, out, lse=None, indices=None
                                          _ptr(q), paged(k), paged(v), _ptr(out), _ptr(lse),
                                          _ptr(indices), _ptr(counts), _ptr(err),
                                          _stream(stream)), "dsa_decode_step_static")
+
+
+def dsa_indexer_prolog(prob, x, w_q, w_g, k_new, k_gamma, qI, qI_scale, w, kI, ws, eps=1e-6,
+                       stream=None):
+    """The indexer prolog: MXFP8 qI / qI_scale = quant(W_q x), w = W_g x, and
+    each row's normalised, quantised new key written into the MXFP8 cache kI
+    ([num_blocks, 66, D_I] uint8).  x [rows, D_x], w_q [H_I * D_I, D_x], w_g
+    [H_I, D_x], k_new [rows, D_I], k_gamma [D_I], all bf16."""
+    _check(load().dsa_indexer_prolog(ctypes.byref(prob), int(x.shape[1]), float(eps), _ptr(x),
+                                     _ptr(w_q), _ptr(w_g), _ptr(k_new), _ptr(k_gamma), _ptr(qI),
+                                     _ptr(qI_scale), _ptr(w), paged(kI), _ptr(ws), ws.numel(),
+                                     _stream(stream)), "dsa_indexer_prolog")
 
 
 def raw_call(name, *args):

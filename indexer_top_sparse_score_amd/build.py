@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["dsa_api.hip", "indexer_scan.hip", "topk.hip", "sparse_attn.hip"]
+SOURCES = ["dsa_api.hip", "indexer_scan.hip", "topk.hip", "sparse_attn.hip", "prolog.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -86,6 +86,15 @@ int check_kI(const dsa_problem* p, const dsa_paged& kI) {
   return DSA_OK;
 }
 
+// The prolog writes MXFP8 operands: the indexer shape with that format.
+int check_prolog_shape(const dsa_problem* p) {
+  if (p->indexer_format != DSA_INDEXER_MXFP8) return DSA_ERR_INVALID;
+  if (p->H_I < 1 || p->D_I < 1) return DSA_ERR_INVALID;
+  if (p->H_I > 64) return DSA_ERR_UNSUPPORTED;
+  if (p->D_I != 64 && p->D_I != 128) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
+}
+
 int check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return DSA_ERR_INVALID;
@@ -389,9 +398,54 @@ size_t dsa_workspace_size(const dsa_problem* p, int op) {
       if (check_indexer_shape(p) != DSA_OK || check_attn_shape(p) != DSA_OK) return 0;
       if (p->num_rows == 0) return kHeader;
       return decode_layout(p).total;
+    case DSA_OP_INDEXER_PROLOG:
+      return check_prolog_shape(p) == DSA_OK ? kHeader : 0;
     default:
       return 0;
   }
+}
+
+int dsa_indexer_prolog(const dsa_problem* p, int32_t D_x, float eps, const uint16_t* x,
+                       const uint16_t* w_q, const uint16_t* w_g, const uint16_t* k_new,
+                       const uint16_t* k_gamma, uint8_t* qI, uint8_t* qI_scale, float* w,
+                       dsa_paged kI, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_rows(p);
+  if (st != DSA_OK) return st;
+  if ((st = check_prolog_shape(p)) != DSA_OK) return st;
+  if (D_x < 32 || D_x % 32) return DSA_ERR_INVALID;
+  if (D_x > 65536) return DSA_ERR_UNSUPPORTED;
+  if (!std::isfinite(eps) || eps < 0.0f) return DSA_ERR_INVALID;
+  if (!x || !w_q || !w_g || !k_new || !k_gamma || !qI || !qI_scale || !w) return DSA_ERR_INVALID;
+  if (!aligned(x, 16) || !aligned(w_q, 16) || !aligned(w_g, 16) || !aligned(qI, 16) ||
+      !aligned(k_new, 4) || !aligned(k_gamma, 4) || !aligned(w, 4))
+    return DSA_ERR_INVALID;
+  if ((st = check_kI(p, kI)) != DSA_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, kHeader)) != DSA_OK) return st;
+  if (p->num_rows == 0) return DSA_OK;
+  PrologLaunch a;
+  a.rows = row_map(p);
+  a.rows.cand = nullptr;  // the prolog writes each row's own position
+  a.rows.cand_len = nullptr;
+  a.rows.n_cand = 0;
+  a.x = x;
+  a.w_q = w_q;
+  a.w_g = w_g;
+  a.k_new = k_new;
+  a.k_gamma = k_gamma;
+  a.qI = qI;
+  a.qI_scale = qI_scale;
+  a.w = w;
+  a.kI = static_cast<uint8_t*>(const_cast<void*>(kI.base));
+  a.kI_block_stride = kI.block_stride;
+  a.kI_row_stride = kI.row_stride;
+  a.kI_num_blocks = kI.num_blocks;
+  a.err = static_cast<uint32_t*>(ws);
+  a.num_rows = p->num_rows;
+  a.D_x = D_x;
+  a.H_I = p->H_I;
+  a.D_I = p->D_I;
+  a.eps = eps;
+  return status_of(launch_indexer_prolog(a, static_cast<hipStream_t>(stream)));
 }
 
 int dsa_indexer_scores(const dsa_problem* p, const uint8_t* qI, const float* w, dsa_paged kI,

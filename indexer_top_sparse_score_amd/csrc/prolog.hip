@@ -1,0 +1,252 @@
+// Indexer prolog on gfx950 (Baidu AI Cloud, "Day0 Inference Support and
+// Performance Optimization for New Architecture LLMs", section 4.3): the Q
+// projection with its per-group MXFP8 quantisation (section 5.1), the
+// head-weight projection, and the RMS normalisation and quantisation of each
+// row's new index key, written into the paged index-key cache.
+//
+// The page overlaps these small operators on three streams.  They are
+// independent of one another, so here they are one dispatch whose grid is cut
+// into three ranges of workgroups, one per operator, and the quantisation is
+// the projection's epilogue: no intermediate tensor goes through memory and
+// there is one launch instead of five.
+//
+// Projections: bf16 products, float32 accumulation (v_mfma_f32_16x16x32_bf16,
+// A = 16 weight rows x 32 inputs, B = 32 inputs x 16 rows of x).  A
+// workgroup owns 32 output features -- one quantisation group of one head,
+// or 32 head weights -- for 16 NT rows.  Its KS waves split the input width;
+// each streams its slice of the 32 weight rows straight into A operands (a
+// load is 16 rows x 64 contiguous bytes) and accumulates the whole tile; the
+// partial tiles are summed through LDS.  The weights are read once per tile
+// of rows: for decode batches of at most 16 rows, once.
+//
+// Arithmetic of the outputs (readings of the page): q, the normalised key
+// and the head weights are bf16 tensors, each the float32 result rounded to
+// nearest even; a group of 32 values shares the scale 2^(floor(log2 amax) -
+// 8) (the OCP microscaling rule, 8 being E4M3's largest exponent; 2^-127 for
+// an all-zero group), and each code is its value over the scale rounded to
+// nearest even in E4M3 and saturated at +-448.
+
+#include "dsa_common.h"
+
+namespace dsa {
+namespace {
+
+// x rounded to nearest even at bf16's 8 significant bits (finite x): adding
+// 0x7FFF plus the kept part's last bit carries exactly past a tie to even.
+__device__ __forceinline__ float bf16_round_f(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return __uint_as_float(u & 0xFFFF0000u);
+}
+
+// E4M3 (OCP FN) code of x, rounded to nearest even, magnitudes from 448 up
+// saturated to 448, the sign bit x's own.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.0f);
+  uint32_t code;
+  if (a < 0.015625f) {  // below 2^-6: multiples of 2^-9 (code 8 is 2^-6)
+    code = (uint32_t)rintf(a * 512.0f);
+  } else {
+    int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;  // 2^e <= a < 2^(e+1)
+    uint32_t m = (uint32_t)rintf((ldexpf(a, -e) - 1.0f) * 8.0f);
+    if (m == 8u) {
+      m = 0u;
+      ++e;
+    }
+    code = ((uint32_t)(e + 7) << 3) | m;
+    code = code > 0x7Eu ? 0x7Eu : code;
+  }
+  return code | sign;
+}
+
+// The group's shared exponent from its largest magnitude (float bits):
+// floor(log2 amax) - 8, clamped to E8M0's -127 .. 127; zero and subnormal
+// maxima give -127.
+__device__ __forceinline__ int mx_shared_exp(float amax) {
+  const int e = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 8;
+  return e < -127 ? -127 : e > 127 ? 127 : e;
+}
+
+// Maximum over the 16 lanes of this lane's row.
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp_f<0x140>(x));  // row_mirror
+  return x;
+}
+// Maximum over the aligned 32 lanes (two rows) holding this lane.
+__device__ __forceinline__ float lanes32_max(float x) { return xor16(row16_max(x), FMax{}); }
+
+// Workgroup -> unit of a range of n units, dealt so that the units each XCD
+// runs are consecutive (workgroups go to the 8 XCDs in turn): tiles of rows
+// that share a feature group share its weight rows through one L2.
+__device__ __forceinline__ int xcd_unit(int bid, int n) {
+  const int per = n / 8, rem = n % 8, x = bid % 8, slot = bid / 8;
+  return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + slot;
+}
+
+template <int NT, int KS>
+__global__ __launch_bounds__(64 * KS) void prolog_kernel(PrologLaunch a) {
+  constexpr int kRows = 16 * NT;                 // rows per tile
+  constexpr int kU = NT == 1 ? 8 : 4;            // 32-wide input steps per batch of loads
+  __shared__ float red[KS][2 * NT * 256];        // the waves' partial tiles
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int F = a.H_I * a.D_I;
+  const int rtiles = (a.num_rows + kRows - 1) / kRows;
+  const int nq = (F / 32) * rtiles, ng = ((a.H_I + 31) / 32) * rtiles;
+  const int bid = blockIdx.x;
+
+  if (bid >= nq + ng) {
+    // ---- K normalisation and quantisation: one wave per row
+    const int r = (bid - nq - ng) * KS + wave;
+    if (r >= a.num_rows) return;
+    int b, p;
+    if (!resolve_row(a.rows, r, b, p)) {
+      if (lane == 0) report(a.err, DSA_DEVERR_ROW);
+      return;
+    }
+    const int page = a.rows.block_table[(int64_t)b * a.rows.max_blocks + p / kBlock];
+    if (page < 0 || page >= a.kI_num_blocks) {
+      if (lane == 0) report(a.err, DSA_DEVERR_BLOCK);
+      return;
+    }
+    const uint16_t* kr = a.k_new + (int64_t)r * a.D_I;
+    float k0, k1 = 0.0f, g0, g1 = 0.0f;
+    if (a.D_I == 128) {  // two elements per lane: 2l, 2l + 1
+      const uint32_t kv = *reinterpret_cast<const uint32_t*>(kr + 2 * lane);
+      const uint32_t gv = *reinterpret_cast<const uint32_t*>(a.k_gamma + 2 * lane);
+      k0 = __uint_as_float(kv << 16);
+      k1 = __uint_as_float(kv & 0xFFFF0000u);
+      g0 = __uint_as_float(gv << 16);
+      g1 = __uint_as_float(gv & 0xFFFF0000u);
+    } else {  // D_I = 64: element l
+      k0 = __uint_as_float((uint32_t)kr[lane] << 16);
+      g0 = __uint_as_float((uint32_t)a.k_gamma[lane] << 16);
+    }
+    const float ss = across_wave(k0 * k0 + k1 * k1, FAdd{});
+    const float inv = 1.0f / sqrtf(ss / (float)a.D_I + a.eps);
+    const float y0 = bf16_round_f(k0 * inv * g0), y1 = bf16_round_f(k1 * inv * g1);
+    // a group of 32 elements is 16 lanes (D_I = 128) or 32 lanes (D_I = 64)
+    const float m = fmaxf(fabsf(y0), fabsf(y1));
+    const float amax = a.D_I == 128 ? row16_max(m) : lanes32_max(m);
+    const int se = mx_shared_exp(amax);
+    uint8_t* blk = a.kI + (int64_t)page * a.kI_block_stride;
+    uint8_t* crow = blk + (int64_t)(p % kBlock) * a.kI_row_stride;
+    uint8_t* srow = blk + (int64_t)kBlock * a.kI_row_stride + (p % kBlock) * (a.D_I / 32);
+    if (a.D_I == 128) {
+      const uint32_t c = e4m3_code(ldexpf(y0, -se)) | (e4m3_code(ldexpf(y1, -se)) << 8);
+      *reinterpret_cast<uint16_t*>(crow + 2 * lane) = (uint16_t)c;
+      if ((lane & 15) == 0) srow[lane >> 4] = (uint8_t)(se + 127);
+    } else {
+      crow[lane] = (uint8_t)e4m3_code(ldexpf(y0, -se));
+      if ((lane & 31) == 0) srow[lane >> 5] = (uint8_t)(se + 127);
+    }
+    return;
+  }
+
+  // ---- a projection tile: 32 features x kRows rows
+  const bool is_q = bid < nq;
+  const int unit = is_q ? xcd_unit(bid, nq) : bid - nq;
+  const int fgroup = unit / rtiles, rtile = unit % rtiles;
+  const int f0 = 32 * fgroup, r0 = kRows * rtile;
+  const uint16_t* W = is_q ? a.w_q : a.w_g;
+  const int nfeat = is_q ? F : a.H_I;
+  const int cidx = lane & 15, kg = lane >> 4;
+  const uint16_t* wrow[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int f = min(f0 + 16 * mt + cidx, nfeat - 1);  // past the last feature: unused
+    wrow[mt] = W + (int64_t)f * a.D_x + 8 * kg;
+  }
+  const uint16_t* xrow[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = min(r0 + 16 * nt + cidx, a.num_rows - 1);  // past the last row: unused
+    xrow[nt] = a.x + (int64_t)r * a.D_x + 8 * kg;
+  }
+  const int nsteps = a.D_x / 32;
+  const int per = (nsteps + KS - 1) / KS;
+  const int s0 = wave * per, s1 = min(nsteps, s0 + per);
+  v4f acc[2][NT];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s = s0; s < s1; s += kU) {
+    v8s av[kU][2], bv[kU][NT];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int k = 32 * min(s + u, s1 - 1);  // a step past the slice reloads its last one
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) av[u][mt] = *reinterpret_cast<const v8s*>(wrow[mt] + k);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) bv[u][nt] = *reinterpret_cast<const v8s*>(xrow[nt] + k);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (s + u < s1) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(v8bf, av[u][mt]), __builtin_bit_cast(v8bf, bv[u][nt]),
+                acc[mt][nt], 0, 0, 0);
+      }
+    }
+  }
+  // lane l, register i of tile (mt, nt) holds feature 16 mt + 4 (l / 16) + i
+  // of the tile, row 16 nt + l % 16
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][(mt * NT + nt) * 256 + 64 * i + lane] = acc[mt][nt][i];
+  __syncthreads();
+
+  // epilogue: 32 consecutive threads hold the 32 features of one row
+  const int feat = tid & 31, within = feat & 15, mt = feat >> 4;
+  const int src_lane_hi = 16 * (within >> 2), ireg = within & 3;
+#pragma unroll
+  for (int rl = tid >> 5; rl < kRows; rl += 2 * KS) {
+    const int nt = rl >> 4;
+    const int idx = (mt * NT + nt) * 256 + 64 * ireg + src_lane_hi + (rl & 15);
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < KS; ++w) v += red[w][idx];
+    const float vb = bf16_round_f(v);
+    const int r = r0 + rl;
+    if (is_q) {
+      const int se = mx_shared_exp(lanes32_max(fabsf(vb)));
+      if (r < a.num_rows) {
+        a.qI[(int64_t)r * F + f0 + feat] = (uint8_t)e4m3_code(ldexpf(vb, -se));
+        if (feat == 0) a.qI_scale[(int64_t)r * (F / 32) + fgroup] = (uint8_t)(se + 127);
+      }
+    } else if (r < a.num_rows && f0 + feat < a.H_I) {
+      a.w[(int64_t)r * a.H_I + f0 + feat] = vb;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_indexer_prolog(const PrologLaunch& a, hipStream_t s) {
+  const int F = a.H_I * a.D_I;
+  if (a.num_rows <= 16) {
+    constexpr int NT = 1, KS = 8;
+    const int rt = (a.num_rows + 16 * NT - 1) / (16 * NT);
+    const int n = (F / 32) * rt + ((a.H_I + 31) / 32) * rt + (a.num_rows + KS - 1) / KS;
+    prolog_kernel<NT, KS><<<n, 64 * KS, 0, s>>>(a);
+  } else {
+    constexpr int NT = 4, KS = 4;
+    const int rt = (a.num_rows + 16 * NT - 1) / (16 * NT);
+    const int n = (F / 32) * rt + ((a.H_I + 31) / 32) * rt + (a.num_rows + KS - 1) / KS;
+    prolog_kernel<NT, KS><<<n, 64 * KS, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -27,7 +27,7 @@ def lib():
 
 def test_exports_every_header_symbol(lib):
     syms = header_symbols()
-    assert len(syms) == 9 and sorted(B.EXPORTS) == syms
+    assert len(syms) == 10 and sorted(B.EXPORTS) == syms
     for s in syms:
         assert getattr(lib, s) is not None
     assert lib.dsa_abi_version() == B.ABI_VERSION
@@ -250,3 +250,41 @@ def test_decode_step_timed_rejections():
     assert call(prob(H_I=100), eight) == B.DSA_ERR_UNSUPPORTED
     assert call(prob(), eight, ws_bytes=0) == B.DSA_ERR_WORKSPACE
     assert call(prob(num_rows=0), eight) == B.DSA_OK
+
+
+def call_prolog(p, D_x=4096, eps=1e-6, x=FAKE, w_q=FAKE + (1 << 28), w_g=FAKE + (2 << 28),
+                k_new=FAKE + (3 << 28), k_gamma=FAKE + (4 << 28), qI=FAKE + (5 << 28),
+                qI_scale=FAKE + (6 << 28), w=FAKE + (7 << 28), kI=None, ws=FAKE + (8 << 28),
+                ws_bytes=256):
+    V = ctypes.c_void_p
+    return B.raw_call("dsa_indexer_prolog", ctypes.byref(p), ctypes.c_int32(D_x),
+                      ctypes.c_float(eps), V(x), V(w_q), V(w_g), V(k_new), V(k_gamma), V(qI),
+                      V(qI_scale), V(w), kI or B.DsaPaged(FAKE + (1 << 30), 64 * 128 + 256, 128, 8192),
+                      V(ws), ctypes.c_size_t(ws_bytes), None)
+
+
+def test_indexer_prolog_rejections():
+    mx = dict(indexer_format=B.DSA_INDEXER_MXFP8)
+    p = prob(**mx)
+    assert ws_size(p, B.DSA_OP_INDEXER_PROLOG) == 256
+    assert ws_size(prob(), B.DSA_OP_INDEXER_PROLOG) == 0               # not MXFP8
+    assert call_prolog(prob(num_rows=0, **mx)) == B.DSA_OK              # empty: nothing runs
+    assert call_prolog(prob(num_rows=0, D_I=64, **mx),
+                       kI=B.DsaPaged(FAKE, 64 * 64 + 128, 64, 4)) == B.DSA_OK
+    assert call_prolog(prob()) == B.DSA_ERR_INVALID                     # E4M3 format
+    assert call_prolog(prob(D_I=96, **mx)) == B.DSA_ERR_UNSUPPORTED
+    assert call_prolog(prob(H_I=65, **mx)) == B.DSA_ERR_UNSUPPORTED
+    assert call_prolog(p, D_x=0) == B.DSA_ERR_INVALID
+    assert call_prolog(p, D_x=4016) == B.DSA_ERR_INVALID                # not a multiple of 32
+    assert call_prolog(p, D_x=65536 + 32) == B.DSA_ERR_UNSUPPORTED
+    assert call_prolog(p, eps=-1.0) == B.DSA_ERR_INVALID
+    assert call_prolog(p, eps=float("nan")) == B.DSA_ERR_INVALID
+    for arg in ("x", "w_q", "w_g", "k_new", "k_gamma", "qI", "qI_scale", "w"):
+        assert call_prolog(p, **{arg: 0}) == B.DSA_ERR_INVALID, arg
+    for arg, off in (("x", 8), ("w_q", 8), ("w_g", 8), ("qI", 8), ("k_new", 2),
+                     ("k_gamma", 2), ("w", 2)):
+        assert call_prolog(p, **{arg: FAKE + off}) == B.DSA_ERR_INVALID, arg   # misaligned
+    assert call_prolog(p, kI=B.DsaPaged(FAKE, 64 * 128, 128, 8)) == B.DSA_ERR_INVALID  # no scale room
+    assert call_prolog(p, ws=0) == B.DSA_ERR_WORKSPACE
+    assert call_prolog(p, ws_bytes=255) == B.DSA_ERR_WORKSPACE
+    assert call_prolog(prob(seq_lens=None, **mx)) == B.DSA_ERR_INVALID

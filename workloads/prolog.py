@@ -41,8 +41,11 @@ class PrologInputs:
         return self.x.shape[1]
 
 
-def make_prolog_inputs(rows, H_I, D_I, D_x=PROLOG_D_X, mode="gauss", seed=0, device="cpu"):
-    """Draw the prolog's inputs for ``rows`` rows from ``seed``."""
+def make_prolog_inputs(rows, H_I, D_I, D_x=PROLOG_D_X, mode="gauss", seed=0, device="cpu",
+                       key_pm4=False):
+    """Draw the prolog's inputs for ``rows`` rows from ``seed``.  ``key_pm4``:
+    every new-key element is +4 or -4 (random signs), a key whose RMS is
+    exactly 4."""
     device = torch.device(device)
     g = torch.Generator(device=device)
     g.manual_seed(seed * 104729 + 31)
@@ -68,6 +71,9 @@ def make_prolog_inputs(rows, H_I, D_I, D_x=PROLOG_D_X, mode="gauss", seed=0, dev
         k_gamma = (1.0 + 0.1 * torch.randn((D_I,), generator=g, device=device)).to(bf)
     else:
         raise ValueError(f"mode {mode!r}")
+    if key_pm4:
+        signs = torch.randint(0, 2, (rows, D_I), generator=g, device=device)
+        k_new = (signs * 8 - 4).to(bf)
     return PrologInputs(x=x, w_q=w_q, w_g=w_g, k_new=k_new, k_gamma=k_gamma)
 
 
