@@ -38,6 +38,10 @@ read_reference a library streaming read (torch.sum over 1 GiB) as a reference fo
 candidate_indexer  the same workload with a candidate-restricted indexer
            (16384 candidate positions per row): the fused step and the scan
            alone, timed the same way (--no-cand skips it)
+indexer_prolog  dsa_indexer_prolog for the headline's rows and for 4096 prefill
+           rows (4096-wide input, 64 x 128 MXFP8 outputs): launch time, HBM
+           fraction of its weight stream, bf16 MFMA fraction (--no-prolog
+           skips it)
 fp8_kv_cache  the same workload over an FP8 KV cache (E4M3 latent rows, one
            float32 scale per tile of 128 elements): the fused step and its
            stage times, with the attention's HBM fraction (--no-fp8-kv skips it)
@@ -79,6 +83,8 @@ def parse():
                     help="skip the candidate-restricted indexer leg")
     ap.add_argument("--no-mxfp8", action="store_true",
                     help="skip the MXFP8-indexer leg (same workload, group-32 scales)")
+    ap.add_argument("--no-prolog", action="store_true",
+                    help="skip the indexer-prolog leg (q and head-weight projections, key norm)")
     ap.add_argument("--no-fp8-kv", action="store_true",
                     help="skip the FP8-KV-cache leg (same workload, E4M3 rows, tile-128 scales)")
     ap.add_argument("--table", default=None)
@@ -314,6 +320,9 @@ def main():
     if not args.no_fp8_kv:
         log("fp8 kv leg")
         result["fp8_kv_cache"] = guarded(fp8_kv_leg, args, wl, lengths, stream)
+    if not args.no_prolog:
+        log("indexer prolog leg")
+        result["indexer_prolog"] = guarded(prolog_leg, args, wl, stream)
     legs = [x for x in args.legs.split(",") if x and x != "none" and x != name]
     if legs:
         del sets, probs, outs, graphs
@@ -694,6 +703,61 @@ def fp8_kv_leg(args, wl, lengths, stream):
             "attention_gbs": round(ab / (st["attention_us"] * 1e-6) / 1e9, 1),
             "attention_hbm_frac": round(ab / (st["attention_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "stages": st}
+
+
+def prolog_leg(args, wl, stream):
+    """dsa_indexer_prolog over a 4096-wide input for the headline's rows and
+    for 4096 prefill rows: average launch time (HIP events on the launch
+    stream, input sets rotating past the Infinity Cache), algorithmic bytes
+    (both weight matrices, x, the new keys and every output) and flops."""
+    import torch
+    from indexer_top_sparse_score_amd import binding as B
+    from workloads import PROLOG_D_X, make_batch, make_prolog_inputs, small_workload
+    dev = torch.device("cuda:0")
+    out = {"D_x": PROLOG_D_X, "indexer": f"{wl.H_I}x{wl.D_I} mxfp8"}
+    F = wl.H_I * wl.D_I
+    for label, rows in (("decode", wl.rows), ("prefill", 4096)):
+        pw = small_workload("prolog", lengths=[64 * (1 + i % 16) for i in range(rows)],
+                            H_I=wl.H_I, D_I=wl.D_I, mode="int", indexer_fmt="mxfp8",
+                            H_q=wl.H_q, D_qk=wl.D_qk, D_v=wl.D_v, K=wl.K, scale=wl.scale)
+        batch = make_batch(pw, device=dev, seed=pw.seed + 11)
+        wbytes = 2 * (F + wl.H_I) * PROLOG_D_X
+        nset = max(1, min(16, -(-4 * MALL_BYTES // wbytes))) if rows <= 64 else 2
+        inps = [make_prolog_inputs(rows, wl.H_I, wl.D_I, D_x=PROLOG_D_X, mode="gauss",
+                                   seed=100 + i, device=dev) for i in range(nset)]
+        prob = B.problem_for_batch(batch)
+        qI = torch.empty((rows, wl.H_I, wl.D_I), dtype=torch.uint8, device=dev)
+        qs = torch.empty((rows, wl.H_I, wl.D_I // 32), dtype=torch.uint8, device=dev)
+        w = torch.empty((rows, wl.H_I), dtype=torch.float32, device=dev)
+        ws = B.workspace(prob, B.DSA_OP_INDEXER_PROLOG, device=dev)
+
+        def run(i):
+            inp = inps[i % nset]
+            B.dsa_indexer_prolog(prob, inp.x, inp.w_q, inp.w_g, inp.k_new, inp.k_gamma, qI, qs,
+                                 w, batch.kI, ws, stream=stream)
+
+        steps = args.steps if rows <= 64 else max(5, args.steps // 5)
+        with torch.cuda.stream(stream):
+            for i in range(args.warmup):
+                run(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(steps):
+                run(i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        assert B.device_errors(ws) == 0
+        us = 1e3 * e0.elapsed_time(e1) / steps
+        byt = (wbytes + 2 * rows * PROLOG_D_X + 2 * rows * wl.D_I + 2 * wl.D_I
+               + rows * (F + F // 32 + 4 * wl.H_I) + rows * (wl.D_I + wl.D_I // 32))
+        flops = 2 * rows * (F + wl.H_I) * PROLOG_D_X
+        out[label] = {"rows": rows, "rotation_sets": nset, "avg_launch_us": round(us, 3),
+                      "bytes": byt, "gbs": round(byt / (us * 1e-6) / 1e9, 1),
+                      "hbm_frac": round(byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                      "tflops": round(flops / (us * 1e-6) / 1e12, 2),
+                      "bf16_mfma_frac": round(flops / (us * 1e-6) / 1e12 / 2500.0, 4)}
+        del inps, batch
+    return out
 
 
 def cand_leg(args, wl, lengths, stream, n_cand=16384):

@@ -7,6 +7,7 @@
 #include <mutex>
 
 #include "dsa_common.h"
+#include "prolog.h"
 
 namespace dsa {
 namespace {

@@ -27,6 +27,7 @@
 // nearest even in E4M3 and saturated at +-448.
 
 #include "dsa_common.h"
+#include "prolog.h"
 
 namespace dsa {
 namespace {
@@ -87,6 +88,70 @@ __device__ __forceinline__ int xcd_unit(int bid, int n) {
   return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + slot;
 }
 
+// The new key of row r (one wave): RMS-normalised with gamma, rounded to
+// bf16, MXFP8-quantised and written at the row's slot of the key cache.
+__device__ __forceinline__ void key_norm_row(const PrologLaunch& a, int r, int lane) {
+  int b, p;
+  if (!resolve_row(a.rows, r, b, p)) {
+    if (lane == 0) report(a.err, DSA_DEVERR_ROW);
+    return;
+  }
+  const int page = a.rows.block_table[(int64_t)b * a.rows.max_blocks + p / kBlock];
+  if (page < 0 || page >= a.kI_num_blocks) {
+    if (lane == 0) report(a.err, DSA_DEVERR_BLOCK);
+    return;
+  }
+  const uint16_t* kr = a.k_new + (int64_t)r * a.D_I;
+  float k0, k1 = 0.0f, g0, g1 = 0.0f;
+  if (a.D_I == 128) {  // two elements per lane: 2l, 2l + 1
+    const uint32_t kv = *reinterpret_cast<const uint32_t*>(kr + 2 * lane);
+    const uint32_t gv = *reinterpret_cast<const uint32_t*>(a.k_gamma + 2 * lane);
+    k0 = __uint_as_float(kv << 16);
+    k1 = __uint_as_float(kv & 0xFFFF0000u);
+    g0 = __uint_as_float(gv << 16);
+    g1 = __uint_as_float(gv & 0xFFFF0000u);
+  } else {  // D_I = 64: element l
+    k0 = __uint_as_float((uint32_t)kr[lane] << 16);
+    g0 = __uint_as_float((uint32_t)a.k_gamma[lane] << 16);
+  }
+  const float ss = across_wave(k0 * k0 + k1 * k1, FAdd{});
+  const float inv = 1.0f / sqrtf(ss / (float)a.D_I + a.eps);
+  const float y0 = bf16_round_f(k0 * inv * g0), y1 = bf16_round_f(k1 * inv * g1);
+  // a group of 32 elements is 16 lanes (D_I = 128) or 32 lanes (D_I = 64)
+  const float m = fmaxf(fabsf(y0), fabsf(y1));
+  const float amax = a.D_I == 128 ? row16_max(m) : lanes32_max(m);
+  const int se = mx_shared_exp(amax);
+  uint8_t* blk = a.kI + (int64_t)page * a.kI_block_stride;
+  uint8_t* crow = blk + (int64_t)(p % kBlock) * a.kI_row_stride;
+  uint8_t* srow = blk + (int64_t)kBlock * a.kI_row_stride + (p % kBlock) * (a.D_I / 32);
+  if (a.D_I == 128) {
+    const uint32_t c = e4m3_code(ldexpf(y0, -se)) | (e4m3_code(ldexpf(y1, -se)) << 8);
+    *reinterpret_cast<uint16_t*>(crow + 2 * lane) = (uint16_t)c;
+    if ((lane & 15) == 0) srow[lane >> 4] = (uint8_t)(se + 127);
+  } else {
+    crow[lane] = (uint8_t)e4m3_code(ldexpf(y0, -se));
+    if ((lane & 31) == 0) srow[lane >> 5] = (uint8_t)(se + 127);
+  }
+}
+
+// One output of a projection, by the 32 consecutive lanes that hold a
+// feature group of one row (feature f0 + feat, value v): q values go out as
+// MXFP8 codes with the group's scale, head weights as float32.
+__device__ __forceinline__ void store_output(const PrologLaunch& a, bool is_q, int r, int fgroup,
+                                             int feat, float v) {
+  const int F = a.H_I * a.D_I, f0 = 32 * fgroup;
+  const float vb = bf16_round_f(v);
+  if (is_q) {
+    const int se = mx_shared_exp(lanes32_max(fabsf(vb)));
+    if (r < a.num_rows) {
+      a.qI[(int64_t)r * F + f0 + feat] = (uint8_t)e4m3_code(ldexpf(vb, -se));
+      if (feat == 0) a.qI_scale[(int64_t)r * (F / 32) + fgroup] = (uint8_t)(se + 127);
+    }
+  } else if (r < a.num_rows && f0 + feat < a.H_I) {
+    a.w[(int64_t)r * a.H_I + f0 + feat] = vb;
+  }
+}
+
 template <int NT, int KS>
 __global__ __launch_bounds__(64 * KS) void prolog_kernel(PrologLaunch a) {
   constexpr int kRows = 16 * NT;                 // rows per tile
@@ -98,51 +163,9 @@ __global__ __launch_bounds__(64 * KS) void prolog_kernel(PrologLaunch a) {
   const int nq = (F / 32) * rtiles, ng = ((a.H_I + 31) / 32) * rtiles;
   const int bid = blockIdx.x;
 
-  if (bid >= nq + ng) {
-    // ---- K normalisation and quantisation: one wave per row
+  if (bid >= nq + ng) {  // K normalisation and quantisation: one wave per row
     const int r = (bid - nq - ng) * KS + wave;
-    if (r >= a.num_rows) return;
-    int b, p;
-    if (!resolve_row(a.rows, r, b, p)) {
-      if (lane == 0) report(a.err, DSA_DEVERR_ROW);
-      return;
-    }
-    const int page = a.rows.block_table[(int64_t)b * a.rows.max_blocks + p / kBlock];
-    if (page < 0 || page >= a.kI_num_blocks) {
-      if (lane == 0) report(a.err, DSA_DEVERR_BLOCK);
-      return;
-    }
-    const uint16_t* kr = a.k_new + (int64_t)r * a.D_I;
-    float k0, k1 = 0.0f, g0, g1 = 0.0f;
-    if (a.D_I == 128) {  // two elements per lane: 2l, 2l + 1
-      const uint32_t kv = *reinterpret_cast<const uint32_t*>(kr + 2 * lane);
-      const uint32_t gv = *reinterpret_cast<const uint32_t*>(a.k_gamma + 2 * lane);
-      k0 = __uint_as_float(kv << 16);
-      k1 = __uint_as_float(kv & 0xFFFF0000u);
-      g0 = __uint_as_float(gv << 16);
-      g1 = __uint_as_float(gv & 0xFFFF0000u);
-    } else {  // D_I = 64: element l
-      k0 = __uint_as_float((uint32_t)kr[lane] << 16);
-      g0 = __uint_as_float((uint32_t)a.k_gamma[lane] << 16);
-    }
-    const float ss = across_wave(k0 * k0 + k1 * k1, FAdd{});
-    const float inv = 1.0f / sqrtf(ss / (float)a.D_I + a.eps);
-    const float y0 = bf16_round_f(k0 * inv * g0), y1 = bf16_round_f(k1 * inv * g1);
-    // a group of 32 elements is 16 lanes (D_I = 128) or 32 lanes (D_I = 64)
-    const float m = fmaxf(fabsf(y0), fabsf(y1));
-    const float amax = a.D_I == 128 ? row16_max(m) : lanes32_max(m);
-    const int se = mx_shared_exp(amax);
-    uint8_t* blk = a.kI + (int64_t)page * a.kI_block_stride;
-    uint8_t* crow = blk + (int64_t)(p % kBlock) * a.kI_row_stride;
-    uint8_t* srow = blk + (int64_t)kBlock * a.kI_row_stride + (p % kBlock) * (a.D_I / 32);
-    if (a.D_I == 128) {
-      const uint32_t c = e4m3_code(ldexpf(y0, -se)) | (e4m3_code(ldexpf(y1, -se)) << 8);
-      *reinterpret_cast<uint16_t*>(crow + 2 * lane) = (uint16_t)c;
-      if ((lane & 15) == 0) srow[lane >> 4] = (uint8_t)(se + 127);
-    } else {
-      crow[lane] = (uint8_t)e4m3_code(ldexpf(y0, -se));
-      if ((lane & 31) == 0) srow[lane >> 5] = (uint8_t)(se + 127);
-    }
+    if (r < a.num_rows) key_norm_row(a, r, lane);
     return;
   }
 
@@ -217,17 +240,172 @@ __global__ __launch_bounds__(64 * KS) void prolog_kernel(PrologLaunch a) {
     float v = 0.0f;
 #pragma unroll
     for (int w = 0; w < KS; ++w) v += red[w][idx];
-    const float vb = bf16_round_f(v);
-    const int r = r0 + rl;
-    if (is_q) {
-      const int se = mx_shared_exp(lanes32_max(fabsf(vb)));
-      if (r < a.num_rows) {
-        a.qI[(int64_t)r * F + f0 + feat] = (uint8_t)e4m3_code(ldexpf(vb, -se));
-        if (feat == 0) a.qI_scale[(int64_t)r * (F / 32) + fgroup] = (uint8_t)(se + 127);
-      }
-    } else if (r < a.num_rows && f0 + feat < a.H_I) {
-      a.w[(int64_t)r * a.H_I + f0 + feat] = vb;
+    store_output(a, is_q, r0 + rl, fgroup, feat, v);
+  }
+}
+
+// Decode batches of at most R rows: the projections as
+// matrix-vector products on the vector ALUs, so that every weight load is
+// one contiguous kilobyte (lane l reads 8 consecutive inputs of one weight
+// row) -- the access HBM and the address units serve best -- instead of the
+// 16 rows x 64 bytes an MFMA operand needs.  A workgroup of 16 waves owns
+// one q group of 32 features, 2 per wave.  Per chunk of
+// inputs each wave issues all its weight loads at once (2 features x 4096
+// inputs: 16 KB in flight per wave, 256 KB per CU), the chunk's R rows of x
+// are staged in LDS meanwhile, and each lane keeps float32 partial sums for
+// its 2 features x R rows, reduced across the wave at the end.
+__device__ __forceinline__ void bf16x8_to_f32(const uint4 v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+// Head weight h of every row (one wave, at most kRmax rows): w[r][h] =
+// bf16(W_g[h] . x[r]), the weight row and the rows of x read in contiguous
+// kilobytes, two 512-input steps per batch of loads.
+template <int kRmax>
+__device__ __forceinline__ void head_weight(const PrologLaunch& a, int h, int lane) {
+  constexpr int kJ = 2;
+  const int R = a.num_rows < kRmax ? a.num_rows : kRmax;
+  float acc[kRmax];
+#pragma unroll
+  for (int r = 0; r < kRmax; ++r) acc[r] = 0.0f;
+  const uint16_t* wrow = a.w_g + (int64_t)h * a.D_x + 8 * lane;
+  for (int j0 = 0; 512 * j0 < a.D_x; j0 += kJ) {
+    // unconditional loads (a piece past the input reads the row's first
+    // piece, a row past the batch row 0; both are dropped where used)
+    uint4 wv[kJ], xv[kJ][kRmax];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int k = 512 * (j0 + j) + 8 * lane;
+      const int off = k < a.D_x ? 512 * (j0 + j) : -8 * lane;
+      wv[j] = *reinterpret_cast<const uint4*>(wrow + off);
+#pragma unroll
+      for (int r = 0; r < kRmax; ++r)
+        xv[j][r] = *reinterpret_cast<const uint4*>(a.x + (int64_t)(r < R ? r : 0) * a.D_x +
+                                                   (k < a.D_x ? k : 0));
     }
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      if (512 * (j0 + j) + 8 * lane >= a.D_x) continue;
+      float wf[8];
+      bf16x8_to_f32(wv[j], wf);
+#pragma unroll
+      for (int r = 0; r < kRmax; ++r) {
+        float xf[8];
+        bf16x8_to_f32(xv[j][r], xf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r] = fmaf(wf[e], xf[e], acc[r]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kRmax; ++r) {
+    const float v = across_wave(acc[r], FAdd{});
+    if (lane == 0 && r < R) a.w[(int64_t)r * a.H_I + h] = bf16_round_f(v);
+  }
+}
+
+template <int R>
+__global__ __launch_bounds__(1024) void prolog_gemv_kernel(PrologLaunch a) {
+  constexpr int kWaves = 16, kFW = 2;  // waves, features per wave
+  constexpr int KC = 16384 / R;        // inputs per chunk: 32 KB of x in LDS
+  constexpr int kJ = KC / 512;         // 512-input loads per feature and chunk
+  __shared__ __attribute__((aligned(16))) uint16_t xs[R * KC];
+  __shared__ float res[32][R + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int F = a.H_I * a.D_I;
+  const int nq = F / 32, ng = (a.H_I + kWaves - 1) / kWaves;
+  const int bid = blockIdx.x;
+  if (bid >= nq) {
+    // after the q groups (which fill the chip's CUs for a 64 x 128
+    // indexer), short workgroups: head weights, one wave per weight, then
+    // the new keys, one wave per row
+    if (bid < nq + ng) {
+      const int h = (bid - nq) * kWaves + wave;
+      if (h < a.H_I) head_weight<R>(a, h, lane);
+    } else {
+      const int r = (bid - nq - ng) * kWaves + wave;
+      if (r < a.num_rows) key_norm_row(a, r, lane);
+    }
+    return;
+  }
+  const int fgroup = bid;
+  const uint16_t* wr[kFW];  // this lane's weight rows
+#pragma unroll
+  for (int f = 0; f < kFW; ++f) wr[f] = a.w_q + (int64_t)(32 * fgroup + kFW * wave + f) * a.D_x;
+  float acc[kFW][R];
+#pragma unroll
+  for (int f = 0; f < kFW; ++f)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[f][r] = 0.0f;
+
+  static_assert(R * KC / 8 == 2 * 64 * kWaves, "two 16-byte pieces of x per thread");
+  for (int c0 = 0; c0 < a.D_x; c0 += KC) {
+    const int kc = min(KC, a.D_x - c0);  // a multiple of 32
+    // this thread's two pieces of the chunk's rows of x, loaded first so
+    // that waiting for them does not wait for the weights behind them
+    // (every load is issued unconditionally -- a piece past the chunk or
+    // past the last row reads a valid address, and its value is dropped
+    // only where it is used -- so that the waits count loads exactly)
+    uint4 xv[2];
+    int xo[2];
+    bool xok[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int i = tid + 64 * kWaves * t, r = i / (KC / 8), k8 = i % (KC / 8);
+      xok[t] = r < a.num_rows && 8 * k8 < kc;
+      xo[t] = r * KC + 8 * k8;
+      xv[t] = *reinterpret_cast<const uint4*>(a.x + (xok[t] ? (int64_t)r * a.D_x + c0 + 8 * k8 : 0));
+    }
+    // load j of a feature covers inputs c0 + 512 j + 8 lane + 0..7 (lanes
+    // past the chunk read its first piece and skip it below); the sums take
+    // the loads in issue order as they arrive
+    uint4 wv[kJ][kFW];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int off = 512 * j + 8 * lane < kc ? c0 + 512 * j + 8 * lane : c0;
+#pragma unroll
+      for (int f = 0; f < kFW; ++f) wv[j][f] = *reinterpret_cast<const uint4*>(wr[f] + off);
+    }
+    __syncthreads();  // the previous chunk's x reads are done
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      *reinterpret_cast<uint4*>(xs + xo[t]) = xok[t] ? xv[t] : uint4{0u, 0u, 0u, 0u};
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int kk = 512 * j + 8 * lane;
+      if (kk < kc) {
+        float wf[kFW][8];
+#pragma unroll
+        for (int f = 0; f < kFW; ++f) bf16x8_to_f32(wv[j][f], wf[f]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float xf[8];
+          bf16x8_to_f32(*reinterpret_cast<const uint4*>(xs + r * KC + kk), xf);
+#pragma unroll
+          for (int f = 0; f < kFW; ++f)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[f][r] = fmaf(wf[f][e], xf[e], acc[f][r]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int f = 0; f < kFW; ++f)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float v = across_wave(acc[f][r], FAdd{});
+      if (lane == 0) res[kFW * wave + f][r] = v;
+    }
+  __syncthreads();
+  if (tid < 32 * R) {  // whole waves: 32 R is a multiple of 64
+    const int r = tid >> 5, feat = tid & 31;
+    store_output(a, true, r, fgroup, feat, res[feat][r]);
   }
 }
 
@@ -235,10 +413,14 @@ __global__ __launch_bounds__(64 * KS) void prolog_kernel(PrologLaunch a) {
 
 hipError_t launch_indexer_prolog(const PrologLaunch& a, hipStream_t s) {
   const int F = a.H_I * a.D_I;
-  if (a.num_rows <= 16) {
+  const int ngemv = F / 32 + (a.H_I + 15) / 16 + (a.num_rows + 15) / 16;
+  // (measured at 4096 inputs, 64 x 128: 4 rows 25.6 us on the vector ALUs
+  // against 25.7 us on the MFMA tile; 8 rows 37.5 against 29.4 us)
+  if (a.num_rows <= 4) {
+    prolog_gemv_kernel<4><<<ngemv, 1024, 0, s>>>(a);
+  } else if (a.num_rows <= 16) {
     constexpr int NT = 1, KS = 8;
-    const int rt = (a.num_rows + 16 * NT - 1) / (16 * NT);
-    const int n = (F / 32) * rt + ((a.H_I + 31) / 32) * rt + (a.num_rows + KS - 1) / KS;
+    const int n = F / 32 + (a.H_I + 31) / 32 + (a.num_rows + KS - 1) / KS;
     prolog_kernel<NT, KS><<<n, 64 * KS, 0, s>>>(a);
   } else {
     constexpr int NT = 4, KS = 4;

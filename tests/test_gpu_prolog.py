@@ -39,7 +39,10 @@ CASES = {
     "decode4_gauss": ([3000, 64, 65, 2049], 64, 128, 4096, "gauss", "shuffled"),
     # one row, the narrowest input, the smallest indexer
     "one_row_tiny": ([1], 4, 64, 32, "int", "identity"),
-    # 16 rows (the largest decode tile) and 17 (the first of the wide tiles)
+    # 4 rows are the vector-ALU kernel's largest batch; 5, 8 and 16 rows take
+    # the 16-row MFMA tile, and 17 the first of the 64-row tiles
+    "rows5_gauss": ([7, 300, 64, 65, 1], 64, 128, 4096, "gauss", "identity"),
+    "rows8_int": ([1 + 97 * i for i in range(8)], 64, 64, 512, "int", "shuffled"),
     "rows16_gauss": ([5 + 37 * i for i in range(16)], 64, 128, 1024, "gauss", "shuffled"),
     "rows17_int": ([1 + 61 * i for i in range(17)], 8, 128, 96, "int", "identity"),
     # ragged row tiles, 48 heads (a half-filled head-weight tile), 64-dim heads
