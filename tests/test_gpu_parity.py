@@ -165,7 +165,19 @@ def test_sparse_attn_on_oracle_indices(name):
 
 @pytest.mark.parametrize("name", ["mla_int", "mla_fp8kv"])
 def test_sparse_attn_skips_padding_and_handles_empty_rows(name):
-    batch = _batch(name, mode="gauss", seed=26)
+    _padding_case(name)
+
+
+# a zero or negative logit scale must not turn the masked (absent) keys into
+# NaN or +inf: the kernels mask after scaling (regression test)
+@pytest.mark.parametrize("scale", [0.0, -1.0 / 24.0])
+@pytest.mark.parametrize("name", ["mla_int", "tiny_int", "mla_fp8kv"])
+def test_sparse_attn_padding_with_zero_and_negative_scale(name, scale):
+    _padding_case(name, scale=scale)
+
+
+def _padding_case(name, **over):
+    batch = _batch(name, mode="gauss", seed=26, **over)
     arr = oracle_arrays(batch)
     K = batch.wl.K
     rng = np.random.default_rng(26)
@@ -185,13 +197,18 @@ def test_sparse_attn_skips_padding_and_handles_empty_rows(name):
         if len(sel) == 0:
             continue
         k_rows = oracle.gather_positions(arr["k_cache"], arr["block_table"][b], sel)
+        D_v = batch.wl.D_v
         if arr["k_scale_cache"] is not None:
             kv = oracle.kv_fp8_to_f64(
                 k_rows, oracle.gather_positions(arr["k_scale_cache"], arr["block_table"][b], sel))
             want_o[i], want_l[i] = oracle.sparse_attn_values(
-                oracle.bf16_to_f64(arr["q"][i]), kv, kv[:, :512], batch.wl.scale)
+                oracle.bf16_to_f64(arr["q"][i]), kv, kv[:, :D_v], batch.wl.scale)
+        elif arr["v_cache"] is not None:
+            v_rows = oracle.gather_positions(arr["v_cache"], arr["block_table"][b], sel)
+            want_o[i], want_l[i] = oracle.sparse_attn_row(arr["q"][i], k_rows, v_rows,
+                                                          batch.wl.scale)
         else:
-            want_o[i], want_l[i] = oracle.sparse_attn_row(arr["q"][i], k_rows, k_rows[:, :512],
+            want_o[i], want_l[i] = oracle.sparse_attn_row(arr["q"][i], k_rows, k_rows[:, :D_v],
                                                           batch.wl.scale)
     slack = None
     if batch.wl.kv_fmt == "fp8":
