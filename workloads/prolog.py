@@ -5,8 +5,8 @@ arithmetic.
 
 Shapes: x [rows, D_x], w_q [H_I * D_I, D_x], w_g [H_I, D_x], k_new
 [rows, D_I], k_gamma [D_I].  The input width defaults to 4096, the input
-dimension THInfer fixes for its projection (GEMM) measurements; the pages
-give no model width for the indexer.
+dimension THInfer fixes for its Linear-operator measurements (experiments,
+part D); the pages give no model width for the indexer.
 
 Modes:
 * "int": x in {-2..2}, both weights in {-1, 0, 1}, k_new in {-3..3},
