@@ -181,6 +181,8 @@ int check_attn_args(const dsa_problem* p, const uint16_t* q, const dsa_paged& k,
     if ((st = check_paged(k, p->D_qk)) != DSA_OK) return st;
     const int64_t tiles = (p->D_qk + 127) / 128;
     if (k.block_stride < 64 * k.row_stride + 64 * 4 * tiles) return DSA_ERR_INVALID;
+    // the attention kernel keeps a gathered row as (block id, row) in 32 bits
+    if (k.num_blocks > (int64_t(1) << 26)) return DSA_ERR_UNSUPPORTED;
     return DSA_OK;
   }
   if (p->kv_format != DSA_KV_BF16) return DSA_ERR_INVALID;
@@ -193,10 +195,10 @@ int check_attn_args(const dsa_problem* p, const uint16_t* q, const dsa_paged& k,
   return DSA_OK;
 }
 
-// The layout the attention kernels see as "latent" (bf16 rows shared by K
-// and V, gathered by DMA); an FP8 cache is staged like a separate V cache.
-bool dma_latent(const dsa_problem* p, const dsa_paged& k, const dsa_paged& v) {
-  return is_latent(k, v) && p->kv_format != DSA_KV_FP8;
+// The layout the attention kernels gather by DMA: rows shared by K and V
+// (bf16, or FP8 codes with their tile scales).
+bool dma_latent(const dsa_problem*, const dsa_paged& k, const dsa_paged& v) {
+  return is_latent(k, v);
 }
 
 AttnLaunch attn_launch(const dsa_problem* p, const uint16_t* q, dsa_paged k, dsa_paged v,
@@ -315,7 +317,7 @@ int decode_run(const dsa_problem* p, const uint8_t* qI, const float* w, dsa_page
     aa.row_begin = row0;
     aa.num_rows = nr;
     // the workspace holds partials for the larger of the two layouts' counts
-    aa.n_chunks = attn_chunks(d.rp, p->H_q, p->D_qk, p->K, aa.latent && !aa.kv8);
+    aa.n_chunks = attn_chunks(d.rp, p->H_q, p->D_qk, p->K, aa.latent);
     aa.partial = aa.n_chunks > 1 ? static_cast<void*>(base + d.part_off) : nullptr;
     if ((st = status_of(launch_sparse_attn(aa, s, stage(2), stage(3)))) != DSA_OK) return st;
   }
@@ -523,7 +525,7 @@ int dsa_sparse_attn(const dsa_problem* p, const uint16_t* q, dsa_paged k, dsa_pa
   if (p->num_rows == 0) return DSA_OK;
   AttnLaunch a = attn_launch(p, q, k, v, out, lse, static_cast<uint32_t*>(ws));
   a.indices = indices;
-  a.n_chunks = attn_chunks(p->num_rows, p->H_q, p->D_qk, p->K, a.latent && !a.kv8);
+  a.n_chunks = attn_chunks(p->num_rows, p->H_q, p->D_qk, p->K, a.latent);
   a.partial = a.n_chunks > 1
                   ? static_cast<void*>(static_cast<char*>(ws) + kHeader)
                   : nullptr;

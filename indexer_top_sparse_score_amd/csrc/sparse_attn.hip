@@ -263,8 +263,13 @@ __device__ __forceinline__ uint4 raw_bf16x8(const Raw8<true>& r, bool keep) {
     f[4 * w + 3] = hi[1];
   }
   const float sc = keep ? r.s : 0.0f;
-  return uint4{pack2(f[0] * sc, f[1] * sc), pack2(f[2] * sc, f[3] * sc),
-               pack2(f[4] * sc, f[5] * sc), pack2(f[6] * sc, f[7] * sc)};
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)  // one packed round-to-nearest-even conversion per pair
+    w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{f[2 * i] * sc, f[2 * i + 1] * sc}), b2));
+  return uint4{w[0], w[1], w[2], w[3]};
 }
 
 // KV8: the latent cache holds E4M3 code rows, and a block keeps its 64 rows'
@@ -577,6 +582,21 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
       : "memory");
 }
 
+// One 4-byte-per-lane DMA, global -> LDS (lane l lands at lds + 4 l), as
+// dma16.
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+
 // Waits until at most `groups` groups of PER DMA instructions are in flight.
 template <int PER>
 __device__ __forceinline__ void wait_vm(int groups) {
@@ -589,30 +609,54 @@ __device__ __forceinline__ void wait_vm(int groups) {
   }
 }
 
+// KV8 (the FP8 latent cache: E4M3 code rows, each with five float32 tile
+// scales in its block's scale area): a step's 64 code rows (576 B each) and
+// their scales move HBM -> LDS by DMA into a ring of two steps, 18 KB of
+// codes per sub-block instead of 36 KB of bf16; once a step has landed, the
+// workgroup decodes it into the bf16 tiles above (code value x its tile's
+// scale, rounded to bf16 -- the same values the register-staged kernel
+// makes), and the MFMA loop runs on them unchanged.
+//
 // KSPLIT: the key halves of a workgroup.  With KSPLIT = 2 the kNW waves are
 // kNW / 2 head waves (16 heads each) times two key halves: both halves share
 // every staged sub-block, half 0 takes the even sub-blocks of the chunk and
 // half 1 the odd ones, and at the end half 1 hands its accumulators to half
 // 0 through LDS, which merges them by log-sum-exp.  Twice the waves per
 // staged byte, and the same partial per workgroup.
-template <int NBUF, int kNW, int KSPLIT>
+template <int NBUF, int kNW, int KSPLIT, bool KV8 = false>
 __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLaunch a, AttnGrid g) {
   using namespace lat;
   constexpr int NT = 64 * kNW;
   constexpr int kHW = kNW / KSPLIT;  // head waves
   constexpr int kDmaPerWave = kDmaPerSB / kNW;
-  constexpr int kPerStep = KSPLIT * kDmaPerWave;  // DMA instructions per wave per step
-  constexpr int kAhead = NBUF / KSPLIT;           // steps staged at once
+  // KV8: per step and wave, code DMAs (16 B per lane) for kSB * KSPLIT rows
+  // of 36 pieces, and scale DMAs (4 B per lane) for those rows' 8-float
+  // slots (5 used)
+  constexpr int kRowsStep = kSB * KSPLIT;
+  constexpr int kCodePieces = kKvDim / 16;  // 36
+  constexpr int kCodeDma = KV8 ? kRowsStep * kCodePieces / 64 / kNW : 0;
+  constexpr int kScaleDma = KV8 ? kRowsStep * 8 / 64 / kNW : 0;
+  constexpr int kPerStep = KV8 ? kCodeDma + kScaleDma : KSPLIT * kDmaPerWave;  // DMA instructions per wave per step
+  constexpr int kCodeBytes = kRowsStep * kKvDim, kStepBytes = kCodeBytes + kRowsStep * 32;
+  constexpr int kCodeSteps = KV8 ? 2 : 0;                        // the code ring, in steps
+  constexpr int kAhead = KV8 ? kCodeSteps : NBUF / KSPLIT;       // steps staged at once
   static_assert(kDmaPerSB % kNW == 0, "DMA instructions per wave");
+  static_assert(!KV8 || (kRowsStep * kCodePieces % (64 * kNW) == 0 && kRowsStep * 8 % (64 * kNW) == 0 &&
+                         KSPLIT == 2 && NBUF == KSPLIT && kRowsStep / kNW * kCodePieces == 64 * kCodeDma),
+                "FP8 steps: whole DMA instructions per wave, one tile per key half");
   static_assert(KSPLIT == 1 || KSPLIT == 2, "key halves");
   static_assert(NBUF % KSPLIT == 0 && kAhead >= 2 && (kAhead - 1) * kPerStep <= 63, "vmcnt");
+  constexpr int kLdsBytes = NBUF * kTileBytes + kCodeSteps * kStepBytes;
   // epilogue staging of the head waves, after the merge area (KSPLIT = 2)
   constexpr int kMergeBytes = KSPLIT == 2 ? kHW * 64 * (kMT * 16 + 8) : 0;
-  static_assert(kMergeBytes + kHW * 16 * (2 * kDv + 16) <= NBUF * kTileBytes,
+  static_assert(kMergeBytes + kHW * 16 * (2 * kDv + 16) <= kLdsBytes,
                 "merge and epilogue staging fit the tiles");
-  __shared__ __attribute__((aligned(16))) uint8_t tile[NBUF][kTileBytes];
+  // the tiles, then (KV8) the code ring; the merge and the epilogue reuse it all
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  auto tile = [&](int i) { return lds + i * kTileBytes; };
   // each slot's row offset in the cache in 16-byte units (the front end
-  // keeps the cache below 64 GiB for this kernel), ~0u for an absent row
+  // keeps the cache below 64 GiB for this kernel), ~0u for an absent row;
+  // KV8: the row's (block id << 6 | row in block) instead
   __shared__ __attribute__((aligned(16))) uint32_t koff[kMaxChunkLat];
 
   int unit, hg;
@@ -641,7 +685,16 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
     const int64_t* ro = a.rowoff + (int64_t)row_local * a.K + slot0;
     for (int i = tid; i < nsb * kSB; i += NT) {
       const int64_t o = i < n_slots ? ro[i] : -1;
-      koff[i] = o >= 0 ? (uint32_t)(o >> 4) : ~0u;
+      if constexpr (KV8) {  // o = block * block_stride + row * row_stride
+        uint32_t kf = ~0u;
+        if (o >= 0) {
+          const int64_t blk = o / a.k.block_stride;
+          kf = (uint32_t)(blk << 6) | (uint32_t)((o - blk * a.k.block_stride) / a.k.row_stride);
+        }
+        koff[i] = kf;
+      } else {
+        koff[i] = o >= 0 ? (uint32_t)(o >> 4) : ~0u;
+      }
     }
   } else {
     int b = 0, p = -1;
@@ -658,14 +711,15 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
         if (idx >= 0 && idx <= p) {
           const int phys = bt[idx >> 6];
           if (phys >= 0 && (int64_t)phys < a.k.num_blocks)
-            ko = (int64_t)phys * a.k.block_stride + (int64_t)(idx & 63) * a.k.row_stride;
+            ko = KV8 ? ((int64_t)phys << 6) | (idx & 63)
+                     : (int64_t)phys * a.k.block_stride + (int64_t)(idx & 63) * a.k.row_stride;
           else
             report(a.err, DSA_DEVERR_BLOCK);
         } else if (idx != -1) {
           report(a.err, DSA_DEVERR_INDEX);
         }
       }
-      koff[i] = ko >= 0 ? (uint32_t)(ko >> 4) : ~0u;
+      koff[i] = ko >= 0 ? (uint32_t)(KV8 ? ko : ko >> 4) : ~0u;
     }
   }
 
@@ -685,7 +739,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
   constexpr int kRowsPW = kSB / kNW;
   static_assert(kRowsPW * kPieces == kDmaPerWave * 64 && kRowsPW % 4 == 0, "rows per wave");
   auto issue = [&](int sb) {
-    uint8_t* buf = tile[sb % NBUF];
+    uint8_t* buf = tile(sb % NBUF);
     uint32_t kr[kRowsPW];
 #pragma unroll
     for (int i = 0; i < kRowsPW; i += 4) {
@@ -711,7 +765,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
     for (int t = 0; t < kDmaPerWave; ++t) dma16(src[t], lds0 + 1024 * t);
   };
   auto zero_absent = [&](int sb) {
-    uint8_t* buf = tile[sb % NBUF];
+    uint8_t* buf = tile(sb % NBUF);
 #pragma unroll
     for (int t = 0; t < kDmaPerWave; ++t) {
       const int i = wave * kDmaPerWave + t;
@@ -724,9 +778,104 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
   // the first step's sub-blocks requested, then Q^T (this lane's head, 8
   // dims per MFMA step), then the rest of the lookahead: what the first
   // MFMAs need is queued ahead of what they do not
-  auto issue_step = [&](int st) {
+  // KV8: the DMAs of step st into ring slot st % kCodeSteps.  Code
+  // instruction i fills the step's 16-byte code slots 64i .. 64i + 63 (slot
+  // s: row s / 36, piece s % 36); scale instruction j fills its float slots
+  // 64j .. 64j + 63 (row d / 8, scale d % 8; slots 5..7 of a row repeat
+  // scale 4 and go unused).  Each wave's instructions cover its own kRW
+  // rows, whose (block, row) come in with a few broadcast LDS reads before
+  // the first DMA.  Absent rows read block 0 and are zeroed when decoded.
+  auto issue8 = [&](int st) {
+    constexpr int kRW = kRowsStep / kNW;
+    uint8_t* ring = lds + NBUF * kTileBytes + (st % (kCodeSteps > 0 ? kCodeSteps : 1)) * kStepBytes;
+    uint32_t kf[kRW];
 #pragma unroll
-    for (int x = 0; x < KSPLIT; ++x) issue(st * KSPLIT + x);
+    for (int i = 0; i < kRW; i += 4) {
+      const uint4 x = *reinterpret_cast<const uint4*>(&koff[st * kRowsStep + kRW * wave + i]);
+      kf[i] = x.x;
+      kf[i + 1] = x.y;
+      kf[i + 2] = x.z;
+      kf[i + 3] = x.w;
+    }
+    auto row_base = [&](uint32_t f) -> int64_t {  // where the row's block starts
+      return f == ~0u ? 0 : (int64_t)(f >> 6) * a.k.block_stride;
+    };
+    const uint8_t* csrc[kCodeDma > 0 ? kCodeDma : 1];
+#pragma unroll
+    for (int t = 0; t < kCodeDma; ++t) {
+      const int sl = 64 * t + lane;       // slot within this wave's rows
+      const int j = sl / kCodePieces;     // at, at + 1 or at + 2
+      const int at = 64 * t / kCodePieces;
+      const uint32_t f = j == at ? kf[at] : j == at + 1 ? kf[at + 1 < kRW ? at + 1 : at]
+                                                         : kf[at + 2 < kRW ? at + 2 : at];
+      const int64_t off = f == ~0u ? 0 : row_base(f) + (int64_t)(f & 63) * a.k.row_stride;
+      csrc[t] = kbase + off + 16 * (sl - j * kCodePieces);
+    }
+    const uint8_t* ssrc[kScaleDma > 0 ? kScaleDma : 1];
+#pragma unroll
+    for (int t = 0; t < kScaleDma; ++t) {
+      uint32_t f = kf[8 * t];  // the row: 8 t + lane / 8 of this wave's
+#pragma unroll
+      for (int q = 1; q < 8; ++q)
+        if ((lane >> 3) == q) f = kf[8 * t + q < kRW ? 8 * t + q : 8 * t];
+      const int k = min(lane & 7, kKvTiles - 1);
+      const int64_t off = f == ~0u ? 0
+                                   : row_base(f) + kBlock * a.k.row_stride +
+                                         (int64_t)(f & 63) * (4 * kKvTiles) + 4 * k;
+      ssrc[t] = kbase + off;
+    }
+    const uint32_t c0 =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ring + 1024 * kCodeDma * wave));
+    const uint32_t s0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(ring + kCodeBytes + 256 * kScaleDma * wave));
+#pragma unroll
+    for (int t = 0; t < kCodeDma; ++t) dma16(csrc[t], c0 + 1024 * t);
+#pragma unroll
+    for (int t = 0; t < kScaleDma; ++t) dma4(ssrc[t], s0 + 256 * t);
+  };
+  // KV8: step st's codes decoded into the bf16 tiles (its key half x's rows
+  // into tile x), code value x tile scale rounded to bf16; absent rows zero.
+  // Thread t decodes row t / kTPR, pieces t % kTPR + kTPR j: one row's
+  // offsets and validity per thread, and for each j a wave reads and writes
+  // 16 rows' worth of whole 16-lane runs.
+  auto convert8 = [&](int st) {
+    constexpr int kTPR = NT / kRowsStep;          // threads per row
+    constexpr int kN = kPieces / kTPR;            // bf16 pieces per thread
+    static_assert(!KV8 || (NT % kRowsStep == 0 && kPieces % kTPR == 0), "whole pieces per thread");
+    const uint8_t* ring = lds + NBUF * kTileBytes + (st % (kCodeSteps > 0 ? kCodeSteps : 1)) * kStepBytes;
+    const int row = tid / kTPR, p0 = tid % kTPR, rr = row & (kSB - 1);
+    static_assert(!KV8 || (kTPR == 4 && kKvTile / 8 == 16), "piece p0 + 4 j lies in scale tile j / 4");
+    const uint8_t* src = ring + row * kKvDim + 8 * p0;
+    const float* sc = reinterpret_cast<const float*>(ring + kCodeBytes) + row * 8;
+    uint8_t* dst = tile(row / kSB) + 16 * (rr * kPieces);
+    const bool keep = koff[st * kRowsStep + row] != ~0u;
+    float s5[kKvTiles];
+#pragma unroll
+    for (int t = 0; t < kKvTiles; ++t) s5[t] = sc[t];
+    constexpr int kB = 6;  // code reads in flight
+    static_assert(!KV8 || kN % kB == 0, "whole batches");
+#pragma unroll
+    for (int j0 = 0; j0 < kN; j0 += kB) {
+      uint2 c[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) c[u] = *reinterpret_cast<const uint2*>(src + 8 * kTPR * (j0 + u));
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int j = j0 + u, p = p0 + kTPR * j;
+        Raw8<true> rw;
+        rw.x = c[u];
+        rw.s = s5[j / 4];
+        *reinterpret_cast<uint4*>(dst + 16 * (p ^ (rr & 7))) = raw_bf16x8(rw, keep);
+      }
+    }
+  };
+  auto issue_step = [&](int st) {
+    if constexpr (KV8) {
+      issue8(st);
+    } else {
+#pragma unroll
+      for (int x = 0; x < KSPLIT; ++x) issue(st * KSPLIT + x);
+    }
   };
   // Q of the workgroup's heads is one contiguous run of rows, staged once
   // per workgroup by DMA into the last kQT tile buffers (as sub-blocks of
@@ -737,7 +886,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
   constexpr int kHG = kHPW * kHW;  // heads per workgroup
   constexpr int kQT = kHG / kSB;   // tile buffers they take
   static_assert(kHG % kSB == 0 && kQT < NBUF, "the workgroup's heads fill whole tiles");
-  constexpr int kStepQ = (NBUF - kQT) / KSPLIT;  // first step that writes a Q buffer
+  // (KV8: the steps go to the code ring, none to a Q buffer; they are
+  // requested after Q, and the wait for Q lets them stay in flight)
+  constexpr int kStepQ = KV8 ? 0 : (NBUF - kQT) / KSPLIT;  // first step that writes a Q buffer
   const int head0_wg = hg * kHG;
   for (int x = 0; x < min(kStepQ, nst); ++x) issue_step(x);
   {
@@ -754,19 +905,24 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
         src[t] = qbase + (int64_t)(h < a.H_q ? h : 0) * (2 * kDqk) + 16 * piece;  // (rows past H_q go unused)
       }
       const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
-          (uint32_t)(uintptr_t)(tile[NBUF - kQT + qt] + 1024 * wave * kDmaPerWave));
+          (uint32_t)(uintptr_t)(tile(NBUF - kQT + qt) + 1024 * wave * kDmaPerWave));
 #pragma unroll
       for (int t = 0; t < kDmaPerWave; ++t) dma16(src[t], lds0 + 1024 * t);
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (KV8) {
+    for (int x = 0; x < min(kAhead, nst); ++x) issue_step(x);
+    wait_vm<kPerStep>(min(kAhead, nst));
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   __syncthreads();
   const int head = head0_wg + hw * kHPW + cidx;
   const bool head_ok = head < a.H_q;
   v8s qb[kKS];
   {
     const int qr = hw * kHPW + cidx;  // row among the workgroup's heads
-    const uint8_t* qrow = tile[NBUF - kQT + qr / kSB] + 16 * ((qr % kSB) * kPieces);
+    const uint8_t* qrow = tile(NBUF - kQT + qr / kSB) + 16 * ((qr % kSB) * kPieces);
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
       const v8s x = *reinterpret_cast<const v8s*>(qrow + 16 * ((grp + 4 * ks) ^ (qr & 7)));
@@ -774,7 +930,8 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
     }
   }
   __syncthreads();  // every wave holds its Q^T: the buffers are free
-  for (int x = kStepQ; x < min(kAhead, nst); ++x) issue_step(x);
+  if constexpr (!KV8)
+    for (int x = kStepQ; x < min(kAhead, nst); ++x) issue_step(x);
   const float c2 = a.scale * kLog2e;
 
   // Per-lane tile offsets.  Logits: lane (grp, cidx) reads row 16kt + cidx,
@@ -824,19 +981,32 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
     for (int st = 0; st < nst; ++st) {
       // steps requested after this one: all but the first kAhead were
       // requested one step ahead
-      const int issued_to = st == 0 ? min(kAhead, nst) - 1 : min(nst - 1, st + kAhead - 2);
+      // (KV8 requests step st + kAhead as soon as step st is decoded, so
+      // kAhead - 1 later steps are in flight here)
+      const int issued_to = KV8 ? min(nst - 1, st + kAhead - 1)
+                                : st == 0 ? min(kAhead, nst) - 1 : min(nst - 1, st + kAhead - 2);
       wait_vm<kPerStep>(issued_to - st);
+      if constexpr (!KV8) {
 #pragma unroll
-      for (int x = 0; x < KSPLIT; ++x) {
-        const int sbx = st * KSPLIT + x;
-        const bool any_absent =
-            __ballot(lane < kSB && koff[sbx * kSB + (lane & (kSB - 1))] == ~0u) != 0;
-        if (any_absent) zero_absent(sbx);
+        for (int x = 0; x < KSPLIT; ++x) {
+          const int sbx = st * KSPLIT + x;
+          const bool any_absent =
+              __ballot(lane < kSB && koff[sbx * kSB + (lane & (kSB - 1))] == ~0u) != 0;
+          if (any_absent) zero_absent(sbx);
+        }
       }
       // every wave's DMAs of this step have landed, and every wave is done
       // with the buffers the next DMAs overwrite (last read in step st-1)
       __syncthreads();
-      if (st >= 1 && st + kAhead - 1 < nst) issue_step(st + kAhead - 1);
+      if constexpr (KV8) {
+        // decode the step into the tiles the MFMAs read; its ring slot is
+        // then free for step st + kAhead
+        convert8(st);
+        __syncthreads();
+        if (st + kAhead < nst) issue_step(st + kAhead);
+      } else {
+        if (st >= 1 && st + kAhead - 1 < nst) issue_step(st + kAhead - 1);
+      }
       const int sb = st * KSPLIT + kh;  // this wave's sub-block
       const uint32_t valid =
           (uint32_t)__ballot(lane < kSB && koff[sb * kSB + (lane & (kSB - 1))] != ~0u);
@@ -844,7 +1014,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
       // No early exit below: every sub-block runs its MFMAs (a sub-block
       // without a valid key, or after an overrun, adds P = 0), so the
       // accumulators have one producer and stay in AGPRs across the loop.
-      const uint8_t* buf = tile[sb % NBUF];
+      const uint8_t* buf = tile(sb % NBUF);
       // ---- logits S^T (keys x heads): two 16-key tiles; every read is one
       //      of two per-lane bases plus an immediate offset
       // The two tiles' MFMA chains alternate (step i: tile i % 2, dims
@@ -962,7 +1132,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
   // buffers are free for the merge and the epilogue staging
   if constexpr (KSPLIT == 2) {
     // half 1 -> LDS: lane-major v4f per 16-dim tile, then (m2, lsum)
-    uint8_t* mbase = &tile[0][0] + hw * (64 * (kMT * 16 + 8));
+    uint8_t* mbase = lds + hw * (64 * (kMT * 16 + 8));
     v4f* mo = reinterpret_cast<v4f*>(mbase);
     float2* mls = reinterpret_cast<float2*>(mbase + 64 * kMT * 16);
     if (kh == 1) {
@@ -994,7 +1164,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
   }
   // the head waves' staging (16.25 KB each) sits after the merge area
   write_out_staged(a, r, head0, lane, o, m2, lsum,
-                   &tile[0][0] + kMergeBytes + hw * (16 * (2 * kDv + 16)));
+                   lds + kMergeBytes + hw * (16 * (2 * kDv + 16)));
 }
 
 // Merges the chunks of each (row, head) by log-sum-exp: with M the largest
@@ -1110,6 +1280,11 @@ hipError_t launch_t(const AttnLaunch& a, hipStream_t s, StageEvents ev, StageEve
           kernel = sparse_attn_latent_kernel<4, 4, 2>;
           threads = 256;
         }
+        // the FP8 cache: codes staged by DMA, decoded into two bf16 tiles
+        if (a.kv8) {
+          kernel = sparse_attn_latent_kernel<2, 4, 2, true>;
+          threads = 256;
+        }
       }
     }
   }
@@ -1166,8 +1341,7 @@ bool attn_uses_rowoff(int D_qk, int D_v, bool latent) {
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s, StageEvents ev,
                               StageEvents merge) {
   if (a.num_rows <= 0) return hipSuccess;
-  // the FP8 cache takes the staged kernel (as a separate V cache does)
-  switch (waves_for(a.H_q, a.D_qk, a.latent && !a.kv8) * 1000 + a.D_qk) {
+  switch (waves_for(a.H_q, a.D_qk, a.latent) * 1000 + a.D_qk) {
     case 2576: return launch_t<576, 512, 2>(a, s, ev, merge);
     case 4576: return launch_t<576, 512, 4>(a, s, ev, merge);
     case 4064: return launch_t<64, 64, 4>(a, s, ev, merge);
