@@ -227,30 +227,22 @@ struct Cfg {
   static constexpr int kVtElems = DV * VP;
 };
 
-// A staging job's raw data: 8 bf16 elements (16 bytes), or with KV8 their 8
-// E4M3 codes (8 bytes) and the float32 scale of their tile.
-template <bool KV8>
-struct Raw8 {
-  uint4 x;
+// A staging job's raw data: 8 bf16 elements (16 bytes).
+template <class C>
+struct Staged {
+  uint4 v[C::kVJ > 0 ? C::kVJ : 1][4];
+  uint4 k[C::kKJ > 0 ? C::kKJ : 1];
 };
-template <>
-struct Raw8<true> {
+
+// Eight FP8 KV elements -- 8 E4M3 codes and the float32 scale of their
+// tile -- as packed bf16: decoded (the hardware conversion is the OCP E4M3
+// one), times the scale and rounded to bf16.  `keep` false gives zeros (an
+// absent row).
+struct Raw8 {
   uint2 x;
   float s;
 };
-template <class C, bool KV8>
-struct Staged {
-  Raw8<KV8> v[C::kVJ > 0 ? C::kVJ : 1][4];
-  Raw8<KV8> k[C::kKJ > 0 ? C::kKJ : 1];
-};
-
-// Eight elements as packed bf16: raw bf16 as they are; KV8 codes decoded
-// (the hardware conversion is the OCP E4M3 one), times the tile's scale and
-// rounded to bf16.  `keep` false gives zeros (an absent row).
-__device__ __forceinline__ uint4 raw_bf16x8(const Raw8<false>& r, bool keep) {
-  return keep_or_zero(r.x, keep);
-}
-__device__ __forceinline__ uint4 raw_bf16x8(const Raw8<true>& r, bool keep) {
+__device__ __forceinline__ uint4 raw_bf16x8(const Raw8& r, bool keep) {
   float f[8];
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
@@ -279,16 +271,14 @@ constexpr int kKvTile = 128;
 constexpr int kKvDim = 576;  // the FP8 cache's rows: the 576-wide latent
 constexpr int kKvTiles = (kKvDim + kKvTile - 1) / kKvTile;  // 5
 
-template <int DQK, int DV, bool LATENT, int NW, bool KV8 = false>
+template <int DQK, int DV, bool LATENT, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, AttnGrid g) {
   using C = Cfg<DQK, DV, LATENT, NW>;
-  static_assert(!KV8 || (LATENT && DQK == kKvDim && DV == 512), "FP8 KV: latent 576/512");
-  constexpr int kEB = KV8 ? 1 : 2;  // bytes per stored element
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::kKsElems];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][C::kVtElems];
   __shared__ int64_t koff[kMaxChunk];
-  // separate V: V row offsets; KV8: tile scale offsets of the rows
-  __shared__ int64_t voff[(LATENT && !KV8) ? 1 : kMaxChunk];
+  // separate V: V row offsets
+  __shared__ int64_t voff[LATENT ? 1 : kMaxChunk];
 
   int unit, hg;
   if (!decode_wg(g, unit, hg)) return;
@@ -321,9 +311,7 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
           const bool okv = LATENT || (phys >= 0 && (int64_t)phys < a.v.num_blocks);
           if (okk && okv) {
             ko = (int64_t)phys * a.k.block_stride + (int64_t)(idx & 63) * a.k.row_stride;
-            vo = KV8 ? (int64_t)phys * a.k.block_stride + 64 * a.k.row_stride +
-                           (int64_t)(idx & 63) * (4 * kKvTiles)
-                     : (int64_t)phys * a.v.block_stride + (int64_t)(idx & 63) * a.v.row_stride;
+            vo = (int64_t)phys * a.v.block_stride + (int64_t)(idx & 63) * a.v.row_stride;
           } else {
             report(a.err, DSA_DEVERR_BLOCK);
           }
@@ -332,7 +320,7 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
         }
       }
       koff[i] = ko;
-      if (!LATENT || KV8) voff[i] = vo;
+      if (!LATENT) voff[i] = vo;
     }
   }
 
@@ -357,19 +345,7 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
   // Loads are unconditional (an absent row reads row 0 of block 0, which
   // always exists) and raw; rows that are absent are zeroed only when they
   // land, so nothing waits on the loads while the previous sub-block runs.
-  // (KV8: an absent row reads the scales of row 0 of block 0 too; the
-  // scale area of a block lies inside it, since block_stride >= 64 *
-  // row_stride + 4 * kKvTiles * 64)
-  const int64_t scale0 = 64 * a.k.row_stride;
-  auto load8 = [&](Raw8<KV8>& r, const uint8_t* p, int64_t soff, int d0) {
-    if constexpr (KV8) {
-      r.x = *reinterpret_cast<const uint2*>(p);
-      r.s = *reinterpret_cast<const float*>(kbase + (soff >= 0 ? soff : scale0) + 4 * (d0 / kKvTile));
-    } else {
-      r.x = *reinterpret_cast<const uint4*>(p);
-    }
-  };
-  auto issue = [&](int sb, Staged<C, KV8>& st) {
+  auto issue = [&](int sb, Staged<C>& st) {
     const int base = sb * kSB;
 #pragma unroll
     for (int i = 0; i < C::kVJ; ++i) {
@@ -378,8 +354,8 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t off = (LATENT ? koff : voff)[base + 4 * kq + j];
-        load8(st.v[i][j], (LATENT ? kbase : vbase) + (off >= 0 ? off : 0) + dg * 8 * kEB,
-              KV8 ? voff[base + 4 * kq + j] : 0, 8 * dg);
+        st.v[i][j] = *reinterpret_cast<const uint4*>((LATENT ? kbase : vbase) + (off >= 0 ? off : 0) +
+                                                     dg * 16);
       }
     }
 #pragma unroll
@@ -388,10 +364,10 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
       const int key = (job / C::kKPieces) % kSB, piece = job % C::kKPieces;
       const int64_t off = koff[base + key];
       const int d0 = (LATENT ? DV : 0) + 8 * piece;
-      load8(st.k[i], kbase + (off >= 0 ? off : 0) + d0 * kEB, KV8 ? voff[base + key] : 0, d0);
+      st.k[i] = *reinterpret_cast<const uint4*>(kbase + (off >= 0 ? off : 0) + d0 * 2);
     }
   };
-  auto land = [&](Staged<C, KV8>& st, int sb, int buf) {
+  auto land = [&](Staged<C>& st, int sb, int buf) {
     const int base = sb * kSB;
     uint16_t* ks = Ks[buf];
     uint16_t* vt = Vt[buf];
@@ -404,7 +380,7 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
       uint4 vv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        vv[j] = raw_bf16x8(st.v[i][j], (LATENT ? koff : voff)[base + 4 * kq + j] >= 0);
+        vv[j] = keep_or_zero(st.v[i][j], (LATENT ? koff : voff)[base + 4 * kq + j] >= 0);
       if (mine) {
       if (LATENT) {
 #pragma unroll
@@ -431,7 +407,7 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
       const bool mine = C::kKJ * C::kThreads == C::kKJobs || job < C::kKJobs;
       const int key = (job / C::kKPieces) % kSB, piece = job % C::kKPieces;
       const int d0 = (LATENT ? DV : 0) + 8 * piece;
-      if (mine) *reinterpret_cast<uint4*>(&ks[key * C::KP + d0]) = raw_bf16x8(st.k[i], koff[base + key] >= 0);
+      if (mine) *reinterpret_cast<uint4*>(&ks[key * C::KP + d0]) = keep_or_zero(st.k[i], koff[base + key] >= 0);
     }
   };
 
@@ -442,7 +418,7 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
   float lsum = 0.0f;             // this lane's share of the running sum
   const float c2 = a.scale * kLog2e;
 
-  Staged<C, KV8> st;
+  Staged<C> st;
   if (nsb > 0) issue(0, st);
   for (int sb = 0; sb < nsb; ++sb) {
     const int buf = sb & 1;
@@ -862,7 +838,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
         const int j = j0 + u, p = p0 + kTPR * j;
-        Raw8<true> rw;
+        Raw8 rw;
         rw.x = c[u];
         rw.s = s5[j / 4];
         *reinterpret_cast<uint4*>(dst + 16 * (p ^ (rr & 7))) = raw_bf16x8(rw, keep);
@@ -1288,14 +1264,10 @@ hipError_t launch_t(const AttnLaunch& a, hipStream_t s, StageEvents ev, StageEve
       }
     }
   }
-  // (the 576-wide staged kernel only ever runs with four waves; it also
-  // serves the FP8 latent cache, decoding rows as it stages them)
+  // (the 576-wide staged kernel only ever runs with four waves)
   if constexpr (DQK != lat::kDqk || NW == 4) {
-    if (!kernel)
+    if (!kernel && !a.kv8)
       kernel = a.latent ? sparse_attn_kernel<DQK, DV, true, NW> : sparse_attn_kernel<DQK, DV, false, NW>;
-    if constexpr (DQK == kKvDim && DV == 512) {
-      if (a.kv8) kernel = a.latent ? sparse_attn_kernel<DQK, DV, true, NW, true> : nullptr;
-    }
   }
   if (!kernel) return hipErrorInvalidConfiguration;
   hipError_t e = launch_kernel(kernel, dim3(grid), dim3(threads), s, ev.start, ev.stop, a, g);
