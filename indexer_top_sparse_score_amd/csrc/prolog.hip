@@ -263,99 +263,55 @@ __device__ __forceinline__ void bf16x8_to_f32(const uint4 v, float (&f)[8]) {
   }
 }
 
-// Head weight h of every row (one wave, at most kRmax rows): w[r][h] =
-// bf16(W_g[h] . x[r]), the weight row and the rows of x read in contiguous
-// kilobytes, two 512-input steps per batch of loads.
-template <int kRmax>
-__device__ __forceinline__ void head_weight(const PrologLaunch& a, int h, int lane) {
-  constexpr int kJ = 2;
-  const int R = a.num_rows < kRmax ? a.num_rows : kRmax;
-  float acc[kRmax];
-#pragma unroll
-  for (int r = 0; r < kRmax; ++r) acc[r] = 0.0f;
-  const uint16_t* wrow = a.w_g + (int64_t)h * a.D_x + 8 * lane;
-  for (int j0 = 0; 512 * j0 < a.D_x; j0 += kJ) {
-    // unconditional loads (a piece past the input reads the row's first
-    // piece, a row past the batch row 0; both are dropped where used)
-    uint4 wv[kJ], xv[kJ][kRmax];
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) {
-      const int k = 512 * (j0 + j) + 8 * lane;
-      const int off = k < a.D_x ? 512 * (j0 + j) : -8 * lane;
-      wv[j] = *reinterpret_cast<const uint4*>(wrow + off);
-#pragma unroll
-      for (int r = 0; r < kRmax; ++r)
-        xv[j][r] = *reinterpret_cast<const uint4*>(a.x + (int64_t)(r < R ? r : 0) * a.D_x +
-                                                   (k < a.D_x ? k : 0));
-    }
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) {
-      if (512 * (j0 + j) + 8 * lane >= a.D_x) continue;
-      float wf[8];
-      bf16x8_to_f32(wv[j], wf);
-#pragma unroll
-      for (int r = 0; r < kRmax; ++r) {
-        float xf[8];
-        bf16x8_to_f32(xv[j][r], xf);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[r] = fmaf(wf[e], xf[e], acc[r]);
-      }
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < kRmax; ++r) {
-    const float v = across_wave(acc[r], FAdd{});
-    if (lane == 0 && r < R) a.w[(int64_t)r * a.H_I + h] = bf16_round_f(v);
-  }
-}
-
 template <int R>
 __global__ __launch_bounds__(1024) void prolog_gemv_kernel(PrologLaunch a) {
-  constexpr int kWaves = 16, kFW = 2;  // waves, features per wave
-  constexpr int KC = 16384 / R;        // inputs per chunk: 32 KB of x in LDS
+  constexpr int kWaves = 16, kFW = 2;  // waves, q features per wave
+  constexpr int KC = 32768 / R < 4096 ? 32768 / R : 4096;  // inputs per chunk (<= 64 KB of x in LDS)
+  constexpr int kXP = R * KC / 8 / (64 * kWaves);          // 16-byte pieces of x per thread
   constexpr int kJ = KC / 512;         // 512-input loads per feature and chunk
   __shared__ __attribute__((aligned(16))) uint16_t xs[R * KC];
   __shared__ float res[32][R + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int F = a.H_I * a.D_I;
-  const int nq = F / 32, ng = (a.H_I + kWaves - 1) / kWaves;
+  const int nq = F / 32;
   const int bid = blockIdx.x;
-  if (bid >= nq) {
-    // after the q groups (which fill the chip's CUs for a 64 x 128
-    // indexer), short workgroups: head weights, one wave per weight, then
-    // the new keys, one wave per row
-    if (bid < nq + ng) {
-      const int h = (bid - nq) * kWaves + wave;
-      if (h < a.H_I) head_weight<R>(a, h, lane);
-    } else {
-      const int r = (bid - nq - ng) * kWaves + wave;
-      if (r < a.num_rows) key_norm_row(a, r, lane);
-    }
-    return;
-  }
-  const int fgroup = bid;
+  // Workgroup b < nq owns q group b.  The head weights and the new keys ride
+  // along in the first workgroups -- head weight b for b < H_I (its kJ
+  // 512-input slices of a chunk spread over waves 0 .. kJ - 1, one load
+  // each), then key row b - H_I in wave 0 -- so a 64 x 128 indexer's 256
+  // workgroups are the whole launch, one round on the chip's 256 CUs, with
+  // no tail of workgroups after them (extra ones only when H_I + rows > nq).
+  const bool has_q = bid < nq;
+  const int gh = bid < a.H_I ? bid : -1;
+  const int kr = bid >= a.H_I && bid < a.H_I + a.num_rows ? bid - a.H_I : -1;
+  const bool gw = wave < kJ && gh >= 0;  // this wave adds slice `wave` of head weight gh
+  __shared__ float gpart[kJ][R];
+  const int fgroup = has_q ? bid : 0;
   const uint16_t* wr[kFW];  // this lane's weight rows
 #pragma unroll
   for (int f = 0; f < kFW; ++f) wr[f] = a.w_q + (int64_t)(32 * fgroup + kFW * wave + f) * a.D_x;
-  float acc[kFW][R];
+  const uint16_t* wg = a.w_g + (int64_t)(gh >= 0 ? gh : 0) * a.D_x;
+  float acc[kFW][R], accg[R];
 #pragma unroll
-  for (int f = 0; f < kFW; ++f)
+  for (int r = 0; r < R; ++r) {
+    accg[r] = 0.0f;
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[f][r] = 0.0f;
+    for (int f = 0; f < kFW; ++f) acc[f][r] = 0.0f;
+  }
 
-  static_assert(R * KC / 8 == 2 * 64 * kWaves, "two 16-byte pieces of x per thread");
-  for (int c0 = 0; c0 < a.D_x; c0 += KC) {
+  static_assert(R * KC / 8 == kXP * 64 * kWaves && kJ <= kWaves, "whole pieces of x per thread");
+  for (int c0 = 0; c0 < a.D_x && (has_q || gh >= 0); c0 += KC) {
     const int kc = min(KC, a.D_x - c0);  // a multiple of 32
-    // this thread's two pieces of the chunk's rows of x, loaded first so
+    // this thread's pieces of the chunk's rows of x, loaded first so
     // that waiting for them does not wait for the weights behind them
     // (every load is issued unconditionally -- a piece past the chunk or
     // past the last row reads a valid address, and its value is dropped
     // only where it is used -- so that the waits count loads exactly)
-    uint4 xv[2];
-    int xo[2];
-    bool xok[2];
+    uint4 xv[kXP];
+    int xo[kXP];
+    bool xok[kXP];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < kXP; ++t) {
       const int i = tid + 64 * kWaves * t, r = i / (KC / 8), k8 = i % (KC / 8);
       xok[t] = r < a.num_rows && 8 * k8 < kc;
       xo[t] = r * KC + 8 * k8;
@@ -364,7 +320,9 @@ __global__ __launch_bounds__(1024) void prolog_gemv_kernel(PrologLaunch a) {
     // load j of a feature covers inputs c0 + 512 j + 8 lane + 0..7 (lanes
     // past the chunk read its first piece and skip it below); the sums take
     // the loads in issue order as they arrive
-    uint4 wv[kJ][kFW];
+    uint4 wv[kJ][kFW], wgv;
+    const int goff = 512 * wave + 8 * lane < kc ? c0 + 512 * wave + 8 * lane : c0;
+    if (gw) wgv = *reinterpret_cast<const uint4*>(wg + goff);
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
       const int off = 512 * j + 8 * lane < kc ? c0 + 512 * j + 8 * lane : c0;
@@ -373,7 +331,7 @@ __global__ __launch_bounds__(1024) void prolog_gemv_kernel(PrologLaunch a) {
     }
     __syncthreads();  // the previous chunk's x reads are done
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < kXP; ++t)
       *reinterpret_cast<uint4*>(xs + xo[t]) = xok[t] ? xv[t] : uint4{0u, 0u, 0u, 0u};
     __syncthreads();
 #pragma unroll
@@ -394,7 +352,36 @@ __global__ __launch_bounds__(1024) void prolog_gemv_kernel(PrologLaunch a) {
         }
       }
     }
+    if (gw && 512 * wave + 8 * lane < kc) {  // this wave's slice of the head weight
+      float gf[8];
+      bf16x8_to_f32(wgv, gf);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float xf[8];
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(xs + r * KC + 512 * wave + 8 * lane), xf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) accg[r] = fmaf(gf[e], xf[e], accg[r]);
+      }
+    }
   }
+  if (gw) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float v = across_wave(accg[r], FAdd{});
+      if (lane == 0) gpart[wave][r] = v;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    if (gh >= 0 && lane < R && lane < a.num_rows) {  // the slices in order
+      float v = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) v += gpart[j][lane];
+      a.w[(int64_t)lane * a.H_I + gh] = bf16_round_f(v);
+    }
+    if (kr >= 0) key_norm_row(a, kr, lane);
+  }
+  if (!has_q) return;
 #pragma unroll
   for (int f = 0; f < kFW; ++f)
 #pragma unroll
@@ -413,9 +400,10 @@ __global__ __launch_bounds__(1024) void prolog_gemv_kernel(PrologLaunch a) {
 
 hipError_t launch_indexer_prolog(const PrologLaunch& a, hipStream_t s) {
   const int F = a.H_I * a.D_I;
-  const int ngemv = F / 32 + (a.H_I + 15) / 16 + (a.num_rows + 15) / 16;
-  // (measured at 4096 inputs, 64 x 128: 4 rows 25.6 us on the vector ALUs
-  // against 25.7 us on the MFMA tile; 8 rows 37.5 against 29.4 us)
+  const int ngemv = max(F / 32, a.H_I + a.num_rows);
+  // (measured at 4096 inputs, 64 x 128: 4 rows 19.9 us on the vector ALUs
+  // against 25.7 us on the MFMA tile; at 8 rows the vector-ALU kernel's
+  // registers spill)
   if (a.num_rows <= 4) {
     prolog_gemv_kernel<4><<<ngemv, 1024, 0, s>>>(a);
   } else if (a.num_rows <= 16) {
