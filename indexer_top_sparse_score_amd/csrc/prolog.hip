@@ -396,6 +396,180 @@ __global__ __launch_bounds__(1024) void prolog_gemv_kernel(PrologLaunch a) {
   }
 }
 
+// Batches of many rows (chunked prefill): the projections as an LDS-tiled
+// GEMM.  A workgroup of 4 waves owns 128 features x 128 rows.  Per stage of
+// 64 inputs the weight tile (128 features x 64) and the x tile (128 rows x
+// 64) move HBM -> LDS by DMA (global_load_lds, 16 B per lane, 8 instructions
+// per wave), two stages deep; the 16-byte pieces of tile row r sit at piece
+// p ^ (r & 7), so the operand reads (16 rows at one piece) spread over the
+// banks.  Each wave computes 64 features x 64 rows (4 x 4 MFMA tiles) from
+// LDS: every byte fetched from L2 feeds 64 rows or features instead of 16.
+namespace gemm {
+constexpr int kBM = 128, kBN = 128, kBK = 64;         // features, rows, inputs per stage
+constexpr int kPieces = kBK * 2 / 16;                  // 16-byte pieces per tile row
+constexpr int kTileBytes = kBM * kBK * 2;              // 16 KB
+constexpr int kStageBytes = 2 * kTileBytes;            // the W tile, then the x tile
+constexpr int kDmaPerWave = kStageBytes / 1024 / 4;    // 8
+static_assert(kBM == kBN, "one tile shape for both operands");
+}  // namespace gemm
+
+// One 16-byte-per-lane DMA, global -> LDS (lane l lands at lds + 16 l).  In
+// inline asm so that the compiler's LDS reads do not all wait for every DMA
+// in flight; the kernel orders the tiles itself (waitcnt + barrier).  M0
+// carries the LDS address and is restored; the s_nop is the wait state an M0
+// write needs before an LDS DMA reads it.
+__device__ __forceinline__ void gemm_dma16(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+
+__global__ __launch_bounds__(256) void prolog_gemm_kernel(PrologLaunch a) {
+  using namespace gemm;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cidx = lane & 15, grp = lane >> 4;
+  const int F = a.H_I * a.D_I;
+  const int nqt = (F + kBM - 1) / kBM, ngt = (a.H_I + kBM - 1) / kBM;
+  const int rtiles = (a.num_rows + kBN - 1) / kBN;
+  const int nproj = (nqt + ngt) * rtiles;
+  const int bid = blockIdx.x;
+  if (bid >= nproj) {  // K normalisation and quantisation: one wave per row
+    const int r = (bid - nproj) * 4 + wave;
+    if (r < a.num_rows) key_norm_row(a, r, lane);
+    return;
+  }
+  // units in (feature tile, row tile) order, dealt so that each XCD runs
+  // consecutive units: the row tiles of a feature tile share its weights in
+  // one L2
+  const int unit = xcd_unit(bid, nproj);
+  const int ft = unit / rtiles, rt = unit % rtiles;
+  const bool is_q = ft < nqt;
+  const uint16_t* W = is_q ? a.w_q : a.w_g;
+  const int nfeat = is_q ? F : a.H_I;
+  const int f0 = kBM * (is_q ? ft : ft - nqt), r0 = kBN * rt;
+  const int nst = (a.D_x + kBK - 1) / kBK;
+
+  // DMA of stage st: instruction i = kDmaPerWave wave + t fills the stage's
+  // slots 64 i .. 64 i + 63: tile i / 16 (0: weights, 1: x), row sl / 8 and
+  // LDS piece sl % 8 of it (sl = 64 (i % 16) + lane).  Rows past the last
+  // feature or row read the last one (unused); inputs past D_x (a last stage
+  // of 32) read the stage's first piece (unused).
+  const uint8_t* src_row[kDmaPerWave];
+  int src_piece[kDmaPerWave];
+#pragma unroll
+  for (int t = 0; t < kDmaPerWave; ++t) {
+    const int i = kDmaPerWave * wave + t, sl = 64 * (i % 16) + lane;
+    const int row = sl / kPieces, pc = sl % kPieces;
+    const bool wt = i < 16;
+    const int g = wt ? min(f0 + row, nfeat - 1) : min(r0 + row, a.num_rows - 1);
+    src_row[t] = reinterpret_cast<const uint8_t*>((wt ? W : a.x) + (int64_t)g * a.D_x);
+    src_piece[t] = pc ^ (row & 7);
+  }
+  auto issue = [&](int st) {
+    const int k0 = kBK * st;
+    const uint32_t base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(lds + (st & 1) * kStageBytes + 1024 * kDmaPerWave * wave));
+#pragma unroll
+    for (int t = 0; t < kDmaPerWave; ++t) {
+      const int k = k0 + 8 * src_piece[t];
+      gemm_dma16(src_row[t] + 2 * (k < a.D_x ? k : k0), base + 1024 * t);
+    }
+  };
+
+  // this wave's 64 x 64 sub-tile and its operand read offsets
+  const int fw = 64 * (wave & 1), rw = 64 * (wave >> 1);
+  v4f acc[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  issue(0);
+  if (nst > 1) issue(1);
+  for (int st = 0; st < nst; ++st) {
+    if (st + 1 < nst)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerWave) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every wave's DMAs of stage st have landed
+    const uint8_t* wt = lds + (st & 1) * kStageBytes;
+    const uint8_t* xt = wt + kTileBytes;
+    const int nks = min(2, (a.D_x - kBK * st) / 32);  // 32-input MFMA steps in the stage
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (ks < nks) {
+        v8s af[4], bf[4];
+        const int pc = 4 * ks + grp;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int ra = fw + 16 * m + cidx, rb = rw + 16 * m + cidx;
+          af[m] = *reinterpret_cast<const v8s*>(wt + 16 * (ra * kPieces + (pc ^ (ra & 7))));
+          bf[m] = *reinterpret_cast<const v8s*>(xt + 16 * (rb * kPieces + (pc ^ (rb & 7))));
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(v8bf, af[mt]), __builtin_bit_cast(v8bf, bf[nt]), acc[mt][nt], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every wave is done with buffer st & 1
+    if (st + 2 < nst) issue(st + 2);
+  }
+
+  // epilogue: lane (grp, cidx), register i of tile (mt, nt) holds feature
+  // f0 + fw + 16 mt + 4 grp + i of row r0 + rw + 16 nt + cidx; a q group of 32
+  // features is the tile pair (2 p, 2 p + 1), spread over the 4 lanes of
+  // equal cidx
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int r = r0 + rw + 16 * nt + cidx;
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+      const int fg = f0 + fw + 32 * pg;  // the group's first feature
+      float vb[2][4];
+      float m = 0.0f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          vb[h][i] = bf16_round_f(acc[2 * pg + h][nt][i]);
+          m = fmaxf(m, fabsf(vb[h][i]));
+        }
+      if (is_q) {
+        const int se = mx_shared_exp(across_rows(m, FMax{}));
+        if (r < a.num_rows && fg < F) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) c |= e4m3_code(ldexpf(vb[h][i], -se)) << (8 * i);
+            *reinterpret_cast<uint32_t*>(a.qI + (int64_t)r * F + fg + 16 * h + 4 * grp) = c;
+          }
+          if (grp == 0) a.qI_scale[(int64_t)r * (F / 32) + fg / 32] = (uint8_t)(se + 127);
+        }
+      } else if (r < a.num_rows) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int f = fg + 16 * h + 4 * grp + i;
+            if (f < a.H_I) a.w[(int64_t)r * a.H_I + f] = vb[h][i];
+          }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_indexer_prolog(const PrologLaunch& a, hipStream_t s) {
@@ -411,10 +585,10 @@ hipError_t launch_indexer_prolog(const PrologLaunch& a, hipStream_t s) {
     const int n = F / 32 + (a.H_I + 31) / 32 + (a.num_rows + KS - 1) / KS;
     prolog_kernel<NT, KS><<<n, 64 * KS, 0, s>>>(a);
   } else {
-    constexpr int NT = 4, KS = 4;
-    const int rt = (a.num_rows + 16 * NT - 1) / (16 * NT);
-    const int n = (F / 32) * rt + ((a.H_I + 31) / 32) * rt + (a.num_rows + KS - 1) / KS;
-    prolog_kernel<NT, KS><<<n, 64 * KS, 0, s>>>(a);
+    using namespace gemm;
+    const int rt = (a.num_rows + kBN - 1) / kBN;
+    const int n = ((F + kBM - 1) / kBM + (a.H_I + kBM - 1) / kBM) * rt + (a.num_rows + 3) / 4;
+    prolog_gemm_kernel<<<n, 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }
