@@ -86,7 +86,8 @@ template <int NKP, int HT, bool MX, bool CAND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void indexer_scan_kernel(IndexerLaunch a) {
   const int r = a.row_begin + (int)blockIdx.y;
   const int tile0 = (int)blockIdx.x * kTile;
-  const int lane = threadIdx.x & 63;
+  const int tid = (int)(threadIdx.x & 255);  // the mask tells the compiler tid < 256
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;  // head row of A, position column of B
   const int g = lane >> 4;    // K slice group
@@ -99,9 +100,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
 
   // Load order matters (vector loads complete in issue order): one round
   // trip fetches the row's length, the tile's block ids and the row's query
-  // and weights (once per workgroup, staged in LDS), then every key load is
-  // issued, and each sub-tile is computed as soon as its own keys have
-  // landed.
+  // and weights (once per workgroup, staged in LDS).  Every key load is
+  // issued as soon as the block ids are back; the query and weights, which
+  // left just after them, are put in LDS only then, so their bytes (a whole
+  // query per workgroup) do not hold up the key stream.  Each sub-tile is
+  // computed as soon as its own keys have landed.
 
   // 1. block ids of the tile's pages, one per lane (read back into scalar
   //    registers per sub-tile), fetched alongside the row's length rather
@@ -127,31 +130,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     for (int j = 0; j < kSubPerWave; ++j)
       cpos[j] = crow[min(tile0 + wave * kSpan + j * kSub + col, a.rows.n_cand - 1)];
   }
+  // the padded query is HT*16 rows of kRowBytes <= 8 KiB: two 16-byte
+  // pieces per thread (clamped reads, selected when stored)
+  const int qbytes = a.H_I * kRowBytes;  // a multiple of 64
+  constexpr int kQBytes = HT * 16 * kRowBytes;
+  const int off0 = tid * 16, off1 = off0 + 256 * 16;
+  v4i q0, q1;
+  float wv;
+  uint32_t qsv = 127u;
   {
-    // the padded query is HT*16 rows of kRowBytes <= 8 KiB: two 16-byte
-    // pieces per thread; all loads are issued before any LDS write
     const uint8_t* qrow = a.qI + (int64_t)r * a.H_I * kRowBytes;
-    const int qbytes = a.H_I * kRowBytes;  // a multiple of 64
-    constexpr int kQBytes = HT * 16 * kRowBytes;
-    const int off0 = threadIdx.x * 16, off1 = off0 + 256 * 16;
-    const v4i z = v4i{0, 0, 0, 0};
-    v4i q0 = *reinterpret_cast<const v4i*>(qrow + min(off0, qbytes - 16));
-    v4i q1 = *reinterpret_cast<const v4i*>(qrow + min(off1, qbytes - 16));
-    float wv = a.w[(int64_t)r * a.H_I + min((int)threadIdx.x, a.H_I - 1)];
-    q0 = off0 < qbytes ? q0 : z;
-    q1 = off1 < qbytes ? q1 : z;
-    wv = (int)threadIdx.x < a.H_I ? wv : 0.0f;
-    if (off0 < kQBytes) *reinterpret_cast<v4i*>(&q_lds[off0]) = q0;
-    if (off1 < kQBytes) *reinterpret_cast<v4i*>(&q_lds[off1]) = q1;
-    if (threadIdx.x < HT * 16) w_lds[threadIdx.x] = wv;
-    if (MX) {  // the row's query scales; padding heads get 127 (x1, zero codes)
+    q0 = *reinterpret_cast<const v4i*>(qrow + min(off0, qbytes - 16));
+    q1 = *reinterpret_cast<const v4i*>(qrow + min(off1, qbytes - 16));
+    wv = a.w[(int64_t)r * a.H_I + min(tid, a.H_I - 1)];
+    if (MX) {  // the row's query scales
       const uint8_t* qsrow = a.qI_scale + (int64_t)r * a.H_I * kNG;
-      const int nqs = a.H_I * kNG;
-      uint32_t qsv = qsrow[min((int)threadIdx.x, nqs - 1)];
-      if ((int)threadIdx.x >= nqs) qsv = 127u;
-      if (threadIdx.x < 64 * kNG) qs_lds[threadIdx.x] = qsv;
+      qsv = qsrow[min(tid, a.H_I * kNG - 1)];
     }
   }
+  // nothing below may be hoisted above these loads, nor they sunk below
+  __builtin_amdgcn_sched_barrier(0);
 
   const int L = row_finish(a.rows, ri);
   if (L == 0) {
@@ -234,6 +232,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+  // the query and weights into LDS, heads past H_I as zero (query scales:
+  // 127, i.e. x1, for padding heads)
+  {
+    const v4i z = v4i{0, 0, 0, 0};
+    q0 = off0 < qbytes ? q0 : z;
+    q1 = off1 < qbytes ? q1 : z;
+    wv = tid < a.H_I ? wv : 0.0f;
+    if (off0 < kQBytes) *reinterpret_cast<v4i*>(&q_lds[off0]) = q0;
+    if (off1 < kQBytes) *reinterpret_cast<v4i*>(&q_lds[off1]) = q1;
+    if (tid < HT * 16) w_lds[tid] = wv;
+    if (MX) {
+      if (tid >= a.H_I * kNG) qsv = 127u;
+      if (tid < 64 * kNG) qs_lds[tid] = qsv;
+    }
+  }
   __syncthreads();
   // A operands (heads 16*ht + col); the head weights of this lane's
   // accumulator rows (register v of a 16x16 tile is row 4*g + v) are read
