@@ -1148,13 +1148,14 @@ __global__ __launch_bounds__(64 * kNW, 1) void sparse_attn_latent_kernel(AttnLau
 // sum_c g_c sum_c.  A workgroup of 32 MTW threads takes one row, one block
 // of 16 heads and MTW of its 16-dim tiles; thread t holds 8 consecutive
 // floats of that slice of every chunk's partial (tile t / 32, head
-// (t / 2) % 16, dims 8 (t % 2) .. +7), loaded kBatch chunks per round trip.
-// Small workgroups make many of them: the merge is a streaming read.
-template <int DV, int MTW>
+// (t / 2) % 16, dims 8 (t % 2) .. +7), loaded kBatch chunks per round trip
+// (kBatch: the chunk count rounded up to a power of two, at most 16, so no
+// load repeats a chunk).  Small workgroups make many of them: the merge is a
+// streaming read.
+template <int DV, int MTW, int kBatch>
 __global__ __launch_bounds__(32 * MTW) void attn_combine_kernel(AttnLaunch a) {
   constexpr int MT = DV / 16;
   static_assert(MT % MTW == 0, "tiles per workgroup");
-  constexpr int kBatch = 16;
   const int row_local = (int)blockIdx.x;
   const int r = a.row_begin + row_local;
   const int hb = (int)blockIdx.y;
@@ -1278,8 +1279,11 @@ hipError_t launch_t(const AttnLaunch& a, hipStream_t s, StageEvents ev, StageEve
     return hipSuccess;
   }
   constexpr int MT = DV / 16, MTW = MT < DSA_ATTN_MERGE_TILES ? MT : DSA_ATTN_MERGE_TILES;
-  return launch_kernel(attn_combine_kernel<DV, MTW>,
-                       dim3(a.num_rows, (a.H_q + 15) / 16, MT / MTW), dim3(32 * MTW), s,
+  void (*combine)(AttnLaunch) = a.n_chunks <= 2   ? attn_combine_kernel<DV, MTW, 2>
+                                : a.n_chunks <= 4 ? attn_combine_kernel<DV, MTW, 4>
+                                : a.n_chunks <= 8 ? attn_combine_kernel<DV, MTW, 8>
+                                                  : attn_combine_kernel<DV, MTW, 16>;
+  return launch_kernel(combine, dim3(a.num_rows, (a.H_q + 15) / 16, MT / MTW), dim3(32 * MTW), s,
                        merge.start, merge.stop, a);
 }
 
