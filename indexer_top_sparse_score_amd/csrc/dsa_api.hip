@@ -317,7 +317,7 @@ int decode_run(const dsa_problem* p, const uint8_t* qI, const float* w, dsa_page
     aa.row_begin = row0;
     aa.num_rows = nr;
     // the workspace holds partials for the larger of the two layouts' counts
-    aa.n_chunks = attn_chunks(d.rp, p->H_q, p->D_qk, p->K, aa.latent);
+    aa.n_chunks = attn_chunks(d.rp, p->H_q, p->D_qk, p->K, aa.latent, aa.kv8);
     aa.partial = aa.n_chunks > 1 ? static_cast<void*>(base + d.part_off) : nullptr;
     if ((st = status_of(launch_sparse_attn(aa, s, stage(2), stage(3)))) != DSA_OK) return st;
   }
@@ -525,7 +525,7 @@ int dsa_sparse_attn(const dsa_problem* p, const uint16_t* q, dsa_paged k, dsa_pa
   if (p->num_rows == 0) return DSA_OK;
   AttnLaunch a = attn_launch(p, q, k, v, out, lse, static_cast<uint32_t*>(ws));
   a.indices = indices;
-  a.n_chunks = attn_chunks(p->num_rows, p->H_q, p->D_qk, p->K, a.latent);
+  a.n_chunks = attn_chunks(p->num_rows, p->H_q, p->D_qk, p->K, a.latent, a.kv8);
   a.partial = a.n_chunks > 1
                   ? static_cast<void*>(static_cast<char*>(ws) + kHeader)
                   : nullptr;

@@ -392,9 +392,10 @@ struct AttnLaunch {
   int32_t n_chunks;
 };
 // Chunks the index list of each row is split into for the kernel that the
-// layout (latent or not) selects, and the most either layout may use (for
-// workspace sizes, which do not know the layout).
-int attn_chunks(int num_rows, int H_q, int D_qk, int K, bool latent);
+// layout (latent or not) and the cache format (kv8: FP8 rows) select, and
+// the most any of them may use (for workspace sizes, which do not know the
+// layout or the format).
+int attn_chunks(int num_rows, int H_q, int D_qk, int K, bool latent, bool kv8);
 int attn_chunks_max(int num_rows, int H_q, int D_qk, int K);
 size_t attn_partial_bytes(int num_rows, int H_q, int D_v, int n_chunks);
 // whether launch_sparse_attn reads row offsets (AttnLaunch.rowoff) for this

@@ -1228,8 +1228,20 @@ __global__ __launch_bounds__(32 * MTW) void attn_combine_kernel(AttnLaunch a) {
 #ifndef DSA_ATTN_LAT_WAVES
 #define DSA_ATTN_LAT_WAVES 2
 #endif
-int waves_for(int H_q, int D_qk, bool latent) {
-  if (D_qk == 576 && latent && DSA_ATTN_LATENT_DMA) return DSA_ATTN_LAT_WAVES;
+//
+// From kWideRows rows on, bf16 latent rows take 64-head workgroups instead
+// (four head waves, no key split: sparse_attn_latent_kernel<4, 4, 1>): each
+// gathered row is then staged by half as many workgroups, which outweighs
+// the larger partials once many rows fill the chip (measured on 32 rows x
+// 32k: attention + merge 49.6 -> 47.2 us; 64 ragged rows up to 128k: 90.9
+// -> 78.4 us; 4096 prefill rows: attention 254 -> 201 us per pass), while
+// with 4 rows the key split of the 32-head workgroup is worth more (12.6
+// against 13.6 us).  FP8 rows keep the 32-head kernel, the only one that
+// decodes them.
+constexpr int kWideRows = 16;
+int waves_for(int H_q, int D_qk, bool latent, int num_rows, bool kv8) {
+  if (D_qk == 576 && latent && DSA_ATTN_LATENT_DMA)
+    return !kv8 && num_rows >= kWideRows ? 4 : DSA_ATTN_LAT_WAVES;
   return (H_q > kHPW || D_qk > 64) ? 4 : 1;
 }
 
@@ -1251,7 +1263,8 @@ hipError_t launch_t(const AttnLaunch& a, hipStream_t s, StageEvents ev, StageEve
     if (uses_latent_kernel(DQK, a.latent)) {
       // two key halves per workgroup (four waves: every SIMD of the CU
       // busy), for split and whole rows alike
-      kernel = sparse_attn_latent_kernel<DSA_ATTN_NBUF, NW, 1>;
+      // (64-head workgroups: four sub-block buffers, two steps in flight)
+      kernel = NW == 4 ? sparse_attn_latent_kernel<4, 4, 1> : sparse_attn_latent_kernel<DSA_ATTN_NBUF, NW, 1>;
       if constexpr (NW == 2) {
         if (DSA_ATTN_KSPLIT == 2) {
           kernel = sparse_attn_latent_kernel<4, 4, 2>;
@@ -1270,7 +1283,8 @@ hipError_t launch_t(const AttnLaunch& a, hipStream_t s, StageEvents ev, StageEve
     if (!kernel && !a.kv8)
       kernel = a.latent ? sparse_attn_kernel<DQK, DV, true, NW> : sparse_attn_kernel<DQK, DV, false, NW>;
   }
-  if (!kernel) return hipErrorInvalidConfiguration;
+  // FP8 rows only ever run the two-head-wave kernel, which decodes them
+  if (!kernel || (a.kv8 && NW != 2)) return hipErrorInvalidConfiguration;
   hipError_t e = launch_kernel(kernel, dim3(grid), dim3(threads), s, ev.start, ev.stop, a, g);
   if (e != hipSuccess) return e;
   if (a.n_chunks == 1) {
@@ -1289,9 +1303,9 @@ hipError_t launch_t(const AttnLaunch& a, hipStream_t s, StageEvents ev, StageEve
 
 }  // namespace
 
-int attn_chunks(int num_rows, int H_q, int D_qk, int K, bool latent) {
+int attn_chunks(int num_rows, int H_q, int D_qk, int K, bool latent, bool kv8) {
   if (num_rows <= 0) return 1;
-  const int hpw = kHPW * waves_for(H_q, D_qk, latent);
+  const int hpw = kHPW * waves_for(H_q, D_qk, latent, num_rows, kv8);
   const int n_hg = (H_q + hpw - 1) / hpw;
   const int want = (DSA_ATTN_TARGET_WGS + num_rows * n_hg - 1) / (num_rows * n_hg);
   const int cap = uses_latent_kernel(D_qk, latent) ? kMaxChunkLat : kMaxChunk;
@@ -1307,7 +1321,9 @@ size_t attn_partial_bytes(int num_rows, int H_q, int D_v, int n_chunks) {
 }
 
 int attn_chunks_max(int num_rows, int H_q, int D_qk, int K) {
-  return max(attn_chunks(num_rows, H_q, D_qk, K, true), attn_chunks(num_rows, H_q, D_qk, K, false));
+  // (FP8 rows, in 32-head workgroups, never take more chunks than bf16 rows)
+  return max(attn_chunks(num_rows, H_q, D_qk, K, true, false),
+             attn_chunks(num_rows, H_q, D_qk, K, false, false));
 }
 
 bool attn_uses_rowoff(int D_qk, int D_v, bool latent) {
@@ -1317,7 +1333,7 @@ bool attn_uses_rowoff(int D_qk, int D_v, bool latent) {
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s, StageEvents ev,
                               StageEvents merge) {
   if (a.num_rows <= 0) return hipSuccess;
-  switch (waves_for(a.H_q, a.D_qk, a.latent) * 1000 + a.D_qk) {
+  switch (waves_for(a.H_q, a.D_qk, a.latent, a.num_rows, a.kv8) * 1000 + a.D_qk) {
     case 2576: return launch_t<576, 512, 2>(a, s, ev, merge);
     case 4576: return launch_t<576, 512, 4>(a, s, ev, merge);
     case 4064: return launch_t<64, 64, 4>(a, s, ev, merge);

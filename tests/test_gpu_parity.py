@@ -55,6 +55,13 @@ CASES = {
     "tiny_cand": dict(lengths=[1, 50, 64, 1024, 3000], mode="int", n_cand=700, **TINY),
     # FP8 KV cache: E4M3 latent rows with one float32 scale per tile of 128
     "mla_fp8kv": dict(lengths=LENGTHS, mode="int", kv_fmt="fp8", table="shuffled", **MLA),
+    # 16 rows and more: bf16 latent rows take the 64-head attention workgroups
+    # (no key split), also with a head count that leaves the second workgroup
+    # of a row 16 heads; FP8 rows keep the 32-head kernel
+    "mla_wide": dict(lengths=LENGTHS * 2, mode="int", table="shuffled", **MLA),
+    "h80_wide": dict(lengths=[777, 2500] * 8 + [3000], mode="int",
+                     **{**MLA, "H_I": 48, "D_I": 64, "H_q": 80}),
+    "mla_fp8kv_wide": dict(lengths=LENGTHS * 2, mode="int", kv_fmt="fp8", **MLA),
 }
 
 
@@ -150,7 +157,7 @@ def test_topk_ties_and_special_values():
 
 
 @pytest.mark.parametrize("name", ["mla_int", "tiny_int", "mla_int_k100", "h48_d64", "mla_sepv",
-                                  "mla_fp8kv"])
+                                  "mla_fp8kv", "mla_wide", "h80_wide", "mla_fp8kv_wide"])
 def test_sparse_attn_on_oracle_indices(name):
     batch = _batch(name, mode="gauss", seed=25)
     arr = oracle_arrays(batch)
@@ -163,7 +170,7 @@ def test_sparse_attn_on_oracle_indices(name):
     say(f"attention {name}: max {mx:.3g} mean {mean:.3g}")
 
 
-@pytest.mark.parametrize("name", ["mla_int", "mla_fp8kv"])
+@pytest.mark.parametrize("name", ["mla_int", "mla_fp8kv", "mla_wide"])
 def test_sparse_attn_skips_padding_and_handles_empty_rows(name):
     _padding_case(name)
 
@@ -171,7 +178,7 @@ def test_sparse_attn_skips_padding_and_handles_empty_rows(name):
 # a zero or negative logit scale must not turn the masked (absent) keys into
 # NaN or +inf: the kernels mask after scaling (regression test)
 @pytest.mark.parametrize("scale", [0.0, -1.0 / 24.0])
-@pytest.mark.parametrize("name", ["mla_int", "tiny_int", "mla_fp8kv"])
+@pytest.mark.parametrize("name", ["mla_int", "tiny_int", "mla_fp8kv", "mla_wide"])
 def test_sparse_attn_padding_with_zero_and_negative_scale(name, scale):
     _padding_case(name, scale=scale)
 
@@ -224,7 +231,8 @@ def _padding_case(name, **over):
 
 @pytest.mark.parametrize("name", ["mla_int", "mla_int_shuffled", "tiny_int", "mla_int_k100",
                                   "mla_sepv", "mla_int_grouped", "mla_mx_int", "mla_cand_int",
-                                  "mla_cand_split", "mla_mx_cand", "tiny_cand", "mla_fp8kv"])
+                                  "mla_cand_split", "mla_mx_cand", "tiny_cand", "mla_fp8kv",
+                                  "mla_wide", "h80_wide", "mla_fp8kv_wide"])
 def test_decode_step_integer_mode(name):
     batch = _batch(name, seed=27)
     arr = oracle_arrays(batch)
