@@ -329,12 +329,279 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
   if (CAND && __builtin_amdgcn_ballot_w64(bad_pos) && lane == 0) report(a.err, DSA_DEVERR_ROW);
 }
 
+// The scan for chunked-prefill rows: NR consecutive rows per workgroup.
+// Rows of one sequence score the same index keys, so a workgroup takes NR
+// rows for its tile and runs every row's MFMAs and epilogue on one set of
+// key loads: NR times fewer key bytes through L2 for the same MFMA work.  A
+// row of another sequence than the workgroup's first (a pass across two
+// prefill chunks) loads its own keys.  Everything else is as in
+// indexer_scan_kernel (no candidate lists here).
+template <int NKP, int HT, bool MX, int NR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void indexer_scan_rows_kernel(IndexerLaunch a) {
+  static_assert(NR > 1, "one row per workgroup: indexer_scan_kernel");
+  const int r0 = a.row_begin + (int)blockIdx.y * NR;
+  const int nr = min(NR, a.row_begin + a.num_rows - r0);  // this workgroup's rows, >= 1
+  const int tile0 = (int)blockIdx.x * kTile;
+  const int tid = (int)(threadIdx.x & 255);  // the mask tells the compiler tid < 256
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15;  // head row of A, position column of B
+  const int g = lane >> 4;    // K slice group
+  constexpr int kRowBytes = 64 * NKP;
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[NR][64 * 128];
+  __shared__ __attribute__((aligned(16))) float w_lds[NR][64];
+  constexpr int kNG = 2 * NKP;                 // 32-dim groups of a row (MX)
+  __shared__ uint32_t qs_lds[NR][MX ? 64 * kNG : 1];  // query scales, one per word
+  __shared__ float sc_lds[NR][kWaves][kSpan];
+
+  // Load order matters (vector loads complete in issue order): one round
+  // trip fetches the rows' lengths, the tile's block ids and the rows'
+  // queries and weights (staged in LDS before the key loads go out, which
+  // keeps their registers free).  Each sub-tile is computed as soon as its
+  // own keys have landed.
+
+  // 1. block ids of the tile's pages, one per lane (read back into scalar
+  //    registers per sub-tile), fetched alongside the rows' lengths rather
+  //    than after them; queries and weights into LDS, heads past H_I as zero
+  constexpr int kPages = kTile / kBlock;
+  static_assert(kPages <= 64, "tile spans more pages than a wave has lanes");
+  // Every load of this round trip is unconditional, from a clamped
+  // (always valid) address, and selected afterwards: a branch would make
+  // the compiler wait for each load where it merges.
+  RowIssue ri[NR];
+#pragma unroll
+  for (int k = 0; k < NR; ++k) ri[k] = row_issue(a.rows, r0 + min(k, nr - 1));
+  const int b = ri[0].b;
+  const bool b_ok = ri[0].b_ok;
+  const int32_t* bt = a.rows.block_table + (int64_t)(b_ok ? b : 0) * a.rows.max_blocks;
+  // block id of the tile's page `lane` (lanes past the tile's pages, or past
+  // the table's columns, read a valid entry that is never used)
+  const int my_page = bt[min(tile0 / kBlock + lane, a.rows.max_blocks - 1)];
+  // the padded query is HT*16 rows of kRowBytes <= 8 KiB: two 16-byte
+  // pieces per thread (clamped reads, selected when stored)
+  const int qbytes = a.H_I * kRowBytes;  // a multiple of 64
+  constexpr int kQBytes = HT * 16 * kRowBytes;
+  const int off0 = tid * 16, off1 = off0 + 256 * 16;
+  v4i q0[NR], q1[NR];
+  float wv[NR];
+  uint32_t qsv[NR];
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    const int rk = r0 + min(k, nr - 1);
+    const uint8_t* qrow = a.qI + (int64_t)rk * a.H_I * kRowBytes;
+    q0[k] = *reinterpret_cast<const v4i*>(qrow + min(off0, qbytes - 16));
+    q1[k] = *reinterpret_cast<const v4i*>(qrow + min(off1, qbytes - 16));
+    wv[k] = a.w[(int64_t)rk * a.H_I + min(tid, a.H_I - 1)];
+    qsv[k] = 127u;
+    if (MX) {  // the row's query scales
+      const uint8_t* qsrow = a.qI_scale + (int64_t)rk * a.H_I * kNG;
+      qsv[k] = qsrow[min(tid, a.H_I * kNG - 1)];
+    }
+  }
+  // nothing below may be hoisted above these loads, nor they sunk below
+  __builtin_amdgcn_sched_barrier(0);
+  // the queries and weights into LDS, heads past H_I as zero (query scales:
+  // 127, i.e. x1, for padding heads)
+  auto stage_queries = [&]() {
+    const v4i z = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      const v4i x0 = off0 < qbytes ? q0[k] : z;
+      const v4i x1 = off1 < qbytes ? q1[k] : z;
+      const float w = tid < a.H_I ? wv[k] : 0.0f;
+      if (off0 < kQBytes) *reinterpret_cast<v4i*>(&q_lds[k][off0]) = x0;
+      if (off1 < kQBytes) *reinterpret_cast<v4i*>(&q_lds[k][off1]) = x1;
+      if (tid < HT * 16) w_lds[k][tid] = w;
+      if (MX) {
+        const uint32_t qs = tid >= a.H_I * kNG ? 127u : qsv[k];
+        if (tid < 64 * kNG) qs_lds[k][tid] = qs;
+      }
+    }
+  };
+  stage_queries();
+
+  // history lengths L and score-row lengths S of the rows; a workgroup whose
+  // rows all end before its tile has nothing to do
+  int Lr[NR], Sr[NR];
+  bool any = false;
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    Lr[k] = k < nr ? row_finish(a.rows, ri[k]) : 0;
+    if (k < nr && Lr[k] == 0 && blockIdx.x == 0 && threadIdx.x == 0) report(a.err, DSA_DEVERR_ROW);
+    Sr[k] = Lr[k];  // slots of the score row: its positions
+    any = any || tile0 < Sr[k];
+  }
+  if (!any) return;
+
+  // 2. keys: this wave owns the kSpan positions from w0; sub-tile j starts
+  //    at w0 + 16j.  Straight-line code lets the compiler wait for each
+  //    sub-tile alone (vmcnt(N)) while the later loads stay in flight.
+  const int w0 = tile0 + wave * kSpan;
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.kI.base);
+  const uint32_t lane_off = (uint32_t)(col * a.kI.row_stride + 16 * g);
+  v8i keys[kSubPerWave];
+  bool page_ok[kSubPerWave];
+  // MX: the scale words of the wave's key rows.  The wave's 128 positions
+  // are two whole blocks (w0 is a multiple of 128), and a block keeps its
+  // 64 rows' scales together after its code rows: lane l takes row l's
+  // scales from block h, so word h of lane l belongs to sub-tile 4h + l / 16,
+  // row l % 16, and each load is one contiguous run.  Each sub-tile fetches
+  // its rows' words across lanes when it needs them, so only two registers
+  // stay in flight.
+  static_assert(kSubPerWave == 8 && kSpan == 2 * kBlock, "two scale words per lane cover the wave");
+  uint32_t ksw[MX ? 2 : 1];
+  // the keys (and MX scale words) of a sequence whose tile block ids are
+  // `page` (one per lane) in a table of max_blocks columns
+  auto load_keys = [&](int page) {
+#pragma unroll
+    for (int j = 0; j < kSubPerWave; ++j) {
+      const int s0 = w0 + j * kSub;
+      const int phys = __builtin_amdgcn_readlane(page, (s0 - tile0) >> 6);
+      // a page past the table's columns, or with an id out of range, is absent
+      page_ok[j] = s0 / kBlock < a.rows.max_blocks && phys >= 0 && (int64_t)phys < a.kI.num_blocks;
+      const uint8_t* sub = kbase + (int64_t)(page_ok[j] ? phys : 0) * a.kI.block_stride +
+                           (int64_t)(s0 & 63) * a.kI.row_stride;
+      keys[j] = load_slice<NKP>(sub, lane_off);
+    }
+    if constexpr (MX) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int phys = __builtin_amdgcn_readlane(page, ((w0 - tile0) >> 6) + h);
+        const uint8_t* area = kbase + (int64_t)(page_ok[4 * h] ? phys : 0) * a.kI.block_stride +
+                              (int64_t)kBlock * a.kI.row_stride;
+        if constexpr (kNG == 4)
+          ksw[h] = *reinterpret_cast<const uint32_t*>(area + 4 * lane);
+        else
+          ksw[h] = *reinterpret_cast<const uint16_t*>(area + 2 * lane);
+      }
+    }
+  };
+  load_keys(my_page);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+
+  // The wave's scores are collected in LDS, every row's before any row's
+  // epilogue (the keys stay live for the next row's MFMAs, the epilogue's
+  // registers come after them), and written with a few full-width stores,
+  // not one narrow store per sub-tile.
+  static_assert(kSpan == 128 && kSubPerWave == 8, "a wave's summary covers two halves of 64");
+  bool bad_page = false;
+  // row k of the workgroup (one that needs this tile): its scores on the
+  // loaded keys into LDS
+  auto score_row = [&](int k) __attribute__((always_inline)) {
+    const int L = Lr[k];
+    float* my_sc = sc_lds[k][wave];
+    // A operands (heads 16*ht + col); the head weights of this lane's
+    // accumulator rows (register v of a 16x16 tile is row 4*g + v) are read
+    // from LDS per use, which keeps the registers for keys in flight
+    v8i aq[HT];
+    // This lane's A scale for head tile ht (group g of head 16ht + col) sits
+    // in byte ht of one register, and the MFMA's op-select immediate picks
+    // the byte; E4M3 keeps 127 (x1) in every byte.
+    int qscale = 0x7F7F7F7F;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const v4i* src = reinterpret_cast<const v4i*>(&q_lds[k][(16 * ht + col) * kRowBytes]);
+      const v4i lo = src[g];
+      const v4i hi = NKP == 2 ? src[g + 4] : v4i{0, 0, 0, 0};
+      aq[ht] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      if (MX && g < kNG)
+        qscale = (qscale & ~(0xFF << (8 * ht))) | ((int)qs_lds[k][(16 * ht + col) * kNG + g] << (8 * ht));
+    }
+#pragma unroll
+    for (int j = 0; j < kSubPerWave; ++j) {
+      float part = 0.0f;
+      // B scale: byte g of the key row's scale word (127, i.e. x1, for
+      // unused groups and for E4M3)
+      int ks = 127;
+      if (MX) {
+        const uint32_t word = (uint32_t)__shfl((int)ksw[MX ? j / 4 : 0], 16 * (j % 4) + col);
+        ks = g < kNG ? (int)((word >> (8 * g)) & 0xFFu) : 127;
+      }
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        v4f acc;
+        switch (ht) {  // the op-select byte must be an immediate (ht is one once unrolled)
+          case 0: acc = mfma_scaled<0>(aq[ht], keys[j], qscale, MX ? ks : 127); break;
+          case 1: acc = mfma_scaled<1>(aq[ht], keys[j], qscale, MX ? ks : 127); break;
+          case 2: acc = mfma_scaled<2>(aq[ht], keys[j], qscale, MX ? ks : 127); break;
+          default: acc = mfma_scaled<3>(aq[ht], keys[j], qscale, MX ? ks : 127); break;
+        }
+        const v4f wr = *reinterpret_cast<const v4f*>(&w_lds[k][16 * ht + 4 * g]);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) part += wr[v] * fmaxf(acc[v], 0.0f);
+      }
+      part = across_rows(part, FAdd());
+      // canonical +0 for a zero score; an absent page scores -inf
+      const float v = page_ok[j] ? part + 0.0f : -__builtin_inff();
+      if (g == 0) my_sc[j * kSub + col] = v;
+      bad_page = bad_page || (w0 + j * kSub < L && !page_ok[j]);
+    }
+  };
+  // row k's epilogue: its scores out, and the Top-K's summary of this
+  // wave's slots (the kSumM largest keys of each segment, with their
+  // offsets, and the segment's next key), both halves at once
+  auto finish_row = [&](int k) __attribute__((always_inline)) {
+    const int S = Sr[k];
+    const int rk = r0 + k;
+    const float* my_sc = sc_lds[k][wave];
+    const bool summ = a.sum.key && w0 < S && sum_row(S, a.topk_K);  // wave-uniform
+    float* out = a.scores + (int64_t)(rk - a.row_begin) * a.ld;
+#pragma unroll
+    for (int h = 0; h < kSpan / 64; ++h) {
+      const int i = 64 * h + lane;
+      if (w0 + i < S) out[w0 + i] = my_sc[i];
+    }
+    if (summ) {
+      const int G = sum_seg(S);
+      const uint32_t ka = w0 + lane < S ? score_key(my_sc[lane]) : 0u;
+      const uint32_t kb = w0 + 64 + lane < S ? score_key(my_sc[64 + lane]) : 0u;
+      HalfSummary ha, hb;
+      summary_halves(ka, kb, G, ha, hb);
+      summary_store(ha, ka, w0, S, G, a.sum, rk - a.row_begin);
+      summary_store(hb, kb, w0 + 64, S, G, a.sum, rk - a.row_begin);
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    if (k < nr && tile0 < Sr[k]) {  // (workgroup-uniform)
+      // a row of another sequence: its own block ids, then its own keys
+      if (k > 0 && !(ri[k].b_ok && ri[k].b == b && b_ok)) {
+        const int32_t* btk = a.rows.block_table + (int64_t)ri[k].b * a.rows.max_blocks;
+        load_keys(btk[min(tile0 / kBlock + lane, a.rows.max_blocks - 1)]);
+      }
+      score_row(k);
+    }
+  }
+  // LDS accesses of one wave complete in order; the fence keeps the
+  // compiler from moving the reads above the writes of other lanes
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+  for (int k = 0; k < NR; ++k)
+    if (k < nr && tile0 < Sr[k]) finish_row(k);
+  if (__builtin_amdgcn_ballot_w64(bad_page) && lane == 0) report(a.err, DSA_DEVERR_BLOCK);
+}
+
+// Rows per workgroup for chunked-prefill rows (an explicit row -> sequence
+// map) with E4M3 operands; MXFP8 operands (two more live registers per lane)
+// and every other batch run one row per workgroup.
+#ifndef DSA_IDX_PREFILL_ROWS
+#define DSA_IDX_PREFILL_ROWS 2
+#endif
+constexpr int kPrefillRows = DSA_IDX_PREFILL_ROWS;
+
 template <int NKP, int HT, bool MX>
 hipError_t launch_t(const IndexerLaunch& a, hipStream_t s, StageEvents ev) {
-  dim3 grid((a.max_len + kTile - 1) / kTile, a.num_rows);
+  const int tiles = (a.max_len + kTile - 1) / kTile;
+  if constexpr (!MX && kPrefillRows > 1) {
+    if (!a.rows.cand && a.rows.row_seq && a.num_rows > 1)
+      return launch_kernel(indexer_scan_rows_kernel<NKP, HT, false, kPrefillRows>,
+                           dim3(tiles, (a.num_rows + kPrefillRows - 1) / kPrefillRows),
+                           dim3(256), s, ev.start, ev.stop, a);
+  }
   return launch_kernel(a.rows.cand ? indexer_scan_kernel<NKP, HT, MX, true>
                                    : indexer_scan_kernel<NKP, HT, MX, false>,
-                       grid, dim3(256), s, ev.start, ev.stop, a);
+                       dim3(tiles, a.num_rows), dim3(256), s, ev.start, ev.stop, a);
 }
 
 template <bool MX>

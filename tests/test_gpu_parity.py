@@ -7,6 +7,8 @@ bit-exact when both sides select from the same scores; attention -- max
 |error| <= 2e-2 and mean |error| <= 2e-3 against the oracle on the same
 indices."""
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -275,6 +277,31 @@ def test_decode_step_prefill_rows():
     arr = oracle_arrays(batch)
     orc = run_oracle(arr, keep_scores=False)
     res = gpu_decode(batch)
+    assert (np_(res["indices"]) == orc["indices"]).all()
+    check_attention(res["out"], res["lse"], orc["out"], orc["lse"])
+
+
+def test_decode_step_rows_of_mixed_sequences():
+    # an explicit row -> sequence map whose neighbouring rows mix sequences
+    # (and an odd row count): the chunked-prefill scan shares a workgroup's
+    # key loads only between rows of one sequence and loads its own keys for
+    # the others; scores bit-exact, indices exact, attention within bounds
+    wl = small_workload("mixed", lengths=[3000, 5000, 700, 4097, 1, 2500, 1200], mode="int",
+                        **MLA)
+    batch = make_batch(wl, device="cuda", seed=33)
+    L = batch.lengths
+    seq = [0, 0, 1, 3, 3, 5, 2]
+    pos = [L[0] - 1, L[0] // 2, L[1] - 1, L[3] - 1, L[3] - 3, L[5] - 1, L[2] - 1]
+    batch = dataclasses.replace(
+        batch, row_seq_host=seq, row_pos_host=pos,
+        row_seq=torch.tensor(seq, dtype=torch.int32, device="cuda"),
+        row_pos=torch.tensor(pos, dtype=torch.int32, device="cuda"))
+    say(f"rows -> sequences {seq}, positions {pos}")
+    arr = oracle_arrays(batch)
+    orc = run_oracle(arr)
+    check_scores_exact(gpu_scores(batch), orc, row_positions(batch))
+    res = gpu_decode(batch)
+    assert (np_(res["counts"]) == orc["counts"]).all()
     assert (np_(res["indices"]) == orc["indices"]).all()
     check_attention(res["out"], res["lse"], orc["out"], orc["lse"])
 
