@@ -133,6 +133,11 @@ int rows_per_pass(const dsa_problem* p, size_t budget = kScoresBudget) {
   const size_t per_row = (size_t)slab_ld(p) * sizeof(float) +
                          (needs_summary(p) ? (size_t)kSumEntries * 5 : 0);
   size_t rp = budget / per_row;
+  // a multiple of 128 rows when there is room for more: the attention of 16
+  // rows and more runs two workgroups per row, so 128 rows fill one round
+  // of the 256 CUs (390 rows per pass left 12 workgroups alone in a fourth
+  // round)
+  if (rp > 128) rp = rp / 128 * 128;
   if (rp < 1) rp = 1;
   if (rp > (size_t)p->num_rows) rp = (size_t)p->num_rows;
   return (int)rp;
