@@ -1261,11 +1261,12 @@ hipError_t launch_t(const AttnLaunch& a, hipStream_t s, StageEvents ev, StageEve
   int threads = 64 * NW;
   if constexpr (DQK == lat::kDqk && NW > 1) {
     if (uses_latent_kernel(DQK, a.latent)) {
-      // two key halves per workgroup (four waves: every SIMD of the CU
-      // busy), for split and whole rows alike
-      // (64-head workgroups: four sub-block buffers, two steps in flight)
+      // four head waves (64-head workgroups, from 16 rows on): no key
+      // split, four sub-block buffers
       kernel = NW == 4 ? sparse_attn_latent_kernel<4, 4, 1> : sparse_attn_latent_kernel<DSA_ATTN_NBUF, NW, 1>;
       if constexpr (NW == 2) {
+        // two head waves times two key halves (four waves: every SIMD of
+        // the CU busy), for split and whole rows alike
         if (DSA_ATTN_KSPLIT == 2) {
           kernel = sparse_attn_latent_kernel<4, 4, 2>;
           threads = 256;
