@@ -23,6 +23,8 @@
 // and the memory pipe never drains between rounds.  A sub-tile never
 // straddles a 64-row page; the tile's block ids are fetched once, one per
 // lane.  The query and weights are staged once per workgroup in LDS.
+// Chunked-prefill rows (an explicit row -> sequence map) take two rows per
+// workgroup on one set of key loads (indexer_scan_rows_kernel below).
 
 #include "dsa_common.h"
 
