@@ -223,6 +223,9 @@ struct Cfg {
   static constexpr int kKPieces = LATENT ? (DQK - DV) / 8 : DQK / 8;
   static constexpr int kKJobs = kSB * kKPieces;
   static constexpr int kKJ = (kKJobs + kThreads - 1) / kThreads;
+  // kKPieces as a divisor (with no K pieces beyond V, kKJ is 0 and it is
+  // never used)
+  static constexpr int kKDiv = kKPieces > 0 ? kKPieces : 1;
   static constexpr int kKsElems = kSB * KP;
   static constexpr int kVtElems = DV * VP;
 };
@@ -361,7 +364,7 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
 #pragma unroll
     for (int i = 0; i < C::kKJ; ++i) {
       const int job = tid + i * C::kThreads;
-      const int key = (job / C::kKPieces) % kSB, piece = job % C::kKPieces;
+      const int key = (job / C::kKDiv) % kSB, piece = job % C::kKDiv;
       const int64_t off = koff[base + key];
       const int d0 = (LATENT ? DV : 0) + 8 * piece;
       st.k[i] = *reinterpret_cast<const uint4*>(kbase + (off >= 0 ? off : 0) + d0 * 2);
@@ -405,7 +408,7 @@ __global__ __launch_bounds__(64 * NW, 1) void sparse_attn_kernel(AttnLaunch a, A
     for (int i = 0; i < C::kKJ; ++i) {
       const int job = tid + i * C::kThreads;
       const bool mine = C::kKJ * C::kThreads == C::kKJobs || job < C::kKJobs;
-      const int key = (job / C::kKPieces) % kSB, piece = job % C::kKPieces;
+      const int key = (job / C::kKDiv) % kSB, piece = job % C::kKDiv;
       const int d0 = (LATENT ? DV : 0) + 8 * piece;
       if (mine) *reinterpret_cast<uint4*>(&ks[key * C::KP + d0]) = keep_or_zero(st.k[i], koff[base + key] >= 0);
     }
